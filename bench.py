@@ -1,0 +1,280 @@
+#!/usr/bin/env python3
+"""Benchmark of the tree-verification attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch: ancestor-bitmask
+build (tree_attn_build_mask) + verification attention (tree_attn_verify,
+split-KV pass with the tree keys masked in registers, then the LSE merge).
+Inputs are resident in HBM before timing; the input sets are rotated over
+enough copies (>= 1 GiB in total) that no step finds its K/V in the 256 MB
+Infinity Cache left there by the previous step.
+
+Prints one JSON line on stdout.  Everything else goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+DEFAULT_WORKLOAD = "qwen3-8b-b256-p4k"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
+ROTATE_BYTES = 1 << 30
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--splits", type=int, default=0,
+                    help="0 = planned by the library")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline")
+    return ap.parse_args()
+
+
+# --------------------------------------------------------------------------
+# algorithmic work of one verify launch
+# --------------------------------------------------------------------------
+
+def algorithmic_work(wl):
+    """(bytes, flops) the method must move / compute for one verify call.
+
+    bytes: K and V of every cached token read once, q read and out written
+    once (bf16), lse written (fp32), the ancestor masks and the page-table
+    entries read once.  flops: 4*d per allowed (query, key) pair (2*d for
+    q.k, 2*d for p*v); masked-out tree pairs are not counted.
+    """
+    d, Hq, Hkv, ps = wl.head_dim, wl.num_q_heads, wl.num_kv_heads, wl.page_size
+    P = wl.prefix_lens.astype(np.int64)
+    B = wl.tree_sizes
+    N = wl.total_nodes
+    W = wl.mask_words()
+    tokens = P + B
+    nbytes = (int(tokens.sum()) * Hkv * d * 2 * 2 + 2 * N * Hq * d * 2 +
+              N * Hq * 4 + N * W * 8 + 4 * int(((tokens + ps - 1) // ps).sum()))
+    pairs = 0
+    for s in range(wl.num_seqs):
+        a, b = int(wl.tree_offsets[s]), int(wl.tree_offsets[s + 1])
+        par = wl.parents[a:b]
+        depth = np.zeros(b - a, dtype=np.int64)
+        for i in range(b - a):
+            depth[i] = 0 if par[i] < 0 else depth[par[i]] + 1
+        pairs += int(P[s]) * (b - a) + int((depth + 1).sum())
+    flops = 4 * d * Hq * pairs
+    return nbytes, flops
+
+
+# --------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, on the host cores
+# --------------------------------------------------------------------------
+
+def cpu_baseline(wl, target_s):
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()]
+                      or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    reps, t = 0, 0.0
+    t0 = time.perf_counter()
+    while True:
+        oracle.workload_masks(wl)
+        oracle.workload_attention(wl)
+        reps += 1
+        t = time.perf_counter() - t0
+        if t >= target_s or t / reps * (reps + 1) > 30.0:
+            break
+    return {"value": wl.total_nodes * reps / t, "unit": "tree tokens/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"{reps} full pass(es) of workload {wl.name} "
+                      f"(mask build + fp64 attention), {t:.1f} s"}
+
+
+# --------------------------------------------------------------------------
+# GPU timing
+# --------------------------------------------------------------------------
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only "
+              f"(--gpus {args.gpus} requested); nothing was run.",
+              file=sys.stderr)
+        return 2
+    import torch
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import tree_masked_attention_amd.api as api
+    from tree_masked_attention_amd.workloads import standard_workload
+
+    assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    log(f"[bench] drawing workload {args.workload}")
+    wl = standard_workload(args.workload)
+    alg_bytes, alg_flops = algorithmic_work(wl)
+    ai = alg_flops / alg_bytes
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    bound = "mfma" if ai > ridge else "hbm"
+
+    bf = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+    host = dict(q=bf(wl.q), k=bf(wl.k_cache), v=bf(wl.v_cache),
+                table=torch.from_numpy(wl.page_table),
+                prefix=torch.from_numpy(wl.prefix_lens),
+                offs=torch.from_numpy(wl.tree_offsets),
+                parents=torch.from_numpy(wl.parents))
+    per_copy = sum(t.numel() * t.element_size() for t in host.values())
+    copies = int(min(256, max(2, math.ceil(ROTATE_BYTES / per_copy))))
+    log(f"[bench] {per_copy / 2**20:.1f} MiB per input set, {copies} copies")
+    sets = []
+    for _ in range(copies):
+        sets.append({k: t.to(dev) for k, t in host.items()})
+
+    N, Hq, d = wl.q.shape
+    S = wl.num_seqs
+    W = wl.mask_words()
+    max_b = max(wl.max_nodes, 1)
+    masks = torch.empty((N, W), dtype=torch.int64, device=dev)
+    bad = torch.empty((max(S, 1),), dtype=torch.int32, device=dev)
+    out = torch.empty((N, Hq, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((N, Hq), dtype=torch.float32, device=dev)
+    ws_bytes = api.workspace_size(S, N, Hq, wl.num_kv_heads, d,
+                                  wl.max_prefix_len, wl.max_nodes, args.splits)
+    ws = torch.empty((max(ws_bytes, 256),), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+
+    # pre-marshalled C-ABI argument lists, one per input copy
+    calls = []
+    for c in sets:
+        mask_args = (c["parents"].data_ptr(), c["offs"].data_ptr(), S, N,
+                     max_b, W, masks.data_ptr(), bad.data_ptr(), sptr)
+        ver_args = (c["q"].data_ptr(), c["k"].data_ptr(), c["v"].data_ptr(),
+                    c["table"].data_ptr(), wl.max_pages_per_seq,
+                    wl.num_pages, wl.page_size, c["prefix"].data_ptr(),
+                    c["offs"].data_ptr(), masks.data_ptr(), W, S, N,
+                    wl.max_prefix_len, wl.max_nodes, Hq, wl.num_kv_heads, d,
+                    wl.scale, args.splits, out.data_ptr(), lse.data_ptr(),
+                    ws.data_ptr(), ws.numel(), sptr)
+        calls.append((mask_args, ver_args))
+    f_mask = api._lib.tree_attn_build_mask
+    f_ver = api._lib.tree_attn_verify
+
+    def step(i, ev=None):
+        ma, va = calls[i % copies]
+        if ev is not None:
+            ev[0].record(stream)
+        rc = f_mask(*ma)
+        if ev is not None:
+            ev[1].record(stream)
+        rc |= f_ver(*va)
+        if ev is not None:
+            ev[2].record(stream)
+        return rc
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        if step(i) != 0:
+            raise RuntimeError("tree_attn call failed during warmup")
+    torch.cuda.synchronize()
+    if (bad[:S] != -1).any():
+        raise RuntimeError("invalid tree in benchmark input")
+
+    # (1) whole-step throughput: K back-to-back steps
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+
+    # (2) per-launch durations of the same calls (events on the launch
+    #     stream around each call; waits between steps keep them apart)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+           for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    mask_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    ver_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    log(f"[bench] step {ms_per_step * 1e3:.1f} us; mask build "
+        f"{mask_ms * 1e3:.1f} us; verify {ver_ms * 1e3:.1f} us")
+
+    value = N / (ms_per_step * 1e-3)
+    v_s = ver_ms * 1e-3
+    if bound == "hbm":
+        achieved, peak, unit = alg_bytes / v_s / 1e9, HBM_PEAK_GBPS, "GB/s"
+    else:
+        achieved, peak, unit = (alg_flops / v_s / 1e12, MFMA_BF16_PEAK_TFLOPS,
+                                "TFLOP/s")
+    result = {
+        "metric": "tree-verify attention tree tokens/s + achieved HBM GB/s "
+                  "/ MFMA% of peak",
+        "value": value,
+        "unit": "tree tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name,
+            "num_seqs": S,
+            "prefix_lens": ([int(x) for x in wl.prefix_lens] if S <= 8
+                            else f"{S} x {int(wl.prefix_lens[0])}"),
+            "tree_nodes_per_seq": int(wl.max_nodes),
+            "q_heads": Hq, "kv_heads": wl.num_kv_heads, "head_dim": d,
+            "page_size": wl.page_size,
+            "splits": args.splits or "planned",
+            "input_copies_rotated": copies,
+        },
+        "roofline": {
+            "bound": bound,
+            "kernel": "tree_attn_verify (attn_fwd_kernel + attn_merge_kernel)",
+            "achieved": achieved,
+            "peak": peak,
+            "unit": unit,
+            "frac": achieved / peak,
+            "traffic": None,
+            "alg_bytes_per_launch": alg_bytes,
+            "alg_flops_per_launch": alg_flops,
+            "avg_launch_us": ver_ms * 1e3,
+        },
+        "attention_tflops": alg_flops / v_s / 1e12,
+        "kv_gbps": alg_bytes / v_s / 1e9,
+        "mfma_frac": alg_flops / v_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        "hbm_frac": alg_bytes / v_s / 1e9 / HBM_PEAK_GBPS,
+        "mask_build_us": mask_ms * 1e3,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] CPU baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,172 @@
+/*
+ * tree_attn.h - C ABI of libtreeattn.so: tree-causal verification attention
+ * for tree speculative decoding on AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  A draft tree of B_s nodes per sequence s, given in
+ * topological order (parent[i] < i), is verified by the target model in one
+ * forward pass.  In that pass every tree node attends to the sequence's
+ * whole input prefix and to its ancestors in the tree, never to its
+ * descendants or to sibling branches (JETFLOW, gist.science 2606.18394,
+ * section 2 "Arquitectura Central", bullet on the tree-causal attention
+ * mask; the branch factorization printed under it makes the ancestor set
+ * the root-to-node path).  The node itself is part of its own context, so a
+ * pure chain is ordinary causal attention.  The pages name the kernel that
+ * does this in their serving engine ("paged FlashAttention with tree-mask
+ * staging", section 3, item 3) but do not describe it; this library is its
+ * own design.  Topological order of the tree is also what DFlash-TfM
+ * (gist.science 2607.06763, method section 3) sorts into before verifying.
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers marked "dev" are device pointers on the current HIP device.
+ *    The caller owns every buffer.  The library never allocates or frees
+ *    device memory and keeps no pointer after a call returns.
+ *  - `stream` is a hipStream_t passed as void* (NULL = default stream).
+ *    Calls only enqueue work on it; none synchronises.
+ *  - Every status is returned synchronously.  When a call returns anything
+ *    but TREE_ATTN_OK, nothing was launched and nothing was written.
+ *  - All arrays are contiguous and row-major.
+ *  - bf16 is the 16-bit bfloat16 format (1 sign, 8 exponent, 7 mantissa).
+ *
+ * Indexing of a tree.  Sequence s owns nodes tree_offsets[s] ..
+ * tree_offsets[s+1]-1 (global node indices).  parents[] holds LOCAL
+ * indices: parents[tree_offsets[s] + i] is the local index of node i's
+ * parent in the same tree, or -1 for a root.  Several roots (a forest) are
+ * allowed; each root sees the prefix plus its own path.
+ *
+ * Where the tree's keys live.  Node j of sequence s has its key and value
+ * cached at logical position prefix_lens[s] + j of that sequence's paged
+ * cache, so the cache of sequence s holds prefix_lens[s] + B_s tokens.
+ */
+#ifndef TREE_ATTN_H
+#define TREE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum tree_attn_status {
+  TREE_ATTN_OK = 0,
+  TREE_ATTN_ERR_NULL = 1,        /* a required pointer is NULL              */
+  TREE_ATTN_ERR_SHAPE = 2,       /* inconsistent sizes                      */
+  TREE_ATTN_ERR_UNSUPPORTED = 3, /* valid, but not supported by this build  */
+  TREE_ATTN_ERR_WORKSPACE = 4,   /* workspace missing or too small          */
+  TREE_ATTN_ERR_HIP = 5          /* a HIP runtime call or launch failed     */
+};
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* tree_attn_status_string(int status);
+
+/* ABI version of this header (increases on any signature change). */
+int tree_attn_abi_version(void);
+
+/* Largest tree a sequence may hold in this build (nodes). */
+#define TREE_ATTN_MAX_NODES 1024
+
+/*
+ * tree_attn_build_mask - per-node ancestor-or-self bitmasks.
+ *
+ * Row i (global node index) of `masks` has bit (j % 64) of 64-bit word
+ * (j / 64) set iff local node j of the same tree lies on the root-to-node
+ * path of node i (node i included).  All other bits of the row, including
+ * every bit >= B_s, are zero.
+ *
+ *   parents       dev int32 [total_nodes]   local parent index, -1 = root
+ *   tree_offsets  dev int32 [num_seqs + 1]  tree_offsets[0] = 0,
+ *                                           tree_offsets[num_seqs] = total_nodes
+ *   num_seqs      >= 0
+ *   total_nodes   >= 0
+ *   max_nodes     host upper bound on every B_s, <= TREE_ATTN_MAX_NODES
+ *   mask_words    W, words per row; W * 64 >= max_nodes, 1 <= W <= 16
+ *   masks         dev uint64 [total_nodes][mask_words]   (output)
+ *   bad_node      dev int32 [num_seqs] (output): -1 when tree s is valid,
+ *                 else the global index of its first node whose parent is
+ *                 outside [-1, i), or of its first node past max_nodes.
+ *                 The rows of an invalid tree are unspecified.
+ *
+ * Host-side errors: ERR_NULL (a NULL pointer with num_seqs > 0), ERR_SHAPE
+ * (negative sizes, mask_words * 64 < max_nodes), ERR_UNSUPPORTED
+ * (max_nodes > TREE_ATTN_MAX_NODES or mask_words > 16), ERR_HIP.
+ */
+int tree_attn_build_mask(const int32_t* parents, const int32_t* tree_offsets,
+                         int32_t num_seqs, int32_t total_nodes,
+                         int32_t max_nodes, int32_t mask_words,
+                         uint64_t* masks, int32_t* bad_node, void* stream);
+
+/*
+ * tree_attn_workspace_size - bytes of device workspace tree_attn_verify
+ * needs for these sizes (0 when the planned launch needs none).
+ * Arguments as for tree_attn_verify.  num_splits: 0 lets the library plan
+ * the split of the key range; n > 0 forces n splits (clamped to what the
+ * key range allows).  Returns 0 for invalid sizes as well.
+ */
+size_t tree_attn_workspace_size(int32_t num_seqs, int32_t total_nodes,
+                                int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t max_prefix_len,
+                                int32_t max_nodes, int32_t num_splits);
+
+/*
+ * tree_attn_verify - tree-causal verification attention over a paged
+ * bf16 KV cache, with the softmax log-sum-exp.
+ *
+ * For node i of sequence s (global row n = tree_offsets[s] + i) and query
+ * head h, with g = h / (num_q_heads / num_kv_heads) (contiguous GQA
+ * groups), the allowed keys are the logical cache positions
+ *     { 0 .. prefix_lens[s]-1 }  and  { prefix_lens[s] + j : bit j of masks[n] }
+ * and, with x_t = scale * <q[n,h,:], K_s[t,g,:]> over the allowed t,
+ *     out[n,h,:] = sum_t exp(x_t) V_s[t,g,:] / sum_t exp(x_t)   (bf16, RNE)
+ *     lse[n,h]   = ln sum_t exp(x_t)                             (fp32)
+ * K_s[t] is read from physical page page_table[s][t / page_size], slot
+ * t % page_size.
+ *
+ *   q             dev bf16 [total_nodes, num_q_heads, head_dim]
+ *   k_cache       dev bf16 [num_pages, page_size, num_kv_heads, head_dim]
+ *   v_cache       dev bf16 [num_pages, page_size, num_kv_heads, head_dim]
+ *   page_table    dev int32 [num_seqs, max_pages_per_seq]: logical page ->
+ *                 physical page; must cover prefix_lens[s] + B_s tokens
+ *   page_size     power of two, 1 .. 4096
+ *   prefix_lens   dev int32 [num_seqs], each 0 .. max_prefix_len
+ *   tree_offsets  dev int32 [num_seqs + 1] (as for tree_attn_build_mask)
+ *   masks         dev uint64 [total_nodes][mask_words], as written by
+ *                 tree_attn_build_mask (any ancestor relation is accepted)
+ *   max_prefix_len, max_nodes   host upper bounds of the device values;
+ *                 they size the launch, so no device-to-host copy is made
+ *   head_dim      128 in this build
+ *   scale         softmax scale (1/sqrt(head_dim) for standard attention)
+ *   num_splits    0 = planned by the library; n > 0 forces n splits
+ *   out           dev bf16 [total_nodes, num_q_heads, head_dim]  (output)
+ *   lse           dev fp32 [total_nodes, num_q_heads], natural log (output)
+ *   workspace     dev scratch of tree_attn_workspace_size(...) bytes, 256-B
+ *                 aligned; may be NULL when that size is 0
+ *
+ * Device values outside the stated bounds (a prefix longer than
+ * max_prefix_len, a tree larger than max_nodes, page ids outside
+ * [0, num_pages)) give unspecified output for the rows concerned, but no
+ * access outside the buffers described above.
+ *
+ * Host-side errors: ERR_NULL, ERR_SHAPE (num_q_heads % num_kv_heads != 0,
+ * mask_words * 64 < max_nodes, page_size not a power of two,
+ * max_pages_per_seq * page_size < max_prefix_len + max_nodes, negative
+ * sizes), ERR_UNSUPPORTED (head_dim != 128, max_nodes >
+ * TREE_ATTN_MAX_NODES), ERR_WORKSPACE, ERR_HIP.
+ */
+int tree_attn_verify(const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* page_table, int32_t max_pages_per_seq,
+                     int32_t num_pages, int32_t page_size,
+                     const int32_t* prefix_lens, const int32_t* tree_offsets,
+                     const uint64_t* masks, int32_t mask_words,
+                     int32_t num_seqs, int32_t total_nodes,
+                     int32_t max_prefix_len, int32_t max_nodes,
+                     int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_dim, float scale, int32_t num_splits,
+                     void* out, float* lse, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TREE_ATTN_H */

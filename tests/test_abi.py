@@ -1,0 +1,102 @@
+"""The C-ABI library on the CPU: it loads, exports every function the header
+declares, and rejects bad arguments before any launch (no GPU needed: each
+call below fails its host-side checks before touching HIP)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tree_attn.h")
+
+api = pytest.importorskip("tree_masked_attention_amd.api")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tree_attn_[a-z_]+)\s*\(", text)))
+
+
+def test_header_functions_exported():
+    lib = ctypes.CDLL(api.LIB_PATH)
+    names = declared_functions()
+    assert set(names) == set(api.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    assert api.status_string(0) == "ok"
+    for c in range(1, 6):
+        assert api.status_string(c) not in ("ok", "unknown status")
+    assert api.status_string(99) == "unknown status"
+    assert api.abi_version() >= 1
+
+
+def test_build_mask_rejects_bad_sizes():
+    f = api.build_mask_raw
+    assert f(1, 1, -1, 4, 4, 1, 1, 1, None) == api.ERR_SHAPE
+    assert f(1, 1, 1, 4, 4, 0, 1, 1, None) == api.ERR_SHAPE
+    assert f(1, 1, 1, 200, 200, 2, 1, 1, None) == api.ERR_SHAPE   # 128 < 200
+    assert f(1, 1, 1, 2000, 2000, 32, 1, 1, None) == api.ERR_UNSUPPORTED
+    assert f(None, 1, 1, 4, 4, 1, 1, 1, None) == api.ERR_NULL
+    assert f(1, None, 1, 4, 4, 1, 1, 1, None) == api.ERR_NULL
+    assert f(1, 1, 1, 4, 4, 1, None, 1, None) == api.ERR_NULL
+    assert f(1, 1, 1, 4, 4, 1, 1, None, None) == api.ERR_NULL
+    assert f(None, None, 0, 0, 0, 1, None, None, None) == api.OK  # no-op
+
+
+def _verify(**over):
+    args = dict(q=1, k=1, v=1, table=1, max_pps=20, num_pages=20,
+                page_size=16, prefix=1, offs=1, masks=1, W=1, S=1, N=16,
+                max_p=256, max_b=16, Hq=8, Hkv=2, d=128, scale=0.088,
+                splits=0, out=1, lse=1, ws=None, ws_bytes=0)
+    args.update(over)
+    a = args
+    return int(api._lib.tree_attn_verify(
+        a["q"], a["k"], a["v"], a["table"], a["max_pps"], a["num_pages"],
+        a["page_size"], a["prefix"], a["offs"], a["masks"], a["W"], a["S"],
+        a["N"], a["max_p"], a["max_b"], a["Hq"], a["Hkv"], a["d"],
+        a["scale"], a["splits"], a["out"], a["lse"], a["ws"], a["ws_bytes"],
+        None))
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(Hkv=3), api.ERR_SHAPE),
+    (dict(d=64), api.ERR_UNSUPPORTED),
+    (dict(max_b=2048, W=32), api.ERR_UNSUPPORTED),
+    (dict(max_b=65, W=1), api.ERR_SHAPE),
+    (dict(page_size=12), api.ERR_SHAPE),
+    (dict(page_size=0), api.ERR_SHAPE),
+    (dict(max_pps=10), api.ERR_SHAPE),          # 160 < 256 + 16 tokens
+    (dict(S=-1), api.ERR_SHAPE),
+    (dict(splits=-2), api.ERR_SHAPE),
+    (dict(scale=float("nan")), api.ERR_SHAPE),
+    (dict(q=None), api.ERR_NULL),
+    (dict(k=None), api.ERR_NULL),
+    (dict(table=None), api.ERR_NULL),
+    (dict(masks=None), api.ERR_NULL),
+    (dict(out=None), api.ERR_NULL),
+    (dict(lse=None), api.ERR_NULL),
+    (dict(splits=4), api.ERR_WORKSPACE),        # forced split needs scratch
+    (dict(splits=4, ws=256, ws_bytes=16), api.ERR_WORKSPACE),
+])
+def test_verify_rejects(over, code):
+    assert _verify(**over) == code
+
+
+def test_verify_empty_is_noop():
+    assert _verify(S=0, N=0, q=None, k=None, v=None) == api.OK
+    assert _verify(N=0) == api.OK
+
+
+def test_workspace_size_rules():
+    # one split needs no workspace; forced splits need partial rows
+    ws1 = api.workspace_size(1, 16, 8, 2, 128, 256, 16, 1)
+    ws4 = api.workspace_size(1, 16, 8, 2, 128, 1024, 16, 4)
+    assert ws1 == 0
+    assert ws4 >= 4 * 16 * 8 * (128 + 2) * 4
+    assert api.workspace_size(1, 16, 8, 3, 128, 256, 16, 0) == 0  # invalid

@@ -1,0 +1,195 @@
+"""HIP path vs the CPU oracle, through the C ABI (needs a gfx950 GPU).
+
+Bar: ancestor bitmasks bit-exact (padding words included); attention
+output max |out - oracle| <= 2e-2 and lse max relative error <= 1e-3
+(relative to max(|lse|, 1)).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import (assert_parity, device_inputs, errors, run_gpu, say)
+from tree_masked_attention_amd.workloads import (STANDARD_ORDER,
+                                                 make_workload,
+                                                 standard_workload)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    import tree_masked_attention_amd.api  # noqa: F401  (fails loudly if unbuilt)
+
+
+def _case(name, seed, **kw):
+    kw.setdefault("num_q_heads", 8)
+    kw.setdefault("num_kv_heads", 2)
+    return make_workload(seed, name=name, **kw)
+
+
+SMALL_CASES = {
+    "ragged-multi": lambda: _case("ragged-multi", 101,
+                                  prefix_lens=[0, 77, 300, 1],
+                                  tree_sizes=[1, 37, 130, 64],
+                                  tree_rules="pchain", p_chain=0.5),
+    "mha": lambda: _case("mha", 102, prefix_lens=[100], tree_sizes=[50],
+                         num_q_heads=4, num_kv_heads=4),
+    "gqa8": lambda: _case("gqa8", 103, prefix_lens=[513], tree_sizes=[16],
+                          num_q_heads=32, num_kv_heads=4),
+    "empty-tree-in-batch": lambda: _case("empty", 104, prefix_lens=[20, 40, 0],
+                                         tree_sizes=[5, 0, 9]),
+    "page1": lambda: _case("page1", 105, prefix_lens=[70, 3],
+                           tree_sizes=[12, 7], page_size=1),
+    "page64": lambda: _case("page64", 106, prefix_lens=[70, 200],
+                            tree_sizes=[12, 70], page_size=64),
+    "max-tree-1024": lambda: _case("b1024", 107, prefix_lens=[50],
+                                   tree_sizes=[1024], num_q_heads=2,
+                                   num_kv_heads=1, p_chain=0.7),
+    "chain": lambda: _case("chain", 108, prefix_lens=[100], tree_sizes=[200],
+                           tree_rules="chain"),
+    "star": lambda: _case("star", 109, prefix_lens=[33], tree_sizes=[300],
+                          tree_rules="star"),
+    "no-prefix": lambda: _case("no-prefix", 110, prefix_lens=[0, 0],
+                               tree_sizes=[64, 65]),
+    "big-key-range": lambda: _case("keyscale", 111, prefix_lens=[900],
+                                   tree_sizes=[40],
+                                   key_factor_range=(0.25, 4.0)),
+    "long-prefix-tiny-tree": lambda: _case("long-tail", 112,
+                                           prefix_lens=[5000, 1234],
+                                           tree_sizes=[3, 1]),
+}
+
+
+def _forest(wl):
+    """Turn every 7th node into an extra root."""
+    par = wl.parents.copy()
+    for s in range(wl.num_seqs):
+        a, b = wl.tree_offsets[s], wl.tree_offsets[s + 1]
+        for i in range(7, b - a, 7):
+            par[a + i] = -1
+    wl.parents = par
+    return wl
+
+
+SMALL_CASES["forest"] = lambda: _forest(_case("forest", 113,
+                                              prefix_lens=[10, 60],
+                                              tree_sizes=[50, 90]))
+
+
+@pytest.mark.parametrize("name", sorted(SMALL_CASES))
+def test_small_case_parity(name):
+    wl = SMALL_CASES[name]()
+    say(f"[gpu] small case {name}: S={wl.num_seqs} P={list(wl.prefix_lens)} "
+        f"B={list(wl.tree_sizes)} Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} "
+        f"page={wl.page_size}")
+    got = run_gpu(wl)
+    assert np.array_equal(got["masks"], oracle.workload_masks(wl))
+    assert (got["bad"] == -1).all()
+    ref_out, ref_lse = oracle.workload_attention(wl)
+    assert_parity(got, ref_out, ref_lse, name)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 5, 64])
+def test_forced_splits_parity(splits):
+    wl = _case("splits", 120, prefix_lens=[1000, 64, 2500],
+               tree_sizes=[33, 100, 7], num_q_heads=16, num_kv_heads=4)
+    say(f"[gpu] forced splits={splits}")
+    got = run_gpu(wl, num_splits=splits)
+    ref_out, ref_lse = oracle.workload_attention(wl)
+    assert_parity(got, ref_out, ref_lse, f"splits={splits}")
+
+
+def test_split_count_changes_only_rounding():
+    wl = _case("splitinv", 121, prefix_lens=[3000], tree_sizes=[64],
+               num_q_heads=16, num_kv_heads=4)
+    say("[gpu] split invariance")
+    a = run_gpu(wl, num_splits=1)
+    for n in (3, 11):
+        b = run_gpu(wl, num_splits=n)
+        assert np.abs(a["out"] - b["out"]).max() <= 8e-3
+        assert np.abs(a["lse"] - b["lse"]).max() <= 1e-5 * 20
+
+
+def test_page_permutation_bit_identical():
+    wl = _case("perm", 122, prefix_lens=[700, 90], tree_sizes=[48, 20],
+               shuffle_pages=False)
+    say("[gpu] page permutation invariance")
+    a = run_gpu(wl)
+    perm = np.random.default_rng(5).permutation(wl.num_pages)
+    inv = np.argsort(perm)
+    wl.k_cache = np.ascontiguousarray(wl.k_cache[perm])
+    wl.v_cache = np.ascontiguousarray(wl.v_cache[perm])
+    wl.page_table = np.where(wl.page_table >= 0,
+                             inv[np.maximum(wl.page_table, 0)],
+                             -1).astype(np.int32)
+    b = run_gpu(wl)
+    assert np.array_equal(a["out_bits"], b["out_bits"])
+    assert np.array_equal(a["lse"], b["lse"])
+
+
+def test_deterministic():
+    wl = standard_workload("qwen3-8b-b256-p4k")
+    say("[gpu] determinism")
+    dev = device_inputs(wl)
+    a = run_gpu(wl, dev=dev)
+    b = run_gpu(wl, dev=dev)
+    assert np.array_equal(a["out_bits"], b["out_bits"])
+    assert np.array_equal(a["lse"], b["lse"])
+    assert np.array_equal(a["masks"], b["masks"])
+
+
+def test_invalid_parents_reported():
+    import tree_masked_attention_amd.api as api
+    wl = _case("bad", 130, prefix_lens=[4, 4, 4], tree_sizes=[6, 5, 4])
+    par = wl.parents.copy()
+    par[0 + 3] = 3          # self loop in tree 0 (global node 3)
+    par[6 + 2] = -2         # below -1 in tree 1 (global node 8)
+    wl.parents = par
+    say("[gpu] invalid parents")
+    dev = device_inputs(wl)
+    _, bad = api.build_mask(dev["parents"], dev["tree_offsets"], 6, 1)
+    torch.cuda.synchronize()
+    assert bad.cpu().tolist() == [3, 8, -1]
+    # a tree larger than max_nodes is flagged at its first excess node
+    wl2 = _case("big", 131, prefix_lens=[4], tree_sizes=[100])
+    dev2 = device_inputs(wl2)
+    masks, bad2 = api.build_mask(dev2["parents"], dev2["tree_offsets"], 64, 1)
+    torch.cuda.synchronize()
+    assert bad2.cpu().tolist() == [64]
+    ref = oracle.ancestor_masks(wl2.parents[:64], np.array([0, 64]), 1)
+    got = masks.cpu().numpy().view(np.uint64)
+    assert np.array_equal(got[:64], ref)
+    assert (got[64:] == 0).all()
+
+
+# --------------------------------------------------------------------------
+# the five standard workloads at full size, planned launch (as benchmarked)
+# --------------------------------------------------------------------------
+
+SAMPLED = {"long-32k-4x-b256": dict(pairs=[(0, 0), (1, 3), (2, 5), (3, 7)])}
+
+
+@pytest.mark.parametrize("name", STANDARD_ORDER)
+def test_standard_workload_parity(name):
+    say(f"[gpu] standard workload {name}: drawing inputs")
+    wl = standard_workload(name)
+    got = run_gpu(wl)
+    assert np.array_equal(got["masks"], oracle.workload_masks(wl))
+    assert np.isfinite(got["out"]).all() and np.isfinite(got["lse"]).all()
+    if name in SAMPLED:
+        for s, g in SAMPLED[name]["pairs"]:
+            ro, rl = oracle.workload_attention(wl, seq_ids=[s],
+                                               kv_head_ids=[g])
+            assert_parity(got, ro, rl, f"{name} seq {s} kv head {g}")
+        # every row: planned split vs a single split agree
+        one = run_gpu(wl, num_splits=1)
+        d_out = np.abs(one["out"] - got["out"]).max()
+        d_lse = np.abs(one["lse"] - got["lse"]).max()
+        say(f"  planned vs 1 split: max|dout|={d_out:.3e} max|dlse|={d_lse:.3e}")
+        assert d_out <= 1e-2 and d_lse <= 1e-3
+    else:
+        ro, rl = oracle.workload_attention(wl)
+        assert_parity(got, ro, rl, name)

@@ -1,0 +1,191 @@
+"""Python binding of libtreeattn.so (argument marshalling only).
+
+Every computation happens in the HIP library; torch supplies device
+memory and the current stream.  The library must be built
+(``python -m tree_masked_attention_amd._build``); without it, importing
+this module raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+from ._build import LIB_PATH
+
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(6)
+MAX_NODES = 1024
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with "
+        "`python -m tree_masked_attention_amd._build` (hipcc, gfx950)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_p = ctypes.c_void_p
+_i = ctypes.c_int32
+_lib.tree_attn_status_string.restype = ctypes.c_char_p
+_lib.tree_attn_status_string.argtypes = [ctypes.c_int]
+_lib.tree_attn_abi_version.restype = ctypes.c_int
+_lib.tree_attn_abi_version.argtypes = []
+_lib.tree_attn_build_mask.restype = ctypes.c_int
+_lib.tree_attn_build_mask.argtypes = [_p, _p, _i, _i, _i, _i, _p, _p, _p]
+_lib.tree_attn_workspace_size.restype = ctypes.c_size_t
+_lib.tree_attn_workspace_size.argtypes = [_i] * 8
+_lib.tree_attn_verify.restype = ctypes.c_int
+_lib.tree_attn_verify.argtypes = (
+    [_p, _p, _p, _p, _i, _i, _i, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i,
+     ctypes.c_float, _i, _p, _p, _p, ctypes.c_size_t, _p])
+
+EXPORTED = ("tree_attn_status_string", "tree_attn_abi_version",
+            "tree_attn_build_mask", "tree_attn_workspace_size",
+            "tree_attn_verify")
+
+
+class TreeAttnError(RuntimeError):
+    pass
+
+
+def status_string(code: int) -> str:
+    return _lib.tree_attn_status_string(int(code)).decode()
+
+
+def abi_version() -> int:
+    return int(_lib.tree_attn_abi_version())
+
+
+def _raise(code: int, what: str) -> None:
+    if code == OK:
+        return
+    msg = f"{what}: {status_string(code)} (status {code})"
+    if code in (ERR_NULL, ERR_SHAPE, ERR_WORKSPACE):
+        raise ValueError(msg)
+    if code == ERR_UNSUPPORTED:
+        raise NotImplementedError(msg)
+    raise TreeAttnError(msg)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _dev(t: torch.Tensor, dtype, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def mask_words_for(max_nodes: int) -> int:
+    return max(1, (int(max_nodes) + 63) // 64)
+
+
+def build_mask_raw(parents, tree_offsets, num_seqs, total_nodes, max_nodes,
+                   mask_words, masks, bad_node, stream=None) -> int:
+    """Direct call of tree_attn_build_mask with raw device pointers."""
+    return int(_lib.tree_attn_build_mask(
+        parents, tree_offsets, num_seqs, total_nodes, max_nodes, mask_words,
+        masks, bad_node, stream))
+
+
+def build_mask(parents: torch.Tensor, tree_offsets: torch.Tensor,
+               max_nodes: int, mask_words: Optional[int] = None,
+               masks: Optional[torch.Tensor] = None,
+               bad_node: Optional[torch.Tensor] = None,
+               stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Ancestor-or-self bitmasks of the draft trees.
+
+    parents int32 [N] (local indices, -1 = root), tree_offsets int32 [S+1].
+    Returns (masks int64 [N, W] holding the uint64 words, bad_node int32
+    [S]: -1 per valid tree, else the first invalid global node).
+    """
+    _dev(parents, torch.int32, "parents")
+    _dev(tree_offsets, torch.int32, "tree_offsets")
+    S = tree_offsets.numel() - 1
+    N = parents.numel()
+    W = mask_words_for(max_nodes) if mask_words is None else int(mask_words)
+    if masks is None:
+        masks = torch.empty((N, W), dtype=torch.int64, device=parents.device)
+    if bad_node is None:
+        bad_node = torch.empty((max(S, 1),), dtype=torch.int32,
+                               device=parents.device)
+    _raise(build_mask_raw(_ptr(parents), _ptr(tree_offsets), S, N,
+                          int(max_nodes), W, _ptr(masks), _ptr(bad_node),
+                          _stream(stream)), "tree_attn_build_mask")
+    return masks, bad_node
+
+
+def workspace_size(num_seqs: int, total_nodes: int, num_q_heads: int,
+                   num_kv_heads: int, head_dim: int, max_prefix_len: int,
+                   max_nodes: int, num_splits: int = 0) -> int:
+    return int(_lib.tree_attn_workspace_size(
+        num_seqs, total_nodes, num_q_heads, num_kv_heads, head_dim,
+        max_prefix_len, max_nodes, num_splits))
+
+
+def verify(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+           page_table: torch.Tensor, prefix_lens: torch.Tensor,
+           tree_offsets: torch.Tensor, masks: torch.Tensor,
+           max_prefix_len: int, max_nodes: int, scale: float,
+           num_splits: int = 0, out: Optional[torch.Tensor] = None,
+           lse: Optional[torch.Tensor] = None,
+           workspace: Optional[torch.Tensor] = None,
+           stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Tree-causal verification attention.
+
+    q bf16 [N, Hq, d]; k_cache / v_cache bf16 [num_pages, page_size, Hkv, d];
+    page_table int32 [S, max_pages_per_seq]; prefix_lens int32 [S];
+    tree_offsets int32 [S+1]; masks int64 [N, W] (uint64 words from
+    build_mask).  Returns (out bf16 [N, Hq, d], lse fp32 [N, Hq]).
+    """
+    for t, dt, n in ((q, torch.bfloat16, "q"), (k_cache, torch.bfloat16, "k_cache"),
+                     (v_cache, torch.bfloat16, "v_cache"),
+                     (page_table, torch.int32, "page_table"),
+                     (prefix_lens, torch.int32, "prefix_lens"),
+                     (tree_offsets, torch.int32, "tree_offsets"),
+                     (masks, torch.int64, "masks")):
+        _dev(t, dt, n)
+    if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("q must be [N, Hq, d] and k/v caches "
+                         "[num_pages, page_size, Hkv, d]")
+    N, Hq, d = q.shape
+    num_pages, page_size, Hkv, dk = k_cache.shape
+    if dk != d:
+        raise ValueError("head_dim of q and the caches differ")
+    S = prefix_lens.numel()
+    if tree_offsets.numel() != S + 1 or page_table.dim() != 2 or \
+            page_table.shape[0] != S:
+        raise ValueError("page_table / tree_offsets do not match prefix_lens")
+    if masks.dim() != 2 or masks.shape[0] != N:
+        raise ValueError("masks must be [N, W]")
+    W = masks.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((N, Hq), dtype=torch.float32, device=q.device)
+    ws_bytes = workspace_size(S, N, Hq, Hkv, d, max_prefix_len, max_nodes,
+                              num_splits)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty((ws_bytes,), dtype=torch.uint8,
+                                device=q.device)
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    code = _lib.tree_attn_verify(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+        page_table.shape[1], num_pages, page_size, _ptr(prefix_lens),
+        _ptr(tree_offsets), _ptr(masks), W, S, N, int(max_prefix_len),
+        int(max_nodes), Hq, Hkv, d, float(scale), int(num_splits), _ptr(out),
+        _ptr(lse), _ptr(workspace), ws_len, _stream(stream))
+    _raise(code, "tree_attn_verify")
+    return out, lse

@@ -1,0 +1,288 @@
+// C ABI of libtreeattn.so: argument checks, launch planning, launches.
+//
+// Every check that can fail runs before the first HIP call, so an error
+// status means nothing was launched.  The library owns no device memory.
+#include "tree_attn.h"
+
+#include <atomic>
+#include <cmath>
+
+#include "attn_fwd.hpp"
+#include "attn_merge.hpp"
+#include "common.hpp"
+#include "mask_build.hpp"
+
+using namespace tree_attn;
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+constexpr int kMaxDevices = 64;
+constexpr int kMaxSplits = 64;
+constexpr int kMinKeysPerSplit = 256;
+
+std::atomic<int> g_cu_count[kMaxDevices];
+std::atomic<int> g_mask_lds[kMaxDevices];  // dynamic LDS limit already set
+
+// Compute units of the current device (queried once per device).
+int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    return 256;
+  }
+  int v = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
+          hipSuccess ||
+      n <= 0) {
+    n = 256;
+  }
+  g_cu_count[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int ilog2(int x) {
+  int r = 0;
+  while ((1 << r) < x) ++r;
+  return r;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Plan {
+  int mblocks = 0;
+  int splits = 1;
+  int chunk = 0;
+  size_t part_o_bytes = 0;
+  size_t part_ml_off = 0;
+  size_t ws_bytes = 0;
+};
+
+// Split planning from host-side bounds only (no device-to-host copy).
+// Rows of a (sequence, kv head) pair are covered by `mblocks` workgroups;
+// the key range [0, max_prefix_len + max_nodes) is cut into `splits`
+// chunks of `chunk` keys (a multiple of the 64-key tile) so that the grid
+// offers about two workgroups per compute unit.
+Plan make_plan(int S, int N, int Hq, int Hkv, int max_prefix_len,
+               int max_nodes, int req_splits, int cus) {
+  Plan pl;
+  const int G = Hq / Hkv;
+  const int rows = G * max_nodes;
+  pl.mblocks = std::max(1, (rows + kRowsPerWG - 1) / kRowsPerWG);
+  const long long T = (long long)max_prefix_len + max_nodes;
+  const long long units = (long long)S * Hkv * pl.mblocks;
+  int splits;
+  if (req_splits > 0) {
+    splits = req_splits;
+  } else {
+    const long long want = (2LL * cus + units - 1) / std::max(1LL, units);
+    const long long by_len = std::max(1LL, T / kMinKeysPerSplit);
+    splits = (int)std::min<long long>(want, by_len);
+  }
+  splits = std::max(1, std::min(splits, kMaxSplits));
+  long long chunk = (T + splits - 1) / splits;
+  chunk = std::max<long long>(kKeyTile, (chunk + kKeyTile - 1) / kKeyTile * kKeyTile);
+  splits = (int)std::max<long long>(1, (T + chunk - 1) / chunk);
+  pl.splits = splits;
+  pl.chunk = (int)chunk;
+  if (splits > 1) {
+    const size_t rows_all = (size_t)N * Hq * splits;
+    pl.part_o_bytes = align_up(rows_all * kHeadDim * sizeof(float), 256);
+    pl.part_ml_off = pl.part_o_bytes;
+    pl.ws_bytes = pl.part_ml_off + align_up(rows_all * 2 * sizeof(float), 256);
+  }
+  return pl;
+}
+
+int check_sizes(int S, int N, int Hq, int Hkv, int head_dim,
+                int max_prefix_len, int max_nodes) {
+  if (S < 0 || N < 0 || Hq <= 0 || Hkv <= 0 || head_dim <= 0 ||
+      max_prefix_len < 0 || max_nodes < 0) {
+    return TREE_ATTN_ERR_SHAPE;
+  }
+  if (Hq % Hkv != 0) return TREE_ATTN_ERR_SHAPE;
+  if (head_dim != kHeadDim) return TREE_ATTN_ERR_UNSUPPORTED;
+  if (max_nodes > TREE_ATTN_MAX_NODES) return TREE_ATTN_ERR_UNSUPPORTED;
+  if ((long long)max_prefix_len + max_nodes > (1LL << 30)) {
+    return TREE_ATTN_ERR_UNSUPPORTED;
+  }
+  return TREE_ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tree_attn_status_string(int status) {
+  switch (status) {
+    case TREE_ATTN_OK: return "ok";
+    case TREE_ATTN_ERR_NULL: return "null pointer argument";
+    case TREE_ATTN_ERR_SHAPE: return "inconsistent sizes";
+    case TREE_ATTN_ERR_UNSUPPORTED: return "unsupported size";
+    case TREE_ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case TREE_ATTN_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int tree_attn_abi_version(void) { return kAbiVersion; }
+
+int tree_attn_build_mask(const int32_t* parents, const int32_t* tree_offsets,
+                         int32_t num_seqs, int32_t total_nodes,
+                         int32_t max_nodes, int32_t mask_words,
+                         uint64_t* masks, int32_t* bad_node, void* stream) {
+  if (num_seqs < 0 || total_nodes < 0 || max_nodes < 0 || mask_words < 1) {
+    return TREE_ATTN_ERR_SHAPE;
+  }
+  if (mask_words > kMaskMaxWords || max_nodes > TREE_ATTN_MAX_NODES) {
+    return TREE_ATTN_ERR_UNSUPPORTED;
+  }
+  if ((long long)mask_words * 64 < max_nodes) return TREE_ATTN_ERR_SHAPE;
+  if (num_seqs == 0) return TREE_ATTN_OK;
+  if (!tree_offsets || !bad_node) return TREE_ATTN_ERR_NULL;
+  if (total_nodes > 0 && (!parents || !masks)) return TREE_ATTN_ERR_NULL;
+
+  const int cap = std::max(1, max_nodes);
+  const size_t lds = (size_t)cap * mask_words * sizeof(uint64_t) +
+                     (size_t)cap * sizeof(int);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return TREE_ATTN_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices ||
+      g_mask_lds[dev].load(std::memory_order_relaxed) < (int)lds) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&build_mask_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)lds) != hipSuccess) {
+      return TREE_ATTN_ERR_HIP;
+    }
+    if (dev >= 0 && dev < kMaxDevices) {
+      g_mask_lds[dev].store((int)lds, std::memory_order_relaxed);
+    }
+  }
+  hipLaunchKernelGGL(build_mask_kernel, dim3(num_seqs), dim3(kMaskThreads),
+                     lds, st, parents, tree_offsets, num_seqs, total_nodes,
+                     cap, (int)mask_words, masks, bad_node);
+  return hipGetLastError() == hipSuccess ? TREE_ATTN_OK : TREE_ATTN_ERR_HIP;
+}
+
+size_t tree_attn_workspace_size(int32_t num_seqs, int32_t total_nodes,
+                                int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t max_prefix_len,
+                                int32_t max_nodes, int32_t num_splits) {
+  if (check_sizes(num_seqs, total_nodes, num_q_heads, num_kv_heads, head_dim,
+                  max_prefix_len, max_nodes) != TREE_ATTN_OK ||
+      num_splits < 0) {
+    return 0;
+  }
+  if (num_seqs == 0 || total_nodes == 0) return 0;
+  return make_plan(num_seqs, total_nodes, num_q_heads, num_kv_heads,
+                   max_prefix_len, max_nodes, num_splits, cu_count())
+      .ws_bytes;
+}
+
+int tree_attn_verify(const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* page_table, int32_t max_pages_per_seq,
+                     int32_t num_pages, int32_t page_size,
+                     const int32_t* prefix_lens, const int32_t* tree_offsets,
+                     const uint64_t* masks, int32_t mask_words,
+                     int32_t num_seqs, int32_t total_nodes,
+                     int32_t max_prefix_len, int32_t max_nodes,
+                     int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_dim, float scale, int32_t num_splits,
+                     void* out, float* lse, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  int st = check_sizes(num_seqs, total_nodes, num_q_heads, num_kv_heads,
+                       head_dim, max_prefix_len, max_nodes);
+  if (st != TREE_ATTN_OK) return st;
+  if (num_splits < 0 || mask_words < 1 || max_pages_per_seq < 0 ||
+      num_pages < 0) {
+    return TREE_ATTN_ERR_SHAPE;
+  }
+  if (!is_pow2(page_size) || page_size > 4096) return TREE_ATTN_ERR_SHAPE;
+  if ((long long)mask_words * 64 < max_nodes) return TREE_ATTN_ERR_SHAPE;
+  if ((long long)max_pages_per_seq * page_size <
+      (long long)max_prefix_len + max_nodes) {
+    return TREE_ATTN_ERR_SHAPE;
+  }
+  if (!std::isfinite(scale)) return TREE_ATTN_ERR_SHAPE;
+  if (num_seqs == 0 || total_nodes == 0) return TREE_ATTN_OK;
+  if (num_pages < 1 || max_pages_per_seq < 1) return TREE_ATTN_ERR_SHAPE;
+  if (!q || !k_cache || !v_cache || !page_table || !prefix_lens ||
+      !tree_offsets || !masks || !out || !lse) {
+    return TREE_ATTN_ERR_NULL;
+  }
+
+  const Plan pl = make_plan(num_seqs, total_nodes, num_q_heads, num_kv_heads,
+                            max_prefix_len, max_nodes, num_splits, cu_count());
+  if (pl.ws_bytes > 0) {
+    if (!workspace) return TREE_ATTN_ERR_WORKSPACE;
+    if (workspace_bytes < pl.ws_bytes) return TREE_ATTN_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) {
+      return TREE_ATTN_ERR_WORKSPACE;
+    }
+  }
+
+  FwdParams fp;
+  fp.q = static_cast<const __bf16*>(q);
+  fp.k = static_cast<const __bf16*>(k_cache);
+  fp.v = static_cast<const __bf16*>(v_cache);
+  fp.page_table = page_table;
+  fp.prefix_lens = prefix_lens;
+  fp.tree_offsets = tree_offsets;
+  fp.masks = masks;
+  fp.out = static_cast<__bf16*>(out);
+  fp.lse = lse;
+  fp.part_o = static_cast<float*>(workspace);
+  fp.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                        pl.part_ml_off);
+  fp.max_pps = max_pages_per_seq;
+  fp.num_pages = num_pages;
+  fp.log2_page = ilog2(page_size);
+  fp.W = mask_words;
+  fp.max_tokens = (int)std::min<long long>((long long)max_pages_per_seq * page_size,
+                                           1LL << 30);
+  fp.S = num_seqs;
+  fp.N = total_nodes;
+  fp.Hq = num_q_heads;
+  fp.Hkv = num_kv_heads;
+  fp.G = num_q_heads / num_kv_heads;
+  fp.mblocks = pl.mblocks;
+  fp.splits = pl.splits;
+  fp.chunk = pl.chunk;
+  fp.scale_log2 = scale * kLog2e;
+
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const long long grid =
+      (long long)num_seqs * num_kv_heads * pl.mblocks * pl.splits;
+  if (grid > 0x7fffffffLL) return TREE_ATTN_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)grid),
+                     dim3(kFwdWaves * 64), 0, hs, fp);
+  if (hipGetLastError() != hipSuccess) return TREE_ATTN_ERR_HIP;
+
+  if (pl.splits > 1) {
+    MergeParams mp;
+    mp.prefix_lens = prefix_lens;
+    mp.tree_offsets = tree_offsets;
+    mp.part_o = fp.part_o;
+    mp.part_ml = fp.part_ml;
+    mp.out = fp.out;
+    mp.lse = lse;
+    mp.S = num_seqs;
+    mp.N = total_nodes;
+    mp.Hq = num_q_heads;
+    mp.splits = pl.splits;
+    mp.chunk = pl.chunk;
+    mp.max_tokens = fp.max_tokens;
+    const long long rows = (long long)total_nodes * num_q_heads;
+    const unsigned mgrid = (unsigned)((rows + kMergeWaves - 1) / kMergeWaves);
+    hipLaunchKernelGGL(attn_merge_kernel, dim3(mgrid), dim3(kMergeWaves * 64),
+                       0, hs, mp);
+    if (hipGetLastError() != hipSuccess) return TREE_ATTN_ERR_HIP;
+  }
+  return TREE_ATTN_OK;
+}
+
+}  // extern "C"
