@@ -148,8 +148,7 @@ size_t tree_attn_workspace_size(int32_t num_seqs, int32_t total_nodes,
  * access outside the buffers described above.
  *
  * Host-side errors: ERR_NULL, ERR_SHAPE (num_q_heads % num_kv_heads != 0,
- * mask_words * 64 < max_nodes, page_size not a power of two,
- * max_pages_per_seq * page_size < max_prefix_len + max_nodes, negative
+ * mask_words * 64 < max_nodes, page_size not a power of two, negative
  * sizes), ERR_UNSUPPORTED (head_dim != 128, max_nodes >
  * TREE_ATTN_MAX_NODES), ERR_WORKSPACE, ERR_HIP.
  */

@@ -71,7 +71,7 @@ def _verify(**over):
     (dict(max_b=65, W=1), api.ERR_SHAPE),
     (dict(page_size=12), api.ERR_SHAPE),
     (dict(page_size=0), api.ERR_SHAPE),
-    (dict(max_pps=10), api.ERR_SHAPE),          # 160 < 256 + 16 tokens
+    (dict(max_pps=-1), api.ERR_SHAPE),
     (dict(S=-1), api.ERR_SHAPE),
     (dict(splits=-2), api.ERR_SHAPE),
     (dict(scale=float("nan")), api.ERR_SHAPE),

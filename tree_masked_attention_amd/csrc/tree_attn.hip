@@ -203,10 +203,6 @@ int tree_attn_verify(const void* q, const void* k_cache, const void* v_cache,
   }
   if (!is_pow2(page_size) || page_size > 4096) return TREE_ATTN_ERR_SHAPE;
   if ((long long)mask_words * 64 < max_nodes) return TREE_ATTN_ERR_SHAPE;
-  if ((long long)max_pages_per_seq * page_size <
-      (long long)max_prefix_len + max_nodes) {
-    return TREE_ATTN_ERR_SHAPE;
-  }
   if (!std::isfinite(scale)) return TREE_ATTN_ERR_SHAPE;
   if (num_seqs == 0 || total_nodes == 0) return TREE_ATTN_OK;
   if (num_pages < 1 || max_pages_per_seq < 1) return TREE_ATTN_ERR_SHAPE;
