@@ -154,7 +154,8 @@ def main():
     out = torch.empty((N, Hq, d), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((N, Hq), dtype=torch.float32, device=dev)
     ws_bytes = api.workspace_size(S, N, Hq, wl.num_kv_heads, d,
-                                  wl.max_prefix_len, wl.max_nodes, args.splits)
+                                  wl.max_prefix_len, wl.max_nodes,
+                                  wl.page_size, args.splits)
     ws = torch.empty((max(ws_bytes, 256),), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream

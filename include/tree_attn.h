@@ -100,13 +100,15 @@ int tree_attn_build_mask(const int32_t* parents, const int32_t* tree_offsets,
  * tree_attn_workspace_size - bytes of device workspace tree_attn_verify
  * needs for these sizes (0 when the planned launch needs none).
  * Arguments as for tree_attn_verify.  num_splits: 0 lets the library plan
- * the split of the key range; n > 0 forces n splits (clamped to what the
- * key range allows).  Returns 0 for invalid sizes as well.
+ * the split of the key range; n > 0 asks for n splits, clamped to what the
+ * key range allows (at least 64 keys per split, at most 1023 pages per
+ * split, at most 256 splits).  Returns 0 for invalid sizes as well.
  */
 size_t tree_attn_workspace_size(int32_t num_seqs, int32_t total_nodes,
                                 int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t max_prefix_len,
-                                int32_t max_nodes, int32_t num_splits);
+                                int32_t max_nodes, int32_t page_size,
+                                int32_t num_splits);
 
 /*
  * tree_attn_verify - tree-causal verification attention over a paged
@@ -135,7 +137,7 @@ size_t tree_attn_workspace_size(int32_t num_seqs, int32_t total_nodes,
  *   max_prefix_len, max_nodes   host upper bounds of the device values;
  *                 they size the launch, so no device-to-host copy is made
  *   head_dim      128 in this build
- *   scale         softmax scale (1/sqrt(head_dim) for standard attention)
+ *   scale         softmax scale > 0 (1/sqrt(head_dim) for standard attention)
  *   num_splits    0 = planned by the library; n > 0 forces n splits
  *   out           dev bf16 [total_nodes, num_q_heads, head_dim]  (output)
  *   lse           dev fp32 [total_nodes, num_q_heads], natural log (output)
@@ -148,8 +150,8 @@ size_t tree_attn_workspace_size(int32_t num_seqs, int32_t total_nodes,
  * access outside the buffers described above.
  *
  * Host-side errors: ERR_NULL, ERR_SHAPE (num_q_heads % num_kv_heads != 0,
- * mask_words * 64 < max_nodes, page_size not a power of two, negative
- * sizes), ERR_UNSUPPORTED (head_dim != 128, max_nodes >
+ * mask_words * 64 < max_nodes, page_size not a power of two, scale not
+ * finite and positive, negative sizes), ERR_UNSUPPORTED (head_dim != 128, max_nodes >
  * TREE_ATTN_MAX_NODES), ERR_WORKSPACE, ERR_HIP.
  */
 int tree_attn_verify(const void* q, const void* k_cache, const void* v_cache,

@@ -75,6 +75,8 @@ def _verify(**over):
     (dict(S=-1), api.ERR_SHAPE),
     (dict(splits=-2), api.ERR_SHAPE),
     (dict(scale=float("nan")), api.ERR_SHAPE),
+    (dict(scale=0.0), api.ERR_SHAPE),
+    (dict(scale=-0.5), api.ERR_SHAPE),
     (dict(q=None), api.ERR_NULL),
     (dict(k=None), api.ERR_NULL),
     (dict(table=None), api.ERR_NULL),
@@ -95,8 +97,12 @@ def test_verify_empty_is_noop():
 
 def test_workspace_size_rules():
     # one split needs no workspace; forced splits need partial rows
-    ws1 = api.workspace_size(1, 16, 8, 2, 128, 256, 16, 1)
-    ws4 = api.workspace_size(1, 16, 8, 2, 128, 1024, 16, 4)
+    ws1 = api.workspace_size(1, 16, 8, 2, 128, 256, 16, 16, 1)
+    ws4 = api.workspace_size(1, 16, 8, 2, 128, 1024, 16, 16, 4)
     assert ws1 == 0
     assert ws4 >= 4 * 16 * 8 * (128 + 2) * 4
-    assert api.workspace_size(1, 16, 8, 3, 128, 256, 16, 0) == 0  # invalid
+    assert api.workspace_size(1, 16, 8, 3, 128, 256, 16, 16, 0) == 0  # invalid
+    assert api.workspace_size(1, 16, 8, 2, 128, 256, 16, 12, 0) == 0  # page
+    # tiny pages force more splits (each split's page slice is bounded)
+    assert api.workspace_size(1, 16, 8, 2, 128, 5000, 16, 1, 1) >= \
+        5 * 16 * 8 * (128 + 2) * 4

@@ -35,7 +35,7 @@ _lib.tree_attn_abi_version.argtypes = []
 _lib.tree_attn_build_mask.restype = ctypes.c_int
 _lib.tree_attn_build_mask.argtypes = [_p, _p, _i, _i, _i, _i, _p, _p, _p]
 _lib.tree_attn_workspace_size.restype = ctypes.c_size_t
-_lib.tree_attn_workspace_size.argtypes = [_i] * 8
+_lib.tree_attn_workspace_size.argtypes = [_i] * 9
 _lib.tree_attn_verify.restype = ctypes.c_int
 _lib.tree_attn_verify.argtypes = (
     [_p, _p, _p, _p, _i, _i, _i, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i,
@@ -129,10 +129,11 @@ def build_mask(parents: torch.Tensor, tree_offsets: torch.Tensor,
 
 def workspace_size(num_seqs: int, total_nodes: int, num_q_heads: int,
                    num_kv_heads: int, head_dim: int, max_prefix_len: int,
-                   max_nodes: int, num_splits: int = 0) -> int:
+                   max_nodes: int, page_size: int = 16,
+                   num_splits: int = 0) -> int:
     return int(_lib.tree_attn_workspace_size(
         num_seqs, total_nodes, num_q_heads, num_kv_heads, head_dim,
-        max_prefix_len, max_nodes, num_splits))
+        max_prefix_len, max_nodes, page_size, num_splits))
 
 
 def verify(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -176,7 +177,7 @@ def verify(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     if lse is None:
         lse = torch.empty((N, Hq), dtype=torch.float32, device=q.device)
     ws_bytes = workspace_size(S, N, Hq, Hkv, d, max_prefix_len, max_nodes,
-                              num_splits)
+                              page_size, num_splits)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty((ws_bytes,), dtype=torch.uint8,
                                 device=q.device)

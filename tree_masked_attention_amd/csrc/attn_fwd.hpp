@@ -8,25 +8,36 @@
 //
 // Work decomposition.  The rows of one (sequence s, kv head g) pair are the
 // G query heads of the group times the B_s nodes, packed node-major
-// (row = i * G + h_in_group), so every K/V tile staged in LDS serves all G
-// heads of the group.  A workgroup owns kRowsPerWG rows and one split of
-// the key range [0, P_s + B_s); the tree keys are the last B_s positions,
-// so the split that reaches them applies the bitmask there (the
-// "tree-block pass" runs as the tail tiles of the last split).  With one
-// split the kernel writes the normalised output and the LSE directly;
-// otherwise it writes (unnormalised O, running max, running sum) partials
-// that the merge kernel combines.
+// (row = i * G + h_in_group), so each K/V tile staged in LDS serves all G
+// heads of the group.  A workgroup of NW waves owns 32*NW rows and one split
+// of the key range [0, P_s + B_s).  The tree keys are the last B_s positions
+// of that range, so the split that reaches them applies the bitmask on its
+// tail tiles (the tree-block pass).  With one split the kernel writes the
+// normalised output and the LSE; otherwise it writes (unnormalised O,
+// running max, running sum) partials for the merge kernel.
 //
-// Matrix-core mapping (v_mfma_f32_32x32x16_bf16, D = A*B + C, A 32x16,
-// B 16x32): scores are computed transposed, S^T = K * Q^T, so the query is
-// the MFMA column and every lane holds 16 scores of ONE query.  Row
-// statistics are then lane-local plus one exchange between the two lane
-// halves.  The K rows fed to the A operand are permuted (sigma below) so
-// that lane half hf holds the 16 CONSECUTIVE keys 16*hf .. 16*hf+15 of a
-// 32-key block; the probabilities then feed O^T = V^T * P^T as the B
-// operand straight from registers, and V^T is read from LDS with 16-byte
-// loads.  Softmax runs in base 2 with scale*log2(e) folded into one
-// multiply; the LSE is converted back to natural log at the end.
+// Matrix-core mapping (v_mfma_f32_32x32x16_bf16, D = A*B + C).  Scores are
+// computed transposed, S^T = K * Q^T: the query is the MFMA column, so a
+// lane holds 16 scores of ONE query and row statistics are lane-local plus
+// one exchange between the two lane halves (v_permlane32_swap).  Register
+// r of lane half h holds key 8*(r/4) + 4*h + r%4 of a 32-key block, i.e.
+// runs of 4 consecutive keys.  O^T = V^T * P^T then takes the probabilities
+// as the B operand straight from registers; its A operand (V^T, 8 keys of
+// one column per lane) comes from the row-major V tile through two
+// transposing LDS reads (ds_read_b64_tr_b16), each delivering the 4
+// consecutive keys of one register run.
+//
+// Pipeline.  The split's slice of the page table is copied to LDS once.
+// K/V tiles of 64 keys are double-buffered in LDS: the global loads of tile
+// j+1 are issued into registers before tile j is computed and written to
+// the other buffer after it, one barrier per tile.
+//
+// Softmax runs in base 2: scale*log2(e) is folded into the FMA that
+// subtracts the running max.  The running max is only raised when a tile's
+// max exceeds it by more than 8 (log2 units); otherwise the stale max is
+// kept, which bounds the probabilities by 2^8 and skips the O rescale.
+// The row sum accumulates the fp32 probabilities (before their rounding to
+// bf16 for the PV product), which keeps the LSE accurate on short rows.
 #pragma once
 
 #include "common.hpp"
@@ -49,37 +60,57 @@ struct FwdParams {
   int max_tokens;  // min(max_pps * page_size, 2^30)
   int S, N, Hq, Hkv, G;
   int mblocks, splits, chunk;
+  int units, per_xcd;  // work units; units handled per XCD slot column
   float scale_log2;
 };
 
-constexpr int kFwdWaves = 4;
-constexpr int kRowsPerWave = 32;
-constexpr int kRowsPerWG = kFwdWaves * kRowsPerWave;
 constexpr int kKeyTile = 64;
-constexpr int kKStride = kHeadDim + 8;  // bf16 per K row in LDS (padded)
-constexpr int kVStride = kKeyTile + 8;  // bf16 per V^T row in LDS (padded)
+constexpr int kKStride = kHeadDim + 8;   // u16 per K row in LDS (272 B)
+constexpr int kVStride = kHeadDim + 32;  // u16 per V row in LDS (320 B)
+constexpr int kPageCache = 1024;         // page-table entries per split
+constexpr float kLazyRescale = 8.f;      // log2 units
 
-// MFMA output row m of a 32-key block holds key sigma(m); chosen so that
-// lane half hf, register r (row 8*(r/4) + 4*hf + r%4) holds key 16*hf + r.
-__device__ __forceinline__ int key_of_row(int m) {
-  return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
-}
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 __device__ __forceinline__ bf16x8 lds_bf16x8(const unsigned short* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
 
-__global__ __launch_bounds__(kFwdWaves * 64) void attn_fwd_kernel(FwdParams p) {
-  __shared__ __align__(16) unsigned short k_lds[kKeyTile * kKStride];
-  __shared__ __align__(16) unsigned short vt_lds[kHeadDim * kVStride];
+// Transposing LDS read: see the file comment.
+__device__ __forceinline__ s16x4 lds_tr4(const unsigned short* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+}
 
-  int bid = blockIdx.x;
-  const int split = bid % p.splits;
-  bid /= p.splits;
-  const int mb = bid % p.mblocks;
-  bid /= p.mblocks;
-  const int g = bid % p.Hkv;
-  const int s = bid / p.Hkv;
+// Value of the other lane half (lane ^ 32).
+__device__ __forceinline__ float other_half(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  // r[0]: lanes 32..63 now hold lanes 0..31; r[1]: lanes 0..31 hold 32..63
+  const unsigned lane = __lane_id();
+  return __builtin_bit_cast(float, lane < 32 ? r[1] : r[0]);
+}
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdParams p) {
+  constexpr int kThreads = NW * 64;
+  constexpr int kRowsPerWG = NW * 32;
+  constexpr int kCPT = (kKeyTile * 16) / kThreads;  // 16-B chunks / thread
+  __shared__ __align__(16) unsigned short k_lds[2][kKeyTile * kKStride];
+  __shared__ __align__(16) unsigned short v_lds[2][kKeyTile * kVStride];
+  __shared__ int pg_lds[kPageCache];
+
+  // XCD-aware decode: consecutive work units (the row blocks of one
+  // (sequence, kv head, split), which read the same K/V) go to one XCD.
+  const int bid = blockIdx.x;
+  int L = (bid & 7) * p.per_xcd + (bid >> 3);
+  if (L >= p.units) return;
+  const int mb = L % p.mblocks;
+  L /= p.mblocks;
+  const int split = L % p.splits;
+  L /= p.splits;
+  const int g = L % p.Hkv;
+  const int s = L / p.Hkv;
 
   const int a = clampi(p.tree_offsets[s], 0, p.N);
   const int b = clampi(p.tree_offsets[s + 1], a, p.N);
@@ -96,7 +127,18 @@ __global__ __launch_bounds__(kFwdWaves * 64) void attn_fwd_kernel(FwdParams p) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int col = lane & 31, half = lane >> 5;
-  const int r = r0 + wave * kRowsPerWave + col;
+
+  // Page-table slice of this split -> LDS.
+  const int lp0 = kbeg >> p.log2_page;
+  const int npg = min(((kend - 1) >> p.log2_page) - lp0 + 1, kPageCache);
+  {
+    const int* ptab = p.page_table + (size_t)s * p.max_pps + lp0;
+    for (int i = tid; i < npg; i += kThreads) {
+      pg_lds[i] = clampi(ptab[i], 0, p.num_pages - 1);
+    }
+  }
+
+  const int r = r0 + wave * 32 + col;
   const bool rvalid = r < rows;
   const int node = rvalid ? r / p.G : B - 1;
   const int head = g * p.G + (rvalid ? r % p.G : 0);
@@ -114,111 +156,166 @@ __global__ __launch_bounds__(kFwdWaves * 64) void attn_fwd_kernel(FwdParams p) {
     }
   }
   const uint64_t* mrow = p.masks + (size_t)(a + node) * p.W;
-  const int* ptab = p.page_table + (size_t)s * p.max_pps;
   const int pmask = (1 << p.log2_page) - 1;
+  const size_t kv_head_off = (size_t)g * kHeadDim;
+  const size_t tok_stride = (size_t)p.Hkv * kHeadDim;
+
+  u32x4 kreg[kCPT], vreg[kCPT];
+  auto load_tile = [&](int t0) {
+#pragma unroll
+    for (int k = 0; k < kCPT; ++k) {
+      const int c = tid + k * kThreads;
+      const int key = c >> 4, part = c & 15;
+      const int pos = t0 + key;
+      kreg[k] = u32x4{0, 0, 0, 0};
+      vreg[k] = u32x4{0, 0, 0, 0};
+      if (pos < kend) {
+        const int pi = clampi((pos >> p.log2_page) - lp0, 0, kPageCache - 1);
+        const size_t tok = ((size_t)pg_lds[pi] << p.log2_page) + (pos & pmask);
+        const size_t off = tok * tok_stride + kv_head_off + part * 8;
+        kreg[k] = *reinterpret_cast<const u32x4*>(p.k + off);
+        vreg[k] = *reinterpret_cast<const u32x4*>(p.v + off);
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int k = 0; k < kCPT; ++k) {
+      const int c = tid + k * kThreads;
+      const int key = c >> 4, part = c & 15;
+      *reinterpret_cast<u32x4*>(&k_lds[buf][key * kKStride + part * 8]) = kreg[k];
+      *reinterpret_cast<u32x4*>(&v_lds[buf][key * kVStride + part * 8]) = vreg[k];
+    }
+  };
 
   f32x16 o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY;  // log2 units, equal in both lane halves
+  float l_run = 0.f;        // this lane half's share of the sum
+  const float c2 = p.scale_log2;
 
-  for (int t0 = kbeg; t0 < kend; t0 += kKeyTile) {
-    __syncthreads();
-    // Stage K (row-major) and V^T (d-major) of keys t0 .. t0+63.
-#pragma unroll
-    for (int j = 0; j < (kKeyTile * 16) / (kFwdWaves * 64); ++j) {
-      const int c = tid + j * kFwdWaves * 64;
-      const int key = c >> 4, part = c & 15;
-      const int pos = t0 + key;
-      u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-      if (pos < kend) {
-        const int pg = clampi(ptab[pos >> p.log2_page], 0, p.num_pages - 1);
-        const size_t tok = ((size_t)pg << p.log2_page) + (pos & pmask);
-        const size_t off = (tok * p.Hkv + g) * kHeadDim + part * 8;
-        kv = *reinterpret_cast<const u32x4*>(p.k + off);
-        vv = *reinterpret_cast<const u32x4*>(p.v + off);
-      }
-      *reinterpret_cast<u32x4*>(&k_lds[key * kKStride + part * 8]) = kv;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        vt_lds[(part * 8 + e) * kVStride + key] =
-            (unsigned short)(vv[e >> 1] >> (16 * (e & 1)));
-      }
-    }
-    __syncthreads();
+  // per-lane constant part of the transposed V read address
+  const int r16 = lane & 15;
+  const int v_lane_off = (4 * half + (r16 >> 2)) * kVStride +
+                         16 * ((lane >> 4) & 1) + 4 * (r16 & 3);
 
-    // S^T (two 32-key blocks x 32 queries per wave).
+  const int ntiles = (kend - kbeg + kKeyTile - 1) / kKeyTile;
+  __syncthreads();  // page slice visible
+  load_tile(kbeg);
+  store_tile(0);
+  __syncthreads();
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int t0 = kbeg + j * kKeyTile;
+    const int buf = j & 1;
+    if (j + 1 < ntiles) load_tile(t0 + kKeyTile);
+
+    // ---- S^T = K Q^T : two 32-key blocks x 32 queries
     f32x16 sc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       sc[kb] = f32x16{};
       const unsigned short* kp =
-          &k_lds[(kb * 32 + key_of_row(col)) * kKStride + half * 8];
+          &k_lds[buf][(kb * 32 + col) * kKStride + half * 8];
 #pragma unroll
       for (int kc = 0; kc < 8; ++kc) {
         sc[kb] = mfma32x32x16(lds_bf16x8(kp + kc * 16), qf[kc], sc[kb]);
       }
     }
 
-    // Scale to log2 units, mask, tile max.
-    const bool tree_tile = (t0 + kKeyTile > P);
+    // ---- mask: keys past the split end, tree keys not on the path
+    if (t0 + kKeyTile > min(P, kend)) {
+      const int nvalid = kend - t0;  // >= 1
+      const int npre = P - t0;
+      uint64_t allow = nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1);
+      uint64_t pre = npre >= 64 ? ~0ull : (npre <= 0 ? 0ull : ((1ull << npre) - 1));
+      uint64_t tree = 0;
+      if (npre < 64) {
+        const int j0 = t0 - P;  // tree node at tile offset 0 (may be < 0)
+        if (j0 >= 0) {
+          const int w0 = min(j0 >> 6, p.W - 1), sh = j0 & 63;
+          tree = mrow[w0] >> sh;
+          if (sh != 0 && w0 + 1 < p.W) tree |= mrow[w0 + 1] << (64 - sh);
+        } else {
+          tree = mrow[0] << (-j0);
+        }
+      }
+      allow &= (pre | tree);
+      allow >>= 4 * half;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const int kk = kb * 32 + 8 * (rr >> 2) + (rr & 3);
+          if (!((allow >> kk) & 1)) sc[kb][rr] = -INFINITY;
+        }
+      }
+    }
+
+    // ---- online softmax (base 2, lazy rescale)
     float tmax = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int pos = t0 + kb * 32 + half * 16 + rr;
-        bool ok = pos < kend;
-        if (tree_tile && ok && pos >= P) {
-          const int jn = pos - P;
-          const uint64_t w = mrow[min(jn >> 6, p.W - 1)];
-          ok = (w >> (jn & 63)) & 1;
-        }
-        const float x = ok ? sc[kb][rr] * p.scale_log2 : -INFINITY;
-        sc[kb][rr] = x;
-        tmax = fmaxf(tmax, x);
+      for (int rr = 0; rr < 16; rr += 2) {
+        tmax = fmaxf(tmax, fmaxf(sc[kb][rr], sc[kb][rr + 1]));
       }
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_ref);
+    tmax = fmaxf(tmax, other_half(tmax)) * c2;
+    const bool need = tmax > m_run + kLazyRescale;
+    if (__any(need)) {
+      const float m_new = need ? tmax : m_run;
+      const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] *= alpha;
+    }
+    const float m_ref = (m_run == -INFINITY) ? 0.f : m_run;
 
     bf16x8 pf[2][2];
-    float psum = 0.f;
+    float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const float e = fast_exp2(sc[kb][rr] - m_ref);
-        psum += e;
-        pf[kb][rr >> 3][rr & 7] = (__bf16)e;
+      for (int rr = 0; rr < 16; rr += 2) {
+        const float e0 = fast_exp2(fmaf(sc[kb][rr], c2, -m_ref));
+        const float e1 = fast_exp2(fmaf(sc[kb][rr + 1], c2, -m_ref));
+        ps0 += e0;
+        ps1 += e1;
+        pf[kb][rr >> 3][rr & 7] = (__bf16)e0;
+        pf[kb][rr >> 3][(rr & 7) + 1] = (__bf16)e1;
       }
     }
-    psum += __shfl_xor(psum, 32);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < 4; ++db) o[db] *= alpha;
+    l_run += ps0 + ps1;
 
-    // O^T += V^T * P^T.
+    // ---- O^T += V^T P^T
+    const unsigned short* vb = &v_lds[buf][v_lane_off];
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-      const unsigned short* vp = &vt_lds[(db * 32 + col) * kVStride + half * 16];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-          o[db] = mfma32x32x16(lds_bf16x8(vp + kb * 32 + hf * 8), pf[kb][hf],
-                               o[db]);
+          const unsigned short* vp = vb + (kb * 32 + hf * 16) * kVStride + db * 32;
+          const s16x4 lo = lds_tr4(vp);
+          const s16x4 hi = lds_tr4(vp + 8 * kVStride);
+          const bf16x8 vf = __builtin_bit_cast(
+              bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          o[db] = mfma32x32x16(vf, pf[kb][hf], o[db]);
         }
       }
     }
+
+    if (j + 1 < ntiles) store_tile(buf ^ 1);
+    __syncthreads();
   }
 
+  const float l_tot = l_run + other_half(l_run);
   if (!rvalid) return;
   if (p.splits == 1) {
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     __bf16* op = p.out + qrow * kHeadDim;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
@@ -231,7 +328,7 @@ __global__ __launch_bounds__(kFwdWaves * 64) void attn_fwd_kernel(FwdParams p) {
       }
     }
     if (half == 0) {
-      p.lse[qrow] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+      p.lse[qrow] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
     }
   } else {
     const size_t prow = (size_t)split * p.N * p.Hq + qrow;
@@ -246,7 +343,7 @@ __global__ __launch_bounds__(kFwdWaves * 64) void attn_fwd_kernel(FwdParams p) {
       }
     }
     if (half == 0) {
-      *reinterpret_cast<f32x2*>(p.part_ml + prow * 2) = f32x2{m_run, l_run};
+      *reinterpret_cast<f32x2*>(p.part_ml + prow * 2) = f32x2{m_run, l_tot};
     }
   }
 }

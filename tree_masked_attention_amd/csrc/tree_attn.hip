@@ -16,9 +16,9 @@ using namespace tree_attn;
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 constexpr int kMaxDevices = 64;
-constexpr int kMaxSplits = 64;
+constexpr int kMaxSplits = 256;
 constexpr int kMinKeysPerSplit = 256;
 
 std::atomic<int> g_cu_count[kMaxDevices];
@@ -53,48 +53,65 @@ int ilog2(int x) {
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct Plan {
-  int mblocks = 0;
-  int splits = 1;
-  int chunk = 0;
-  size_t part_o_bytes = 0;
+  int nw = 8;        // waves per workgroup (32 rows each)
+  int mblocks = 0;   // row blocks per (sequence, kv head)
+  int splits = 1;    // key-range splits
+  int chunk = 0;     // keys per split (multiple of the 64-key tile)
+  int units = 0;     // sequences * kv heads * splits * row blocks
   size_t part_ml_off = 0;
   size_t ws_bytes = 0;
 };
 
-// Split planning from host-side bounds only (no device-to-host copy).
-// Rows of a (sequence, kv head) pair are covered by `mblocks` workgroups;
-// the key range [0, max_prefix_len + max_nodes) is cut into `splits`
-// chunks of `chunk` keys (a multiple of the 64-key tile) so that the grid
-// offers about two workgroups per compute unit.
-Plan make_plan(int S, int N, int Hq, int Hkv, int max_prefix_len,
-               int max_nodes, int req_splits, int cus) {
+// Launch planning from host-side bounds only (no device-to-host copy).
+// Row blocks: 256 rows (8 waves) when a (sequence, kv head) pair has more
+// than 128 rows, else 128 rows (4 waves, two workgroups per CU).  The key
+// range [0, max_prefix_len + max_nodes) is cut into splits so that the
+// grid fills every workgroup slot once, with at least 256 keys per split,
+// and each split's page-table slice fits the kernel's LDS page cache.
+int make_plan(int S, int N, int Hq, int Hkv, int max_prefix_len,
+              int max_nodes, int page_size, int req_splits, int cus,
+              Plan* out) {
   Plan pl;
   const int G = Hq / Hkv;
-  const int rows = G * max_nodes;
-  pl.mblocks = std::max(1, (rows + kRowsPerWG - 1) / kRowsPerWG);
-  const long long T = (long long)max_prefix_len + max_nodes;
-  const long long units = (long long)S * Hkv * pl.mblocks;
-  int splits;
+  const long long rows = (long long)G * max_nodes;
+  pl.nw = rows > 128 ? 8 : 4;
+  const int rows_per_wg = 32 * pl.nw;
+  pl.mblocks = (int)std::max(1LL, (rows + rows_per_wg - 1) / rows_per_wg);
+  const long long T = std::max(1LL, (long long)max_prefix_len + max_nodes);
+  const long long units0 = (long long)S * Hkv * pl.mblocks;
+  const long long slots = (long long)cus * (pl.nw == 8 ? 1 : 2);
+  const long long max_chunk =
+      std::max<long long>(kKeyTile, ((long long)(kPageCache - 1) * page_size) /
+                                        kKeyTile * kKeyTile);
+  const long long min_splits = (T + max_chunk - 1) / max_chunk;
+  long long splits;
   if (req_splits > 0) {
     splits = req_splits;
   } else {
-    const long long want = (2LL * cus + units - 1) / std::max(1LL, units);
-    const long long by_len = std::max(1LL, T / kMinKeysPerSplit);
-    splits = (int)std::min<long long>(want, by_len);
+    splits = (slots + units0 - 1) / std::max(1LL, units0);
+    splits = std::min(splits, std::max(1LL, T / kMinKeysPerSplit));
   }
-  splits = std::max(1, std::min(splits, kMaxSplits));
+  splits = std::max(std::max(1LL, splits), min_splits);
+  if (splits > kMaxSplits) {
+    if (min_splits > kMaxSplits) return TREE_ATTN_ERR_UNSUPPORTED;
+    splits = kMaxSplits;
+  }
   long long chunk = (T + splits - 1) / splits;
-  chunk = std::max<long long>(kKeyTile, (chunk + kKeyTile - 1) / kKeyTile * kKeyTile);
-  splits = (int)std::max<long long>(1, (T + chunk - 1) / chunk);
-  pl.splits = splits;
+  chunk = (chunk + kKeyTile - 1) / kKeyTile * kKeyTile;
+  chunk = std::min(chunk, max_chunk);
+  splits = (T + chunk - 1) / chunk;
+  pl.splits = (int)splits;
   pl.chunk = (int)chunk;
+  const long long units = units0 * splits;
+  if (units > (1LL << 30)) return TREE_ATTN_ERR_UNSUPPORTED;
+  pl.units = (int)units;
   if (splits > 1) {
     const size_t rows_all = (size_t)N * Hq * splits;
-    pl.part_o_bytes = align_up(rows_all * kHeadDim * sizeof(float), 256);
-    pl.part_ml_off = pl.part_o_bytes;
+    pl.part_ml_off = align_up(rows_all * kHeadDim * sizeof(float), 256);
     pl.ws_bytes = pl.part_ml_off + align_up(rows_all * 2 * sizeof(float), 256);
   }
-  return pl;
+  *out = pl;
+  return TREE_ATTN_OK;
 }
 
 int check_sizes(int S, int N, int Hq, int Hkv, int head_dim,
@@ -171,16 +188,21 @@ int tree_attn_build_mask(const int32_t* parents, const int32_t* tree_offsets,
 size_t tree_attn_workspace_size(int32_t num_seqs, int32_t total_nodes,
                                 int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t max_prefix_len,
-                                int32_t max_nodes, int32_t num_splits) {
+                                int32_t max_nodes, int32_t page_size,
+                                int32_t num_splits) {
   if (check_sizes(num_seqs, total_nodes, num_q_heads, num_kv_heads, head_dim,
                   max_prefix_len, max_nodes) != TREE_ATTN_OK ||
-      num_splits < 0) {
+      num_splits < 0 || !is_pow2(page_size) || page_size > 4096) {
     return 0;
   }
   if (num_seqs == 0 || total_nodes == 0) return 0;
-  return make_plan(num_seqs, total_nodes, num_q_heads, num_kv_heads,
-                   max_prefix_len, max_nodes, num_splits, cu_count())
-      .ws_bytes;
+  Plan pl;
+  if (make_plan(num_seqs, total_nodes, num_q_heads, num_kv_heads,
+                max_prefix_len, max_nodes, page_size, num_splits, cu_count(),
+                &pl) != TREE_ATTN_OK) {
+    return 0;
+  }
+  return pl.ws_bytes;
 }
 
 int tree_attn_verify(const void* q, const void* k_cache, const void* v_cache,
@@ -203,7 +225,7 @@ int tree_attn_verify(const void* q, const void* k_cache, const void* v_cache,
   }
   if (!is_pow2(page_size) || page_size > 4096) return TREE_ATTN_ERR_SHAPE;
   if ((long long)mask_words * 64 < max_nodes) return TREE_ATTN_ERR_SHAPE;
-  if (!std::isfinite(scale)) return TREE_ATTN_ERR_SHAPE;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return TREE_ATTN_ERR_SHAPE;
   if (num_seqs == 0 || total_nodes == 0) return TREE_ATTN_OK;
   if (num_pages < 1 || max_pages_per_seq < 1) return TREE_ATTN_ERR_SHAPE;
   if (!q || !k_cache || !v_cache || !page_table || !prefix_lens ||
@@ -211,8 +233,11 @@ int tree_attn_verify(const void* q, const void* k_cache, const void* v_cache,
     return TREE_ATTN_ERR_NULL;
   }
 
-  const Plan pl = make_plan(num_seqs, total_nodes, num_q_heads, num_kv_heads,
-                            max_prefix_len, max_nodes, num_splits, cu_count());
+  Plan pl;
+  st = make_plan(num_seqs, total_nodes, num_q_heads, num_kv_heads,
+                 max_prefix_len, max_nodes, page_size, num_splits, cu_count(),
+                 &pl);
+  if (st != TREE_ATTN_OK) return st;
   if (pl.ws_bytes > 0) {
     if (!workspace) return TREE_ATTN_ERR_WORKSPACE;
     if (workspace_bytes < pl.ws_bytes) return TREE_ATTN_ERR_WORKSPACE;
@@ -248,14 +273,17 @@ int tree_attn_verify(const void* q, const void* k_cache, const void* v_cache,
   fp.mblocks = pl.mblocks;
   fp.splits = pl.splits;
   fp.chunk = pl.chunk;
+  fp.units = pl.units;
+  fp.per_xcd = (pl.units + 7) / 8;
   fp.scale_log2 = scale * kLog2e;
 
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  const long long grid =
-      (long long)num_seqs * num_kv_heads * pl.mblocks * pl.splits;
-  if (grid > 0x7fffffffLL) return TREE_ATTN_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)grid),
-                     dim3(kFwdWaves * 64), 0, hs, fp);
+  const unsigned grid = 8u * (unsigned)fp.per_xcd;
+  if (pl.nw == 8) {
+    hipLaunchKernelGGL(attn_fwd_kernel<8>, dim3(grid), dim3(8 * 64), 0, hs, fp);
+  } else {
+    hipLaunchKernelGGL(attn_fwd_kernel<4>, dim3(grid), dim3(4 * 64), 0, hs, fp);
+  }
   if (hipGetLastError() != hipSuccess) return TREE_ATTN_ERR_HIP;
 
   if (pl.splits > 1) {
