@@ -27,17 +27,30 @@
 // transposing LDS reads (ds_read_b64_tr_b16), each delivering the 4
 // consecutive keys of one register run.
 //
-// Pipeline.  The split's slice of the page table is copied to LDS once.
-// K/V tiles of 64 keys are double-buffered in LDS: the global loads of tile
-// j+1 are issued into registers before tile j is computed and written to
-// the other buffer after it, one barrier per tile.
+// Memory pipeline.  K/V tiles of 64 keys (16 KB each) flow through a
+// 4-stage LDS ring filled by global_load_lds_dwordx4: the load unit writes
+// each lane's 16 bytes straight to LDS (lane l of an instruction lands at
+// M0 + 16*l), so no registers stage the data.  The loads are issued from
+// inline assembly and waited for with explicit vmcnt counts, because the
+// compiler would otherwise drain every such load before each barrier and
+// the ring would never hold more than one tile in flight.  Tile j+3 is
+// issued while tile j is consumed.  Rows are stored unpadded with an XOR
+// swizzle of their 16-byte chunks (K: chunk ^ (row & 15); V: chunk ^
+// 4*(row & 3)) so that the MFMA operand reads hit distinct LDS banks.  The
+// split's page-table slice and the window of ancestor-mask words its tree
+// keys need are copied to LDS before the ring starts, so the loop issues no
+// other global loads.
 //
-// Softmax runs in base 2: scale*log2(e) is folded into the FMA that
-// subtracts the running max.  The running max is only raised when a tile's
-// max exceeds it by more than 8 (log2 units); otherwise the stale max is
-// kept, which bounds the probabilities by 2^8 and skips the O rescale.
-// The row sum accumulates the fp32 probabilities (before their rounding to
-// bf16 for the PV product), which keeps the LSE accurate on short rows.
+// Compute pipeline.  Four waves per workgroup and one workgroup per CU, so
+// every wave owns a SIMD and its whole register file; a wave covers QB
+// blocks of 32 queries, and each K or V operand it reads from LDS feeds QB
+// MFMAs.  The S^T MFMAs of tile j+1 are issued before the softmax of tile
+// j, in the same basic block, so the matrix core works while the vector
+// ALU exponentiates.  Softmax runs in base 2 with scale*log2(e) folded into the
+// FMA that subtracts the running max; the running max is only raised when a
+// tile's max exceeds it by more than 8 (log2 units), which bounds the
+// probabilities by 2^8 and skips most O rescales.  The row sum accumulates
+// the fp32 probabilities (before their rounding to bf16 for the PV product).
 #pragma once
 
 #include "common.hpp"
@@ -65,21 +78,44 @@ struct FwdParams {
 };
 
 constexpr int kKeyTile = 64;
-constexpr int kKStride = kHeadDim + 8;   // u16 per K row in LDS (272 B)
-constexpr int kVStride = kHeadDim + 32;  // u16 per V row in LDS (320 B)
-constexpr int kPageCache = 1024;         // page-table entries per split
-constexpr float kLazyRescale = 8.f;      // log2 units
+constexpr int kStages = 4;
+constexpr int kTileBytes = kKeyTile * kHeadDim * 2;   // 16 KB per matrix
+constexpr int kStageBytes = 2 * kTileBytes;           // K then V
+constexpr int kPageCache = 1024;                      // page ids per split
+constexpr int kMaskCache = 2304;                      // mask words per WG
+constexpr float kLazyRescale = 8.f;                   // log2 units
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
-__device__ __forceinline__ bf16x8 lds_bf16x8(const unsigned short* p) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+__device__ __forceinline__ bf16x8 lds_read16(unsigned addr) {
+  return __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(size_t)addr);
 }
 
-// Transposing LDS read: see the file comment.
-__device__ __forceinline__ s16x4 lds_tr4(const unsigned short* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+// Transposing LDS read (see the file comment).
+__device__ __forceinline__ s16x4 lds_read_tr(unsigned addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(size_t)addr);
+}
+
+// 16 bytes per lane from global memory to LDS at lds_base + 16 * lane.
+// The compiler does not track these loads; callers wait with wait_vmcnt.
+__device__ __forceinline__ void dma16(const void* gptr, unsigned lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds_base), "v"(gptr) : "memory");
+}
+
+// Same, with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane
+// offset (no per-lane 64-bit address arithmetic).
+__device__ __forceinline__ void dma16_sbase(const void* sbase, unsigned voff,
+                                            unsigned lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds_base), "v"(voff), "s"(sbase) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
 
 // Value of the other lane half (lane ^ 32).
@@ -87,18 +123,38 @@ __device__ __forceinline__ float other_half(float x) {
   const unsigned u = __builtin_bit_cast(unsigned, x);
   auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
   // r[0]: lanes 32..63 now hold lanes 0..31; r[1]: lanes 0..31 hold 32..63
-  const unsigned lane = __lane_id();
-  return __builtin_bit_cast(float, lane < 32 ? r[1] : r[0]);
+  return __builtin_bit_cast(float, __lane_id() < 32 ? r[1] : r[0]);
 }
 
-template <int NW>
-__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdParams p) {
+// Applies the mask of one tile (keys past the split end; tree keys off the
+// node's root-to-node path) to the scores of one 32-query block.
+__device__ __forceinline__ void apply_tile_mask(f32x16 (&S)[2], uint64_t allow,
+                                                int half) {
+  allow >>= 4 * half;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int kk = kb * 32 + 8 * (rr >> 2) + (rr & 3);
+      if (!((allow >> kk) & 1)) S[kb][rr] = -INFINITY;
+    }
+  }
+}
+
+// QB = 32-query column blocks per wave (1 or 2).  Four waves per workgroup,
+// one workgroup per CU (the LDS ring fills the CU), so each wave has a SIMD
+// and its full register file to itself.
+template <int QB>
+__global__ __launch_bounds__(256, 1) void attn_fwd_kernel(FwdParams p) {
+  constexpr int NW = 4;
   constexpr int kThreads = NW * 64;
-  constexpr int kRowsPerWG = NW * 32;
-  constexpr int kCPT = (kKeyTile * 16) / kThreads;  // 16-B chunks / thread
-  __shared__ __align__(16) unsigned short k_lds[2][kKeyTile * kKStride];
-  __shared__ __align__(16) unsigned short v_lds[2][kKeyTile * kVStride];
+  constexpr int kRowsPerWave = 32 * QB;
+  constexpr int kRowsPerWG = NW * kRowsPerWave;
+  constexpr int kOpsPerMat = 16 / NW;        // 1-KB DMA ops per wave per matrix
+  constexpr int kOps = 2 * kOpsPerMat;       // per wave per tile
+  __shared__ __align__(1024) unsigned char ring[kStages * kStageBytes];
   __shared__ int pg_lds[kPageCache];
+  __shared__ uint64_t mk_lds[kMaskCache];
 
   // XCD-aware decode: consecutive work units (the row blocks of one
   // (sequence, kv head, split), which read the same K/V) go to one XCD.
@@ -123,227 +179,530 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdParams p) {
   const int kbeg = split * p.chunk;
   if (kbeg >= T) return;
   const int kend = min(T, kbeg + p.chunk);
+  const int ntiles = (kend - kbeg + kKeyTile - 1) / kKeyTile;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  // readfirstlane tells the compiler the wave index is wave-uniform
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
   const int col = lane & 31, half = lane >> 5;
 
-  // Page-table slice of this split -> LDS.
+  // ---- page-table slice of this split -> LDS
   const int lp0 = kbeg >> p.log2_page;
-  const int npg = min(((kend - 1) >> p.log2_page) - lp0 + 1, kPageCache);
   {
+    const int npg = min(((kend - 1) >> p.log2_page) - lp0 + 1, kPageCache);
     const int* ptab = p.page_table + (size_t)s * p.max_pps + lp0;
     for (int i = tid; i < npg; i += kThreads) {
       pg_lds[i] = clampi(ptab[i], 0, p.num_pages - 1);
     }
   }
 
-  const int r = r0 + wave * 32 + col;
-  const bool rvalid = r < rows;
-  const int node = rvalid ? r / p.G : B - 1;
-  const int head = g * p.G + (rvalid ? r % p.G : 0);
-  const size_t qrow = (size_t)(a + node) * p.Hq + head;
+  // ---- ancestor-mask words of this workgroup's nodes for the split's
+  // tree keys -> LDS (window of words wlo..whi of each node's row).  The
+  // host sizes the workgroup so that nnodes * nwin <= kMaskCache.
+  const int n_lo = r0 / p.G;
+  const int n_hi = (min(r0 + kRowsPerWG, rows) - 1) / p.G;
+  const int nnodes = n_hi - n_lo + 1;
+  const bool has_tree = kend > P;
+  const int wlo = has_tree ? (max(kbeg, P) - P) >> 6 : 0;
+  const int whi = has_tree ? min(p.W - 1, ((kend - 1 - P) >> 6) + 1) : 0;
+  const int nwin = whi - wlo + 1;
+  if (has_tree) {
+    const int nm = min(nnodes * nwin, kMaskCache);
+    for (int i = tid; i < nm; i += kThreads) {
+      const int nn = i / nwin, w = i - nn * nwin;
+      mk_lds[i] = p.masks[(size_t)(a + n_lo + nn) * p.W + wlo + w];
+    }
+  }
 
-  // Q^T fragments (B operand): query `col`, d = kc*16 + half*8 + 0..7.
-  bf16x8 qf[8];
-  {
-    const __bf16* qp = p.q + qrow * kHeadDim + half * 8;
+  // ---- this lane's query rows (one per column block)
+  bool rvalid[QB];
+  int node[QB];
+  size_t qrow[QB];
+  bf16x8 qf[QB][8];  // Q^T fragments (B operand): d = kc*16 + half*8 + 0..7
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int r = r0 + wave * kRowsPerWave + qb * 32 + col;
+    rvalid[qb] = r < rows;
+    node[qb] = rvalid[qb] ? r / p.G : n_hi;
+    const int head = g * p.G + (rvalid[qb] ? r % p.G : 0);
+    qrow[qb] = (size_t)(a + node[qb]) * p.Hq + head;
+    const __bf16* qp = p.q + qrow[qb] * kHeadDim + half * 8;
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) {
-      u32x4 raw = rvalid ? *reinterpret_cast<const u32x4*>(qp + kc * 16)
-                         : u32x4{0, 0, 0, 0};
-      qf[kc] = __builtin_bit_cast(bf16x8, raw);
+      u32x4 raw = rvalid[qb] ? *reinterpret_cast<const u32x4*>(qp + kc * 16)
+                             : u32x4{0, 0, 0, 0};
+      qf[qb][kc] = __builtin_bit_cast(bf16x8, raw);
     }
   }
-  const uint64_t* mrow = p.masks + (size_t)(a + node) * p.W;
-  const int pmask = (1 << p.log2_page) - 1;
-  const size_t kv_head_off = (size_t)g * kHeadDim;
-  const size_t tok_stride = (size_t)p.Hkv * kHeadDim;
 
-  u32x4 kreg[kCPT], vreg[kCPT];
-  auto load_tile = [&](int t0) {
+  // ---- LDS addresses
+  const unsigned ring_base =
+      (unsigned)(size_t)(__attribute__((address_space(3))) unsigned char*)ring;
+  // K operand: row kb*32 + col, 16-B chunk (2*kc + half) ^ (col & 15)
+  unsigned k_off[8];
 #pragma unroll
-    for (int k = 0; k < kCPT; ++k) {
-      const int c = tid + k * kThreads;
-      const int key = c >> 4, part = c & 15;
-      const int pos = t0 + key;
-      kreg[k] = u32x4{0, 0, 0, 0};
-      vreg[k] = u32x4{0, 0, 0, 0};
-      if (pos < kend) {
-        const int pi = clampi((pos >> p.log2_page) - lp0, 0, kPageCache - 1);
-        const size_t tok = ((size_t)pg_lds[pi] << p.log2_page) + (pos & pmask);
-        const size_t off = tok * tok_stride + kv_head_off + part * 8;
-        kreg[k] = *reinterpret_cast<const u32x4*>(p.k + off);
-        vreg[k] = *reinterpret_cast<const u32x4*>(p.v + off);
+  for (int kc = 0; kc < 8; ++kc) {
+    k_off[kc] = col * 256 + (((2 * kc + half) ^ (col & 15)) << 4);
+  }
+  // V^T operand: rows kbase + 4*half + y (y = lane%16 / 4), chunk
+  // 4*db + x, x = 2*((lane/16)&1) + (lane%4)/2, swizzled by 4*y.
+  const int y = (lane & 15) >> 2;
+  const int x = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  unsigned v_off[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    v_off[db] = kTileBytes + (4 * half + y) * 256 +
+                ((4 * (db ^ y) + x) << 4) + 8 * (lane & 1);
+  }
+
+  // ---- DMA of one tile: wave w moves rows 4*i .. 4*i+3 for
+  // i in [w*kOpsPerMat, (w+1)*kOpsPerMat) of K and of V.  The byte offset
+  // of a lane's 16 bytes is page * page_bytes + slot * tok_bytes +
+  // (head and swizzled chunk), the last part fixed per lane and row.
+  const int pmask = (1 << p.log2_page) - 1;
+  const unsigned tok_bytes = (unsigned)p.Hkv * kHeadDim * 2;
+  const unsigned page_bytes = tok_bytes << p.log2_page;
+  const int lrow = lane >> 4, lchunk = lane & 15;
+  unsigned k_lane[kOpsPerMat], v_lane[kOpsPerMat];
+#pragma unroll
+  for (int k = 0; k < kOpsPerMat; ++k) {
+    const int row = 4 * (wave * kOpsPerMat + k) + lrow;
+    k_lane[k] = g * kHeadDim * 2 + ((lchunk ^ (row & 15)) << 4);
+    v_lane[k] = g * kHeadDim * 2 + ((lchunk ^ (4 * (row & 3))) << 4);
+  }
+  const char* kbase = reinterpret_cast<const char*>(p.k);
+  const char* vbase = reinterpret_cast<const char*>(p.v);
+  // Fast path: with pages of >= 16 tokens the 16 rows a wave moves
+  // (4*kOpsPerMat rows starting at a multiple of 16) lie in one page, so
+  // the page lookup is wave-uniform and the loads use an SGPR base plus a
+  // per-lane offset fixed for the whole loop.
+  static_assert(4 * kOpsPerMat == 16, "a wave moves 16 rows per matrix");
+  const bool fast_pages = p.log2_page >= 4;
+  unsigned k_row_off[kOpsPerMat], v_row_off[kOpsPerMat];
+#pragma unroll
+  for (int k = 0; k < kOpsPerMat; ++k) {
+    const int r16 = 4 * k + lrow;  // row within the wave's 16
+    k_row_off[k] = r16 * tok_bytes + ((lchunk ^ (r16 & 15)) << 4);
+    v_row_off[k] = r16 * tok_bytes + ((lchunk ^ (4 * (r16 & 3))) << 4);
+  }
+  // fast-path DMA of tile t, issued in pieces: plan (page lookup) first,
+  // then parts k = 0 .. kOpsPerMat-1 (one K and one V instruction each)
+  struct DmaPlan {
+    const char* kb0;
+    const char* vb0;
+    unsigned st;
+  };
+  auto fast_ok = [&](int t) {
+    return fast_pages && kbeg + t * kKeyTile + 16 * wave + 15 < kend;
+  };
+  auto dma_plan = [&](int t) -> DmaPlan {
+    const int w0 = kbeg + t * kKeyTile + 16 * wave;
+    const int pi = clampi((w0 >> p.log2_page) - lp0, 0, kPageCache - 1);
+    const unsigned pgu = (unsigned)__builtin_amdgcn_readfirstlane(pg_lds[pi]);
+    const size_t off = (size_t)pgu * page_bytes +
+                       (unsigned)(w0 & pmask) * tok_bytes + g * kHeadDim * 2;
+    return DmaPlan{kbase + off, vbase + off,
+                   ring_base + (unsigned)(t % kStages) * kStageBytes};
+  };
+  auto dma_part = [&](const DmaPlan& dp, int k) {
+    const unsigned dst = dp.st + (wave * kOpsPerMat + k) * 1024;
+    dma16_sbase(dp.kb0, k_row_off[k], dst);
+    dma16_sbase(dp.vb0, v_row_off[k], dst + kTileBytes);
+  };
+  auto issue = [&](int t) {
+    const int t0 = kbeg + t * kKeyTile;
+    const unsigned st = ring_base + (unsigned)(t % kStages) * kStageBytes;
+    const int w0 = t0 + 16 * wave;  // first position this wave moves
+    if (fast_pages && w0 + 15 < kend) {
+      const int pi = clampi((w0 >> p.log2_page) - lp0, 0, kPageCache - 1);
+      const unsigned pgu = (unsigned)__builtin_amdgcn_readfirstlane(pg_lds[pi]);
+      const size_t off = (size_t)pgu * page_bytes +
+                         (unsigned)(w0 & pmask) * tok_bytes + g * kHeadDim * 2;
+      const char* kb0 = kbase + off;
+      const char* vb0 = vbase + off;
+#pragma unroll
+      for (int k = 0; k < kOpsPerMat; ++k) {
+        const unsigned dst = st + (wave * kOpsPerMat + k) * 1024;
+        dma16_sbase(kb0, k_row_off[k], dst);
+        dma16_sbase(vb0, v_row_off[k], dst + kTileBytes);
+      }
+      return;
+    }
+    int pg[kOpsPerMat], slot[kOpsPerMat];
+#pragma unroll
+    for (int k = 0; k < kOpsPerMat; ++k) {  // page ids first, one LDS wait
+      const int pos = min(t0 + 4 * (wave * kOpsPerMat + k) + lrow, kend - 1);
+      slot[k] = pos & pmask;
+      pg[k] = pg_lds[clampi((pos >> p.log2_page) - lp0, 0, kPageCache - 1)];
+    }
+#pragma unroll
+    for (int k = 0; k < kOpsPerMat; ++k) {
+      const int i = wave * kOpsPerMat + k;
+      const size_t off = (size_t)(unsigned)pg[k] * page_bytes +
+                         (unsigned)slot[k] * tok_bytes;
+      const unsigned dst = __builtin_amdgcn_readfirstlane(st + i * 1024);
+      dma16(kbase + off + k_lane[k], dst);
+      dma16(vbase + off + v_lane[k], dst + kTileBytes);
+    }
+  };
+
+  // ---- S^T = K Q^T of tile t: all K fragments are read before the
+  // MFMAs so the LDS latency is paid once; 2*QB accumulation chains.
+  auto read_k = [&](int t, bf16x8 (&kf)[2][8]) {
+    const unsigned st = ring_base + (unsigned)(t % kStages) * kStageBytes;
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        kf[kb][kc] = lds_read16(st + kb * 32 * 256 + k_off[kc]);
       }
     }
   };
-  auto store_tile = [&](int buf) {
+  auto qk_part = [&](bf16x8 (&kf)[2][8], f32x16 (&S)[QB][2], int kc0,
+                     int kc1) {
+    if (kc0 == 0) {
 #pragma unroll
-    for (int k = 0; k < kCPT; ++k) {
-      const int c = tid + k * kThreads;
-      const int key = c >> 4, part = c & 15;
-      *reinterpret_cast<u32x4*>(&k_lds[buf][key * kKStride + part * 8]) = kreg[k];
-      *reinterpret_cast<u32x4*>(&v_lds[buf][key * kVStride + part * 8]) = vreg[k];
+      for (int qb = 0; qb < QB; ++qb) {
+        S[qb][0] = f32x16{};
+        S[qb][1] = f32x16{};
+      }
+    }
+#pragma unroll
+    for (int kc = kc0; kc < kc1; ++kc) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          S[qb][kb] = mfma32x32x16(kf[kb][kc], qf[qb][kc], S[qb][kb]);
+        }
+      }
     }
   };
+  auto qk = [&](int t, f32x16 (&S)[QB][2]) {
+    bf16x8 kf[2][8];
+    read_k(t, kf);
+    qk_part(kf, S, 0, 8);
+  };
 
-  f32x16 o[4];
+  // ---- 64-bit allowed-key mask of tile t for a node (tree tiles only)
+  auto tile_allow = [&](int t0, int nd) -> uint64_t {
+    const int nvalid = kend - t0;  // >= 1
+    const int npre = P - t0;
+    uint64_t allow = nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1);
+    const uint64_t pre =
+        npre >= 64 ? ~0ull : (npre <= 0 ? 0ull : ((1ull << npre) - 1));
+    uint64_t tree = 0;
+    if (npre < 64) {
+      const int mrow_lds = (nd - n_lo) * nwin - wlo;
+      const int j0 = t0 - P;  // tree node at tile offset 0 (may be < 0)
+      if (j0 >= 0) {
+        const int w0 = min(j0 >> 6, p.W - 1);
+        const int sh = j0 & 63;
+        tree = mk_lds[clampi(mrow_lds + w0, 0, kMaskCache - 1)] >> sh;
+        if (sh != 0 && w0 + 1 < p.W) {
+          tree |= mk_lds[clampi(mrow_lds + w0 + 1, 0, kMaskCache - 1)]
+                  << (64 - sh);
+        }
+      } else {
+        tree = mk_lds[clampi(mrow_lds, 0, kMaskCache - 1)] << (-j0);
+      }
+    }
+    return allow & (pre | tree);
+  };
+
+  f32x16 o[QB][4];
+  float l_run[QB];  // this lane half's share of the row sum
 #pragma unroll
-  for (int db = 0; db < 4; ++db) o[db] = f32x16{};
-  float m_run = -INFINITY;  // log2 units, equal in both lane halves
-  float l_run = 0.f;        // this lane half's share of the sum
+  for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[qb][db] = f32x16{};
+    l_run[qb] = 0.f;
+  }
   const float c2 = p.scale_log2;
 
-  // per-lane constant part of the transposed V read address
-  const int r16 = lane & 15;
-  const int v_lane_off = (4 * half + (r16 >> 2)) * kVStride +
-                         16 * ((lane >> 4) & 1) + 4 * (r16 & 3);
-
-  const int ntiles = (kend - kbeg + kKeyTile - 1) / kKeyTile;
-  __syncthreads();  // page slice visible
-  load_tile(kbeg);
-  store_tile(0);
-  __syncthreads();
-
-  for (int j = 0; j < ntiles; ++j) {
-    const int t0 = kbeg + j * kKeyTile;
-    const int buf = j & 1;
-    if (j + 1 < ntiles) load_tile(t0 + kKeyTile);
-
-    // ---- S^T = K Q^T : two 32-key blocks x 32 queries
-    f32x16 sc[2];
+  // ---- V^T fragments of tile j
+  auto read_v = [&](int j, bf16x8 (&vf)[2][2][4], int kb0 = 0, int kb1 = 2) {
+    const unsigned st = ring_base + (unsigned)(j % kStages) * kStageBytes;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sc[kb] = f32x16{};
-      const unsigned short* kp =
-          &k_lds[buf][(kb * 32 + col) * kKStride + half * 8];
+    for (int kb = kb0; kb < kb1; ++kb) {
 #pragma unroll
-      for (int kc = 0; kc < 8; ++kc) {
-        sc[kb] = mfma32x32x16(lds_bf16x8(kp + kc * 16), qf[kc], sc[kb]);
-      }
-    }
-
-    // ---- mask: keys past the split end, tree keys not on the path
-    if (t0 + kKeyTile > min(P, kend)) {
-      const int nvalid = kend - t0;  // >= 1
-      const int npre = P - t0;
-      uint64_t allow = nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1);
-      uint64_t pre = npre >= 64 ? ~0ull : (npre <= 0 ? 0ull : ((1ull << npre) - 1));
-      uint64_t tree = 0;
-      if (npre < 64) {
-        const int j0 = t0 - P;  // tree node at tile offset 0 (may be < 0)
-        if (j0 >= 0) {
-          const int w0 = min(j0 >> 6, p.W - 1), sh = j0 & 63;
-          tree = mrow[w0] >> sh;
-          if (sh != 0 && w0 + 1 < p.W) tree |= mrow[w0 + 1] << (64 - sh);
-        } else {
-          tree = mrow[0] << (-j0);
-        }
-      }
-      allow &= (pre | tree);
-      allow >>= 4 * half;
+      for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const int kk = kb * 32 + 8 * (rr >> 2) + (rr & 3);
-          if (!((allow >> kk) & 1)) sc[kb][rr] = -INFINITY;
-        }
-      }
-    }
-
-    // ---- online softmax (base 2, lazy rescale)
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int rr = 0; rr < 16; rr += 2) {
-        tmax = fmaxf(tmax, fmaxf(sc[kb][rr], sc[kb][rr + 1]));
-      }
-    }
-    tmax = fmaxf(tmax, other_half(tmax)) * c2;
-    const bool need = tmax > m_run + kLazyRescale;
-    if (__any(need)) {
-      const float m_new = need ? tmax : m_run;
-      const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] *= alpha;
-    }
-    const float m_ref = (m_run == -INFINITY) ? 0.f : m_run;
-
-    bf16x8 pf[2][2];
-    float ps0 = 0.f, ps1 = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int rr = 0; rr < 16; rr += 2) {
-        const float e0 = fast_exp2(fmaf(sc[kb][rr], c2, -m_ref));
-        const float e1 = fast_exp2(fmaf(sc[kb][rr + 1], c2, -m_ref));
-        ps0 += e0;
-        ps1 += e1;
-        pf[kb][rr >> 3][rr & 7] = (__bf16)e0;
-        pf[kb][rr >> 3][(rr & 7) + 1] = (__bf16)e1;
-      }
-    }
-    l_run += ps0 + ps1;
-
-    // ---- O^T += V^T P^T
-    const unsigned short* vb = &v_lds[buf][v_lane_off];
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const unsigned short* vp = vb + (kb * 32 + hf * 16) * kVStride + db * 32;
-          const s16x4 lo = lds_tr4(vp);
-          const s16x4 hi = lds_tr4(vp + 8 * kVStride);
-          const bf16x8 vf = __builtin_bit_cast(
+        for (int db = 0; db < 4; ++db) {
+          const unsigned va = st + v_off[db] + (kb * 32 + hf * 16) * 256;
+          const s16x4 lo = lds_read_tr(va);
+          const s16x4 hi = lds_read_tr(va + 8 * 256);
+          vf[kb][hf][db] = __builtin_bit_cast(
               bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          o[db] = mfma32x32x16(vf, pf[kb][hf], o[db]);
         }
       }
     }
+  };
 
-    if (j + 1 < ntiles) store_tile(buf ^ 1);
+  // ---- probabilities of a tile against the reference max m_ref (log2
+  // units); adds their fp32 sum to l_run
+  float m_ref[QB];
+  auto exps = [&](f32x16 (&S)[QB][2], bf16x8 (&pf)[QB][2][2], int kb0 = 0,
+                  int kb1 = 2) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float mu = (m_ref[qb] == -INFINITY) ? 0.f : m_ref[qb];
+      float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+      for (int kb = kb0; kb < kb1; ++kb) {
+#pragma unroll
+        for (int rr = 0; rr < 16; rr += 2) {
+          const float e0 = fast_exp2(fmaf(S[qb][kb][rr], c2, -mu));
+          const float e1 = fast_exp2(fmaf(S[qb][kb][rr + 1], c2, -mu));
+          ps0 += e0;
+          ps1 += e1;
+          pf[qb][kb][rr >> 3][rr & 7] = (__bf16)e0;
+          pf[qb][kb][rr >> 3][(rr & 7) + 1] = (__bf16)e1;
+        }
+      }
+      l_run[qb] += ps0 + ps1;
+    }
+  };
+
+  // ---- reference max for a tile: raised (lazily) when the tile's max
+  // exceeds the current one by more than kLazyRescale; alpha rescales the
+  // accumulated O and l.  Returns whether any row changed its reference.
+  auto next_ref = [&](f32x16 (&S)[QB][2], float (&m_new)[QB],
+                      float (&alpha)[QB]) -> bool {
+    bool any_need = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      // IEEE maximum (v_maximum3_f32): no NaN canonicalisation of inputs
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int rr = 0; rr < 16; rr += 2) {
+          tmax = __builtin_elementwise_maximum(
+              tmax, __builtin_elementwise_maximum(S[qb][kb][rr],
+                                                  S[qb][kb][rr + 1]));
+        }
+      }
+      tmax = __builtin_elementwise_maximum(tmax, other_half(tmax)) * c2;
+      const bool need = tmax > m_ref[qb] + kLazyRescale;
+      m_new[qb] = need ? tmax : m_ref[qb];
+      alpha[qb] = need ? fast_exp2(m_ref[qb] - m_new[qb]) : 1.f;
+      any_need |= need;
+    }
+    return any_need;
+  };
+
+  // ---- O^T += V^T P^T: 4*QB independent accumulation chains
+  auto pv = [&](bf16x8 (&vf)[2][2][4], bf16x8 (&pf)[QB][2][2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            o[qb][db] = mfma32x32x16(vf[kb][hf][db], pf[qb][kb][hf], o[qb][db]);
+          }
+        }
+      }
+    }
+  };
+
+  // ---- one pipeline step over tile j.  Tile j's scores (masked, with
+  // their reference max m_ref) were computed in the previous step.  In
+  // branch-free blocks: S^T of tile j+1 on the matrix core while the
+  // vector ALU exponentiates tile j; then PV of tile j while the ALU finds
+  // tile j+1's max.  The rare rescale of O comes last.  After the last
+  // tile the S^T is computed on stale LDS data and dropped.
+  //
+  // With dma_inbody the DMA of tile j+3 is issued from inside the step, in
+  // two bursts between segments: issuing it all right after the barrier
+  // makes the four waves queue 32 instructions at the CU's address unit at
+  // once and stall for it.
+  auto body = [&](int j, f32x16 (&Scur)[QB][2], f32x16 (&Snext)[QB][2],
+                  bool mask_next, bool dma_inbody, float (&m_new)[QB],
+                  float (&alpha)[QB]) -> bool {
+    bf16x8 kf[2][8];
+    bf16x8 vf[2][2][4];
+    bf16x8 pf[QB][2][2];
+    DmaPlan dp{};
+    if (dma_inbody) dp = dma_plan(j + kStages - 1);
+    read_k(j + 1, kf);
+    // segment 1: S^T MFMAs kc 0..3, V^T reads and probabilities of keys 0..31
+    qk_part(kf, Snext, 0, 4);
+    read_v(j, vf, 0, 1);
+    exps(Scur, pf, 0, 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+#pragma unroll
+    for (int i = 0; i < 8 * QB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    }
+    if (dma_inbody) {
+      __builtin_amdgcn_sched_barrier(0);
+      dma_part(dp, 0);
+      dma_part(dp, 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // segment 2: S^T MFMAs kc 4..7, keys 32..63
+    qk_part(kf, Snext, 4, 8);
+    read_v(j, vf, 1, 2);
+    exps(Scur, pf, 1, 2);
+#pragma unroll
+    for (int i = 0; i < 8 * QB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    }
+    if (dma_inbody) {
+      __builtin_amdgcn_sched_barrier(0);
+      dma_part(dp, 2);
+      dma_part(dp, 3);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // segment 3: PV of tile j, max of tile j+1
+    pv(vf, pf);
+    if (mask_next) {
+      const int t1 = kbeg + (j + 1) * kKeyTile;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        apply_tile_mask(Snext[qb], tile_allow(t1, node[qb]), half);
+      }
+    }
+    const bool r = next_ref(Snext, m_new, alpha);
+#pragma unroll
+    for (int i = 0; i < 16 * QB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    }
+    return r;
+  };
+  auto step = [&](int j, f32x16 (&Scur)[QB][2], f32x16 (&Snext)[QB][2]) {
+    if (j + 1 < ntiles) {
+      // tile j+1 must have landed; tile j+2 may still be in flight
+      if (j + 2 < ntiles) wait_vmcnt<kOps>();
+      else wait_vmcnt<0>();
+    }
     __syncthreads();
-  }
+    const int t1 = kbeg + (j + 1) * kKeyTile;
+    float m_new[QB], alpha[QB];
+    bool r;
+    const bool has_next_dma = j + kStages - 1 < ntiles;
+    if (j + 1 < ntiles && t1 + kKeyTile > min(P, kend)) {
+      if (has_next_dma) issue(j + kStages - 1);
+      r = body(j, Scur, Snext, true, false, m_new, alpha);
+    } else if (has_next_dma && fast_ok(j + kStages - 1)) {
+      r = body(j, Scur, Snext, false, true, m_new, alpha);
+    } else {
+      if (has_next_dma) issue(j + kStages - 1);
+      r = body(j, Scur, Snext, false, false, m_new, alpha);
+    }
+    if (j + 1 >= ntiles) {  // the scores past the last tile are not data
+      r = false;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) m_new[qb] = m_ref[qb];
+    }
+    if (__any(r)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        l_run[qb] *= alpha[qb];
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[qb][db] *= alpha[qb];
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) m_ref[qb] = m_new[qb];
+  };
 
-  const float l_tot = l_run + other_half(l_run);
-  if (!rvalid) return;
-  if (p.splits == 1) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    __bf16* op = p.out + qrow * kHeadDim;
+  // Make the compiler wait for the Q loads here, before the first DMA:
+  // its own wait at the first use of qf would also drain the ring.
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
+  for (int qb = 0; qb < QB; ++qb) {
+    asm volatile("" :: "v"(qf[qb][0]), "v"(qf[qb][1]), "v"(qf[qb][2]),
+                 "v"(qf[qb][3]), "v"(qf[qb][4]), "v"(qf[qb][5]),
+                 "v"(qf[qb][6]), "v"(qf[qb][7]));
+  }
+  __syncthreads();  // page slice and mask window visible
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        bf16x4 v4;
+  for (int t = 0; t < kStages - 1; ++t) {
+    if (t < ntiles) issue(t);
+  }
+  // wait for tile 0: later tiles may stay in flight
+  if (ntiles >= 3) wait_vmcnt<2 * kOps>();
+  else if (ntiles == 2) wait_vmcnt<kOps>();
+  else wait_vmcnt<0>();
+  __syncthreads();
+  f32x16 SA[QB][2], SB[QB][2];
+  qk(0, SA);
+  if (kbeg + kKeyTile > min(P, kend)) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(o[db][g4 * 4 + e] * inv);
-        *reinterpret_cast<bf16x4*>(op + db * 32 + g4 * 8 + half * 4) = v4;
+    for (int qb = 0; qb < QB; ++qb) {
+      apply_tile_mask(SA[qb], tile_allow(kbeg, node[qb]), half);
+    }
+  }
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) m_ref[qb] = -INFINITY;
+  {
+    float m_new[QB], alpha[QB];
+    next_ref(SA, m_new, alpha);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) m_ref[qb] = m_new[qb];
+  }
+  // unrolled by the ring depth so that every stage index is a constant
+  for (int i = 0; 4 * i < ntiles; ++i) {
+    const int j = 4 * i;
+    step(j, SA, SB);
+    if (j + 1 < ntiles) step(j + 1, SB, SA);
+    if (j + 2 < ntiles) step(j + 2, SA, SB);
+    if (j + 3 < ntiles) step(j + 3, SB, SA);
+  }
+  float m_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) m_run[qb] = m_ref[qb];
+
+  // ---- epilogue
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float l_tot = l_run[qb] + other_half(l_run[qb]);
+    if (!rvalid[qb]) continue;
+    if (p.splits == 1) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      __bf16* op = p.out + qrow[qb] * kHeadDim;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          bf16x4 v4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v4[e] = (__bf16)(o[qb][db][g4 * 4 + e] * inv);
+          }
+          *reinterpret_cast<bf16x4*>(op + db * 32 + g4 * 8 + half * 4) = v4;
+        }
       }
-    }
-    if (half == 0) {
-      p.lse[qrow] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
-    }
-  } else {
-    const size_t prow = (size_t)split * p.N * p.Hq + qrow;
-    float* pp = p.part_o + prow * kHeadDim;
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        f32x4 v4 = {o[db][g4 * 4 + 0], o[db][g4 * 4 + 1], o[db][g4 * 4 + 2],
-                    o[db][g4 * 4 + 3]};
-        *reinterpret_cast<f32x4*>(pp + db * 32 + g4 * 8 + half * 4) = v4;
+      if (half == 0) {
+        p.lse[qrow[qb]] =
+            l_tot > 0.f ? (m_run[qb] + log2f(l_tot)) * kLn2 : -INFINITY;
       }
-    }
-    if (half == 0) {
-      *reinterpret_cast<f32x2*>(p.part_ml + prow * 2) = f32x2{m_run, l_tot};
+    } else {
+      const size_t prow = (size_t)split * p.N * p.Hq + qrow[qb];
+      float* pp = p.part_o + prow * kHeadDim;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          f32x4 v4 = {o[qb][db][g4 * 4 + 0], o[qb][db][g4 * 4 + 1],
+                      o[qb][db][g4 * 4 + 2], o[qb][db][g4 * 4 + 3]};
+          *reinterpret_cast<f32x4*>(pp + db * 32 + g4 * 8 + half * 4) = v4;
+        }
+      }
+      if (half == 0) {
+        *reinterpret_cast<f32x2*>(p.part_ml + prow * 2) =
+            f32x2{m_run[qb], l_tot};
+      }
     }
   }
 }

@@ -20,6 +20,9 @@ constexpr int kAbiVersion = 2;
 constexpr int kMaxDevices = 64;
 constexpr int kMaxSplits = 256;
 constexpr int kMinKeysPerSplit = 256;
+// The two-block (64 queries per wave) variant exceeds the register file
+// with the current schedule; one 32-query block per wave is used.
+constexpr bool kUseTwoQueryBlocks = false;
 
 std::atomic<int> g_cu_count[kMaxDevices];
 std::atomic<int> g_mask_lds[kMaxDevices];  // dynamic LDS limit already set
@@ -53,7 +56,7 @@ int ilog2(int x) {
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct Plan {
-  int nw = 8;        // waves per workgroup (32 rows each)
+  int nw = 8;        // 32-row query blocks per workgroup (4 waves)
   int mblocks = 0;   // row blocks per (sequence, kv head)
   int splits = 1;    // key-range splits
   int chunk = 0;     // keys per split (multiple of the 64-key tile)
@@ -64,22 +67,30 @@ struct Plan {
 
 // Launch planning from host-side bounds only (no device-to-host copy).
 // Row blocks: 256 rows (8 waves) when a (sequence, kv head) pair has more
-// than 128 rows, else 128 rows (4 waves, two workgroups per CU).  The key
-// range [0, max_prefix_len + max_nodes) is cut into splits so that the
-// grid fills every workgroup slot once, with at least 256 keys per split,
-// and each split's page-table slice fits the kernel's LDS page cache.
+// than 128 rows, else 128 rows (4 waves); either way one workgroup fills a
+// CU's LDS.  The key range [0, max_prefix_len + max_nodes) is cut into
+// splits so that the grid offers about one workgroup per CU, with at least
+// 256 keys per split, and each split's page-table slice fits the kernel's
+// LDS page cache.
 int make_plan(int S, int N, int Hq, int Hkv, int max_prefix_len,
               int max_nodes, int page_size, int req_splits, int cus,
               Plan* out) {
   Plan pl;
   const int G = Hq / Hkv;
   const long long rows = (long long)G * max_nodes;
-  pl.nw = rows > 128 ? 8 : 4;
+  // Two 32-query blocks per wave (256 rows per workgroup) when there are
+  // enough rows and the ancestor-mask words of such a block (at most
+  // 256/G + 1 nodes) fit the kernel's LDS cache; else one (128 rows, at
+  // most 129 nodes x 16 words, which always fits).
+  const long long mask_words = (max_nodes + 63) / 64;
+  const long long nodes8 = (8 * 32 + G - 1) / G + 1;
+  pl.nw = (kUseTwoQueryBlocks && rows > 128 && nodes8 * mask_words <= kMaskCache)
+              ? 8 : 4;
   const int rows_per_wg = 32 * pl.nw;
   pl.mblocks = (int)std::max(1LL, (rows + rows_per_wg - 1) / rows_per_wg);
   const long long T = std::max(1LL, (long long)max_prefix_len + max_nodes);
   const long long units0 = (long long)S * Hkv * pl.mblocks;
-  const long long slots = (long long)cus * (pl.nw == 8 ? 1 : 2);
+  const long long slots = cus;
   const long long max_chunk =
       std::max<long long>(kKeyTile, ((long long)(kPageCache - 1) * page_size) /
                                         kKeyTile * kKeyTile);
@@ -279,11 +290,7 @@ int tree_attn_verify(const void* q, const void* k_cache, const void* v_cache,
 
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const unsigned grid = 8u * (unsigned)fp.per_xcd;
-  if (pl.nw == 8) {
-    hipLaunchKernelGGL(attn_fwd_kernel<8>, dim3(grid), dim3(8 * 64), 0, hs, fp);
-  } else {
-    hipLaunchKernelGGL(attn_fwd_kernel<4>, dim3(grid), dim3(4 * 64), 0, hs, fp);
-  }
+  hipLaunchKernelGGL(attn_fwd_kernel<1>, dim3(grid), dim3(256), 0, hs, fp);
   if (hipGetLastError() != hipSuccess) return TREE_ATTN_ERR_HIP;
 
   if (pl.splits > 1) {
