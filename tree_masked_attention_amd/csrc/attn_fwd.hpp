@@ -651,8 +651,42 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) m_ref[qb] = m_new[qb];
   }
-  // unrolled by the ring depth so that every stage index is a constant
-  for (int i = 0; 4 * i < ntiles; ++i) {
+  // Hot steps: tile j+1 lies wholly in the prefix and tile j+3 is a full
+  // tile on the fast DMA path.  They run in a loop of their own, so that
+  // its code holds no branch between step variants (a join of variants
+  // makes the compiler copy the accumulators between registers).
+  auto hot_step = [&](int j, f32x16 (&Scur)[QB][2], f32x16 (&Snext)[QB][2]) {
+    wait_vmcnt<kOps>();
+    __syncthreads();
+    float m_new[QB], alpha[QB];
+    const bool r = body(j, Scur, Snext, false, true, m_new, alpha);
+    if (__any(r)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        l_run[qb] *= alpha[qb];
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[qb][db] *= alpha[qb];
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) m_ref[qb] = m_new[qb];
+  };
+  int n_hot = 0;
+  if (fast_pages) {
+    const int last = min((kend - kbeg) / kKeyTile - kStages,
+                         (P - kbeg) / kKeyTile - 2);
+    n_hot = max(last + 1, 0) & ~(kStages - 1);
+  }
+  // both loops are unrolled by the ring depth and start at a multiple of
+  // it, so that every stage index is a constant
+  for (int i = 0; 4 * i < n_hot; ++i) {
+    const int j = 4 * i;
+    hot_step(j, SA, SB);
+    hot_step(j + 1, SB, SA);
+    hot_step(j + 2, SA, SB);
+    hot_step(j + 3, SB, SA);
+  }
+  for (int i = n_hot / 4; 4 * i < ntiles; ++i) {
     const int j = 4 * i;
     step(j, SA, SB);
     if (j + 1 < ntiles) step(j + 1, SB, SA);
