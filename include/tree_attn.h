@@ -101,7 +101,7 @@ int tree_attn_build_mask(const int32_t* parents, const int32_t* tree_offsets,
  * needs for these sizes (0 when the planned launch needs none).
  * Arguments as for tree_attn_verify.  num_splits: 0 lets the library plan
  * the split of the key range; n > 0 asks for n splits, clamped to what the
- * key range allows (at least 64 keys per split, at most 1023 pages per
+ * key range allows (at least 64 keys per split, at most 1039 pages per
  * split, at most 256 splits).  Returns 0 for invalid sizes as well.
  */
 size_t tree_attn_workspace_size(int32_t num_seqs, int32_t total_nodes,
@@ -109,6 +109,20 @@ size_t tree_attn_workspace_size(int32_t num_seqs, int32_t total_nodes,
                                 int32_t head_dim, int32_t max_prefix_len,
                                 int32_t max_nodes, int32_t page_size,
                                 int32_t num_splits);
+
+/*
+ * tree_attn_describe_plan - the launch tree_attn_verify would make for
+ * these sizes, for tests and benchmarks.  Arguments as for
+ * tree_attn_workspace_size; info is a host array of 4 int32 that receives
+ * { waves per workgroup (4 or 8), splits of the key range, keys per split,
+ *   workgroups launched }.  Returns TREE_ATTN_OK, or the status
+ * tree_attn_verify would return for these sizes (info untouched).
+ */
+int tree_attn_describe_plan(int32_t num_seqs, int32_t total_nodes,
+                            int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t max_prefix_len,
+                            int32_t max_nodes, int32_t page_size,
+                            int32_t num_splits, int32_t* info);
 
 /*
  * tree_attn_verify - tree-causal verification attention over a paged

@@ -106,3 +106,24 @@ def test_workspace_size_rules():
     # tiny pages force more splits (each split's page slice is bounded)
     assert api.workspace_size(1, 16, 8, 2, 128, 5000, 16, 1, 1) >= \
         5 * 16 * 8 * (128 + 2) * 4
+
+
+def test_describe_plan():
+    # small work: four waves; the key range is split to fill the CUs
+    p = api.describe_plan(1, 16, 8, 2, 128, 256, 16, 16, 0)
+    assert p["waves"] == 4 and p["splits"] >= 1
+    assert p["chunk"] % 64 == 0 and p["chunk"] * p["splits"] >= 256 + 16
+    # 1024 rows per kv head and one long split: eight waves
+    p = api.describe_plan(4, 1024, 32, 8, 128, 32768, 256, 16, 0)
+    assert p["waves"] == 8 and p["splits"] == 2
+    assert p["workgroups"] == 4 * 8 * 4 * 2
+    # short splits of the same rows stay on four waves
+    p = api.describe_plan(1, 256, 32, 8, 128, 4096, 256, 16, 0)
+    assert p["waves"] == 4
+    # forced split count is honoured, clamped by the key range
+    p = api.describe_plan(1, 64, 16, 4, 128, 6000, 64, 16, 1)
+    assert p["splits"] == 1 and p["waves"] == 8 and p["chunk"] >= 6064
+    with pytest.raises(ValueError):
+        api.describe_plan(1, 16, 8, 3, 128, 256, 16, 16, 0)
+    with pytest.raises(NotImplementedError):
+        api.describe_plan(1, 16, 8, 2, 64, 256, 16, 16, 0)

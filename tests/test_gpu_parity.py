@@ -92,6 +92,46 @@ def test_small_case_parity(name):
     assert_parity(got, ref_out, ref_lse, name)
 
 
+# Cases sized so that the planner takes the eight-wave kernel (at least
+# 256 query rows per kv head and at least 4096 keys per split).
+EIGHT_WAVE_CASES = {
+    "w8-ragged": (lambda: _case("w8-ragged", 140,
+                                prefix_lens=[4100, 4500, 6000],
+                                tree_sizes=[70, 1, 130], num_q_heads=16,
+                                num_kv_heads=4), 1),
+    "w8-page8": (lambda: _case("w8-page8", 141, prefix_lens=[4200],
+                               tree_sizes=[64], page_size=8), 1),
+    "w8-page4-slow-dma": (lambda: _case("w8-page4", 142, prefix_lens=[4000],
+                                        tree_sizes=[96], page_size=4), 1),
+    "w8-five-mask-words": (lambda: _case("w8-wide", 143, prefix_lens=[4000],
+                                         tree_sizes=[300], num_q_heads=2,
+                                         num_kv_heads=2), 1),
+    "w8-two-splits": (lambda: _case("w8-2s", 144, prefix_lens=[9000, 8300],
+                                    tree_sizes=[64, 90], num_q_heads=16,
+                                    num_kv_heads=4), 2),
+    "w8-chain": (lambda: _case("w8-chain", 145, prefix_lens=[4500],
+                               tree_sizes=[128], tree_rules="chain"), 1),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EIGHT_WAVE_CASES))
+def test_eight_wave_parity(name):
+    import tree_masked_attention_amd.api as api
+    make, splits = EIGHT_WAVE_CASES[name]
+    wl = make()
+    plan = api.describe_plan(wl.num_seqs, wl.total_nodes, wl.num_q_heads,
+                             wl.num_kv_heads, wl.head_dim,
+                             wl.max_prefix_len, wl.max_nodes, wl.page_size,
+                             splits)
+    say(f"[gpu] eight-wave case {name}: P={list(wl.prefix_lens)} "
+        f"B={list(wl.tree_sizes)} page={wl.page_size} plan={plan}")
+    assert plan["waves"] == 8
+    got = run_gpu(wl, num_splits=splits)
+    assert np.array_equal(got["masks"], oracle.workload_masks(wl))
+    ref_out, ref_lse = oracle.workload_attention(wl)
+    assert_parity(got, ref_out, ref_lse, name)
+
+
 @pytest.mark.parametrize("splits", [1, 2, 5, 64])
 def test_forced_splits_parity(splits):
     wl = _case("splits", 120, prefix_lens=[1000, 64, 2500],

@@ -6,7 +6,8 @@ inputs.  The binding is loaded on first use of one of its names, so the
 input generator can be imported on machines without the built library.
 """
 
-_API_NAMES = ("build_mask", "verify", "workspace_size", "status_string",
+_API_NAMES = ("build_mask", "verify", "workspace_size", "describe_plan",
+              "status_string",
               "abi_version", "mask_words_for", "TreeAttnError")
 
 

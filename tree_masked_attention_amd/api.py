@@ -41,9 +41,12 @@ _lib.tree_attn_verify.argtypes = (
     [_p, _p, _p, _p, _i, _i, _i, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i,
      ctypes.c_float, _i, _p, _p, _p, ctypes.c_size_t, _p])
 
+_lib.tree_attn_describe_plan.restype = ctypes.c_int
+_lib.tree_attn_describe_plan.argtypes = [_i] * 9 + [_p]
+
 EXPORTED = ("tree_attn_status_string", "tree_attn_abi_version",
             "tree_attn_build_mask", "tree_attn_workspace_size",
-            "tree_attn_verify")
+            "tree_attn_describe_plan", "tree_attn_verify")
 
 
 class TreeAttnError(RuntimeError):
@@ -134,6 +137,22 @@ def workspace_size(num_seqs: int, total_nodes: int, num_q_heads: int,
     return int(_lib.tree_attn_workspace_size(
         num_seqs, total_nodes, num_q_heads, num_kv_heads, head_dim,
         max_prefix_len, max_nodes, page_size, num_splits))
+
+
+def describe_plan(num_seqs: int, total_nodes: int, num_q_heads: int,
+                  num_kv_heads: int, head_dim: int, max_prefix_len: int,
+                  max_nodes: int, page_size: int = 16,
+                  num_splits: int = 0) -> dict:
+    """The launch verify() makes for these sizes: waves per workgroup,
+    splits of the key range, keys per split, workgroups."""
+    info = (ctypes.c_int32 * 4)()
+    code = _lib.tree_attn_describe_plan(
+        num_seqs, total_nodes, num_q_heads, num_kv_heads, head_dim,
+        max_prefix_len, max_nodes, page_size, num_splits,
+        ctypes.cast(info, ctypes.c_void_p))
+    _raise(code, "tree_attn_describe_plan")
+    return {"waves": info[0], "splits": info[1], "chunk": info[2],
+            "workgroups": info[3]}
 
 
 def verify(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

@@ -28,7 +28,8 @@
 // consecutive keys of one register run.
 //
 // Memory pipeline.  K/V tiles of 64 keys (16 KB each) flow through a
-// 4-stage LDS ring filled by global_load_lds_dwordx4: the load unit writes
+// 4-stage LDS ring (K tiles of all stages, then V tiles) filled by
+// global_load_lds_dwordx4: the load unit writes
 // each lane's 16 bytes straight to LDS (lane l of an instruction lands at
 // M0 + 16*l), so no registers stage the data.  The loads are issued from
 // inline assembly and waited for with explicit vmcnt counts, because the
@@ -80,8 +81,12 @@ struct FwdParams {
 constexpr int kKeyTile = 64;
 constexpr int kStages = 4;
 constexpr int kTileBytes = kKeyTile * kHeadDim * 2;   // 16 KB per matrix
-constexpr int kStageBytes = 2 * kTileBytes;           // K then V
-constexpr int kPageCache = 1024;                      // page ids per split
+constexpr int kStageBytes = 2 * kTileBytes;           // K and V of a tile
+// The ring holds the K tiles of all stages in its first half and the V
+// tiles in its second, so that every operand offset of a stage fits the
+// 16-bit immediate of an LDS instruction.
+constexpr int kVOff = kStages * kTileBytes;
+constexpr int kPageCache = 1040;                      // page ids per split
 constexpr int kMaskCache = 2304;                      // mask words per WG
 constexpr float kLazyRescale = 8.f;                   // log2 units
 
@@ -152,7 +157,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(FwdParams p) {
   constexpr int kRowsPerWG = NW * kRowsPerWave;
   constexpr int kOpsPerMat = 16 / NW;        // 1-KB DMA ops per wave per matrix
   constexpr int kOps = 2 * kOpsPerMat;       // per wave per tile
-  __shared__ __align__(1024) unsigned char ring[kStages * kStageBytes];
+  __shared__ __align__(1024) unsigned char ring[2 * kVOff];
   __shared__ int pg_lds[kPageCache];
   __shared__ uint64_t mk_lds[kMaskCache];
 
@@ -252,7 +257,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(FwdParams p) {
   unsigned v_off[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
-    v_off[db] = kTileBytes + (4 * half + y) * 256 +
+    v_off[db] = kVOff + (4 * half + y) * 256 +
                 ((4 * (db ^ y) + x) << 4) + 8 * (lane & 1);
   }
 
@@ -303,16 +308,16 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(FwdParams p) {
     const size_t off = (size_t)pgu * page_bytes +
                        (unsigned)(w0 & pmask) * tok_bytes + g * kHeadDim * 2;
     return DmaPlan{kbase + off, vbase + off,
-                   ring_base + (unsigned)(t % kStages) * kStageBytes};
+                   ring_base + (unsigned)(t % kStages) * kTileBytes};
   };
   auto dma_part = [&](const DmaPlan& dp, int k) {
     const unsigned dst = dp.st + (wave * kOpsPerMat + k) * 1024;
     dma16_sbase(dp.kb0, k_row_off[k], dst);
-    dma16_sbase(dp.vb0, v_row_off[k], dst + kTileBytes);
+    dma16_sbase(dp.vb0, v_row_off[k], dst + kVOff);
   };
   auto issue = [&](int t) {
     const int t0 = kbeg + t * kKeyTile;
-    const unsigned st = ring_base + (unsigned)(t % kStages) * kStageBytes;
+    const unsigned st = ring_base + (unsigned)(t % kStages) * kTileBytes;
     const int w0 = t0 + 16 * wave;  // first position this wave moves
     if (fast_pages && w0 + 15 < kend) {
       const int pi = clampi((w0 >> p.log2_page) - lp0, 0, kPageCache - 1);
@@ -325,7 +330,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(FwdParams p) {
       for (int k = 0; k < kOpsPerMat; ++k) {
         const unsigned dst = st + (wave * kOpsPerMat + k) * 1024;
         dma16_sbase(kb0, k_row_off[k], dst);
-        dma16_sbase(vb0, v_row_off[k], dst + kTileBytes);
+        dma16_sbase(vb0, v_row_off[k], dst + kVOff);
       }
       return;
     }
@@ -343,25 +348,25 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(FwdParams p) {
                          (unsigned)slot[k] * tok_bytes;
       const unsigned dst = __builtin_amdgcn_readfirstlane(st + i * 1024);
       dma16(kbase + off + k_lane[k], dst);
-      dma16(vbase + off + v_lane[k], dst + kTileBytes);
+      dma16(vbase + off + v_lane[k], dst + kVOff);
     }
   };
 
-  // ---- S^T = K Q^T of tile t: all K fragments are read before the
-  // MFMAs so the LDS latency is paid once; 2*QB accumulation chains.
-  auto read_k = [&](int t, bf16x8 (&kf)[2][8]) {
-    const unsigned st = ring_base + (unsigned)(t % kStages) * kStageBytes;
+  // ---- S^T = K Q^T of tile t, in two halves of the head dimension
+  // (kc = 4h .. 4h+3) so that only half of the K fragments are live at a
+  // time; 2*QB accumulation chains.
+  auto read_k_half = [&](int t, int h, bf16x8 (&kf)[2][4]) {
+    const unsigned st = ring_base + (unsigned)(t % kStages) * kTileBytes;
 #pragma unroll
-    for (int kc = 0; kc < 8; ++kc) {
+    for (int c = 0; c < 4; ++c) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        kf[kb][kc] = lds_read16(st + kb * 32 * 256 + k_off[kc]);
+        kf[kb][c] = lds_read16(st + kb * 32 * 256 + k_off[4 * h + c]);
       }
     }
   };
-  auto qk_part = [&](bf16x8 (&kf)[2][8], f32x16 (&S)[QB][2], int kc0,
-                     int kc1) {
-    if (kc0 == 0) {
+  auto qk_half = [&](bf16x8 (&kf)[2][4], f32x16 (&S)[QB][2], int h) {
+    if (h == 0) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         S[qb][0] = f32x16{};
@@ -369,20 +374,22 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(FwdParams p) {
       }
     }
 #pragma unroll
-    for (int kc = kc0; kc < kc1; ++kc) {
+    for (int c = 0; c < 4; ++c) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-          S[qb][kb] = mfma32x32x16(kf[kb][kc], qf[qb][kc], S[qb][kb]);
+          S[qb][kb] = mfma32x32x16(kf[kb][c], qf[qb][4 * h + c], S[qb][kb]);
         }
       }
     }
   };
   auto qk = [&](int t, f32x16 (&S)[QB][2]) {
-    bf16x8 kf[2][8];
-    read_k(t, kf);
-    qk_part(kf, S, 0, 8);
+    bf16x8 kf0[2][4], kf1[2][4];
+    read_k_half(t, 0, kf0);
+    read_k_half(t, 1, kf1);
+    qk_half(kf0, S, 0);
+    qk_half(kf1, S, 1);
   };
 
   // ---- 64-bit allowed-key mask of tile t for a node (tree tiles only)
@@ -423,7 +430,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(FwdParams p) {
 
   // ---- V^T fragments of tile j
   auto read_v = [&](int j, bf16x8 (&vf)[2][2][4], int kb0 = 0, int kb1 = 2) {
-    const unsigned st = ring_base + (unsigned)(j % kStages) * kStageBytes;
+    const unsigned st = ring_base + (unsigned)(j % kStages) * kTileBytes;
 #pragma unroll
     for (int kb = kb0; kb < kb1; ++kb) {
 #pragma unroll
@@ -524,21 +531,23 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(FwdParams p) {
   auto body = [&](int j, f32x16 (&Scur)[QB][2], f32x16 (&Snext)[QB][2],
                   bool mask_next, bool dma_inbody, float (&m_new)[QB],
                   float (&alpha)[QB]) -> bool {
-    bf16x8 kf[2][8];
+    bf16x8 kf0[2][4], kf1[2][4];
     bf16x8 vf[2][2][4];
     bf16x8 pf[QB][2][2];
     DmaPlan dp{};
     if (dma_inbody) dp = dma_plan(j + kStages - 1);
-    read_k(j + 1, kf);
-    // segment 1: S^T MFMAs kc 0..3, V^T reads and probabilities of keys 0..31
-    qk_part(kf, Snext, 0, 4);
+    read_k_half(j + 1, 0, kf0);
+    // segment 1: S^T MFMAs kc 0..3; the other K half, V^T of keys 0..31
+    // and their probabilities are loaded and computed beside them
+    qk_half(kf0, Snext, 0);
+    read_k_half(j + 1, 1, kf1);
     read_v(j, vf, 0, 1);
     exps(Scur, pf, 0, 1);
-    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
     for (int i = 0; i < 8 * QB; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 24 / (8 * QB), 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
     }
     if (dma_inbody) {
@@ -548,13 +557,13 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(FwdParams p) {
       __builtin_amdgcn_sched_barrier(0);
     }
     // segment 2: S^T MFMAs kc 4..7, keys 32..63
-    qk_part(kf, Snext, 4, 8);
+    qk_half(kf1, Snext, 1);
     read_v(j, vf, 1, 2);
     exps(Scur, pf, 1, 2);
 #pragma unroll
     for (int i = 0; i < 8 * QB; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 16 / (8 * QB), 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
     }
     if (dma_inbody) {

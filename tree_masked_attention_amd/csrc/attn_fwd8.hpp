@@ -1,0 +1,463 @@
+// Eight-wave variant of the split-KV tree-verification attention kernel,
+// for (sequence, kv head) pairs with at least 256 query rows.
+//
+// Same operation, data layout, MFMA mapping, LDS ring format and pipeline
+// as the four-wave kernel (attn_fwd.hpp), with eight waves of 32 query
+// rows (256 rows per workgroup), two waves per SIMD.  Each K/V tile staged
+// in LDS then serves twice the rows, and two waves share every SIMD: the
+// vector ALU of a SIMD issues about twice as many instructions per cycle
+// (and the exponential about three times as many) when two waves feed it,
+// and one wave's matrix instructions run while the other's softmax does.
+// Each wave still overlaps its own S^T MFMAs of tile j+1 with the softmax
+// of tile j.  The register budget is 256 per wave, so scores are built one
+// 32-key block at a time and the K/V operands are read from LDS a quarter
+// tile at a time.
+#pragma once
+
+#include "attn_fwd.hpp"
+
+namespace tree_attn {
+
+constexpr int kRowsPerWG8 = 256;
+
+__global__ __launch_bounds__(512, 1) void attn_fwd8_kernel(FwdParams p) {
+  constexpr int NW = 8;
+  constexpr int kThreads = NW * 64;
+  constexpr int kOpsPerMat = 16 / NW;  // 1-KB DMA ops per wave per matrix
+  constexpr int kOps = 2 * kOpsPerMat;
+  static_assert(kOps == 4, "the vmcnt immediates below assume 4 ops");
+  __shared__ __align__(1024) unsigned char ring[2 * kVOff];
+  __shared__ int pg_lds[kPageCache];
+  __shared__ uint64_t mk_lds[kMaskCache];
+
+  // XCD-aware decode, as in the four-wave kernel
+  const int bid = blockIdx.x;
+  int L = (bid & 7) * p.per_xcd + (bid >> 3);
+  if (L >= p.units) return;
+  const int mb = L % p.mblocks;
+  L /= p.mblocks;
+  const int split = L % p.splits;
+  L /= p.splits;
+  const int g = L % p.Hkv;
+  const int s = L / p.Hkv;
+
+  const int a = clampi(p.tree_offsets[s], 0, p.N);
+  const int b = clampi(p.tree_offsets[s + 1], a, p.N);
+  const int B = b - a;
+  const int P = max(p.prefix_lens[s], 0);
+  const int rows = p.G * B;
+  const int r0 = mb * kRowsPerWG8;
+  if (r0 >= rows) return;
+  const int T = min(P + B, p.max_tokens);
+  const int kbeg = split * p.chunk;
+  if (kbeg >= T) return;
+  const int kend = min(T, kbeg + p.chunk);
+  const int n = (kend - kbeg + kKeyTile - 1) / kKeyTile;  // tiles, >= 1
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
+  const int lane = tid & 63;
+  const int col = lane & 31, half = lane >> 5;
+
+  // ---- page-table slice and ancestor-mask window -> LDS
+  const int lp0 = kbeg >> p.log2_page;
+  {
+    const int npg = min(((kend - 1) >> p.log2_page) - lp0 + 1, kPageCache);
+    const int* ptab = p.page_table + (size_t)s * p.max_pps + lp0;
+    for (int i = tid; i < npg; i += kThreads) {
+      pg_lds[i] = clampi(ptab[i], 0, p.num_pages - 1);
+    }
+  }
+  const int n_lo = r0 / p.G;
+  const int n_hi = (min(r0 + kRowsPerWG8, rows) - 1) / p.G;
+  const int nnodes = n_hi - n_lo + 1;
+  const bool has_tree = kend > P;
+  const int wlo = has_tree ? (max(kbeg, P) - P) >> 6 : 0;
+  const int whi = has_tree ? min(p.W - 1, ((kend - 1 - P) >> 6) + 1) : 0;
+  const int nwin = whi - wlo + 1;
+  if (has_tree) {
+    const int nm = min(nnodes * nwin, kMaskCache);
+    for (int i = tid; i < nm; i += kThreads) {
+      const int nn = i / nwin, w = i - nn * nwin;
+      mk_lds[i] = p.masks[(size_t)(a + n_lo + nn) * p.W + wlo + w];
+    }
+  }
+
+  // ---- this lane's query row
+  const int r = r0 + wave * 32 + col;
+  const bool rvalid = r < rows;
+  const int node = rvalid ? r / p.G : n_hi;
+  const size_t qrow =
+      (size_t)(a + node) * p.Hq + g * p.G + (rvalid ? r % p.G : 0);
+  bf16x8 qf[8];
+  {
+    const __bf16* qp = p.q + qrow * kHeadDim + half * 8;
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) {
+      u32x4 raw = rvalid ? *reinterpret_cast<const u32x4*>(qp + kc * 16)
+                         : u32x4{0, 0, 0, 0};
+      qf[kc] = __builtin_bit_cast(bf16x8, raw);
+    }
+  }
+
+  // ---- LDS operand addresses (stage 0; the stage offset is added per tile)
+  const unsigned ring_base =
+      (unsigned)(size_t)(__attribute__((address_space(3))) unsigned char*)ring;
+  unsigned k_off[8];
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) {
+    k_off[kc] = ring_base + col * 256 + (((2 * kc + half) ^ (col & 15)) << 4);
+  }
+  const int y = (lane & 15) >> 2;
+  const int x = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  unsigned v_off[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    v_off[db] = ring_base + kVOff + (4 * half + y) * 256 +
+                ((4 * (db ^ y) + x) << 4) + 8 * (lane & 1);
+  }
+
+  // ---- DMA of one tile: wave w moves rows 8w .. 8w+7 of K and of V, as
+  // kOpsPerMat instructions of 4 rows (lane l: row 4k + l/16, chunk l%16).
+  const int pmask = (1 << p.log2_page) - 1;
+  const unsigned tok_bytes = (unsigned)p.Hkv * kHeadDim * 2;
+  const unsigned page_bytes = tok_bytes << p.log2_page;
+  const int lrow = lane >> 4, lchunk = lane & 15;
+  const char* kbase = reinterpret_cast<const char*>(p.k);
+  const char* vbase = reinterpret_cast<const char*>(p.v);
+  // fast path: the wave's 8 rows lie in one page (pages of >= 8 tokens)
+  const bool fast_pages = p.log2_page >= 3;
+  unsigned k_row_off[kOpsPerMat], v_row_off[kOpsPerMat];
+#pragma unroll
+  for (int k = 0; k < kOpsPerMat; ++k) {
+    const int r8 = 4 * k + lrow;
+    const int row = 8 * wave + r8;  // row within the tile
+    k_row_off[k] = r8 * tok_bytes + ((lchunk ^ (row & 15)) << 4);
+    v_row_off[k] = r8 * tok_bytes + ((lchunk ^ (4 * (row & 3))) << 4);
+  }
+  auto issue_fast = [&](int t) {  // full tile, pages of >= 8 tokens
+    const unsigned st = ring_base + (unsigned)(t & (kStages - 1)) * kTileBytes;
+    const int w0 = kbeg + t * kKeyTile + 8 * wave;
+    const int pi = clampi((w0 >> p.log2_page) - lp0, 0, kPageCache - 1);
+    const unsigned pgu = (unsigned)__builtin_amdgcn_readfirstlane(pg_lds[pi]);
+    const size_t off = (size_t)pgu * page_bytes +
+                       (unsigned)(w0 & pmask) * tok_bytes + g * kHeadDim * 2;
+#pragma unroll
+    for (int k = 0; k < kOpsPerMat; ++k) {
+      const unsigned dst = st + (wave * kOpsPerMat + k) * 1024;
+      dma16_sbase(kbase + off, k_row_off[k], dst);
+      dma16_sbase(vbase + off, v_row_off[k], dst + kVOff);
+    }
+  };
+  auto issue = [&](int t) {
+    const int t0 = kbeg + t * kKeyTile;
+    const unsigned st = ring_base + (unsigned)(t & (kStages - 1)) * kTileBytes;
+    const int w0 = t0 + 8 * wave;
+    if (fast_pages && w0 + 7 < kend) {
+      const int pi = clampi((w0 >> p.log2_page) - lp0, 0, kPageCache - 1);
+      const unsigned pgu =
+          (unsigned)__builtin_amdgcn_readfirstlane(pg_lds[pi]);
+      const size_t off = (size_t)pgu * page_bytes +
+                         (unsigned)(w0 & pmask) * tok_bytes + g * kHeadDim * 2;
+#pragma unroll
+      for (int k = 0; k < kOpsPerMat; ++k) {
+        const unsigned dst = st + (wave * kOpsPerMat + k) * 1024;
+        dma16_sbase(kbase + off, k_row_off[k], dst);
+        dma16_sbase(vbase + off, v_row_off[k], dst + kVOff);
+      }
+      return;
+    }
+    int pg[kOpsPerMat], slot[kOpsPerMat];
+#pragma unroll
+    for (int k = 0; k < kOpsPerMat; ++k) {
+      const int pos = min(w0 + 4 * k + lrow, kend - 1);
+      slot[k] = pos & pmask;
+      pg[k] = pg_lds[clampi((pos >> p.log2_page) - lp0, 0, kPageCache - 1)];
+    }
+#pragma unroll
+    for (int k = 0; k < kOpsPerMat; ++k) {
+      const int row = 8 * wave + 4 * k + lrow;
+      const size_t off = (size_t)(unsigned)pg[k] * page_bytes +
+                         (unsigned)slot[k] * tok_bytes + g * kHeadDim * 2;
+      const unsigned dst = st + (wave * kOpsPerMat + k) * 1024;
+      dma16(kbase + off + ((lchunk ^ (row & 15)) << 4), dst);
+      dma16(vbase + off + ((lchunk ^ (4 * (row & 3))) << 4), dst + kVOff);
+    }
+  };
+
+  // ---- 64-bit allowed-key mask of tile t (first key t0) for this node
+  auto tile_allow = [&](int t0) -> uint64_t {
+    const int nvalid = kend - t0;
+    const int npre = P - t0;
+    uint64_t allow = nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1);
+    const uint64_t pre =
+        npre >= 64 ? ~0ull : (npre <= 0 ? 0ull : ((1ull << npre) - 1));
+    uint64_t tree = 0;
+    if (npre < 64) {
+      const int mrow_lds = (node - n_lo) * nwin - wlo;
+      const int j0 = t0 - P;
+      if (j0 >= 0) {
+        const int w0 = min(j0 >> 6, p.W - 1);
+        const int sh = j0 & 63;
+        tree = mk_lds[clampi(mrow_lds + w0, 0, kMaskCache - 1)] >> sh;
+        if (sh != 0 && w0 + 1 < p.W) {
+          tree |= mk_lds[clampi(mrow_lds + w0 + 1, 0, kMaskCache - 1)]
+                  << (64 - sh);
+        }
+      } else {
+        tree = mk_lds[clampi(mrow_lds, 0, kMaskCache - 1)] << (-j0);
+      }
+    }
+    return allow & (pre | tree);
+  };
+
+  f32x16 o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) o[db] = f32x16{};
+  float l_run = 0.f;          // this lane half's share of the row sum
+  float m_ref = -INFINITY;    // reference max, log2 units
+  const float c2 = p.scale_log2;
+
+  // ---- LDS operand reads.  K fragments of key block kb, head-dim chunks
+  // kc = 4h .. 4h+3; V^T fragments of key block kb, 16-key half hf.
+  auto read_kq = [&](int t, int kb, int h, bf16x8 (&kf)[4]) {
+    const unsigned so = (unsigned)(t & (kStages - 1)) * kTileBytes;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      kf[c] = lds_read16(k_off[4 * h + c] + so + kb * 32 * 256);
+    }
+  };
+  auto read_vq = [&](int t, int kb, int hf, bf16x8 (&vf)[4]) {
+    const unsigned so = (unsigned)(t & (kStages - 1)) * kTileBytes;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const unsigned va = v_off[db] + so + (kb * 32 + hf * 16) * 256;
+      const s16x4 lo = lds_read_tr(va);
+      const s16x4 hi = lds_read_tr(va + 8 * 256);
+      vf[db] = __builtin_bit_cast(
+          bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+  // S^T of key block kb of tile t: one accumulation chain over the head
+  // dimension, K fragments streamed a quarter tile at a time
+  auto qk_block = [&](int t, int kb, f32x16& Sk) {
+    bf16x8 kf0[4], kf1[4];
+    read_kq(t, kb, 0, kf0);
+    read_kq(t, kb, 1, kf1);
+    Sk = f32x16{};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) Sk = mfma32x32x16(kf0[c], qf[c], Sk);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) Sk = mfma32x32x16(kf1[c], qf[4 + c], Sk);
+  };
+  // O^T += V^T P^T over key block kb of tile t (4 accumulation chains)
+  auto pv_block = [&](int t, int kb, const bf16x8 (&pk)[2]) {
+    bf16x8 vf0[4], vf1[4];
+    read_vq(t, kb, 0, vf0);
+    read_vq(t, kb, 1, vf1);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[db] = mfma32x32x16(vf0[db], pk[0], o[db]);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[db] = mfma32x32x16(vf1[db], pk[1], o[db]);
+  };
+  // probabilities of key block kb against m_ref; adds their fp32 sum
+  auto exps_block = [&](const f32x16& Sk, bf16x8 (&pk)[2]) {
+    const float mu = (m_ref == -INFINITY) ? 0.f : m_ref;
+    float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+    for (int rr = 0; rr < 16; rr += 2) {
+      const float e0 = fast_exp2(fmaf(Sk[rr], c2, -mu));
+      const float e1 = fast_exp2(fmaf(Sk[rr + 1], c2, -mu));
+      ps0 += e0;
+      ps1 += e1;
+      pk[rr >> 3][rr & 7] = (__bf16)e0;
+      pk[rr >> 3][(rr & 7) + 1] = (__bf16)e1;
+    }
+    l_run += ps0 + ps1;
+  };
+  // reference max for a tile (lazy raise, as in the four-wave kernel)
+  auto next_ref = [&](const f32x16 (&Sx)[2], float& m_new, float& alpha) {
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int rr = 0; rr < 16; rr += 2) {
+        tmax = __builtin_elementwise_maximum(
+            tmax, __builtin_elementwise_maximum(Sx[kb][rr], Sx[kb][rr + 1]));
+      }
+    }
+    tmax = __builtin_elementwise_maximum(tmax, other_half(tmax)) * c2;
+    const bool need = tmax > m_ref + kLazyRescale;
+    m_new = need ? tmax : m_ref;
+    alpha = need ? fast_exp2(m_ref - m_new) : 1.f;
+    return need;
+  };
+
+  // ---- one pipeline step over tile j.  Tile j's scores Scur (masked, with
+  // reference max m_ref) come from the previous step; this step computes
+  // the scores of tile j+1 on the matrix core while the vector ALU turns
+  // Scur into probabilities, then PV of tile j while the ALU finds tile
+  // j+1's max.  The scores are built one 32-key block at a time, so that
+  // only one and a half score tiles are live.  After the last tile the
+  // scores are computed on stale LDS data and dropped.
+  auto body = [&](int j, f32x16 (&Scur)[2], f32x16 (&Snext)[2],
+                  bool mask_next, float& m_new, float& alpha) -> bool {
+    bf16x8 pf[2][2];
+    // segment 1: S^T(j+1) keys 0..31 | probabilities of keys 0..31
+    qk_block(j + 1, 0, Snext[0]);
+    exps_block(Scur[0], pf[0]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+    }
+    // segment 2: S^T(j+1) keys 32..63, PV(j) keys 0..31 | probabilities
+    // of keys 32..63
+    qk_block(j + 1, 1, Snext[1]);
+    pv_block(j, 0, pf[0]);
+    exps_block(Scur[1], pf[1]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    }
+    // segment 3: PV(j) keys 32..63 | max of tile j+1
+    pv_block(j, 1, pf[1]);
+    if (mask_next) {
+      apply_tile_mask(Snext, tile_allow(kbeg + (j + 1) * kKeyTile), half);
+    }
+    return next_ref(Snext, m_new, alpha);
+  };
+  auto finish = [&](bool r, float m_new, float alpha) {
+    if (__any(r)) {
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] *= alpha;
+    }
+    m_ref = m_new;
+  };
+  auto step = [&](int j, f32x16 (&Scur)[2], f32x16 (&Snext)[2]) {
+    if (j + 1 < n) {
+      // tile j+1 must have landed; tile j+2 may still be in flight
+      if (j + 2 < n) wait_vmcnt<kOps>();
+      else wait_vmcnt<0>();
+    }
+    __syncthreads();
+    if (j + kStages - 1 < n) issue(j + kStages - 1);
+    float m_new, alpha;
+    bool r;
+    if (j + 1 < n && kbeg + (j + 2) * kKeyTile > min(P, kend)) {
+      r = body(j, Scur, Snext, true, m_new, alpha);
+    } else {
+      r = body(j, Scur, Snext, false, m_new, alpha);
+    }
+    if (j + 1 >= n) {  // the scores past the last tile are not data
+      r = false;
+      m_new = m_ref;
+    }
+    finish(r, m_new, alpha);
+  };
+  // hot steps: tile j+1 pure prefix, tile j+3 a full tile on the fast path
+  auto hot_step = [&](int j, f32x16 (&Scur)[2], f32x16 (&Snext)[2]) {
+    wait_vmcnt<kOps>();
+    __syncthreads();
+    issue_fast(j + kStages - 1);
+    float m_new, alpha;
+    const bool r = body(j, Scur, Snext, false, m_new, alpha);
+    finish(r, m_new, alpha);
+  };
+
+  // Make the compiler wait for the Q loads before the first DMA (its own
+  // wait at the first use of qf would also drain the ring).
+  asm volatile("" :: "v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]),
+               "v"(qf[4]), "v"(qf[5]), "v"(qf[6]), "v"(qf[7]));
+  __syncthreads();  // page slice and mask window visible
+#pragma unroll
+  for (int t = 0; t < kStages - 1; ++t) {
+    if (t < n) issue(t);
+  }
+  if (n >= 3) wait_vmcnt<2 * kOps>();
+  else if (n == 2) wait_vmcnt<kOps>();
+  else wait_vmcnt<0>();
+  __syncthreads();
+  f32x16 SA[2], SB[2];
+  qk_block(0, 0, SA[0]);
+  qk_block(0, 1, SA[1]);
+  if (kbeg + kKeyTile > min(P, kend)) {
+    apply_tile_mask(SA, tile_allow(kbeg), half);
+  }
+  {
+    float m_new, alpha;
+    next_ref(SA, m_new, alpha);
+    m_ref = m_new;
+  }
+  int n_hot = 0;
+  if (fast_pages) {
+    const int last = min((kend - kbeg) / kKeyTile - kStages,
+                         (P - kbeg) / kKeyTile - 2);
+    n_hot = max(last + 1, 0) & ~(kStages - 1);
+  }
+  // both loops are unrolled by the ring depth and start at a multiple of
+  // it, so that every stage offset is a constant
+  for (int i = 0; 4 * i < n_hot; ++i) {
+    const int j = 4 * i;
+    hot_step(j, SA, SB);
+    hot_step(j + 1, SB, SA);
+    hot_step(j + 2, SA, SB);
+    hot_step(j + 3, SB, SA);
+  }
+  for (int i = n_hot / 4; 4 * i < n; ++i) {
+    const int j = 4 * i;
+    step(j, SA, SB);
+    if (j + 1 < n) step(j + 1, SB, SA);
+    if (j + 2 < n) step(j + 2, SA, SB);
+    if (j + 3 < n) step(j + 3, SB, SA);
+  }
+
+  // ---- epilogue
+  const float l_tot = l_run + other_half(l_run);
+  if (!rvalid) return;
+  if (p.splits == 1) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    __bf16* op = p.out + qrow * kHeadDim;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        bf16x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(o[db][g4 * 4 + e] * inv);
+        *reinterpret_cast<bf16x4*>(op + db * 32 + g4 * 8 + half * 4) = v4;
+      }
+    }
+    if (half == 0) {
+      p.lse[qrow] = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+  } else {
+    const size_t prow = (size_t)split * p.N * p.Hq + qrow;
+    float* pp = p.part_o + prow * kHeadDim;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        f32x4 v4 = {o[db][g4 * 4 + 0], o[db][g4 * 4 + 1], o[db][g4 * 4 + 2],
+                    o[db][g4 * 4 + 3]};
+        *reinterpret_cast<f32x4*>(pp + db * 32 + g4 * 8 + half * 4) = v4;
+      }
+    }
+    if (half == 0) {
+      *reinterpret_cast<f32x2*>(p.part_ml + prow * 2) = f32x2{m_ref, l_tot};
+    }
+  }
+}
+
+}  // namespace tree_attn

@@ -8,6 +8,7 @@
 #include <cmath>
 
 #include "attn_fwd.hpp"
+#include "attn_fwd8.hpp"
 #include "attn_merge.hpp"
 #include "common.hpp"
 #include "mask_build.hpp"
@@ -16,13 +17,12 @@ using namespace tree_attn;
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 constexpr int kMaxDevices = 64;
 constexpr int kMaxSplits = 256;
 constexpr int kMinKeysPerSplit = 256;
-// The two-block (64 queries per wave) variant exceeds the register file
-// with the current schedule; one 32-query block per wave is used.
-constexpr bool kUseTwoQueryBlocks = false;
+// keys per workgroup from which the eight-wave kernel is used
+constexpr int kMinKeysPerWG8 = 4096;
 
 std::atomic<int> g_cu_count[kMaxDevices];
 std::atomic<int> g_mask_lds[kMaxDevices];  // dynamic LDS limit already set
@@ -78,39 +78,57 @@ int make_plan(int S, int N, int Hq, int Hkv, int max_prefix_len,
   Plan pl;
   const int G = Hq / Hkv;
   const long long rows = (long long)G * max_nodes;
-  // Two 32-query blocks per wave (256 rows per workgroup) when there are
-  // enough rows and the ancestor-mask words of such a block (at most
-  // 256/G + 1 nodes) fit the kernel's LDS cache; else one (128 rows, at
-  // most 129 nodes x 16 words, which always fits).
-  const long long mask_words = (max_nodes + 63) / 64;
-  const long long nodes8 = (8 * 32 + G - 1) / G + 1;
-  pl.nw = (kUseTwoQueryBlocks && rows > 128 && nodes8 * mask_words <= kMaskCache)
-              ? 8 : 4;
-  const int rows_per_wg = 32 * pl.nw;
-  pl.mblocks = (int)std::max(1LL, (rows + rows_per_wg - 1) / rows_per_wg);
   const long long T = std::max(1LL, (long long)max_prefix_len + max_nodes);
-  const long long units0 = (long long)S * Hkv * pl.mblocks;
-  const long long slots = cus;
   const long long max_chunk =
       std::max<long long>(kKeyTile, ((long long)(kPageCache - 1) * page_size) /
                                         kKeyTile * kKeyTile);
   const long long min_splits = (T + max_chunk - 1) / max_chunk;
-  long long splits;
-  if (req_splits > 0) {
-    splits = req_splits;
-  } else {
-    splits = (slots + units0 - 1) / std::max(1LL, units0);
-    splits = std::min(splits, std::max(1LL, T / kMinKeysPerSplit));
+  // Splits of the key range so that the work units fill the CUs (or the
+  // requested count), each a whole number of 64-key tiles.
+  long long splits = 0, chunk = 0, units0 = 0;
+  auto choose = [&](int nw) -> int {
+    const int rows_per_wg = 32 * nw;
+    pl.nw = nw;
+    pl.mblocks = (int)std::max(1LL, (rows + rows_per_wg - 1) / rows_per_wg);
+    units0 = (long long)S * Hkv * pl.mblocks;
+    if (req_splits > 0) {
+      splits = req_splits;
+    } else {
+      splits = (cus + units0 - 1) / std::max(1LL, units0);
+      splits = std::min(splits, std::max(1LL, T / kMinKeysPerSplit));
+    }
+    splits = std::max(std::max(1LL, splits), min_splits);
+    if (splits > kMaxSplits) {
+      if (min_splits > kMaxSplits) return TREE_ATTN_ERR_UNSUPPORTED;
+      splits = kMaxSplits;
+    }
+    chunk = (T + splits - 1) / splits;
+    chunk = (chunk + kKeyTile - 1) / kKeyTile * kKeyTile;
+    chunk = std::min(chunk, max_chunk);
+    splits = (T + chunk - 1) / chunk;
+    return TREE_ATTN_OK;
+  };
+  // Eight waves (256 rows per workgroup, two waves per SIMD) pay off on
+  // long key ranges per workgroup; they need 256 rows and the ancestor-mask
+  // words of such a block (at most 256/G + 1 nodes) in the kernel's LDS
+  // cache.  Else four waves (128 rows; at most 129 nodes x 16 words, which
+  // always fits).
+  const long long mask_words = (max_nodes + 63) / 64;
+  const long long nodes8 = (kRowsPerWG8 + G - 1) / G + 1;
+  const bool can8 = rows >= kRowsPerWG8 && nodes8 * mask_words <= kMaskCache;
+  int nw = 4;
+  if (can8) {
+    const int st = choose(8);
+    if (st != TREE_ATTN_OK) return st;
+    if (chunk >= kMinKeysPerWG8) nw = 8;
   }
-  splits = std::max(std::max(1LL, splits), min_splits);
-  if (splits > kMaxSplits) {
-    if (min_splits > kMaxSplits) return TREE_ATTN_ERR_UNSUPPORTED;
-    splits = kMaxSplits;
+#ifdef TREE_ATTN_FORCE_NW  // build-time override for tuning runs
+  if (TREE_ATTN_FORCE_NW == 4 || can8) nw = TREE_ATTN_FORCE_NW;
+#endif
+  {
+    const int st = choose(nw);
+    if (st != TREE_ATTN_OK) return st;
   }
-  long long chunk = (T + splits - 1) / splits;
-  chunk = (chunk + kKeyTile - 1) / kKeyTile * kKeyTile;
-  chunk = std::min(chunk, max_chunk);
-  splits = (T + chunk - 1) / chunk;
   pl.splits = (int)splits;
   pl.chunk = (int)chunk;
   const long long units = units0 * splits;
@@ -216,6 +234,30 @@ size_t tree_attn_workspace_size(int32_t num_seqs, int32_t total_nodes,
   return pl.ws_bytes;
 }
 
+int tree_attn_describe_plan(int32_t num_seqs, int32_t total_nodes,
+                            int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t max_prefix_len,
+                            int32_t max_nodes, int32_t page_size,
+                            int32_t num_splits, int32_t* info) {
+  if (info == nullptr) return TREE_ATTN_ERR_NULL;
+  int st = check_sizes(num_seqs, total_nodes, num_q_heads, num_kv_heads,
+                       head_dim, max_prefix_len, max_nodes);
+  if (st != TREE_ATTN_OK) return st;
+  if (num_splits < 0 || !is_pow2(page_size) || page_size > 4096) {
+    return TREE_ATTN_ERR_SHAPE;
+  }
+  Plan pl;
+  st = make_plan(num_seqs, total_nodes, num_q_heads, num_kv_heads,
+                 max_prefix_len, max_nodes, page_size, num_splits, cu_count(),
+                 &pl);
+  if (st != TREE_ATTN_OK) return st;
+  info[0] = pl.nw;
+  info[1] = pl.splits;
+  info[2] = pl.chunk;
+  info[3] = 8 * ((pl.units + 7) / 8);
+  return TREE_ATTN_OK;
+}
+
 int tree_attn_verify(const void* q, const void* k_cache, const void* v_cache,
                      const int32_t* page_table, int32_t max_pages_per_seq,
                      int32_t num_pages, int32_t page_size,
@@ -290,7 +332,11 @@ int tree_attn_verify(const void* q, const void* k_cache, const void* v_cache,
 
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const unsigned grid = 8u * (unsigned)fp.per_xcd;
-  hipLaunchKernelGGL(attn_fwd_kernel<1>, dim3(grid), dim3(256), 0, hs, fp);
+  if (pl.nw == 8) {
+    hipLaunchKernelGGL(attn_fwd8_kernel, dim3(grid), dim3(512), 0, hs, fp);
+  } else {
+    hipLaunchKernelGGL(attn_fwd_kernel<1>, dim3(grid), dim3(256), 0, hs, fp);
+  }
   if (hipGetLastError() != hipSuccess) return TREE_ATTN_ERR_HIP;
 
   if (pl.splits > 1) {
