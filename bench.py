@@ -43,7 +43,62 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run plain 512 MiB device copies (the "
+                         "reference kernel for scaling HBM byte counters)")
     return ap.parse_args()
+
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "hbm_traffic.txt")
+
+
+def kernel_source_hash():
+    """Hash of the HIP sources: HBM counters taken on other sources are
+    not reported."""
+    import hashlib
+    csrc = os.path.join(HERE, "tree_masked_attention_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per verify launch from the committed counter summary,
+    when it was taken on the current sources; else None."""
+    try:
+        lines = open(TRAFFIC_FILE).read().splitlines()
+    except OSError:
+        return None
+    src = kernel_source_hash()
+    for ln in lines:
+        f = ln.split()
+        if len(f) < 4 or f[0] != workload:
+            continue
+        kv = dict(x.split("=", 1) for x in f[1:] if "=" in x)
+        if kv.get("sources") != src:
+            return None
+        try:
+            return float(kv["bytes_per_launch"])
+        except (KeyError, ValueError):
+            return None
+    return None
+
+
+def copy_calibration(torch):
+    dev = torch.device("cuda:0")
+    n = 512 << 20
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n,
+                      "launches": 5}), flush=True)
+    return 0
 
 
 # --------------------------------------------------------------------------
@@ -124,6 +179,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        return copy_calibration(torch)
 
     log(f"[bench] drawing workload {args.workload}")
     wl = standard_workload(args.workload)
@@ -220,6 +277,12 @@ def main():
     log(f"[bench] step {ms_per_step * 1e3:.1f} us; mask build "
         f"{mask_ms * 1e3:.1f} us; verify {ver_ms * 1e3:.1f} us")
 
+    plan = api.describe_plan(S, N, Hq, wl.num_kv_heads, d, wl.max_prefix_len,
+                             wl.max_nodes, wl.page_size, args.splits)
+    kname = ("attn_fwd8_kernel" if plan["waves"] == 8
+             else "attn_fwd_kernel<1>")
+    if plan["splits"] > 1:
+        kname += " + attn_merge_kernel"
     value = N / (ms_per_step * 1e-3)
     v_s = ver_ms * 1e-3
     if bound == "hbm":
@@ -249,17 +312,18 @@ def main():
             "tree_nodes_per_seq": int(wl.max_nodes),
             "q_heads": Hq, "kv_heads": wl.num_kv_heads, "head_dim": d,
             "page_size": wl.page_size,
-            "splits": args.splits or "planned",
+            "splits_requested": args.splits or "planned",
+            "plan": plan,
             "input_copies_rotated": copies,
         },
         "roofline": {
             "bound": bound,
-            "kernel": "tree_attn_verify (attn_fwd_kernel + attn_merge_kernel)",
+            "kernel": f"tree_attn_verify ({kname})",
             "achieved": achieved,
             "peak": peak,
             "unit": unit,
             "frac": achieved / peak,
-            "traffic": None,
+            "traffic": measured_traffic(wl.name),
             "alg_bytes_per_launch": alg_bytes,
             "alg_flops_per_launch": alg_flops,
             "avg_launch_us": ver_ms * 1e3,
