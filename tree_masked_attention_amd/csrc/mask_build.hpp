@@ -1,18 +1,23 @@
-// Ancestor-or-self bitmasks of draft trees by pointer jumping.
+// Ancestor-or-self bitmasks of draft trees.
 //
 // Rule implemented: a tree node attends to its ancestors (JETFLOW,
 // gist.science 2606.18394, section 2 "Arquitectura Central", tree-causal
 // attention mask), the root-to-node path including the node itself.
+// Nodes come in topological order (parent[i] < i), so every ancestor of i
+// has a smaller index.
 //
-// One workgroup per sequence, one thread per node.  Instead of walking each
-// node's path (up to B dependent steps), node i keeps its set A_i (W words,
-// in registers) and a jump pointer J_i.  Initially A_i = {i} and
-// J_i = parent(i).  A round publishes every (A_i, J_i) to LDS and then sets
-//     A_i <- A_i | A_{J_i}        J_i <- J_{J_i}
-// so after r rounds A_i holds the ancestors within distance < 2^r and J_i
-// is the ancestor at distance 2^r (or -1).  At most ceil(log2 B) rounds
-// are needed; the loop stops as soon as every jump pointer is -1.
-// Ancestors of i have indices <= i, so only words 0 .. i/64 can be set.
+// One workgroup per sequence, one thread per node, one wave per chunk of 64
+// consecutive nodes (chunk c = nodes 64c .. 64c+63, mask word c).
+//  1. Inside a wave, pointer jumping over the in-chunk part of each path,
+//     with cross-lane reads (ds_bpermute) and no barrier: node i keeps
+//     loc_i (its ancestor-or-self bits inside its own chunk), J_i (an
+//     in-chunk ancestor not yet merged, or -1) and E_i (its nearest ancestor
+//     in an earlier chunk, or -1; final once J_i = -1).  A round sets
+//     loc_i |= loc_{J_i}, E_i = E_{J_i}, J_i = J_{J_i}; six rounds cover 64.
+//  2. loc and E of every node go to LDS (one barrier).  Word w of node i's
+//     mask is then loc_i for w = c, zero for w > c, and for w < c the loc of
+//     the node where the chain E_i, E_{E_i}, ... passes through chunk w
+//     (each step of that chain lands in a strictly earlier chunk), or zero.
 #pragma once
 
 #include "common.hpp"
@@ -22,14 +27,16 @@ namespace tree_attn {
 constexpr int kMaskThreads = 1024;  // = largest supported tree
 constexpr int kMaskMaxWords = 16;
 
-// LDS: sets [max_nodes][W] u64 followed by jump [max_nodes] int32.
+__device__ __forceinline__ int lane_read(int v, int src_lane) {
+  return __builtin_amdgcn_ds_bpermute(src_lane << 2, v);
+}
+
 __global__ __launch_bounds__(kMaskThreads) void build_mask_kernel(
     const int32_t* __restrict__ parents, const int32_t* __restrict__ offsets,
     int num_seqs, int total_nodes, int max_nodes, int W,
     uint64_t* __restrict__ masks, int32_t* __restrict__ bad_node) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  uint64_t* sets = reinterpret_cast<uint64_t*>(smem);
-  int* jump = reinterpret_cast<int*>(sets + (size_t)max_nodes * W);
+  __shared__ uint64_t loc_lds[kMaskThreads];
+  __shared__ int ext_lds[kMaskThreads];
   __shared__ int first_bad;
 
   const int s = blockIdx.x;
@@ -41,48 +48,56 @@ __global__ __launch_bounds__(kMaskThreads) void build_mask_kernel(
   if (i == 0) first_bad = (b - a > cap) ? cap : 0x7fffffff;
   __syncthreads();
 
+  const int lane = i & 63;
+  const int c0 = i & ~63;  // first node of this wave's chunk
   const bool mine = i < B;
-  uint64_t my[kMaskMaxWords];
-  int jp = -1;
+  int p = -1;
   if (mine) {
-    const int p = parents[a + i];
-    const bool ok = (p >= -1) && (p < i);
-    if (!ok) atomicMin(&first_bad, i);
-    jp = ok ? p : -1;
-  }
-#pragma unroll
-  for (int w = 0; w < kMaskMaxWords; ++w) {
-    my[w] = (mine && w == (i >> 6)) ? (uint64_t(1) << (i & 63)) : uint64_t(0);
+    p = parents[a + i];
+    if (!(p >= -1 && p < i)) {  // not topological: report, treat as a root
+      atomicMin(&first_bad, i);
+      p = -1;
+    }
   }
 
-  for (int round = 0; round < 11; ++round) {
-    if (mine) {
-#pragma unroll
-      for (int w = 0; w < kMaskMaxWords; ++w) {
-        if (w < W && w <= (i >> 6)) sets[i * W + w] = my[w];
-      }
-      jump[i] = jp;
+  // 1. in-chunk pointer jumping
+  uint64_t loc = mine ? (1ull << lane) : 0ull;
+  int J = (p >= c0) ? p - c0 : -1;
+  int E = (p >= 0 && p < c0) ? p : -1;
+  for (int r = 0; r < 6 && __any(J >= 0); ++r) {
+    const int src = J >= 0 ? J : lane;
+    const unsigned lo = (unsigned)lane_read((int)(unsigned)loc, src);
+    const unsigned hi = (unsigned)lane_read((int)(unsigned)(loc >> 32), src);
+    const int J2 = lane_read(J, src);
+    const int E2 = lane_read(E, src);
+    if (J >= 0) {
+      loc |= ((uint64_t)hi << 32) | lo;
+      E = E2;
+      J = J2;
     }
-    // barrier that also tells every thread whether any pointer is left
-    if (!__syncthreads_or(jp >= 0)) break;
-    if (jp >= 0) {
-#pragma unroll
-      for (int w = 0; w < kMaskMaxWords; ++w) {
-        if (w < W && w <= (jp >> 6)) my[w] |= sets[jp * W + w];
-      }
-      jp = jump[jp];
-    }
-    __syncthreads();
   }
+  loc_lds[i] = loc;
+  ext_lds[i] = E;
+  __syncthreads();
 
+  // 2. words of the row, highest first, following the chain of exits
   if (mine) {
-#pragma unroll
-    for (int w = 0; w < kMaskMaxWords; ++w) {
-      if (w < W) masks[(size_t)(a + i) * W + w] = my[w];
+    const int c = i >> 6;
+    uint64_t* row = masks + (size_t)(a + i) * W;
+    int e = E;
+    for (int w = W - 1; w >= 0; --w) {
+      uint64_t v = 0;
+      if (w == c) {
+        v = loc;
+      } else if (w < c && e >= 0 && (e >> 6) == w) {
+        v = loc_lds[e];
+        e = ext_lds[e];
+      }
+      row[w] = v;
     }
   }
   // rows past the handled part of an oversized tree are zeroed
-  for (int e = B * W + i; e < (b - a) * W; e += kMaskThreads) {
+  for (int e = B * W + i; e < (b - a) * W; e += blockDim.x) {
     masks[(size_t)a * W + e] = 0;
   }
   __syncthreads();
