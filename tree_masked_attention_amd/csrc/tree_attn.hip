@@ -25,7 +25,6 @@ constexpr int kMinKeysPerSplit = 256;
 constexpr int kMinKeysPerWG8 = 4096;
 
 std::atomic<int> g_cu_count[kMaxDevices];
-std::atomic<int> g_mask_lds[kMaxDevices];  // dynamic LDS limit already set
 
 // Compute units of the current device (queried once per device).
 int cu_count() {
@@ -192,25 +191,12 @@ int tree_attn_build_mask(const int32_t* parents, const int32_t* tree_offsets,
   if (total_nodes > 0 && (!parents || !masks)) return TREE_ATTN_ERR_NULL;
 
   const int cap = std::max(1, max_nodes);
-  const size_t lds = (size_t)cap * mask_words * sizeof(uint64_t) +
-                     (size_t)cap * sizeof(int);
+  // one thread per node of the largest tree, whole waves
+  const int threads = std::min(kMaskThreads, (cap + 63) / 64 * 64);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return TREE_ATTN_ERR_HIP;
-  if (dev < 0 || dev >= kMaxDevices ||
-      g_mask_lds[dev].load(std::memory_order_relaxed) < (int)lds) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&build_mask_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)lds) != hipSuccess) {
-      return TREE_ATTN_ERR_HIP;
-    }
-    if (dev >= 0 && dev < kMaxDevices) {
-      g_mask_lds[dev].store((int)lds, std::memory_order_relaxed);
-    }
-  }
-  hipLaunchKernelGGL(build_mask_kernel, dim3(num_seqs), dim3(kMaskThreads),
-                     lds, st, parents, tree_offsets, num_seqs, total_nodes,
-                     cap, (int)mask_words, masks, bad_node);
+  hipLaunchKernelGGL(build_mask_kernel, dim3(num_seqs), dim3(threads), 0, st,
+                     parents, tree_offsets, num_seqs, total_nodes, cap,
+                     (int)mask_words, masks, bad_node);
   return hipGetLastError() == hipSuccess ? TREE_ATTN_OK : TREE_ATTN_ERR_HIP;
 }
 
