@@ -6,8 +6,9 @@
 //     out = sum_c w_c O_c / sum_c w_c l_c,
 //     lse = ln2 * (m* + log2 sum_c w_c l_c).
 // A split in which the row saw no allowed key has m_c = -inf, l_c = 0 and
-// contributes nothing.  One wave per (node, head) row; each lane owns two
-// of the 128 output columns.
+// contributes nothing.  The sums are accumulated with a running maximum,
+// which gives the same values up to rounding order.  Each lane owns two of
+// the 128 output columns of a row.
 #pragma once
 
 #include "common.hpp"
@@ -21,53 +22,91 @@ struct MergeParams {
   const float* part_ml;
   __bf16* out;
   float* lse;
-  int S, N, Hq, splits, chunk, max_tokens;
+  int S, N, Hq, Hkv, G, splits, chunk, max_tokens;
+  int mblocks, rows_per_block;  // row blocks of the attention launch
 };
 
 constexpr int kMergeWaves = 4;
+constexpr int kMergeRows = 4;    // rows per wave
+constexpr int kMergeSplits = 4;  // splits whose loads are issued together
+constexpr int kMergeRowsPerWG = kMergeWaves * kMergeRows;
 
+// Workgroups are laid out like the attention launch: (sequence, kv head,
+// row block), each row block cut into pieces of kMergeRowsPerWG rows, so
+// the sequence of every row is known from the workgroup id.  A wave merges
+// kMergeRows rows; the loads of kMergeSplits splits of all its rows are
+// issued before any is used, and the sums run with a running maximum.
 __global__ __launch_bounds__(kMergeWaves * 64) void attn_merge_kernel(
     MergeParams p) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int row = blockIdx.x * kMergeWaves + wave;
-  const int NH = p.N * p.Hq;
-  if (row >= NH) return;
-  const int node = row / p.Hq;
-
-  // sequence owning this node: last s with tree_offsets[s] <= node
-  int lo = 0, hi = p.S - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (p.tree_offsets[mid] <= node) lo = mid; else hi = mid - 1;
-  }
-  const int a = clampi(p.tree_offsets[lo], 0, p.N);
-  const int b = clampi(p.tree_offsets[lo + 1], a, p.N);
-  const int P = max(p.prefix_lens[lo], 0);
+  const int pieces = p.rows_per_block / kMergeRowsPerWG;
+  int L = blockIdx.x / pieces;
+  const int piece = blockIdx.x - L * pieces;
+  const int mb = L % p.mblocks;
+  L /= p.mblocks;
+  const int g = L % p.Hkv;
+  const int s = L / p.Hkv;
+  const int a = clampi(p.tree_offsets[s], 0, p.N);
+  const int b = clampi(p.tree_offsets[s + 1], a, p.N);
+  const int rows = p.G * (b - a);
+  const int r0 = mb * p.rows_per_block + piece * kMergeRowsPerWG +
+                 wave * kMergeRows;
+  if (r0 >= rows) return;
+  const int P = max(p.prefix_lens[s], 0);
   const int T = min(P + (b - a), p.max_tokens);
   const int nsplit = min(p.splits, (T + p.chunk - 1) / p.chunk);
+  const size_t NH = (size_t)p.N * p.Hq;
 
-  float mstar = -INFINITY;
-  for (int c = 0; c < nsplit; ++c) {
-    mstar = fmaxf(mstar, p.part_ml[((size_t)c * NH + row) * 2]);
+  size_t qrow[kMergeRows];
+  float m_run[kMergeRows], l_run[kMergeRows];
+  f32x2 acc[kMergeRows];
+#pragma unroll
+  for (int k = 0; k < kMergeRows; ++k) {
+    const int r = min(r0 + k, rows - 1);
+    qrow[k] = (size_t)(a + r / p.G) * p.Hq + g * p.G + r % p.G;
+    m_run[k] = -INFINITY;
+    l_run[k] = 0.f;
+    acc[k] = f32x2{0.f, 0.f};
   }
-  const float mref = (mstar == -INFINITY) ? 0.f : mstar;
-  float lsum = 0.f;
-  f32x2 acc = {0.f, 0.f};
-  for (int c = 0; c < nsplit; ++c) {
-    const size_t prow = (size_t)c * NH + row;
-    const f32x2 ml = *reinterpret_cast<const f32x2*>(p.part_ml + prow * 2);
-    const float w = fast_exp2(ml[0] - mref);
-    lsum += w * ml[1];
-    const f32x2 oc =
-        *reinterpret_cast<const f32x2*>(p.part_o + prow * kHeadDim + lane * 2);
-    acc[0] += w * oc[0];
-    acc[1] += w * oc[1];
+  for (int c0 = 0; c0 < nsplit; c0 += kMergeSplits) {
+    f32x2 ml[kMergeRows][kMergeSplits], oc[kMergeRows][kMergeSplits];
+#pragma unroll
+    for (int k = 0; k < kMergeRows; ++k) {
+#pragma unroll
+      for (int u = 0; u < kMergeSplits; ++u) {
+        const int c = min(c0 + u, nsplit - 1);  // in range; unused if past
+        const size_t prow = (size_t)c * NH + qrow[k];
+        ml[k][u] = *reinterpret_cast<const f32x2*>(p.part_ml + prow * 2);
+        oc[k][u] = *reinterpret_cast<const f32x2*>(p.part_o + prow * kHeadDim +
+                                                   lane * 2);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kMergeSplits; ++u) {
+      if (c0 + u >= nsplit) break;
+#pragma unroll
+      for (int k = 0; k < kMergeRows; ++k) {
+        const float m_new = fmaxf(m_run[k], ml[k][u][0]);
+        if (m_new == -INFINITY) continue;  // no key seen yet
+        const float s_old = fast_exp2(m_run[k] - m_new);
+        const float w = fast_exp2(ml[k][u][0] - m_new);
+        l_run[k] = l_run[k] * s_old + w * ml[k][u][1];
+        acc[k][0] = acc[k][0] * s_old + w * oc[k][u][0];
+        acc[k][1] = acc[k][1] * s_old + w * oc[k][u][1];
+        m_run[k] = m_new;
+      }
+    }
   }
-  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-  bf16x2 r2 = {(__bf16)(acc[0] * inv), (__bf16)(acc[1] * inv)};
-  *reinterpret_cast<bf16x2*>(p.out + (size_t)row * kHeadDim + lane * 2) = r2;
-  if (lane == 0) {
-    p.lse[row] = lsum > 0.f ? (mstar + log2f(lsum)) * kLn2 : -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kMergeRows; ++k) {
+    if (r0 + k >= rows) continue;
+    const float inv = l_run[k] > 0.f ? 1.f / l_run[k] : 0.f;
+    bf16x2 r2 = {(__bf16)(acc[k][0] * inv), (__bf16)(acc[k][1] * inv)};
+    *reinterpret_cast<bf16x2*>(p.out + qrow[k] * kHeadDim + lane * 2) = r2;
+    if (lane == 0) {
+      p.lse[qrow[k]] =
+          l_run[k] > 0.f ? (m_run[k] + log2f(l_run[k])) * kLn2 : -INFINITY;
+    }
   }
 }
 

@@ -336,13 +336,17 @@ int tree_attn_verify(const void* q, const void* k_cache, const void* v_cache,
     mp.S = num_seqs;
     mp.N = total_nodes;
     mp.Hq = num_q_heads;
+    mp.Hkv = num_kv_heads;
+    mp.G = fp.G;
     mp.splits = pl.splits;
     mp.chunk = pl.chunk;
     mp.max_tokens = fp.max_tokens;
-    const long long rows = (long long)total_nodes * num_q_heads;
-    const unsigned mgrid = (unsigned)((rows + kMergeWaves - 1) / kMergeWaves);
-    hipLaunchKernelGGL(attn_merge_kernel, dim3(mgrid), dim3(kMergeWaves * 64),
-                       0, hs, mp);
+    mp.mblocks = pl.mblocks;
+    mp.rows_per_block = 32 * pl.nw;
+    const long long mgrid = (long long)num_seqs * num_kv_heads * pl.mblocks *
+                            (mp.rows_per_block / kMergeRowsPerWG);
+    hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)mgrid),
+                       dim3(kMergeWaves * 64), 0, hs, mp);
     if (hipGetLastError() != hipSuccess) return TREE_ATTN_ERR_HIP;
   }
   return TREE_ATTN_OK;
