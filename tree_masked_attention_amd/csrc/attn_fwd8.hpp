@@ -313,6 +313,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd8_kernel(FwdParams p) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
     }
+    // the segments are scheduled separately: without this fence the
+    // scheduler mixes their groups and the matrix core waits more
+    __builtin_amdgcn_sched_barrier(0);
     // segment 2: S^T(j+1) keys 32..63, PV(j) keys 0..31 | probabilities
     // of keys 32..63
     qk_block(j + 1, 1, Snext[1]);
@@ -330,6 +333,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd8_kernel(FwdParams p) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
     }
+    __builtin_amdgcn_sched_barrier(0);
     // segment 3: PV(j) keys 32..63 | max of tile j+1
     pv_block(j, 1, pf[1]);
     if (mask_next) {
