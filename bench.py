@@ -8,6 +8,9 @@ Inputs are resident in HBM before timing; the input sets are rotated over
 enough copies (>= 1 GiB in total) that no step finds its K/V in the 256 MB
 Infinity Cache left there by the previous step.
 
+Warmup runs the requested W steps and keeps going until the path has run
+for at least 0.3 s, so that the timed K steps see settled clocks.
+
 Prints one JSON line on stdout.  Everything else goes to stderr.
 """
 
@@ -26,6 +29,7 @@ DEFAULT_WORKLOAD = "qwen3-8b-b256-p4k"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
 ROTATE_BYTES = 1 << 30
+WARM_SECONDS = 0.3
 
 
 def log(*a):
@@ -245,11 +249,20 @@ def main():
             ev[2].record(stream)
         return rc
 
-    log(f"[bench] warmup {args.warmup} steps")
-    for i in range(args.warmup):
-        if step(i) != 0:
+    # W warmup steps, continued until the GPU has run the path for at least
+    # WARM_SECONDS (clocks and power settle; a cold first loop runs ~15%
+    # slower on the long-context workload)
+    t_w = time.perf_counter()
+    n_warm = 0
+    while n_warm < args.warmup or time.perf_counter() - t_w < WARM_SECONDS:
+        if step(n_warm) != 0:
             raise RuntimeError("tree_attn call failed during warmup")
+        n_warm += 1
+        if n_warm % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+    log(f"[bench] warmup: {n_warm} steps ({args.warmup} requested), "
+        f"{time.perf_counter() - t_w:.2f} s")
     if (bad[:S] != -1).any():
         raise RuntimeError("invalid tree in benchmark input")
 
@@ -298,6 +311,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": n_warm,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
