@@ -8,8 +8,8 @@ Inputs are resident in HBM before timing; the input sets are rotated over
 enough copies (>= 1 GiB in total) that no step finds its K/V in the 256 MB
 Infinity Cache left there by the previous step.
 
-Warmup runs the requested W steps and keeps going until the path has run
-for at least 0.3 s, so that the timed K steps see settled clocks.
+Warmup runs the requested W steps and keeps going, back to back, until the
+path has run for about 0.3 s.
 
 Prints one JSON line on stdout.  Everything else goes to stderr.
 """
@@ -249,17 +249,24 @@ def main():
             ev[2].record(stream)
         return rc
 
-    # W warmup steps, continued until the GPU has run the path for at least
-    # WARM_SECONDS (clocks and power settle; a cold first loop runs ~15%
-    # slower on the long-context workload)
+    # W warmup steps, then as many more as fill WARM_SECONDS, enqueued back
+    # to back like the timed steps.  Under sustained back-to-back load the
+    # GPU's power management lowers clocks (long-context kernels go from
+    # ~570 us to 620-770 us within ~20 launches), so the whole-step figure
+    # below is the sustained rate; the per-launch figures, taken with small
+    # gaps between launches, run at higher clocks.
     t_w = time.perf_counter()
     n_warm = 0
-    while n_warm < args.warmup or time.perf_counter() - t_w < WARM_SECONDS:
+    for _ in range(max(args.warmup, 1)):
         if step(n_warm) != 0:
             raise RuntimeError("tree_attn call failed during warmup")
         n_warm += 1
-        if n_warm % 8 == 0:
-            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    per = (time.perf_counter() - t_w) / n_warm
+    extra = int(max(0.0, WARM_SECONDS - (time.perf_counter() - t_w)) / per)
+    for _ in range(extra):
+        step(n_warm)
+        n_warm += 1
     torch.cuda.synchronize()
     log(f"[bench] warmup: {n_warm} steps ({args.warmup} requested), "
         f"{time.perf_counter() - t_w:.2f} s")

@@ -173,6 +173,31 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(FwdParams p) {
   const int g = L % p.Hkv;
   const int s = L / p.Hkv;
 
+  const int tid = threadIdx.x;
+  // readfirstlane tells the compiler the wave index is wave-uniform
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int col = lane & 31, half = lane >> 5;
+
+  // The prologue issues all its loads before it waits for any: the
+  // split's page-table entries first (they depend only on the sequence and
+  // the split), then, once the tree bounds are in, the mask words and Q.
+  const int kbeg = split * p.chunk;
+  const int lp0 = kbeg >> p.log2_page;
+  constexpr int kPgPer = (kPageCache + kThreads - 1) / kThreads;
+  int pgv[kPgPer];
+  {
+    // pages a split can span, within the page-table row
+    const int npg_max = min(min(((p.chunk - 1) >> p.log2_page) + 2, kPageCache),
+                            p.max_pps - lp0);
+    const int* ptab = p.page_table + (size_t)s * p.max_pps + lp0;
+#pragma unroll
+    for (int k = 0; k < kPgPer; ++k) {
+      const int i = tid + k * kThreads;
+      pgv[k] = i < npg_max ? ptab[i] : 0;
+    }
+  }
+
   const int a = clampi(p.tree_offsets[s], 0, p.N);
   const int b = clampi(p.tree_offsets[s + 1], a, p.N);
   const int B = b - a;
@@ -181,26 +206,10 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(FwdParams p) {
   const int r0 = mb * kRowsPerWG;
   if (r0 >= rows) return;
   const int T = min(P + B, p.max_tokens);
-  const int kbeg = split * p.chunk;
   if (kbeg >= T) return;
   const int kend = min(T, kbeg + p.chunk);
   const int ntiles = (kend - kbeg + kKeyTile - 1) / kKeyTile;
-
-  const int tid = threadIdx.x;
-  // readfirstlane tells the compiler the wave index is wave-uniform
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int col = lane & 31, half = lane >> 5;
-
-  // ---- page-table slice of this split -> LDS
-  const int lp0 = kbeg >> p.log2_page;
-  {
-    const int npg = min(((kend - 1) >> p.log2_page) - lp0 + 1, kPageCache);
-    const int* ptab = p.page_table + (size_t)s * p.max_pps + lp0;
-    for (int i = tid; i < npg; i += kThreads) {
-      pg_lds[i] = clampi(ptab[i], 0, p.num_pages - 1);
-    }
-  }
+  const int npg = min(((kend - 1) >> p.log2_page) - lp0 + 1, kPageCache);
 
   // ---- ancestor-mask words of this workgroup's nodes for the split's
   // tree keys -> LDS (window of words wlo..whi of each node's row).  The
@@ -212,11 +221,24 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(FwdParams p) {
   const int wlo = has_tree ? (max(kbeg, P) - P) >> 6 : 0;
   const int whi = has_tree ? min(p.W - 1, ((kend - 1 - P) >> 6) + 1) : 0;
   const int nwin = whi - wlo + 1;
-  if (has_tree) {
-    const int nm = min(nnodes * nwin, kMaskCache);
-    for (int i = tid; i < nm; i += kThreads) {
-      const int nn = i / nwin, w = i - nn * nwin;
-      mk_lds[i] = p.masks[(size_t)(a + n_lo + nn) * p.W + wlo + w];
+  const int nm = has_tree ? min(nnodes * nwin, kMaskCache) : 0;
+  constexpr int kMkPer = (kMaskCache + kThreads - 1) / kThreads;
+  uint64_t mkv[kMkPer];
+  {
+    // entry i = tid + k*kThreads is word w of node nn, i = nn*nwin + w;
+    // stepped by kThreads without a division per entry
+    const int dq = kThreads / nwin, dr = kThreads - dq * nwin;
+    int nn = tid / nwin, w = tid - nn * nwin;
+#pragma unroll
+    for (int k = 0; k < kMkPer; ++k) {
+      const int i = tid + k * kThreads;
+      mkv[k] = i < nm ? p.masks[(size_t)(a + n_lo + nn) * p.W + wlo + w] : 0;
+      nn += dq;
+      w += dr;
+      if (w >= nwin) {
+        w -= nwin;
+        ++nn;
+      }
     }
   }
 
@@ -239,6 +261,18 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(FwdParams p) {
                              : u32x4{0, 0, 0, 0};
       qf[qb][kc] = __builtin_bit_cast(bf16x8, raw);
     }
+  }
+
+  // ---- page slice and mask window -> LDS
+#pragma unroll
+  for (int k = 0; k < kPgPer; ++k) {
+    const int i = tid + k * kThreads;
+    if (i < npg) pg_lds[i] = clampi(pgv[k], 0, p.num_pages - 1);
+  }
+#pragma unroll
+  for (int k = 0; k < kMkPer; ++k) {
+    const int i = tid + k * kThreads;
+    if (i < nm) mk_lds[i] = mkv[k];
   }
 
   // ---- LDS addresses

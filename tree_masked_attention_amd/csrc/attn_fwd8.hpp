@@ -41,6 +41,29 @@ __global__ __launch_bounds__(512, 1) void attn_fwd8_kernel(FwdParams p) {
   const int g = L % p.Hkv;
   const int s = L / p.Hkv;
 
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int col = lane & 31, half = lane >> 5;
+
+  // All prologue loads are issued before any is waited for: the split's
+  // page-table entries first (they need only the sequence and the split),
+  // then, once the tree bounds are in, the mask words and Q.
+  const int kbeg = split * p.chunk;
+  const int lp0 = kbeg >> p.log2_page;
+  constexpr int kPgPer = (kPageCache + kThreads - 1) / kThreads;
+  int pgv[kPgPer];
+  {
+    const int npg_max = min(min(((p.chunk - 1) >> p.log2_page) + 2, kPageCache),
+                            p.max_pps - lp0);
+    const int* ptab = p.page_table + (size_t)s * p.max_pps + lp0;
+#pragma unroll
+    for (int k = 0; k < kPgPer; ++k) {
+      const int i = tid + k * kThreads;
+      pgv[k] = i < npg_max ? ptab[i] : 0;
+    }
+  }
+
   const int a = clampi(p.tree_offsets[s], 0, p.N);
   const int b = clampi(p.tree_offsets[s + 1], a, p.N);
   const int B = b - a;
@@ -49,26 +72,11 @@ __global__ __launch_bounds__(512, 1) void attn_fwd8_kernel(FwdParams p) {
   const int r0 = mb * kRowsPerWG8;
   if (r0 >= rows) return;
   const int T = min(P + B, p.max_tokens);
-  const int kbeg = split * p.chunk;
   if (kbeg >= T) return;
   const int kend = min(T, kbeg + p.chunk);
   const int n = (kend - kbeg + kKeyTile - 1) / kKeyTile;  // tiles, >= 1
+  const int npg = min(((kend - 1) >> p.log2_page) - lp0 + 1, kPageCache);
 
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave >> 2;
-  const int lane = tid & 63;
-  const int col = lane & 31, half = lane >> 5;
-
-  // ---- page-table slice and ancestor-mask window -> LDS
-  const int lp0 = kbeg >> p.log2_page;
-  {
-    const int npg = min(((kend - 1) >> p.log2_page) - lp0 + 1, kPageCache);
-    const int* ptab = p.page_table + (size_t)s * p.max_pps + lp0;
-    for (int i = tid; i < npg; i += kThreads) {
-      pg_lds[i] = clampi(ptab[i], 0, p.num_pages - 1);
-    }
-  }
   const int n_lo = r0 / p.G;
   const int n_hi = (min(r0 + kRowsPerWG8, rows) - 1) / p.G;
   const int nnodes = n_hi - n_lo + 1;
@@ -76,11 +84,22 @@ __global__ __launch_bounds__(512, 1) void attn_fwd8_kernel(FwdParams p) {
   const int wlo = has_tree ? (max(kbeg, P) - P) >> 6 : 0;
   const int whi = has_tree ? min(p.W - 1, ((kend - 1 - P) >> 6) + 1) : 0;
   const int nwin = whi - wlo + 1;
-  if (has_tree) {
-    const int nm = min(nnodes * nwin, kMaskCache);
-    for (int i = tid; i < nm; i += kThreads) {
-      const int nn = i / nwin, w = i - nn * nwin;
-      mk_lds[i] = p.masks[(size_t)(a + n_lo + nn) * p.W + wlo + w];
+  const int nm = has_tree ? min(nnodes * nwin, kMaskCache) : 0;
+  constexpr int kMkPer = (kMaskCache + kThreads - 1) / kThreads;
+  uint64_t mkv[kMkPer];
+  {
+    const int dq = kThreads / nwin, dr = kThreads - dq * nwin;
+    int nn = tid / nwin, w = tid - nn * nwin;
+#pragma unroll
+    for (int k = 0; k < kMkPer; ++k) {
+      const int i = tid + k * kThreads;
+      mkv[k] = i < nm ? p.masks[(size_t)(a + n_lo + nn) * p.W + wlo + w] : 0;
+      nn += dq;
+      w += dr;
+      if (w >= nwin) {
+        w -= nwin;
+        ++nn;
+      }
     }
   }
 
@@ -99,6 +118,18 @@ __global__ __launch_bounds__(512, 1) void attn_fwd8_kernel(FwdParams p) {
                          : u32x4{0, 0, 0, 0};
       qf[kc] = __builtin_bit_cast(bf16x8, raw);
     }
+  }
+
+  // ---- page slice and mask window -> LDS
+#pragma unroll
+  for (int k = 0; k < kPgPer; ++k) {
+    const int i = tid + k * kThreads;
+    if (i < npg) pg_lds[i] = clampi(pgv[k], 0, p.num_pages - 1);
+  }
+#pragma unroll
+  for (int k = 0; k < kMkPer; ++k) {
+    const int i = tid + k * kThreads;
+    if (i < nm) mk_lds[i] = mkv[k];
   }
 
   // ---- LDS operand addresses (stage 0; the stage offset is added per tile)
