@@ -115,7 +115,7 @@ def test_describe_plan():
     assert p["chunk"] % 64 == 0 and p["chunk"] * p["splits"] >= 256 + 16
     # 1024 rows per kv head and one long split: eight waves
     p = api.describe_plan(4, 1024, 32, 8, 128, 32768, 256, 16, 0)
-    assert p["waves"] == 8 and p["splits"] == 2
+    assert p["waves"] == 8 and p["rows"] == 256 and p["splits"] == 2
     assert p["workgroups"] == 4 * 8 * 4 * 2
     # short splits of the same rows stay on four waves
     p = api.describe_plan(1, 256, 32, 8, 128, 4096, 256, 16, 0)

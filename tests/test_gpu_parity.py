@@ -125,7 +125,7 @@ def test_eight_wave_parity(name):
                              splits)
     say(f"[gpu] eight-wave case {name}: P={list(wl.prefix_lens)} "
         f"B={list(wl.tree_sizes)} page={wl.page_size} plan={plan}")
-    assert plan["waves"] == 8
+    assert plan["waves"] == 8 and plan["rows"] == 256
     got = run_gpu(wl, num_splits=splits)
     assert np.array_equal(got["masks"], oracle.workload_masks(wl))
     ref_out, ref_lse = oracle.workload_attention(wl)

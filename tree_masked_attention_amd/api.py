@@ -144,15 +144,16 @@ def describe_plan(num_seqs: int, total_nodes: int, num_q_heads: int,
                   max_nodes: int, page_size: int = 16,
                   num_splits: int = 0) -> dict:
     """The launch verify() makes for these sizes: waves per workgroup,
-    splits of the key range, keys per split, workgroups."""
-    info = (ctypes.c_int32 * 4)()
+    query rows per workgroup, splits of the key range, keys per split,
+    workgroups."""
+    info = (ctypes.c_int32 * 5)()
     code = _lib.tree_attn_describe_plan(
         num_seqs, total_nodes, num_q_heads, num_kv_heads, head_dim,
         max_prefix_len, max_nodes, page_size, num_splits,
         ctypes.cast(info, ctypes.c_void_p))
     _raise(code, "tree_attn_describe_plan")
-    return {"waves": info[0], "splits": info[1], "chunk": info[2],
-            "workgroups": info[3]}
+    return {"waves": info[0], "rows": info[1], "splits": info[2],
+            "chunk": info[3], "workgroups": info[4]}
 
 
 def verify(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

@@ -1,17 +1,21 @@
-// Eight-wave variant of the split-KV tree-verification attention kernel,
-// for (sequence, kv head) pairs with at least 256 query rows.
+// 256-row variants of the split-KV tree-verification attention kernel, for
+// (sequence, kv head) pairs with at least 256 query rows.
 //
 // Same operation, data layout, MFMA mapping, LDS ring format and pipeline
-// as the four-wave kernel (attn_fwd.hpp), with eight waves of 32 query
-// rows (256 rows per workgroup), two waves per SIMD.  Each K/V tile staged
-// in LDS then serves twice the rows, and two waves share every SIMD: the
-// vector ALU of a SIMD issues about twice as many instructions per cycle
-// (and the exponential about three times as many) when two waves feed it,
-// and one wave's matrix instructions run while the other's softmax does.
-// Each wave still overlaps its own S^T MFMAs of tile j+1 with the softmax
-// of tile j.  The register budget is 256 per wave, so scores are built one
-// 32-key block at a time and the K/V operands are read from LDS a quarter
-// tile at a time.
+// as the four-wave 128-row kernel (attn_fwd.hpp); each K/V tile staged in
+// LDS serves 256 rows.  Two shapes:
+//  * NW = 8 waves of 32 rows, two waves per SIMD: the vector ALU of a SIMD
+//    issues about twice as many instructions per cycle (and the exponential
+//    about three times as many) when two waves feed it; 256 registers per
+//    wave.
+//  * NW = 4 waves of 64 rows (QB = 2 query blocks), one wave per SIMD with
+//    up to 512 registers: each K or V operand read from LDS feeds two
+//    MFMAs, which halves the LDS reads per flop (every wave reads the whole
+//    K and V tile; with 32 rows per wave those reads come close to the
+//    LDS bandwidth).
+// Each wave overlaps its own S^T MFMAs of tile j+1 with the softmax of
+// tile j; scores are built one 32-key block at a time and the K/V operands
+// are read from LDS a quarter tile at a time.
 #pragma once
 
 #include "attn_fwd.hpp"
@@ -20,12 +24,15 @@ namespace tree_attn {
 
 constexpr int kRowsPerWG8 = 256;
 
-__global__ __launch_bounds__(512, 1) void attn_fwd8_kernel(FwdParams p) {
-  constexpr int NW = 8;
+template <int NW>
+__global__ __launch_bounds__(NW * 64, 1) void attn_fwd256_kernel(FwdParams p) {
+  constexpr int QB = 8 / NW;             // 32-query blocks per wave
   constexpr int kThreads = NW * 64;
-  constexpr int kOpsPerMat = 16 / NW;  // 1-KB DMA ops per wave per matrix
+  constexpr int kOpsPerMat = 16 / NW;    // 1-KB DMA ops per wave per matrix
   constexpr int kOps = 2 * kOpsPerMat;
-  static_assert(kOps == 4, "the vmcnt immediates below assume 4 ops");
+  constexpr int kDmaRows = 4 * kOpsPerMat;  // tile rows a wave moves
+  constexpr int kLog2DmaRows = NW == 8 ? 3 : 4;
+  static_assert(QB * NW == 8 && (1 << kLog2DmaRows) == kDmaRows, "shape");
   __shared__ __align__(1024) unsigned char ring[2 * kVOff];
   __shared__ int pg_lds[kPageCache];
   __shared__ uint64_t mk_lds[kMaskCache];
@@ -103,20 +110,24 @@ __global__ __launch_bounds__(512, 1) void attn_fwd8_kernel(FwdParams p) {
     }
   }
 
-  // ---- this lane's query row
-  const int r = r0 + wave * 32 + col;
-  const bool rvalid = r < rows;
-  const int node = rvalid ? r / p.G : n_hi;
-  const size_t qrow =
-      (size_t)(a + node) * p.Hq + g * p.G + (rvalid ? r % p.G : 0);
-  bf16x8 qf[8];
-  {
-    const __bf16* qp = p.q + qrow * kHeadDim + half * 8;
+  // ---- this lane's query rows (one per query block)
+  bool rvalid[QB];
+  int node[QB];
+  size_t qrow[QB];
+  bf16x8 qf[QB][8];  // Q^T fragments (B operand): d = kc*16 + half*8 + 0..7
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int r = r0 + (wave * QB + qb) * 32 + col;
+    rvalid[qb] = r < rows;
+    node[qb] = rvalid[qb] ? r / p.G : n_hi;
+    qrow[qb] = (size_t)(a + node[qb]) * p.Hq + g * p.G +
+               (rvalid[qb] ? r % p.G : 0);
+    const __bf16* qp = p.q + qrow[qb] * kHeadDim + half * 8;
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) {
-      u32x4 raw = rvalid ? *reinterpret_cast<const u32x4*>(qp + kc * 16)
-                         : u32x4{0, 0, 0, 0};
-      qf[kc] = __builtin_bit_cast(bf16x8, raw);
+      u32x4 raw = rvalid[qb] ? *reinterpret_cast<const u32x4*>(qp + kc * 16)
+                             : u32x4{0, 0, 0, 0};
+      qf[qb][kc] = __builtin_bit_cast(bf16x8, raw);
     }
   }
 
@@ -149,7 +160,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd8_kernel(FwdParams p) {
                 ((4 * (db ^ y) + x) << 4) + 8 * (lane & 1);
   }
 
-  // ---- DMA of one tile: wave w moves rows 8w .. 8w+7 of K and of V, as
+  // ---- DMA of one tile: wave w moves rows kDmaRows*w .. of K and of V, as
   // kOpsPerMat instructions of 4 rows (lane l: row 4k + l/16, chunk l%16).
   const int pmask = (1 << p.log2_page) - 1;
   const unsigned tok_bytes = (unsigned)p.Hkv * kHeadDim * 2;
@@ -157,19 +168,19 @@ __global__ __launch_bounds__(512, 1) void attn_fwd8_kernel(FwdParams p) {
   const int lrow = lane >> 4, lchunk = lane & 15;
   const char* kbase = reinterpret_cast<const char*>(p.k);
   const char* vbase = reinterpret_cast<const char*>(p.v);
-  // fast path: the wave's 8 rows lie in one page (pages of >= 8 tokens)
-  const bool fast_pages = p.log2_page >= 3;
+  // fast path: the wave's rows lie in one page (pages of >= kDmaRows tokens)
+  const bool fast_pages = p.log2_page >= kLog2DmaRows;
   unsigned k_row_off[kOpsPerMat], v_row_off[kOpsPerMat];
 #pragma unroll
   for (int k = 0; k < kOpsPerMat; ++k) {
-    const int r8 = 4 * k + lrow;
-    const int row = 8 * wave + r8;  // row within the tile
-    k_row_off[k] = r8 * tok_bytes + ((lchunk ^ (row & 15)) << 4);
-    v_row_off[k] = r8 * tok_bytes + ((lchunk ^ (4 * (row & 3))) << 4);
+    const int rw = 4 * k + lrow;
+    const int row = kDmaRows * wave + rw;  // row within the tile
+    k_row_off[k] = rw * tok_bytes + ((lchunk ^ (row & 15)) << 4);
+    v_row_off[k] = rw * tok_bytes + ((lchunk ^ (4 * (row & 3))) << 4);
   }
-  auto issue_fast = [&](int t) {  // full tile, pages of >= 8 tokens
+  auto issue_fast = [&](int t) {  // full tile, pages of >= kDmaRows tokens
     const unsigned st = ring_base + (unsigned)(t & (kStages - 1)) * kTileBytes;
-    const int w0 = kbeg + t * kKeyTile + 8 * wave;
+    const int w0 = kbeg + t * kKeyTile + kDmaRows * wave;
     const int pi = clampi((w0 >> p.log2_page) - lp0, 0, kPageCache - 1);
     const unsigned pgu = (unsigned)__builtin_amdgcn_readfirstlane(pg_lds[pi]);
     const size_t off = (size_t)pgu * page_bytes +
@@ -184,8 +195,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd8_kernel(FwdParams p) {
   auto issue = [&](int t) {
     const int t0 = kbeg + t * kKeyTile;
     const unsigned st = ring_base + (unsigned)(t & (kStages - 1)) * kTileBytes;
-    const int w0 = t0 + 8 * wave;
-    if (fast_pages && w0 + 7 < kend) {
+    const int w0 = t0 + kDmaRows * wave;
+    if (fast_pages && w0 + kDmaRows - 1 < kend) {
       const int pi = clampi((w0 >> p.log2_page) - lp0, 0, kPageCache - 1);
       const unsigned pgu =
           (unsigned)__builtin_amdgcn_readfirstlane(pg_lds[pi]);
@@ -208,7 +219,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd8_kernel(FwdParams p) {
     }
 #pragma unroll
     for (int k = 0; k < kOpsPerMat; ++k) {
-      const int row = 8 * wave + 4 * k + lrow;
+      const int row = kDmaRows * wave + 4 * k + lrow;
       const size_t off = (size_t)(unsigned)pg[k] * page_bytes +
                          (unsigned)slot[k] * tok_bytes + g * kHeadDim * 2;
       const unsigned dst = st + (wave * kOpsPerMat + k) * 1024;
@@ -218,7 +229,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd8_kernel(FwdParams p) {
   };
 
   // ---- 64-bit allowed-key mask of tile t (first key t0) for this node
-  auto tile_allow = [&](int t0) -> uint64_t {
+  auto tile_allow = [&](int t0, int nd) -> uint64_t {
     const int nvalid = kend - t0;
     const int npre = P - t0;
     uint64_t allow = nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1);
@@ -226,7 +237,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd8_kernel(FwdParams p) {
         npre >= 64 ? ~0ull : (npre <= 0 ? 0ull : ((1ull << npre) - 1));
     uint64_t tree = 0;
     if (npre < 64) {
-      const int mrow_lds = (node - n_lo) * nwin - wlo;
+      const int mrow_lds = (nd - n_lo) * nwin - wlo;
       const int j0 = t0 - P;
       if (j0 >= 0) {
         const int w0 = min(j0 >> 6, p.W - 1);
@@ -243,11 +254,16 @@ __global__ __launch_bounds__(512, 1) void attn_fwd8_kernel(FwdParams p) {
     return allow & (pre | tree);
   };
 
-  f32x16 o[4];
+  f32x16 o[QB][4];
+  float l_run[QB];  // this lane half's share of the row sum
+  float m_ref[QB];  // reference max, log2 units
 #pragma unroll
-  for (int db = 0; db < 4; ++db) o[db] = f32x16{};
-  float l_run = 0.f;          // this lane half's share of the row sum
-  float m_ref = -INFINITY;    // reference max, log2 units
+  for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[qb][db] = f32x16{};
+    l_run[qb] = 0.f;
+    m_ref[qb] = -INFINITY;
+  }
   const float c2 = p.scale_log2;
 
   // ---- LDS operand reads.  K fragments of key block kb, head-dim chunks
@@ -270,59 +286,91 @@ __global__ __launch_bounds__(512, 1) void attn_fwd8_kernel(FwdParams p) {
           bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
   };
-  // S^T of key block kb of tile t: one accumulation chain over the head
-  // dimension, K fragments streamed a quarter tile at a time
-  auto qk_block = [&](int t, int kb, f32x16& Sk) {
+  // S^T of key block kb of tile t for every query block: QB accumulation
+  // chains over the head dimension, K fragments a quarter tile at a time
+  auto qk_block = [&](int t, int kb, f32x16 (&S)[QB][2]) {
     bf16x8 kf0[4], kf1[4];
     read_kq(t, kb, 0, kf0);
     read_kq(t, kb, 1, kf1);
-    Sk = f32x16{};
 #pragma unroll
-    for (int c = 0; c < 4; ++c) Sk = mfma32x32x16(kf0[c], qf[c], Sk);
+    for (int qb = 0; qb < QB; ++qb) S[qb][kb] = f32x16{};
 #pragma unroll
-    for (int c = 0; c < 4; ++c) Sk = mfma32x32x16(kf1[c], qf[4 + c], Sk);
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        S[qb][kb] = mfma32x32x16(kf0[c], qf[qb][c], S[qb][kb]);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        S[qb][kb] = mfma32x32x16(kf1[c], qf[qb][4 + c], S[qb][kb]);
+      }
+    }
   };
-  // O^T += V^T P^T over key block kb of tile t (4 accumulation chains)
-  auto pv_block = [&](int t, int kb, const bf16x8 (&pk)[2]) {
+  // O^T += V^T P^T over key block kb of tile t (4*QB accumulation chains)
+  auto pv_block = [&](int t, int kb, const bf16x8 (&pf)[QB][2][2]) {
     bf16x8 vf0[4], vf1[4];
     read_vq(t, kb, 0, vf0);
     read_vq(t, kb, 1, vf1);
 #pragma unroll
-    for (int db = 0; db < 4; ++db) o[db] = mfma32x32x16(vf0[db], pk[0], o[db]);
+    for (int db = 0; db < 4; ++db) {
 #pragma unroll
-    for (int db = 0; db < 4; ++db) o[db] = mfma32x32x16(vf1[db], pk[1], o[db]);
-  };
-  // probabilities of key block kb against m_ref; adds their fp32 sum
-  auto exps_block = [&](const f32x16& Sk, bf16x8 (&pk)[2]) {
-    const float mu = (m_ref == -INFINITY) ? 0.f : m_ref;
-    float ps0 = 0.f, ps1 = 0.f;
-#pragma unroll
-    for (int rr = 0; rr < 16; rr += 2) {
-      const float e0 = fast_exp2(fmaf(Sk[rr], c2, -mu));
-      const float e1 = fast_exp2(fmaf(Sk[rr + 1], c2, -mu));
-      ps0 += e0;
-      ps1 += e1;
-      pk[rr >> 3][rr & 7] = (__bf16)e0;
-      pk[rr >> 3][(rr & 7) + 1] = (__bf16)e1;
-    }
-    l_run += ps0 + ps1;
-  };
-  // reference max for a tile (lazy raise, as in the four-wave kernel)
-  auto next_ref = [&](const f32x16 (&Sx)[2], float& m_new, float& alpha) {
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int rr = 0; rr < 16; rr += 2) {
-        tmax = __builtin_elementwise_maximum(
-            tmax, __builtin_elementwise_maximum(Sx[kb][rr], Sx[kb][rr + 1]));
+      for (int qb = 0; qb < QB; ++qb) {
+        o[qb][db] = mfma32x32x16(vf0[db], pf[qb][kb][0], o[qb][db]);
       }
     }
-    tmax = __builtin_elementwise_maximum(tmax, other_half(tmax)) * c2;
-    const bool need = tmax > m_ref + kLazyRescale;
-    m_new = need ? tmax : m_ref;
-    alpha = need ? fast_exp2(m_ref - m_new) : 1.f;
-    return need;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        o[qb][db] = mfma32x32x16(vf1[db], pf[qb][kb][1], o[qb][db]);
+      }
+    }
+  };
+  // probabilities of key block kb against m_ref; adds their fp32 sums
+  auto exps_block = [&](const f32x16 (&S)[QB][2], int kb,
+                        bf16x8 (&pf)[QB][2][2]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float mu = (m_ref[qb] == -INFINITY) ? 0.f : m_ref[qb];
+      float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+      for (int rr = 0; rr < 16; rr += 2) {
+        const float e0 = fast_exp2(fmaf(S[qb][kb][rr], c2, -mu));
+        const float e1 = fast_exp2(fmaf(S[qb][kb][rr + 1], c2, -mu));
+        ps0 += e0;
+        ps1 += e1;
+        pf[qb][kb][rr >> 3][rr & 7] = (__bf16)e0;
+        pf[qb][kb][rr >> 3][(rr & 7) + 1] = (__bf16)e1;
+      }
+      l_run[qb] += ps0 + ps1;
+    }
+  };
+  // reference max for a tile (lazy raise, as in the four-wave kernel)
+  auto next_ref = [&](const f32x16 (&Sx)[QB][2], float (&m_new)[QB],
+                      float (&alpha)[QB]) -> bool {
+    bool any_need = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int rr = 0; rr < 16; rr += 2) {
+          tmax = __builtin_elementwise_maximum(
+              tmax, __builtin_elementwise_maximum(Sx[qb][kb][rr],
+                                                  Sx[qb][kb][rr + 1]));
+        }
+      }
+      tmax = __builtin_elementwise_maximum(tmax, other_half(tmax)) * c2;
+      const bool need = tmax > m_ref[qb] + kLazyRescale;
+      m_new[qb] = need ? tmax : m_ref[qb];
+      alpha[qb] = need ? fast_exp2(m_ref[qb] - m_new[qb]) : 1.f;
+      any_need |= need;
+    }
+    return any_need;
   };
 
   // ---- one pipeline step over tile j.  Tile j's scores Scur (masked, with
@@ -332,15 +380,16 @@ __global__ __launch_bounds__(512, 1) void attn_fwd8_kernel(FwdParams p) {
   // j+1's max.  The scores are built one 32-key block at a time, so that
   // only one and a half score tiles are live.  After the last tile the
   // scores are computed on stale LDS data and dropped.
-  auto body = [&](int j, f32x16 (&Scur)[2], f32x16 (&Snext)[2],
-                  bool mask_next, float& m_new, float& alpha) -> bool {
-    bf16x8 pf[2][2];
+  auto body = [&](int j, f32x16 (&Scur)[QB][2], f32x16 (&Snext)[QB][2],
+                  bool mask_next, float (&m_new)[QB],
+                  float (&alpha)[QB]) -> bool {
+    bf16x8 pf[QB][2][2];
     // segment 1: S^T(j+1) keys 0..31 | probabilities of keys 0..31
-    qk_block(j + 1, 0, Snext[0]);
-    exps_block(Scur[0], pf[0]);
+    qk_block(j + 1, 0, Snext);
+    exps_block(Scur, 0, pf);
     __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 8 * QB; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
     }
@@ -349,38 +398,47 @@ __global__ __launch_bounds__(512, 1) void attn_fwd8_kernel(FwdParams p) {
     __builtin_amdgcn_sched_barrier(0);
     // segment 2: S^T(j+1) keys 32..63, PV(j) keys 0..31 | probabilities
     // of keys 32..63
-    qk_block(j + 1, 1, Snext[1]);
-    pv_block(j, 0, pf[0]);
-    exps_block(Scur[1], pf[1]);
+    qk_block(j + 1, 1, Snext);
+    pv_block(j, 0, pf);
+    exps_block(Scur, 1, pf);
     __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 8 * QB; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 / QB, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 8 * QB; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
     // segment 3: PV(j) keys 32..63 | max of tile j+1
-    pv_block(j, 1, pf[1]);
+    pv_block(j, 1, pf);
     if (mask_next) {
-      apply_tile_mask(Snext, tile_allow(kbeg + (j + 1) * kKeyTile), half);
+      const int t1 = kbeg + (j + 1) * kKeyTile;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        apply_tile_mask(Snext[qb], tile_allow(t1, node[qb]), half);
+      }
     }
     return next_ref(Snext, m_new, alpha);
   };
-  auto finish = [&](bool r, float m_new, float alpha) {
+  auto finish = [&](bool r, const float (&m_new)[QB],
+                    const float (&alpha)[QB]) {
     if (__any(r)) {
-      l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] *= alpha;
+      for (int qb = 0; qb < QB; ++qb) {
+        l_run[qb] *= alpha[qb];
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[qb][db] *= alpha[qb];
+      }
     }
-    m_ref = m_new;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) m_ref[qb] = m_new[qb];
   };
-  auto step = [&](int j, f32x16 (&Scur)[2], f32x16 (&Snext)[2]) {
+  auto step = [&](int j, f32x16 (&Scur)[QB][2], f32x16 (&Snext)[QB][2]) {
     if (j + 1 < n) {
       // tile j+1 must have landed; tile j+2 may still be in flight
       if (j + 2 < n) wait_vmcnt<kOps>();
@@ -388,7 +446,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd8_kernel(FwdParams p) {
     }
     __syncthreads();
     if (j + kStages - 1 < n) issue(j + kStages - 1);
-    float m_new, alpha;
+    float m_new[QB], alpha[QB];
     bool r;
     if (j + 1 < n && kbeg + (j + 2) * kKeyTile > min(P, kend)) {
       r = body(j, Scur, Snext, true, m_new, alpha);
@@ -397,24 +455,29 @@ __global__ __launch_bounds__(512, 1) void attn_fwd8_kernel(FwdParams p) {
     }
     if (j + 1 >= n) {  // the scores past the last tile are not data
       r = false;
-      m_new = m_ref;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) m_new[qb] = m_ref[qb];
     }
     finish(r, m_new, alpha);
   };
   // hot steps: tile j+1 pure prefix, tile j+3 a full tile on the fast path
-  auto hot_step = [&](int j, f32x16 (&Scur)[2], f32x16 (&Snext)[2]) {
+  auto hot_step = [&](int j, f32x16 (&Scur)[QB][2], f32x16 (&Snext)[QB][2]) {
     wait_vmcnt<kOps>();
     __syncthreads();
     issue_fast(j + kStages - 1);
-    float m_new, alpha;
+    float m_new[QB], alpha[QB];
     const bool r = body(j, Scur, Snext, false, m_new, alpha);
     finish(r, m_new, alpha);
   };
 
   // Make the compiler wait for the Q loads before the first DMA (its own
   // wait at the first use of qf would also drain the ring).
-  asm volatile("" :: "v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]),
-               "v"(qf[4]), "v"(qf[5]), "v"(qf[6]), "v"(qf[7]));
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    asm volatile("" :: "v"(qf[qb][0]), "v"(qf[qb][1]), "v"(qf[qb][2]),
+                 "v"(qf[qb][3]), "v"(qf[qb][4]), "v"(qf[qb][5]),
+                 "v"(qf[qb][6]), "v"(qf[qb][7]));
+  }
   __syncthreads();  // page slice and mask window visible
 #pragma unroll
   for (int t = 0; t < kStages - 1; ++t) {
@@ -424,16 +487,20 @@ __global__ __launch_bounds__(512, 1) void attn_fwd8_kernel(FwdParams p) {
   else if (n == 2) wait_vmcnt<kOps>();
   else wait_vmcnt<0>();
   __syncthreads();
-  f32x16 SA[2], SB[2];
-  qk_block(0, 0, SA[0]);
-  qk_block(0, 1, SA[1]);
+  f32x16 SA[QB][2], SB[QB][2];
+  qk_block(0, 0, SA);
+  qk_block(0, 1, SA);
   if (kbeg + kKeyTile > min(P, kend)) {
-    apply_tile_mask(SA, tile_allow(kbeg), half);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      apply_tile_mask(SA[qb], tile_allow(kbeg, node[qb]), half);
+    }
   }
   {
-    float m_new, alpha;
+    float m_new[QB], alpha[QB];
     next_ref(SA, m_new, alpha);
-    m_ref = m_new;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) m_ref[qb] = m_new[qb];
   }
   int n_hot = 0;
   if (fast_pages) {
@@ -459,38 +526,45 @@ __global__ __launch_bounds__(512, 1) void attn_fwd8_kernel(FwdParams p) {
   }
 
   // ---- epilogue
-  const float l_tot = l_run + other_half(l_run);
-  if (!rvalid) return;
-  if (p.splits == 1) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    __bf16* op = p.out + qrow * kHeadDim;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
+  for (int qb = 0; qb < QB; ++qb) {
+    const float l_tot = l_run[qb] + other_half(l_run[qb]);
+    if (!rvalid[qb]) continue;
+    if (p.splits == 1) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      __bf16* op = p.out + qrow[qb] * kHeadDim;
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        bf16x4 v4;
+      for (int db = 0; db < 4; ++db) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(o[db][g4 * 4 + e] * inv);
-        *reinterpret_cast<bf16x4*>(op + db * 32 + g4 * 8 + half * 4) = v4;
+        for (int g4 = 0; g4 < 4; ++g4) {
+          bf16x4 v4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v4[e] = (__bf16)(o[qb][db][g4 * 4 + e] * inv);
+          }
+          *reinterpret_cast<bf16x4*>(op + db * 32 + g4 * 8 + half * 4) = v4;
+        }
       }
-    }
-    if (half == 0) {
-      p.lse[qrow] = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
-    }
-  } else {
-    const size_t prow = (size_t)split * p.N * p.Hq + qrow;
-    float* pp = p.part_o + prow * kHeadDim;
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        f32x4 v4 = {o[db][g4 * 4 + 0], o[db][g4 * 4 + 1], o[db][g4 * 4 + 2],
-                    o[db][g4 * 4 + 3]};
-        *reinterpret_cast<f32x4*>(pp + db * 32 + g4 * 8 + half * 4) = v4;
+      if (half == 0) {
+        p.lse[qrow[qb]] =
+            l_tot > 0.f ? (m_ref[qb] + log2f(l_tot)) * kLn2 : -INFINITY;
       }
-    }
-    if (half == 0) {
-      *reinterpret_cast<f32x2*>(p.part_ml + prow * 2) = f32x2{m_ref, l_tot};
+    } else {
+      const size_t prow = (size_t)split * p.N * p.Hq + qrow[qb];
+      float* pp = p.part_o + prow * kHeadDim;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          f32x4 v4 = {o[qb][db][g4 * 4 + 0], o[qb][db][g4 * 4 + 1],
+                      o[qb][db][g4 * 4 + 2], o[qb][db][g4 * 4 + 3]};
+          *reinterpret_cast<f32x4*>(pp + db * 32 + g4 * 8 + half * 4) = v4;
+        }
+      }
+      if (half == 0) {
+        *reinterpret_cast<f32x2*>(p.part_ml + prow * 2) =
+            f32x2{m_ref[qb], l_tot};
+      }
     }
   }
 }

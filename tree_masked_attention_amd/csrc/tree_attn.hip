@@ -17,12 +17,16 @@ using namespace tree_attn;
 
 namespace {
 
-constexpr int kAbiVersion = 3;
+constexpr int kAbiVersion = 4;
 constexpr int kMaxDevices = 64;
 constexpr int kMaxSplits = 256;
 constexpr int kMinKeysPerSplit = 256;
-// keys per workgroup from which the eight-wave kernel is used
-constexpr int kMinKeysPerWG8 = 4096;
+// keys per workgroup from which the 256-row kernel (8 waves of 32 rows) is
+// used.  Its 4-wave shape (64 rows per wave) halves the LDS reads per flop
+// but does not fit the register file with this schedule (the compiler
+// spills and shuffles accumulators), so it is not launched.
+constexpr int kMinKeysPerWG8 = 2048;
+constexpr int kWaves256 = 8;
 
 std::atomic<int> g_cu_count[kMaxDevices];
 
@@ -55,7 +59,8 @@ int ilog2(int x) {
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct Plan {
-  int nw = 8;        // 32-row query blocks per workgroup (4 waves)
+  int nw = 4;        // waves per workgroup
+  int qb = 1;        // 32-row query blocks per wave
   int mblocks = 0;   // row blocks per (sequence, kv head)
   int splits = 1;    // key-range splits
   int chunk = 0;     // keys per split (multiple of the 64-key tile)
@@ -85,9 +90,10 @@ int make_plan(int S, int N, int Hq, int Hkv, int max_prefix_len,
   // Splits of the key range so that the work units fill the CUs (or the
   // requested count), each a whole number of 64-key tiles.
   long long splits = 0, chunk = 0, units0 = 0;
-  auto choose = [&](int nw) -> int {
-    const int rows_per_wg = 32 * nw;
+  auto choose = [&](int nw, int qb) -> int {
+    const int rows_per_wg = 32 * nw * qb;
     pl.nw = nw;
+    pl.qb = qb;
     pl.mblocks = (int)std::max(1LL, (rows + rows_per_wg - 1) / rows_per_wg);
     units0 = (long long)S * Hkv * pl.mblocks;
     if (req_splits > 0) {
@@ -107,25 +113,29 @@ int make_plan(int S, int N, int Hq, int Hkv, int max_prefix_len,
     splits = (T + chunk - 1) / chunk;
     return TREE_ATTN_OK;
   };
-  // Eight waves (256 rows per workgroup, two waves per SIMD) pay off on
-  // long key ranges per workgroup; they need 256 rows and the ancestor-mask
-  // words of such a block (at most 256/G + 1 nodes) in the kernel's LDS
-  // cache.  Else four waves (128 rows; at most 129 nodes x 16 words, which
-  // always fits).
+  // 256 rows per workgroup (each staged K/V tile serves twice the rows)
+  // pays off on long key ranges per workgroup; it needs 256 rows and the
+  // ancestor-mask words of such a block (at most 256/G + 1 nodes) in the
+  // kernel's LDS cache.  Else 128 rows (at most 129 nodes x 16 words,
+  // which always fits).
   const long long mask_words = (max_nodes + 63) / 64;
   const long long nodes8 = (kRowsPerWG8 + G - 1) / G + 1;
   const bool can8 = rows >= kRowsPerWG8 && nodes8 * mask_words <= kMaskCache;
-  int nw = 4;
+  int nw = 4, qb = 1;
   if (can8) {
-    const int st = choose(8);
+    const int st = choose(kWaves256, 8 / kWaves256);
     if (st != TREE_ATTN_OK) return st;
-    if (chunk >= kMinKeysPerWG8) nw = 8;
+    if (chunk >= kMinKeysPerWG8) {
+      nw = kWaves256;
+      qb = 8 / kWaves256;
+    }
   }
-#ifdef TREE_ATTN_FORCE_NW  // build-time override for tuning runs
-  if (TREE_ATTN_FORCE_NW == 4 || can8) nw = TREE_ATTN_FORCE_NW;
+#ifdef TREE_ATTN_FORCE_SHAPE  // build-time override for tuning runs
+  if (TREE_ATTN_FORCE_SHAPE == 1) { nw = 4; qb = 1; }
+  if (TREE_ATTN_FORCE_SHAPE == 2 && can8) { nw = 8; qb = 1; }
 #endif
   {
-    const int st = choose(nw);
+    const int st = choose(nw, qb);
     if (st != TREE_ATTN_OK) return st;
   }
   pl.splits = (int)splits;
@@ -238,9 +248,10 @@ int tree_attn_describe_plan(int32_t num_seqs, int32_t total_nodes,
                  &pl);
   if (st != TREE_ATTN_OK) return st;
   info[0] = pl.nw;
-  info[1] = pl.splits;
-  info[2] = pl.chunk;
-  info[3] = 8 * ((pl.units + 7) / 8);
+  info[1] = 32 * pl.nw * pl.qb;
+  info[2] = pl.splits;
+  info[3] = pl.chunk;
+  info[4] = 8 * ((pl.units + 7) / 8);
   return TREE_ATTN_OK;
 }
 
@@ -319,7 +330,7 @@ int tree_attn_verify(const void* q, const void* k_cache, const void* v_cache,
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const unsigned grid = 8u * (unsigned)fp.per_xcd;
   if (pl.nw == 8) {
-    hipLaunchKernelGGL(attn_fwd8_kernel, dim3(grid), dim3(512), 0, hs, fp);
+    hipLaunchKernelGGL(attn_fwd256_kernel<8>, dim3(grid), dim3(512), 0, hs, fp);
   } else {
     hipLaunchKernelGGL(attn_fwd_kernel<1>, dim3(grid), dim3(256), 0, hs, fp);
   }
@@ -342,7 +353,7 @@ int tree_attn_verify(const void* q, const void* k_cache, const void* v_cache,
     mp.chunk = pl.chunk;
     mp.max_tokens = fp.max_tokens;
     mp.mblocks = pl.mblocks;
-    mp.rows_per_block = 32 * pl.nw;
+    mp.rows_per_block = 32 * pl.nw * pl.qb;
     const long long mgrid = (long long)num_seqs * num_kv_heads * pl.mblocks *
                             (mp.rows_per_block / kMergeRowsPerWG);
     hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)mgrid),
