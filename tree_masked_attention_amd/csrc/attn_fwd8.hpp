@@ -178,19 +178,27 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd256_kernel(FwdParams p) {
     k_row_off[k] = rw * tok_bytes + ((lchunk ^ (row & 15)) << 4);
     v_row_off[k] = rw * tok_bytes + ((lchunk ^ (4 * (row & 3))) << 4);
   }
-  auto issue_fast = [&](int t) {  // full tile, pages of >= kDmaRows tokens
-    const unsigned st = ring_base + (unsigned)(t & (kStages - 1)) * kTileBytes;
+  // DMA of a full tile on the fast path (pages of >= kDmaRows tokens), in
+  // pieces: the page lookup first, then part k (one K and one V
+  // instruction), so that a step can spread its DMA between segments
+  struct DmaPlan {
+    const char* kb0;
+    const char* vb0;
+    unsigned st;
+  };
+  auto dma_plan = [&](int t) -> DmaPlan {
     const int w0 = kbeg + t * kKeyTile + kDmaRows * wave;
     const int pi = clampi((w0 >> p.log2_page) - lp0, 0, kPageCache - 1);
     const unsigned pgu = (unsigned)__builtin_amdgcn_readfirstlane(pg_lds[pi]);
     const size_t off = (size_t)pgu * page_bytes +
                        (unsigned)(w0 & pmask) * tok_bytes + g * kHeadDim * 2;
-#pragma unroll
-    for (int k = 0; k < kOpsPerMat; ++k) {
-      const unsigned dst = st + (wave * kOpsPerMat + k) * 1024;
-      dma16_sbase(kbase + off, k_row_off[k], dst);
-      dma16_sbase(vbase + off, v_row_off[k], dst + kVOff);
-    }
+    return DmaPlan{kbase + off, vbase + off,
+                   ring_base + (unsigned)(t & (kStages - 1)) * kTileBytes};
+  };
+  auto dma_part = [&](const DmaPlan& dp, int k) {
+    const unsigned dst = dp.st + (wave * kOpsPerMat + k) * 1024;
+    dma16_sbase(dp.kb0, k_row_off[k], dst);
+    dma16_sbase(dp.vb0, v_row_off[k], dst + kVOff);
   };
   auto issue = [&](int t) {
     const int t0 = kbeg + t * kKeyTile;
@@ -381,9 +389,11 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd256_kernel(FwdParams p) {
   // only one and a half score tiles are live.  After the last tile the
   // scores are computed on stale LDS data and dropped.
   auto body = [&](int j, f32x16 (&Scur)[QB][2], f32x16 (&Snext)[QB][2],
-                  bool mask_next, float (&m_new)[QB],
+                  bool mask_next, bool dma_inbody, float (&m_new)[QB],
                   float (&alpha)[QB]) -> bool {
     bf16x8 pf[QB][2][2];
+    DmaPlan dp{};
+    if (dma_inbody) dp = dma_plan(j + kStages - 1);
     // segment 1: S^T(j+1) keys 0..31 | probabilities of keys 0..31
     qk_block(j + 1, 0, Snext);
     exps_block(Scur, 0, pf);
@@ -396,6 +406,11 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd256_kernel(FwdParams p) {
     // the segments are scheduled separately: without this fence the
     // scheduler mixes their groups and the matrix core waits more
     __builtin_amdgcn_sched_barrier(0);
+    if (dma_inbody) {  // first half of tile j+3's DMA
+#pragma unroll
+      for (int k = 0; k < kOpsPerMat / 2; ++k) dma_part(dp, k);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // segment 2: S^T(j+1) keys 32..63, PV(j) keys 0..31 | probabilities
     // of keys 32..63
     qk_block(j + 1, 1, Snext);
@@ -414,6 +429,11 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd256_kernel(FwdParams p) {
       __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
+    if (dma_inbody) {  // second half
+#pragma unroll
+      for (int k = kOpsPerMat / 2; k < kOpsPerMat; ++k) dma_part(dp, k);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // segment 3: PV(j) keys 32..63 | max of tile j+1
     pv_block(j, 1, pf);
     if (mask_next) {
@@ -449,9 +469,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd256_kernel(FwdParams p) {
     float m_new[QB], alpha[QB];
     bool r;
     if (j + 1 < n && kbeg + (j + 2) * kKeyTile > min(P, kend)) {
-      r = body(j, Scur, Snext, true, m_new, alpha);
+      r = body(j, Scur, Snext, true, false, m_new, alpha);
     } else {
-      r = body(j, Scur, Snext, false, m_new, alpha);
+      r = body(j, Scur, Snext, false, false, m_new, alpha);
     }
     if (j + 1 >= n) {  // the scores past the last tile are not data
       r = false;
@@ -464,9 +484,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd256_kernel(FwdParams p) {
   auto hot_step = [&](int j, f32x16 (&Scur)[QB][2], f32x16 (&Snext)[QB][2]) {
     wait_vmcnt<kOps>();
     __syncthreads();
-    issue_fast(j + kStages - 1);
     float m_new[QB], alpha[QB];
-    const bool r = body(j, Scur, Snext, false, m_new, alpha);
+    const bool r = body(j, Scur, Snext, false, true, m_new, alpha);
     finish(r, m_new, alpha);
   };
 
