@@ -299,7 +299,7 @@ def main():
 
     plan = api.describe_plan(S, N, Hq, wl.num_kv_heads, d, wl.max_prefix_len,
                              wl.max_nodes, wl.page_size, args.splits)
-    kname = ("attn_fwd8_kernel" if plan["waves"] == 8
+    kname = ("attn_fwd256_kernel<8>" if plan["rows"] == 256
              else "attn_fwd_kernel<1>")
     if plan["splits"] > 1:
         kname += " + attn_merge_kernel"
