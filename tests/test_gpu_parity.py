@@ -233,3 +233,52 @@ def test_standard_workload_parity(name):
     else:
         ro, rl = oracle.workload_attention(wl)
         assert_parity(got, ro, rl, name)
+
+
+# --------------------------------------------------------------------------
+# randomised shapes: seeded draws of heads, page size, prefixes, tree sizes
+# and shapes, split count (both kernel shapes get drawn)
+# --------------------------------------------------------------------------
+
+def _random_case(seed, wide=False):
+    """wide: shapes that take the 256-row kernel (>= 256 rows per kv head,
+    long key ranges, one or planned splits)."""
+    r = np.random.default_rng(seed)
+    hkv = int(r.choice([1, 2, 4]))
+    g = int(r.choice([4, 8]) if wide else r.choice([1, 2, 4, 8]))
+    s = int(r.integers(1, 5))
+    long_keys = wide or bool(r.integers(0, 2))
+    hi = 5000 if long_keys else 1500
+    prefix = [int(x) for x in r.integers(2500 if wide else 0, hi, size=s)]
+    sizes = [int(x) for x in r.integers(0, 300, size=s)]
+    if wide:
+        sizes[0] = max(sizes[0], 256 // g)
+    if max(sizes) == 0:
+        sizes[0] = 1
+    rules = [str(x) for x in r.choice(["pchain", "wide", "chain", "star"], size=s)]
+    page = int(r.choice([2, 4, 8, 16, 32, 64]))
+    splits = int(r.choice([0, 1] if wide else [0, 0, 1, 1, 2, 3, 7]))
+    wl = make_workload(seed, prefix_lens=prefix, tree_sizes=sizes,
+                       num_q_heads=g * hkv, num_kv_heads=hkv, page_size=page,
+                       tree_rules=rules, p_chain=float(r.uniform(0.2, 0.95)),
+                       name=f"random-{seed}")
+    return wl, splits
+
+
+@pytest.mark.parametrize("seed", list(range(500, 524)))
+def test_random_shapes_parity(seed):
+    import tree_masked_attention_amd.api as api
+    wl, splits = _random_case(seed, wide=seed >= 516)
+    plan = api.describe_plan(wl.num_seqs, wl.total_nodes, wl.num_q_heads,
+                             wl.num_kv_heads, wl.head_dim,
+                             wl.max_prefix_len, wl.max_nodes, wl.page_size,
+                             splits)
+    say(f"[gpu] random case {seed}: P={[int(x) for x in wl.prefix_lens]} "
+        f"B={[int(x) for x in wl.tree_sizes]} Hq={wl.num_q_heads} "
+        f"Hkv={wl.num_kv_heads} "
+        f"page={wl.page_size} splits={splits} plan={plan}")
+    got = run_gpu(wl, num_splits=splits)
+    assert np.array_equal(got["masks"], oracle.workload_masks(wl))
+    assert (got["bad"] == -1).all()
+    ref_out, ref_lse = oracle.workload_attention(wl)
+    assert_parity(got, ref_out, ref_lse, f"random-{seed}")
