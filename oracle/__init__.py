@@ -1,9 +1,10 @@
-"""CPU oracle for tree-causal verification attention (test infrastructure
-only: imported by the tests, the smoke check and the benchmark's CPU
+"""CPU oracle for tree-causal verification attention and the acceptance /
+KV-commit step after it (test infrastructure only: imported by the tests, the smoke check and the benchmark's CPU
 baseline, never by the library)."""
 
+from .accept_oracle import accept, accept_tree, commit_kv
 from .tree_oracle import (ancestor_masks, tree_attention, widen_bf16,
                           workload_attention, workload_masks)
 
-__all__ = ["ancestor_masks", "tree_attention", "widen_bf16",
+__all__ = ["accept", "accept_tree", "commit_kv", "ancestor_masks", "tree_attention", "widen_bf16",
            "workload_attention", "workload_masks"]

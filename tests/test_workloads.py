@@ -61,3 +61,16 @@ def test_standard_workload_structure(name):
                                    wl.tree_offsets[s + 1]]
                         == np.arange(63)) for s in range(8)]
         assert min(deep[1::2]) > 0.75 and max(deep[0::2]) < 0.5
+
+
+def test_draw_tokens_gives_multi_node_paths():
+    from oracle import accept
+    from tree_masked_attention_amd.workloads import draw_tokens, make_workload
+    wl = make_workload(3, prefix_lens=[5, 0, 17, 2], tree_sizes=[40, 1, 64, 9],
+                       num_q_heads=4, num_kv_heads=2)
+    d, t, r = draw_tokens(wl, 3)
+    assert d.shape == t.shape == (wl.total_nodes,) and r.shape == (4,)
+    lens, nodes, _ = accept(wl.parents, wl.tree_offsets, d, t, r, wl.max_nodes)
+    assert lens.max() >= 3
+    d2, t2, r2 = draw_tokens(wl, 3)
+    assert (d == d2).all() and (t == t2).all() and (r == r2).all()

@@ -339,6 +339,35 @@ STANDARD: Dict[str, tuple] = {
 STANDARD_ORDER = list(STANDARD.keys())
 
 
+def draw_tokens(wl: Workload, seed: int, vocab: int = 8,
+                p_agree: float = 0.7):
+    """Synthetic tokens for the acceptance step: each node's draft token,
+    the target's token after each node, and the target's token after each
+    sequence's prefix.  With probability p_agree the target's token after a
+    node (or after the prefix) is the draft token of one of the node's
+    children (or of one of the roots), so that accepted paths of several
+    nodes occur; otherwise it is uniform in [0, vocab)."""
+    rng = np.random.default_rng([seed, 7])
+    N, S = wl.total_nodes, wl.num_seqs
+    draft = rng.integers(0, vocab, size=N).astype(np.int32)
+    target = rng.integers(0, vocab, size=N).astype(np.int32)
+    root = rng.integers(0, vocab, size=S).astype(np.int32)
+    for s in range(S):
+        a, b = int(wl.tree_offsets[s]), int(wl.tree_offsets[s + 1])
+        children: Dict[int, List[int]] = {}
+        for i in range(b - a):
+            children.setdefault(int(wl.parents[a + i]), []).append(i)
+        for n in [-1] + list(range(b - a)):
+            ch = children.get(n)
+            if ch and rng.random() < p_agree:
+                tok = draft[a + ch[int(rng.integers(0, len(ch)))]]
+                if n < 0:
+                    root[s] = tok
+                else:
+                    target[a + n] = tok
+    return draft, target, root
+
+
 def standard_workload(name: str) -> Workload:
     seed, kw = STANDARD[name]
     return make_workload(seed, name=name, **kw)
