@@ -47,6 +47,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline")
+    ap.add_argument("--stage", choices=("verify", "accept-commit"),
+                    default="verify",
+                    help="verify: the verification path (default); "
+                         "accept-commit: tree acceptance + KV commit, the "
+                         "step after it")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain 512 MiB device copies (the "
                          "reference kernel for scaling HBM byte counters)")
@@ -164,6 +169,150 @@ def cpu_baseline(wl, target_s):
                       f"(mask build + fp64 attention), {t:.1f} s"}
 
 
+def cpu_baseline_accept(wl, tokens, target_s):
+    import oracle
+    d, t, r = tokens
+    reps, el = 0, 0.0
+    t0 = time.perf_counter()
+    while True:
+        lens, nodes, _ = oracle.accept(wl.parents, wl.tree_offsets, d, t, r,
+                                       wl.max_nodes)
+        oracle.commit_kv(wl.k_cache, wl.v_cache, wl.page_table,
+                         wl.prefix_lens, lens, nodes)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or el / reps * (reps + 1) > 30.0:
+            break
+    return {"value": wl.total_nodes * reps / el, "unit": "tree tokens/s",
+            "cores": 1, "kind": "oracle",
+            "sample": f"{reps} full pass(es) of workload {wl.name} "
+                      f"(acceptance + commit on copies of the caches), "
+                      f"{el:.1f} s"}
+
+
+def accept_commit_stage(args, torch, api, wl, sets, stream):
+    """Times tree_attn_accept + tree_attn_commit_kv, the step after the
+    verification: masks are built once per input copy beforehand."""
+    from tree_masked_attention_amd.workloads import draw_tokens
+    dev = torch.device("cuda:0")
+    N, S, W = wl.total_nodes, wl.num_seqs, wl.mask_words()
+    max_b = max(wl.max_nodes, 1)
+    tokens = draw_tokens(wl, 1)
+    tok = [torch.from_numpy(a).to(dev) for a in tokens]
+    lens = torch.empty((max(S, 1),), dtype=torch.int32, device=dev)
+    nodes = torch.empty((max(S, 1), max_b), dtype=torch.int32, device=dev)
+    bonus = torch.empty((max(S, 1),), dtype=torch.int32, device=dev)
+    token_bytes = wl.num_kv_heads * wl.head_dim * 2
+    sptr = stream.cuda_stream
+    calls = []
+    for c in sets:
+        masks, _ = api.build_mask(c["parents"], c["offs"], max_b, W)
+        c["masks"] = masks
+        acc = (c["parents"].data_ptr(), c["offs"].data_ptr(),
+               masks.data_ptr(), W, tok[0].data_ptr(), tok[1].data_ptr(),
+               tok[2].data_ptr(), S, N, max_b, lens.data_ptr(),
+               nodes.data_ptr(), bonus.data_ptr(), sptr)
+        com = (c["k"].data_ptr(), c["v"].data_ptr(), c["table"].data_ptr(),
+               wl.max_pages_per_seq, wl.num_pages, wl.page_size,
+               c["prefix"].data_ptr(), lens.data_ptr(), nodes.data_ptr(), S,
+               max_b, token_bytes, sptr)
+        calls.append((acc, com))
+    f_acc = api._lib.tree_attn_accept
+    f_com = api._lib.tree_attn_commit_kv
+
+    def step(i, ev=None):
+        a, cm = calls[i % len(calls)]
+        if ev is not None:
+            ev[0].record(stream)
+        rc = f_acc(*a)
+        if ev is not None:
+            ev[1].record(stream)
+        rc |= f_com(*cm)
+        if ev is not None:
+            ev[2].record(stream)
+        return rc
+
+    n_warm = 0
+    t_w = time.perf_counter()
+    while n_warm < max(args.warmup, 1) or time.perf_counter() - t_w < 0.1:
+        if step(n_warm) != 0:
+            raise RuntimeError("tree_attn call failed during warmup")
+        n_warm += 1
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+           for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    acc_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    com_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+
+    L = lens[:S].cpu().numpy()
+    nd = nodes[:S].cpu().numpy()
+    moved = int(sum(int((nd[s, :L[s]] != np.arange(L[s])).sum())
+                    for s in range(S)))
+    # commit: each moved row read once and written once, in K and in V;
+    # the accepted lists and page-table entries read once
+    com_bytes = moved * token_bytes * 2 * 2 + S * (max_b * 4 + 12) + \
+        8 * moved
+    # accept: per node its parent, draft and target token, the target token
+    # of its parent and its mask row; per sequence the outputs
+    acc_bytes = N * (16 + W * 8) + S * (max_b * 4 + 12)
+    log(f"[bench] accept {acc_ms * 1e3:.1f} us, commit {com_ms * 1e3:.1f} us, "
+        f"step {ms_per_step * 1e3:.1f} us; tau {L.tolist()[:8]}, "
+        f"{moved} rows moved")
+    achieved = com_bytes / (com_ms * 1e-3) / 1e9
+    result = {
+        "metric": "tree acceptance + KV commit, tree tokens/s",
+        "value": N / (ms_per_step * 1e-3),
+        "unit": "tree tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "warmup_steps_run": n_warm,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int32",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "stage": "accept-commit", "num_seqs": S,
+            "tree_nodes_per_seq": int(wl.max_nodes),
+            "token_bytes": token_bytes, "accepted": [int(x) for x in L][:8],
+            "rows_moved": moved,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "tree_attn_commit_kv (commit_kv_kernel)",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": None,
+            "alg_bytes_per_launch": com_bytes,
+            "avg_launch_us": com_ms * 1e3,
+        },
+        "accept_us": acc_ms * 1e3,
+        "accept_alg_bytes": acc_bytes,
+        "commit_us": com_ms * 1e3,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] CPU baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline_accept(wl, tokens,
+                                                     args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 # --------------------------------------------------------------------------
 # GPU timing
 # --------------------------------------------------------------------------
@@ -206,6 +355,10 @@ def main():
     for _ in range(copies):
         sets.append({k: t.to(dev) for k, t in host.items()})
 
+    stream = torch.cuda.current_stream()
+    if args.stage == "accept-commit":
+        return accept_commit_stage(args, torch, api, wl, sets, stream)
+
     N, Hq, d = wl.q.shape
     S = wl.num_seqs
     W = wl.mask_words()
@@ -218,7 +371,6 @@ def main():
                                   wl.max_prefix_len, wl.max_nodes,
                                   wl.page_size, args.splits)
     ws = torch.empty((max(ws_bytes, 256),), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
 
     # pre-marshalled C-ABI argument lists, one per input copy

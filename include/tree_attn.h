@@ -180,6 +180,102 @@ int tree_attn_verify(const void* q, const void* k_cache, const void* v_cache,
                      void* out, float* lse, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/*
+ * tree_attn_accept - the accepted path of every verified draft tree.
+ *
+ * After the verification pass the target model has, for every tree node n,
+ * the token it would emit next (target_tokens[n]) and, per sequence, the
+ * token it would emit right after the prefix (root_tokens[s]).  Decoding
+ * then keeps the accepted part of the tree, tau tokens per step (JETFLOW,
+ * gist.science 2606.18394, section 4, where tau is reported per budget).
+ * The pages do not spell out the acceptance rule; this library takes
+ * exact match against the target's choices:
+ *  - local node i of tree s matches when draft_tokens[n] (n the global
+ *    index) equals the target's token after its parent: root_tokens[s] for
+ *    a root, else target_tokens[tree_offsets[s] + parents[n]];
+ *  - the accepted path is the longest root-to-node path whose nodes all
+ *    match; among equally long ones, the one ending at the smallest local
+ *    index.  With distinct draft tokens among siblings this is the usual
+ *    walk down the one matching child.
+ *
+ *   parents, tree_offsets, num_seqs, total_nodes, max_nodes
+ *                 as for tree_attn_build_mask
+ *   masks, mask_words   the rows tree_attn_build_mask wrote for these trees
+ *                 (W words per node; the path is read from them)
+ *   draft_tokens  dev int32 [total_nodes]  token of each draft node
+ *   target_tokens dev int32 [total_nodes]  target's token after each node
+ *   root_tokens   dev int32 [num_seqs]     target's token after the prefix
+ *   accept_len    dev int32 [num_seqs] (output): tau_s, 0 .. B_s
+ *   accept_nodes  dev int32 [num_seqs][max_nodes] (output): the accepted
+ *                 path as local node indices, root first, then -1 to the
+ *                 end of the row
+ *   bonus_tokens  dev int32 [num_seqs] (output): the target's token after
+ *                 the last accepted node, root_tokens[s] when tau_s = 0
+ *
+ * Trees that tree_attn_build_mask reports invalid, or masks that are not
+ * its rows for these trees, give unspecified output for that sequence but
+ * no access outside the buffers above.
+ *
+ * Host-side errors: ERR_SHAPE (negative sizes, mask_words < 1,
+ * mask_words * 64 < max_nodes), ERR_UNSUPPORTED (mask_words > 16,
+ * max_nodes > TREE_ATTN_MAX_NODES), ERR_NULL (a NULL pointer that the
+ * sizes make necessary), ERR_HIP.
+ */
+int tree_attn_accept(const int32_t* parents, const int32_t* tree_offsets,
+                     const uint64_t* masks, int32_t mask_words,
+                     const int32_t* draft_tokens, const int32_t* target_tokens,
+                     const int32_t* root_tokens, int32_t num_seqs,
+                     int32_t total_nodes, int32_t max_nodes,
+                     int32_t* accept_len, int32_t* accept_nodes,
+                     int32_t* bonus_tokens, void* stream);
+
+/*
+ * tree_attn_commit_kv - moves the accepted nodes' keys and values to the
+ * front of the tree's region of the paged cache, in place.
+ *
+ * The cache commit waits until the accepted branch is known (DFlash-TfM,
+ * gist.science 2607.06763, method section on rollback-free verification;
+ * there for the recurrent state, here for the attention cache).  Node n of
+ * sequence s sits at logical position prefix_lens[s] + n (as in
+ * tree_attn_verify); for j = 0 .. accept_len[s]-1 the token row at
+ * position prefix_lens[s] + accept_nodes[s][j] is copied to position
+ * prefix_lens[s] + j, in k_cache and in v_cache, byte for byte.  Rows
+ * already in place are not copied; every other row keeps its contents.
+ * The result equals doing the copies one by one in increasing j, which
+ * never reads a row an earlier copy wrote, provided accept_nodes[s] is
+ * strictly increasing (as tree_attn_accept writes it).
+ *
+ *   k_cache, v_cache  dev [num_pages, page_size, token_bytes] bytes of any
+ *                 element type (bf16 [.., num_kv_heads, head_dim] gives
+ *                 token_bytes = num_kv_heads * head_dim * 2); 16-byte
+ *                 aligned; read and written
+ *   page_table    dev int32 [num_seqs, max_pages_per_seq]
+ *   page_size     power of two
+ *   prefix_lens   dev int32 [num_seqs]
+ *   accept_len, accept_nodes   as written by tree_attn_accept
+ *   max_nodes     columns of accept_nodes, <= TREE_ATTN_MAX_NODES
+ *   token_bytes   bytes of one token row of one cache, a positive multiple
+ *                 of 16, at most 1 MiB
+ *
+ * Pages that hold positions at or past prefix_lens[s] must belong to
+ * sequence s alone.  A copy whose source or destination page lies outside
+ * the page table or outside [0, num_pages) is skipped; a row list that is
+ * not strictly increasing gives unspecified rows of that sequence, but no
+ * access outside the buffers above.
+ *
+ * Host-side errors: ERR_SHAPE (negative sizes, page_size not a power of
+ * two, token_bytes not a positive multiple of 16, caches not 16-byte
+ * aligned), ERR_UNSUPPORTED (max_nodes > TREE_ATTN_MAX_NODES, token_bytes
+ * > 1 MiB), ERR_NULL, ERR_HIP.
+ */
+int tree_attn_commit_kv(void* k_cache, void* v_cache,
+                        const int32_t* page_table, int32_t max_pages_per_seq,
+                        int32_t num_pages, int32_t page_size,
+                        const int32_t* prefix_lens, const int32_t* accept_len,
+                        const int32_t* accept_nodes, int32_t num_seqs,
+                        int32_t max_nodes, int32_t token_bytes,
+                        void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -127,3 +127,74 @@ def test_describe_plan():
         api.describe_plan(1, 16, 8, 3, 128, 256, 16, 16, 0)
     with pytest.raises(NotImplementedError):
         api.describe_plan(1, 16, 8, 2, 64, 256, 16, 16, 0)
+
+
+def _accept(**over):
+    a = dict(parents=1, offs=1, masks=1, W=1, draft=1, target=1, root=1, S=1,
+             N=16, max_b=16, lens=1, nodes=1, bonus=1)
+    a.update(over)
+    return int(api._lib.tree_attn_accept(
+        a["parents"], a["offs"], a["masks"], a["W"], a["draft"], a["target"],
+        a["root"], a["S"], a["N"], a["max_b"], a["lens"], a["nodes"],
+        a["bonus"], None))
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(S=-1), api.ERR_SHAPE),
+    (dict(N=-1), api.ERR_SHAPE),
+    (dict(W=0), api.ERR_SHAPE),
+    (dict(max_b=65, W=1), api.ERR_SHAPE),
+    (dict(max_b=2000, W=32), api.ERR_UNSUPPORTED),
+    (dict(max_b=16, W=17), api.ERR_UNSUPPORTED),
+    (dict(parents=None), api.ERR_NULL),
+    (dict(masks=None), api.ERR_NULL),
+    (dict(draft=None), api.ERR_NULL),
+    (dict(target=None), api.ERR_NULL),
+    (dict(root=None), api.ERR_NULL),
+    (dict(lens=None), api.ERR_NULL),
+    (dict(nodes=None), api.ERR_NULL),
+    (dict(bonus=None), api.ERR_NULL),
+])
+def test_accept_rejects(over, code):
+    assert _accept(**over) == code
+
+
+def test_accept_empty_is_noop():
+    assert _accept(S=0, parents=None, offs=None, masks=None, lens=None,
+                   nodes=None) == api.OK
+
+
+def _commit(**over):
+    a = dict(k=256, v=512, table=1, max_pps=4, num_pages=8, page_size=16,
+             prefix=1, lens=1, nodes=1, S=1, max_b=16, token_bytes=4096)
+    a.update(over)
+    return int(api._lib.tree_attn_commit_kv(
+        a["k"], a["v"], a["table"], a["max_pps"], a["num_pages"],
+        a["page_size"], a["prefix"], a["lens"], a["nodes"], a["S"],
+        a["max_b"], a["token_bytes"], None))
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(S=-1), api.ERR_SHAPE),
+    (dict(max_pps=-1), api.ERR_SHAPE),
+    (dict(num_pages=-1), api.ERR_SHAPE),
+    (dict(page_size=12), api.ERR_SHAPE),
+    (dict(token_bytes=0), api.ERR_SHAPE),
+    (dict(token_bytes=24), api.ERR_SHAPE),
+    (dict(k=8), api.ERR_SHAPE),                 # not 16-byte aligned
+    (dict(token_bytes=(1 << 20) + 16), api.ERR_UNSUPPORTED),
+    (dict(max_b=2048), api.ERR_UNSUPPORTED),
+    (dict(k=None), api.ERR_NULL),
+    (dict(v=None), api.ERR_NULL),
+    (dict(table=None), api.ERR_NULL),
+    (dict(prefix=None), api.ERR_NULL),
+    (dict(lens=None), api.ERR_NULL),
+    (dict(nodes=None), api.ERR_NULL),
+])
+def test_commit_rejects(over, code):
+    assert _commit(**over) == code
+
+
+def test_commit_empty_is_noop():
+    assert _commit(S=0, k=None, v=None) == api.OK
+    assert _commit(max_b=0, k=None) == api.OK

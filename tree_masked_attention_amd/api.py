@@ -44,9 +44,17 @@ _lib.tree_attn_verify.argtypes = (
 _lib.tree_attn_describe_plan.restype = ctypes.c_int
 _lib.tree_attn_describe_plan.argtypes = [_i] * 9 + [_p]
 
+_lib.tree_attn_accept.restype = ctypes.c_int
+_lib.tree_attn_accept.argtypes = [_p, _p, _p, _i, _p, _p, _p, _i, _i, _i,
+                                  _p, _p, _p, _p]
+_lib.tree_attn_commit_kv.restype = ctypes.c_int
+_lib.tree_attn_commit_kv.argtypes = [_p, _p, _p, _i, _i, _i, _p, _p, _p, _i,
+                                     _i, _i, _p]
+
 EXPORTED = ("tree_attn_status_string", "tree_attn_abi_version",
             "tree_attn_build_mask", "tree_attn_workspace_size",
-            "tree_attn_describe_plan", "tree_attn_verify")
+            "tree_attn_describe_plan", "tree_attn_verify",
+            "tree_attn_accept", "tree_attn_commit_kv")
 
 
 class TreeAttnError(RuntimeError):
@@ -210,3 +218,77 @@ def verify(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         _ptr(lse), _ptr(workspace), ws_len, _stream(stream))
     _raise(code, "tree_attn_verify")
     return out, lse
+
+
+def accept(parents: torch.Tensor, tree_offsets: torch.Tensor,
+           masks: torch.Tensor, draft_tokens: torch.Tensor,
+           target_tokens: torch.Tensor, root_tokens: torch.Tensor,
+           max_nodes: int, accept_len: Optional[torch.Tensor] = None,
+           accept_nodes: Optional[torch.Tensor] = None,
+           bonus_tokens: Optional[torch.Tensor] = None,
+           stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Accepted path of every draft tree (exact match on the target's
+    tokens).  parents / tree_offsets / masks as for build_mask; draft and
+    target tokens int32 [N], root_tokens int32 [S].  Returns (accept_len
+    int32 [S], accept_nodes int32 [S, max_nodes] padded with -1,
+    bonus_tokens int32 [S])."""
+    for t, n in ((parents, "parents"), (tree_offsets, "tree_offsets"),
+                 (draft_tokens, "draft_tokens"),
+                 (target_tokens, "target_tokens"),
+                 (root_tokens, "root_tokens")):
+        _dev(t, torch.int32, n)
+    _dev(masks, torch.int64, "masks")
+    S = tree_offsets.numel() - 1
+    N = parents.numel()
+    if draft_tokens.numel() != N or target_tokens.numel() != N or \
+            root_tokens.numel() != S:
+        raise ValueError("token arrays do not match the trees")
+    if masks.dim() != 2 or masks.shape[0] != N:
+        raise ValueError("masks must be [N, W]")
+    dev = parents.device
+    if accept_len is None:
+        accept_len = torch.empty((max(S, 1),), dtype=torch.int32, device=dev)
+    if accept_nodes is None:
+        accept_nodes = torch.empty((max(S, 1), int(max_nodes)),
+                                   dtype=torch.int32, device=dev)
+    if bonus_tokens is None:
+        bonus_tokens = torch.empty((max(S, 1),), dtype=torch.int32,
+                                   device=dev)
+    code = _lib.tree_attn_accept(
+        _ptr(parents), _ptr(tree_offsets), _ptr(masks), masks.shape[1],
+        _ptr(draft_tokens), _ptr(target_tokens), _ptr(root_tokens), S, N,
+        int(max_nodes), _ptr(accept_len), _ptr(accept_nodes),
+        _ptr(bonus_tokens), _stream(stream))
+    _raise(code, "tree_attn_accept")
+    return accept_len[:S], accept_nodes[:S], bonus_tokens[:S]
+
+
+def commit_kv(k_cache: torch.Tensor, v_cache: torch.Tensor,
+              page_table: torch.Tensor, prefix_lens: torch.Tensor,
+              accept_len: torch.Tensor, accept_nodes: torch.Tensor,
+              stream=None) -> None:
+    """Moves the accepted nodes' cache rows to positions P_s .. P_s+tau-1,
+    in place.  k_cache / v_cache [num_pages, page_size, ...] of any dtype
+    (same shape and dtype); accept_len / accept_nodes from accept()."""
+    for t, n in ((page_table, "page_table"), (prefix_lens, "prefix_lens"),
+                 (accept_len, "accept_len"), (accept_nodes, "accept_nodes")):
+        _dev(t, torch.int32, n)
+    _dev(k_cache, k_cache.dtype, "k_cache")
+    _dev(v_cache, k_cache.dtype, "v_cache")
+    if k_cache.shape != v_cache.shape or k_cache.dim() < 2:
+        raise ValueError("k_cache and v_cache must both be "
+                         "[num_pages, page_size, ...]")
+    S = prefix_lens.numel()
+    if page_table.dim() != 2 or page_table.shape[0] != S or \
+            accept_len.numel() != S or accept_nodes.dim() != 2 or \
+            accept_nodes.shape[0] != S:
+        raise ValueError("page_table / accept arrays do not match prefix_lens")
+    num_pages, page_size = k_cache.shape[0], k_cache.shape[1]
+    token_bytes = (k_cache[0, 0].numel() * k_cache.element_size()
+                   if num_pages else 16)
+    code = _lib.tree_attn_commit_kv(
+        _ptr(k_cache), _ptr(v_cache), _ptr(page_table), page_table.shape[1],
+        num_pages, page_size, _ptr(prefix_lens), _ptr(accept_len),
+        _ptr(accept_nodes), S, accept_nodes.shape[1], token_bytes,
+        _stream(stream))
+    _raise(code, "tree_attn_commit_kv")

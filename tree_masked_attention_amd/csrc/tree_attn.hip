@@ -7,6 +7,7 @@
 #include <atomic>
 #include <cmath>
 
+#include "accept_commit.hpp"
 #include "attn_fwd.hpp"
 #include "attn_fwd8.hpp"
 #include "attn_merge.hpp"
@@ -17,7 +18,7 @@ using namespace tree_attn;
 
 namespace {
 
-constexpr int kAbiVersion = 4;
+constexpr int kAbiVersion = 5;
 constexpr int kMaxDevices = 64;
 constexpr int kMaxSplits = 256;
 constexpr int kMinKeysPerSplit = 256;
@@ -27,6 +28,7 @@ constexpr int kMinKeysPerSplit = 256;
 // spills and shuffles accumulators), so it is not launched.
 constexpr int kMinKeysPerWG8 = 2048;
 constexpr int kWaves256 = 8;
+constexpr int kMaxTokenBytes = 1 << 20;
 
 std::atomic<int> g_cu_count[kMaxDevices];
 
@@ -361,6 +363,85 @@ int tree_attn_verify(const void* q, const void* k_cache, const void* v_cache,
     if (hipGetLastError() != hipSuccess) return TREE_ATTN_ERR_HIP;
   }
   return TREE_ATTN_OK;
+}
+
+int tree_attn_accept(const int32_t* parents, const int32_t* tree_offsets,
+                     const uint64_t* masks, int32_t mask_words,
+                     const int32_t* draft_tokens, const int32_t* target_tokens,
+                     const int32_t* root_tokens, int32_t num_seqs,
+                     int32_t total_nodes, int32_t max_nodes,
+                     int32_t* accept_len, int32_t* accept_nodes,
+                     int32_t* bonus_tokens, void* stream) {
+  if (num_seqs < 0 || total_nodes < 0 || max_nodes < 0 || mask_words < 1) {
+    return TREE_ATTN_ERR_SHAPE;
+  }
+  if (mask_words > kAcceptMaxWords || max_nodes > TREE_ATTN_MAX_NODES) {
+    return TREE_ATTN_ERR_UNSUPPORTED;
+  }
+  if ((long long)mask_words * 64 < max_nodes) return TREE_ATTN_ERR_SHAPE;
+  if (num_seqs == 0) return TREE_ATTN_OK;
+  if (!tree_offsets || !root_tokens || !accept_len || !bonus_tokens) {
+    return TREE_ATTN_ERR_NULL;
+  }
+  if (max_nodes > 0 && !accept_nodes) return TREE_ATTN_ERR_NULL;
+  if (total_nodes > 0 &&
+      (!parents || !masks || !draft_tokens || !target_tokens)) {
+    return TREE_ATTN_ERR_NULL;
+  }
+  // one thread per node of the largest tree, whole waves
+  const int threads = (std::max(1, (int)max_nodes) + 63) / 64 * 64;
+  hipLaunchKernelGGL(accept_kernel, dim3(num_seqs), dim3(threads), 0,
+                     reinterpret_cast<hipStream_t>(stream), parents,
+                     tree_offsets, masks, (int)mask_words, draft_tokens,
+                     target_tokens, root_tokens, (int)total_nodes,
+                     (int)max_nodes, accept_len, accept_nodes, bonus_tokens);
+  return hipGetLastError() == hipSuccess ? TREE_ATTN_OK : TREE_ATTN_ERR_HIP;
+}
+
+int tree_attn_commit_kv(void* k_cache, void* v_cache,
+                        const int32_t* page_table, int32_t max_pages_per_seq,
+                        int32_t num_pages, int32_t page_size,
+                        const int32_t* prefix_lens, const int32_t* accept_len,
+                        const int32_t* accept_nodes, int32_t num_seqs,
+                        int32_t max_nodes, int32_t token_bytes,
+                        void* stream) {
+  if (num_seqs < 0 || max_nodes < 0 || max_pages_per_seq < 0 ||
+      num_pages < 0 || token_bytes <= 0 || token_bytes % 16 != 0 ||
+      !is_pow2(page_size)) {
+    return TREE_ATTN_ERR_SHAPE;
+  }
+  if (max_nodes > TREE_ATTN_MAX_NODES || token_bytes > kMaxTokenBytes) {
+    return TREE_ATTN_ERR_UNSUPPORTED;
+  }
+  if (num_seqs == 0 || max_nodes == 0) return TREE_ATTN_OK;
+  if (!k_cache || !v_cache || !page_table || !prefix_lens || !accept_len ||
+      !accept_nodes) {
+    return TREE_ATTN_ERR_NULL;
+  }
+  if ((reinterpret_cast<uintptr_t>(k_cache) |
+       reinterpret_cast<uintptr_t>(v_cache)) % 16 != 0) {
+    return TREE_ATTN_ERR_SHAPE;
+  }
+  CommitParams cp;
+  cp.k = static_cast<uint8_t*>(k_cache);
+  cp.v = static_cast<uint8_t*>(v_cache);
+  cp.page_table = page_table;
+  cp.prefix_lens = prefix_lens;
+  cp.accept_len = accept_len;
+  cp.accept_nodes = accept_nodes;
+  cp.max_pages = max_pages_per_seq;
+  cp.num_pages = num_pages;
+  cp.log2_page = ilog2(page_size);
+  cp.max_nodes = max_nodes;
+  cp.pieces = token_bytes / 16;
+  cp.slices = (2 * cp.pieces + kCommitThreads - 1) / kCommitThreads;
+  cp.token_bytes = token_bytes;
+  const long long grid = (long long)num_seqs * cp.slices;
+  if (grid > 0x7fffffffLL) return TREE_ATTN_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(commit_kv_kernel, dim3((unsigned)grid),
+                     dim3(kCommitThreads), 0,
+                     reinterpret_cast<hipStream_t>(stream), cp);
+  return hipGetLastError() == hipSuccess ? TREE_ATTN_OK : TREE_ATTN_ERR_HIP;
 }
 
 }  // extern "C"
