@@ -11,6 +11,10 @@ Infinity Cache left there by the previous step.
 Warmup runs the requested W steps and keeps going, back to back, until the
 path has run for about 0.3 s.
 
+--stage accept-commit times the step after the verification instead:
+tree acceptance and the commit of the accepted rows' K/V (one fused launch,
+with the two-launch form beside it), on tokens drawn for the workload.
+
 Prints one JSON line on stdout.  Everything else goes to stderr.
 """
 
@@ -62,14 +66,18 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "hbm_traffic.txt")
 
 
+VERIFY_PATH_EXCLUDED = ("accept_commit.hpp",)  # kernels after the path
+
+
 def kernel_source_hash():
-    """Hash of the HIP sources: HBM counters taken on other sources are
-    not reported."""
+    """Hash of the HIP sources of the verification path: HBM counters
+    taken on other sources are not reported."""
     import hashlib
     csrc = os.path.join(HERE, "tree_masked_attention_amd", "csrc")
     h = hashlib.sha256()
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp", ".h")):
+        if name.endswith((".hip", ".hpp", ".h")) and \
+                name not in VERIFY_PATH_EXCLUDED:
             with open(os.path.join(csrc, name), "rb") as f:
                 h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -191,8 +199,10 @@ def cpu_baseline_accept(wl, tokens, target_s):
 
 
 def accept_commit_stage(args, torch, api, wl, sets, stream):
-    """Times tree_attn_accept + tree_attn_commit_kv, the step after the
-    verification: masks are built once per input copy beforehand."""
+    """Times the step after the verification: tree_attn_accept +
+    tree_attn_commit_kv (two launches) and tree_attn_accept_commit (one
+    launch, the reported value).  Masks are built once per input copy
+    beforehand."""
     from tree_masked_attention_amd.workloads import draw_tokens
     dev = torch.device("cuda:0")
     N, S, W = wl.total_nodes, wl.num_seqs, wl.mask_words()
@@ -219,8 +229,9 @@ def accept_commit_stage(args, torch, api, wl, sets, stream):
         calls.append((acc, com))
     f_acc = api._lib.tree_attn_accept
     f_com = api._lib.tree_attn_commit_kv
+    f_fused = api._lib.tree_attn_accept_commit
 
-    def step(i, ev=None):
+    def step_separate(i, ev=None):
         a, cm = calls[i % len(calls)]
         if ev is not None:
             ev[0].record(stream)
@@ -232,28 +243,45 @@ def accept_commit_stage(args, torch, api, wl, sets, stream):
             ev[2].record(stream)
         return rc
 
-    n_warm = 0
-    t_w = time.perf_counter()
-    while n_warm < max(args.warmup, 1) or time.perf_counter() - t_w < 0.1:
-        if step(n_warm) != 0:
-            raise RuntimeError("tree_attn call failed during warmup")
-        n_warm += 1
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = t0.elapsed_time(t1) / args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
-           for _ in range(args.steps)]
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    acc_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    com_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    def step_fused(i, ev=None):
+        a, cm = calls[i % len(calls)]
+        if ev is not None:
+            ev[0].record(stream)
+        # tree_attn_accept_commit takes the accept arguments, then the
+        # cache arguments of tree_attn_commit_kv, then the outputs
+        rc = f_fused(*a[:10], cm[0], cm[1], cm[2], cm[3], cm[4], cm[5],
+                     cm[6], cm[11], *a[10:])
+        if ev is not None:
+            ev[1].record(stream)
+        return rc
+
+    def timed(step, n_ev):
+        n_warm = 0
+        t_w = time.perf_counter()
+        while n_warm < max(args.warmup, 1) or time.perf_counter() - t_w < 0.1:
+            if step(n_warm) != 0:
+                raise RuntimeError("tree_attn call failed during warmup")
+            n_warm += 1
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for i in range(args.steps):
+            step(i)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / args.steps
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+               for _ in range(args.steps)]
+        for i in range(args.steps):
+            step(i, evs[i])
+        torch.cuda.synchronize()
+        per = [float(np.mean([e[k].elapsed_time(e[k + 1]) for e in evs]))
+               for k in range(n_ev - 1)]
+        return ms, per, n_warm
+
+    sep_ms, (acc_ms, com_ms), _ = timed(step_separate, 3)
+    ms_per_step, (fused_ms,), n_warm = timed(step_fused, 2)
 
     L = lens[:S].cpu().numpy()
     nd = nodes[:S].cpu().numpy()
@@ -266,10 +294,12 @@ def accept_commit_stage(args, torch, api, wl, sets, stream):
     # accept: per node its parent, draft and target token, the target token
     # of its parent and its mask row; per sequence the outputs
     acc_bytes = N * (16 + W * 8) + S * (max_b * 4 + 12)
-    log(f"[bench] accept {acc_ms * 1e3:.1f} us, commit {com_ms * 1e3:.1f} us, "
-        f"step {ms_per_step * 1e3:.1f} us; tau {L.tolist()[:8]}, "
-        f"{moved} rows moved")
-    achieved = com_bytes / (com_ms * 1e-3) / 1e9
+    log(f"[bench] separate: accept {acc_ms * 1e3:.1f} us, commit "
+        f"{com_ms * 1e3:.1f} us, step {sep_ms * 1e3:.1f} us; fused: launch "
+        f"{fused_ms * 1e3:.1f} us, step {ms_per_step * 1e3:.1f} us; "
+        f"tau {L.tolist()[:8]}, {moved} rows moved")
+    fused_bytes = com_bytes + acc_bytes
+    achieved = fused_bytes / (fused_ms * 1e-3) / 1e9
     result = {
         "metric": "tree acceptance + KV commit, tree tokens/s",
         "value": N / (ms_per_step * 1e-3),
@@ -292,18 +322,20 @@ def accept_commit_stage(args, torch, api, wl, sets, stream):
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "tree_attn_commit_kv (commit_kv_kernel)",
+            "kernel": "tree_attn_accept_commit (accept_commit_kernel)",
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
             "traffic": None,
-            "alg_bytes_per_launch": com_bytes,
-            "avg_launch_us": com_ms * 1e3,
+            "alg_bytes_per_launch": fused_bytes,
+            "avg_launch_us": fused_ms * 1e3,
         },
+        "separate_ms_per_step": sep_ms,
         "accept_us": acc_ms * 1e3,
         "accept_alg_bytes": acc_bytes,
         "commit_us": com_ms * 1e3,
+        "commit_alg_bytes": com_bytes,
     }
     if not args.no_cpu_baseline:
         log("[bench] CPU baseline (oracle)")

@@ -276,6 +276,28 @@ int tree_attn_commit_kv(void* k_cache, void* v_cache,
                         int32_t max_nodes, int32_t token_bytes,
                         void* stream);
 
+/*
+ * tree_attn_accept_commit - tree_attn_accept followed by
+ * tree_attn_commit_kv, in one launch.
+ *
+ * Arguments as for those two calls (token_bytes, the caches and the page
+ * table as for tree_attn_commit_kv; the accepted lists are outputs here).
+ * Results are identical to the two calls made in order: the path is found
+ * on chip and the copies are planned from it without a round trip through
+ * memory.
+ *
+ * Host-side errors: those of both calls.
+ */
+int tree_attn_accept_commit(
+    const int32_t* parents, const int32_t* tree_offsets,
+    const uint64_t* masks, int32_t mask_words, const int32_t* draft_tokens,
+    const int32_t* target_tokens, const int32_t* root_tokens,
+    int32_t num_seqs, int32_t total_nodes, int32_t max_nodes, void* k_cache,
+    void* v_cache, const int32_t* page_table, int32_t max_pages_per_seq,
+    int32_t num_pages, int32_t page_size, const int32_t* prefix_lens,
+    int32_t token_bytes, int32_t* accept_len, int32_t* accept_nodes,
+    int32_t* bonus_tokens, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

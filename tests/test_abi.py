@@ -198,3 +198,37 @@ def test_commit_rejects(over, code):
 def test_commit_empty_is_noop():
     assert _commit(S=0, k=None, v=None) == api.OK
     assert _commit(max_b=0, k=None) == api.OK
+
+
+def _fused(**over):
+    a = dict(parents=1, offs=1, masks=1, W=1, draft=1, target=1, root=1, S=1,
+             N=16, max_b=16, k=256, v=512, table=1, max_pps=4, num_pages=8,
+             page_size=16, prefix=1, token_bytes=4096, lens=1, nodes=1,
+             bonus=1)
+    a.update(over)
+    return int(api._lib.tree_attn_accept_commit(
+        a["parents"], a["offs"], a["masks"], a["W"], a["draft"], a["target"],
+        a["root"], a["S"], a["N"], a["max_b"], a["k"], a["v"], a["table"],
+        a["max_pps"], a["num_pages"], a["page_size"], a["prefix"],
+        a["token_bytes"], a["lens"], a["nodes"], a["bonus"], None))
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(W=0), api.ERR_SHAPE),
+    (dict(max_b=65, W=1), api.ERR_SHAPE),
+    (dict(page_size=3), api.ERR_SHAPE),
+    (dict(token_bytes=8), api.ERR_SHAPE),
+    (dict(v=8), api.ERR_SHAPE),
+    (dict(W=17), api.ERR_UNSUPPORTED),
+    (dict(token_bytes=1 << 21), api.ERR_UNSUPPORTED),
+    (dict(masks=None), api.ERR_NULL),
+    (dict(nodes=None), api.ERR_NULL),
+    (dict(k=None), api.ERR_NULL),
+    (dict(prefix=None), api.ERR_NULL),
+])
+def test_accept_commit_rejects(over, code):
+    assert _fused(**over) == code
+
+
+def test_accept_commit_empty_is_noop():
+    assert _fused(S=0, parents=None, k=None, v=None, lens=None) == api.OK

@@ -238,27 +238,41 @@ def test_commit_skips_rows_outside_page_table():
     assert np.array_equal(gk, rk) and np.array_equal(gv, rv)
 
 
+def _run_path(mode, dev_parents, dev_offs, masks, d, t, r, max_nodes, kd, vd,
+              table, prefix):
+    import tree_masked_attention_amd.api as api
+    if mode == "fused":
+        out = api.accept_commit(dev_parents, dev_offs, masks, _i32(d),
+                                _i32(t), _i32(r), max_nodes, kd, vd, table,
+                                prefix)
+    else:
+        out = api.accept(dev_parents, dev_offs, masks, _i32(d), _i32(t),
+                         _i32(r), max_nodes)
+        api.commit_kv(kd, vd, table, prefix, out[0], out[1])
+    torch.cuda.synchronize()
+    return [x.cpu().numpy() for x in out]
+
+
+@pytest.mark.parametrize("mode", ["separate", "fused"])
 @pytest.mark.parametrize("name", STANDARD_ORDER)
-def test_accept_commit_standard_workloads(name):
+def test_accept_commit_standard_workloads(name, mode):
     """build_mask -> accept -> commit on the workload's own bf16 caches."""
     import tree_masked_attention_amd.api as api
-    say(f"[gpu] accept + commit, standard workload {name}")
+    say(f"[gpu] accept + commit ({mode}), standard workload {name}")
     wl = standard_workload(name)
     d, t, r = draw_tokens(wl, 2)
     dev = device_inputs(wl)
     masks, _ = api.build_mask(dev["parents"], dev["tree_offsets"],
                               wl.max_nodes, wl.mask_words())
-    lens, nodes, bonus = api.accept(dev["parents"], dev["tree_offsets"],
-                                    masks, _i32(d), _i32(t), _i32(r),
-                                    wl.max_nodes)
-    api.commit_kv(dev["k_cache"], dev["v_cache"], dev["page_table"],
-                  dev["prefix_lens"], lens, nodes)
-    torch.cuda.synchronize()
+    lens, nodes, bonus = _run_path(mode, dev["parents"], dev["tree_offsets"],
+                                   masks, d, t, r, wl.max_nodes,
+                                   dev["k_cache"], dev["v_cache"],
+                                   dev["page_table"], dev["prefix_lens"])
     rl, rn, rb = oracle.accept(wl.parents, wl.tree_offsets, d, t, r,
                                wl.max_nodes)
-    assert np.array_equal(lens.cpu().numpy(), rl)
-    assert np.array_equal(nodes.cpu().numpy(), rn)
-    assert np.array_equal(bonus.cpu().numpy(), rb)
+    assert np.array_equal(lens, rl)
+    assert np.array_equal(nodes, rn)
+    assert np.array_equal(bonus, rb)
     rk, rv = oracle.commit_kv(wl.k_cache, wl.v_cache, wl.page_table,
                               wl.prefix_lens, rl, rn)
     gk = dev["k_cache"].view(torch.int16).cpu().numpy()
@@ -266,3 +280,43 @@ def test_accept_commit_standard_workloads(name):
     assert np.array_equal(gk, rk.view(np.int16))
     assert np.array_equal(gv, rv.view(np.int16))
     say(f"  tau = {rl.tolist()[:8]}")
+
+
+FUSED_CASES = {
+    # (prefix lens, tree sizes, rule, page size, token bytes, vocab, agree)
+    "ragged-small-rows": ([0, 5, 33, 100], [40, 7, 300, 1], "pchain", 4, 48,
+                          3, 0.9),
+    "two-slices": ([17, 3], [64, 90], "pchain", 16, 4096 + 16, 4, 0.95),
+    "max-1024-deep": ([9], [1024], "pchain", 8, 512, 2, 0.99),
+    "page1-wide": ([3, 0], [200, 30], "wide", 1, 32, 2, 0.8),
+    "empty-trees": ([4, 4, 4], [0, 12, 0], "pchain", 16, 256, 4, 0.9),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FUSED_CASES))
+def test_accept_commit_fused_vs_oracle(name):
+    import tree_masked_attention_amd.api as api
+    pre, sizes, rule, page, tb, vocab, agree = FUSED_CASES[name]
+    wl = make_workload(zlib.crc32(name.encode()) % 1000 + 1700,
+                       prefix_lens=pre, tree_sizes=sizes, tree_rules=rule,
+                       p_chain=0.6, num_q_heads=1, num_kv_heads=1,
+                       page_size=page, name=name)
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    k, v, table = _paged(rng, pre, sizes, page, tb)
+    mb = max(wl.max_nodes, 1)
+    for seed in range(2):
+        d, t, r = draw_tokens(wl, seed, vocab=vocab, p_agree=agree)
+        say(f"[gpu] fused accept + commit {name} seed {seed}")
+        p, o = _i32(wl.parents), _i32(wl.tree_offsets)
+        masks, _ = api.build_mask(p, o, mb, api.mask_words_for(mb))
+        kd = torch.from_numpy(k.copy()).to("cuda:0")
+        vd = torch.from_numpy(v.copy()).to("cuda:0")
+        lens, nodes, bonus = _run_path("fused", p, o, masks, d, t, r, mb, kd,
+                                       vd, _i32(table), _i32(pre))
+        rl, rn, rb = oracle.accept(wl.parents, wl.tree_offsets, d, t, r, mb)
+        assert np.array_equal(lens, rl) and np.array_equal(nodes, rn)
+        assert np.array_equal(bonus, rb)
+        rk, rv = oracle.commit_kv(k, v, table, pre, rl, rn)
+        assert np.array_equal(kd.cpu().numpy(), rk)
+        assert np.array_equal(vd.cpu().numpy(), rv)
+        say(f"  tau = {rl.tolist()}")

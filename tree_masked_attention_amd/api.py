@@ -51,10 +51,16 @@ _lib.tree_attn_commit_kv.restype = ctypes.c_int
 _lib.tree_attn_commit_kv.argtypes = [_p, _p, _p, _i, _i, _i, _p, _p, _p, _i,
                                      _i, _i, _p]
 
+_lib.tree_attn_accept_commit.restype = ctypes.c_int
+_lib.tree_attn_accept_commit.argtypes = [_p, _p, _p, _i, _p, _p, _p, _i, _i,
+                                         _i, _p, _p, _p, _i, _i, _i, _p, _i,
+                                         _p, _p, _p, _p]
+
 EXPORTED = ("tree_attn_status_string", "tree_attn_abi_version",
             "tree_attn_build_mask", "tree_attn_workspace_size",
             "tree_attn_describe_plan", "tree_attn_verify",
-            "tree_attn_accept", "tree_attn_commit_kv")
+            "tree_attn_accept", "tree_attn_commit_kv",
+            "tree_attn_accept_commit")
 
 
 class TreeAttnError(RuntimeError):
@@ -284,11 +290,68 @@ def commit_kv(k_cache: torch.Tensor, v_cache: torch.Tensor,
             accept_nodes.shape[0] != S:
         raise ValueError("page_table / accept arrays do not match prefix_lens")
     num_pages, page_size = k_cache.shape[0], k_cache.shape[1]
-    token_bytes = (k_cache[0, 0].numel() * k_cache.element_size()
-                   if num_pages else 16)
+    token_bytes = _token_bytes(k_cache)
     code = _lib.tree_attn_commit_kv(
         _ptr(k_cache), _ptr(v_cache), _ptr(page_table), page_table.shape[1],
         num_pages, page_size, _ptr(prefix_lens), _ptr(accept_len),
         _ptr(accept_nodes), S, accept_nodes.shape[1], token_bytes,
         _stream(stream))
     _raise(code, "tree_attn_commit_kv")
+
+
+def _token_bytes(k_cache: torch.Tensor) -> int:
+    return (k_cache[0, 0].numel() * k_cache.element_size()
+            if k_cache.shape[0] else 16)
+
+
+def accept_commit(parents: torch.Tensor, tree_offsets: torch.Tensor,
+                  masks: torch.Tensor, draft_tokens: torch.Tensor,
+                  target_tokens: torch.Tensor, root_tokens: torch.Tensor,
+                  max_nodes: int, k_cache: torch.Tensor,
+                  v_cache: torch.Tensor, page_table: torch.Tensor,
+                  prefix_lens: torch.Tensor,
+                  accept_len: Optional[torch.Tensor] = None,
+                  accept_nodes: Optional[torch.Tensor] = None,
+                  bonus_tokens: Optional[torch.Tensor] = None,
+                  stream=None) -> Tuple[torch.Tensor, torch.Tensor,
+                                        torch.Tensor]:
+    """accept() then commit_kv() in one launch; same arguments and
+    results (the caches are updated in place)."""
+    for t, n in ((parents, "parents"), (tree_offsets, "tree_offsets"),
+                 (draft_tokens, "draft_tokens"),
+                 (target_tokens, "target_tokens"),
+                 (root_tokens, "root_tokens"), (page_table, "page_table"),
+                 (prefix_lens, "prefix_lens")):
+        _dev(t, torch.int32, n)
+    _dev(masks, torch.int64, "masks")
+    _dev(k_cache, k_cache.dtype, "k_cache")
+    _dev(v_cache, k_cache.dtype, "v_cache")
+    S = tree_offsets.numel() - 1
+    N = parents.numel()
+    if draft_tokens.numel() != N or target_tokens.numel() != N or \
+            root_tokens.numel() != S or prefix_lens.numel() != S:
+        raise ValueError("token arrays / prefix_lens do not match the trees")
+    if masks.dim() != 2 or masks.shape[0] != N:
+        raise ValueError("masks must be [N, W]")
+    if k_cache.shape != v_cache.shape or k_cache.dim() < 2 or \
+            page_table.dim() != 2 or page_table.shape[0] != S:
+        raise ValueError("caches must both be [num_pages, page_size, ...] "
+                         "and page_table [S, max_pages_per_seq]")
+    dev = parents.device
+    if accept_len is None:
+        accept_len = torch.empty((max(S, 1),), dtype=torch.int32, device=dev)
+    if accept_nodes is None:
+        accept_nodes = torch.empty((max(S, 1), int(max_nodes)),
+                                   dtype=torch.int32, device=dev)
+    if bonus_tokens is None:
+        bonus_tokens = torch.empty((max(S, 1),), dtype=torch.int32,
+                                   device=dev)
+    code = _lib.tree_attn_accept_commit(
+        _ptr(parents), _ptr(tree_offsets), _ptr(masks), masks.shape[1],
+        _ptr(draft_tokens), _ptr(target_tokens), _ptr(root_tokens), S, N,
+        int(max_nodes), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+        page_table.shape[1], k_cache.shape[0], k_cache.shape[1],
+        _ptr(prefix_lens), _token_bytes(k_cache), _ptr(accept_len),
+        _ptr(accept_nodes), _ptr(bonus_tokens), _stream(stream))
+    _raise(code, "tree_attn_accept_commit")
+    return accept_len[:S], accept_nodes[:S], bonus_tokens[:S]

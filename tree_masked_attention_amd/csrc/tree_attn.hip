@@ -169,6 +169,103 @@ int check_sizes(int S, int N, int Hq, int Hkv, int head_dim,
   return TREE_ATTN_OK;
 }
 
+int check_accept(const int32_t* parents, const int32_t* tree_offsets,
+                 const uint64_t* masks, int mask_words,
+                 const int32_t* draft_tokens, const int32_t* target_tokens,
+                 const int32_t* root_tokens, int num_seqs, int total_nodes,
+                 int max_nodes, const int32_t* accept_len,
+                 const int32_t* accept_nodes, const int32_t* bonus_tokens) {
+  if (num_seqs < 0 || total_nodes < 0 || max_nodes < 0 || mask_words < 1) {
+    return TREE_ATTN_ERR_SHAPE;
+  }
+  if (mask_words > kAcceptMaxWords || max_nodes > TREE_ATTN_MAX_NODES) {
+    return TREE_ATTN_ERR_UNSUPPORTED;
+  }
+  if ((long long)mask_words * 64 < max_nodes) return TREE_ATTN_ERR_SHAPE;
+  if (num_seqs == 0) return TREE_ATTN_OK;
+  if (!tree_offsets || !root_tokens || !accept_len || !bonus_tokens) {
+    return TREE_ATTN_ERR_NULL;
+  }
+  if (max_nodes > 0 && !accept_nodes) return TREE_ATTN_ERR_NULL;
+  if (total_nodes > 0 &&
+      (!parents || !masks || !draft_tokens || !target_tokens)) {
+    return TREE_ATTN_ERR_NULL;
+  }
+  return TREE_ATTN_OK;
+}
+
+AcceptArgs accept_args(const int32_t* parents, const int32_t* tree_offsets,
+                       const uint64_t* masks, int mask_words,
+                       const int32_t* draft_tokens,
+                       const int32_t* target_tokens,
+                       const int32_t* root_tokens, int total_nodes,
+                       int max_nodes, int32_t* accept_len,
+                       int32_t* accept_nodes, int32_t* bonus_tokens) {
+  AcceptArgs ap;
+  ap.parents = parents;
+  ap.offsets = tree_offsets;
+  ap.masks = masks;
+  ap.draft = draft_tokens;
+  ap.target = target_tokens;
+  ap.root_tokens = root_tokens;
+  ap.accept_len = accept_len;
+  ap.accept_nodes = accept_nodes;
+  ap.bonus = bonus_tokens;
+  ap.W = mask_words;
+  ap.total_nodes = total_nodes;
+  ap.max_nodes = max_nodes;
+  return ap;
+}
+
+// Checks of the cache arguments of a commit (the accepted lists are
+// checked by the caller: the fused call writes them itself).
+int check_commit(const void* k_cache, const void* v_cache,
+                 const int32_t* page_table, int max_pages_per_seq,
+                 int num_pages, int page_size, const int32_t* prefix_lens,
+                 int num_seqs, int max_nodes, int token_bytes) {
+  if (num_seqs < 0 || max_nodes < 0 || max_pages_per_seq < 0 ||
+      num_pages < 0 || token_bytes <= 0 || token_bytes % 16 != 0 ||
+      !is_pow2(page_size)) {
+    return TREE_ATTN_ERR_SHAPE;
+  }
+  if (max_nodes > TREE_ATTN_MAX_NODES || token_bytes > kMaxTokenBytes) {
+    return TREE_ATTN_ERR_UNSUPPORTED;
+  }
+  if (num_seqs == 0 || max_nodes == 0) return TREE_ATTN_OK;
+  if (!k_cache || !v_cache || !page_table || !prefix_lens) {
+    return TREE_ATTN_ERR_NULL;
+  }
+  if ((reinterpret_cast<uintptr_t>(k_cache) |
+       reinterpret_cast<uintptr_t>(v_cache)) % 16 != 0) {
+    return TREE_ATTN_ERR_SHAPE;
+  }
+  return TREE_ATTN_OK;
+}
+
+CommitParams commit_params(void* k_cache, void* v_cache,
+                           const int32_t* page_table, int max_pages_per_seq,
+                           int num_pages, int page_size,
+                           const int32_t* prefix_lens,
+                           const int32_t* accept_len,
+                           const int32_t* accept_nodes, int max_nodes,
+                           int token_bytes, int threads) {
+  CommitParams cp;
+  cp.k = static_cast<uint8_t*>(k_cache);
+  cp.v = static_cast<uint8_t*>(v_cache);
+  cp.page_table = page_table;
+  cp.prefix_lens = prefix_lens;
+  cp.accept_len = accept_len;
+  cp.accept_nodes = accept_nodes;
+  cp.max_pages = max_pages_per_seq;
+  cp.num_pages = num_pages;
+  cp.log2_page = ilog2(page_size);
+  cp.max_nodes = max_nodes;
+  cp.pieces = token_bytes / 16;
+  cp.slices = (2 * cp.pieces + threads - 1) / threads;
+  cp.token_bytes = token_bytes;
+  return cp;
+}
+
 }  // namespace
 
 extern "C" {
@@ -372,29 +469,19 @@ int tree_attn_accept(const int32_t* parents, const int32_t* tree_offsets,
                      int32_t total_nodes, int32_t max_nodes,
                      int32_t* accept_len, int32_t* accept_nodes,
                      int32_t* bonus_tokens, void* stream) {
-  if (num_seqs < 0 || total_nodes < 0 || max_nodes < 0 || mask_words < 1) {
-    return TREE_ATTN_ERR_SHAPE;
-  }
-  if (mask_words > kAcceptMaxWords || max_nodes > TREE_ATTN_MAX_NODES) {
-    return TREE_ATTN_ERR_UNSUPPORTED;
-  }
-  if ((long long)mask_words * 64 < max_nodes) return TREE_ATTN_ERR_SHAPE;
-  if (num_seqs == 0) return TREE_ATTN_OK;
-  if (!tree_offsets || !root_tokens || !accept_len || !bonus_tokens) {
-    return TREE_ATTN_ERR_NULL;
-  }
-  if (max_nodes > 0 && !accept_nodes) return TREE_ATTN_ERR_NULL;
-  if (total_nodes > 0 &&
-      (!parents || !masks || !draft_tokens || !target_tokens)) {
-    return TREE_ATTN_ERR_NULL;
-  }
+  const int st = check_accept(parents, tree_offsets, masks, mask_words,
+                              draft_tokens, target_tokens, root_tokens,
+                              num_seqs, total_nodes, max_nodes, accept_len,
+                              accept_nodes, bonus_tokens);
+  if (st != TREE_ATTN_OK || num_seqs == 0) return st;
   // one thread per node of the largest tree, whole waves
   const int threads = (std::max(1, (int)max_nodes) + 63) / 64 * 64;
+  const AcceptArgs ap = accept_args(parents, tree_offsets, masks, mask_words,
+                                    draft_tokens, target_tokens, root_tokens,
+                                    total_nodes, max_nodes, accept_len,
+                                    accept_nodes, bonus_tokens);
   hipLaunchKernelGGL(accept_kernel, dim3(num_seqs), dim3(threads), 0,
-                     reinterpret_cast<hipStream_t>(stream), parents,
-                     tree_offsets, masks, (int)mask_words, draft_tokens,
-                     target_tokens, root_tokens, (int)total_nodes,
-                     (int)max_nodes, accept_len, accept_nodes, bonus_tokens);
+                     reinterpret_cast<hipStream_t>(stream), ap);
   return hipGetLastError() == hipSuccess ? TREE_ATTN_OK : TREE_ATTN_ERR_HIP;
 }
 
@@ -405,42 +492,57 @@ int tree_attn_commit_kv(void* k_cache, void* v_cache,
                         const int32_t* accept_nodes, int32_t num_seqs,
                         int32_t max_nodes, int32_t token_bytes,
                         void* stream) {
-  if (num_seqs < 0 || max_nodes < 0 || max_pages_per_seq < 0 ||
-      num_pages < 0 || token_bytes <= 0 || token_bytes % 16 != 0 ||
-      !is_pow2(page_size)) {
-    return TREE_ATTN_ERR_SHAPE;
-  }
-  if (max_nodes > TREE_ATTN_MAX_NODES || token_bytes > kMaxTokenBytes) {
-    return TREE_ATTN_ERR_UNSUPPORTED;
-  }
-  if (num_seqs == 0 || max_nodes == 0) return TREE_ATTN_OK;
-  if (!k_cache || !v_cache || !page_table || !prefix_lens || !accept_len ||
-      !accept_nodes) {
-    return TREE_ATTN_ERR_NULL;
-  }
-  if ((reinterpret_cast<uintptr_t>(k_cache) |
-       reinterpret_cast<uintptr_t>(v_cache)) % 16 != 0) {
-    return TREE_ATTN_ERR_SHAPE;
-  }
-  CommitParams cp;
-  cp.k = static_cast<uint8_t*>(k_cache);
-  cp.v = static_cast<uint8_t*>(v_cache);
-  cp.page_table = page_table;
-  cp.prefix_lens = prefix_lens;
-  cp.accept_len = accept_len;
-  cp.accept_nodes = accept_nodes;
-  cp.max_pages = max_pages_per_seq;
-  cp.num_pages = num_pages;
-  cp.log2_page = ilog2(page_size);
-  cp.max_nodes = max_nodes;
-  cp.pieces = token_bytes / 16;
-  cp.slices = (2 * cp.pieces + kCommitThreads - 1) / kCommitThreads;
-  cp.token_bytes = token_bytes;
+  const int st = check_commit(k_cache, v_cache, page_table, max_pages_per_seq,
+                              num_pages, page_size, prefix_lens, num_seqs,
+                              max_nodes, token_bytes);
+  if (st != TREE_ATTN_OK || num_seqs == 0 || max_nodes == 0) return st;
+  if (!accept_len || !accept_nodes) return TREE_ATTN_ERR_NULL;
+  const CommitParams cp = commit_params(
+      k_cache, v_cache, page_table, max_pages_per_seq, num_pages, page_size,
+      prefix_lens, accept_len, accept_nodes, max_nodes, token_bytes,
+      kCommitThreads);
   const long long grid = (long long)num_seqs * cp.slices;
   if (grid > 0x7fffffffLL) return TREE_ATTN_ERR_UNSUPPORTED;
   hipLaunchKernelGGL(commit_kv_kernel, dim3((unsigned)grid),
                      dim3(kCommitThreads), 0,
                      reinterpret_cast<hipStream_t>(stream), cp);
+  return hipGetLastError() == hipSuccess ? TREE_ATTN_OK : TREE_ATTN_ERR_HIP;
+}
+
+int tree_attn_accept_commit(
+    const int32_t* parents, const int32_t* tree_offsets,
+    const uint64_t* masks, int32_t mask_words, const int32_t* draft_tokens,
+    const int32_t* target_tokens, const int32_t* root_tokens,
+    int32_t num_seqs, int32_t total_nodes, int32_t max_nodes, void* k_cache,
+    void* v_cache, const int32_t* page_table, int32_t max_pages_per_seq,
+    int32_t num_pages, int32_t page_size, const int32_t* prefix_lens,
+    int32_t token_bytes, int32_t* accept_len, int32_t* accept_nodes,
+    int32_t* bonus_tokens, void* stream) {
+  int st = check_accept(parents, tree_offsets, masks, mask_words,
+                        draft_tokens, target_tokens, root_tokens, num_seqs,
+                        total_nodes, max_nodes, accept_len, accept_nodes,
+                        bonus_tokens);
+  if (st != TREE_ATTN_OK) return st;
+  st = check_commit(k_cache, v_cache, page_table, max_pages_per_seq,
+                    num_pages, page_size, prefix_lens, num_seqs, max_nodes,
+                    token_bytes);
+  if (st != TREE_ATTN_OK || num_seqs == 0) return st;
+  // one thread per node of the largest tree and per 16-byte column of the
+  // slice, whole waves
+  const int threads =
+      std::max(kCommitThreads, (std::max(1, (int)max_nodes) + 63) / 64 * 64);
+  const AcceptArgs ap = accept_args(parents, tree_offsets, masks, mask_words,
+                                    draft_tokens, target_tokens, root_tokens,
+                                    total_nodes, max_nodes, accept_len,
+                                    accept_nodes, bonus_tokens);
+  const CommitParams cp = commit_params(
+      k_cache, v_cache, page_table, max_pages_per_seq, num_pages, page_size,
+      prefix_lens, accept_len, accept_nodes, max_nodes, token_bytes, threads);
+  const long long grid = (long long)num_seqs * cp.slices;
+  if (grid > 0x7fffffffLL) return TREE_ATTN_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(accept_commit_kernel, dim3((unsigned)grid),
+                     dim3(threads), 0, reinterpret_cast<hipStream_t>(stream),
+                     ap, cp);
   return hipGetLastError() == hipSuccess ? TREE_ATTN_OK : TREE_ATTN_ERR_HIP;
 }
 
