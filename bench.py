@@ -484,7 +484,7 @@ def main():
     plan = api.describe_plan(S, N, Hq, wl.num_kv_heads, d, wl.max_prefix_len,
                              wl.max_nodes, wl.page_size, args.splits)
     kname = ("attn_fwd256_kernel<8>" if plan["rows"] == 256
-             else "attn_fwd_kernel<1>")
+             else "attn_fwd128h_kernel")
     if plan["splits"] > 1:
         kname += " + attn_merge_kernel"
     value = N / (ms_per_step * 1e-3)

@@ -114,7 +114,7 @@ size_t tree_attn_workspace_size(int32_t num_seqs, int32_t total_nodes,
  * tree_attn_describe_plan - the launch tree_attn_verify would make for
  * these sizes, for tests and benchmarks.  Arguments as for
  * tree_attn_workspace_size; info is a host array of 5 int32 that receives
- * { waves per workgroup (4 or 8), query rows per workgroup (128 or 256),
+ * { waves per workgroup (8), query rows per workgroup (128 or 256),
  *   splits of the key range, keys per split, workgroups launched }.  Returns TREE_ATTN_OK, or the status
  * tree_attn_verify would return for these sizes (info untouched).
  */

@@ -109,17 +109,18 @@ def test_workspace_size_rules():
 
 
 def test_describe_plan():
-    # small work: four waves; the key range is split to fill the CUs
+    # small work: 128-row blocks (eight waves: four row groups x two key
+    # halves); the key range is split to fill the CUs
     p = api.describe_plan(1, 16, 8, 2, 128, 256, 16, 16, 0)
-    assert p["waves"] == 4 and p["splits"] >= 1
+    assert p["waves"] == 8 and p["rows"] == 128 and p["splits"] >= 1
     assert p["chunk"] % 64 == 0 and p["chunk"] * p["splits"] >= 256 + 16
     # 1024 rows per kv head and one long split: eight waves
     p = api.describe_plan(4, 1024, 32, 8, 128, 32768, 256, 16, 0)
     assert p["waves"] == 8 and p["rows"] == 256 and p["splits"] == 2
     assert p["workgroups"] == 4 * 8 * 4 * 2
-    # short splits of the same rows stay on four waves
+    # short splits of the same rows stay on 128-row blocks
     p = api.describe_plan(1, 256, 32, 8, 128, 4096, 256, 16, 0)
-    assert p["waves"] == 4
+    assert p["rows"] == 128
     # forced split count is honoured, clamped by the key range
     p = api.describe_plan(1, 64, 16, 4, 128, 6000, 64, 16, 1)
     assert p["splits"] == 1 and p["waves"] == 8 and p["chunk"] >= 6064

@@ -1,0 +1,530 @@
+// 128-row variant of the split-KV tree-verification attention kernel with
+// eight waves: two waves per SIMD on the same 32 query rows, each taking
+// one 32-key half of every 64-key tile.
+//
+// Same operation, data layout, MFMA mapping, LDS ring format, DMA and mask
+// handling as the 256-row kernel (definitions in attn_fwd.hpp).  Wave w
+// owns query rows 32 (w & 3) .. +31 of the workgroup's 128 and keys
+// 32 (w >> 2) .. +31 of each tile; waves w and w + 4 share a SIMD, so every
+// SIMD holds two waves and its vector ALU issues at the two-wave rate
+// (about twice the one-wave rate, three times for the exponential), where
+// four waves of 32 rows would leave one wave per SIMD.  Each wave keeps
+// its own online-softmax state (reference max, row sum, O) over its half
+// of the keys; at the end the wave of the upper half hands its state to the
+// lower-half wave of the same rows through LDS, which combines the two
+// (m* = max(m0, m1), weights 2^(m_c - m*)) and writes the result.  Each
+// wave reads half of the K and V tile for its 32 rows.
+#pragma once
+
+#include "attn_fwd.hpp"
+
+namespace tree_attn {
+
+constexpr int kRowsPerWG128 = 128;
+
+__global__ __launch_bounds__(512, 1) void attn_fwd128h_kernel(FwdParams p) {
+  constexpr int NW = 8;
+  constexpr int kThreads = NW * 64;
+  constexpr int kOpsPerMat = 16 / NW;    // 1-KB DMA ops per wave per matrix
+  constexpr int kOps = 2 * kOpsPerMat;
+  constexpr int kDmaRows = 4 * kOpsPerMat;  // tile rows a wave moves
+  constexpr int kLog2DmaRows = 3;
+  static_assert((1 << kLog2DmaRows) == kDmaRows, "shape");
+  __shared__ __align__(1024) unsigned char ring[2 * kVOff];
+  __shared__ int pg_lds[kPageCache];
+  __shared__ uint64_t mk_lds[kMaskCache];
+
+  // XCD-aware decode, as in the other kernels
+  const int bid = blockIdx.x;
+  int L = (bid & 7) * p.per_xcd + (bid >> 3);
+  if (L >= p.units) return;
+  const int mb = L % p.mblocks;
+  L /= p.mblocks;
+  const int split = L % p.splits;
+  L /= p.splits;
+  const int g = L % p.Hkv;
+  const int s = L / p.Hkv;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rg = wave & 3;   // 32-row group
+  const int kh = wave >> 2;  // key half of every tile (32-key block)
+  const int lane = tid & 63;
+  const int col = lane & 31, half = lane >> 5;
+
+  const unsigned ring_base =
+      (unsigned)(size_t)(__attribute__((address_space(3))) unsigned char*)ring;
+  const unsigned pg_base =
+      (unsigned)(size_t)(__attribute__((address_space(3))) int*)pg_lds;
+  const unsigned mk_base =
+      (unsigned)(size_t)(__attribute__((address_space(3))) uint64_t*)mk_lds;
+  const int lrow = lane >> 4, lchunk = lane & 15;
+
+  // Prologue, two rounds of memory latency before the first tile's scores:
+  // (1) the split's page-table entries go to LDS by DMA while the tree
+  // bounds load; (2) once the entries are in, Q (staged in ring stage 3,
+  // which tile 3 only overwrites after every wave has read it), the
+  // ancestor-mask rows and tiles 0-2 are all in flight together.
+  const int kbeg = split * p.chunk;
+  const int lp0 = kbeg >> p.log2_page;
+  {
+    const int npg_max = min(min(((p.chunk - 1) >> p.log2_page) + 2, kPageCache),
+                            p.max_pps - lp0);
+    const int* ptab = p.page_table + (size_t)s * p.max_pps + lp0;
+    for (int i0 = wave * 64; i0 < npg_max; i0 += kThreads) {
+      if (i0 + lane < npg_max) dma4(ptab + i0 + lane, pg_base + 4 * i0);
+    }
+  }
+
+  const int a = clampi(p.tree_offsets[s], 0, p.N);
+  const int b = clampi(p.tree_offsets[s + 1], a, p.N);
+  const int B = b - a;
+  const int P = max(p.prefix_lens[s], 0);
+  const int rows = p.G * B;
+  const int r0 = mb * kRowsPerWG128;
+  const int T = min(P + B, p.max_tokens);
+  if (r0 >= rows || kbeg >= T) {
+    wait_vmcnt<0>();  // no DMA into LDS outlives the workgroup
+    return;
+  }
+  const int kend = min(T, kbeg + p.chunk);
+  const int n = (kend - kbeg + kKeyTile - 1) / kKeyTile;  // tiles, >= 1
+
+  // ancestor-mask rows of the workgroup's nodes, all W words (the window
+  // of words the split needs starts at word 0)
+  const int n_lo = r0 / p.G;
+  const int n_hi = (min(r0 + kRowsPerWG128, rows) - 1) / p.G;
+  const int nnodes = n_hi - n_lo + 1;
+  const bool has_tree = kend > P;
+  const int wlo = 0;
+  const int nwin = p.W;
+  const int nm = has_tree ? min(nnodes * nwin, kMaskCache) : 0;
+
+  // ---- this lane's query row
+  const int r = r0 + rg * 32 + col;
+  const bool rvalid = r < rows;
+  const int node = rvalid ? r / p.G : n_hi;
+  const size_t qrow =
+      (size_t)(a + node) * p.Hq + g * p.G + (rvalid ? r % p.G : 0);
+  bf16x8 qf[8];  // Q^T fragments (B operand): d = kc*16 + half*8 + 0..7,
+                 // read from LDS once the prologue DMA has landed
+
+  wait_vmcnt<0>();
+  __syncthreads();  // page slice visible
+  // Q rows r0 .. r0+127 (rows past the last one repeat it): instruction i
+  // moves rows 4i .. 4i+3, chunk-swizzled like K; rows 0-63 go to the K
+  // half of stage 3, rows 64-127 to its V half
+  const unsigned q_lds = ring_base + 3 * kTileBytes;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = 4 * wave + k;
+    const int rl = 4 * i + lrow;
+    const int rq = min(r0 + rl, rows - 1);
+    const size_t qr = (size_t)(a + rq / p.G) * p.Hq + g * p.G + rq % p.G;
+    dma16(reinterpret_cast<const char*>(p.q + qr * kHeadDim) +
+              ((lchunk ^ (rl & 15)) << 4),
+          q_lds + (i < 16 ? 0u : (unsigned)kVOff) + ((4 * i) & 63) * 256);
+  }
+  if (nm > 0) {
+    const int nd = 2 * nm;  // dwords
+    const char* msrc =
+        reinterpret_cast<const char*>(p.masks + (size_t)(a + n_lo) * p.W);
+    for (int i0 = wave * 64; i0 < nd; i0 += kThreads) {
+      if (i0 + lane < nd) dma4(msrc + 4 * (i0 + lane), mk_base + 4 * i0);
+    }
+  }
+
+  // ---- LDS operand addresses of this wave's key half (stage 0)
+  unsigned k_off[8];
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) {
+    k_off[kc] = ring_base + (kh * 32 + col) * 256 +
+                (((2 * kc + half) ^ (col & 15)) << 4);
+  }
+  const int y = (lane & 15) >> 2;
+  const int x = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  unsigned v_off[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    v_off[db] = ring_base + kVOff + (kh * 32 + 4 * half + y) * 256 +
+                ((4 * (db ^ y) + x) << 4) + 8 * (lane & 1);
+  }
+
+  // ---- DMA of one tile: wave w moves rows kDmaRows*w .. of K and of V
+  const int pmask = (1 << p.log2_page) - 1;
+  const unsigned tok_bytes = (unsigned)p.Hkv * kHeadDim * 2;
+  const unsigned page_bytes = tok_bytes << p.log2_page;
+  const char* kbase = reinterpret_cast<const char*>(p.k);
+  const char* vbase = reinterpret_cast<const char*>(p.v);
+  const bool fast_pages = p.log2_page >= kLog2DmaRows;
+  // page ids are clamped to the cache when used (the table is not checked)
+  const unsigned pg_last = (unsigned)max(p.num_pages - 1, 0);
+  unsigned k_row_off[kOpsPerMat], v_row_off[kOpsPerMat];
+#pragma unroll
+  for (int k = 0; k < kOpsPerMat; ++k) {
+    const int rw = 4 * k + lrow;
+    const int row = kDmaRows * wave + rw;  // row within the tile
+    k_row_off[k] = rw * tok_bytes + ((lchunk ^ (row & 15)) << 4);
+    v_row_off[k] = rw * tok_bytes + ((lchunk ^ (4 * (row & 3))) << 4);
+  }
+  struct DmaPlan {
+    const char* kb0;
+    const char* vb0;
+    unsigned st;
+  };
+  auto dma_plan = [&](int t) -> DmaPlan {
+    const int w0 = kbeg + t * kKeyTile + kDmaRows * wave;
+    const int pi = clampi((w0 >> p.log2_page) - lp0, 0, kPageCache - 1);
+    const unsigned pgu =
+        min((unsigned)__builtin_amdgcn_readfirstlane(pg_lds[pi]), pg_last);
+    const size_t off = (size_t)pgu * page_bytes +
+                       (unsigned)(w0 & pmask) * tok_bytes + g * kHeadDim * 2;
+    return DmaPlan{kbase + off, vbase + off,
+                   ring_base + (unsigned)(t & (kStages - 1)) * kTileBytes};
+  };
+  auto dma_part = [&](const DmaPlan& dp, int k) {
+    const unsigned dst = dp.st + (wave * kOpsPerMat + k) * 1024;
+    dma16_sbase(dp.kb0, k_row_off[k], dst);
+    dma16_sbase(dp.vb0, v_row_off[k], dst + kVOff);
+  };
+  auto issue = [&](int t) {
+    const int t0 = kbeg + t * kKeyTile;
+    const unsigned st = ring_base + (unsigned)(t & (kStages - 1)) * kTileBytes;
+    const int w0 = t0 + kDmaRows * wave;
+    if (fast_pages && w0 + kDmaRows - 1 < kend) {
+      const DmaPlan dp = dma_plan(t);
+#pragma unroll
+      for (int k = 0; k < kOpsPerMat; ++k) dma_part(dp, k);
+      return;
+    }
+    int pg[kOpsPerMat], slot[kOpsPerMat];
+#pragma unroll
+    for (int k = 0; k < kOpsPerMat; ++k) {
+      const int pos = min(w0 + 4 * k + lrow, kend - 1);
+      slot[k] = pos & pmask;
+      pg[k] = clampi(pg_lds[clampi((pos >> p.log2_page) - lp0, 0,
+                                   kPageCache - 1)],
+                     0, p.num_pages - 1);
+    }
+#pragma unroll
+    for (int k = 0; k < kOpsPerMat; ++k) {
+      const int row = kDmaRows * wave + 4 * k + lrow;
+      const size_t off = (size_t)(unsigned)pg[k] * page_bytes +
+                         (unsigned)slot[k] * tok_bytes + g * kHeadDim * 2;
+      const unsigned dst = st + (wave * kOpsPerMat + k) * 1024;
+      dma16(kbase + off + ((lchunk ^ (row & 15)) << 4), dst);
+      dma16(vbase + off + ((lchunk ^ (4 * (row & 3))) << 4), dst + kVOff);
+    }
+  };
+
+  // ---- allowed keys of this wave's half of tile t (first key t0), in the
+  // bit order of a 32-key block: bit kk = key t0 + 32 kh + kk
+  auto half_allow = [&](int t0) -> uint32_t {
+    const int nvalid = kend - t0;
+    const int npre = P - t0;
+    uint64_t allow = nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1);
+    const uint64_t pre =
+        npre >= 64 ? ~0ull : (npre <= 0 ? 0ull : ((1ull << npre) - 1));
+    uint64_t tree = 0;
+    if (npre < 64) {
+      const int mrow_lds = (node - n_lo) * nwin - wlo;
+      const int j0 = t0 - P;
+      if (j0 >= 0) {
+        const int w0 = min(j0 >> 6, p.W - 1);
+        const int sh = j0 & 63;
+        tree = mk_lds[clampi(mrow_lds + w0, 0, kMaskCache - 1)] >> sh;
+        if (sh != 0 && w0 + 1 < p.W) {
+          tree |= mk_lds[clampi(mrow_lds + w0 + 1, 0, kMaskCache - 1)]
+                  << (64 - sh);
+        }
+      } else {
+        tree = mk_lds[clampi(mrow_lds, 0, kMaskCache - 1)] << (-j0);
+      }
+    }
+    return (uint32_t)((allow & (pre | tree)) >> (32 * kh));
+  };
+  auto apply_half_mask = [&](f32x16& S, uint32_t allow) {
+    allow >>= 4 * half;
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int kk = 8 * (rr >> 2) + (rr & 3);
+      if (!((allow >> kk) & 1u)) S[rr] = -INFINITY;
+    }
+  };
+
+  f32x16 o[4];
+  float l_run = 0.f;        // this lane half's share of the row sum
+  float m_ref = -INFINITY;  // reference max, log2 units
+#pragma unroll
+  for (int db = 0; db < 4; ++db) o[db] = f32x16{};
+  const float c2 = p.scale_log2;
+
+  // ---- S^T of this wave's key half of tile t (one accumulation chain over
+  // the head dimension; the other wave of the SIMD fills its latency)
+  auto qk_half = [&](int t, f32x16& S) {
+    const unsigned so = (unsigned)(t & (kStages - 1)) * kTileBytes;
+    bf16x8 kf[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) kf[c] = lds_read16(k_off[c] + so);
+    S = f32x16{};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) S = mfma32x32x16(kf[c], qf[c], S);
+  };
+  // O^T += V^T P^T over this wave's key half of tile t
+  auto pv_half = [&](int t, const bf16x8 (&pf)[2]) {
+    const unsigned so = (unsigned)(t & (kStages - 1)) * kTileBytes;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      bf16x8 vf[4];
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const unsigned va = v_off[db] + so + hf * 16 * 256;
+        const s16x4 lo = lds_read_tr(va);
+        const s16x4 hi = lds_read_tr(va + 8 * 256);
+        vf[db] = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        o[db] = mfma32x32x16(vf[db], pf[hf], o[db]);
+      }
+    }
+  };
+  // probabilities against m_ref; adds their fp32 sum
+  auto exps_half = [&](const f32x16& S, bf16x8 (&pf)[2]) {
+    const float mu = (m_ref == -INFINITY) ? 0.f : m_ref;
+    float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+    for (int rr = 0; rr < 16; rr += 2) {
+      const float e0 = fast_exp2(fmaf(S[rr], c2, -mu));
+      const float e1 = fast_exp2(fmaf(S[rr + 1], c2, -mu));
+      ps0 += e0;
+      ps1 += e1;
+      pf[rr >> 3][rr & 7] = (__bf16)e0;
+      pf[rr >> 3][(rr & 7) + 1] = (__bf16)e1;
+    }
+    l_run += ps0 + ps1;
+  };
+  // reference max for the next half tile (lazy raise, as in the others)
+  auto next_ref = [&](const f32x16& Sx, float& m_new, float& alpha) -> bool {
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int rr = 0; rr < 16; rr += 2) {
+      tmax = __builtin_elementwise_maximum(
+          tmax, __builtin_elementwise_maximum(Sx[rr], Sx[rr + 1]));
+    }
+    tmax = __builtin_elementwise_maximum(tmax, other_half(tmax)) * c2;
+    const bool need = tmax > m_ref + kLazyRescale;
+    m_new = need ? tmax : m_ref;
+    alpha = need ? fast_exp2(m_ref - m_new) : 1.f;
+    return need;
+  };
+
+  // ---- one pipeline step over tile j (this wave's half of it): S^T of
+  // the next half tile on the matrix core while the vector ALU turns the
+  // current scores into probabilities, then PV of tile j while the ALU
+  // finds the next half tile's max.  After the last tile the scores are
+  // computed on stale LDS data and dropped.
+  auto body = [&](int j, f32x16& Scur, f32x16& Snext, bool mask_next,
+                  bool dma_inbody, float& m_new, float& alpha) -> bool {
+    bf16x8 pf[2];
+    DmaPlan dp{};
+    if (dma_inbody) dp = dma_plan(j + kStages - 1);
+    // segment 1: S^T(j+1) | probabilities of tile j (K operands read two
+    // ahead of their MFMA)
+    qk_half(j + 1, Snext);
+    exps_half(Scur, pf);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (dma_inbody) {  // first half of tile j+3's DMA
+      dma_part(dp, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // segment 2: PV(j) | mask and max of tile j+1
+    pv_half(j, pf);
+    if (mask_next) {
+      apply_half_mask(Snext, half_allow(kbeg + (j + 1) * kKeyTile));
+    }
+    const bool need = next_ref(Snext, m_new, alpha);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < 6) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (dma_inbody) {  // second half
+      dma_part(dp, 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return need;
+  };
+  auto finish = [&](bool r, float m_new, float alpha) {
+    if (__any(r)) {
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] *= alpha;
+    }
+    m_ref = m_new;
+  };
+  auto step = [&](int j, f32x16& Scur, f32x16& Snext) {
+    if (j + 1 < n) {
+      // tile j+1 must have landed; tile j+2 may still be in flight
+      if (j + 2 < n) wait_vmcnt<kOps>();
+      else wait_vmcnt<0>();
+    }
+    __syncthreads();
+    if (j + kStages - 1 < n) issue(j + kStages - 1);
+    float m_new, alpha;
+    bool r;
+    if (j + 1 < n && kbeg + (j + 2) * kKeyTile > min(P, kend)) {
+      r = body(j, Scur, Snext, true, false, m_new, alpha);
+    } else {
+      r = body(j, Scur, Snext, false, false, m_new, alpha);
+    }
+    if (j + 1 >= n) {  // the scores past the last tile are not data
+      r = false;
+      m_new = m_ref;
+    }
+    finish(r, m_new, alpha);
+  };
+  // hot steps: tile j+1 pure prefix, tile j+3 a full tile on the fast path
+  auto hot_step = [&](int j, f32x16& Scur, f32x16& Snext) {
+    wait_vmcnt<kOps>();
+    __syncthreads();
+    float m_new, alpha;
+    const bool r = body(j, Scur, Snext, false, true, m_new, alpha);
+    finish(r, m_new, alpha);
+  };
+
+#pragma unroll
+  for (int t = 0; t < kStages - 1; ++t) {
+    if (t < n) issue(t);
+  }
+  // Q, the mask rows and tile 0 have landed; tiles 1-2 may be in flight
+  if (n >= 3) wait_vmcnt<2 * kOps>();
+  else if (n == 2) wait_vmcnt<kOps>();
+  else wait_vmcnt<0>();
+  __syncthreads();
+  {
+    const int rl = rg * 32 + col;
+    const unsigned qa = q_lds + (rg < 2 ? 0u : (unsigned)kVOff) + (rl & 63) * 256;
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) {
+      qf[kc] = lds_read16(qa + (((2 * kc + half) ^ (col & 15)) << 4));
+    }
+  }
+  f32x16 SA, SB;
+  qk_half(0, SA);
+  if (kbeg + kKeyTile > min(P, kend)) apply_half_mask(SA, half_allow(kbeg));
+  {
+    float m_new, alpha;
+    next_ref(SA, m_new, alpha);
+    m_ref = m_new;
+  }
+  int n_hot = 0;
+  if (fast_pages) {
+    const int last = min((kend - kbeg) / kKeyTile - kStages,
+                         (P - kbeg) / kKeyTile - 2);
+    n_hot = max(last + 1, 0) & ~(kStages - 1);
+  }
+  for (int i = 0; 4 * i < n_hot; ++i) {
+    const int j = 4 * i;
+    hot_step(j, SA, SB);
+    hot_step(j + 1, SB, SA);
+    hot_step(j + 2, SA, SB);
+    hot_step(j + 3, SB, SA);
+  }
+  for (int i = n_hot / 4; 4 * i < n; ++i) {
+    const int j = 4 * i;
+    step(j, SA, SB);
+    if (j + 1 < n) step(j + 1, SB, SA);
+    if (j + 2 < n) step(j + 2, SA, SB);
+    if (j + 3 < n) step(j + 3, SB, SA);
+  }
+
+  // ---- combine the two key halves: the upper-half wave of each row group
+  // leaves (max, row sum, O) in the ring, the lower-half wave merges them
+  float l_tot = l_run + other_half(l_run);
+  __syncthreads();  // every wave is done with the ring
+  float* xo = reinterpret_cast<float*>(ring) + rg * (64 * 64);
+  float* xml = reinterpret_cast<float*>(ring) + 4 * 64 * 64 + rg * 128;
+  if (kh == 1) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        *reinterpret_cast<f32x4*>(xo + ((db * 4 + g4) * 64 + lane) * 4) =
+            f32x4{o[db][g4 * 4 + 0], o[db][g4 * 4 + 1], o[db][g4 * 4 + 2],
+                  o[db][g4 * 4 + 3]};
+      }
+    }
+    xml[lane] = m_ref;
+    xml[64 + lane] = l_tot;
+  }
+  __syncthreads();
+  if (kh == 1 || !rvalid) return;
+  {
+    const float m1 = xml[lane], l1 = xml[64 + lane];
+    const float mx = __builtin_elementwise_maximum(m_ref, m1);
+    const float a0 = mx == -INFINITY ? 0.f : fast_exp2(m_ref - mx);
+    const float a1 = mx == -INFINITY ? 0.f : fast_exp2(m1 - mx);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 u =
+            *reinterpret_cast<const f32x4*>(xo + ((db * 4 + g4) * 64 + lane) * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          o[db][g4 * 4 + e] = o[db][g4 * 4 + e] * a0 + u[e] * a1;
+        }
+      }
+    }
+    l_tot = l_tot * a0 + l1 * a1;
+    m_ref = mx;
+  }
+
+  // ---- epilogue (lower-half waves)
+  if (p.splits == 1) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    __bf16* op = p.out + qrow * kHeadDim;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        bf16x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(o[db][g4 * 4 + e] * inv);
+        *reinterpret_cast<bf16x4*>(op + db * 32 + g4 * 8 + half * 4) = v4;
+      }
+    }
+    if (half == 0) {
+      p.lse[qrow] = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+  } else {
+    const size_t prow = (size_t)split * p.N * p.Hq + qrow;
+    float* pp = p.part_o + prow * kHeadDim;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        f32x4 v4 = {o[db][g4 * 4 + 0], o[db][g4 * 4 + 1], o[db][g4 * 4 + 2],
+                    o[db][g4 * 4 + 3]};
+        *reinterpret_cast<f32x4*>(pp + db * 32 + g4 * 8 + half * 4) = v4;
+      }
+    }
+    if (half == 0) {
+      *reinterpret_cast<f32x2*>(p.part_ml + prow * 2) = f32x2{m_ref, l_tot};
+    }
+  }
+}
+
+}  // namespace tree_attn

@@ -2,8 +2,8 @@
 // (sequence, kv head) pairs with at least 256 query rows.
 //
 // Same operation, data layout, MFMA mapping, LDS ring format and pipeline
-// as the four-wave 128-row kernel (attn_fwd.hpp); each K/V tile staged in
-// LDS serves 256 rows.  Two shapes:
+// as the 128-row kernel (definitions in attn_fwd.hpp); each K/V tile staged
+// in LDS serves 256 rows.  Two shapes (only NW = 8 is launched):
 //  * NW = 8 waves of 32 rows, two waves per SIMD: the vector ALU of a SIMD
 //    issues about twice as many instructions per cycle (and the exponential
 //    about three times as many) when two waves feed it; 256 registers per
@@ -37,7 +37,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd256_kernel(FwdParams p) {
   __shared__ int pg_lds[kPageCache];
   __shared__ uint64_t mk_lds[kMaskCache];
 
-  // XCD-aware decode, as in the four-wave kernel
+  // XCD-aware decode: consecutive work units (the row blocks of one
+  // (sequence, kv head, split), which read the same K/V) go to one XCD.
   const int bid = blockIdx.x;
   int L = (bid & 7) * p.per_xcd + (bid >> 3);
   if (L >= p.units) return;
@@ -356,7 +357,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd256_kernel(FwdParams p) {
       l_run[qb] += ps0 + ps1;
     }
   };
-  // reference max for a tile (lazy raise, as in the four-wave kernel)
+  // reference max for a tile, raised only past the lazy-rescale margin
   auto next_ref = [&](const f32x16 (&Sx)[QB][2], float (&m_new)[QB],
                       float (&alpha)[QB]) -> bool {
     bool any_need = false;

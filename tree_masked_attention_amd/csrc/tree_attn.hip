@@ -9,6 +9,7 @@
 
 #include "accept_commit.hpp"
 #include "attn_fwd.hpp"
+#include "attn_fwd128h.hpp"
 #include "attn_fwd8.hpp"
 #include "attn_merge.hpp"
 #include "common.hpp"
@@ -23,11 +24,10 @@ constexpr int kMaxDevices = 64;
 constexpr int kMaxSplits = 256;
 constexpr int kMinKeysPerSplit = 256;
 // keys per workgroup from which the 256-row kernel (8 waves of 32 rows) is
-// used.  Its 4-wave shape (64 rows per wave) halves the LDS reads per flop
-// but does not fit the register file with this schedule (the compiler
-// spills and shuffles accumulators), so it is not launched.
+// used; shorter key ranges take the 128-row kernel (8 waves: 4 row groups
+// x 2 key halves).  Both kernels run 8 waves per workgroup.
 constexpr int kMinKeysPerWG8 = 2048;
-constexpr int kWaves256 = 8;
+constexpr int kWaves = 8;
 constexpr int kMaxTokenBytes = 1 << 20;
 
 std::atomic<int> g_cu_count[kMaxDevices];
@@ -61,8 +61,7 @@ int ilog2(int x) {
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct Plan {
-  int nw = 4;        // waves per workgroup
-  int qb = 1;        // 32-row query blocks per wave
+  int rows = 128;    // query rows per workgroup (128 or 256; 8 waves)
   int mblocks = 0;   // row blocks per (sequence, kv head)
   int splits = 1;    // key-range splits
   int chunk = 0;     // keys per split (multiple of the 64-key tile)
@@ -72,9 +71,10 @@ struct Plan {
 };
 
 // Launch planning from host-side bounds only (no device-to-host copy).
-// Row blocks: 256 rows (8 waves) when a (sequence, kv head) pair has more
-// than 128 rows, else 128 rows (4 waves); either way one workgroup fills a
-// CU's LDS.  The key range [0, max_prefix_len + max_nodes) is cut into
+// Row blocks: 256 rows (8 waves of 32 rows) when a (sequence, kv head)
+// pair has at least 256 rows and a workgroup gets a long key range, else
+// 128 rows (8 waves: 4 row groups x 2 key halves); either way one workgroup
+// fills a CU's LDS.  The key range [0, max_prefix_len + max_nodes) is cut into
 // splits so that the grid offers about one workgroup per CU, with at least
 // 256 keys per split, and each split's page-table slice fits the kernel's
 // LDS page cache.
@@ -92,10 +92,8 @@ int make_plan(int S, int N, int Hq, int Hkv, int max_prefix_len,
   // Splits of the key range so that the work units fill the CUs (or the
   // requested count), each a whole number of 64-key tiles.
   long long splits = 0, chunk = 0, units0 = 0;
-  auto choose = [&](int nw, int qb) -> int {
-    const int rows_per_wg = 32 * nw * qb;
-    pl.nw = nw;
-    pl.qb = qb;
+  auto choose = [&](int rows_per_wg) -> int {
+    pl.rows = rows_per_wg;
     pl.mblocks = (int)std::max(1LL, (rows + rows_per_wg - 1) / rows_per_wg);
     units0 = (long long)S * Hkv * pl.mblocks;
     if (req_splits > 0) {
@@ -123,21 +121,18 @@ int make_plan(int S, int N, int Hq, int Hkv, int max_prefix_len,
   const long long mask_words = (max_nodes + 63) / 64;
   const long long nodes8 = (kRowsPerWG8 + G - 1) / G + 1;
   const bool can8 = rows >= kRowsPerWG8 && nodes8 * mask_words <= kMaskCache;
-  int nw = 4, qb = 1;
+  int rpw = kRowsPerWG128;
   if (can8) {
-    const int st = choose(kWaves256, 8 / kWaves256);
+    const int st = choose(kRowsPerWG8);
     if (st != TREE_ATTN_OK) return st;
-    if (chunk >= kMinKeysPerWG8) {
-      nw = kWaves256;
-      qb = 8 / kWaves256;
-    }
+    if (chunk >= kMinKeysPerWG8) rpw = kRowsPerWG8;
   }
 #ifdef TREE_ATTN_FORCE_SHAPE  // build-time override for tuning runs
-  if (TREE_ATTN_FORCE_SHAPE == 1) { nw = 4; qb = 1; }
-  if (TREE_ATTN_FORCE_SHAPE == 2 && can8) { nw = 8; qb = 1; }
+  if (TREE_ATTN_FORCE_SHAPE == 2 && can8) rpw = kRowsPerWG8;
+  if (TREE_ATTN_FORCE_SHAPE == 3) rpw = kRowsPerWG128;
 #endif
   {
-    const int st = choose(nw, qb);
+    const int st = choose(rpw);
     if (st != TREE_ATTN_OK) return st;
   }
   pl.splits = (int)splits;
@@ -346,8 +341,8 @@ int tree_attn_describe_plan(int32_t num_seqs, int32_t total_nodes,
                  max_prefix_len, max_nodes, page_size, num_splits, cu_count(),
                  &pl);
   if (st != TREE_ATTN_OK) return st;
-  info[0] = pl.nw;
-  info[1] = 32 * pl.nw * pl.qb;
+  info[0] = kWaves;
+  info[1] = pl.rows;
   info[2] = pl.splits;
   info[3] = pl.chunk;
   info[4] = 8 * ((pl.units + 7) / 8);
@@ -428,10 +423,10 @@ int tree_attn_verify(const void* q, const void* k_cache, const void* v_cache,
 
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const unsigned grid = 8u * (unsigned)fp.per_xcd;
-  if (pl.nw == 8) {
+  if (pl.rows == kRowsPerWG8) {
     hipLaunchKernelGGL(attn_fwd256_kernel<8>, dim3(grid), dim3(512), 0, hs, fp);
   } else {
-    hipLaunchKernelGGL(attn_fwd_kernel<1>, dim3(grid), dim3(256), 0, hs, fp);
+    hipLaunchKernelGGL(attn_fwd128h_kernel, dim3(grid), dim3(512), 0, hs, fp);
   }
   if (hipGetLastError() != hipSuccess) return TREE_ATTN_ERR_HIP;
 
@@ -452,7 +447,7 @@ int tree_attn_verify(const void* q, const void* k_cache, const void* v_cache,
     mp.chunk = pl.chunk;
     mp.max_tokens = fp.max_tokens;
     mp.mblocks = pl.mblocks;
-    mp.rows_per_block = 32 * pl.nw * pl.qb;
+    mp.rows_per_block = pl.rows;
     const long long mgrid = (long long)num_seqs * num_kv_heads * pl.mblocks *
                             (mp.rows_per_block / kMergeRowsPerWG);
     hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)mgrid),
