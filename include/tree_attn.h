@@ -158,6 +158,13 @@ int tree_attn_describe_plan(int32_t num_seqs, int32_t total_nodes,
  *   workspace     dev scratch of tree_attn_workspace_size(...) bytes, 256-B
  *                 aligned; may be NULL when that size is 0
  *
+ * Precision.  Scores, softmax and the P*V products accumulate in fp32
+ * (P rounded to bf16 for the matrix cores).  When the key range is split
+ * (workspace size > 0), each split's output, normalised by its own row
+ * sum, passes through the workspace in fp16 (a convex combination of V
+ * rows, so it needs V entries within fp16's range, |v| <= 65504; larger
+ * values saturate there) before the log-sum-exp merge in fp32.
+ *
  * Device values outside the stated bounds (a prefix longer than
  * max_prefix_len, a tree larger than max_nodes, page ids outside
  * [0, num_pages)) give unspecified output for the rows concerned, but no

@@ -100,12 +100,13 @@ def test_workspace_size_rules():
     ws1 = api.workspace_size(1, 16, 8, 2, 128, 256, 16, 16, 1)
     ws4 = api.workspace_size(1, 16, 8, 2, 128, 1024, 16, 16, 4)
     assert ws1 == 0
-    assert ws4 >= 4 * 16 * 8 * (128 + 2) * 4
+    # per split and row: the fp16 output (256 B) and fp32 (max, sum)
+    assert ws4 >= 4 * 16 * 8 * (128 * 2 + 2 * 4)
     assert api.workspace_size(1, 16, 8, 3, 128, 256, 16, 16, 0) == 0  # invalid
     assert api.workspace_size(1, 16, 8, 2, 128, 256, 16, 12, 0) == 0  # page
     # tiny pages force more splits (each split's page slice is bounded)
     assert api.workspace_size(1, 16, 8, 2, 128, 5000, 16, 1, 1) >= \
-        5 * 16 * 8 * (128 + 2) * 4
+        5 * 16 * 8 * (128 * 2 + 2 * 4)
 
 
 def test_describe_plan():

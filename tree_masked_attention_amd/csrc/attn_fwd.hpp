@@ -16,8 +16,10 @@
 // the key range [0, P_s + B_s).  The tree keys are the last B_s positions
 // of that range, so the split that reaches them applies the bitmask on its
 // tail tiles (the tree-block pass).  With one split a kernel writes the
-// normalised output and the LSE; otherwise it writes (unnormalised O,
-// running max, running sum) partials for the merge kernel.
+// normalised output and the LSE; otherwise it writes partials for the
+// merge kernel: the split's output normalised by its own row sum, in fp16
+// (a convex combination of V rows, so within V's range), and the running
+// max and row sum in fp32.
 //
 // Matrix-core mapping (v_mfma_f32_32x32x16_bf16, D = A*B + C).  Scores are
 // computed transposed, S^T = K * Q^T: the query is the MFMA column, so a
@@ -66,8 +68,8 @@ struct FwdParams {
   const uint64_t* masks;
   __bf16* out;
   float* lse;
-  float* part_o;   // [splits][N*Hq][128]
-  float* part_ml;  // [splits][N*Hq][2]  (max in log2 units, sum)
+  _Float16* part_o;  // [splits][N*Hq][128]  O of the split / its row sum
+  float* part_ml;    // [splits][N*Hq][2]  (max in log2 units, row sum)
   int max_pps, num_pages, log2_page, W;
   int max_tokens;  // min(max_pps * page_size, 2^30)
   int S, N, Hq, Hkv, G;
@@ -94,6 +96,40 @@ typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
 __device__ __forceinline__ bf16x8 lds_read16(unsigned addr) {
   return __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(size_t)addr);
+}
+
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+
+__device__ __forceinline__ void lds_write8(unsigned addr, u32x2 v) {
+  *(lds_u32x2*)(size_t)addr = v;
+}
+
+// Stores a wave's 32 rows of 128 two-byte values, held transposed in
+// registers (lane (col, half): row col; pk[c] = columns 8c + 4 half .. +3),
+// as whole 16-byte row chunks: the rows go to the wave's own 8 KB of LDS at
+// stg (16-byte chunks XOR-swizzled by row), then each lane stores 16 bytes,
+// four full 256-byte rows per instruction.  row: the global row index of
+// this lane's row (rows of 256 bytes from base), or -1 for a row that is
+// not written.  Uses only the calling wave's data: no barrier.
+__device__ __forceinline__ void store_rows_staged(const u32x2 (&pk)[16],
+                                                  unsigned stg, int row,
+                                                  char* base, int lane) {
+  const int col = lane & 31, half = lane >> 5;
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    lds_write8(stg + col * 256 + ((c ^ (col & 15)) << 4) + half * 8, pk[c]);
+  }
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int rr = 4 * k + (lane >> 4), ch = lane & 15;
+    const u32x4 v = *(const lds_u32x4*)(size_t)(stg + rr * 256 +
+                                                ((ch ^ (rr & 15)) << 4));
+    const int dr = __shfl(row, rr);
+    if (dr >= 0) {
+      *reinterpret_cast<u32x4*>(base + (size_t)dr * 256 + ch * 16) = v;
+    }
+  }
 }
 
 // Transposing LDS read (see the file comment).

@@ -545,44 +545,51 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd256_kernel(FwdParams p) {
     if (j + 3 < n) step(j + 3, SB, SA);
   }
 
-  // ---- epilogue
+  // ---- epilogue: the normalised output in bf16 (one split) or fp16 (a
+  // split's partial), each wave's rows staged through its own 8 KB of the
+  // ring so that the stores write whole rows
+  __syncthreads();  // every wave is done with the ring
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = l_run[qb] + other_half(l_run[qb]);
-    if (!rvalid[qb]) continue;
-    if (p.splits == 1) {
-      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      __bf16* op = p.out + qrow[qb] * kHeadDim;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    u32x2 pk[16];
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
+    for (int db = 0; db < 4; ++db) {
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
+      for (int g4 = 0; g4 < 4; ++g4) {
+        if (p.splits == 1) {
           bf16x4 v4;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             v4[e] = (__bf16)(o[qb][db][g4 * 4 + e] * inv);
           }
-          *reinterpret_cast<bf16x4*>(op + db * 32 + g4 * 8 + half * 4) = v4;
+          pk[db * 4 + g4] = __builtin_bit_cast(u32x2, v4);
+        } else {
+          f16x4 v4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v4[e] = to_f16_sat(o[qb][db][g4 * 4 + e] * inv);
+          }
+          pk[db * 4 + g4] = __builtin_bit_cast(u32x2, v4);
         }
       }
-      if (half == 0) {
+    }
+    const unsigned stg = ring_base + (unsigned)(wave * QB + qb) * 8192;
+    const int row = rvalid[qb] ? (int)qrow[qb] : -1;
+    if (p.splits == 1) {
+      store_rows_staged(pk, stg, row, reinterpret_cast<char*>(p.out), lane);
+      if (half == 0 && rvalid[qb]) {
         p.lse[qrow[qb]] =
             l_tot > 0.f ? (m_ref[qb] + log2f(l_tot)) * kLn2 : -INFINITY;
       }
     } else {
-      const size_t prow = (size_t)split * p.N * p.Hq + qrow[qb];
-      float* pp = p.part_o + prow * kHeadDim;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          f32x4 v4 = {o[qb][db][g4 * 4 + 0], o[qb][db][g4 * 4 + 1],
-                      o[qb][db][g4 * 4 + 2], o[qb][db][g4 * 4 + 3]};
-          *reinterpret_cast<f32x4*>(pp + db * 32 + g4 * 8 + half * 4) = v4;
-        }
-      }
-      if (half == 0) {
-        *reinterpret_cast<f32x2*>(p.part_ml + prow * 2) =
+      const size_t prow0 = (size_t)split * p.N * p.Hq;
+      store_rows_staged(pk, stg, row,
+                        reinterpret_cast<char*>(p.part_o + prow0 * kHeadDim),
+                        lane);
+      if (half == 0 && rvalid[qb]) {
+        *reinterpret_cast<f32x2*>(p.part_ml + (prow0 + qrow[qb]) * 2) =
             f32x2{m_ref[qb], l_tot};
       }
     }

@@ -1,10 +1,10 @@
 // Log-sum-exp merge of split-KV partials.
 //
-// Each split c of a row's key range left an unnormalised output O_c, its
-// running max m_c (log2 units) and running sum l_c.  With
-// m* = max_c m_c and w_c = 2^(m_c - m*):
-//     out = sum_c w_c O_c / sum_c w_c l_c,
-//     lse = ln2 * (m* + log2 sum_c w_c l_c).
+// Each split c of a row's key range left its output normalised by its own
+// row sum, O'_c = O_c / l_c (fp16), its running max m_c (log2 units) and
+// its row sum l_c.  With m* = max_c m_c and w_c = 2^(m_c - m*) l_c:
+//     out = sum_c w_c O'_c / sum_c w_c,
+//     lse = ln2 * (m* + log2 sum_c w_c).
 // A split in which the row saw no allowed key has m_c = -inf, l_c = 0 and
 // contributes nothing.  The sums are accumulated with a running maximum,
 // which gives the same values up to rounding order.  Each lane owns two of
@@ -18,7 +18,7 @@ namespace tree_attn {
 struct MergeParams {
   const int32_t* prefix_lens;
   const int32_t* tree_offsets;
-  const float* part_o;
+  const _Float16* part_o;
   const float* part_ml;
   __bf16* out;
   float* lse;
@@ -69,7 +69,8 @@ __global__ __launch_bounds__(kMergeWaves * 64) void attn_merge_kernel(
     acc[k] = f32x2{0.f, 0.f};
   }
   for (int c0 = 0; c0 < nsplit; c0 += kMergeSplits) {
-    f32x2 ml[kMergeRows][kMergeSplits], oc[kMergeRows][kMergeSplits];
+    f32x2 ml[kMergeRows][kMergeSplits];
+    f16x2 oc[kMergeRows][kMergeSplits];
 #pragma unroll
     for (int k = 0; k < kMergeRows; ++k) {
 #pragma unroll
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(kMergeWaves * 64) void attn_merge_kernel(
         const int c = min(c0 + u, nsplit - 1);  // in range; unused if past
         const size_t prow = (size_t)c * NH + qrow[k];
         ml[k][u] = *reinterpret_cast<const f32x2*>(p.part_ml + prow * 2);
-        oc[k][u] = *reinterpret_cast<const f32x2*>(p.part_o + prow * kHeadDim +
+        oc[k][u] = *reinterpret_cast<const f16x2*>(p.part_o + prow * kHeadDim +
                                                    lane * 2);
       }
     }
@@ -89,10 +90,10 @@ __global__ __launch_bounds__(kMergeWaves * 64) void attn_merge_kernel(
         const float m_new = fmaxf(m_run[k], ml[k][u][0]);
         if (m_new == -INFINITY) continue;  // no key seen yet
         const float s_old = fast_exp2(m_run[k] - m_new);
-        const float w = fast_exp2(ml[k][u][0] - m_new);
-        l_run[k] = l_run[k] * s_old + w * ml[k][u][1];
-        acc[k][0] = acc[k][0] * s_old + w * oc[k][u][0];
-        acc[k][1] = acc[k][1] * s_old + w * oc[k][u][1];
+        const float w = fast_exp2(ml[k][u][0] - m_new) * ml[k][u][1];
+        l_run[k] = l_run[k] * s_old + w;
+        acc[k][0] = acc[k][0] * s_old + w * (float)oc[k][u][0];
+        acc[k][1] = acc[k][1] * s_old + w * (float)oc[k][u][1];
         m_run[k] = m_new;
       }
     }

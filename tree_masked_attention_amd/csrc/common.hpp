@@ -14,6 +14,16 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kF16Max = 65504.f;
+
+// fp32 -> fp16 (round to nearest even), saturated to the finite range.
+__device__ __forceinline__ _Float16 to_f16_sat(float x) {
+  return (_Float16)__builtin_elementwise_min(
+      __builtin_elementwise_max(x, -kF16Max), kF16Max);
+}
 
 constexpr int kHeadDim = 128;
 constexpr float kLn2 = 0.693147180559945309f;

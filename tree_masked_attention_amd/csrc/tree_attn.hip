@@ -142,7 +142,7 @@ int make_plan(int S, int N, int Hq, int Hkv, int max_prefix_len,
   pl.units = (int)units;
   if (splits > 1) {
     const size_t rows_all = (size_t)N * Hq * splits;
-    pl.part_ml_off = align_up(rows_all * kHeadDim * sizeof(float), 256);
+    pl.part_ml_off = align_up(rows_all * kHeadDim * sizeof(_Float16), 256);
     pl.ws_bytes = pl.part_ml_off + align_up(rows_all * 2 * sizeof(float), 256);
   }
   *out = pl;
@@ -400,7 +400,7 @@ int tree_attn_verify(const void* q, const void* k_cache, const void* v_cache,
   fp.masks = masks;
   fp.out = static_cast<__bf16*>(out);
   fp.lse = lse;
-  fp.part_o = static_cast<float*>(workspace);
+  fp.part_o = static_cast<_Float16*>(workspace);
   fp.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                         pl.part_ml_off);
   fp.max_pps = max_pages_per_seq;
