@@ -83,9 +83,9 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload):
-    """HBM bytes per verify launch from the committed counter summary,
-    when it was taken on the current sources; else None."""
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of one kernel from the committed counter
+    summary, when it was taken on the current sources; else None."""
     try:
         lines = open(TRAFFIC_FILE).read().splitlines()
     except OSError:
@@ -95,13 +95,16 @@ def measured_traffic(workload):
         f = ln.split()
         if len(f) < 4 or f[0] != workload:
             continue
-        kv = dict(x.split("=", 1) for x in f[1:] if "=" in x)
+        kv = dict(x.split("=", 1) for x in f[1:] if "=" in x and ":" not in x)
         if kv.get("sources") != src:
             return None
-        try:
-            return float(kv["bytes_per_launch"])
-        except (KeyError, ValueError):
-            return None
+        for x in f[1:]:
+            if x.startswith(kernel + ":"):
+                parts = dict(y.split("=") for y in x[len(kernel) + 1:].split(","))
+                try:
+                    return float(parts["fetch"]) + float(parts["write"])
+                except (KeyError, ValueError):
+                    return None
     return None
 
 
@@ -122,13 +125,15 @@ def copy_calibration(torch):
 # algorithmic work of one verify launch
 # --------------------------------------------------------------------------
 
-def algorithmic_work(wl):
+def algorithmic_work(wl, with_output=True):
     """(bytes, flops) the method must move / compute for one verify call.
 
     bytes: K and V of every cached token read once, q read and out written
     once (bf16), lse written (fp32), the ancestor masks and the page-table
-    entries read once.  flops: 4*d per allowed (query, key) pair (2*d for
-    q.k, 2*d for p*v); masked-out tree pairs are not counted.
+    entries read once (without out and lse when with_output is False: the
+    split pass of a split call leaves them to the merge).  flops: 4*d per
+    allowed (query, key) pair (2*d for q.k, 2*d for p*v); masked-out tree
+    pairs are not counted.
     """
     d, Hq, Hkv, ps = wl.head_dim, wl.num_q_heads, wl.num_kv_heads, wl.page_size
     P = wl.prefix_lens.astype(np.int64)
@@ -136,8 +141,10 @@ def algorithmic_work(wl):
     N = wl.total_nodes
     W = wl.mask_words()
     tokens = P + B
-    nbytes = (int(tokens.sum()) * Hkv * d * 2 * 2 + 2 * N * Hq * d * 2 +
-              N * Hq * 4 + N * W * 8 + 4 * int(((tokens + ps - 1) // ps).sum()))
+    nbytes = (int(tokens.sum()) * Hkv * d * 2 * 2 + N * Hq * d * 2 +
+              N * W * 8 + 4 * int(((tokens + ps - 1) // ps).sum()))
+    if with_output:
+        nbytes += N * Hq * d * 2 + N * Hq * 4
     pairs = 0
     for s in range(wl.num_seqs):
         a, b = int(wl.tree_offsets[s]), int(wl.tree_offsets[s + 1])
@@ -231,31 +238,24 @@ def accept_commit_stage(args, torch, api, wl, sets, stream):
     f_com = api._lib.tree_attn_commit_kv
     f_fused = api._lib.tree_attn_accept_commit
 
-    def step_separate(i, ev=None):
-        a, cm = calls[i % len(calls)]
-        if ev is not None:
-            ev[0].record(stream)
-        rc = f_acc(*a)
-        if ev is not None:
-            ev[1].record(stream)
-        rc |= f_com(*cm)
-        if ev is not None:
-            ev[2].record(stream)
-        return rc
+    def step_accept(i):
+        return f_acc(*calls[i % len(calls)][0])
 
-    def step_fused(i, ev=None):
+    def step_commit(i):
+        return f_com(*calls[i % len(calls)][1])
+
+    def step_separate(i):
+        return step_accept(i) | step_commit(i)
+
+    def step_fused(i):
         a, cm = calls[i % len(calls)]
-        if ev is not None:
-            ev[0].record(stream)
         # tree_attn_accept_commit takes the accept arguments, then the
         # cache arguments of tree_attn_commit_kv, then the outputs
-        rc = f_fused(*a[:10], cm[0], cm[1], cm[2], cm[3], cm[4], cm[5],
-                     cm[6], cm[11], *a[10:])
-        if ev is not None:
-            ev[1].record(stream)
-        return rc
+        return f_fused(*a[:10], cm[0], cm[1], cm[2], cm[3], cm[4], cm[5],
+                       cm[6], cm[11], *a[10:])
 
-    def timed(step, n_ev):
+    def loop_ms(step):
+        """per-step time of K back-to-back steps after a warmup"""
         n_warm = 0
         t_w = time.perf_counter()
         while n_warm < max(args.warmup, 1) or time.perf_counter() - t_w < 0.1:
@@ -270,18 +270,13 @@ def accept_commit_stage(args, torch, api, wl, sets, stream):
             step(i)
         t1.record(stream)
         torch.cuda.synchronize()
-        ms = t0.elapsed_time(t1) / args.steps
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
-               for _ in range(args.steps)]
-        for i in range(args.steps):
-            step(i, evs[i])
-        torch.cuda.synchronize()
-        per = [float(np.mean([e[k].elapsed_time(e[k + 1]) for e in evs]))
-               for k in range(n_ev - 1)]
-        return ms, per, n_warm
+        return t0.elapsed_time(t1) / args.steps, n_warm
 
-    sep_ms, (acc_ms, com_ms), _ = timed(step_separate, 3)
-    ms_per_step, (fused_ms,), n_warm = timed(step_fused, 2)
+    acc_ms, _ = loop_ms(step_accept)
+    com_ms, _ = loop_ms(step_commit)
+    sep_ms, _ = loop_ms(step_separate)
+    ms_per_step, n_warm = loop_ms(step_fused)
+    fused_ms = ms_per_step
 
     L = lens[:S].cpu().numpy()
     nd = nodes[:S].cpu().numpy()
@@ -294,10 +289,9 @@ def accept_commit_stage(args, torch, api, wl, sets, stream):
     # accept: per node its parent, draft and target token, the target token
     # of its parent and its mask row; per sequence the outputs
     acc_bytes = N * (16 + W * 8) + S * (max_b * 4 + 12)
-    log(f"[bench] separate: accept {acc_ms * 1e3:.1f} us, commit "
-        f"{com_ms * 1e3:.1f} us, step {sep_ms * 1e3:.1f} us; fused: launch "
-        f"{fused_ms * 1e3:.1f} us, step {ms_per_step * 1e3:.1f} us; "
-        f"tau {L.tolist()[:8]}, {moved} rows moved")
+    log(f"[bench] back-to-back launches: accept {acc_ms * 1e3:.1f} us, "
+        f"commit {com_ms * 1e3:.1f} us, both {sep_ms * 1e3:.1f} us; fused "
+        f"{fused_ms * 1e3:.1f} us; tau {L.tolist()[:8]}, {moved} rows moved")
     fused_bytes = com_bytes + acc_bytes
     achieved = fused_bytes / (fused_ms * 1e-3) / 1e9
     result = {
@@ -421,17 +415,9 @@ def main():
     f_mask = api._lib.tree_attn_build_mask
     f_ver = api._lib.tree_attn_verify
 
-    def step(i, ev=None):
+    def step(i):
         ma, va = calls[i % copies]
-        if ev is not None:
-            ev[0].record(stream)
-        rc = f_mask(*ma)
-        if ev is not None:
-            ev[1].record(stream)
-        rc |= f_ver(*va)
-        if ev is not None:
-            ev[2].record(stream)
-        return rc
+        return f_mask(*ma) | f_ver(*va)
 
     # W warmup steps, then as many more as fill WARM_SECONDS, enqueued back
     # to back like the timed steps.  Under sustained back-to-back load the
@@ -469,31 +455,49 @@ def main():
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
 
-    # (2) per-launch durations of the same calls (events on the launch
-    #     stream around each call; waits between steps keep them apart)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
-           for _ in range(args.steps)]
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    mask_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    ver_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    log(f"[bench] step {ms_per_step * 1e3:.1f} us; mask build "
-        f"{mask_ms * 1e3:.1f} us; verify {ver_ms * 1e3:.1f} us")
-
+    # (2) per-launch durations: each launch made K times back to back on
+    #     the launch stream between one pair of events (input copies
+    #     rotated as above), so the figure is the kernel's own time plus
+    #     the dispatch gap between consecutive launches
     plan = api.describe_plan(S, N, Hq, wl.num_kv_heads, d, wl.max_prefix_len,
                              wl.max_nodes, wl.page_size, args.splits)
+    f_att = api._lib.tree_attn_verify_attend
+    f_mer = api._lib.tree_attn_verify_merge
+
+    def per_launch(fn, pick):
+        for i in range(3):
+            fn(*pick(i))
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(args.steps):
+            if fn(*pick(i)) != 0:
+                raise RuntimeError("tree_attn call failed")
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    mask_ms = per_launch(f_mask, lambda i: calls[i % copies][0])
+    att_ms = per_launch(f_att, lambda i: calls[i % copies][1])
+    mer_ms = (per_launch(f_mer, lambda i: calls[i % copies][1])
+              if plan["splits"] > 1 else 0.0)
+    ver_ms = per_launch(f_ver, lambda i: calls[i % copies][1])
+    log(f"[bench] step {ms_per_step * 1e3:.1f} us; mask build "
+        f"{mask_ms * 1e3:.1f} us; verify {ver_ms * 1e3:.1f} us = attend "
+        f"{att_ms * 1e3:.1f} us + merge {mer_ms * 1e3:.1f} us")
+
     kname = ("attn_fwd256_kernel<8>" if plan["rows"] == 256
              else "attn_fwd128h_kernel")
-    if plan["splits"] > 1:
-        kname += " + attn_merge_kernel"
+    att_bytes, _ = algorithmic_work(wl, with_output=plan["splits"] == 1)
     value = N / (ms_per_step * 1e-3)
-    v_s = ver_ms * 1e-3
+    a_s = att_ms * 1e-3
     if bound == "hbm":
-        achieved, peak, unit = alg_bytes / v_s / 1e9, HBM_PEAK_GBPS, "GB/s"
+        achieved, peak, unit = att_bytes / a_s / 1e9, HBM_PEAK_GBPS, "GB/s"
     else:
-        achieved, peak, unit = (alg_flops / v_s / 1e12, MFMA_BF16_PEAK_TFLOPS,
+        achieved, peak, unit = (alg_flops / a_s / 1e12, MFMA_BF16_PEAK_TFLOPS,
                                 "TFLOP/s")
+    v_s = ver_ms * 1e-3
     result = {
         "metric": "tree-verify attention tree tokens/s + achieved HBM GB/s "
                   "/ MFMA% of peak",
@@ -523,21 +527,21 @@ def main():
         },
         "roofline": {
             "bound": bound,
-            "kernel": f"tree_attn_verify ({kname})",
+            "kernel": f"{kname} (tree_attn_verify_attend)",
             "achieved": achieved,
             "peak": peak,
             "unit": unit,
             "frac": achieved / peak,
-            "traffic": measured_traffic(wl.name),
-            "alg_bytes_per_launch": alg_bytes,
+            "traffic": measured_traffic(wl.name, kname),
+            "alg_bytes_per_launch": att_bytes,
             "alg_flops_per_launch": alg_flops,
-            "avg_launch_us": ver_ms * 1e3,
+            "avg_launch_us": att_ms * 1e3,
         },
-        "attention_tflops": alg_flops / v_s / 1e12,
-        "kv_gbps": alg_bytes / v_s / 1e9,
-        "mfma_frac": alg_flops / v_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-        "hbm_frac": alg_bytes / v_s / 1e9 / HBM_PEAK_GBPS,
+        "verify_us": ver_ms * 1e3,
+        "merge_us": mer_ms * 1e3,
         "mask_build_us": mask_ms * 1e3,
+        "verify_tflops": alg_flops / v_s / 1e12,
+        "verify_hbm_gbps": alg_bytes / v_s / 1e9,
     }
     if not args.no_cpu_baseline:
         log("[bench] CPU baseline (oracle)")

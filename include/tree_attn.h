@@ -188,6 +188,38 @@ int tree_attn_verify(const void* q, const void* k_cache, const void* v_cache,
                      size_t workspace_bytes, void* stream);
 
 /*
+ * tree_attn_verify_attend, tree_attn_verify_merge - the two launches of
+ * tree_attn_verify, for callers that schedule or time them separately.
+ *
+ * Same arguments and checks as tree_attn_verify.  _attend runs the split-KV
+ * pass over the prefix with the tree block masked in registers; with one
+ * planned split it writes out and lse itself, otherwise it leaves the
+ * split partials in the workspace.  _merge then combines the partials into
+ * out and lse (log-sum-exp merge), and launches nothing when the plan has
+ * one split.  _attend followed by _merge on the same stream, with the same
+ * arguments and workspace, gives exactly the results of tree_attn_verify.
+ */
+int tree_attn_verify_attend(
+    const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* page_table, int32_t max_pages_per_seq, int32_t num_pages,
+    int32_t page_size, const int32_t* prefix_lens,
+    const int32_t* tree_offsets, const uint64_t* masks, int32_t mask_words,
+    int32_t num_seqs, int32_t total_nodes, int32_t max_prefix_len,
+    int32_t max_nodes, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, float scale, int32_t num_splits, void* out, float* lse,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+int tree_attn_verify_merge(
+    const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* page_table, int32_t max_pages_per_seq, int32_t num_pages,
+    int32_t page_size, const int32_t* prefix_lens,
+    const int32_t* tree_offsets, const uint64_t* masks, int32_t mask_words,
+    int32_t num_seqs, int32_t total_nodes, int32_t max_prefix_len,
+    int32_t max_nodes, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, float scale, int32_t num_splits, void* out, float* lse,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * tree_attn_accept - the accepted path of every verified draft tree.
  *
  * After the verification pass the target model has, for every tree node n,

@@ -234,3 +234,20 @@ def test_accept_commit_rejects(over, code):
 
 def test_accept_commit_empty_is_noop():
     assert _fused(S=0, parents=None, k=None, v=None, lens=None) == api.OK
+
+
+@pytest.mark.parametrize("fn", ["tree_attn_verify_attend", "tree_attn_verify_merge"])
+def test_verify_phases_check_like_verify(fn):
+    f = getattr(api._lib, fn)
+    base = dict(q=1, k=1, v=1, table=1, max_pps=20, num_pages=20,
+                page_size=16, prefix=1, offs=1, masks=1, W=1, S=1, N=16,
+                max_p=256, max_b=16, Hq=8, Hkv=2, d=128, scale=0.088,
+                splits=0, out=1, lse=1, ws=None, ws_bytes=0)
+    for over, code in ((dict(Hkv=3), api.ERR_SHAPE), (dict(d=64), api.ERR_UNSUPPORTED),
+                       (dict(q=None), api.ERR_NULL), (dict(splits=4), api.ERR_WORKSPACE)):
+        a = dict(base, **over)
+        assert int(f(a["q"], a["k"], a["v"], a["table"], a["max_pps"],
+                     a["num_pages"], a["page_size"], a["prefix"], a["offs"],
+                     a["masks"], a["W"], a["S"], a["N"], a["max_p"], a["max_b"],
+                     a["Hq"], a["Hkv"], a["d"], a["scale"], a["splits"],
+                     a["out"], a["lse"], a["ws"], a["ws_bytes"], None)) == code

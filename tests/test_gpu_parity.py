@@ -282,3 +282,35 @@ def test_random_shapes_parity(seed):
     assert (got["bad"] == -1).all()
     ref_out, ref_lse = oracle.workload_attention(wl)
     assert_parity(got, ref_out, ref_lse, f"random-{seed}")
+
+
+# --------------------------------------------------------------------------
+# the two launches of a verify call, made separately
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_attend_then_merge_equals_verify(splits):
+    import tree_masked_attention_amd.api as api
+    wl = _case("phases", 140, prefix_lens=[300, 77, 1500], tree_sizes=[40, 9, 70])
+    say(f"[gpu] attend + merge vs verify, splits={splits}")
+    dev = device_inputs(wl)
+    masks, _ = api.build_mask(dev["parents"], dev["tree_offsets"],
+                              wl.max_nodes, wl.mask_words())
+    args = (dev["q"], dev["k_cache"], dev["v_cache"], dev["page_table"],
+            dev["prefix_lens"], dev["tree_offsets"], masks, wl.max_prefix_len,
+            wl.max_nodes, wl.scale)
+    out1, lse1 = api.verify(*args, num_splits=splits)
+    nbytes = api.workspace_size(wl.num_seqs, wl.total_nodes, wl.num_q_heads,
+                                wl.num_kv_heads, wl.head_dim,
+                                wl.max_prefix_len, wl.max_nodes,
+                                wl.page_size, splits)
+    ws = torch.empty((max(nbytes, 256),), dtype=torch.uint8, device="cuda:0")
+    out2 = torch.empty_like(out1)
+    lse2 = torch.empty_like(lse1)
+    api.verify(*args, num_splits=splits, out=out2, lse=lse2, workspace=ws,
+               phase="attend")
+    api.verify(*args, num_splits=splits, out=out2, lse=lse2, workspace=ws,
+               phase="merge")
+    torch.cuda.synchronize()
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(lse1, lse2)

@@ -41,6 +41,13 @@ _lib.tree_attn_verify.argtypes = (
     [_p, _p, _p, _p, _i, _i, _i, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i,
      ctypes.c_float, _i, _p, _p, _p, ctypes.c_size_t, _p])
 
+_VERIFY_ARGS = ([_p, _p, _p, _p, _i, _i, _i, _p, _p, _p, _i, _i, _i, _i, _i,
+                 _i, _i, _i, ctypes.c_float, _i, _p, _p, _p, ctypes.c_size_t,
+                 _p])
+for _name in ("tree_attn_verify_attend", "tree_attn_verify_merge"):
+    getattr(_lib, _name).restype = ctypes.c_int
+    getattr(_lib, _name).argtypes = _VERIFY_ARGS
+
 _lib.tree_attn_describe_plan.restype = ctypes.c_int
 _lib.tree_attn_describe_plan.argtypes = [_i] * 9 + [_p]
 
@@ -59,6 +66,7 @@ _lib.tree_attn_accept_commit.argtypes = [_p, _p, _p, _i, _p, _p, _p, _i, _i,
 EXPORTED = ("tree_attn_status_string", "tree_attn_abi_version",
             "tree_attn_build_mask", "tree_attn_workspace_size",
             "tree_attn_describe_plan", "tree_attn_verify",
+            "tree_attn_verify_attend", "tree_attn_verify_merge",
             "tree_attn_accept", "tree_attn_commit_kv",
             "tree_attn_accept_commit")
 
@@ -177,13 +185,17 @@ def verify(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
            num_splits: int = 0, out: Optional[torch.Tensor] = None,
            lse: Optional[torch.Tensor] = None,
            workspace: Optional[torch.Tensor] = None,
-           stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+           stream=None, phase: str = "both") -> Tuple[torch.Tensor,
+                                                      torch.Tensor]:
     """Tree-causal verification attention.
 
     q bf16 [N, Hq, d]; k_cache / v_cache bf16 [num_pages, page_size, Hkv, d];
     page_table int32 [S, max_pages_per_seq]; prefix_lens int32 [S];
     tree_offsets int32 [S+1]; masks int64 [N, W] (uint64 words from
     build_mask).  Returns (out bf16 [N, Hq, d], lse fp32 [N, Hq]).
+    phase: "both" (tree_attn_verify), or "attend" / "merge" for its two
+    launches (tree_attn_verify_attend / _merge; pass the same out, lse and
+    workspace to both).
     """
     for t, dt, n in ((q, torch.bfloat16, "q"), (k_cache, torch.bfloat16, "k_cache"),
                      (v_cache, torch.bfloat16, "v_cache"),
@@ -216,13 +228,16 @@ def verify(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         workspace = torch.empty((ws_bytes,), dtype=torch.uint8,
                                 device=q.device)
     ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    code = _lib.tree_attn_verify(
+    fn = {"both": _lib.tree_attn_verify,
+          "attend": _lib.tree_attn_verify_attend,
+          "merge": _lib.tree_attn_verify_merge}[phase]
+    code = fn(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
         page_table.shape[1], num_pages, page_size, _ptr(prefix_lens),
         _ptr(tree_offsets), _ptr(masks), W, S, N, int(max_prefix_len),
         int(max_nodes), Hq, Hkv, d, float(scale), int(num_splits), _ptr(out),
         _ptr(lse), _ptr(workspace), ws_len, _stream(stream))
-    _raise(code, "tree_attn_verify")
+    _raise(code, f"tree_attn_verify ({phase})")
     return out, lse
 
 

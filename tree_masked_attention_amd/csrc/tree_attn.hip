@@ -19,7 +19,7 @@ using namespace tree_attn;
 
 namespace {
 
-constexpr int kAbiVersion = 5;
+constexpr int kAbiVersion = 6;
 constexpr int kMaxDevices = 64;
 constexpr int kMaxSplits = 256;
 constexpr int kMinKeysPerSplit = 256;
@@ -261,6 +261,119 @@ CommitParams commit_params(void* k_cache, void* v_cache,
   return cp;
 }
 
+// Phases of a verify call: the split-KV + tree pass, then the LSE merge.
+enum { kPhaseAttend = 1, kPhaseMerge = 2 };
+
+int run_verify(int phases, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* page_table, int32_t max_pages_per_seq,
+                     int32_t num_pages, int32_t page_size,
+                     const int32_t* prefix_lens, const int32_t* tree_offsets,
+                     const uint64_t* masks, int32_t mask_words,
+                     int32_t num_seqs, int32_t total_nodes,
+                     int32_t max_prefix_len, int32_t max_nodes,
+                     int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_dim, float scale, int32_t num_splits,
+                     void* out, float* lse, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  int st = check_sizes(num_seqs, total_nodes, num_q_heads, num_kv_heads,
+                       head_dim, max_prefix_len, max_nodes);
+  if (st != TREE_ATTN_OK) return st;
+  if (num_splits < 0 || mask_words < 1 || max_pages_per_seq < 0 ||
+      num_pages < 0) {
+    return TREE_ATTN_ERR_SHAPE;
+  }
+  if (!is_pow2(page_size) || page_size > 4096) return TREE_ATTN_ERR_SHAPE;
+  if ((long long)mask_words * 64 < max_nodes) return TREE_ATTN_ERR_SHAPE;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return TREE_ATTN_ERR_SHAPE;
+  if (num_seqs == 0 || total_nodes == 0) return TREE_ATTN_OK;
+  if (num_pages < 1 || max_pages_per_seq < 1) return TREE_ATTN_ERR_SHAPE;
+  if (!q || !k_cache || !v_cache || !page_table || !prefix_lens ||
+      !tree_offsets || !masks || !out || !lse) {
+    return TREE_ATTN_ERR_NULL;
+  }
+
+  Plan pl;
+  st = make_plan(num_seqs, total_nodes, num_q_heads, num_kv_heads,
+                 max_prefix_len, max_nodes, page_size, num_splits, cu_count(),
+                 &pl);
+  if (st != TREE_ATTN_OK) return st;
+  if (pl.ws_bytes > 0) {
+    if (!workspace) return TREE_ATTN_ERR_WORKSPACE;
+    if (workspace_bytes < pl.ws_bytes) return TREE_ATTN_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) {
+      return TREE_ATTN_ERR_WORKSPACE;
+    }
+  }
+
+  FwdParams fp;
+  fp.q = static_cast<const __bf16*>(q);
+  fp.k = static_cast<const __bf16*>(k_cache);
+  fp.v = static_cast<const __bf16*>(v_cache);
+  fp.page_table = page_table;
+  fp.prefix_lens = prefix_lens;
+  fp.tree_offsets = tree_offsets;
+  fp.masks = masks;
+  fp.out = static_cast<__bf16*>(out);
+  fp.lse = lse;
+  fp.part_o = static_cast<_Float16*>(workspace);
+  fp.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                        pl.part_ml_off);
+  fp.max_pps = max_pages_per_seq;
+  fp.num_pages = num_pages;
+  fp.log2_page = ilog2(page_size);
+  fp.W = mask_words;
+  fp.max_tokens = (int)std::min<long long>((long long)max_pages_per_seq * page_size,
+                                           1LL << 30);
+  fp.S = num_seqs;
+  fp.N = total_nodes;
+  fp.Hq = num_q_heads;
+  fp.Hkv = num_kv_heads;
+  fp.G = num_q_heads / num_kv_heads;
+  fp.mblocks = pl.mblocks;
+  fp.splits = pl.splits;
+  fp.chunk = pl.chunk;
+  fp.units = pl.units;
+  fp.per_xcd = (pl.units + 7) / 8;
+  fp.scale_log2 = scale * kLog2e;
+
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const unsigned grid = 8u * (unsigned)fp.per_xcd;
+  if (!(phases & kPhaseAttend)) {
+    // merge only
+  } else if (pl.rows == kRowsPerWG8) {
+    hipLaunchKernelGGL(attn_fwd256_kernel<8>, dim3(grid), dim3(512), 0, hs, fp);
+  } else {
+    hipLaunchKernelGGL(attn_fwd128h_kernel, dim3(grid), dim3(512), 0, hs, fp);
+  }
+  if (hipGetLastError() != hipSuccess) return TREE_ATTN_ERR_HIP;
+
+  if ((phases & kPhaseMerge) && pl.splits > 1) {
+    MergeParams mp;
+    mp.prefix_lens = prefix_lens;
+    mp.tree_offsets = tree_offsets;
+    mp.part_o = fp.part_o;
+    mp.part_ml = fp.part_ml;
+    mp.out = fp.out;
+    mp.lse = lse;
+    mp.S = num_seqs;
+    mp.N = total_nodes;
+    mp.Hq = num_q_heads;
+    mp.Hkv = num_kv_heads;
+    mp.G = fp.G;
+    mp.splits = pl.splits;
+    mp.chunk = pl.chunk;
+    mp.max_tokens = fp.max_tokens;
+    mp.mblocks = pl.mblocks;
+    mp.rows_per_block = pl.rows;
+    const long long mgrid = (long long)num_seqs * num_kv_heads * pl.mblocks *
+                            (mp.rows_per_block / kMergeRowsPerWG);
+    hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)mgrid),
+                       dim3(kMergeWaves * 64), 0, hs, mp);
+    if (hipGetLastError() != hipSuccess) return TREE_ATTN_ERR_HIP;
+  }
+  return TREE_ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -360,101 +473,46 @@ int tree_attn_verify(const void* q, const void* k_cache, const void* v_cache,
                      int32_t head_dim, float scale, int32_t num_splits,
                      void* out, float* lse, void* workspace,
                      size_t workspace_bytes, void* stream) {
-  int st = check_sizes(num_seqs, total_nodes, num_q_heads, num_kv_heads,
-                       head_dim, max_prefix_len, max_nodes);
-  if (st != TREE_ATTN_OK) return st;
-  if (num_splits < 0 || mask_words < 1 || max_pages_per_seq < 0 ||
-      num_pages < 0) {
-    return TREE_ATTN_ERR_SHAPE;
-  }
-  if (!is_pow2(page_size) || page_size > 4096) return TREE_ATTN_ERR_SHAPE;
-  if ((long long)mask_words * 64 < max_nodes) return TREE_ATTN_ERR_SHAPE;
-  if (!std::isfinite(scale) || !(scale > 0.f)) return TREE_ATTN_ERR_SHAPE;
-  if (num_seqs == 0 || total_nodes == 0) return TREE_ATTN_OK;
-  if (num_pages < 1 || max_pages_per_seq < 1) return TREE_ATTN_ERR_SHAPE;
-  if (!q || !k_cache || !v_cache || !page_table || !prefix_lens ||
-      !tree_offsets || !masks || !out || !lse) {
-    return TREE_ATTN_ERR_NULL;
-  }
+  return run_verify(kPhaseAttend | kPhaseMerge, q, k_cache, v_cache,
+                    page_table, max_pages_per_seq, num_pages, page_size,
+                    prefix_lens, tree_offsets, masks, mask_words, num_seqs,
+                    total_nodes, max_prefix_len, max_nodes, num_q_heads,
+                    num_kv_heads, head_dim, scale, num_splits, out, lse,
+                    workspace, workspace_bytes, stream);
+}
 
-  Plan pl;
-  st = make_plan(num_seqs, total_nodes, num_q_heads, num_kv_heads,
-                 max_prefix_len, max_nodes, page_size, num_splits, cu_count(),
-                 &pl);
-  if (st != TREE_ATTN_OK) return st;
-  if (pl.ws_bytes > 0) {
-    if (!workspace) return TREE_ATTN_ERR_WORKSPACE;
-    if (workspace_bytes < pl.ws_bytes) return TREE_ATTN_ERR_WORKSPACE;
-    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) {
-      return TREE_ATTN_ERR_WORKSPACE;
-    }
-  }
+int tree_attn_verify_attend(
+    const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* page_table, int32_t max_pages_per_seq, int32_t num_pages,
+    int32_t page_size, const int32_t* prefix_lens,
+    const int32_t* tree_offsets, const uint64_t* masks, int32_t mask_words,
+    int32_t num_seqs, int32_t total_nodes, int32_t max_prefix_len,
+    int32_t max_nodes, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, float scale, int32_t num_splits, void* out, float* lse,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  return run_verify(kPhaseAttend, q, k_cache, v_cache, page_table,
+                    max_pages_per_seq, num_pages, page_size, prefix_lens,
+                    tree_offsets, masks, mask_words, num_seqs, total_nodes,
+                    max_prefix_len, max_nodes, num_q_heads, num_kv_heads,
+                    head_dim, scale, num_splits, out, lse, workspace,
+                    workspace_bytes, stream);
+}
 
-  FwdParams fp;
-  fp.q = static_cast<const __bf16*>(q);
-  fp.k = static_cast<const __bf16*>(k_cache);
-  fp.v = static_cast<const __bf16*>(v_cache);
-  fp.page_table = page_table;
-  fp.prefix_lens = prefix_lens;
-  fp.tree_offsets = tree_offsets;
-  fp.masks = masks;
-  fp.out = static_cast<__bf16*>(out);
-  fp.lse = lse;
-  fp.part_o = static_cast<_Float16*>(workspace);
-  fp.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                        pl.part_ml_off);
-  fp.max_pps = max_pages_per_seq;
-  fp.num_pages = num_pages;
-  fp.log2_page = ilog2(page_size);
-  fp.W = mask_words;
-  fp.max_tokens = (int)std::min<long long>((long long)max_pages_per_seq * page_size,
-                                           1LL << 30);
-  fp.S = num_seqs;
-  fp.N = total_nodes;
-  fp.Hq = num_q_heads;
-  fp.Hkv = num_kv_heads;
-  fp.G = num_q_heads / num_kv_heads;
-  fp.mblocks = pl.mblocks;
-  fp.splits = pl.splits;
-  fp.chunk = pl.chunk;
-  fp.units = pl.units;
-  fp.per_xcd = (pl.units + 7) / 8;
-  fp.scale_log2 = scale * kLog2e;
-
-  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  const unsigned grid = 8u * (unsigned)fp.per_xcd;
-  if (pl.rows == kRowsPerWG8) {
-    hipLaunchKernelGGL(attn_fwd256_kernel<8>, dim3(grid), dim3(512), 0, hs, fp);
-  } else {
-    hipLaunchKernelGGL(attn_fwd128h_kernel, dim3(grid), dim3(512), 0, hs, fp);
-  }
-  if (hipGetLastError() != hipSuccess) return TREE_ATTN_ERR_HIP;
-
-  if (pl.splits > 1) {
-    MergeParams mp;
-    mp.prefix_lens = prefix_lens;
-    mp.tree_offsets = tree_offsets;
-    mp.part_o = fp.part_o;
-    mp.part_ml = fp.part_ml;
-    mp.out = fp.out;
-    mp.lse = lse;
-    mp.S = num_seqs;
-    mp.N = total_nodes;
-    mp.Hq = num_q_heads;
-    mp.Hkv = num_kv_heads;
-    mp.G = fp.G;
-    mp.splits = pl.splits;
-    mp.chunk = pl.chunk;
-    mp.max_tokens = fp.max_tokens;
-    mp.mblocks = pl.mblocks;
-    mp.rows_per_block = pl.rows;
-    const long long mgrid = (long long)num_seqs * num_kv_heads * pl.mblocks *
-                            (mp.rows_per_block / kMergeRowsPerWG);
-    hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)mgrid),
-                       dim3(kMergeWaves * 64), 0, hs, mp);
-    if (hipGetLastError() != hipSuccess) return TREE_ATTN_ERR_HIP;
-  }
-  return TREE_ATTN_OK;
+int tree_attn_verify_merge(
+    const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* page_table, int32_t max_pages_per_seq, int32_t num_pages,
+    int32_t page_size, const int32_t* prefix_lens,
+    const int32_t* tree_offsets, const uint64_t* masks, int32_t mask_words,
+    int32_t num_seqs, int32_t total_nodes, int32_t max_prefix_len,
+    int32_t max_nodes, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, float scale, int32_t num_splits, void* out, float* lse,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  return run_verify(kPhaseMerge, q, k_cache, v_cache, page_table,
+                    max_pages_per_seq, num_pages, page_size, prefix_lens,
+                    tree_offsets, masks, mask_words, num_seqs, total_nodes,
+                    max_prefix_len, max_nodes, num_q_heads, num_kv_heads,
+                    head_dim, scale, num_splits, out, lse, workspace,
+                    workspace_bytes, stream);
 }
 
 int tree_attn_accept(const int32_t* parents, const int32_t* tree_offsets,
