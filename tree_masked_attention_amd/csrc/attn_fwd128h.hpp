@@ -325,47 +325,27 @@ __global__ __launch_bounds__(512, 1) void attn_fwd128h_kernel(FwdParams p) {
   // ---- one pipeline step over tile j (this wave's half of it): S^T of
   // the next half tile on the matrix core while the vector ALU turns the
   // current scores into probabilities, then PV of tile j while the ALU
-  // finds the next half tile's max.  After the last tile the scores are
-  // computed on stale LDS data and dropped.
+  // finds the next half tile's max.  The instruction order inside a step
+  // is left to the compiler: with two waves per SIMD, explicit interleave
+  // groups and scheduling fences (as the 256-row kernel uses) made this
+  // kernel 2-3% slower.  After the last tile the scores are computed on
+  // stale LDS data and dropped.
   auto body = [&](int j, f32x16& Scur, f32x16& Snext, bool mask_next,
                   bool dma_inbody, float& m_new, float& alpha) -> bool {
     bf16x8 pf[2];
     DmaPlan dp{};
     if (dma_inbody) dp = dma_plan(j + kStages - 1);
-    // segment 1: S^T(j+1) | probabilities of tile j (K operands read two
-    // ahead of their MFMA)
+    // S^T(j+1) on the matrix core | probabilities of tile j
     qk_half(j + 1, Snext);
     exps_half(Scur, pf);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if (dma_inbody) {  // first half of tile j+3's DMA
-      dma_part(dp, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // segment 2: PV(j) | mask and max of tile j+1
+    if (dma_inbody) dma_part(dp, 0);  // first half of tile j+3's DMA
+    // PV(j) | mask and max of tile j+1
     pv_half(j, pf);
     if (mask_next) {
       apply_half_mask(Snext, half_allow(kbeg + (j + 1) * kKeyTile));
     }
     const bool need = next_ref(Snext, m_new, alpha);
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i < 6) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if (dma_inbody) {  // second half
-      dma_part(dp, 1);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    if (dma_inbody) dma_part(dp, 1);  // second half
     return need;
   };
   auto finish = [&](bool r, float m_new, float alpha) {
