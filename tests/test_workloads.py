@@ -74,3 +74,13 @@ def test_draw_tokens_gives_multi_node_paths():
     assert lens.max() >= 3
     d2, t2, r2 = draw_tokens(wl, 3)
     assert (d == d2).all() and (t == t2).all() and (r == r2).all()
+
+
+def test_draw_draft_topk_sorted_and_seeded():
+    from tree_masked_attention_amd.workloads import draw_draft_topk
+    lp, tok = draw_draft_topk(3, 5, 4, seed=9)
+    assert lp.shape == tok.shape == (3, 5, 4) and lp.dtype == np.float32
+    assert (np.diff(lp, axis=2) <= 0).all() and (lp <= 0).all()
+    assert np.isclose(np.exp(lp).sum(axis=2), 1.0).sum() == 0  # top-k only
+    lp2, tok2 = draw_draft_topk(3, 5, 4, seed=9)
+    assert (lp == lp2).all() and (tok == tok2).all()

@@ -368,6 +368,26 @@ def draw_tokens(wl: Workload, seed: int, vocab: int = 8,
     return draft, target, root
 
 
+def draw_draft_topk(num_seqs: int, depth: int, topk: int, seed: int,
+                    vocab: int = 32000, pool: int = 64):
+    """Synthetic per-depth outputs of a drafting head for tree construction:
+    for every sequence and depth, the top-k log-probabilities (fp32, sorted
+    non-increasing) of a softmax over `pool` random logits with a random
+    sharpness in [1, 4), and their tokens (distinct in [0, vocab))."""
+    rng = np.random.default_rng([seed, 11])
+    S, D, K = num_seqs, depth, topk
+    z = rng.standard_normal((S, D, pool)) * rng.uniform(1.0, 4.0, (S, D, 1))
+    z = z - z.max(axis=2, keepdims=True)
+    lse = np.log(np.exp(z).sum(axis=2, keepdims=True))
+    lp = np.sort(z - lse, axis=2)[:, :, ::-1][:, :, :K].astype(np.float32)
+    lp = np.ascontiguousarray(lp)
+    tok = np.empty((S, D, K), dtype=np.int32)
+    for s in range(S):
+        for d in range(D):
+            tok[s, d] = rng.choice(vocab, size=K, replace=False)
+    return lp, tok
+
+
 def standard_workload(name: str) -> Workload:
     seed, kw = STANDARD[name]
     return make_workload(seed, name=name, **kw)
