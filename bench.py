@@ -51,11 +51,16 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline")
-    ap.add_argument("--stage", choices=("verify", "accept-commit"),
+    ap.add_argument("--stage", choices=("verify", "accept-commit",
+                                        "tree-build"),
                     default="verify",
                     help="verify: the verification path (default); "
                          "accept-commit: tree acceptance + KV commit, the "
-                         "step after it")
+                         "step after it; tree-build: draft-tree "
+                         "construction, the step before it")
+    ap.add_argument("--width", type=int, default=1,
+                    help="tree-build: candidates taken per step (1 = strict "
+                         "best-first)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain 512 MiB device copies (the "
                          "reference kernel for scaling HBM byte counters)")
@@ -276,6 +281,12 @@ def accept_commit_stage(args, torch, api, wl, sets, stream):
     com_ms, _ = loop_ms(step_commit)
     sep_ms, _ = loop_ms(step_separate)
     ms_per_step, n_warm = loop_ms(step_fused)
+
+    # The fused kernel runs for a few microseconds, about what the host
+    # needs to issue a launch from Python, so this per-launch figure is
+    # bounded by the launch rate; the kernel trace gives the kernel's own
+    # time.  (A HIP graph of the launches is no way out: its kernels
+    # overlapped, 0.9 us per launch for a 3.6 us kernel.)
     fused_ms = ms_per_step
 
     L = lens[:S].cpu().numpy()
@@ -290,8 +301,9 @@ def accept_commit_stage(args, torch, api, wl, sets, stream):
     # of its parent and its mask row; per sequence the outputs
     acc_bytes = N * (16 + W * 8) + S * (max_b * 4 + 12)
     log(f"[bench] back-to-back launches: accept {acc_ms * 1e3:.1f} us, "
-        f"commit {com_ms * 1e3:.1f} us, both {sep_ms * 1e3:.1f} us; fused "
-        f"{fused_ms * 1e3:.1f} us; tau {L.tolist()[:8]}, {moved} rows moved")
+        f"commit {com_ms * 1e3:.1f} us, both {sep_ms * 1e3:.1f} us, fused "
+        f"{ms_per_step * 1e3:.1f} us; tau {L.tolist()[:8]}, {moved} rows "
+        f"moved")
     fused_bytes = com_bytes + acc_bytes
     achieved = fused_bytes / (fused_ms * 1e-3) / 1e9
     result = {
@@ -339,6 +351,96 @@ def accept_commit_stage(args, torch, api, wl, sets, stream):
     return 0
 
 
+TREE_DEPTH, TREE_TOPK = 16, 8  # per-depth head outputs for tree building
+
+
+def tree_build_stage(args, torch, api, wl, stream):
+    """Times tree_attn_build_tree for the workload's trees: num_seqs trees
+    of its budget from synthetic per-depth top-k head outputs."""
+    from tree_masked_attention_amd.workloads import draw_draft_topk
+    import oracle
+    dev = torch.device("cuda:0")
+    S, B = wl.num_seqs, int(wl.max_nodes)
+    D, K = TREE_DEPTH, TREE_TOPK
+    lp, tok = draw_draft_topk(S, D, K, seed=3)
+    lp_d, tok_d = torch.from_numpy(lp).to(dev), torch.from_numpy(tok).to(dev)
+    outs = [torch.empty((S, B), dtype=dt, device=dev)
+            for dt in (torch.int32, torch.int32, torch.int32, torch.float32)]
+    sizes = torch.empty((S,), dtype=torch.int32, device=dev)
+    f = api._lib.tree_attn_build_tree
+    argv = (lp_d.data_ptr(), tok_d.data_ptr(), S, D, K, B, args.width,
+            outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(),
+            outs[3].data_ptr(), sizes.data_ptr(), stream.cuda_stream)
+    n_warm = 0
+    t_w = time.perf_counter()
+    while n_warm < max(args.warmup, 1) or time.perf_counter() - t_w < 0.1:
+        if f(*argv) != 0:
+            raise RuntimeError("tree_attn_build_tree failed")
+        n_warm += 1
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        f(*argv)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    # check the last result against the oracle before reporting
+    ref = oracle.build_trees(lp, tok, B, args.width)
+    if not (np.array_equal(outs[0].cpu().numpy(), ref["parents"]) and
+            np.array_equal(sizes.cpu().numpy(), ref["sizes"])):
+        raise RuntimeError("tree build differs from the oracle")
+    alg_bytes = S * D * K * 8 + S * B * 16 + 4 * S
+    log(f"[bench] tree build: {S} x {B} nodes (depth {D}, top-{K}, width "
+        f"{args.width}): {ms * 1e3:.2f} us per launch")
+    result = {
+        "metric": "draft-tree construction, tree nodes/s",
+        "value": S * B / (ms * 1e-3),
+        "unit": "tree nodes/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "warmup_steps_run": n_warm,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "stage": "tree-build",
+                   "num_seqs": S, "budget": B, "depth": D, "topk": K,
+                   "width": args.width},
+        "roofline": {
+            "bound": "latency",
+            "kernel": "build_tree_kernel (tree_attn_build_tree)",
+            "achieved": alg_bytes / (ms * 1e-3) / 1e9,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "traffic": None,
+            "alg_bytes_per_launch": alg_bytes,
+            "avg_launch_us": ms * 1e3,
+            "note": "one wave per tree, B dependent extraction steps",
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] CPU baseline (oracle)")
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.build_trees(lp, tok, B, args.width)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= min(args.cpu_seconds, 5.0) or el / reps * (reps + 1) > 30:
+                break
+        result["cpu_baseline"] = {
+            "value": S * B * reps / el, "unit": "tree nodes/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{reps} full pass(es) of the same {S} trees, {el:.1f} s"}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 # --------------------------------------------------------------------------
 # GPU timing
 # --------------------------------------------------------------------------
@@ -363,6 +465,9 @@ def main():
 
     log(f"[bench] drawing workload {args.workload}")
     wl = standard_workload(args.workload)
+    if args.stage == "tree-build":
+        return tree_build_stage(args, torch, api, wl,
+                                torch.cuda.current_stream())
     alg_bytes, alg_flops = algorithmic_work(wl)
     ai = alg_flops / alg_bytes
     ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)

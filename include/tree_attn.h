@@ -220,6 +220,55 @@ int tree_attn_verify_merge(
     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * tree_attn_build_tree - draft trees by best-first expansion, the step
+ * before the verification.
+ *
+ * The drafting head emits logits for all tree depths at once; nodes are
+ * ranked by their cumulative draft log-probability and best-first
+ * expansion builds the tree up to a token budget (JETFLOW, gist.science
+ * 2606.18394, section 2, bullet on tree construction).  Each step may take
+ * the w best candidates at once and expand them together, which builds a
+ * B-node tree in ceil(B / w) steps (DFlash-TfM, gist.science 2607.06763,
+ * method section 2, tree construction).  The rule, per sequence s:
+ *  - candidates at depth d = 1 .. depth are (parent, rank j) with
+ *    tokens[s][d-1][j] and score = parent's score + logp[s][d-1][j] (fp32;
+ *    a depth-1 candidate has no parent node and score logp[s][0][j]);
+ *  - the candidate set starts with the topk depth-1 candidates; each step
+ *    removes the best min(width, budget - size) candidates -- higher score
+ *    first, then lower parent node index (none counts as -1), then lower
+ *    rank -- appends them as nodes in that order, then adds the topk
+ *    children of each of them (none past the last depth);
+ *  - it stops at budget nodes or when no candidate is left.
+ * Node indices are insertion order, so parents[i] < i (the topological
+ * order tree_attn_build_mask takes; depth-1 nodes are roots).
+ *
+ *   logp       dev fp32 [num_seqs][depth][topk], every row non-increasing
+ *              (as a top-k returns it) and finite
+ *   tokens     dev int32 [num_seqs][depth][topk]
+ *   depth      >= 0; topk 1 .. 64; depth * topk <= 8192
+ *   budget     0 .. TREE_ATTN_MAX_NODES; width >= 1 (1 = strict best-first)
+ *   parents, node_tokens, depths   dev int32 [num_seqs][budget] (outputs):
+ *              parent node index (-1 for a depth-1 node), token, depth;
+ *              past the tree's size: -1, -1, 0
+ *   scores     dev fp32 [num_seqs][budget] (output): node scores, 0 past
+ *              the size
+ *   sizes      dev int32 [num_seqs] (output): nodes built,
+ *              min(budget, number of nodes of the full tree)
+ *
+ * Rows that are not non-increasing, or not finite, give unspecified trees
+ * for that sequence, but no access outside the buffers above.
+ *
+ * Host-side errors: ERR_SHAPE (negative sizes, topk < 1, width < 1),
+ * ERR_UNSUPPORTED (budget > TREE_ATTN_MAX_NODES, topk > 64,
+ * depth * topk > 8192), ERR_NULL, ERR_HIP.
+ */
+int tree_attn_build_tree(const float* logp, const int32_t* tokens,
+                         int32_t num_seqs, int32_t depth, int32_t topk,
+                         int32_t budget, int32_t width, int32_t* parents,
+                         int32_t* node_tokens, int32_t* depths, float* scores,
+                         int32_t* sizes, void* stream);
+
+/*
  * tree_attn_accept - the accepted path of every verified draft tree.
  *
  * After the verification pass the target model has, for every tree node n,

@@ -251,3 +251,35 @@ def test_verify_phases_check_like_verify(fn):
                      a["masks"], a["W"], a["S"], a["N"], a["max_p"], a["max_b"],
                      a["Hq"], a["Hkv"], a["d"], a["scale"], a["splits"],
                      a["out"], a["lse"], a["ws"], a["ws_bytes"], None)) == code
+
+
+def _tree(**over):
+    a = dict(logp=1, tokens=1, S=1, D=4, K=4, B=16, w=1, par=1, tok=1,
+             dep=1, sc=1, sizes=1)
+    a.update(over)
+    return int(api._lib.tree_attn_build_tree(
+        a["logp"], a["tokens"], a["S"], a["D"], a["K"], a["B"], a["w"],
+        a["par"], a["tok"], a["dep"], a["sc"], a["sizes"], None))
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(S=-1), api.ERR_SHAPE),
+    (dict(D=-1), api.ERR_SHAPE),
+    (dict(K=0), api.ERR_SHAPE),
+    (dict(B=-1), api.ERR_SHAPE),
+    (dict(w=0), api.ERR_SHAPE),
+    (dict(B=1025), api.ERR_UNSUPPORTED),
+    (dict(K=65), api.ERR_UNSUPPORTED),
+    (dict(D=1025, K=8), api.ERR_UNSUPPORTED),
+    (dict(logp=None), api.ERR_NULL),
+    (dict(tokens=None), api.ERR_NULL),
+    (dict(par=None), api.ERR_NULL),
+    (dict(sc=None), api.ERR_NULL),
+    (dict(sizes=None), api.ERR_NULL),
+])
+def test_build_tree_rejects(over, code):
+    assert _tree(**over) == code
+
+
+def test_build_tree_empty_is_noop():
+    assert _tree(S=0, logp=None, sizes=None) == api.OK

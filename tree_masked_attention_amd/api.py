@@ -63,12 +63,16 @@ _lib.tree_attn_accept_commit.argtypes = [_p, _p, _p, _i, _p, _p, _p, _i, _i,
                                          _i, _p, _p, _p, _i, _i, _i, _p, _i,
                                          _p, _p, _p, _p]
 
+_lib.tree_attn_build_tree.restype = ctypes.c_int
+_lib.tree_attn_build_tree.argtypes = [_p, _p, _i, _i, _i, _i, _i, _p, _p, _p,
+                                      _p, _p, _p]
+
 EXPORTED = ("tree_attn_status_string", "tree_attn_abi_version",
             "tree_attn_build_mask", "tree_attn_workspace_size",
             "tree_attn_describe_plan", "tree_attn_verify",
             "tree_attn_verify_attend", "tree_attn_verify_merge",
             "tree_attn_accept", "tree_attn_commit_kv",
-            "tree_attn_accept_commit")
+            "tree_attn_accept_commit", "tree_attn_build_tree")
 
 
 class TreeAttnError(RuntimeError):
@@ -370,3 +374,30 @@ def accept_commit(parents: torch.Tensor, tree_offsets: torch.Tensor,
         _ptr(accept_nodes), _ptr(bonus_tokens), _stream(stream))
     _raise(code, "tree_attn_accept_commit")
     return accept_len[:S], accept_nodes[:S], bonus_tokens[:S]
+
+
+def build_tree(logp: torch.Tensor, tokens: torch.Tensor, budget: int,
+               width: int = 1, stream=None) -> dict:
+    """Draft trees by best-first expansion (width candidates per step).
+    logp fp32 [S, D, K] (rows non-increasing), tokens int32 [S, D, K].
+    Returns {"parents", "tokens", "depths": int32 [S, budget],
+    "scores": fp32 [S, budget], "sizes": int32 [S]}."""
+    _dev(logp, torch.float32, "logp")
+    _dev(tokens, torch.int32, "tokens")
+    if logp.dim() != 3 or tokens.shape != logp.shape:
+        raise ValueError("logp and tokens must both be [S, D, K]")
+    S, D, K = logp.shape
+    dev = logp.device
+    B = int(budget)
+    out = {"parents": torch.empty((S, B), dtype=torch.int32, device=dev),
+           "tokens": torch.empty((S, B), dtype=torch.int32, device=dev),
+           "depths": torch.empty((S, B), dtype=torch.int32, device=dev),
+           "scores": torch.empty((S, B), dtype=torch.float32, device=dev),
+           "sizes": torch.empty((max(S, 1),), dtype=torch.int32, device=dev)}
+    code = _lib.tree_attn_build_tree(
+        _ptr(logp), _ptr(tokens), S, D, K, B, int(width),
+        _ptr(out["parents"]), _ptr(out["tokens"]), _ptr(out["depths"]),
+        _ptr(out["scores"]), _ptr(out["sizes"]), _stream(stream))
+    _raise(code, "tree_attn_build_tree")
+    out["sizes"] = out["sizes"][:S]
+    return out

@@ -14,12 +14,13 @@
 #include "attn_merge.hpp"
 #include "common.hpp"
 #include "mask_build.hpp"
+#include "tree_build.hpp"
 
 using namespace tree_attn;
 
 namespace {
 
-constexpr int kAbiVersion = 6;
+constexpr int kAbiVersion = 7;
 constexpr int kMaxDevices = 64;
 constexpr int kMaxSplits = 256;
 constexpr int kMinKeysPerSplit = 256;
@@ -513,6 +514,56 @@ int tree_attn_verify_merge(
                     max_prefix_len, max_nodes, num_q_heads, num_kv_heads,
                     head_dim, scale, num_splits, out, lse, workspace,
                     workspace_bytes, stream);
+}
+
+int tree_attn_build_tree(const float* logp, const int32_t* tokens,
+                         int32_t num_seqs, int32_t depth, int32_t topk,
+                         int32_t budget, int32_t width, int32_t* parents,
+                         int32_t* node_tokens, int32_t* depths, float* scores,
+                         int32_t* sizes, void* stream) {
+  if (num_seqs < 0 || depth < 0 || topk < 1 || budget < 0 || width < 1) {
+    return TREE_ATTN_ERR_SHAPE;
+  }
+  if (budget > TREE_ATTN_MAX_NODES || topk > kTreeMaxTopK ||
+      (long long)depth * topk > kTreeMaxLogp) {
+    return TREE_ATTN_ERR_UNSUPPORTED;
+  }
+  if (num_seqs == 0) return TREE_ATTN_OK;
+  if (!sizes) return TREE_ATTN_ERR_NULL;
+  if (depth > 0 && (!logp || !tokens)) return TREE_ATTN_ERR_NULL;
+  if (budget > 0 && (!parents || !node_tokens || !depths || !scores)) {
+    return TREE_ATTN_ERR_NULL;
+  }
+  TreeParams tp;
+  tp.logp = logp;
+  tp.tokens = tokens;
+  tp.parents = parents;
+  tp.out_tokens = node_tokens;
+  tp.depths = depths;
+  tp.scores = scores;
+  tp.sizes = sizes;
+  tp.D = depth;
+  tp.K = topk;
+  tp.B = budget;
+  tp.W = width;
+  // slots 0 .. budget, 64 per register of a lane
+  const int ms = budget / 64 + 1;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const dim3 grid(num_seqs), block(64);
+  if (ms <= 1) {
+    hipLaunchKernelGGL(build_tree_kernel<1>, grid, block, 0, hs, tp);
+  } else if (ms <= 2) {
+    hipLaunchKernelGGL(build_tree_kernel<2>, grid, block, 0, hs, tp);
+  } else if (ms <= 4) {
+    hipLaunchKernelGGL(build_tree_kernel<4>, grid, block, 0, hs, tp);
+  } else if (ms <= 8) {
+    hipLaunchKernelGGL(build_tree_kernel<8>, grid, block, 0, hs, tp);
+  } else if (ms <= 16) {
+    hipLaunchKernelGGL(build_tree_kernel<16>, grid, block, 0, hs, tp);
+  } else {
+    hipLaunchKernelGGL(build_tree_kernel<17>, grid, block, 0, hs, tp);
+  }
+  return hipGetLastError() == hipSuccess ? TREE_ATTN_OK : TREE_ATTN_ERR_HIP;
 }
 
 int tree_attn_accept(const int32_t* parents, const int32_t* tree_offsets,
