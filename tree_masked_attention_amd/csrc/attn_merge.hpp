@@ -7,8 +7,7 @@
 //     lse = ln2 * (m* + log2 sum_c w_c).
 // A split in which the row saw no allowed key has m_c = -inf, l_c = 0 and
 // contributes nothing.  The sums are accumulated with a running maximum,
-// which gives the same values up to rounding order.  Each lane owns two of
-// the 128 output columns of a row.
+// which gives the same values up to rounding order.
 #pragma once
 
 #include "common.hpp"
@@ -27,18 +26,22 @@ struct MergeParams {
 };
 
 constexpr int kMergeWaves = 4;
-constexpr int kMergeRows = 4;    // rows per wave
+constexpr int kMergeRows = 8;    // rows per wave: 4 per lane half
 constexpr int kMergeSplits = 4;  // splits whose loads are issued together
 constexpr int kMergeRowsPerWG = kMergeWaves * kMergeRows;
 
 // Workgroups are laid out like the attention launch: (sequence, kv head,
 // row block), each row block cut into pieces of kMergeRowsPerWG rows, so
 // the sequence of every row is known from the workgroup id.  A wave merges
-// kMergeRows rows; the loads of kMergeSplits splits of all its rows are
-// issued before any is used, and the sums run with a running maximum.
+// kMergeRows rows, each lane half one row at a time with four columns per
+// lane (8-byte loads, a whole 256-byte row per half-wave instruction); the
+// loads of kMergeSplits splits of all its rows are issued before any is
+// used, and the sums run with a running maximum.
 __global__ __launch_bounds__(kMergeWaves * 64) void attn_merge_kernel(
     MergeParams p) {
+  constexpr int RL = kMergeRows / 2;  // rows per lane
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int half = lane >> 5, c4 = (lane & 31) * 4;
   const int pieces = p.rows_per_block / kMergeRowsPerWG;
   int L = blockIdx.x / pieces;
   const int piece = blockIdx.x - L * pieces;
@@ -57,54 +60,58 @@ __global__ __launch_bounds__(kMergeWaves * 64) void attn_merge_kernel(
   const int nsplit = min(p.splits, (T + p.chunk - 1) / p.chunk);
   const size_t NH = (size_t)p.N * p.Hq;
 
-  size_t qrow[kMergeRows];
-  float m_run[kMergeRows], l_run[kMergeRows];
-  f32x2 acc[kMergeRows];
+  size_t qrow[RL];
+  float m_run[RL], l_run[RL];
+  f32x4 acc[RL];
 #pragma unroll
-  for (int k = 0; k < kMergeRows; ++k) {
-    const int r = min(r0 + k, rows - 1);
+  for (int k = 0; k < RL; ++k) {
+    const int r = min(r0 + 2 * k + half, rows - 1);
     qrow[k] = (size_t)(a + r / p.G) * p.Hq + g * p.G + r % p.G;
     m_run[k] = -INFINITY;
     l_run[k] = 0.f;
-    acc[k] = f32x2{0.f, 0.f};
+    acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   for (int c0 = 0; c0 < nsplit; c0 += kMergeSplits) {
-    f32x2 ml[kMergeRows][kMergeSplits];
-    f16x2 oc[kMergeRows][kMergeSplits];
+    f32x2 ml[RL][kMergeSplits];
+    f16x4 oc[RL][kMergeSplits];
 #pragma unroll
-    for (int k = 0; k < kMergeRows; ++k) {
+    for (int k = 0; k < RL; ++k) {
 #pragma unroll
       for (int u = 0; u < kMergeSplits; ++u) {
         const int c = min(c0 + u, nsplit - 1);  // in range; unused if past
         const size_t prow = (size_t)c * NH + qrow[k];
         ml[k][u] = *reinterpret_cast<const f32x2*>(p.part_ml + prow * 2);
-        oc[k][u] = *reinterpret_cast<const f16x2*>(p.part_o + prow * kHeadDim +
-                                                   lane * 2);
+        oc[k][u] = *reinterpret_cast<const f16x4*>(p.part_o + prow * kHeadDim +
+                                                   c4);
       }
     }
 #pragma unroll
     for (int u = 0; u < kMergeSplits; ++u) {
       if (c0 + u >= nsplit) break;
 #pragma unroll
-      for (int k = 0; k < kMergeRows; ++k) {
+      for (int k = 0; k < RL; ++k) {
         const float m_new = fmaxf(m_run[k], ml[k][u][0]);
         if (m_new == -INFINITY) continue;  // no key seen yet
         const float s_old = fast_exp2(m_run[k] - m_new);
         const float w = fast_exp2(ml[k][u][0] - m_new) * ml[k][u][1];
         l_run[k] = l_run[k] * s_old + w;
-        acc[k][0] = acc[k][0] * s_old + w * (float)oc[k][u][0];
-        acc[k][1] = acc[k][1] * s_old + w * (float)oc[k][u][1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[k][e] = acc[k][e] * s_old + w * (float)oc[k][u][e];
+        }
         m_run[k] = m_new;
       }
     }
   }
 #pragma unroll
-  for (int k = 0; k < kMergeRows; ++k) {
-    if (r0 + k >= rows) continue;
+  for (int k = 0; k < RL; ++k) {
+    if (r0 + 2 * k + half >= rows) continue;
     const float inv = l_run[k] > 0.f ? 1.f / l_run[k] : 0.f;
-    bf16x2 r2 = {(__bf16)(acc[k][0] * inv), (__bf16)(acc[k][1] * inv)};
-    *reinterpret_cast<bf16x2*>(p.out + qrow[k] * kHeadDim + lane * 2) = r2;
-    if (lane == 0) {
+    bf16x4 r4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r4[e] = (__bf16)(acc[k][e] * inv);
+    *reinterpret_cast<bf16x4*>(p.out + qrow[k] * kHeadDim + c4) = r4;
+    if ((lane & 31) == 0) {
       p.lse[qrow[k]] =
           l_run[k] > 0.f ? (m_run[k] + log2f(l_run[k])) * kLn2 : -INFINITY;
     }
