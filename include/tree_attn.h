@@ -386,6 +386,97 @@ int tree_attn_accept_commit(
     int32_t token_bytes, int32_t* accept_len, int32_t* accept_nodes,
     int32_t* bonus_tokens, void* stream);
 
+/* Largest tree tree_attn_gdn_verify takes (nodes). */
+#define TREE_ATTN_GDN_MAX_NODES 128
+
+/*
+ * tree_attn_gdn_verify - rollback-free verification of a draft tree through
+ * one Gated DeltaNet (GDN) layer.
+ *
+ * DFlash-TfM (gist.science 2607.06763, method section 3, rollback-free tree
+ * verification for GDN) gives the GDN state recurrence
+ *   S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,
+ * sorts the tree topologically and verifies it through a masked triangular
+ * solve (I + X) U = beta V over ancestor relations, committing the state
+ * only after acceptance.  The pages leave the per-node quantities open;
+ * this call fixes them as follows.  Per node i and head h: alpha_i =
+ * e^{g_i}; node i's state S_i is the recurrence run along its
+ * root-to-node path starting from the committed state S0 of its sequence
+ * (siblings and descendants play no part); the outputs are
+ *   out_i = S_i^T q_i                          (after node i's own update)
+ *   u_i   = beta_i (v_i - alpha_i S_parent^T k_i),
+ * so that S_i = alpha_i S_parent + k_i u_i^T (S_parent = S0 for a root).
+ * u is what tree_attn_gdn_commit needs.  A chain gives the ordinary
+ * token-by-token recurrence.
+ *
+ *   q, k, v       dev bf16 [total_nodes][num_heads][head_dim]
+ *   g             dev fp32 [total_nodes][num_heads]  log-decay (<= 0)
+ *   beta          dev fp32 [total_nodes][num_heads]
+ *   state         dev fp32 [num_seqs][num_heads][head_dim (k)][head_dim (v)]
+ *                 S0 per sequence and head, k-major; read only
+ *   tree_offsets  dev int32 [num_seqs + 1], as for tree_attn_build_mask
+ *   masks, mask_words   as written by tree_attn_build_mask
+ *   max_nodes     host upper bound on every B_s,
+ *                 <= TREE_ATTN_GDN_MAX_NODES (128)
+ *   num_heads     >= 1 (q, k, v, g and beta all carry num_heads heads)
+ *   head_dim      d_k = d_v; must be 128
+ *   out           dev bf16 [total_nodes][num_heads][head_dim] (output)
+ *   u             dev fp32 [total_nodes][num_heads][head_dim] (output)
+ *
+ * Precision: products run on the bf16 matrix cores; fp32 operands (S0 and
+ * the triangular factors) are split into two bf16 parts, which keeps about
+ * 16 mantissa bits per product; accumulation is fp32.  out is rounded to
+ * bf16 once at the end.
+ * A tree with more than 128 nodes (tree_offsets breaking max_nodes) is
+ * skipped without writing.
+ *
+ * Host-side errors: ERR_SHAPE (negative sizes, num_heads < 1, mask_words *
+ * 64 < max_nodes), ERR_UNSUPPORTED (head_dim != 128, max_nodes > 128,
+ * num_seqs * num_heads > 2^31 - 1), ERR_NULL, ERR_HIP.
+ */
+int tree_attn_gdn_verify(const void* q, const void* k, const void* v,
+                         const float* g, const float* beta,
+                         const float* state, const int32_t* tree_offsets,
+                         const uint64_t* masks, int32_t mask_words,
+                         int32_t num_seqs, int32_t total_nodes,
+                         int32_t max_nodes, int32_t num_heads,
+                         int32_t head_dim, void* out, float* u,
+                         void* stream);
+
+/*
+ * tree_attn_gdn_commit - the deferred GDN state commit (DFlash-TfM,
+ * gist.science 2607.06763, method section 3: the state is committed once
+ * the accepted branch is known).
+ *
+ * For every sequence s and head h, state[s][h] is replaced, in place, by
+ * the state of the last accepted node: with p_1 .. p_n the accepted path
+ * (accept_nodes[s][0 .. n-1], n = accept_len[s], root first, as written
+ * by tree_attn_accept) and G_j the sum of g over p_1 .. p_j,
+ *   S_new = e^{G_n} S0 + sum_j e^{G_n - G_j} k_{p_j} u_{p_j}^T,
+ * which equals the recurrence S <- alpha S + k u^T run along the path.
+ * n = 0 leaves the state unchanged.  u is the output of
+ * tree_attn_gdn_verify for the same tree.
+ *
+ *   k, u, g       as for tree_attn_gdn_verify (u as it wrote it)
+ *   tree_offsets  dev int32 [num_seqs + 1]
+ *   accept_len    dev int32 [num_seqs]
+ *   accept_nodes  dev int32 [num_seqs][max_nodes], local node indices
+ *   max_nodes     columns of accept_nodes, <= TREE_ATTN_MAX_NODES
+ *   state         dev fp32 [num_seqs][num_heads][head_dim][head_dim],
+ *                 updated in place
+ *
+ * Path entries outside the tree are skipped; accept_len is clamped to
+ * [0, max_nodes].  Host-side errors: ERR_SHAPE (negative sizes,
+ * num_heads < 1), ERR_UNSUPPORTED (head_dim != 128, max_nodes >
+ * TREE_ATTN_MAX_NODES), ERR_NULL, ERR_HIP.
+ */
+int tree_attn_gdn_commit(const void* k, const float* u, const float* g,
+                         const int32_t* tree_offsets,
+                         const int32_t* accept_len,
+                         const int32_t* accept_nodes, int32_t num_seqs,
+                         int32_t max_nodes, int32_t num_heads,
+                         int32_t head_dim, float* state, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

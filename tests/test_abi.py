@@ -283,3 +283,68 @@ def test_build_tree_rejects(over, code):
 
 def test_build_tree_empty_is_noop():
     assert _tree(S=0, logp=None, sizes=None) == api.OK
+
+
+def _gdn(**over):
+    a = dict(q=1, k=1, v=1, g=1, beta=1, st=1, offs=1, masks=1, W=2, S=2,
+             N=20, max_b=128, H=4, d=128, out=1, u=1)
+    a.update(over)
+    return int(api._lib.tree_attn_gdn_verify(
+        a["q"], a["k"], a["v"], a["g"], a["beta"], a["st"], a["offs"],
+        a["masks"], a["W"], a["S"], a["N"], a["max_b"], a["H"], a["d"],
+        a["out"], a["u"], None))
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(S=-1), api.ERR_SHAPE),
+    (dict(N=-1), api.ERR_SHAPE),
+    (dict(H=0), api.ERR_SHAPE),
+    (dict(W=0), api.ERR_SHAPE),
+    (dict(W=1, max_b=65), api.ERR_SHAPE),
+    (dict(d=64), api.ERR_UNSUPPORTED),
+    (dict(max_b=129, W=3), api.ERR_UNSUPPORTED),
+    (dict(S=1 << 20, H=1 << 12), api.ERR_UNSUPPORTED),
+    (dict(q=None), api.ERR_NULL),
+    (dict(beta=None), api.ERR_NULL),
+    (dict(st=None), api.ERR_NULL),
+    (dict(masks=None), api.ERR_NULL),
+    (dict(out=None), api.ERR_NULL),
+    (dict(u=None), api.ERR_NULL),
+])
+def test_gdn_verify_rejects(over, code):
+    assert _gdn(**over) == code
+
+
+def test_gdn_verify_empty_is_noop():
+    assert _gdn(S=0, q=None) == api.OK
+    assert _gdn(N=0, q=None) == api.OK
+
+
+def _gdn_commit(**over):
+    a = dict(k=1, u=1, g=1, offs=1, alen=1, anodes=1, S=2, max_b=16, H=4,
+             d=128, st=1)
+    a.update(over)
+    return int(api._lib.tree_attn_gdn_commit(
+        a["k"], a["u"], a["g"], a["offs"], a["alen"], a["anodes"], a["S"],
+        a["max_b"], a["H"], a["d"], a["st"], None))
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(S=-1), api.ERR_SHAPE),
+    (dict(max_b=-1), api.ERR_SHAPE),
+    (dict(H=0), api.ERR_SHAPE),
+    (dict(d=256), api.ERR_UNSUPPORTED),
+    (dict(max_b=1025), api.ERR_UNSUPPORTED),
+    (dict(S=1 << 20, H=1 << 12), api.ERR_UNSUPPORTED),
+    (dict(k=None), api.ERR_NULL),
+    (dict(alen=None), api.ERR_NULL),
+    (dict(anodes=None), api.ERR_NULL),
+    (dict(st=None), api.ERR_NULL),
+])
+def test_gdn_commit_rejects(over, code):
+    assert _gdn_commit(**over) == code
+
+
+def test_gdn_commit_empty_is_noop():
+    assert _gdn_commit(S=0, k=None) == api.OK
+    assert _gdn_commit(max_b=0, k=None) == api.OK

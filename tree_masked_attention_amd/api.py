@@ -67,12 +67,21 @@ _lib.tree_attn_build_tree.restype = ctypes.c_int
 _lib.tree_attn_build_tree.argtypes = [_p, _p, _i, _i, _i, _i, _i, _p, _p, _p,
                                       _p, _p, _p]
 
+_lib.tree_attn_gdn_verify.restype = ctypes.c_int
+_lib.tree_attn_gdn_verify.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _i, _i,
+                                      _i, _i, _i, _i, _p, _p, _p]
+_lib.tree_attn_gdn_commit.restype = ctypes.c_int
+_lib.tree_attn_gdn_commit.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i,
+                                      _p, _p]
+
 EXPORTED = ("tree_attn_status_string", "tree_attn_abi_version",
             "tree_attn_build_mask", "tree_attn_workspace_size",
             "tree_attn_describe_plan", "tree_attn_verify",
             "tree_attn_verify_attend", "tree_attn_verify_merge",
             "tree_attn_accept", "tree_attn_commit_kv",
-            "tree_attn_accept_commit", "tree_attn_build_tree")
+            "tree_attn_accept_commit", "tree_attn_build_tree",
+            "tree_attn_gdn_verify", "tree_attn_gdn_commit")
+GDN_MAX_NODES = 128
 
 
 class TreeAttnError(RuntimeError):
@@ -401,3 +410,67 @@ def build_tree(logp: torch.Tensor, tokens: torch.Tensor, budget: int,
     _raise(code, "tree_attn_build_tree")
     out["sizes"] = out["sizes"][:S]
     return out
+
+
+def gdn_verify(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+               g: torch.Tensor, beta: torch.Tensor, state: torch.Tensor,
+               tree_offsets: torch.Tensor, masks: torch.Tensor,
+               max_nodes: int, out: Optional[torch.Tensor] = None,
+               u: Optional[torch.Tensor] = None,
+               stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Gated DeltaNet tree verification.  q, k, v bf16 [N, H, 128]; g, beta
+    fp32 [N, H]; state fp32 [S, H, 128, 128] (S0, read only); masks from
+    build_mask.  Returns (out bf16 [N, H, 128], u fp32 [N, H, 128])."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, torch.bfloat16, n)
+    for t, n in ((g, "g"), (beta, "beta"), (state, "state")):
+        _dev(t, torch.float32, n)
+    _dev(tree_offsets, torch.int32, "tree_offsets")
+    _dev(masks, torch.int64, "masks")
+    if q.dim() != 3 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k and v must all be [N, H, d]")
+    N, H, d = q.shape
+    S = tree_offsets.numel() - 1
+    if g.shape != (N, H) or beta.shape != (N, H) or \
+            state.shape != (S, H, d, d):
+        raise ValueError("g / beta must be [N, H] and state [S, H, d, d]")
+    if masks.dim() != 2 or masks.shape[0] != N:
+        raise ValueError("masks must be [N, W]")
+    if out is None:
+        out = torch.empty_like(q)
+    if u is None:
+        u = torch.empty((N, H, d), dtype=torch.float32, device=q.device)
+    code = _lib.tree_attn_gdn_verify(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
+        _ptr(tree_offsets), _ptr(masks), masks.shape[1], S, N,
+        int(max_nodes), H, d, _ptr(out), _ptr(u), _stream(stream))
+    _raise(code, "tree_attn_gdn_verify")
+    return out, u
+
+
+def gdn_commit(k: torch.Tensor, u: torch.Tensor, g: torch.Tensor,
+               tree_offsets: torch.Tensor, accept_len: torch.Tensor,
+               accept_nodes: torch.Tensor, state: torch.Tensor,
+               stream=None) -> None:
+    """Deferred GDN state commit, in place on state fp32 [S, H, 128, 128]:
+    the state of the last accepted node (accept_len / accept_nodes from
+    accept()); k bf16 and u fp32 [N, H, 128], g fp32 [N, H]."""
+    _dev(k, torch.bfloat16, "k")
+    for t, n in ((u, "u"), (g, "g"), (state, "state")):
+        _dev(t, torch.float32, n)
+    for t, n in ((tree_offsets, "tree_offsets"), (accept_len, "accept_len"),
+                 (accept_nodes, "accept_nodes")):
+        _dev(t, torch.int32, n)
+    if k.dim() != 3 or u.shape != k.shape:
+        raise ValueError("k and u must both be [N, H, d]")
+    N, H, d = k.shape
+    S = tree_offsets.numel() - 1
+    if g.shape != (N, H) or state.shape != (S, H, d, d) or \
+            accept_len.numel() != S or accept_nodes.dim() != 2 or \
+            accept_nodes.shape[0] != S:
+        raise ValueError("g / state / accept arrays do not match")
+    code = _lib.tree_attn_gdn_commit(
+        _ptr(k), _ptr(u), _ptr(g), _ptr(tree_offsets), _ptr(accept_len),
+        _ptr(accept_nodes), S, accept_nodes.shape[1], H, d, _ptr(state),
+        _stream(stream))
+    _raise(code, "tree_attn_gdn_commit")

@@ -13,6 +13,7 @@
 #include "attn_fwd8.hpp"
 #include "attn_merge.hpp"
 #include "common.hpp"
+#include "gdn.hpp"
 #include "mask_build.hpp"
 #include "tree_build.hpp"
 
@@ -20,7 +21,7 @@ using namespace tree_attn;
 
 namespace {
 
-constexpr int kAbiVersion = 7;
+constexpr int kAbiVersion = 8;
 constexpr int kMaxDevices = 64;
 constexpr int kMaxSplits = 256;
 constexpr int kMinKeysPerSplit = 256;
@@ -647,6 +648,85 @@ int tree_attn_accept_commit(
   hipLaunchKernelGGL(accept_commit_kernel, dim3((unsigned)grid),
                      dim3(threads), 0, reinterpret_cast<hipStream_t>(stream),
                      ap, cp);
+  return hipGetLastError() == hipSuccess ? TREE_ATTN_OK : TREE_ATTN_ERR_HIP;
+}
+
+int tree_attn_gdn_verify(const void* q, const void* k, const void* v,
+                         const float* g, const float* beta,
+                         const float* state, const int32_t* tree_offsets,
+                         const uint64_t* masks, int32_t mask_words,
+                         int32_t num_seqs, int32_t total_nodes,
+                         int32_t max_nodes, int32_t num_heads,
+                         int32_t head_dim, void* out, float* u,
+                         void* stream) {
+  if (num_seqs < 0 || total_nodes < 0 || max_nodes < 0 || num_heads < 1 ||
+      mask_words < 1) {
+    return TREE_ATTN_ERR_SHAPE;
+  }
+  if (head_dim != kHeadDim || max_nodes > kGdnMaxNodes) {
+    return TREE_ATTN_ERR_UNSUPPORTED;
+  }
+  if ((long long)mask_words * 64 < max_nodes) return TREE_ATTN_ERR_SHAPE;
+  if ((long long)num_seqs * num_heads > 0x7fffffffLL) {
+    return TREE_ATTN_ERR_UNSUPPORTED;
+  }
+  if (num_seqs == 0 || total_nodes == 0) return TREE_ATTN_OK;
+  if (!q || !k || !v || !g || !beta || !state || !tree_offsets || !masks ||
+      !out || !u) {
+    return TREE_ATTN_ERR_NULL;
+  }
+  GdnParams gp;
+  gp.q = static_cast<const __bf16*>(q);
+  gp.k = static_cast<const __bf16*>(k);
+  gp.v = static_cast<const __bf16*>(v);
+  gp.g = g;
+  gp.beta = beta;
+  gp.state = state;
+  gp.tree_offsets = tree_offsets;
+  gp.masks = masks;
+  gp.out = static_cast<__bf16*>(out);
+  gp.u = u;
+  gp.H = num_heads;
+  gp.W = mask_words;
+  hipLaunchKernelGGL(gdn_verify_kernel, dim3((unsigned)(num_seqs * num_heads)),
+                     dim3(kGdnThreads), 0,
+                     reinterpret_cast<hipStream_t>(stream), gp);
+  return hipGetLastError() == hipSuccess ? TREE_ATTN_OK : TREE_ATTN_ERR_HIP;
+}
+
+int tree_attn_gdn_commit(const void* k, const float* u, const float* g,
+                         const int32_t* tree_offsets,
+                         const int32_t* accept_len,
+                         const int32_t* accept_nodes, int32_t num_seqs,
+                         int32_t max_nodes, int32_t num_heads,
+                         int32_t head_dim, float* state, void* stream) {
+  if (num_seqs < 0 || max_nodes < 0 || num_heads < 1) {
+    return TREE_ATTN_ERR_SHAPE;
+  }
+  if (head_dim != kHeadDim || max_nodes > TREE_ATTN_MAX_NODES) {
+    return TREE_ATTN_ERR_UNSUPPORTED;
+  }
+  if ((long long)num_seqs * num_heads > 0x7fffffffLL) {
+    return TREE_ATTN_ERR_UNSUPPORTED;
+  }
+  if (num_seqs == 0 || max_nodes == 0) return TREE_ATTN_OK;
+  if (!k || !u || !g || !tree_offsets || !accept_len || !accept_nodes ||
+      !state) {
+    return TREE_ATTN_ERR_NULL;
+  }
+  GdnCommitParams cp;
+  cp.k = static_cast<const __bf16*>(k);
+  cp.u = u;
+  cp.g = g;
+  cp.tree_offsets = tree_offsets;
+  cp.accept_len = accept_len;
+  cp.accept_nodes = accept_nodes;
+  cp.state = state;
+  cp.H = num_heads;
+  cp.max_nodes = max_nodes;
+  hipLaunchKernelGGL(gdn_commit_kernel, dim3((unsigned)(num_seqs * num_heads)),
+                     dim3(kGdnThreads), 0,
+                     reinterpret_cast<hipStream_t>(stream), cp);
   return hipGetLastError() == hipSuccess ? TREE_ATTN_OK : TREE_ATTN_ERR_HIP;
 }
 

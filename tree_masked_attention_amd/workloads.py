@@ -388,26 +388,42 @@ def draw_draft_topk(num_seqs: int, depth: int, topk: int, seed: int,
     return lp, tok
 
 
-def draw_gdn_inputs(wl: Workload, seed: int, heads: int = 8,
-                    dim: int = 128):
-    """Synthetic Gated DeltaNet layer inputs for the trees of `wl`: per node
-    and head q, k (unit length, then rounded to bf16), v (N(0, 1), bf16),
-    log-decays g = -U(0.001, 0.1) (alpha = e^g near 1), write strengths
-    beta = sigmoid(N(0, 1)) (fp32), and per sequence and head a committed
-    state S0 with N(0, 0.25) entries (fp32).  Returns bf16 arrays as uint16
-    bits and fp32 arrays: (q, k, v, g, beta, S0)."""
+def draw_gdn_inputs(num_seqs: int, total_nodes: int, seed: int,
+                    heads: int = 8, dim: int = 128):
+    """Synthetic Gated DeltaNet layer inputs for num_seqs trees with
+    total_nodes nodes: per node and head q, k (unit length, then rounded to
+    bf16), v (N(0, 1), bf16), log-decays g = -U(0.001, 0.1) (alpha = e^g
+    near 1), write strengths beta = sigmoid(N(0, 1)) (fp32), and per
+    sequence and head a committed state S0 with N(0, 0.25) entries (fp32).
+    Returns bf16 arrays as uint16 bits and fp32 arrays:
+    (q, k, v, g, beta, S0)."""
     rng = np.random.default_rng([seed, 13])
-    N, S, H, d = wl.total_nodes, wl.num_seqs, heads, dim
-    q = rng.standard_normal((N, H, d)).astype(np.float32)
-    k = rng.standard_normal((N, H, d)).astype(np.float32)
-    q /= np.linalg.norm(q, axis=2, keepdims=True)
-    k /= np.linalg.norm(k, axis=2, keepdims=True)
-    v = rng.standard_normal((N, H, d)).astype(np.float32)
+    N, S, H, d = int(total_nodes), int(num_seqs), int(heads), int(dim)
+    q = rng.standard_normal((N, H, d), dtype=np.float32)
+    k = rng.standard_normal((N, H, d), dtype=np.float32)
+    q /= np.maximum(np.linalg.norm(q, axis=2, keepdims=True), 1e-30)
+    k /= np.maximum(np.linalg.norm(k, axis=2, keepdims=True), 1e-30)
+    v = rng.standard_normal((N, H, d), dtype=np.float32)
     g = (-rng.uniform(0.001, 0.1, size=(N, H))).astype(np.float32)
     beta = (1.0 / (1.0 + np.exp(-rng.standard_normal((N, H))))).astype(np.float32)
-    S0 = (rng.standard_normal((S, H, d, d)) * 0.5).astype(np.float32)
+    S0 = rng.standard_normal((S, H, d, d), dtype=np.float32) * np.float32(0.5)
     return (f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v),
             g, beta, S0)
+
+
+def gdn_trees(tree_sizes: Sequence[int], rules: Sequence[str] | str,
+              seed: int, p_chain: float = 0.5):
+    """Parent arrays and tree offsets of a batch of draft trees drawn with
+    draw_tree (rules per tree or one for all)."""
+    rng = np.random.default_rng([seed, 17])
+    S = len(tree_sizes)
+    rules = [rules] * S if isinstance(rules, str) else list(rules)
+    par = [draw_tree(rng, int(b), r, p_chain) for b, r in zip(tree_sizes, rules)]
+    offsets = np.zeros(S + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(tree_sizes)
+    parents = (np.concatenate(par).astype(np.int32) if S
+               else np.zeros(0, np.int32))
+    return parents, offsets
 
 
 def standard_workload(name: str) -> Workload:
