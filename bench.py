@@ -14,6 +14,11 @@ path has run for about 0.3 s.
 --stage accept-commit times the step after the verification instead:
 tree acceptance and the commit of the accepted rows' K/V (one fused launch,
 with the two-launch form beside it), on tokens drawn for the workload.
+--stage tree-build times the draft-tree construction before it.
+--stage gdn times tree verification through a Gated DeltaNet layer
+(tree_attn_gdn_verify) on its own synthetic workload (--gdn-seqs trees of
+--gdn-nodes nodes, --gdn-heads heads of d_k = d_v = 128), with the
+deferred state commit of an accepted path timed beside it.
 
 Prints one JSON line on stdout.  Everything else goes to stderr.
 """
@@ -52,12 +57,20 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline")
     ap.add_argument("--stage", choices=("verify", "accept-commit",
-                                        "tree-build"),
+                                        "tree-build", "gdn"),
                     default="verify",
                     help="verify: the verification path (default); "
                          "accept-commit: tree acceptance + KV commit, the "
                          "step after it; tree-build: draft-tree "
-                         "construction, the step before it")
+                         "construction, the step before it; gdn: tree "
+                         "verification through a Gated DeltaNet layer "
+                         "(and its state commit)")
+    ap.add_argument("--gdn-seqs", type=int, default=16,
+                    help="gdn: draft trees (sequences)")
+    ap.add_argument("--gdn-nodes", type=int, default=128,
+                    help="gdn: nodes per tree (<= 128)")
+    ap.add_argument("--gdn-heads", type=int, default=32,
+                    help="gdn: heads (d_k = d_v = 128)")
     ap.add_argument("--width", type=int, default=1,
                     help="tree-build: candidates taken per step (1 = strict "
                          "best-first)")
@@ -442,6 +455,205 @@ def tree_build_stage(args, torch, api, wl, stream):
 
 
 # --------------------------------------------------------------------------
+# Gated DeltaNet tree verification
+# --------------------------------------------------------------------------
+
+def gdn_work(S, B, H, depth_sum, W, d=128):
+    """(bytes, flops) of one tree_attn_gdn_verify call that the method
+    needs: q, k, v read once (bf16), g and beta (fp32), the ancestor masks
+    (once per tree), S0 (fp32, d x d per sequence and head), out (bf16) and
+    u (fp32) written once.  flops: K S0 and Q S0 (2 * 2 B d^2), the Gram
+    products over ancestor-or-self pairs (2 * 2 d each), the triangular
+    solve over strict-ancestor pairs and the output over ancestor-or-self
+    pairs (2 d each), per sequence and head; depth_sum = sum over all
+    nodes of the number of ancestor-or-self nodes."""
+    N = S * B
+    nbytes = (N * H * d * 2 * 3 + N * H * 4 * 2 + N * W * 8 +
+              S * H * d * d * 4 + N * H * d * (2 + 4))
+    anc_self = depth_sum
+    strict = depth_sum - N
+    flops = H * (2 * 2 * N * d * d + 2 * 2 * anc_self * d +
+                 2 * strict * d + 2 * anc_self * d)
+    return nbytes, flops
+
+
+def gdn_stage(args, torch, api):
+    """Times tree_attn_gdn_verify (and tree_attn_gdn_commit) on synthetic
+    Gated DeltaNet inputs: --gdn-seqs trees of --gdn-nodes nodes drawn with
+    the pchain rule, --gdn-heads heads."""
+    from tree_masked_attention_amd.workloads import (draw_gdn_inputs,
+                                                     gdn_trees)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    S, B, H, d = args.gdn_seqs, args.gdn_nodes, args.gdn_heads, 128
+    N = S * B
+    name = f"gdn-h{H}-b{B}-x{S}"
+    parents, offsets = gdn_trees([B] * S, "pchain", 7)
+    x = draw_gdn_inputs(S, N, 7, heads=H)
+    depth = np.zeros(N, np.int64)
+    for i in range(N):
+        p = int(parents[i])
+        local = i - int(offsets[i // B])
+        depth[i] = 1 if p < 0 else depth[i - local + p] + 1
+    W = api.mask_words_for(B)
+    alg_bytes, alg_flops = gdn_work(S, B, H, int(depth.sum()), W, d)
+    # input copies rotated so that no launch finds its inputs in the
+    # 256 MB Infinity Cache
+    copies = max(2, min(16, int(math.ceil(ROTATE_BYTES / alg_bytes))))
+    bf = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+    par_d = torch.from_numpy(parents).to(dev)
+    off_d = torch.from_numpy(offsets).to(dev)
+    masks, _ = api.build_mask(par_d, off_d, B)
+    sets = []
+    for c in range(copies):
+        q, k, v = (bf(a).to(dev) for a in x[:3])
+        g, beta, S0 = (torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+                       for a in x[3:])
+        out = torch.empty((N, H, d), dtype=torch.bfloat16, device=dev)
+        u = torch.empty((N, H, d), dtype=torch.float32, device=dev)
+        sets.append((q, k, v, g, beta, S0, out, u))
+    f = api._lib.tree_attn_gdn_verify
+    argv = [(t[0].data_ptr(), t[1].data_ptr(), t[2].data_ptr(),
+             t[3].data_ptr(), t[4].data_ptr(), t[5].data_ptr(),
+             off_d.data_ptr(), masks.data_ptr(), W, S, N, B, H, d,
+             t[6].data_ptr(), t[7].data_ptr(), stream.cuda_stream)
+            for t in sets]
+    n_warm = 0
+    t_w = time.perf_counter()
+    while n_warm < max(args.warmup, 1) or time.perf_counter() - t_w < \
+            WARM_SECONDS:
+        if f(*argv[n_warm % copies]) != 0:
+            raise RuntimeError("tree_attn_gdn_verify failed")
+        n_warm += 1
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        f(*argv[i % copies])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # the commit of one accepted root path per tree (depth-first to the
+    # deepest node of the tree), back to back on the same stream
+    rng = np.random.default_rng(8)
+    lens = np.zeros(S, np.int32)
+    nodes = np.full((S, B), -1, np.int32)
+    for s in range(S):
+        a = int(offsets[s])
+        j = int(np.argmax(depth[a:a + B]))
+        path = []
+        while j >= 0:
+            path.append(j)
+            j = int(parents[a + j])
+        lens[s] = len(path)
+        nodes[s, :len(path)] = path[::-1]
+    lens_d = torch.from_numpy(lens).to(dev)
+    nodes_d = torch.from_numpy(nodes).to(dev)
+    fc = api._lib.tree_attn_gdn_commit
+    cargv = [(t[1].data_ptr(), t[7].data_ptr(), t[3].data_ptr(),
+              off_d.data_ptr(), lens_d.data_ptr(), nodes_d.data_ptr(), S, B,
+              H, d, t[5].data_ptr(), stream.cuda_stream) for t in sets]
+    for i in range(3):
+        fc(*cargv[i % copies])
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        if fc(*cargv[i % copies]) != 0:
+            raise RuntimeError("tree_attn_gdn_commit failed")
+    e1.record(stream)
+    torch.cuda.synchronize()
+    commit_ms = e0.elapsed_time(e1) / args.steps
+    commit_bytes = S * H * d * d * 4 * 2 + int(lens.sum()) * H * (d * 6 + 4)
+
+    # check one (sequence, head) of the last launch against the oracle
+    import oracle
+    from tree_masked_attention_amd.workloads import bf16_bits_to_f32
+    sets[0][5].copy_(torch.from_numpy(x[5]))  # the commits changed S0
+    f(*argv[0])
+    torch.cuda.synchronize()
+    o_gpu = sets[0][6][:B, 0].float().cpu().numpy()
+    u_gpu = sets[0][7][:B, 0].cpu().numpy()
+    q32, k32, v32 = (bf16_bits_to_f32(a)[:B, :1] for a in x[:3])
+    ro, ru = oracle.gdn_tree_verify(parents[:B], q32, k32, v32, x[3][:B, :1],
+                                    x[4][:B, :1], x[5][0, :1])
+    if not (np.abs(u_gpu - ru[:, 0]).max() <= 2e-4 * (1 + np.abs(ru).max()) and
+            np.abs(o_gpu - ro[:, 0]).max() <= 2 ** -8 * np.abs(ro).max() + 2e-4):
+        raise RuntimeError("GDN verify differs from the oracle")
+
+    sec = ms * 1e-3
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    NT = (B + 31) // 32
+    T1 = NT * (NT + 1) // 2
+    mfma_per_wg = 4 * (NT * 8 * 4 + 6 * (NT * (NT - 1) // 2) + 6 * NT +
+                       6 * T1) + 2 * T1 * 8
+    exec_flops = S * H * mfma_per_wg * 32 * 32 * 16 * 2
+    log(f"[bench] gdn verify {name}: {ms * 1e3:.1f} us per launch "
+        f"({alg_bytes / sec / 1e9:.0f} GB/s algorithmic, "
+        f"{alg_flops / sec / 1e12:.1f} TFLOP/s algorithmic, "
+        f"{exec_flops / sec / 1e12:.1f} TFLOP/s executed on MFMA); "
+        f"commit {commit_ms * 1e3:.1f} us")
+    result = {
+        "metric": "GDN tree-verify tree tokens/s + achieved HBM GB/s",
+        "value": N / sec,
+        "unit": "tree tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "warmup_steps_run": n_warm,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 in, f32 math",
+        "data": "synthetic",
+        "config": {"workload": name, "stage": "gdn", "num_seqs": S,
+                   "tree_nodes_per_seq": B, "heads": H, "d_k": d, "d_v": d,
+                   "tree_rule": "pchain 0.5", "input_copies_rotated": copies},
+        "roofline": {
+            "bound": "hbm" if alg_flops / alg_bytes < ridge else "mfma",
+            "kernel": "gdn_verify_kernel (tree_attn_gdn_verify)",
+            "achieved": alg_bytes / sec / 1e9,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": alg_bytes / sec / 1e9 / HBM_PEAK_GBPS,
+            "traffic": measured_traffic(name, "gdn_verify_kernel"),
+            "alg_bytes_per_launch": alg_bytes,
+            "alg_flops_per_launch": alg_flops,
+            "avg_launch_us": ms * 1e3,
+            "executed_mfma_tflops": exec_flops / sec / 1e12,
+            "executed_mfma_frac": exec_flops / sec / 1e12 /
+                                  MFMA_BF16_PEAK_TFLOPS,
+        },
+        "commit_us": commit_ms * 1e3,
+        "commit_hbm_gbps": commit_bytes / (commit_ms * 1e-3) / 1e9,
+        "commit_path_lens": f"{int(lens.min())}..{int(lens.max())}",
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] CPU baseline (oracle)")
+        q32, k32, v32 = (bf16_bits_to_f32(a[:B]) for a in x[:3])
+        heads, t0 = 0, time.perf_counter()
+        while heads < H:
+            hs = slice(heads, heads + 1)
+            oracle.gdn_tree_verify(parents[:B], q32[:, hs], k32[:, hs],
+                                   v32[:, hs], x[3][:B, hs], x[4][:B, hs],
+                                   x[5][0, hs])
+            heads += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds or el / heads * (heads + 1) > 30:
+                break
+        el = time.perf_counter() - t0
+        result["cpu_baseline"] = {
+            "value": B * heads / H / el, "unit": "tree tokens/s",
+            "cores": 1, "kind": "oracle",
+            "sample": f"tree 0 ({B} nodes), {heads} of {H} heads, "
+                      f"{el:.1f} s"}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+# --------------------------------------------------------------------------
 # GPU timing
 # --------------------------------------------------------------------------
 
@@ -463,6 +675,8 @@ def main():
     if args.copy_calibration:
         return copy_calibration(torch)
 
+    if args.stage == "gdn":
+        return gdn_stage(args, torch, api)
     log(f"[bench] drawing workload {args.workload}")
     wl = standard_workload(args.workload)
     if args.stage == "tree-build":

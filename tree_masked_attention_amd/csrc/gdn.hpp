@@ -57,6 +57,8 @@
 // an MFMA is free, so permuting k in both operands gives the same sum).
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace tree_attn {
@@ -72,8 +74,10 @@ constexpr int kGdnMat = kGdnMaxNodes * kGdnXPitch;
 constexpr int kGdnXhi = 0, kGdnXlo = kGdnMat, kGdnYhi = 2 * kGdnMat,
               kGdnYlo = 3 * kGdnMat;
 constexpr int kGdnLOff = 4 * kGdnMat;       // fp32 diagonal blocks of X
+constexpr int kGdnVOff = 2 * kGdnQOff;      // V rows (256 bytes), phase 1-4
 constexpr int kGdnLdsBytes = kGdnLOff + 4 * 32 * 32 * 4;
-static_assert(2 * kGdnQOff <= kGdnLOff, "K / Q staging must fit");
+static_assert(kGdnVOff + kGdnMaxNodes * 256 <= kGdnLOff,
+              "K / Q / V staging must fit below the fp32 blocks");
 
 struct GdnParams {
   const __bf16* q;              // [N][H][128]
@@ -137,58 +141,131 @@ __device__ __forceinline__ f32x16 gdn_mfma3(bf16x8 ah, bf16x8 al, bf16x8 bh,
   return acc;
 }
 
-__global__ __launch_bounds__(kGdnThreads, 1) void gdn_verify_kernel(
-    GdnParams p) {
-  __shared__ __align__(16) unsigned char lds[kGdnLdsBytes];
-  __shared__ uint64_t mk[kGdnMaxNodes][2];
-  __shared__ float gl[kGdnMaxNodes];   // g
-  __shared__ float Gc[kGdnMaxNodes];   // G (sum of g over the root path)
-  __shared__ float gam[kGdnMaxNodes];  // e^G
-  __shared__ float bl[kGdnMaxNodes];   // beta
+struct GdnSmall {
+  uint64_t mk[kGdnMaxNodes][2];  // ancestor-or-self words of each node
+  float gl[kGdnMaxNodes];        // g
+  float Gc[kGdnMaxNodes];        // G: sum of g over the root path
+  float gam[kGdnMaxNodes];       // e^G
+  float bl[kGdnMaxNodes];        // beta
+};
 
-  const int H = p.H;
-  const int s = blockIdx.x / H, h = blockIdx.x - s * H;
-  const int n0 = p.tree_offsets[s];
-  const int B = p.tree_offsets[s + 1] - n0;
-  // trees beyond the supported size are rejected on the host through
-  // max_nodes; a tree that breaks that bound is skipped, never overrun
-  if (B <= 0 || B > kGdnMaxNodes) return;
-  const int NT = (B + 31) >> 5, Bp = NT * 32;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+typedef __attribute__((address_space(3))) float gdn_lds_f32;
+
+// Highest strict ancestor (the parent) of local node i from its mask row.
+__device__ __forceinline__ int gdn_parent(const GdnSmall& sm, int i) {
+  uint64_t m0 = sm.mk[i][0], m1 = sm.mk[i][1];
+  if (i < 64) {
+    m0 &= ~(1ull << i);
+  } else {
+    m1 &= ~(1ull << (i - 64));
+  }
+  if (m1) return 127 - __builtin_clzll(m1);
+  if (m0) return 63 - __builtin_clzll(m0);
+  return -1;
+}
+
+__device__ __forceinline__ float gdn_bperm(int lane_src, float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_ds_bpermute(lane_src << 2,
+                                          __builtin_bit_cast(int, x)));
+}
+
+__device__ __forceinline__ int gdn_bperm(int lane_src, int x) {
+  return __builtin_amdgcn_ds_bpermute(lane_src << 2, x);
+}
+
+// Stores a 32 x 32 fp32 accumulator tile (lane (col, half), register r:
+// row row0 + 8 (r/4) + 4 half + r%4, column col) straight from registers:
+// each store writes two 32-column row segments.  Rows >= nrows are skipped
+// (no test at all when the tile is whole).  With kBf16 the values are
+// rounded to bf16 first.
+template <bool kBf16>
+__device__ __forceinline__ void gdn_store_tile(const f32x16& c, char* dst,
+                                               size_t ld_bytes, int row0,
+                                               int nrows, int lane) {
   const int col = lane & 31, half = lane >> 5;
-  const unsigned base =
-      (unsigned)(size_t)(__attribute__((address_space(3))) unsigned char*)lds;
+  constexpr int esz = kBf16 ? 2 : 4;
+  char* d = dst + (size_t)(row0 + 4 * half) * ld_bytes + col * esz;
+  auto put = [&](int r) {
+    char* a = d + (size_t)(8 * (r >> 2) + (r & 3)) * ld_bytes;
+    if (kBf16) {
+      *reinterpret_cast<__bf16*>(a) = (__bf16)c[r];
+    } else {
+      *reinterpret_cast<float*>(a) = c[r];
+    }
+  };
+  if (row0 + 32 <= nrows) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) put(r);
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      if (row0 + 8 * (r >> 2) + 4 * half + (r & 3) < nrows) put(r);
+    }
+  }
+}
 
-  // ---- 1. staging
-  for (int x = tid; x < Bp * 16; x += kGdnThreads) {
-    const int i = x >> 4, c = x & 15;
-    u32x4 kv = {0u, 0u, 0u, 0u}, qv = {0u, 0u, 0u, 0u};
-    if (i < B) {
-      const size_t off = ((size_t)(n0 + i) * H + h) * kHeadDim + c * 8;
-      kv = *reinterpret_cast<const u32x4*>(p.k + off);
-      qv = *reinterpret_cast<const u32x4*>(p.q + off);
+// Keeps a value computed where it stands: without it the optimizer sinks
+// pure arithmetic past a barrier to its use and keeps the loaded operands
+// alive across the barrier instead.
+__device__ __forceinline__ void gdn_pin(float& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void gdn_pin(f32x16& x) {
+  asm volatile("" : "+v"(x));
+}
+
+// Row j of T = (I + L)^{-1} (L strictly lower triangular, 32 x 32, its
+// transpose at Lb in fp32) for the lane's row col, by backward
+// substitution t_j = [j == col] - sum_{i > j} t_i L_ij, for j = J .. 0.
+// Row j - 1 of L^T is read while row j is computed, and slot(31 - j) issues
+// matrix-core work that runs beside the row's FMAs.  One instantiation per
+// row keeps every index static; the scheduling barrier between rows keeps
+// the compiler from hoisting all reads of L to the top (and spilling them).
+template <int J, class Slot>
+__device__ __forceinline__ void gdn_t_row(float (&tr)[32], f32x4 (&Lc)[8],
+                                          f32x4 (&Ln)[8], unsigned Lb,
+                                          int col, Slot& slot) {
+  if constexpr (J > 0) {
+#pragma unroll
+    for (int i4 = J / 4; i4 < 8; ++i4) {
+      Ln[i4] = *(const gdn_lds_f32x4*)(size_t)(Lb + (J - 1) * 128 + i4 * 16);
     }
-    *(gdn_lds_u32x4*)(size_t)(base + kGdnKOff + i * kGdnKPitch + c * 16) = kv;
-    *(gdn_lds_u32x4*)(size_t)(base + kGdnQOff + i * kGdnKPitch + c * 16) = qv;
   }
-  if (tid < Bp) {
-    const int i = tid;
-    uint64_t m0 = 0, m1 = 0;
-    float gv = 0.f, bv = 0.f;
-    if (i < B) {
-      const uint64_t* mrow = p.masks + (size_t)(n0 + i) * p.W;
-      m0 = mrow[0];
-      if (B > 64 && p.W > 1) m1 = mrow[1];
-      gv = p.g[(size_t)(n0 + i) * H + h];
-      bv = p.beta[(size_t)(n0 + i) * H + h];
+  slot(std::integral_constant<int, 31 - J>{});
+  // four partial sums (by i mod 4) shorten the dependent FMA chain
+  float a4[4] = {(J == col) ? 1.f : 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i4 = (J + 1) / 4; i4 < 8; ++i4) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (4 * i4 + e > J) a4[e] -= Lc[i4][e] * tr[4 * i4 + e];
     }
-    mk[i][0] = m0;
-    mk[i][1] = m1;
-    gl[i] = gv;
-    bl[i] = bv;
   }
-  // S0 columns 32 w + col, rows 16 ks + 8 half + e: B operands of K S0
-  bf16x8 shi[8], slo[8];
+  tr[J] = (a4[0] + a4[1]) + (a4[2] + a4[3]);
+  gdn_pin(tr[J]);
+#pragma unroll
+  for (int i4 = 0; i4 < 8; ++i4) Lc[i4] = Ln[i4];
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (J > 0) gdn_t_row<J - 1>(tr, Lc, Ln, Lb, col, slot);
+}
+
+// The work of one (sequence, head) whose tree has B nodes, NT = ceil(B/32).
+template <int NT>
+__device__ __forceinline__ void gdn_verify_tree(const GdnParams& p,
+                                                unsigned base, GdnSmall& sm,
+                                                int s, int h, int n0, int B) {
+  constexpr int Bp = NT * 32;
+  constexpr int NX = NT * (NT - 1) / 2;   // off-diagonal X tiles
+  constexpr int T1 = NT * (NT + 1) / 2;   // Y tiles (lower triangle)
+  constexpr int NG = (NX + T1 + 3) / 4;   // Gram tiles per wave, at most
+  constexpr int kJumps = NT == 1 ? 5 : (NT == 2 ? 6 : 7);  // ceil log2 Bp
+  const int H = p.H;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int col = lane & 31, half = lane >> 5;
+
+  // ---- 1. every global load of the tree issued up front: S0 into
+  // registers, K / Q / V rows through registers into LDS
+  float sraw[64];  // S0 rows 16 ks + 8 half + e, column 32 w + col
   {
     const float* st = p.state + ((size_t)s * H + h) * kHeadDim * kHeadDim +
                       32 * w + col;
@@ -196,107 +273,250 @@ __global__ __launch_bounds__(kGdnThreads, 1) void gdn_verify_kernel(
     for (int ks = 0; ks < 8; ++ks) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        __bf16 a, b;
-        gdn_split(st[(size_t)(16 * ks + 8 * half + e) * kHeadDim], a, b);
-        shi[ks][e] = a;
-        slo[ks][e] = b;
+        sraw[8 * ks + e] = st[(size_t)(16 * ks + 8 * half + e) * kHeadDim];
       }
+    }
+  }
+  {
+    u32x4 kreg[Bp / 16], qreg[Bp / 16], vreg[Bp / 16];
+#pragma unroll
+    for (int m = 0; m < Bp / 16; ++m) {
+      const int i = (tid >> 4) + 16 * m;
+      const size_t off =
+          ((size_t)(n0 + min(i, B - 1)) * H + h) * kHeadDim + (tid & 15) * 8;
+      kreg[m] = *reinterpret_cast<const u32x4*>(p.k + off);
+      qreg[m] = *reinterpret_cast<const u32x4*>(p.q + off);
+      vreg[m] = *reinterpret_cast<const u32x4*>(p.v + off);
+    }
+    if (tid < Bp) {
+      const int i = tid;
+      uint64_t m0 = 0, m1 = 0;
+      float gv = 0.f, bv = 0.f;
+      if (i < B) {
+        const uint64_t* mrow = p.masks + (size_t)(n0 + i) * p.W;
+        m0 = mrow[0];
+        if (B > 64 && p.W > 1) m1 = mrow[1];
+        gv = p.g[(size_t)(n0 + i) * H + h];
+        bv = p.beta[(size_t)(n0 + i) * H + h];
+      }
+      sm.mk[i][0] = m0;
+      sm.mk[i][1] = m1;
+      sm.gl[i] = gv;
+      sm.bl[i] = bv;
+    }
+#pragma unroll
+    for (int m = 0; m < Bp / 16; ++m) {
+      const int i = (tid >> 4) + 16 * m;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      const unsigned o = i * kGdnKPitch + (tid & 15) * 16;
+      *(gdn_lds_u32x4*)(size_t)(base + kGdnKOff + o) = i < B ? kreg[m] : z;
+      *(gdn_lds_u32x4*)(size_t)(base + kGdnQOff + o) = i < B ? qreg[m] : z;
+      // rows past the tree keep finite values (clamped), beta = 0 there
+      *(gdn_lds_u32x4*)(size_t)(base + kGdnVOff + i * 256 + (tid & 15) * 16) =
+          vreg[m];
     }
   }
   __syncthreads();
 
-  // ---- 2. G_i over the ancestor-or-self bits, in increasing node order
-  if (tid < Bp) {
-    float G = 0.f;
-    if (tid < B) {
+  // ---- 2. G by pointer jumping over parents (wave 0; lane l holds nodes
+  // l and l + 64): G_i += G_{P_i}, P_i <- P_{P_i}, until every P is -1
+  if (w == 0) {
+    int P0 = lane < Bp ? gdn_parent(sm, lane) : -1;
+    int P1 = lane + 64 < Bp ? gdn_parent(sm, lane + 64) : -1;
+    float G0 = lane < Bp ? sm.gl[lane] : 0.f;
+    float G1 = lane + 64 < Bp ? sm.gl[lane + 64] : 0.f;
 #pragma unroll
-      for (int wd = 0; wd < 2; ++wd) {
-        uint64_t m = mk[tid][wd];
-        while (m) {
-          G += gl[wd * 64 + __builtin_ctzll(m)];
-          m &= m - 1;
-        }
+    for (int it = 0; it < kJumps; ++it) {
+      const int a0 = P0 & 63, a1 = P1 & 63;
+      const float g00 = gdn_bperm(a0, G0), g01 = gdn_bperm(a0, G1);
+      const int p00 = gdn_bperm(a0, P0), p01 = gdn_bperm(a0, P1);
+      const float g10 = gdn_bperm(a1, G0), g11 = gdn_bperm(a1, G1);
+      const int p10 = gdn_bperm(a1, P0), p11 = gdn_bperm(a1, P1);
+      if (P0 >= 0) {
+        G0 += P0 < 64 ? g00 : g01;
+        P0 = P0 < 64 ? p00 : p01;
+      }
+      if (P1 >= 0) {
+        G1 += P1 < 64 ? g10 : g11;
+        P1 = P1 < 64 ? p10 : p11;
       }
     }
-    Gc[tid] = G;
-    gam[tid] = fast_exp2(G * kLog2e);
+    if (lane < Bp) {
+      sm.Gc[lane] = G0;
+      sm.gam[lane] = fast_exp2(G0 * kLog2e);
+    }
+    if (lane + 64 < Bp) {
+      sm.Gc[lane + 64] = G1;
+      sm.gam[lane + 64] = fast_exp2(G1 * kLog2e);
+    }
   }
   __syncthreads();
 
-  // ---- 3a. K S0 and Q S0 for this wave's 32 columns
-  f32x16 ks[4], qs[4];
+  // Gram tile (I, J) of X (isx) or Y, masked and decayed.  Computed
+  // transposed (K_J times the row block's K or Q), so lane (col, half)
+  // holds row I*32 + col, columns J*32 + 8 (r/4) + 4 half + r%4.
+  auto gram = [&](bool isx, int I, int J) {
+    const unsigned src = base + (isx ? kGdnKOff : kGdnQOff);
+    f32x16 acc = f32x16{};
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+    for (int kk = 0; kk < 8; ++kk) {
+      const unsigned off = (2 * kk + half) * 16;
+      const bf16x8 a =
+          gdn_read16(base + kGdnKOff + (J * 32 + col) * kGdnKPitch + off);
+      const bf16x8 b = gdn_read16(src + (I * 32 + col) * kGdnKPitch + off);
+      acc = mfma32x32x16(a, b, acc);
+    }
+    const int i = I * 32 + col;
+    const float Gi = sm.Gc[i], bl_i = sm.bl[i];
+    const float bi = isx ? bl_i : 1.f;
+    const uint32_t mw = (uint32_t)(sm.mk[i][J >> 1] >> ((J & 1) * 32));
+    // G of the 16 columns, read unconditionally: a read under the ancestor
+    // test would become a branch and a wait per element
+    f32x4 Gj[4];
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm) {
+      Gj[mm] = *reinterpret_cast<const f32x4*>(&sm.Gc[J * 32 + 8 * mm + 4 * half]);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int jl = 8 * (r >> 2) + 4 * half + (r & 3);
+      const bool anc = ((mw >> jl) & 1u) && (!isx || J * 32 + jl != i);
+      // e^{G_i - G_j} for an ancestor, e^{-inf} = 0 otherwise
+      const float d = anc ? (Gi - Gj[r >> 2][r & 3]) * kLog2e : -__builtin_inff();
+      acc[r] = bi * fast_exp2(d) * acc[r];
+    }
+    return acc;
+  };
+
+  // ---- 3. diagonal X block w in fp32, transposed (L^T), to LDS
+  if (w < NT) {
+    const f32x16 d = gram(true, w, w);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int jl = 8 * (r >> 2) + 4 * half + (r & 3);
+      *(gdn_lds_f32*)(size_t)(base + kGdnLOff + w * 4096 + jl * 128 +
+                              col * 4) = d[r];
+    }
+  }
+  __syncthreads();
+
+  // ---- 4. K S0 and Q S0 on the matrix cores, interleaved with (VALU) row
+  // col of T_w = (I + L_w)^{-1}: 32 slots of 4 products, one per row of T
+  f32x16 ks[NT], qs[NT];
+  bf16x8 shi[8], slo[8];
+#pragma unroll
+  for (int k8 = 0; k8 < 8; ++k8) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      __bf16 a, b;
+      gdn_split(sraw[8 * k8 + e], a, b);
+      shi[k8][e] = a;
+      slo[k8][e] = b;
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
     ks[t] = f32x16{};
     qs[t] = f32x16{};
-    if (t < NT) {
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const unsigned ra = (t * 32 + col) * kGdnKPitch + (2 * kk + half) * 16;
-        const bf16x8 ak = gdn_read16(base + kGdnKOff + ra);
-        const bf16x8 aq = gdn_read16(base + kGdnQOff + ra);
-        ks[t] = mfma32x32x16(ak, shi[kk], ks[t]);
-        ks[t] = mfma32x32x16(ak, slo[kk], ks[t]);
-        qs[t] = mfma32x32x16(aq, shi[kk], qs[t]);
-        qs[t] = mfma32x32x16(aq, slo[kk], qs[t]);
-      }
+  }
+  // slot sl issues the four products of (kk, t) = (sl / NT, sl % NT) with
+  // A operands read one slot earlier, and reads those of the next slot
+  bf16x8 ak, aq;
+  auto read_a = [&](int sl) {
+    const int kk = sl / NT, t = sl % NT;
+    const unsigned ra = (t * 32 + col) * kGdnKPitch + (2 * kk + half) * 16;
+    ak = gdn_read16(base + kGdnKOff + ra);
+    aq = gdn_read16(base + kGdnQOff + ra);
+  };
+  read_a(0);
+  auto slot = [&](auto sc) {
+    constexpr int sl = decltype(sc)::value;
+    if constexpr (sl < 8 * NT) {
+      constexpr int kk = sl / NT, t = sl % NT;
+      const bf16x8 a_k = ak, a_q = aq;
+      if constexpr (sl + 1 < 8 * NT) read_a(sl + 1);
+      ks[t] = mfma32x32x16(a_k, shi[kk], ks[t]);
+      qs[t] = mfma32x32x16(a_q, shi[kk], qs[t]);
+      ks[t] = mfma32x32x16(a_k, slo[kk], ks[t]);
+      qs[t] = mfma32x32x16(a_q, slo[kk], qs[t]);
     }
+  };
+  __builtin_amdgcn_sched_barrier(0);
+  float tr[32];
+  {
+    // waves >= NT run it on a block no tree uses and discard the result
+    f32x4 Lc[8], Ln[8];
+#pragma unroll
+    for (int i4 = 0; i4 < 8; ++i4) {
+      Lc[i4] = f32x4{};
+      Ln[i4] = f32x4{};
+    }
+    gdn_t_row<31>(tr, Lc, Ln, base + kGdnLOff + w * 4096, col, slot);
+  }
+  // R = beta (V - gamma K S0), in place of K S0
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = t * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+      const float vv = (float)*(const gdn_lds_bf16*)(size_t)(
+          base + kGdnVOff + row * 256 + (32 * w + col) * 2);
+      ks[t][r] = sm.bl[row] * (vv - sm.gam[row] * ks[t][r]);
+    }
+    gdn_pin(ks[t]);
   }
 
-  // ---- 3b. Gram tiles: tile n < T1 is X tile (I, J) of the lower
-  // triangle in row order, tile T1 + n the Y tile; wave w takes w, w+4, ..
-  const int T1 = NT * (NT + 1) / 2;
-  f32x16 gt[5];
-  int tI[5], tJ[5];
+  // ---- 5. the other Gram tiles: off-diagonal X tiles in row order, then
+  // the Y tiles of the lower triangle; wave w takes w, w + 4, ...
+  // Tiles are decoded first (scalar loops) so that the products of all of
+  // a wave's tiles form one block the scheduler can interleave; a wave with
+  // fewer tiles repeats the last one and drops it.
+  f32x16 gt[NG];
+  int tI[NG], tJ[NG];
+  bool tX[NG];
 #pragma unroll
-  for (int m = 0; m < 5; ++m) {
-    const int n = w + 4 * m;
-    gt[m] = f32x16{};
-    tI[m] = -1;
-    tJ[m] = 0;
-    if (n < 2 * T1) {
-      const bool isx = n < T1;
-      int idx = isx ? n : n - T1, I = 0;
+  for (int m = 0; m < NG; ++m) {
+    const int n0t = w + 4 * m;
+    const int n = min(n0t, NX + T1 - 1);
+    const bool isx = n < NX;
+    int I, J;
+    if (isx) {
+      int idx = n;
+      I = 1;
+      while (idx >= I) {
+        idx -= I;
+        ++I;
+      }
+      J = idx;
+    } else {
+      int idx = n - NX;
+      I = 0;
       while (idx > I) {
         idx -= I + 1;
         ++I;
       }
-      const int J = idx;
-      tI[m] = I;
-      tJ[m] = J;
-      const unsigned src = base + (isx ? kGdnKOff : kGdnQOff);
-      f32x16 acc = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const unsigned off = (2 * kk + half) * 16;
-        const bf16x8 a =
-            gdn_read16(base + kGdnKOff + (J * 32 + col) * kGdnKPitch + off);
-        const bf16x8 b = gdn_read16(src + (I * 32 + col) * kGdnKPitch + off);
-        acc = mfma32x32x16(a, b, acc);
-      }
-      // lane: row i of X / Y, columns J*32 + 8 (r/4) + 4 half + r%4
-      const int i = I * 32 + col;
-      const float Gi = Gc[i], bi = bl[i];
-      const uint32_t mw = (uint32_t)(mk[i][J >> 1] >> ((J & 1) * 32));
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int jl = 8 * (r >> 2) + 4 * half + (r & 3);
-        const int j = J * 32 + jl;
-        const bool anc = ((mw >> jl) & 1u) && (!isx || j != i);
-        const float e = fast_exp2((Gi - Gc[j]) * kLog2e);
-        gt[m][r] = anc ? (isx ? bi * e * acc[r] : e * acc[r]) : 0.f;
-      }
-      if (!isx) tI[m] += 8;  // marks a Y tile (I + 8)
+      J = idx;
     }
+    tX[m] = isx;
+    tI[m] = n0t < NX + T1 ? I : -1;
+    tJ[m] = J;
+    gt[m] = f32x16{};
   }
-  __syncthreads();  // K / Q rows consumed
-
-  // ---- 4. X (negated) / Y split into LDS; diagonal X blocks in fp32
 #pragma unroll
-  for (int m = 0; m < 5; ++m) {
+  for (int m = 0; m < NG; ++m) {
+    gt[m] = gram(tX[m], max(tI[m], 0), tJ[m]);
+  }
+#pragma unroll
+  for (int m = 0; m < NG; ++m) gdn_pin(gt[m]);
+  __syncthreads();  // K / Q / V rows and the fp32 blocks consumed
+
+  // ---- 6. X (negated) / Y split into LDS over the staged rows; T_w in
+  // the diagonal block w of the X arrays
+#pragma unroll
+  for (int m = 0; m < NG; ++m) {
     if (tI[m] >= 0) {
-      const bool isx = tI[m] < 8;
-      const int I = isx ? tI[m] : tI[m] - 8, J = tJ[m];
+      const bool isx = tX[m];
+      const int I = tI[m], J = tJ[m];
       const int row = I * 32 + col;
       const unsigned hi_arr = base + (isx ? kGdnXhi : kGdnYhi);
       const unsigned lo_arr = base + (isx ? kGdnXlo : kGdnYlo);
@@ -311,125 +531,117 @@ __global__ __launch_bounds__(kGdnThreads, 1) void gdn_verify_kernel(
           hv[e] = a;
           lv[e] = b;
         }
-        const unsigned off = row * kGdnXPitch + (J * 32 + 8 * mm + 4 * half) * 2;
+        const unsigned off =
+            row * kGdnXPitch + (J * 32 + 8 * mm + 4 * half) * 2;
         *(gdn_lds_u32x2*)(size_t)(hi_arr + off) = __builtin_bit_cast(u32x2, hv);
         *(gdn_lds_u32x2*)(size_t)(lo_arr + off) = __builtin_bit_cast(u32x2, lv);
-        if (isx && I == J) {
-          const f32x4 xv = {gt[m][4 * mm], gt[m][4 * mm + 1],
-                            gt[m][4 * mm + 2], gt[m][4 * mm + 3]};
-          *(gdn_lds_f32x4*)(size_t)(base + kGdnLOff + J * 4096 + col * 128 +
-                                    (8 * mm + 4 * half) * 4) = xv;
-        }
       }
     }
   }
-  __syncthreads();
-
-  // ---- 5. T_J = (I + X_JJ)^{-1}: lane c computes column c
-  if (w < NT) {
-    const int J = w, c = col;
-    const unsigned Lb = base + kGdnLOff + J * 4096;
-    float t[32];
+  if (w < NT && half == 0) {
+    const unsigned off = (w * 32 + col) * kGdnXPitch + w * 32 * 2;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      float acc = (i == c) ? 1.f : 0.f;
+    for (int c4 = 0; c4 < 8; ++c4) {
+      bf16x4 hv, lv;
 #pragma unroll
-      for (int j4 = 0; j4 < (i + 3) / 4; ++j4) {
-        const f32x4 L = *(const gdn_lds_f32x4*)(size_t)(Lb + i * 128 + j4 * 16);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (4 * j4 + e < i) acc -= L[e] * t[4 * j4 + e];
-        }
-      }
-      t[i] = acc;
-    }
-    if (half == 0) {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
+      for (int e = 0; e < 4; ++e) {
         __bf16 a, b;
-        gdn_split(t[i], a, b);
-        const unsigned off = (J * 32 + i) * kGdnXPitch + (J * 32 + c) * 2;
-        *(gdn_lds_bf16*)(size_t)(base + kGdnXhi + off) = a;
-        *(gdn_lds_bf16*)(size_t)(base + kGdnXlo + off) = b;
+        gdn_split(tr[4 * c4 + e], a, b);
+        hv[e] = a;
+        lv[e] = b;
       }
+      *(gdn_lds_u32x2*)(size_t)(base + kGdnXhi + off + c4 * 8) =
+          __builtin_bit_cast(u32x2, hv);
+      *(gdn_lds_u32x2*)(size_t)(base + kGdnXlo + off + c4 * 8) =
+          __builtin_bit_cast(u32x2, lv);
     }
   }
   __syncthreads();
 
-  // ---- 6. R = beta (V - gamma K S0) in place of K S0
-  const size_t colg = (size_t)h * kHeadDim + 32 * w + col;
+  // ---- 7. blocked forward substitution, right-looking: U_I = T_I R_I,
+  // then R_J -= X_JI U_I for every later block J; U is stored as soon as
+  // it is known
+  const size_t row_elems = (size_t)H * kHeadDim;
+  char* out_base = reinterpret_cast<char*>(p.out + (size_t)n0 * row_elems +
+                                           (size_t)h * kHeadDim + 32 * w);
+  char* u_base = reinterpret_cast<char*>(p.u + (size_t)n0 * row_elems +
+                                         (size_t)h * kHeadDim + 32 * w);
+  bf16x8 uh[NT][2], ul[NT][2];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    if (t < NT) {
+  for (int I = 0; I < NT; ++I) {
+    const int row = I * 32 + col;
+    bf16x8 rh0, rl0, rh1, rl1;
+    gdn_split_tile<0>(ks[I], rh0, rl0);
+    gdn_split_tile<1>(ks[I], rh1, rl1);
+    // the two k-steps of each product accumulate separately (shorter
+    // dependent chains on the critical path), then add
+    f32x16 ua = gdn_mfma3(gdn_read_perm(base + kGdnXhi, row, I * 32, half),
+                          gdn_read_perm(base + kGdnXlo, row, I * 32, half),
+                          rh0, rl0, f32x16{});
+    const f32x16 ub = gdn_mfma3(
+        gdn_read_perm(base + kGdnXhi, row, I * 32 + 16, half),
+        gdn_read_perm(base + kGdnXlo, row, I * 32 + 16, half), rh1, rl1,
+        f32x16{});
+    ua += ub;
+    gdn_split_tile<0>(ua, uh[I][0], ul[I][0]);
+    gdn_split_tile<1>(ua, uh[I][1], ul[I][1]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = t * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        float vv = 0.f;
-        if (row < B) vv = (float)p.v[(size_t)(n0 + row) * H * kHeadDim + colg];
-        ks[t][r] = bl[row] * (vv - gam[row] * ks[t][r]);
-      }
+    for (int J = I + 1; J < NT; ++J) {
+      const int rj = J * 32 + col;
+      ks[J] = gdn_mfma3(gdn_read_perm(base + kGdnXhi, rj, I * 32, half),
+                        gdn_read_perm(base + kGdnXlo, rj, I * 32, half),
+                        uh[I][0], ul[I][0], ks[J]);
+      const f32x16 pj = gdn_mfma3(
+          gdn_read_perm(base + kGdnXhi, rj, I * 32 + 16, half),
+          gdn_read_perm(base + kGdnXlo, rj, I * 32 + 16, half), uh[I][1],
+          ul[I][1], f32x16{});
+      ks[J] += pj;
     }
+    gdn_store_tile<false>(ua, u_base, row_elems * 4, I * 32, B, lane);
   }
 
-  // blocked forward substitution, one 32-row block at a time
-  f32x16 uu[4];
-  bf16x8 uh[4][2], ul[4][2];
+  // ---- 8. O_J = gamma (Q S0)_J + sum_{I <= J} Y_JI U_I
 #pragma unroll
-  for (int J = 0; J < 4; ++J) {
-    uu[J] = f32x16{};
-    if (J < NT) {
-      f32x16 acc = ks[J];
-      const int row = J * 32 + col;
+  for (int J = 0; J < NT; ++J) {
+    const int row = J * 32 + col;
+    f32x16 o = f32x16{}, o1 = f32x16{};
 #pragma unroll
-      for (int I = 0; I < J; ++I) {
-        acc = gdn_mfma3(gdn_read_perm(base + kGdnXhi, row, I * 32, half),
-                        gdn_read_perm(base + kGdnXlo, row, I * 32, half),
-                        uh[I][0], ul[I][0], acc);
-        acc = gdn_mfma3(gdn_read_perm(base + kGdnXhi, row, I * 32 + 16, half),
-                        gdn_read_perm(base + kGdnXlo, row, I * 32 + 16, half),
-                        uh[I][1], ul[I][1], acc);
-      }
-      bf16x8 rh0, rl0, rh1, rl1;
-      gdn_split_tile<0>(acc, rh0, rl0);
-      gdn_split_tile<1>(acc, rh1, rl1);
-      f32x16 uj = f32x16{};
-      uj = gdn_mfma3(gdn_read_perm(base + kGdnXhi, row, J * 32, half),
-                     gdn_read_perm(base + kGdnXlo, row, J * 32, half), rh0,
-                     rl0, uj);
-      uj = gdn_mfma3(gdn_read_perm(base + kGdnXhi, row, J * 32 + 16, half),
-                     gdn_read_perm(base + kGdnXlo, row, J * 32 + 16, half),
-                     rh1, rl1, uj);
-      uu[J] = uj;
-      gdn_split_tile<0>(uj, uh[J][0], ul[J][0]);
-      gdn_split_tile<1>(uj, uh[J][1], ul[J][1]);
+    for (int I = 0; I <= J; ++I) {
+      o = gdn_mfma3(gdn_read_perm(base + kGdnYhi, row, I * 32, half),
+                    gdn_read_perm(base + kGdnYlo, row, I * 32, half),
+                    uh[I][0], ul[I][0], o);
+      o1 = gdn_mfma3(gdn_read_perm(base + kGdnYhi, row, I * 32 + 16, half),
+                     gdn_read_perm(base + kGdnYlo, row, I * 32 + 16, half),
+                     uh[I][1], ul[I][1], o1);
     }
+    o += o1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int rr = J * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+      o[r] += sm.gam[rr] * qs[J][r];
+    }
+    gdn_store_tile<true>(o, out_base, row_elems * 2, J * 32, B, lane);
   }
+}
 
-  // output stage
-#pragma unroll
-  for (int J = 0; J < 4; ++J) {
-    if (J < NT) {
-      const int row = J * 32 + col;
-      f32x16 acc = f32x16{};
-#pragma unroll
-      for (int I = 0; I <= J; ++I) {
-        acc = gdn_mfma3(gdn_read_perm(base + kGdnYhi, row, I * 32, half),
-                        gdn_read_perm(base + kGdnYlo, row, I * 32, half),
-                        uh[I][0], ul[I][0], acc);
-        acc = gdn_mfma3(gdn_read_perm(base + kGdnYhi, row, I * 32 + 16, half),
-                        gdn_read_perm(base + kGdnYlo, row, I * 32 + 16, half),
-                        uh[I][1], ul[I][1], acc);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rr = J * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (rr < B) {
-          const size_t o = (size_t)(n0 + rr) * H * kHeadDim + colg;
-          p.out[o] = (__bf16)(gam[rr] * qs[J][r] + acc[r]);
-          p.u[o] = uu[J][r];
-        }
-      }
-    }
+__global__ __launch_bounds__(kGdnThreads, 1) void gdn_verify_kernel(
+    GdnParams p) {
+  __shared__ __align__(16) unsigned char lds[kGdnLdsBytes];
+  __shared__ __align__(16) GdnSmall sm;
+  const int H = p.H;
+  const int s = blockIdx.x / H, h = blockIdx.x - s * H;
+  const int n0 = p.tree_offsets[s];
+  const int B = p.tree_offsets[s + 1] - n0;
+  // trees beyond the supported size are rejected on the host through
+  // max_nodes; a tree that breaks that bound is skipped, never overrun
+  if (B <= 0 || B > kGdnMaxNodes) return;
+  const unsigned base =
+      (unsigned)(size_t)(__attribute__((address_space(3))) unsigned char*)lds;
+  switch ((B + 31) >> 5) {
+    case 1: gdn_verify_tree<1>(p, base, sm, s, h, n0, B); break;
+    case 2: gdn_verify_tree<2>(p, base, sm, s, h, n0, B); break;
+    case 3: gdn_verify_tree<3>(p, base, sm, s, h, n0, B); break;
+    default: gdn_verify_tree<4>(p, base, sm, s, h, n0, B); break;
   }
 }
 
