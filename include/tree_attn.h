@@ -418,7 +418,7 @@ int tree_attn_accept_commit(
  *   masks, mask_words   as written by tree_attn_build_mask
  *   max_nodes     host upper bound on every B_s,
  *                 <= TREE_ATTN_GDN_MAX_NODES (128)
- *   num_heads     >= 1 (q, k, v, g and beta all carry num_heads heads)
+ *   num_heads     1 .. 16384 (q, k, v, g and beta all carry num_heads heads)
  *   head_dim      d_k = d_v; must be 128
  *   out           dev bf16 [total_nodes][num_heads][head_dim] (output)
  *   u             dev fp32 [total_nodes][num_heads][head_dim] (output)
@@ -432,7 +432,7 @@ int tree_attn_accept_commit(
  *
  * Host-side errors: ERR_SHAPE (negative sizes, num_heads < 1, mask_words *
  * 64 < max_nodes), ERR_UNSUPPORTED (head_dim != 128, max_nodes > 128,
- * num_seqs * num_heads > 2^31 - 1), ERR_NULL, ERR_HIP.
+ * num_heads > 16384, num_seqs * num_heads > 2^31 - 1), ERR_NULL, ERR_HIP.
  */
 int tree_attn_gdn_verify(const void* q, const void* k, const void* v,
                          const float* g, const float* beta,

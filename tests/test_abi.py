@@ -303,6 +303,7 @@ def _gdn(**over):
     (dict(W=1, max_b=65), api.ERR_SHAPE),
     (dict(d=64), api.ERR_UNSUPPORTED),
     (dict(max_b=129, W=3), api.ERR_UNSUPPORTED),
+    (dict(H=16385), api.ERR_UNSUPPORTED),
     (dict(S=1 << 20, H=1 << 12), api.ERR_UNSUPPORTED),
     (dict(q=None), api.ERR_NULL),
     (dict(beta=None), api.ERR_NULL),

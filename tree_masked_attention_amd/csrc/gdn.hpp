@@ -64,6 +64,7 @@
 namespace tree_attn {
 
 constexpr int kGdnMaxNodes = 128;
+constexpr int kGdnMaxHeads = 16384;  // keeps a tree's u rows below 2^31 bytes
 constexpr int kGdnThreads = 256;
 constexpr int kGdnKPitch = 272;  // bytes per staged K / Q row (256 + 16)
 constexpr int kGdnXPitch = 264;  // bytes per split X / Y row (256 + 8)
@@ -113,9 +114,17 @@ __device__ __forceinline__ bf16x8 gdn_read_perm(unsigned arr, int row, int cb,
   return __builtin_bit_cast(bf16x8, r);
 }
 
-__device__ __forceinline__ void gdn_split(float x, __bf16& hi, __bf16& lo) {
-  hi = (__bf16)x;
-  lo = (__bf16)(x - (float)hi);
+// Two values split at once (one packed conversion per part): hi and lo
+// hold the bf16 pairs (x0 in the low half).
+__device__ __forceinline__ void gdn_split2(float x0, float x1, uint32_t& hi,
+                                           uint32_t& lo) {
+  const bf16x2 h = {(__bf16)x0, (__bf16)x1};
+  const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+  const float h0 = __builtin_bit_cast(float, hb << 16);
+  const float h1 = __builtin_bit_cast(float, hb & 0xffff0000u);
+  const bf16x2 l = {(__bf16)(x0 - h0), (__bf16)(x1 - h1)};
+  hi = hb;
+  lo = __builtin_bit_cast(uint32_t, l);
 }
 
 // B operand (k-step s2 of a 32-row product) from an accumulator tile:
@@ -123,13 +132,16 @@ __device__ __forceinline__ void gdn_split(float x, __bf16& hi, __bf16& lo) {
 template <int S2>
 __device__ __forceinline__ void gdn_split_tile(const f32x16& c, bf16x8& hi,
                                                bf16x8& lo) {
+  u32x4 h, l;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    __bf16 a, b;
-    gdn_split(c[8 * S2 + e], a, b);
-    hi[e] = a;
-    lo[e] = b;
+  for (int e = 0; e < 4; ++e) {
+    uint32_t a, b;
+    gdn_split2(c[8 * S2 + 2 * e], c[8 * S2 + 2 * e + 1], a, b);
+    h[e] = a;
+    l[e] = b;
   }
+  hi = __builtin_bit_cast(bf16x8, h);
+  lo = __builtin_bit_cast(bf16x8, l);
 }
 
 // acc += A * B with both operands split (three bf16 products).
@@ -144,7 +156,7 @@ __device__ __forceinline__ f32x16 gdn_mfma3(bf16x8 ah, bf16x8 al, bf16x8 bh,
 struct GdnSmall {
   uint64_t mk[kGdnMaxNodes][2];  // ancestor-or-self words of each node
   float gl[kGdnMaxNodes];        // g
-  float Gc[kGdnMaxNodes];        // G: sum of g over the root path
+  float Gc[kGdnMaxNodes];        // G log2(e): G the sum of g over the root path
   float gam[kGdnMaxNodes];       // e^G
   float bl[kGdnMaxNodes];        // beta
 };
@@ -174,33 +186,40 @@ __device__ __forceinline__ int gdn_bperm(int lane_src, int x) {
   return __builtin_amdgcn_ds_bpermute(lane_src << 2, x);
 }
 
+// Raw buffer resource over `bytes` bytes from p: loads past the end read 0,
+// stores past the end are dropped by the hardware range check.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t gdn_rsrc(void* p,
+                                                          uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)bytes,
+                                           0x00020000);
+}
+
 // Stores a 32 x 32 fp32 accumulator tile (lane (col, half), register r:
-// row row0 + 8 (r/4) + 4 half + r%4, column col) straight from registers:
-// each store writes two 32-column row segments.  Rows >= nrows are skipped
-// (no test at all when the tile is whole).  With kBf16 the values are
-// rounded to bf16 first.
+// row row0 + 8 (r/4) + 4 half + r%4, column col) straight from registers
+// through a buffer resource whose range ends at the tree's last row, so
+// rows past the tree are dropped without a test.  Each store writes two
+// 32-column row segments.  With kBf16 the values are rounded to bf16.
 template <bool kBf16>
-__device__ __forceinline__ void gdn_store_tile(const f32x16& c, char* dst,
-                                               size_t ld_bytes, int row0,
-                                               int nrows, int lane) {
+__device__ __forceinline__ void gdn_store_tile(const f32x16& c,
+                                               __amdgpu_buffer_rsrc_t rs,
+                                               uint32_t ld_bytes, int row0,
+                                               int lane) {
   const int col = lane & 31, half = lane >> 5;
   constexpr int esz = kBf16 ? 2 : 4;
-  char* d = dst + (size_t)(row0 + 4 * half) * ld_bytes + col * esz;
-  auto put = [&](int r) {
-    char* a = d + (size_t)(8 * (r >> 2) + (r & 3)) * ld_bytes;
+  const uint32_t lo = 4 * half * ld_bytes + col * esz;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const uint32_t off = lo + (uint32_t)(row0 + 8 * (r >> 2) + (r & 3)) * ld_bytes;
+    // through a scalar: a bit cast of the vector element itself reads
+    // element 0 (seen with this compiler)
+    const float x = c[r];
     if (kBf16) {
-      *reinterpret_cast<__bf16*>(a) = (__bf16)c[r];
+      const __bf16 y = (__bf16)x;
+      __builtin_amdgcn_raw_buffer_store_b16(
+          __builtin_bit_cast(unsigned short, y), rs, off, 0, 0);
     } else {
-      *reinterpret_cast<float*>(a) = c[r];
-    }
-  };
-  if (row0 + 32 <= nrows) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) put(r);
-  } else {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      if (row0 + 8 * (r >> 2) + 4 * half + (r & 3) < nrows) put(r);
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x),
+                                            rs, off, 0, 0);
     }
   }
 }
@@ -342,11 +361,11 @@ __device__ __forceinline__ void gdn_verify_tree(const GdnParams& p,
       }
     }
     if (lane < Bp) {
-      sm.Gc[lane] = G0;
+      sm.Gc[lane] = G0 * kLog2e;
       sm.gam[lane] = fast_exp2(G0 * kLog2e);
     }
     if (lane + 64 < Bp) {
-      sm.Gc[lane + 64] = G1;
+      sm.Gc[lane + 64] = G1 * kLog2e;
       sm.gam[lane + 64] = fast_exp2(G1 * kLog2e);
     }
   }
@@ -355,7 +374,10 @@ __device__ __forceinline__ void gdn_verify_tree(const GdnParams& p,
   // Gram tile (I, J) of X (isx) or Y, masked and decayed.  Computed
   // transposed (K_J times the row block's K or Q), so lane (col, half)
   // holds row I*32 + col, columns J*32 + 8 (r/4) + 4 half + r%4.
-  auto gram = [&](bool isx, int I, int J) {
+  // sgn: sign applied to X (the solve reads -X); kDiag: a diagonal X tile,
+  // whose own diagonal (j == i) is not an ancestor relation
+  auto gram = [&](auto diag_c, bool isx, float sgn, int I, int J) {
+    constexpr bool kDiag = decltype(diag_c)::value;
     const unsigned src = base + (isx ? kGdnKOff : kGdnQOff);
     f32x16 acc = f32x16{};
 #pragma unroll
@@ -368,8 +390,10 @@ __device__ __forceinline__ void gdn_verify_tree(const GdnParams& p,
     }
     const int i = I * 32 + col;
     const float Gi = sm.Gc[i], bl_i = sm.bl[i];
-    const float bi = isx ? bl_i : 1.f;
-    const uint32_t mw = (uint32_t)(sm.mk[i][J >> 1] >> ((J & 1) * 32));
+    const float bi = isx ? sgn * bl_i : 1.f;
+    // this lane's 16 columns are bits 8 (r/4) + r%4 of mwh
+    const uint32_t mwh =
+        (uint32_t)(sm.mk[i][J >> 1] >> ((J & 1) * 32)) >> (4 * half);
     // G of the 16 columns, read unconditionally: a read under the ancestor
     // test would become a branch and a wait per element
     f32x4 Gj[4];
@@ -379,18 +403,19 @@ __device__ __forceinline__ void gdn_verify_tree(const GdnParams& p,
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int jl = 8 * (r >> 2) + 4 * half + (r & 3);
-      const bool anc = ((mw >> jl) & 1u) && (!isx || J * 32 + jl != i);
-      // e^{G_i - G_j} for an ancestor, e^{-inf} = 0 otherwise
-      const float d = anc ? (Gi - Gj[r >> 2][r & 3]) * kLog2e : -__builtin_inff();
-      acc[r] = bi * fast_exp2(d) * acc[r];
+      bool anc = (mwh >> (8 * (r >> 2) + (r & 3))) & 1u;
+      if constexpr (kDiag) anc = anc && (8 * (r >> 2) + 4 * half + (r & 3) != col);
+      // e^{G_i - G_j} for an ancestor, 2^{-inf} = 0 otherwise
+      const float d = anc ? Gi - Gj[r >> 2][r & 3] : -__builtin_inff();
+      acc[r] = fast_exp2(d) * acc[r];
     }
+    if (isx) acc *= bi;
     return acc;
   };
 
   // ---- 3. diagonal X block w in fp32, transposed (L^T), to LDS
   if (w < NT) {
-    const f32x16 d = gram(true, w, w);
+    const f32x16 d = gram(std::true_type{}, true, 1.f, w, w);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int jl = 8 * (r >> 2) + 4 * half + (r & 3);
@@ -406,13 +431,16 @@ __device__ __forceinline__ void gdn_verify_tree(const GdnParams& p,
   bf16x8 shi[8], slo[8];
 #pragma unroll
   for (int k8 = 0; k8 < 8; ++k8) {
+    u32x4 h, l;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      __bf16 a, b;
-      gdn_split(sraw[8 * k8 + e], a, b);
-      shi[k8][e] = a;
-      slo[k8][e] = b;
+    for (int e = 0; e < 4; ++e) {
+      uint32_t a, b;
+      gdn_split2(sraw[8 * k8 + 2 * e], sraw[8 * k8 + 2 * e + 1], a, b);
+      h[e] = a;
+      l[e] = b;
     }
+    shi[k8] = __builtin_bit_cast(bf16x8, h);
+    slo[k8] = __builtin_bit_cast(bf16x8, l);
   }
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
@@ -504,7 +532,7 @@ __device__ __forceinline__ void gdn_verify_tree(const GdnParams& p,
   }
 #pragma unroll
   for (int m = 0; m < NG; ++m) {
-    gt[m] = gram(tX[m], max(tI[m], 0), tJ[m]);
+    gt[m] = gram(std::false_type{}, tX[m], -1.f, max(tI[m], 0), tJ[m]);
   }
 #pragma unroll
   for (int m = 0; m < NG; ++m) gdn_pin(gt[m]);
@@ -522,19 +550,18 @@ __device__ __forceinline__ void gdn_verify_tree(const GdnParams& p,
       const unsigned lo_arr = base + (isx ? kGdnXlo : kGdnYlo);
 #pragma unroll
       for (int mm = 0; mm < 4; ++mm) {
-        bf16x4 hv, lv;
+        u32x2 hv, lv;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float x = isx ? -gt[m][4 * mm + e] : gt[m][4 * mm + e];
-          __bf16 a, b;
-          gdn_split(x, a, b);
+        for (int e = 0; e < 2; ++e) {
+          uint32_t a, b;
+          gdn_split2(gt[m][4 * mm + 2 * e], gt[m][4 * mm + 2 * e + 1], a, b);
           hv[e] = a;
           lv[e] = b;
         }
         const unsigned off =
             row * kGdnXPitch + (J * 32 + 8 * mm + 4 * half) * 2;
-        *(gdn_lds_u32x2*)(size_t)(hi_arr + off) = __builtin_bit_cast(u32x2, hv);
-        *(gdn_lds_u32x2*)(size_t)(lo_arr + off) = __builtin_bit_cast(u32x2, lv);
+        *(gdn_lds_u32x2*)(size_t)(hi_arr + off) = hv;
+        *(gdn_lds_u32x2*)(size_t)(lo_arr + off) = lv;
       }
     }
   }
@@ -542,18 +569,16 @@ __device__ __forceinline__ void gdn_verify_tree(const GdnParams& p,
     const unsigned off = (w * 32 + col) * kGdnXPitch + w * 32 * 2;
 #pragma unroll
     for (int c4 = 0; c4 < 8; ++c4) {
-      bf16x4 hv, lv;
+      u32x2 hv, lv;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        __bf16 a, b;
-        gdn_split(tr[4 * c4 + e], a, b);
+      for (int e = 0; e < 2; ++e) {
+        uint32_t a, b;
+        gdn_split2(tr[4 * c4 + 2 * e], tr[4 * c4 + 2 * e + 1], a, b);
         hv[e] = a;
         lv[e] = b;
       }
-      *(gdn_lds_u32x2*)(size_t)(base + kGdnXhi + off + c4 * 8) =
-          __builtin_bit_cast(u32x2, hv);
-      *(gdn_lds_u32x2*)(size_t)(base + kGdnXlo + off + c4 * 8) =
-          __builtin_bit_cast(u32x2, lv);
+      *(gdn_lds_u32x2*)(size_t)(base + kGdnXhi + off + c4 * 8) = hv;
+      *(gdn_lds_u32x2*)(size_t)(base + kGdnXlo + off + c4 * 8) = lv;
     }
   }
   __syncthreads();
@@ -561,11 +586,13 @@ __device__ __forceinline__ void gdn_verify_tree(const GdnParams& p,
   // ---- 7. blocked forward substitution, right-looking: U_I = T_I R_I,
   // then R_J -= X_JI U_I for every later block J; U is stored as soon as
   // it is known
-  const size_t row_elems = (size_t)H * kHeadDim;
-  char* out_base = reinterpret_cast<char*>(p.out + (size_t)n0 * row_elems +
-                                           (size_t)h * kHeadDim + 32 * w);
-  char* u_base = reinterpret_cast<char*>(p.u + (size_t)n0 * row_elems +
-                                         (size_t)h * kHeadDim + 32 * w);
+  const uint32_t row_elems = (uint32_t)H * kHeadDim;
+  const __amdgpu_buffer_rsrc_t out_rs = gdn_rsrc(
+      p.out + (size_t)n0 * row_elems + (size_t)h * kHeadDim + 32 * w,
+      (uint32_t)B * row_elems * 2);
+  const __amdgpu_buffer_rsrc_t u_rs = gdn_rsrc(
+      p.u + (size_t)n0 * row_elems + (size_t)h * kHeadDim + 32 * w,
+      (uint32_t)B * row_elems * 4);
   bf16x8 uh[NT][2], ul[NT][2];
 #pragma unroll
   for (int I = 0; I < NT; ++I) {
@@ -597,7 +624,7 @@ __device__ __forceinline__ void gdn_verify_tree(const GdnParams& p,
           ul[I][1], f32x16{});
       ks[J] += pj;
     }
-    gdn_store_tile<false>(ua, u_base, row_elems * 4, I * 32, B, lane);
+    gdn_store_tile<false>(ua, u_rs, row_elems * 4, I * 32, lane);
   }
 
   // ---- 8. O_J = gamma (Q S0)_J + sum_{I <= J} Y_JI U_I
@@ -620,7 +647,7 @@ __device__ __forceinline__ void gdn_verify_tree(const GdnParams& p,
       const int rr = J * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
       o[r] += sm.gam[rr] * qs[J][r];
     }
-    gdn_store_tile<true>(o, out_base, row_elems * 2, J * 32, B, lane);
+    gdn_store_tile<true>(o, out_rs, row_elems * 2, J * 32, lane);
   }
 }
 

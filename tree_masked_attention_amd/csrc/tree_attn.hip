@@ -663,7 +663,9 @@ int tree_attn_gdn_verify(const void* q, const void* k, const void* v,
       mask_words < 1) {
     return TREE_ATTN_ERR_SHAPE;
   }
-  if (head_dim != kHeadDim || max_nodes > kGdnMaxNodes) {
+  // one tree's rows of u must stay below 2^31 bytes (buffer ranges)
+  if (head_dim != kHeadDim || max_nodes > kGdnMaxNodes ||
+      num_heads > kGdnMaxHeads) {
     return TREE_ATTN_ERR_UNSUPPORTED;
   }
   if ((long long)mask_words * 64 < max_nodes) return TREE_ATTN_ERR_SHAPE;
