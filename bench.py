@@ -84,41 +84,44 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "hbm_traffic.txt")
 
 
-VERIFY_PATH_EXCLUDED = ("accept_commit.hpp",)  # kernels after the path
+# HIP sources of each measured kernel: HBM counters taken on other sources
+# of that kernel are not reported
+KERNEL_SOURCES = {
+    "attn_fwd128h_kernel": ("common.hpp", "attn_fwd.hpp", "attn_fwd128h.hpp"),
+    "attn_fwd256_kernel<8>": ("common.hpp", "attn_fwd.hpp", "attn_fwd8.hpp"),
+    "attn_merge_kernel": ("common.hpp", "attn_merge.hpp"),
+    "gdn_verify_kernel": ("common.hpp", "gdn.hpp"),
+}
 
 
-def kernel_source_hash():
-    """Hash of the HIP sources of the verification path: HBM counters
-    taken on other sources are not reported."""
+def kernel_source_hash(kernel):
+    """Hash of the HIP sources a kernel is built from."""
     import hashlib
     csrc = os.path.join(HERE, "tree_masked_attention_amd", "csrc")
     h = hashlib.sha256()
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp", ".h")) and \
-                name not in VERIFY_PATH_EXCLUDED:
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
 def measured_traffic(workload, kernel):
     """HBM bytes per launch of one kernel from the committed counter
-    summary, when it was taken on the current sources; else None."""
+    summary, when it was taken on the kernel's current sources; else
+    None."""
     try:
         lines = open(TRAFFIC_FILE).read().splitlines()
     except OSError:
         return None
-    src = kernel_source_hash()
     for ln in lines:
         f = ln.split()
-        if len(f) < 4 or f[0] != workload:
+        if len(f) < 2 or f[0] != workload:
             continue
-        kv = dict(x.split("=", 1) for x in f[1:] if "=" in x and ":" not in x)
-        if kv.get("sources") != src:
-            return None
         for x in f[1:]:
             if x.startswith(kernel + ":"):
                 parts = dict(y.split("=") for y in x[len(kernel) + 1:].split(","))
+                if parts.get("sources") != kernel_source_hash(kernel):
+                    return None
                 try:
                     return float(parts["fetch"]) + float(parts["write"])
                 except (KeyError, ValueError):
@@ -632,23 +635,25 @@ def gdn_stage(args, torch, api):
     }
     if not args.no_cpu_baseline:
         log("[bench] CPU baseline (oracle)")
-        q32, k32, v32 = (bf16_bits_to_f32(a[:B]) for a in x[:3])
-        heads, t0 = 0, time.perf_counter()
-        while heads < H:
-            hs = slice(heads, heads + 1)
-            oracle.gdn_tree_verify(parents[:B], q32[:, hs], k32[:, hs],
-                                   v32[:, hs], x[3][:B, hs], x[4][:B, hs],
-                                   x[5][0, hs])
-            heads += 1
+        q32, k32, v32 = (bf16_bits_to_f32(a) for a in x[:3])
+        pairs, t0 = 0, time.perf_counter()
+        while pairs < S * H:
+            sq, hd = divmod(pairs, H)
+            a, hs = sq * B, slice(hd, hd + 1)
+            oracle.gdn_tree_verify(parents[a:a + B], q32[a:a + B, hs],
+                                   k32[a:a + B, hs], v32[a:a + B, hs],
+                                   x[3][a:a + B, hs], x[4][a:a + B, hs],
+                                   x[5][sq, hs])
+            pairs += 1
             el = time.perf_counter() - t0
-            if el >= args.cpu_seconds or el / heads * (heads + 1) > 30:
+            if el >= args.cpu_seconds or el / pairs * (pairs + 1) > 30:
                 break
         el = time.perf_counter() - t0
         result["cpu_baseline"] = {
-            "value": B * heads / H / el, "unit": "tree tokens/s",
+            "value": B * pairs / H / el, "unit": "tree tokens/s",
             "cores": 1, "kind": "oracle",
-            "sample": f"tree 0 ({B} nodes), {heads} of {H} heads, "
-                      f"{el:.1f} s"}
+            "sample": f"{pairs} (tree, head) pairs of {B} nodes, first "
+                      f"trees first, all heads of a tree in turn, {el:.1f} s"}
     print(json.dumps(result), flush=True)
     return 0
 

@@ -232,39 +232,38 @@ __device__ __forceinline__ void gdn_pin(f32x16& x) {
   asm volatile("" : "+v"(x));
 }
 
-// Row j of T = (I + L)^{-1} (L strictly lower triangular, 32 x 32, its
-// transpose at Lb in fp32) for the lane's row col, by backward
-// substitution t_j = [j == col] - sum_{i > j} t_i L_ij, for j = J .. 0.
-// Row j - 1 of L^T is read while row j is computed, and slot(31 - j) issues
-// matrix-core work that runs beside the row's FMAs.  One instantiation per
-// row keeps every index static; the scheduling barrier between rows keeps
-// the compiler from hoisting all reads of L to the top (and spilling them).
-template <int J, class Slot>
-__device__ __forceinline__ void gdn_t_row(float (&tr)[32], f32x4 (&Lc)[8],
-                                          f32x4 (&Ln)[8], unsigned Lb,
-                                          int col, Slot& slot) {
-  if constexpr (J > 0) {
+// Row col of T = (I + L)^{-1} (L strictly lower triangular, 32 x 32, row
+// major at Lb in fp32), right-looking: t holds the partial sums
+// t_j = [j == col] - sum_{i > j, done} t_i L_ij; step I takes t_I as final
+// and subtracts t_I L_Ij from every t_j, j < I.  The FMAs of a step are
+// independent of each other and row I - 2 of L is read during step I, so
+// a step is bound by issue, not latency, and slot(31 - I) issues matrix-core
+// work beside it.  One instantiation per step keeps every index static;
+// the scheduling barrier between steps keeps the compiler from hoisting
+// all reads of L to the top (and spilling them).
+template <int I, class Slot>
+__device__ __forceinline__ void gdn_t_step(float (&tr)[32], f32x4 (&L0)[8],
+                                           f32x4 (&L1)[8], f32x4 (&L2)[8],
+                                           unsigned Lb, Slot& slot) {
+  // L0 holds row I, L1 row I - 1 (in flight); read row I - 2 into L2
+  if constexpr (I > 2) {
 #pragma unroll
-    for (int i4 = J / 4; i4 < 8; ++i4) {
-      Ln[i4] = *(const gdn_lds_f32x4*)(size_t)(Lb + (J - 1) * 128 + i4 * 16);
+    for (int j4 = 0; j4 < (I - 2 + 3) / 4; ++j4) {
+      L2[j4] = *(const gdn_lds_f32x4*)(size_t)(Lb + (I - 2) * 128 + j4 * 16);
     }
   }
-  slot(std::integral_constant<int, 31 - J>{});
-  // four partial sums (by i mod 4) shorten the dependent FMA chain
-  float a4[4] = {(J == col) ? 1.f : 0.f, 0.f, 0.f, 0.f};
+  slot(std::integral_constant<int, 31 - I>{});
+  const float ti = tr[I];
 #pragma unroll
-  for (int i4 = (J + 1) / 4; i4 < 8; ++i4) {
+  for (int j = 0; j < I; ++j) tr[j] -= ti * L0[j >> 2][j & 3];
+  gdn_pin(tr[I]);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (4 * i4 + e > J) a4[e] -= Lc[i4][e] * tr[4 * i4 + e];
-    }
+  for (int j4 = 0; j4 < 8; ++j4) {
+    L0[j4] = L1[j4];
+    L1[j4] = L2[j4];
   }
-  tr[J] = (a4[0] + a4[1]) + (a4[2] + a4[3]);
-  gdn_pin(tr[J]);
-#pragma unroll
-  for (int i4 = 0; i4 < 8; ++i4) Lc[i4] = Ln[i4];
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (J > 0) gdn_t_row<J - 1>(tr, Lc, Ln, Lb, col, slot);
+  if constexpr (I > 0) gdn_t_step<I - 1>(tr, L0, L1, L2, Lb, slot);
 }
 
 // The work of one (sequence, head) whose tree has B nodes, NT = ceil(B/32).
@@ -413,20 +412,20 @@ __device__ __forceinline__ void gdn_verify_tree(const GdnParams& p,
     return acc;
   };
 
-  // ---- 3. diagonal X block w in fp32, transposed (L^T), to LDS
+  // ---- 3. diagonal X block w in fp32 (row major) to LDS
   if (w < NT) {
     const f32x16 d = gram(std::true_type{}, true, 1.f, w, w);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int jl = 8 * (r >> 2) + 4 * half + (r & 3);
-      *(gdn_lds_f32*)(size_t)(base + kGdnLOff + w * 4096 + jl * 128 +
-                              col * 4) = d[r];
+    for (int mm = 0; mm < 4; ++mm) {
+      const f32x4 x4 = {d[4 * mm], d[4 * mm + 1], d[4 * mm + 2], d[4 * mm + 3]};
+      *(gdn_lds_f32x4*)(size_t)(base + kGdnLOff + w * 4096 + col * 128 +
+                                (8 * mm + 4 * half) * 4) = x4;
     }
   }
   __syncthreads();
 
   // ---- 4. K S0 and Q S0 on the matrix cores, interleaved with (VALU) row
-  // col of T_w = (I + L_w)^{-1}: 32 slots of 4 products, one per row of T
+  // col of T_w = (I + L_w)^{-1}: 32 slots of 4 products, one per step
   f32x16 ks[NT], qs[NT];
   bf16x8 shi[8], slo[8];
 #pragma unroll
@@ -447,39 +446,59 @@ __device__ __forceinline__ void gdn_verify_tree(const GdnParams& p,
     ks[t] = f32x16{};
     qs[t] = f32x16{};
   }
-  // slot sl issues the four products of (kk, t) = (sl / NT, sl % NT) with
-  // A operands read one slot earlier, and reads those of the next slot
-  bf16x8 ak, aq;
-  auto read_a = [&](int sl) {
-    const int kk = sl / NT, t = sl % NT;
-    const unsigned ra = (t * 32 + col) * kGdnKPitch + (2 * kk + half) * 16;
-    ak = gdn_read16(base + kGdnKOff + ra);
-    aq = gdn_read16(base + kGdnQOff + ra);
+  // 8 NT slots of four products each.  Per k-step kk the slots take the
+  // hi parts of S0 for tile pairs (0, 1), (2, 3), then the lo parts, so
+  // two products into one accumulator are several MFMAs apart; a single
+  // tile (NT odd) pairs with itself.  A operands are read one k-step ahead.
+  constexpr int NP = (NT + 1) / 2;  // tile pairs
+  bf16x8 ak[NT], aq[NT], akn[NT], aqn[NT];
+  auto read_ks = [&](int kk, bf16x8 (&k_)[NT], bf16x8 (&q_)[NT]) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const unsigned ra = (t * 32 + col) * kGdnKPitch + (2 * kk + half) * 16;
+      k_[t] = gdn_read16(base + kGdnKOff + ra);
+      q_[t] = gdn_read16(base + kGdnQOff + ra);
+    }
   };
-  read_a(0);
+  read_ks(0, ak, aq);
   auto slot = [&](auto sc) {
     constexpr int sl = decltype(sc)::value;
-    if constexpr (sl < 8 * NT) {
-      constexpr int kk = sl / NT, t = sl % NT;
-      const bf16x8 a_k = ak, a_q = aq;
-      if constexpr (sl + 1 < 8 * NT) read_a(sl + 1);
-      ks[t] = mfma32x32x16(a_k, shi[kk], ks[t]);
-      qs[t] = mfma32x32x16(a_q, shi[kk], qs[t]);
-      ks[t] = mfma32x32x16(a_k, slo[kk], ks[t]);
-      qs[t] = mfma32x32x16(a_q, slo[kk], qs[t]);
+    if constexpr (sl < 16 * NP) {
+      constexpr int kk = sl / (2 * NP), r = sl % (2 * NP);
+      constexpr bool lo = r >= NP;
+      constexpr int t0 = 2 * (r % NP), t1 = t0 + 1 < NT ? t0 + 1 : t0;
+      if constexpr (r == 0 && kk + 1 < 8) read_ks(kk + 1, akn, aqn);
+      const bf16x8 bs = lo ? slo[kk] : shi[kk];
+      ks[t0] = mfma32x32x16(ak[t0], bs, ks[t0]);
+      qs[t0] = mfma32x32x16(aq[t0], bs, qs[t0]);
+      if constexpr (t1 != t0) {
+        ks[t1] = mfma32x32x16(ak[t1], bs, ks[t1]);
+        qs[t1] = mfma32x32x16(aq[t1], bs, qs[t1]);
+      }
+      if constexpr (r == 2 * NP - 1) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          ak[t] = akn[t];
+          aq[t] = aqn[t];
+        }
+      }
     }
   };
   __builtin_amdgcn_sched_barrier(0);
   float tr[32];
   {
     // waves >= NT run it on a block no tree uses and discard the result
-    f32x4 Lc[8], Ln[8];
+    const unsigned Lb = base + kGdnLOff + w * 4096;
+    f32x4 L0[8], L1[8], L2[8];
 #pragma unroll
-    for (int i4 = 0; i4 < 8; ++i4) {
-      Lc[i4] = f32x4{};
-      Ln[i4] = f32x4{};
+    for (int j = 0; j < 32; ++j) tr[j] = (j == col) ? 1.f : 0.f;
+#pragma unroll
+    for (int j4 = 0; j4 < 8; ++j4) {
+      L0[j4] = *(const gdn_lds_f32x4*)(size_t)(Lb + 31 * 128 + j4 * 16);
+      L1[j4] = *(const gdn_lds_f32x4*)(size_t)(Lb + 30 * 128 + j4 * 16);
+      L2[j4] = f32x4{};
     }
-    gdn_t_row<31>(tr, Lc, Ln, base + kGdnLOff + w * 4096, col, slot);
+    gdn_t_step<31>(tr, L0, L1, L2, Lb, slot);
   }
   // R = beta (V - gamma K S0), in place of K S0
 #pragma unroll
@@ -600,16 +619,12 @@ __device__ __forceinline__ void gdn_verify_tree(const GdnParams& p,
     bf16x8 rh0, rl0, rh1, rl1;
     gdn_split_tile<0>(ks[I], rh0, rl0);
     gdn_split_tile<1>(ks[I], rh1, rl1);
-    // the two k-steps of each product accumulate separately (shorter
-    // dependent chains on the critical path), then add
     f32x16 ua = gdn_mfma3(gdn_read_perm(base + kGdnXhi, row, I * 32, half),
                           gdn_read_perm(base + kGdnXlo, row, I * 32, half),
                           rh0, rl0, f32x16{});
-    const f32x16 ub = gdn_mfma3(
-        gdn_read_perm(base + kGdnXhi, row, I * 32 + 16, half),
-        gdn_read_perm(base + kGdnXlo, row, I * 32 + 16, half), rh1, rl1,
-        f32x16{});
-    ua += ub;
+    ua = gdn_mfma3(gdn_read_perm(base + kGdnXhi, row, I * 32 + 16, half),
+                   gdn_read_perm(base + kGdnXlo, row, I * 32 + 16, half), rh1,
+                   rl1, ua);
     gdn_split_tile<0>(ua, uh[I][0], ul[I][0]);
     gdn_split_tile<1>(ua, uh[I][1], ul[I][1]);
 #pragma unroll
@@ -618,11 +633,9 @@ __device__ __forceinline__ void gdn_verify_tree(const GdnParams& p,
       ks[J] = gdn_mfma3(gdn_read_perm(base + kGdnXhi, rj, I * 32, half),
                         gdn_read_perm(base + kGdnXlo, rj, I * 32, half),
                         uh[I][0], ul[I][0], ks[J]);
-      const f32x16 pj = gdn_mfma3(
-          gdn_read_perm(base + kGdnXhi, rj, I * 32 + 16, half),
-          gdn_read_perm(base + kGdnXlo, rj, I * 32 + 16, half), uh[I][1],
-          ul[I][1], f32x16{});
-      ks[J] += pj;
+      ks[J] = gdn_mfma3(gdn_read_perm(base + kGdnXhi, rj, I * 32 + 16, half),
+                        gdn_read_perm(base + kGdnXlo, rj, I * 32 + 16, half),
+                        uh[I][1], ul[I][1], ks[J]);
     }
     gdn_store_tile<false>(ua, u_rs, row_elems * 4, I * 32, lane);
   }
@@ -631,17 +644,16 @@ __device__ __forceinline__ void gdn_verify_tree(const GdnParams& p,
 #pragma unroll
   for (int J = 0; J < NT; ++J) {
     const int row = J * 32 + col;
-    f32x16 o = f32x16{}, o1 = f32x16{};
+    f32x16 o = f32x16{};
 #pragma unroll
     for (int I = 0; I <= J; ++I) {
       o = gdn_mfma3(gdn_read_perm(base + kGdnYhi, row, I * 32, half),
                     gdn_read_perm(base + kGdnYlo, row, I * 32, half),
                     uh[I][0], ul[I][0], o);
-      o1 = gdn_mfma3(gdn_read_perm(base + kGdnYhi, row, I * 32 + 16, half),
-                     gdn_read_perm(base + kGdnYlo, row, I * 32 + 16, half),
-                     uh[I][1], ul[I][1], o1);
+      o = gdn_mfma3(gdn_read_perm(base + kGdnYhi, row, I * 32 + 16, half),
+                    gdn_read_perm(base + kGdnYlo, row, I * 32 + 16, half),
+                    uh[I][1], ul[I][1], o);
     }
-    o += o1;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int rr = J * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
