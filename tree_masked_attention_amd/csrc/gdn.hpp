@@ -34,22 +34,22 @@
 // Higher-Precision Computations" (ARITH 2019).
 //
 // Phases (barriers between them):
-//  1. K and Q rows (bf16) to LDS; per node the mask words, g and beta; the
-//     wave's 128 x 32 slice of S0 straight from global memory into B
-//     operand registers (split).
-//  2. G_i from the ancestor bitmask (the masks the attention path uses).
-//  3. K S0 and Q S0 for the wave's columns (accumulators stay in
-//     registers), and the lower-triangular 32 x 32 tiles of K K^T and
-//     Q K^T, four waves sharing the tiles; a tile is computed transposed
-//     (K_J times the row block's K or Q) so that a lane ends up holding
-//     runs of 4 consecutive columns of one row of X or Y.
-//  4. X (negated) and Y, masked and decayed, written over K / Q in LDS as
-//     bf16 hi / lo rows; the diagonal 32 x 32 blocks of X also in fp32.
-//  5. T_J = (I + X_JJ)^{-1} of every diagonal block by forward substitution
-//     (one wave per block, one column per lane), written over X_JJ.
-//  6. Per wave: R = beta (V - gamma K S0); blocked forward substitution
-//     U_J = T_J (R_J - sum_{I<J} X_JI U_I); O_J = gamma (Q S0)_J +
-//     sum_{I<=J} Y_JI U_I; stores of O (bf16) and U (fp32).
+//  1. Every global load of the tree issued up front: the wave's 128 x 32
+//     slice of S0 into registers, K, Q and V rows through registers into
+//     LDS, per node the mask words, g and beta.
+//  2. G_i by pointer jumping over the parents read from the mask rows.
+//  3. The diagonal 32 x 32 X blocks in fp32 (one per wave).
+//  4. K S0 and Q S0 on the matrix cores, interleaved with the inversion
+//     T_w = (I + X_ww)^{-1} of diagonal block w (right-looking
+//     substitution, VALU); then R = beta (V - gamma K S0).
+//  5. The off-diagonal X tiles and all Y tiles of the lower triangle, four
+//     waves sharing them; a tile is computed transposed (K_J times the row
+//     block's K or Q) so that a lane holds runs of 4 consecutive columns
+//     of one row of X or Y.
+//  6. -X, Y and T_w written over the staged rows as bf16 hi / lo rows.
+//  7. Per wave: blocked forward substitution U_I = T_I (R_I - sum_{I'<I}
+//     X_II' U_I'), right-looking; O_J = gamma (Q S0)_J + sum_{I<=J} Y_JI
+//     U_I; U (fp32) and O (bf16) stored straight from registers.
 // U never leaves registers between the solve and the output stage: a
 // 32 x 32 accumulator tile held by a lane pair as runs of 4 rows is used
 // directly as the B operand of the next product, with the A operand's
