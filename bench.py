@@ -71,6 +71,12 @@ def parse():
                     help="gdn: nodes per tree (<= 128)")
     ap.add_argument("--gdn-heads", type=int, default=32,
                     help="gdn: heads (d_k = d_v = 128)")
+    ap.add_argument("--kv", choices=("bf16", "e4m3"), default="bf16",
+                    help="verify: K/V cache element type (e4m3: FP8 with "
+                         "per-kv-head scales, through tree_attn_verify_ex)")
+    ap.add_argument("--head-dim", type=int, choices=(64, 128), default=128,
+                    help="verify: head dimension (64 runs through "
+                         "tree_attn_verify_ex)")
     ap.add_argument("--width", type=int, default=1,
                     help="tree-build: candidates taken per step (1 = strict "
                          "best-first)")
@@ -91,6 +97,7 @@ KERNEL_SOURCES = {
     "attn_fwd256_kernel<8>": ("common.hpp", "attn_fwd.hpp", "attn_fwd8.hpp"),
     "attn_merge_kernel": ("common.hpp", "attn_merge.hpp"),
     "gdn_verify_kernel": ("common.hpp", "gdn.hpp"),
+    "attn_var_kernel": ("common.hpp", "attn_var.hpp"),
 }
 
 
@@ -146,7 +153,7 @@ def copy_calibration(torch):
 # algorithmic work of one verify launch
 # --------------------------------------------------------------------------
 
-def algorithmic_work(wl, with_output=True):
+def algorithmic_work(wl, with_output=True, kv_bytes=None):
     """(bytes, flops) the method must move / compute for one verify call.
 
     bytes: K and V of every cached token read once, q read and out written
@@ -157,12 +164,14 @@ def algorithmic_work(wl, with_output=True):
     pairs are not counted.
     """
     d, Hq, Hkv, ps = wl.head_dim, wl.num_q_heads, wl.num_kv_heads, wl.page_size
+    if kv_bytes is None:
+        kv_bytes = 1 if wl.kv_format == "e4m3" else 2
     P = wl.prefix_lens.astype(np.int64)
     B = wl.tree_sizes
     N = wl.total_nodes
     W = wl.mask_words()
     tokens = P + B
-    nbytes = (int(tokens.sum()) * Hkv * d * 2 * 2 + N * Hq * d * 2 +
+    nbytes = (int(tokens.sum()) * Hkv * d * kv_bytes * 2 + N * Hq * d * 2 +
               N * W * 8 + 4 * int(((tokens + ps - 1) // ps).sum()))
     if with_output:
         nbytes += N * Hq * d * 2 + N * Hq * 4
@@ -683,7 +692,9 @@ def main():
     if args.stage == "gdn":
         return gdn_stage(args, torch, api)
     log(f"[bench] drawing workload {args.workload}")
-    wl = standard_workload(args.workload)
+    wl = standard_workload(args.workload, kv_format=args.kv,
+                           head_dim=args.head_dim)
+    variant = args.kv != "bf16" or args.head_dim != 128
     if args.stage == "tree-build":
         return tree_build_stage(args, torch, api, wl,
                                 torch.cuda.current_stream())
@@ -693,7 +704,14 @@ def main():
     bound = "mfma" if ai > ridge else "hbm"
 
     bf = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
-    host = dict(q=bf(wl.q), k=bf(wl.k_cache), v=bf(wl.v_cache),
+    if wl.kv_format == "bf16":
+        kv_host = dict(k=bf(wl.k_cache), v=bf(wl.v_cache))
+    else:
+        kv_host = dict(k=torch.from_numpy(wl.k_cache),
+                       v=torch.from_numpy(wl.v_cache),
+                       ks=torch.from_numpy(wl.k_scale),
+                       vs=torch.from_numpy(wl.v_scale))
+    host = dict(q=bf(wl.q), **kv_host,
                 table=torch.from_numpy(wl.page_table),
                 prefix=torch.from_numpy(wl.prefix_lens),
                 offs=torch.from_numpy(wl.tree_offsets),
@@ -717,9 +735,10 @@ def main():
     bad = torch.empty((max(S, 1),), dtype=torch.int32, device=dev)
     out = torch.empty((N, Hq, d), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((N, Hq), dtype=torch.float32, device=dev)
-    ws_bytes = api.workspace_size(S, N, Hq, wl.num_kv_heads, d,
-                                  wl.max_prefix_len, wl.max_nodes,
-                                  wl.page_size, args.splits)
+    kvd = api.KV_FP8_E4M3 if wl.kv_format == "e4m3" else api.KV_BF16
+    ws_bytes = int(api._lib.tree_attn_workspace_size_ex(
+        kvd, S, N, Hq, wl.num_kv_heads, d, wl.max_prefix_len, wl.max_nodes,
+        wl.page_size, args.splits))
     ws = torch.empty((max(ws_bytes, 256),), dtype=torch.uint8, device=dev)
     sptr = stream.cuda_stream
 
@@ -728,16 +747,30 @@ def main():
     for c in sets:
         mask_args = (c["parents"].data_ptr(), c["offs"].data_ptr(), S, N,
                      max_b, W, masks.data_ptr(), bad.data_ptr(), sptr)
-        ver_args = (c["q"].data_ptr(), c["k"].data_ptr(), c["v"].data_ptr(),
-                    c["table"].data_ptr(), wl.max_pages_per_seq,
-                    wl.num_pages, wl.page_size, c["prefix"].data_ptr(),
-                    c["offs"].data_ptr(), masks.data_ptr(), W, S, N,
-                    wl.max_prefix_len, wl.max_nodes, Hq, wl.num_kv_heads, d,
-                    wl.scale, args.splits, out.data_ptr(), lse.data_ptr(),
-                    ws.data_ptr(), ws.numel(), sptr)
+        if variant:
+            ver_args = (c["q"].data_ptr(), c["k"].data_ptr(),
+                        c["v"].data_ptr(), kvd,
+                        c["ks"].data_ptr() if "ks" in c else None,
+                        c["vs"].data_ptr() if "vs" in c else None,
+                        c["table"].data_ptr(), wl.max_pages_per_seq,
+                        wl.num_pages, wl.page_size, c["prefix"].data_ptr(),
+                        c["offs"].data_ptr(), masks.data_ptr(), W, S, N,
+                        wl.max_prefix_len, wl.max_nodes, Hq, wl.num_kv_heads,
+                        d, wl.scale, args.splits, out.data_ptr(),
+                        lse.data_ptr(), ws.data_ptr(), ws.numel(), sptr)
+        else:
+            ver_args = (c["q"].data_ptr(), c["k"].data_ptr(),
+                        c["v"].data_ptr(), c["table"].data_ptr(),
+                        wl.max_pages_per_seq, wl.num_pages, wl.page_size,
+                        c["prefix"].data_ptr(), c["offs"].data_ptr(),
+                        masks.data_ptr(), W, S, N, wl.max_prefix_len,
+                        wl.max_nodes, Hq, wl.num_kv_heads, d, wl.scale,
+                        args.splits, out.data_ptr(), lse.data_ptr(),
+                        ws.data_ptr(), ws.numel(), sptr)
         calls.append((mask_args, ver_args))
     f_mask = api._lib.tree_attn_build_mask
-    f_ver = api._lib.tree_attn_verify
+    f_ver = (api._lib.tree_attn_verify_ex if variant
+             else api._lib.tree_attn_verify)
 
     def step(i):
         ma, va = calls[i % copies]
@@ -783,8 +816,13 @@ def main():
     #     the launch stream between one pair of events (input copies
     #     rotated as above), so the figure is the kernel's own time plus
     #     the dispatch gap between consecutive launches
-    plan = api.describe_plan(S, N, Hq, wl.num_kv_heads, d, wl.max_prefix_len,
-                             wl.max_nodes, wl.page_size, args.splits)
+    if variant:
+        plan = {"kernel": "attn_var_kernel (+ attn_var_merge_kernel)",
+                "rows": 128, "workspace_bytes": ws_bytes}
+    else:
+        plan = api.describe_plan(S, N, Hq, wl.num_kv_heads, d,
+                                 wl.max_prefix_len, wl.max_nodes,
+                                 wl.page_size, args.splits)
     f_att = api._lib.tree_attn_verify_attend
     f_mer = api._lib.tree_attn_verify_merge
 
@@ -803,17 +841,26 @@ def main():
         return e0.elapsed_time(e1) / args.steps
 
     mask_ms = per_launch(f_mask, lambda i: calls[i % copies][0])
-    att_ms = per_launch(f_att, lambda i: calls[i % copies][1])
-    mer_ms = (per_launch(f_mer, lambda i: calls[i % copies][1])
-              if plan["splits"] > 1 else 0.0)
-    ver_ms = per_launch(f_ver, lambda i: calls[i % copies][1])
+    if variant:
+        # one entry point (attention kernel, then the merge when split)
+        ver_ms = per_launch(f_ver, lambda i: calls[i % copies][1])
+        att_ms, mer_ms = ver_ms, 0.0
+    else:
+        att_ms = per_launch(f_att, lambda i: calls[i % copies][1])
+        mer_ms = (per_launch(f_mer, lambda i: calls[i % copies][1])
+                  if plan["splits"] > 1 else 0.0)
+        ver_ms = per_launch(f_ver, lambda i: calls[i % copies][1])
     log(f"[bench] step {ms_per_step * 1e3:.1f} us; mask build "
         f"{mask_ms * 1e3:.1f} us; verify {ver_ms * 1e3:.1f} us = attend "
         f"{att_ms * 1e3:.1f} us + merge {mer_ms * 1e3:.1f} us")
 
-    kname = ("attn_fwd256_kernel<8>" if plan["rows"] == 256
-             else "attn_fwd128h_kernel")
-    att_bytes, _ = algorithmic_work(wl, with_output=plan["splits"] == 1)
+    if variant:
+        kname = "attn_var_kernel"
+        att_bytes, _ = algorithmic_work(wl, with_output=True)
+    else:
+        kname = ("attn_fwd256_kernel<8>" if plan["rows"] == 256
+                 else "attn_fwd128h_kernel")
+        att_bytes, _ = algorithmic_work(wl, with_output=plan["splits"] == 1)
     value = N / (ms_per_step * 1e-3)
     a_s = att_ms * 1e-3
     if bound == "hbm":
@@ -835,10 +882,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if wl.kv_format == "bf16" else "bf16 q, e4m3 kv",
         "data": "synthetic",
         "config": {
             "workload": wl.name,
+            "kv_format": wl.kv_format,
             "num_seqs": S,
             "prefix_lens": ([int(x) for x in wl.prefix_lens] if S <= 8
                             else f"{S} x {int(wl.prefix_lens[0])}"),
@@ -851,7 +899,9 @@ def main():
         },
         "roofline": {
             "bound": bound,
-            "kernel": f"{kname} (tree_attn_verify_attend)",
+            "kernel": (f"{kname} with its merge (tree_attn_verify_ex, one "
+                       f"call)" if variant
+                       else f"{kname} (tree_attn_verify_attend)"),
             "achieved": achieved,
             "peak": peak,
             "unit": unit,

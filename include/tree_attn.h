@@ -477,6 +477,56 @@ int tree_attn_gdn_commit(const void* k, const float* u, const float* g,
                          int32_t max_nodes, int32_t num_heads,
                          int32_t head_dim, float* state, void* stream);
 
+/* K/V element types of tree_attn_verify_ex. */
+#define TREE_ATTN_KV_BF16 0     /* bfloat16 */
+#define TREE_ATTN_KV_FP8_E4M3 1 /* OCP FP8 E4M3 (e4m3fn), scaled per kv head */
+
+/*
+ * tree_attn_verify_ex - tree_attn_verify for more cache formats and head
+ * dimensions (the same operation, JETFLOW section 2 "Arquitectura
+ * Central", bullet on the tree-causal mask).
+ *
+ * Arguments as for tree_attn_verify, plus:
+ *   kv_dtype      TREE_ATTN_KV_BF16 or TREE_ATTN_KV_FP8_E4M3: the element
+ *                 type of k_cache and v_cache ([num_pages][page_size]
+ *                 [num_kv_heads][head_dim] elements, 1 or 2 bytes each)
+ *   k_scale, v_scale
+ *                 dev fp32 [num_kv_heads]: for FP8 the cached value of kv
+ *                 head g stands for (E4M3 value) * scale[g]; NULL = 1.
+ *                 Ignored for bf16.
+ *   head_dim      64 or 128 (q, out: [total_nodes][num_q_heads][head_dim])
+ * With bf16 and head_dim 128 this is exactly tree_attn_verify (the same
+ * kernels).  The other combinations run a separate kernel (128 query rows
+ * per workgroup, fp8 converted to bf16 exactly on its way into LDS, bf16
+ * matrix cores, fp32 accumulation, split partials in fp32); its workspace
+ * size comes from tree_attn_workspace_size_ex.
+ *
+ * Host-side errors: as tree_attn_verify; ERR_UNSUPPORTED also for
+ * head_dim not 64 or 128 and for an unknown kv_dtype.
+ */
+int tree_attn_verify_ex(const void* q, const void* k_cache,
+                        const void* v_cache, int32_t kv_dtype,
+                        const float* k_scale, const float* v_scale,
+                        const int32_t* page_table, int32_t max_pages_per_seq,
+                        int32_t num_pages, int32_t page_size,
+                        const int32_t* prefix_lens,
+                        const int32_t* tree_offsets, const uint64_t* masks,
+                        int32_t mask_words, int32_t num_seqs,
+                        int32_t total_nodes, int32_t max_prefix_len,
+                        int32_t max_nodes, int32_t num_q_heads,
+                        int32_t num_kv_heads, int32_t head_dim, float scale,
+                        int32_t num_splits, void* out, float* lse,
+                        void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/* Workspace bytes tree_attn_verify_ex needs for these sizes (0: none, or
+ * sizes it would reject). */
+size_t tree_attn_workspace_size_ex(int32_t kv_dtype, int32_t num_seqs,
+                                   int32_t total_nodes, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t max_prefix_len, int32_t max_nodes,
+                                   int32_t page_size, int32_t num_splits);
+
 #ifdef __cplusplus
 }
 #endif

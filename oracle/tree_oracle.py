@@ -50,6 +50,21 @@ def widen_bf16(bits: np.ndarray) -> np.ndarray:
     return b.view(np.float32).astype(np.float64)
 
 
+def widen_e4m3(codes: np.ndarray) -> np.ndarray:
+    """OCP FP8 E4M3 (e4m3fn) codes (uint8) -> float64, exact, from the
+    format's definition: sign bit, 4 exponent bits (bias 7), 3 mantissa
+    bits; exponent 0 is subnormal, m/8 * 2^-6; S.1111.111 is NaN; there are
+    no infinities (S.1111.110 = 448 is the largest finite value)."""
+    b = np.asarray(codes).astype(np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = (b & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6,
+                   (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    mag = np.where((b & 0x7F) == 0x7F, np.nan, mag)
+    return sign * mag
+
+
 def _check_parents(parents_local: np.ndarray) -> None:
     for i, p in enumerate(parents_local.tolist()):
         if not (-1 <= p < i):
@@ -105,16 +120,26 @@ def ancestor_masks(parents: np.ndarray, tree_offsets: np.ndarray,
 # --------------------------------------------------------------------------
 
 def _gather_tokens(cache_bits: np.ndarray, table_row: np.ndarray,
-                   num_tokens: int) -> np.ndarray:
+                   num_tokens: int, kv_format: str = "bf16",
+                   head_scale: Optional[np.ndarray] = None) -> np.ndarray:
     """Logical tokens 0..num_tokens-1 of one sequence -> float64
     [num_tokens, Hkv, d], reading physical page table_row[t // page_size],
-    slot t % page_size."""
+    slot t % page_size.  kv_format "bf16" (uint16 bit patterns) or "e4m3"
+    (uint8 codes, each kv head's values times head_scale[head])."""
     num_pages, page_size = cache_bits.shape[0], cache_bits.shape[1]
     t = np.arange(num_tokens)
     pages = np.asarray(table_row, dtype=np.int64)[t // page_size]
     if num_tokens and (pages.min() < 0 or pages.max() >= num_pages):
         raise ValueError("page table entry outside the page pool")
-    return widen_bf16(cache_bits[pages, t % page_size])
+    raw = cache_bits[pages, t % page_size]
+    if kv_format == "bf16":
+        return widen_bf16(raw)
+    if kv_format != "e4m3":
+        raise ValueError(f"unknown kv_format {kv_format!r}")
+    vals = widen_e4m3(raw)
+    if head_scale is not None:
+        vals = vals * np.asarray(head_scale, np.float64)[None, :, None]
+    return vals
 
 
 def _kv_head_of(h: int, num_q_heads: int, num_kv_heads: int) -> int:
@@ -157,12 +182,17 @@ def tree_attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
                    tree_offsets: np.ndarray, parents: np.ndarray,
                    scale: float,
                    seq_ids: Optional[Iterable[int]] = None,
-                   kv_head_ids: Optional[Iterable[int]] = None
+                   kv_head_ids: Optional[Iterable[int]] = None,
+                   kv_format: str = "bf16",
+                   k_scale: Optional[np.ndarray] = None,
+                   v_scale: Optional[np.ndarray] = None
                    ) -> Tuple[np.ndarray, np.ndarray]:
     """Tree-causal verification attention, float64.
 
-    q: bf16 bits [N, Hq, d]; k_cache / v_cache: bf16 bits
-    [num_pages, page_size, Hkv, d]; page_table int [S, max_pages];
+    q: bf16 bits [N, Hq, d]; k_cache / v_cache: bf16 bits (kv_format
+    "bf16") or E4M3 codes with per-kv-head scales k_scale / v_scale
+    (kv_format "e4m3") [num_pages, page_size, Hkv, d]; page_table int
+    [S, max_pages];
     prefix_lens [S]; tree_offsets [S+1]; parents [N] (local, -1 = root).
 
     For node i of sequence s and query head h the allowed keys are the
@@ -195,8 +225,10 @@ def tree_attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
         anc = _ancestor_sets(parents[a:b])
         allowed_nodes = np.stack([_allowed_keys(P, anc[i], B)
                                   for i in range(B)])          # [B, P+B]
-        K = _gather_tokens(k_cache, page_table[s], P + B)       # [T, Hkv, d]
-        V = _gather_tokens(v_cache, page_table[s], P + B)
+        K = _gather_tokens(k_cache, page_table[s], P + B, kv_format,
+                           k_scale)                              # [T, Hkv, d]
+        V = _gather_tokens(v_cache, page_table[s], P + B, kv_format,
+                           v_scale)
         qs = widen_bf16(q[a:b])                                  # [B, Hq, d]
         for g in groups:
             heads = [h for h in range(Hq)
@@ -214,7 +246,8 @@ def workload_attention(wl, **kw):
     """tree_attention on an object with the workload attribute names."""
     return tree_attention(wl.q, wl.k_cache, wl.v_cache, wl.page_table,
                           wl.prefix_lens, wl.tree_offsets, wl.parents,
-                          wl.scale, **kw)
+                          wl.scale, kv_format=wl.kv_format,
+                          k_scale=wl.k_scale, v_scale=wl.v_scale, **kw)
 
 
 def workload_masks(wl, mask_words: Optional[int] = None) -> np.ndarray:

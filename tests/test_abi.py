@@ -349,3 +349,63 @@ def test_gdn_commit_rejects(over, code):
 def test_gdn_commit_empty_is_noop():
     assert _gdn_commit(S=0, k=None) == api.OK
     assert _gdn_commit(max_b=0, k=None) == api.OK
+
+
+def _vex(**over):
+    a = dict(q=1, k=1, v=1, kv=1, ks=None, vs=None, table=1, max_pps=4,
+             num_pages=8, page_size=16, prefix=1, offs=1, masks=1, W=1, S=1,
+             N=8, max_p=40, max_b=8, Hq=8, Hkv=2, d=64, scale=0.125,
+             splits=0, out=1, lse=1, ws=None, ws_bytes=0)
+    a.update(over)
+    return int(api._lib.tree_attn_verify_ex(
+        a["q"], a["k"], a["v"], a["kv"], a["ks"], a["vs"], a["table"],
+        a["max_pps"], a["num_pages"], a["page_size"], a["prefix"], a["offs"],
+        a["masks"], a["W"], a["S"], a["N"], a["max_p"], a["max_b"], a["Hq"],
+        a["Hkv"], a["d"], a["scale"], a["splits"], a["out"], a["lse"],
+        a["ws"], a["ws_bytes"], None))
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(S=-1), api.ERR_SHAPE),
+    (dict(Hq=6, Hkv=4), api.ERR_SHAPE),
+    (dict(page_size=24), api.ERR_SHAPE),
+    (dict(W=0), api.ERR_SHAPE),
+    (dict(W=1, max_b=65), api.ERR_SHAPE),
+    (dict(scale=0.0), api.ERR_SHAPE),
+    (dict(num_pages=0), api.ERR_SHAPE),
+    (dict(d=96), api.ERR_UNSUPPORTED),
+    (dict(d=256), api.ERR_UNSUPPORTED),
+    (dict(kv=2), api.ERR_UNSUPPORTED),
+    (dict(max_b=1025, W=17), api.ERR_UNSUPPORTED),
+    (dict(q=None), api.ERR_NULL),
+    (dict(k=None), api.ERR_NULL),
+    (dict(masks=None), api.ERR_NULL),
+    (dict(lse=None), api.ERR_NULL),
+    (dict(max_p=100000, S=64, N=64), api.ERR_WORKSPACE),
+])
+def test_verify_ex_rejects(over, code):
+    assert _vex(**over) == code
+
+
+def test_verify_ex_bf16_d128_checks_like_verify():
+    # the bf16 / d = 128 combination is tree_attn_verify itself
+    assert _vex(kv=0, d=128, q=None) == api.ERR_NULL
+    assert _vex(kv=0, d=128, page_size=24) == api.ERR_SHAPE
+
+
+def test_verify_ex_empty_is_noop():
+    assert _vex(S=0, q=None) == api.OK
+    assert _vex(N=0, q=None) == api.OK
+
+
+def test_workspace_size_ex_rules():
+    f = api._lib.tree_attn_workspace_size_ex
+    # one sequence with a short range: a single split, no workspace
+    assert f(1, 1, 8, 8, 2, 64, 40, 8, 16, 1) == 0
+    # forced splits: fp32 partials (N * Hq * d * 4 per split) + (m, l)
+    n = f(1, 1, 8, 8, 2, 64, 4000, 8, 16, 4)
+    assert n >= 4 * 8 * 8 * 64 * 4 + 4 * 8 * 8 * 8
+    # bf16 / d = 128 uses the tuned path's size
+    assert f(0, 1, 8, 8, 2, 128, 4000, 8, 16, 4) == \
+        api._lib.tree_attn_workspace_size(1, 8, 8, 2, 128, 4000, 8, 16, 4)
+    assert f(1, 1, 8, 8, 2, 96, 4000, 8, 16, 4) == 0   # rejected sizes

@@ -1,0 +1,129 @@
+"""Cache-format and head-dimension variants of the verification attention
+(tree_attn_verify_ex): head_dim 64, and FP8 E4M3 K/V pages with per-kv-head
+scales, against the CPU oracle through the C ABI (needs a gfx950 GPU).
+Bar: out max-abs <= 2e-2, lse relative <= 1e-3 (the oracle decodes the same
+E4M3 codes, so the cache format adds no error of its own)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import LSE_RTOL, OUT_ATOL, say
+from tree_masked_attention_amd.workloads import (make_workload,
+                                                 standard_workload)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    import tree_masked_attention_amd.api  # noqa: F401  (fails loudly if unbuilt)
+
+
+def run_ex(wl, num_splits=0, W=None):
+    import tree_masked_attention_amd.api as api
+    dev = torch.device("cuda:0")
+    bf = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    if wl.kv_format == "bf16":
+        k, v = bf(wl.k_cache), bf(wl.v_cache)
+        ks = vs = None
+    else:
+        k = torch.from_numpy(wl.k_cache).to(dev)
+        v = torch.from_numpy(wl.v_cache).to(dev)
+        ks = torch.from_numpy(wl.k_scale).to(dev)
+        vs = torch.from_numpy(wl.v_scale).to(dev)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    masks, bad = api.build_mask(i32(wl.parents), i32(wl.tree_offsets),
+                                max(wl.max_nodes, 1), W)
+    out, lse = api.verify_ex(bf(wl.q), k, v, i32(wl.page_table),
+                             i32(wl.prefix_lens), i32(wl.tree_offsets), masks,
+                             wl.max_prefix_len, wl.max_nodes, wl.scale, ks, vs,
+                             num_splits=num_splits)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), lse.cpu().numpy().astype(np.float64)
+
+
+def check(wl, label, num_splits=0, **okw):
+    out, lse = run_ex(wl, num_splits)
+    ref_o, ref_l = oracle.workload_attention(wl, **okw)
+    sel = ~np.isnan(ref_l)
+    eo = np.abs(out - ref_o)[sel].max() if sel.any() else 0.0
+    el = (np.abs(lse - ref_l) / np.maximum(np.abs(ref_l), 1))[sel].max() \
+        if sel.any() else 0.0
+    say(f"  {label}: max|dout| {eo:.2e}, max rel dlse {el:.2e}")
+    assert eo <= OUT_ATOL and el <= LSE_RTOL, label
+
+
+def _case(name, seed, fmt, d, **kw):
+    kw.setdefault("num_q_heads", 8)
+    kw.setdefault("num_kv_heads", 2)
+    return make_workload(seed, name=name, kv_format=fmt, head_dim=d, **kw)
+
+
+CASES = {
+    "ragged-multi": dict(prefix_lens=[0, 77, 300, 1],
+                         tree_sizes=[1, 37, 130, 64]),
+    "gqa8": dict(prefix_lens=[513], tree_sizes=[16], num_q_heads=32,
+                 num_kv_heads=4),
+    "empty-tree-in-batch": dict(prefix_lens=[20, 40, 0], tree_sizes=[5, 0, 9]),
+    "page1": dict(prefix_lens=[70, 3], tree_sizes=[12, 7], page_size=1),
+    "page64": dict(prefix_lens=[70, 200], tree_sizes=[12, 70], page_size=64),
+    "max-tree-1024": dict(prefix_lens=[50], tree_sizes=[1024], num_q_heads=2,
+                          num_kv_heads=1, p_chain=0.7),
+    "star": dict(prefix_lens=[33], tree_sizes=[300], tree_rules="star"),
+    "long-prefix": dict(prefix_lens=[5000, 1234], tree_sizes=[3, 40]),
+    "big-key-range": dict(prefix_lens=[900], tree_sizes=[40],
+                          key_factor_range=(0.25, 4.0)),
+    # the draft head's use of the mask (JETFLOW's parallel drafter): its own
+    # short KV, a budget-256 tree, the target's head shape
+    "draft-head": dict(prefix_lens=[600, 1500], tree_sizes=[256, 256],
+                       num_q_heads=32, num_kv_heads=8),
+}
+FORMATS = [("bf16", 64), ("e4m3", 64), ("e4m3", 128)]
+
+
+@pytest.mark.parametrize("fmt,d", FORMATS, ids=lambda x: str(x))
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_variant_parity(name, fmt, d):
+    seed = sum(map(ord, name)) + d
+    say(f"[gpu] verify_ex {name} {fmt} d={d}")
+    check(_case(name, seed, fmt, d, **CASES[name]), f"{name}/{fmt}/d{d}")
+
+
+@pytest.mark.parametrize("splits", [1, 2, 5])
+@pytest.mark.parametrize("fmt,d", FORMATS, ids=lambda x: str(x))
+def test_variant_forced_splits(fmt, d, splits):
+    wl = _case("splits", 41, fmt, d, prefix_lens=[2000, 300],
+               tree_sizes=[64, 17])
+    say(f"[gpu] verify_ex splits={splits} {fmt} d={d}")
+    check(wl, f"splits{splits}/{fmt}/d{d}", num_splits=splits)
+
+
+def test_draft_head_bf16_d128_is_the_tuned_path():
+    # bf16, d = 128 through verify_ex runs tree_attn_verify's kernels
+    wl = _case("draft-head", 7, "bf16", 128, **CASES["draft-head"])
+    say("[gpu] verify_ex draft-head bf16 d=128")
+    check(wl, "draft-head/bf16/d128")
+
+
+@pytest.mark.parametrize("name", ["qwen3-30b-a3b-32x-b16-p2k",
+                                  "long-32k-4x-b256"])
+@pytest.mark.parametrize("fmt,d", [("e4m3", 128), ("bf16", 64)],
+                         ids=lambda x: str(x))
+def test_variant_full_size_sampled(name, fmt, d):
+    wl = standard_workload(name, kv_format=fmt, head_dim=d)
+    say(f"[gpu] verify_ex full size {wl.name}")
+    out, lse = run_ex(wl)
+    rng = np.random.default_rng(5)
+    seqs = [int(rng.integers(0, wl.num_seqs))]
+    heads = [int(rng.integers(0, wl.num_kv_heads))]
+    ref_o, ref_l = oracle.workload_attention(wl, seq_ids=seqs,
+                                             kv_head_ids=heads)
+    sel = ~np.isnan(ref_l)
+    eo = np.abs(out - ref_o)[sel].max()
+    el = (np.abs(lse - ref_l) / np.maximum(np.abs(ref_l), 1))[sel].max()
+    say(f"  {wl.name} seqs {seqs} kv head {heads}: max|dout| {eo:.2e}, "
+        f"max rel dlse {el:.2e}")
+    assert eo <= OUT_ATOL and el <= LSE_RTOL

@@ -44,7 +44,8 @@ def _gqa_modulo(h, hq, hkv):
     return h % hkv
 
 
-def _no_table(cache_bits, table_row, num_tokens):
+def _no_table(cache_bits, table_row, num_tokens, kv_format="bf16",
+              head_scale=None):
     ps = cache_bits.shape[1]
     t = np.arange(num_tokens)
     first = int(table_row[0])

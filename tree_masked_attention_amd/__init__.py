@@ -8,7 +8,7 @@ input generator can be imported on machines without the built library.
 
 _API_NAMES = ("build_mask", "verify", "workspace_size", "describe_plan",
               "accept", "commit_kv", "accept_commit", "build_tree",
-              "gdn_verify", "gdn_commit",
+              "gdn_verify", "gdn_commit", "verify_ex",
               "status_string",
               "abi_version", "mask_words_for", "TreeAttnError")
 

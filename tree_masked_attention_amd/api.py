@@ -74,13 +74,23 @@ _lib.tree_attn_gdn_commit.restype = ctypes.c_int
 _lib.tree_attn_gdn_commit.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i,
                                       _p, _p]
 
+_lib.tree_attn_verify_ex.restype = ctypes.c_int
+_lib.tree_attn_verify_ex.argtypes = (
+    [_p, _p, _p, _i, _p, _p, _p, _i, _i, _i, _p, _p, _p, _i, _i, _i, _i, _i,
+     _i, _i, _i, ctypes.c_float, _i, _p, _p, _p, ctypes.c_size_t, _p])
+_lib.tree_attn_workspace_size_ex.restype = ctypes.c_size_t
+_lib.tree_attn_workspace_size_ex.argtypes = [_i] * 10
+
+KV_BF16, KV_FP8_E4M3 = 0, 1
+
 EXPORTED = ("tree_attn_status_string", "tree_attn_abi_version",
             "tree_attn_build_mask", "tree_attn_workspace_size",
             "tree_attn_describe_plan", "tree_attn_verify",
             "tree_attn_verify_attend", "tree_attn_verify_merge",
             "tree_attn_accept", "tree_attn_commit_kv",
             "tree_attn_accept_commit", "tree_attn_build_tree",
-            "tree_attn_gdn_verify", "tree_attn_gdn_commit")
+            "tree_attn_gdn_verify", "tree_attn_gdn_commit",
+            "tree_attn_verify_ex", "tree_attn_workspace_size_ex")
 GDN_MAX_NODES = 128
 
 
@@ -474,3 +484,74 @@ def gdn_commit(k: torch.Tensor, u: torch.Tensor, g: torch.Tensor,
         _ptr(accept_nodes), S, accept_nodes.shape[1], H, d, _ptr(state),
         _stream(stream))
     _raise(code, "tree_attn_gdn_commit")
+
+
+def verify_ex(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+              page_table: torch.Tensor, prefix_lens: torch.Tensor,
+              tree_offsets: torch.Tensor, masks: torch.Tensor,
+              max_prefix_len: int, max_nodes: int, scale: float,
+              k_scale: Optional[torch.Tensor] = None,
+              v_scale: Optional[torch.Tensor] = None, num_splits: int = 0,
+              out: Optional[torch.Tensor] = None,
+              lse: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None,
+              stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """verify() for bf16 or FP8 E4M3 caches and head_dim 64 or 128.
+
+    q bf16 [N, Hq, d]; k_cache / v_cache bf16, or uint8 /
+    torch.float8_e4m3fn (E4M3 codes, with fp32 k_scale / v_scale [Hkv]),
+    [num_pages, page_size, Hkv, d]; the rest as for verify()."""
+    _dev(q, torch.bfloat16, "q")
+    if k_cache.dtype == torch.bfloat16:
+        kv = KV_BF16
+    elif k_cache.dtype in (torch.uint8, torch.float8_e4m3fn):
+        kv = KV_FP8_E4M3
+    else:
+        raise ValueError(f"unsupported cache dtype {k_cache.dtype}")
+    _dev(k_cache, k_cache.dtype, "k_cache")
+    _dev(v_cache, k_cache.dtype, "v_cache")
+    for t, n in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+        if t is not None:
+            _dev(t, torch.float32, n)
+    for t, dt, n in ((page_table, torch.int32, "page_table"),
+                     (prefix_lens, torch.int32, "prefix_lens"),
+                     (tree_offsets, torch.int32, "tree_offsets"),
+                     (masks, torch.int64, "masks")):
+        _dev(t, dt, n)
+    if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("q must be [N, Hq, d] and k/v caches "
+                         "[num_pages, page_size, Hkv, d]")
+    N, Hq, d = q.shape
+    num_pages, page_size, Hkv, dk = k_cache.shape
+    if dk != d:
+        raise ValueError("head_dim of q and the caches differ")
+    S = prefix_lens.numel()
+    if tree_offsets.numel() != S + 1 or page_table.dim() != 2 or \
+            page_table.shape[0] != S:
+        raise ValueError("page_table / tree_offsets do not match prefix_lens")
+    if masks.dim() != 2 or masks.shape[0] != N:
+        raise ValueError("masks must be [N, W]")
+    for t, n in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+        if t is not None and t.numel() != Hkv:
+            raise ValueError(f"{n} must have num_kv_heads entries")
+    W = masks.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((N, Hq), dtype=torch.float32, device=q.device)
+    ws_bytes = int(_lib.tree_attn_workspace_size_ex(
+        kv, S, N, Hq, Hkv, d, int(max_prefix_len), int(max_nodes), page_size,
+        int(num_splits)))
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty((ws_bytes,), dtype=torch.uint8,
+                                device=q.device)
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    code = _lib.tree_attn_verify_ex(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), kv, _ptr(k_scale),
+        _ptr(v_scale), _ptr(page_table), page_table.shape[1], num_pages,
+        page_size, _ptr(prefix_lens), _ptr(tree_offsets), _ptr(masks), W, S,
+        N, int(max_prefix_len), int(max_nodes), Hq, Hkv, d, float(scale),
+        int(num_splits), _ptr(out), _ptr(lse), _ptr(workspace), ws_len,
+        _stream(stream))
+    _raise(code, "tree_attn_verify_ex")
+    return out, lse

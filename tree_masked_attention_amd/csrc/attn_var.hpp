@@ -1,0 +1,394 @@
+// Tree-verification attention for the variants the tuned kernels
+// (attn_fwd128h.hpp, attn_fwd8.hpp) do not cover: head dimension 64, and
+// K/V pages stored in fp8 (OCP E4M3, one fp32 scale per kv head) for head
+// dimension 64 or 128.  The operation is the same as theirs -- every tree
+// node attends to its sequence's prefix and to its ancestors (JETFLOW,
+// gist.science 2606.18394, section 2 "Arquitectura Central", bullet on the
+// tree-causal mask) -- and so is the split-KV decomposition with an LSE
+// merge; JETFLOW's parallel draft head uses the same mask over its own KV.
+//
+// Design (simpler than the tuned kernels, and written for occupancy
+// instead of a deep pipeline): a workgroup of four waves owns 128 query
+// rows (GQA heads packed node-major, row = node * G + head) of one
+// (sequence, kv head) and one key split.  Per tile of 64 keys the threads
+// load the K and V rows through the page table, convert fp8 to bf16 (exact:
+// every E4M3 value is a bf16 value) and write K row-major and V transposed
+// (V^T[d][key]) to LDS, 34 KB in all, so up to four workgroups share a CU
+// and hide each other's latency.  Scores are computed transposed, S^T =
+// K Q^T (v_mfma_f32_32x32x16_bf16; the query is the MFMA column, so a lane
+// holds 16 scores of one query row), the ancestor mask is applied to the
+// tree keys in registers, the online softmax runs in base 2, and
+// O^T += V^T P^T takes the probabilities straight from the score registers
+// as the B operand (k permuted consistently in both operands).  The fp8
+// scales fold into the softmax scale (K) and the output (V).
+#pragma once
+
+#include "common.hpp"
+
+namespace tree_attn {
+
+constexpr int kVarRows = 128;   // query rows per workgroup (4 waves x 32)
+constexpr int kVarTile = 64;    // keys per tile
+constexpr int kVarThreads = 256;
+constexpr int kVarVPitch = kVarTile * 2 + 8;  // bytes per V^T row in LDS
+
+struct VarParams {
+  const __bf16* q;             // [N][Hq][D]
+  const unsigned char* k;      // [num_pages][page_size][Hkv][D] elements
+  const unsigned char* v;
+  const float* k_scale;        // [Hkv] (fp8) or null
+  const float* v_scale;
+  const int32_t* page_table;   // [S][max_pps]
+  const int32_t* prefix_lens;  // [S]
+  const int32_t* tree_offsets; // [S + 1]
+  const uint64_t* masks;       // [N][W]
+  __bf16* out;                 // [N][Hq][D]
+  float* lse;                  // [N][Hq]
+  float* part_o;               // [splits][N * Hq][D]  unnormalised O
+  float* part_ml;              // [splits][N * Hq][2]  (max, log2 units; sum)
+  int max_pps, num_pages, log2_page, W;
+  int max_tokens;  // min(max_pps * page_size, 2^30): keys the table covers
+  int S, N, Hq, Hkv, G;
+  int mblocks, splits, chunk;
+  float scale_log2;
+};
+
+typedef __attribute__((address_space(3))) u32x4 var_lds_u32x4;
+typedef __attribute__((address_space(3))) u32x2 var_lds_u32x2;
+typedef __attribute__((address_space(3))) __bf16 var_lds_bf16;
+
+__device__ __forceinline__ bf16x8 var_read16(unsigned addr) {
+  return __builtin_bit_cast(bf16x8, *(const var_lds_u32x4*)(size_t)addr);
+}
+
+// A operand whose B operand is an accumulator tile (runs of 4 keys per lane
+// half): keys cb + 4 half .. +3 and cb + 8 + 4 half .. +3 of V^T row `row`.
+__device__ __forceinline__ bf16x8 var_read_perm(unsigned arr, int row, int cb,
+                                                int half) {
+  const unsigned a = arr + row * kVarVPitch + (cb + 4 * half) * 2;
+  const u32x2 x = *(const var_lds_u32x2*)(size_t)a;
+  const u32x2 y = *(const var_lds_u32x2*)(size_t)(a + 16);
+  const u32x4 r = {x.x, x.y, y.x, y.y};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Two E4M3 codes (bytes 2 sel, 2 sel + 1 of w) -> two bf16 in one word.
+// v_cvt_pk_f32_fp8 decodes OCP E4M3 on gfx950 (checked against the format
+// definition on all 256 codes); every E4M3 value is a bf16 value, so the
+// top halves of the fp32 results are exact.
+template <bool kHi>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(w, kHi);
+  // elements through scalars: a bit cast of a vector element itself reads
+  // element 0 with this compiler
+  const float f0 = f[0], f1 = f[1];
+  return (__builtin_bit_cast(uint32_t, f0) >> 16) |
+         (__builtin_bit_cast(uint32_t, f1) & 0xffff0000u);
+}
+
+template <int D, bool FP8>
+__global__ __launch_bounds__(kVarThreads, 2) void attn_var_kernel(VarParams p) {
+  constexpr int EB = FP8 ? 1 : 2;         // bytes per cached element
+  constexpr int RB = D * EB;              // bytes per cached (token, head)
+  constexpr int CR = RB / 16;             // 16-byte chunks per row
+  constexpr int KP = D * 2 + 16;          // K row pitch in LDS (bf16)
+  constexpr int NCH = kVarTile * CR / kVarThreads;  // chunks per thread
+  constexpr int DT = D / 32;              // output tiles of 32 dims
+  constexpr int KS = D / 16;              // k-steps of the score product
+  static_assert(NCH >= 1 && kVarTile * CR % kVarThreads == 0, "tile split");
+  __shared__ __align__(16) unsigned char kl[kVarTile * KP];
+  __shared__ __align__(16) unsigned char vl[D * kVarVPitch];
+  const unsigned kb =
+      (unsigned)(size_t)(__attribute__((address_space(3))) unsigned char*)kl;
+  const unsigned vb =
+      (unsigned)(size_t)(__attribute__((address_space(3))) unsigned char*)vl;
+
+  int idx = blockIdx.x;
+  const int c = idx % p.splits;
+  idx /= p.splits;
+  const int mb = idx % p.mblocks;
+  idx /= p.mblocks;
+  const int g = idx % p.Hkv;
+  const int s = idx / p.Hkv;
+  const int n0 = p.tree_offsets[s];
+  const int B = p.tree_offsets[s + 1] - n0;
+  const int P = p.prefix_lens[s];
+  const int rows = B * p.G;
+  if (mb * kVarRows >= rows) return;
+  const int T = min(P + B, p.max_tokens);
+  const int k0 = c * p.chunk, k1 = min(T, k0 + p.chunk);
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int r = mb * kVarRows + w * 32 + col;  // this lane's query row
+  const bool valid = r < rows;
+  const int node = valid ? r / p.G : 0;
+  const int h = g * p.G + (valid ? r % p.G : 0);
+  const size_t qrow = (size_t)(n0 + node) * p.Hq + h;
+
+  // Q^T fragments: lane (row r, half) holds dims 16 ks + 8 half .. +7
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (valid) {
+      qf[ks] = *reinterpret_cast<const bf16x8*>(p.q + qrow * D + 16 * ks +
+                                                8 * half);
+    } else {
+      qf[ks] = bf16x8{};
+    }
+  }
+  const float ksc = FP8 && p.k_scale ? p.k_scale[g] : 1.f;
+  const float vsc = FP8 && p.v_scale ? p.v_scale[g] : 1.f;
+  const float sl2 = p.scale_log2 * ksc;
+  const uint64_t* mrow = p.masks + (size_t)(n0 + node) * p.W;
+
+  f32x16 oacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
+  float m = -__builtin_inff(), l = 0.f;
+
+  const int32_t* table = p.page_table + (size_t)s * p.max_pps;
+  const int pmask = (1 << p.log2_page) - 1;
+  // Staging: thread t moves 16-byte chunk ch = t % CR of NCH consecutive
+  // keys kq .. kq + NCH - 1, so that its V^T writes cover NCH keys of one
+  // dimension at once.  The next tile is loaded into registers while the
+  // current one is in use.
+  const int ch = tid % CR, kq = (tid / CR) * NCH;
+  u32x4 kc[NCH], vc[NCH];
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int key = t + kq + j;
+      kc[j] = u32x4{0u, 0u, 0u, 0u};
+      vc[j] = u32x4{0u, 0u, 0u, 0u};
+      if (key < k1) {
+        // a page id outside the pool is clamped into it (never read past)
+        const int page =
+            min(max(table[key >> p.log2_page], 0), p.num_pages - 1);
+        const size_t off =
+            (((size_t)page << p.log2_page) + (key & pmask)) * p.Hkv + g;
+        kc[j] = *reinterpret_cast<const u32x4*>(p.k + off * RB + ch * 16);
+        vc[j] = *reinterpret_cast<const u32x4*>(p.v + off * RB + ch * 16);
+      }
+    }
+  };
+  if (k0 < k1) load_tile(k0);
+  for (int t = k0; t < k1; t += kVarTile) {
+    __syncthreads();  // the previous tile's products are done
+    // ---- K rows (bf16) and V^T[d][key] to LDS
+    constexpr int DPC = 16 / EB;  // dims per chunk
+    uint32_t vt[DPC][(NCH + 1) / 2];  // V^T: NCH keys of each dim, packed
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      uint32_t vv[DPC / 2];  // this key's dims as bf16 pairs
+      if (FP8) {
+        u32x4 lo4, hi4;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const uint32_t a0 = e4m3x2_to_bf16x2<false>(kc[j][q4]);
+          const uint32_t a1 = e4m3x2_to_bf16x2<true>(kc[j][q4]);
+          if (q4 < 2) {
+            lo4[2 * q4] = a0;
+            lo4[2 * q4 + 1] = a1;
+          } else {
+            hi4[2 * q4 - 4] = a0;
+            hi4[2 * q4 - 3] = a1;
+          }
+          vv[2 * q4] = e4m3x2_to_bf16x2<false>(vc[j][q4]);
+          vv[2 * q4 + 1] = e4m3x2_to_bf16x2<true>(vc[j][q4]);
+        }
+        *(var_lds_u32x4*)(size_t)(kb + (kq + j) * KP + ch * 32) = lo4;
+        *(var_lds_u32x4*)(size_t)(kb + (kq + j) * KP + ch * 32 + 16) = hi4;
+      } else {
+        *(var_lds_u32x4*)(size_t)(kb + (kq + j) * KP + ch * 16) = kc[j];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) vv[q4] = vc[j][q4];
+      }
+      // dim e of this key -> 16-bit slot j of vt[e]
+#pragma unroll
+      for (int e = 0; e < DPC; ++e) {
+        const uint32_t x = (vv[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+        if ((j & 1) == 0) {
+          vt[e][j >> 1] = x;
+        } else {
+          vt[e][j >> 1] |= x << 16;
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < DPC; ++e) {
+      const unsigned a = vb + (DPC * ch + e) * kVarVPitch + kq * 2;
+      if (NCH == 4) {
+        *(var_lds_u32x2*)(size_t)a = u32x2{vt[e][0], vt[e][(NCH + 1) / 2 - 1]};
+      } else if (NCH == 2) {
+        *(__attribute__((address_space(3))) uint32_t*)(size_t)a = vt[e][0];
+      } else {
+        *(var_lds_bf16*)(size_t)a =
+            __builtin_bit_cast(__bf16, (unsigned short)(vt[e][0] & 0xffffu));
+      }
+    }
+    __syncthreads();
+    if (t + kVarTile < k1) load_tile(t + kVarTile);
+
+    // ---- S^T = K Q^T, two halves of 32 keys
+    f32x16 sc[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      sc[kt] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 a =
+            var_read16(kb + (kt * 32 + col) * KP + (2 * ks + half) * 16);
+        sc[kt] = mfma32x32x16(a, qf[ks], sc[kt]);
+      }
+    }
+    // ---- scale, mask (keys past the split; tree keys off the path)
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int kbase = t + kt * 32 + 4 * half;
+      // mask bits of this lane's 16 tree keys, when the half reaches them
+      uint32_t bits = 0xffffffffu;
+      const int j0 = kbase - P;  // tree index of the first key (may be < 0)
+      if (kbase + 28 >= P) {
+        bits = 0u;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          for (int e = 0; e < 4; ++e) {
+            const int j = j0 + 8 * q + e;
+            bool on;
+            if (j < 0) {
+              on = true;
+            } else {
+              on = j < B && ((mrow[j >> 6] >> (j & 63)) & 1u);
+            }
+            bits |= (on ? 1u : 0u) << (4 * q + e);
+          }
+        }
+      }
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int key = kbase + 8 * (rr >> 2) + (rr & 3);
+        const bool ok = key < k1 && ((bits >> rr) & 1u);
+        const float x = ok ? sc[kt][rr] * sl2 : -__builtin_inff();
+        sc[kt][rr] = x;
+        mx = __builtin_fmaxf(mx, x);
+      }
+    }
+    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = __builtin_fmaxf(m, mx);
+    const float mref = mnew == -__builtin_inff() ? 0.f : mnew;
+    const float alpha = fast_exp2(m - mref);
+    float ps = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const float e = fast_exp2(sc[kt][rr] - mref);
+        sc[kt][rr] = e;
+        ps += e;
+      }
+    }
+    ps += __shfl_xor(ps, 32);
+    l = l * alpha + ps;
+    m = mnew;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        bf16x8 pb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[e] = (__bf16)sc[kt][8 * s2 + e];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const bf16x8 a =
+              var_read_perm(vb, dt * 32 + col, kt * 32 + 16 * s2, half);
+          oacc[dt] = mfma32x32x16(a, pb, oacc[dt]);
+        }
+      }
+    }
+  }
+
+  // ---- epilogue: lane (row r, half) holds dims 32 dt + 8 (i/4) + 4 half +
+  // i%4 of its row
+  if (!valid) return;
+  if (p.splits == 1) {
+    const float inv = l > 0.f ? vsc / l : 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        bf16x4 o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x = oacc[dt][4 * q + e] * inv;
+          o4[e] = (__bf16)x;
+        }
+        *reinterpret_cast<bf16x4*>(p.out + qrow * D + 32 * dt + 8 * q +
+                                   4 * half) = o4;
+      }
+    }
+    if (half == 0) {
+      p.lse[qrow] = l > 0.f ? (m + __builtin_log2f(l)) * kLn2
+                            : -__builtin_inff();
+    }
+  } else {
+    const size_t rows_all = (size_t)p.N * p.Hq;
+    float* po = p.part_o + ((size_t)c * rows_all + qrow) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f32x4 o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = oacc[dt][4 * q + e] * vsc;
+        *reinterpret_cast<f32x4*>(po + 32 * dt + 8 * q + 4 * half) = o4;
+      }
+    }
+    if (half == 0) {
+      float* ml = p.part_ml + ((size_t)c * rows_all + qrow) * 2;
+      ml[0] = m;
+      ml[1] = l;
+    }
+  }
+}
+
+// LSE merge of the split partials: m* = max m_c, w_c = 2^(m_c - m*),
+// out = sum w_c O_c / sum w_c l_c, lse = ln 2 (m* + log2 sum w_c l_c).  One
+// thread per (row, 4 dims).
+template <int D>
+__global__ __launch_bounds__(256) void attn_var_merge_kernel(VarParams p) {
+  const size_t rows_all = (size_t)p.N * p.Hq;
+  const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t row = gid / (D / 4);
+  const int d4 = (int)(gid % (D / 4)) * 4;
+  if (row >= rows_all) return;
+  float mx = -__builtin_inff();
+  for (int c = 0; c < p.splits; ++c) {
+    mx = __builtin_fmaxf(mx, p.part_ml[((size_t)c * rows_all + row) * 2]);
+  }
+  const float mref = mx == -__builtin_inff() ? 0.f : mx;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  for (int c = 0; c < p.splits; ++c) {
+    const float* ml = p.part_ml + ((size_t)c * rows_all + row) * 2;
+    const float wc = fast_exp2(ml[0] - mref);
+    den += wc * ml[1];
+    acc += wc * *reinterpret_cast<const f32x4*>(
+                    p.part_o + ((size_t)c * rows_all + row) * D + d4);
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  bf16x4 o4;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(acc[e] * inv);
+  *reinterpret_cast<bf16x4*>(p.out + row * D + d4) = o4;
+  if (d4 == 0) {
+    p.lse[row] = den > 0.f ? (mx + __builtin_log2f(den)) * kLn2
+                           : -__builtin_inff();
+  }
+}
+
+}  // namespace tree_attn

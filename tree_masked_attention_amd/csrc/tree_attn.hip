@@ -12,6 +12,7 @@
 #include "attn_fwd128h.hpp"
 #include "attn_fwd8.hpp"
 #include "attn_merge.hpp"
+#include "attn_var.hpp"
 #include "common.hpp"
 #include "gdn.hpp"
 #include "mask_build.hpp"
@@ -21,7 +22,7 @@ using namespace tree_attn;
 
 namespace {
 
-constexpr int kAbiVersion = 8;
+constexpr int kAbiVersion = 9;
 constexpr int kMaxDevices = 64;
 constexpr int kMaxSplits = 256;
 constexpr int kMinKeysPerSplit = 256;
@@ -261,6 +262,73 @@ CommitParams commit_params(void* k_cache, void* v_cache,
   cp.slices = (2 * cp.pieces + threads - 1) / threads;
   cp.token_bytes = token_bytes;
   return cp;
+}
+
+// Plan of the variant kernel (head dim 64, or fp8 K/V): 128 query rows per
+// workgroup, up to four workgroups per CU, so the key range is cut until
+// the grid offers about four workgroups per CU (at least 256 keys per
+// split, at most kMaxSplits splits).
+struct VarPlan {
+  int mblocks = 0;
+  int splits = 1;
+  int chunk = 0;
+  long long grid = 0;
+  size_t part_ml_off = 0;
+  size_t ws_bytes = 0;
+};
+
+int make_var_plan(int S, int N, int Hq, int Hkv, int D, int max_prefix_len,
+                  int max_nodes, int req_splits, int cus, VarPlan* out) {
+  VarPlan pl;
+  const long long G = Hq / Hkv;
+  const long long rows = G * max_nodes;
+  const long long T = std::max(1LL, (long long)max_prefix_len + max_nodes);
+  pl.mblocks = (int)std::max(1LL, (rows + kVarRows - 1) / kVarRows);
+  const long long units0 = (long long)S * Hkv * pl.mblocks;
+  long long splits = req_splits;
+  if (splits <= 0) {
+    splits = (4LL * cus + units0 - 1) / std::max(1LL, units0);
+    splits = std::min(splits, std::max(1LL, T / kMinKeysPerSplit));
+  }
+  splits = std::min<long long>(std::max(1LL, splits), kMaxSplits);
+  long long chunk = (T + splits - 1) / splits;
+  chunk = (chunk + kVarTile - 1) / kVarTile * kVarTile;
+  splits = (T + chunk - 1) / chunk;
+  pl.splits = (int)splits;
+  pl.chunk = (int)chunk;
+  pl.grid = units0 * splits;
+  if (pl.grid > 0x7fffffffLL) return TREE_ATTN_ERR_UNSUPPORTED;
+  if (splits > 1) {
+    const size_t rows_all = (size_t)N * Hq * splits;
+    pl.part_ml_off = align_up(rows_all * D * sizeof(float), 256);
+    pl.ws_bytes = pl.part_ml_off + align_up(rows_all * 2 * sizeof(float), 256);
+  }
+  *out = pl;
+  return TREE_ATTN_OK;
+}
+
+int check_var_sizes(int kv_dtype, int S, int N, int Hq, int Hkv, int D,
+                    int max_prefix_len, int max_nodes, int page_size,
+                    int num_splits) {
+  if (S < 0 || N < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 ||
+      max_prefix_len < 0 || max_nodes < 0 || num_splits < 0 ||
+      Hq % Hkv != 0) {
+    return TREE_ATTN_ERR_SHAPE;
+  }
+  if (!is_pow2(page_size) || page_size > 4096) return TREE_ATTN_ERR_SHAPE;
+  if ((D != 64 && D != 128) ||
+      (kv_dtype != TREE_ATTN_KV_BF16 && kv_dtype != TREE_ATTN_KV_FP8_E4M3) ||
+      max_nodes > TREE_ATTN_MAX_NODES ||
+      (long long)max_prefix_len + max_nodes > (1LL << 30)) {
+    return TREE_ATTN_ERR_UNSUPPORTED;
+  }
+  return TREE_ATTN_OK;
+}
+
+template <int D, bool FP8>
+void launch_var(const VarPlan& pl, const VarParams& vp, hipStream_t hs) {
+  hipLaunchKernelGGL((attn_var_kernel<D, FP8>), dim3((unsigned)pl.grid),
+                     dim3(kVarThreads), 0, hs, vp);
 }
 
 // Phases of a verify call: the split-KV + tree pass, then the LSE merge.
@@ -730,6 +798,132 @@ int tree_attn_gdn_commit(const void* k, const float* u, const float* g,
                      dim3(kGdnThreads), 0,
                      reinterpret_cast<hipStream_t>(stream), cp);
   return hipGetLastError() == hipSuccess ? TREE_ATTN_OK : TREE_ATTN_ERR_HIP;
+}
+
+size_t tree_attn_workspace_size_ex(int32_t kv_dtype, int32_t num_seqs,
+                                   int32_t total_nodes, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t max_prefix_len, int32_t max_nodes,
+                                   int32_t page_size, int32_t num_splits) {
+  if (kv_dtype == TREE_ATTN_KV_BF16 && head_dim == kHeadDim) {
+    return tree_attn_workspace_size(num_seqs, total_nodes, num_q_heads,
+                                    num_kv_heads, head_dim, max_prefix_len,
+                                    max_nodes, page_size, num_splits);
+  }
+  if (check_var_sizes(kv_dtype, num_seqs, total_nodes, num_q_heads,
+                      num_kv_heads, head_dim, max_prefix_len, max_nodes,
+                      page_size, num_splits) != TREE_ATTN_OK ||
+      num_seqs == 0 || total_nodes == 0) {
+    return 0;
+  }
+  VarPlan pl;
+  if (make_var_plan(num_seqs, total_nodes, num_q_heads, num_kv_heads,
+                    head_dim, max_prefix_len, max_nodes, num_splits,
+                    cu_count(), &pl) != TREE_ATTN_OK) {
+    return 0;
+  }
+  return pl.ws_bytes;
+}
+
+int tree_attn_verify_ex(const void* q, const void* k_cache,
+                        const void* v_cache, int32_t kv_dtype,
+                        const float* k_scale, const float* v_scale,
+                        const int32_t* page_table, int32_t max_pages_per_seq,
+                        int32_t num_pages, int32_t page_size,
+                        const int32_t* prefix_lens,
+                        const int32_t* tree_offsets, const uint64_t* masks,
+                        int32_t mask_words, int32_t num_seqs,
+                        int32_t total_nodes, int32_t max_prefix_len,
+                        int32_t max_nodes, int32_t num_q_heads,
+                        int32_t num_kv_heads, int32_t head_dim, float scale,
+                        int32_t num_splits, void* out, float* lse,
+                        void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  if (kv_dtype == TREE_ATTN_KV_BF16 && head_dim == kHeadDim) {
+    return run_verify(kPhaseAttend | kPhaseMerge, q, k_cache, v_cache,
+                      page_table, max_pages_per_seq, num_pages, page_size,
+                      prefix_lens, tree_offsets, masks, mask_words, num_seqs,
+                      total_nodes, max_prefix_len, max_nodes, num_q_heads,
+                      num_kv_heads, head_dim, scale, num_splits, out, lse,
+                      workspace, workspace_bytes, stream);
+  }
+  int st = check_var_sizes(kv_dtype, num_seqs, total_nodes, num_q_heads,
+                           num_kv_heads, head_dim, max_prefix_len, max_nodes,
+                           page_size, num_splits);
+  if (st != TREE_ATTN_OK) return st;
+  if (mask_words < 1 || max_pages_per_seq < 0 || num_pages < 0) {
+    return TREE_ATTN_ERR_SHAPE;
+  }
+  if ((long long)mask_words * 64 < max_nodes) return TREE_ATTN_ERR_SHAPE;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return TREE_ATTN_ERR_SHAPE;
+  if (num_seqs == 0 || total_nodes == 0) return TREE_ATTN_OK;
+  if (num_pages < 1 || max_pages_per_seq < 1) return TREE_ATTN_ERR_SHAPE;
+  if (!q || !k_cache || !v_cache || !page_table || !prefix_lens ||
+      !tree_offsets || !masks || !out || !lse) {
+    return TREE_ATTN_ERR_NULL;
+  }
+  VarPlan pl;
+  st = make_var_plan(num_seqs, total_nodes, num_q_heads, num_kv_heads,
+                     head_dim, max_prefix_len, max_nodes, num_splits,
+                     cu_count(), &pl);
+  if (st != TREE_ATTN_OK) return st;
+  if (pl.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < pl.ws_bytes ||
+        reinterpret_cast<uintptr_t>(workspace) % 256 != 0) {
+      return TREE_ATTN_ERR_WORKSPACE;
+    }
+  }
+  VarParams vp;
+  vp.q = static_cast<const __bf16*>(q);
+  vp.k = static_cast<const unsigned char*>(k_cache);
+  vp.v = static_cast<const unsigned char*>(v_cache);
+  vp.k_scale = k_scale;
+  vp.v_scale = v_scale;
+  vp.page_table = page_table;
+  vp.prefix_lens = prefix_lens;
+  vp.tree_offsets = tree_offsets;
+  vp.masks = masks;
+  vp.out = static_cast<__bf16*>(out);
+  vp.lse = lse;
+  vp.part_o = static_cast<float*>(workspace);
+  vp.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                        pl.part_ml_off);
+  vp.max_pps = max_pages_per_seq;
+  vp.num_pages = num_pages;
+  vp.max_tokens = (int)std::min<long long>(
+      (long long)max_pages_per_seq * page_size, 1LL << 30);
+  vp.log2_page = ilog2(page_size);
+  vp.W = mask_words;
+  vp.S = num_seqs;
+  vp.N = total_nodes;
+  vp.Hq = num_q_heads;
+  vp.Hkv = num_kv_heads;
+  vp.G = num_q_heads / num_kv_heads;
+  vp.mblocks = pl.mblocks;
+  vp.splits = pl.splits;
+  vp.chunk = pl.chunk;
+  vp.scale_log2 = scale * kLog2e;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const bool fp8 = kv_dtype == TREE_ATTN_KV_FP8_E4M3;
+  if (head_dim == 64) {
+    if (fp8) launch_var<64, true>(pl, vp, hs); else launch_var<64, false>(pl, vp, hs);
+  } else {
+    if (fp8) launch_var<128, true>(pl, vp, hs); else launch_var<128, false>(pl, vp, hs);
+  }
+  if (hipGetLastError() != hipSuccess) return TREE_ATTN_ERR_HIP;
+  if (pl.splits > 1) {
+    const long long work = (long long)total_nodes * num_q_heads * (head_dim / 4);
+    const unsigned mgrid = (unsigned)((work + 255) / 256);
+    if (head_dim == 64) {
+      hipLaunchKernelGGL(attn_var_merge_kernel<64>, dim3(mgrid), dim3(256), 0,
+                         hs, vp);
+    } else {
+      hipLaunchKernelGGL(attn_var_merge_kernel<128>, dim3(mgrid), dim3(256),
+                         0, hs, vp);
+    }
+    if (hipGetLastError() != hipSuccess) return TREE_ATTN_ERR_HIP;
+  }
+  return TREE_ATTN_OK;
 }
 
 }  // extern "C"

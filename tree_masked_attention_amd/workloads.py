@@ -106,6 +106,22 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return out.reshape(x.shape)
 
 
+def quantize_e4m3(x: np.ndarray):
+    """Per-kv-head FP8 E4M3 quantisation of a cache [pages, slots, Hkv, d]:
+    scale_h = 2^ceil(log2(amax_h / 448)) (a power of two, so a stored code
+    times its scale is exact in bf16 and fp32), codes = E4M3(x / scale_h)
+    with round-to-nearest-even (torch's float8_e4m3fn conversion).  Returns
+    (uint8 codes, fp32 scales [Hkv])."""
+    import torch
+    amax = np.abs(x).max(axis=(0, 1, 3)).astype(np.float64)
+    amax = np.maximum(amax, 1e-30)
+    scale = np.exp2(np.ceil(np.log2(amax / 448.0))).astype(np.float32)
+    y = torch.from_numpy(np.ascontiguousarray(x / scale[None, None, :, None],
+                                              dtype=np.float32))
+    codes = y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return codes, scale
+
+
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     """Widen bf16 bit patterns (uint16) to float32 exactly."""
     b = np.ascontiguousarray(b, dtype=np.uint16)
@@ -167,6 +183,9 @@ class Workload:
     head_dim: int
     page_size: int
     scale: float
+    kv_format: str = "bf16"            # "bf16" (uint16 bits) or "e4m3" (uint8)
+    k_scale: Optional[np.ndarray] = None  # fp32 [Hkv] for "e4m3"
+    v_scale: Optional[np.ndarray] = None
 
     @property
     def num_seqs(self) -> int:
@@ -212,6 +231,7 @@ def make_workload(seed: int, prefix_lens: Sequence[int] | None = None,
                   prefix_range: Optional[tuple] = None,
                   num_seqs: Optional[int] = None,
                   extra_pages: int = 0,
+                  kv_format: str = "bf16",
                   name: str = "custom") -> Workload:
     """Draw one synthetic workload.
 
@@ -277,11 +297,19 @@ def make_workload(seed: int, prefix_lens: Sequence[int] | None = None,
         fac = _bulk_uniform(ss_f, (num_pages, page_size), lo, hi)
         k32 *= fac[:, :, None, None]
     v32 = _bulk_normal(ss_v, kv_shape)
+    k_scale = v_scale = None
+    if kv_format == "e4m3":
+        k_cache, k_scale = quantize_e4m3(k32)
+        v_cache, v_scale = quantize_e4m3(v32)
+    elif kv_format == "bf16":
+        k_cache, v_cache = f32_to_bf16_bits(k32), f32_to_bf16_bits(v32)
+    else:
+        raise ValueError(f"unknown kv_format {kv_format!r}")
     wl = Workload(
         name=name,
         q=f32_to_bf16_bits(q32),
-        k_cache=f32_to_bf16_bits(k32),
-        v_cache=f32_to_bf16_bits(v32),
+        k_cache=k_cache,
+        v_cache=v_cache,
         page_table=table,
         prefix_lens=prefix,
         tree_offsets=offsets,
@@ -291,6 +319,9 @@ def make_workload(seed: int, prefix_lens: Sequence[int] | None = None,
         head_dim=head_dim,
         page_size=page_size,
         scale=1.0 / math.sqrt(head_dim),
+        kv_format=kv_format,
+        k_scale=k_scale,
+        v_scale=v_scale,
     )
     return wl
 
@@ -426,6 +457,13 @@ def gdn_trees(tree_sizes: Sequence[int], rules: Sequence[str] | str,
     return parents, offsets
 
 
-def standard_workload(name: str) -> Workload:
+def standard_workload(name: str, kv_format: str = "bf16",
+                      head_dim: int = 128) -> Workload:
+    """One of the standard workloads; kv_format / head_dim give the same
+    workload with an FP8 E4M3 cache or head dimension 64 (the name gets a
+    suffix, e.g. "qwen3-8b-b256-p4k+e4m3+d64")."""
     seed, kw = STANDARD[name]
-    return make_workload(seed, name=name, **kw)
+    full = name + ("" if kv_format == "bf16" else "+" + kv_format) + \
+        ("" if head_dim == 128 else f"+d{head_dim}")
+    return make_workload(seed, name=full, kv_format=kv_format,
+                         head_dim=head_dim, **kw)
