@@ -688,9 +688,9 @@ __global__ __launch_bounds__(kGdnThreads, 1) void gdn_verify_kernel(
 // State commit.  One workgroup per (sequence, head) updates S0 in place to
 // S_n = gamma_n S0 + sum_j e^{G_n - G_{p_j}} k_{p_j} u_{p_j}^T over the
 // accepted path p_1 .. p_n (the order tree_attn_accept writes it in).
-// Thread t owns 4 consecutive columns 4 (t % 32) .. +3 of the rows
-// t / 32 + 8 m; the path's k (fp32) and u (scaled by its decay to the end
-// of the path) pass through LDS 32 nodes at a time.
+// Thread t owns 4 consecutive columns of 16 consecutive rows; the path's
+// k (fp32) and u (scaled by its decay to the end of the path) pass through
+// LDS 32 nodes at a time.
 
 constexpr int kGdnCommitChunk = 32;
 constexpr int kGdnMaxPath = 1024;
@@ -721,27 +721,35 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_commit_kernel(
   const int B = p.tree_offsets[s + 1] - n0;
   const int tau = min(max(p.accept_len[s], 0), min(p.max_nodes, kGdnMaxPath));
   if (tau == 0) return;  // nothing accepted: the state stays S0
-  const int32_t* path = p.accept_nodes + (size_t)s * p.max_nodes;
-  for (int j = tid; j < tau; j += kGdnThreads) {
-    const int v = path[j];
-    nd[j] = (v >= 0 && v < B) ? n0 + v : -1;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    // suffix sums of g from the end of the path
-    float acc = 0.f;
-    for (int j = tau - 1; j >= 0; --j) {
-      cf[j] = fast_exp2(acc * kLog2e);
-      if (nd[j] >= 0) acc += p.g[(size_t)nd[j] * H + h];
-    }
-    gam_n = fast_exp2(acc * kLog2e);
-  }
-  const int c4 = (tid & 31) * 4, r0 = tid >> 5;
+  // thread t owns rows 16 (t / 32) .. +15, columns 4 (t % 32) .. +3: a row
+  // of the state is read and written by 32 consecutive threads (512
+  // bytes); its loads go out first, beside the path's
+  const int c4 = (tid & 31) * 4, r0 = (tid >> 5) * 16;
   float* st = p.state + ((size_t)s * H + h) * kHeadDim * kHeadDim;
   f32x4 acc[16];
 #pragma unroll
   for (int m = 0; m < 16; ++m) {
-    acc[m] = *reinterpret_cast<const f32x4*>(st + (r0 + 8 * m) * kHeadDim + c4);
+    acc[m] = *reinterpret_cast<const f32x4*>(st + (r0 + m) * kHeadDim + c4);
+  }
+  const int32_t* path = p.accept_nodes + (size_t)s * p.max_nodes;
+  // the path's nodes and their log-decays, read in parallel (cf holds g
+  // until the suffix sums replace it)
+  for (int j = tid; j < tau; j += kGdnThreads) {
+    const int v = path[j];
+    const int n = (v >= 0 && v < B) ? n0 + v : -1;
+    nd[j] = n;
+    cf[j] = n >= 0 ? p.g[(size_t)n * H + h] : 0.f;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    // suffix sums of g from the end of the path, over LDS
+    float gsum = 0.f;
+    for (int j = tau - 1; j >= 0; --j) {
+      const float gj = cf[j];
+      cf[j] = fast_exp2(gsum * kLog2e);
+      gsum += gj;
+    }
+    gam_n = fast_exp2(gsum * kLog2e);
   }
   __syncthreads();
   const float gn = gam_n;
@@ -750,28 +758,56 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_commit_kernel(
 
   for (int j0 = 0; j0 < tau; j0 += kGdnCommitChunk) {
     const int nc = min(kGdnCommitChunk, tau - j0);
-    for (int x = tid; x < kGdnCommitChunk * kHeadDim; x += kGdnThreads) {
-      const int jj = x >> 7, e = x & 127;
-      float kv = 0.f, uv = 0.f;
+    // 32 nodes x (16 k chunks + 32 u chunks) of 16 bytes, six per thread,
+    // all loads issued before the LDS writes
+    constexpr int kChunks = kGdnCommitChunk * 48 / kGdnThreads;
+    u32x4 raw[kChunks];
+#pragma unroll
+    for (int q = 0; q < kChunks; ++q) {
+      const int x = tid + kGdnThreads * q;
+      const int jj = x / 48, ch = x % 48;
+      raw[q] = u32x4{0u, 0u, 0u, 0u};
       if (jj < nc && nd[j0 + jj] >= 0) {
-        const size_t o = ((size_t)nd[j0 + jj] * H + h) * kHeadDim + e;
-        kv = (float)p.k[o];
-        uv = p.u[o] * cf[j0 + jj];
+        const size_t o = ((size_t)nd[j0 + jj] * H + h) * kHeadDim;
+        raw[q] = ch < 16
+            ? *reinterpret_cast<const u32x4*>(p.k + o + ch * 8)
+            : *reinterpret_cast<const u32x4*>(p.u + o + (ch - 16) * 4);
       }
-      kc[jj][e] = kv;
-      uc[jj][e] = uv;
+    }
+#pragma unroll
+    for (int q = 0; q < kChunks; ++q) {
+      const int x = tid + kGdnThreads * q;
+      const int jj = x / 48, ch = x % 48;
+      if (ch < 16) {
+        // 8 bf16 of k -> fp32
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t w32 = raw[q][e];
+          kc[jj][ch * 8 + 2 * e] = __builtin_bit_cast(float, w32 << 16);
+          kc[jj][ch * 8 + 2 * e + 1] =
+              __builtin_bit_cast(float, w32 & 0xffff0000u);
+        }
+      } else {
+        const float c = jj < nc ? cf[j0 + jj] : 0.f;
+        f32x4 uv = __builtin_bit_cast(f32x4, raw[q]);
+        *reinterpret_cast<f32x4*>(&uc[jj][(ch - 16) * 4]) = uv * c;
+      }
     }
     __syncthreads();
     for (int jj = 0; jj < nc; ++jj) {
       const f32x4 uv = *reinterpret_cast<const f32x4*>(&uc[jj][c4]);
 #pragma unroll
-      for (int m = 0; m < 16; ++m) acc[m] += kc[jj][r0 + 8 * m] * uv;
+      for (int m4 = 0; m4 < 4; ++m4) {
+        const f32x4 kv = *reinterpret_cast<const f32x4*>(&kc[jj][r0 + 4 * m4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[4 * m4 + e] += kv[e] * uv;
+      }
     }
     __syncthreads();
   }
 #pragma unroll
   for (int m = 0; m < 16; ++m) {
-    *reinterpret_cast<f32x4*>(st + (r0 + 8 * m) * kHeadDim + c4) = acc[m];
+    *reinterpret_cast<f32x4*>(st + (r0 + m) * kHeadDim + c4) = acc[m];
   }
 }
 
