@@ -498,8 +498,9 @@ int tree_attn_gdn_commit(const void* k, const float* u, const float* g,
  * With bf16 and head_dim 128 this is exactly tree_attn_verify (the same
  * kernels).  The other combinations run a separate kernel (128 query rows
  * per workgroup, fp8 converted to bf16 exactly on its way into LDS, bf16
- * matrix cores, fp32 accumulation, split partials in fp32); its workspace
- * size comes from tree_attn_workspace_size_ex.
+ * matrix cores, fp32 accumulation, split partials normalised by their
+ * own row sum in fp16, as for tree_attn_verify, so |v| * scale must stay
+ * below 65504); its workspace size comes from tree_attn_workspace_size_ex.
  *
  * Host-side errors: as tree_attn_verify; ERR_UNSUPPORTED also for
  * head_dim not 64 or 128 and for an unknown kv_dtype.

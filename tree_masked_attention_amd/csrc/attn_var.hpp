@@ -20,7 +20,9 @@
 // tree keys in registers, the online softmax runs in base 2, and
 // O^T += V^T P^T takes the probabilities straight from the score registers
 // as the B operand (k permuted consistently in both operands).  The fp8
-// scales fold into the softmax scale (K) and the output (V).
+// scales fold into the softmax scale (K) and the output (V).  A split
+// writes its output normalised by its own row sum in fp16 (a convex
+// combination of V rows, so within V's range) and (max, sum) in fp32.
 #pragma once
 
 #include "common.hpp"
@@ -44,7 +46,7 @@ struct VarParams {
   const uint64_t* masks;       // [N][W]
   __bf16* out;                 // [N][Hq][D]
   float* lse;                  // [N][Hq]
-  float* part_o;               // [splits][N * Hq][D]  unnormalised O
+  _Float16* part_o;            // [splits][N * Hq][D]  the split's O / its l
   float* part_ml;              // [splits][N * Hq][2]  (max, log2 units; sum)
   int max_pps, num_pages, log2_page, W;
   int max_tokens;  // min(max_pps * page_size, 2^30): keys the table covers
@@ -337,15 +339,16 @@ __global__ __launch_bounds__(kVarThreads, 2) void attn_var_kernel(VarParams p) {
     }
   } else {
     const size_t rows_all = (size_t)p.N * p.Hq;
-    float* po = p.part_o + ((size_t)c * rows_all + qrow) * D;
+    _Float16* po = p.part_o + ((size_t)c * rows_all + qrow) * D;
+    const float inv = l > 0.f ? vsc / l : 0.f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        f32x4 o4;
+        f16x4 o4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o4[e] = oacc[dt][4 * q + e] * vsc;
-        *reinterpret_cast<f32x4*>(po + 32 * dt + 8 * q + 4 * half) = o4;
+        for (int e = 0; e < 4; ++e) o4[e] = to_f16_sat(oacc[dt][4 * q + e] * inv);
+        *reinterpret_cast<f16x4*>(po + 32 * dt + 8 * q + 4 * half) = o4;
       }
     }
     if (half == 0) {
@@ -356,9 +359,9 @@ __global__ __launch_bounds__(kVarThreads, 2) void attn_var_kernel(VarParams p) {
   }
 }
 
-// LSE merge of the split partials: m* = max m_c, w_c = 2^(m_c - m*),
-// out = sum w_c O_c / sum w_c l_c, lse = ln 2 (m* + log2 sum w_c l_c).  One
-// thread per (row, 4 dims).
+// LSE merge of the split partials: m* = max m_c, w_c = l_c 2^(m_c - m*),
+// out = sum w_c O'_c / sum w_c with O'_c = O_c / l_c, lse = ln 2 (m* +
+// log2 sum w_c).  One thread per (row, 4 dims).
 template <int D>
 __global__ __launch_bounds__(256) void attn_var_merge_kernel(VarParams p) {
   const size_t rows_all = (size_t)p.N * p.Hq;
@@ -375,10 +378,12 @@ __global__ __launch_bounds__(256) void attn_var_merge_kernel(VarParams p) {
   float den = 0.f;
   for (int c = 0; c < p.splits; ++c) {
     const float* ml = p.part_ml + ((size_t)c * rows_all + row) * 2;
-    const float wc = fast_exp2(ml[0] - mref);
-    den += wc * ml[1];
-    acc += wc * *reinterpret_cast<const f32x4*>(
-                    p.part_o + ((size_t)c * rows_all + row) * D + d4);
+    const float wc = fast_exp2(ml[0] - mref) * ml[1];
+    den += wc;
+    const f16x4 o = *reinterpret_cast<const f16x4*>(
+        p.part_o + ((size_t)c * rows_all + row) * D + d4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += wc * (float)o[e];
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
   bf16x4 o4;

@@ -265,9 +265,10 @@ CommitParams commit_params(void* k_cache, void* v_cache,
 }
 
 // Plan of the variant kernel (head dim 64, or fp8 K/V): 128 query rows per
-// workgroup, up to four workgroups per CU, so the key range is cut until
-// the grid offers about four workgroups per CU (at least 256 keys per
-// split, at most kMaxSplits splits).
+// workgroup, up to four workgroups per CU; the key range is cut until the
+// grid offers about two workgroups per CU (at least 256 keys per split, at
+// most kMaxSplits splits) -- more splits would cost more in partials than
+// they gain in occupancy.
 struct VarPlan {
   int mblocks = 0;
   int splits = 1;
@@ -287,7 +288,7 @@ int make_var_plan(int S, int N, int Hq, int Hkv, int D, int max_prefix_len,
   const long long units0 = (long long)S * Hkv * pl.mblocks;
   long long splits = req_splits;
   if (splits <= 0) {
-    splits = (4LL * cus + units0 - 1) / std::max(1LL, units0);
+    splits = (2LL * cus + units0 - 1) / std::max(1LL, units0);
     splits = std::min(splits, std::max(1LL, T / kMinKeysPerSplit));
   }
   splits = std::min<long long>(std::max(1LL, splits), kMaxSplits);
@@ -300,7 +301,7 @@ int make_var_plan(int S, int N, int Hq, int Hkv, int D, int max_prefix_len,
   if (pl.grid > 0x7fffffffLL) return TREE_ATTN_ERR_UNSUPPORTED;
   if (splits > 1) {
     const size_t rows_all = (size_t)N * Hq * splits;
-    pl.part_ml_off = align_up(rows_all * D * sizeof(float), 256);
+    pl.part_ml_off = align_up(rows_all * D * sizeof(_Float16), 256);
     pl.ws_bytes = pl.part_ml_off + align_up(rows_all * 2 * sizeof(float), 256);
   }
   *out = pl;
@@ -885,7 +886,7 @@ int tree_attn_verify_ex(const void* q, const void* k_cache,
   vp.masks = masks;
   vp.out = static_cast<__bf16*>(out);
   vp.lse = lse;
-  vp.part_o = static_cast<float*>(workspace);
+  vp.part_o = static_cast<_Float16*>(workspace);
   vp.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                         pl.part_ml_off);
   vp.max_pps = max_pages_per_seq;
