@@ -156,7 +156,21 @@ int tree_attn_describe_plan(int32_t num_seqs, int32_t total_nodes,
  *   out           dev bf16 [total_nodes, num_q_heads, head_dim]  (output)
  *   lse           dev fp32 [total_nodes, num_q_heads], natural log (output)
  *   workspace     dev scratch of tree_attn_workspace_size(...) bytes, 256-B
- *                 aligned; may be NULL when that size is 0
+ *                 aligned; may be NULL when that size is 0.  Owned by the
+ *                 caller and reusable across calls of any sizes, one call
+ *                 at a time (calls that overlap on one workspace race).
+ *                 Its first 64 KB hold arrival counters: they must be zero
+ *                 before the workspace's first use (e.g. hipMemset once
+ *                 after allocation), and every call that completes leaves
+ *                 them at zero.  Nonzero counters give wrong output, never
+ *                 a hang or an access outside the buffers.
+ *
+ * Launches.  One attention launch.  With more than one split, every split
+ * workgroup leaves its partial in the workspace and the last one of a row
+ * block to finish (a device-scope counter, no waiting) merges the block's
+ * partials into out and lse.  Sizes with more than 16384 (sequence, kv
+ * head, row block) triples merge in a second launch instead
+ * (tree_attn_verify_merge); the results are the same bits either way.
  *
  * Precision.  Scores, softmax and the P*V products accumulate in fp32
  * (P rounded to bf16 for the matrix cores).  When the key range is split
@@ -198,6 +212,7 @@ int tree_attn_verify(const void* q, const void* k_cache, const void* v_cache,
  * out and lse (log-sum-exp merge), and launches nothing when the plan has
  * one split.  _attend followed by _merge on the same stream, with the same
  * arguments and workspace, gives exactly the results of tree_attn_verify.
+ * Neither touches the workspace's arrival counters.
  */
 int tree_attn_verify_attend(
     const void* q, const void* k_cache, const void* v_cache,
@@ -521,7 +536,8 @@ int tree_attn_verify_ex(const void* q, const void* k_cache,
                         void* stream);
 
 /* Workspace bytes tree_attn_verify_ex needs for these sizes (0: none, or
- * sizes it would reject). */
+ * sizes it would reject).  Same layout and rules as tree_attn_verify's
+ * (the first 64 KB are the counter area), so one workspace serves both. */
 size_t tree_attn_workspace_size_ex(int32_t kv_dtype, int32_t num_seqs,
                                    int32_t total_nodes, int32_t num_q_heads,
                                    int32_t num_kv_heads, int32_t head_dim,

@@ -314,3 +314,60 @@ def test_attend_then_merge_equals_verify(splits):
     torch.cuda.synchronize()
     assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
     assert torch.equal(lse1, lse2)
+
+
+def test_one_launch_merge_reuses_workspace():
+    # One zero-filled workspace for a run of calls of different shapes,
+    # kernels (128 and 256 rows per workgroup) and split counts: every call
+    # gives the bits of the two-launch form (attention kernel writing the
+    # partials, then the merge kernel) and leaves the arrival counters at
+    # zero for the next one.
+    import tree_masked_attention_amd.api as api
+    cases = [
+        (_case("reuse-a", 150, prefix_lens=[300, 77, 1500],
+               tree_sizes=[40, 9, 70]), 3),
+        (_case("reuse-w8", 151, prefix_lens=[9000, 8300],
+               tree_sizes=[64, 90], num_q_heads=16, num_kv_heads=4), 2),
+        (_case("reuse-b", 152, prefix_lens=[2000, 0, 5],
+               tree_sizes=[128, 31, 1]), 0),
+        (_case("reuse-a2", 153, prefix_lens=[300, 77, 1500],
+               tree_sizes=[40, 9, 70]), 7),
+    ]
+    sizes = []
+    for wl, splits in cases:
+        sizes.append(api.workspace_size(wl.num_seqs, wl.total_nodes,
+                                        wl.num_q_heads, wl.num_kv_heads,
+                                        wl.head_dim, wl.max_prefix_len,
+                                        wl.max_nodes, wl.page_size, splits))
+    ws = torch.zeros((max(sizes),), dtype=torch.uint8, device="cuda:0")
+    for (wl, splits), nbytes in zip(cases, sizes):
+        plan = api.describe_plan(wl.num_seqs, wl.total_nodes, wl.num_q_heads,
+                                 wl.num_kv_heads, wl.head_dim,
+                                 wl.max_prefix_len, wl.max_nodes,
+                                 wl.page_size, splits)
+        say(f"[gpu] workspace reuse {wl.name}: plan {plan}")
+        assert plan["splits"] > 1
+        dev = device_inputs(wl)
+        masks, _ = api.build_mask(dev["parents"], dev["tree_offsets"],
+                                  wl.max_nodes, wl.mask_words())
+        args = (dev["q"], dev["k_cache"], dev["v_cache"], dev["page_table"],
+                dev["prefix_lens"], dev["tree_offsets"], masks,
+                wl.max_prefix_len, wl.max_nodes, wl.scale)
+        out1, lse1 = api.verify(*args, num_splits=splits, workspace=ws)
+        ws2 = torch.zeros((nbytes,), dtype=torch.uint8, device="cuda:0")
+        out2 = torch.empty_like(out1)
+        lse2 = torch.empty_like(lse1)
+        api.verify(*args, num_splits=splits, out=out2, lse=lse2,
+                   workspace=ws2, phase="attend")
+        api.verify(*args, num_splits=splits, out=out2, lse=lse2,
+                   workspace=ws2, phase="merge")
+        torch.cuda.synchronize()
+        assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+        assert torch.equal(lse1, lse2)
+        assert int(ws[:65536].count_nonzero()) == 0, "counters left set"
+        ref_out, ref_lse = oracle.workload_attention(wl)
+        eo, el = errors(out1.float().cpu().numpy().astype(np.float64),
+                        lse1.cpu().numpy().astype(np.float64), ref_out,
+                        ref_lse)
+        say(f"  max|dout| {eo:.2e}, lse rel {el:.2e}")
+        assert eo <= 2e-2 and el <= 1e-3

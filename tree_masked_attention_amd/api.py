@@ -218,7 +218,9 @@ def verify(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     build_mask).  Returns (out bf16 [N, Hq, d], lse fp32 [N, Hq]).
     phase: "both" (tree_attn_verify), or "attend" / "merge" for its two
     launches (tree_attn_verify_attend / _merge; pass the same out, lse and
-    workspace to both).
+    workspace to both).  A workspace passed in must be zero-filled before
+    its first use (its first bytes are the split launch's arrival counters,
+    which every call leaves at zero); one allocated here is.
     """
     for t, dt, n in ((q, torch.bfloat16, "q"), (k_cache, torch.bfloat16, "k_cache"),
                      (v_cache, torch.bfloat16, "v_cache"),
@@ -248,7 +250,7 @@ def verify(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     ws_bytes = workspace_size(S, N, Hq, Hkv, d, max_prefix_len, max_nodes,
                               page_size, num_splits)
     if workspace is None and ws_bytes > 0:
-        workspace = torch.empty((ws_bytes,), dtype=torch.uint8,
+        workspace = torch.zeros((ws_bytes,), dtype=torch.uint8,
                                 device=q.device)
     ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
     fn = {"both": _lib.tree_attn_verify,
@@ -543,7 +545,7 @@ def verify_ex(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         kv, S, N, Hq, Hkv, d, int(max_prefix_len), int(max_nodes), page_size,
         int(num_splits)))
     if workspace is None and ws_bytes > 0:
-        workspace = torch.empty((ws_bytes,), dtype=torch.uint8,
+        workspace = torch.zeros((ws_bytes,), dtype=torch.uint8,
                                 device=q.device)
     ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
     code = _lib.tree_attn_verify_ex(

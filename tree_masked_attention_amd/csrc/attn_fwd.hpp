@@ -16,10 +16,12 @@
 // the key range [0, P_s + B_s).  The tree keys are the last B_s positions
 // of that range, so the split that reaches them applies the bitmask on its
 // tail tiles (the tree-block pass).  With one split a kernel writes the
-// normalised output and the LSE; otherwise it writes partials for the
-// merge kernel: the split's output normalised by its own row sum, in fp16
-// (a convex combination of V rows, so within V's range), and the running
-// max and row sum in fp32.
+// normalised output and the LSE; otherwise it writes partials: the split's
+// output normalised by its own row sum, in fp16 (a convex combination of V
+// rows, so within V's range), and the running max and row sum in fp32.
+// The partials are merged either by the merge kernel (a launch of its own)
+// or, when the launch is given arrival counters, by the last of a row
+// block's split workgroups to finish (merge_if_last below).
 //
 // Matrix-core mapping (v_mfma_f32_32x32x16_bf16, D = A*B + C).  Scores are
 // computed transposed, S^T = K * Q^T: the query is the MFMA column, so a
@@ -54,6 +56,7 @@
 // product).
 #pragma once
 
+#include "attn_merge.hpp"
 #include "common.hpp"
 
 namespace tree_attn {
@@ -70,6 +73,8 @@ struct FwdParams {
   float* lse;
   _Float16* part_o;  // [splits][N*Hq][128]  O of the split / its row sum
   float* part_ml;    // [splits][N*Hq][2]  (max in log2 units, row sum)
+  unsigned* counters;  // [S][Hkv][mblocks] arrival counts, or null: the
+                       // merge kernel merges the partials
   int max_pps, num_pages, log2_page, W;
   int max_tokens;  // min(max_pps * page_size, 2^30)
   int S, N, Hq, Hkv, G;
@@ -110,10 +115,13 @@ __device__ __forceinline__ void lds_write8(unsigned addr, u32x2 v) {
 // stg (16-byte chunks XOR-swizzled by row), then each lane stores 16 bytes,
 // four full 256-byte rows per instruction.  row: the global row index of
 // this lane's row (rows of 256 bytes from base), or -1 for a row that is
-// not written.  Uses only the calling wave's data: no barrier.
+// not written.  Uses only the calling wave's data: no barrier.  coherent:
+// device-coherent stores, for partials that another workgroup of the same
+// launch merges (merge_if_last waits for them before counting in).
 __device__ __forceinline__ void store_rows_staged(const u32x2 (&pk)[16],
                                                   unsigned stg, int row,
-                                                  char* base, int lane) {
+                                                  char* base, int lane,
+                                                  bool coherent = false) {
   const int col = lane & 31, half = lane >> 5;
 #pragma unroll
   for (int c = 0; c < 16; ++c) {
@@ -127,7 +135,15 @@ __device__ __forceinline__ void store_rows_staged(const u32x2 (&pk)[16],
                                                 ((ch ^ (rr & 15)) << 4));
     const int dr = __shfl(row, rr);
     if (dr >= 0) {
-      *reinterpret_cast<u32x4*>(base + (size_t)dr * 256 + ch * 16) = v;
+      char* dst = base + (size_t)dr * 256 + ch * 16;
+      if (coherent) {
+        // device-coherent (sc1) 16-byte store; the compiler does not track
+        // it, so the caller waits for it with wait_vmcnt<0>
+        asm volatile("global_store_dwordx4 %0, %1, off sc1"
+                     :: "v"(dst), "v"(v) : "memory");
+      } else {
+        *reinterpret_cast<u32x4*>(dst) = v;
+      }
     }
   }
 }
@@ -184,6 +200,43 @@ __device__ __forceinline__ void apply_tile_mask(f32x16 (&S)[2], uint64_t allow,
       if (!((allow >> kk) & 1)) S[kb][rr] = -INFINITY;
     }
   }
+}
+
+// Epilogue of a split workgroup when the launch merges its own partials.
+// Every workgroup of the row block (s, g, mb) that reaches its epilogue
+// (splits whose first key is below T) has stored its partials; each then
+// stored its partials with device-coherent stores (the reader may run on
+// another XCD, whose L2 does not see this one's lines), waits for them to
+// complete and counts itself in by a wrapping atomic increment at device
+// scope.  The one that sees the count reach nsplit - 1 is the last, resets
+// the counter to zero by the same increment (so that the next call finds
+// it at zero) and merges the block's rows, reading the partials with
+// device-coherent loads.  This is the release/acquire pattern with the
+// cache-wide writeback and invalidate left out, which only plain
+// (non-coherent) accesses need.  No workgroup waits for another.
+template <int NT>
+__device__ __forceinline__ void merge_if_last(const FwdParams& p, int s, int g,
+                                              int mb, int a, int rows, int r0,
+                                              int rows_per_wg, int T, int tid,
+                                              int* flag_lds) {
+  const int nsplit = min(p.splits, (T + p.chunk - 1) / p.chunk);
+  unsigned* ctr = p.counters + ((size_t)s * p.Hkv + g) * p.mblocks + mb;
+  // the partials went out as device-coherent stores: once they have
+  // completed (vmcnt 0) they are visible to every XCD
+  wait_vmcnt<0>();
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned old = __builtin_amdgcn_atomic_inc32(
+        ctr, (unsigned)(nsplit - 1), __ATOMIC_RELAXED, "agent");
+    *flag_lds = old == (unsigned)(nsplit - 1) ? 1 : 0;
+  }
+  __syncthreads();
+  if (*flag_lds == 0) return;
+  // issued after the barrier, i.e. after the count was seen complete;
+  // device-coherent loads read what the other workgroups stored
+  merge_rows_wg<NT, true>(p.part_o, p.part_ml, p.out, p.lse, (size_t)p.N * p.Hq,
+                    p.Hq, p.G, g, a, r0, min(r0 + rows_per_wg, rows), nsplit,
+                    tid);
 }
 
 }  // namespace tree_attn

@@ -452,8 +452,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd128h_kernel(FwdParams p) {
     xml[64 + lane] = l_tot;
   }
   __syncthreads();
-  if (kh == 1) return;
-  {
+  if (kh == 0) {
     const float m1 = xml[lane], l1 = xml[64 + lane];
     const float mx = __builtin_elementwise_maximum(m_ref, m1);
     const float a0 = mx == -INFINITY ? 0.f : fast_exp2(m_ref - mx);
@@ -472,46 +471,55 @@ __global__ __launch_bounds__(512, 1) void attn_fwd128h_kernel(FwdParams p) {
     }
     l_tot = l_tot * a0 + l1 * a1;
     m_ref = mx;
-  }
 
-  // ---- epilogue (lower-half waves): the normalised output in bf16 (one
-  // split) or fp16 (a split's partial), staged through LDS past the
-  // exchange area so that the stores write whole rows
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  u32x2 pk[16];
+    // ---- epilogue (lower-half waves): the normalised output in bf16 (one
+    // split) or fp16 (a split's partial), staged through LDS past the
+    // exchange area so that the stores write whole rows
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    u32x2 pk[16];
 #pragma unroll
-  for (int db = 0; db < 4; ++db) {
+    for (int db = 0; db < 4; ++db) {
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      if (p.splits == 1) {
-        bf16x4 v4;
+      for (int g4 = 0; g4 < 4; ++g4) {
+        if (p.splits == 1) {
+          bf16x4 v4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(o[db][g4 * 4 + e] * inv);
-        pk[db * 4 + g4] = __builtin_bit_cast(u32x2, v4);
-      } else {
-        f16x4 v4;
+          for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(o[db][g4 * 4 + e] * inv);
+          pk[db * 4 + g4] = __builtin_bit_cast(u32x2, v4);
+        } else {
+          f16x4 v4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = to_f16_sat(o[db][g4 * 4 + e] * inv);
-        pk[db * 4 + g4] = __builtin_bit_cast(u32x2, v4);
+          for (int e = 0; e < 4; ++e) v4[e] = to_f16_sat(o[db][g4 * 4 + e] * inv);
+          pk[db * 4 + g4] = __builtin_bit_cast(u32x2, v4);
+        }
+      }
+    }
+    const unsigned stg = ring_base + kEpilogueStage + rg * 8192;
+    const int row = rvalid ? (int)qrow : -1;
+    if (p.splits == 1) {
+      store_rows_staged(pk, stg, row, reinterpret_cast<char*>(p.out), lane);
+      if (half == 0 && rvalid) {
+        p.lse[qrow] = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
+      }
+    } else {
+      const size_t prow0 = (size_t)split * p.N * p.Hq;
+      store_rows_staged(pk, stg, row,
+                        reinterpret_cast<char*>(p.part_o + prow0 * kHeadDim),
+                        lane, p.counters != nullptr);
+      if (half == 0 && rvalid) {
+        float* dst = p.part_ml + (prow0 + qrow) * 2;
+        if (p.counters != nullptr) {
+          store_coherent8(dst, (uint64_t)__float_as_uint(m_ref) |
+                                   ((uint64_t)__float_as_uint(l_tot) << 32));
+        } else {
+          *reinterpret_cast<f32x2*>(dst) = f32x2{m_ref, l_tot};
+        }
       }
     }
   }
-  const unsigned stg = ring_base + kEpilogueStage + rg * 8192;
-  const int row = rvalid ? (int)qrow : -1;
-  if (p.splits == 1) {
-    store_rows_staged(pk, stg, row, reinterpret_cast<char*>(p.out), lane);
-    if (half == 0 && rvalid) {
-      p.lse[qrow] = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
-    }
-  } else {
-    const size_t prow0 = (size_t)split * p.N * p.Hq;
-    store_rows_staged(pk, stg, row,
-                      reinterpret_cast<char*>(p.part_o + prow0 * kHeadDim),
-                      lane);
-    if (half == 0 && rvalid) {
-      *reinterpret_cast<f32x2*>(p.part_ml + (prow0 + qrow) * 2) =
-          f32x2{m_ref, l_tot};
-    }
+  if (p.counters != nullptr) {
+    merge_if_last<kThreads>(p, s, g, mb, a, rows, r0, kRowsPerWG128, T, tid,
+                            pg_lds);
   }
 }
 

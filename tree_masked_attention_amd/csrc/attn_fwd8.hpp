@@ -587,12 +587,21 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd256_kernel(FwdParams p) {
       const size_t prow0 = (size_t)split * p.N * p.Hq;
       store_rows_staged(pk, stg, row,
                         reinterpret_cast<char*>(p.part_o + prow0 * kHeadDim),
-                        lane);
+                        lane, p.counters != nullptr);
       if (half == 0 && rvalid[qb]) {
-        *reinterpret_cast<f32x2*>(p.part_ml + (prow0 + qrow[qb]) * 2) =
-            f32x2{m_ref[qb], l_tot};
+        float* dst = p.part_ml + (prow0 + qrow[qb]) * 2;
+        if (p.counters != nullptr) {
+          store_coherent8(dst, (uint64_t)__float_as_uint(m_ref[qb]) |
+                                   ((uint64_t)__float_as_uint(l_tot) << 32));
+        } else {
+          *reinterpret_cast<f32x2*>(dst) = f32x2{m_ref[qb], l_tot};
+        }
       }
     }
+  }
+  if (p.counters != nullptr) {
+    merge_if_last<kThreads>(p, s, g, mb, a, rows, r0, kRowsPerWG8, T, tid,
+                            pg_lds);
   }
 }
 

@@ -8,11 +8,52 @@
 // A split in which the row saw no allowed key has m_c = -inf, l_c = 0 and
 // contributes nothing.  The sums are accumulated with a running maximum,
 // which gives the same values up to rounding order.
+//
+// Two users: attn_merge_kernel (a launch of its own after the attention
+// kernel) and merge_rows_wg, which the attention kernel's last split
+// workgroup of a row block runs in its epilogue.  Both take every element
+// through merge_weights and the same multiply-adds, splits in index
+// order, so they produce identical bits.
 #pragma once
 
 #include "common.hpp"
 
 namespace tree_attn {
+
+// The workspace of a split launch starts with this many 32-bit arrival
+// counters, one per (sequence, kv head, row block), then the partials.
+constexpr int kMergeCounters = 16384;
+constexpr size_t kCounterBytes = (size_t)kMergeCounters * 4;
+
+// Folds split c's (m_c, l_c) into a row's running (m, l); returns false
+// when no split so far saw an allowed key (the row's sums stay zero), else
+// the factors for acc <- acc * s_old + w * O'_c (merge_acc).
+__device__ __forceinline__ bool merge_weights(float& m_run, float& l_run,
+                                              f32x2 ml, float& s_old,
+                                              float& w) {
+  const float m_new = fmaxf(m_run, ml[0]);
+  if (m_new == -INFINITY) return false;
+  s_old = fast_exp2(m_run - m_new);
+  w = fast_exp2(ml[0] - m_new) * ml[1];
+  l_run = __builtin_fmaf(l_run, s_old, w);
+  m_run = m_new;
+  return true;
+}
+
+// One output element's running sum (an explicit fma, so that no compiler
+// contraction choice can make the two merge paths differ).
+__device__ __forceinline__ float merge_acc(float acc, float s_old, float w,
+                                          float o) {
+  return __builtin_fmaf(w, o, acc * s_old);
+}
+
+__device__ __forceinline__ float merge_inv(float l_run) {
+  return l_run > 0.f ? 1.f / l_run : 0.f;
+}
+
+__device__ __forceinline__ float merge_lse(float m_run, float l_run) {
+  return l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+}
 
 struct MergeParams {
   const int32_t* prefix_lens;
@@ -90,30 +131,104 @@ __global__ __launch_bounds__(kMergeWaves * 64) void attn_merge_kernel(
       if (c0 + u >= nsplit) break;
 #pragma unroll
       for (int k = 0; k < RL; ++k) {
-        const float m_new = fmaxf(m_run[k], ml[k][u][0]);
-        if (m_new == -INFINITY) continue;  // no key seen yet
-        const float s_old = fast_exp2(m_run[k] - m_new);
-        const float w = fast_exp2(ml[k][u][0] - m_new) * ml[k][u][1];
-        l_run[k] = l_run[k] * s_old + w;
+        float s_old, w;
+        if (!merge_weights(m_run[k], l_run[k], ml[k][u], s_old, w)) continue;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          acc[k][e] = acc[k][e] * s_old + w * (float)oc[k][u][e];
+          acc[k][e] = merge_acc(acc[k][e], s_old, w, (float)oc[k][u][e]);
         }
-        m_run[k] = m_new;
       }
     }
   }
 #pragma unroll
   for (int k = 0; k < RL; ++k) {
     if (r0 + 2 * k + half >= rows) continue;
-    const float inv = l_run[k] > 0.f ? 1.f / l_run[k] : 0.f;
+    const float inv = merge_inv(l_run[k]);
     bf16x4 r4;
 #pragma unroll
     for (int e = 0; e < 4; ++e) r4[e] = (__bf16)(acc[k][e] * inv);
     *reinterpret_cast<bf16x4*>(p.out + qrow[k] * kHeadDim + c4) = r4;
-    if ((lane & 31) == 0) {
-      p.lse[qrow[k]] =
-          l_run[k] > 0.f ? (m_run[k] + log2f(l_run[k])) * kLn2 : -INFINITY;
+    if ((lane & 31) == 0) p.lse[qrow[k]] = merge_lse(m_run[k], l_run[k]);
+  }
+}
+
+// Merges rows [r_lo, r_hi) of the (sequence, kv head g) pair whose tree
+// starts at node a, over its nsplit splits, with the NT threads of a
+// workgroup: thread t takes the 16-byte column chunk t % 16 of rows
+// r_lo + t / 16 + k * NT / 16; the loads of kMergeRowsPerThread rows and
+// kMergeSplits splits are issued before any is used.  kCoherent: the
+// partials are read with device-coherent loads (written by other
+// workgroups of the running launch).
+constexpr int kMergeRowsPerThread = 4;
+
+template <int NT, bool kCoherent>
+__device__ __forceinline__ void merge_rows_wg(
+    const _Float16* part_o, const float* part_ml, __bf16* out, float* lse,
+    size_t NH, int Hq, int G, int g, int a, int r_lo, int r_hi, int nsplit,
+    int tid) {
+  constexpr int RS = NT / 16;                // rows per pass of the group
+  constexpr int RT = kMergeRowsPerThread;
+  constexpr int KS = kMergeSplits;
+  typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+  const int ch = tid & 15, rsub = tid / 16;
+  for (int rb = r_lo; rb < r_hi; rb += RS * RT) {
+    size_t qrow[RT];
+    float m_run[RT], l_run[RT], acc[RT][8];
+#pragma unroll
+    for (int k = 0; k < RT; ++k) {
+      const int r = min(rb + rsub + k * RS, r_hi - 1);
+      qrow[k] = (size_t)(a + r / G) * Hq + g * G + r % G;
+      m_run[k] = -INFINITY;
+      l_run[k] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[k][e] = 0.f;
+    }
+    for (int c0 = 0; c0 < nsplit; c0 += KS) {
+      f32x2 ml[RT][KS];
+      f16x8 oc[RT][KS];
+#pragma unroll
+      for (int k = 0; k < RT; ++k) {
+#pragma unroll
+        for (int u = 0; u < KS; ++u) {
+          const int c = min(c0 + u, nsplit - 1);  // in range; unused if past
+          const size_t prow = (size_t)c * NH + qrow[k];
+          const _Float16* po = part_o + prow * kHeadDim + ch * 8;
+          if (kCoherent) {
+            const uint64_t m2 = load_coherent8(part_ml + prow * 2);
+            const uint64_t o0 = load_coherent8(po);
+            const uint64_t o1 = load_coherent8(po + 4);
+            ml[k][u] = f32x2{__uint_as_float((unsigned)m2),
+                             __uint_as_float((unsigned)(m2 >> 32))};
+            oc[k][u] = __builtin_bit_cast(f16x8, u64x2{o0, o1});
+          } else {
+            ml[k][u] = *reinterpret_cast<const f32x2*>(part_ml + prow * 2);
+            oc[k][u] = *reinterpret_cast<const f16x8*>(po);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < KS; ++u) {
+        if (c0 + u >= nsplit) break;
+#pragma unroll
+        for (int k = 0; k < RT; ++k) {
+          float s_old, w;
+          if (!merge_weights(m_run[k], l_run[k], ml[k][u], s_old, w)) continue;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            acc[k][e] = merge_acc(acc[k][e], s_old, w, (float)oc[k][u][e]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < RT; ++k) {
+      if (rb + rsub + k * RS >= r_hi) continue;
+      const float inv = merge_inv(l_run[k]);
+      bf16x8 r8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) r8[e] = (__bf16)(acc[k][e] * inv);
+      *reinterpret_cast<bf16x8*>(out + qrow[k] * kHeadDim + ch * 8) = r8;
+      if (ch == 0) lse[qrow[k]] = merge_lse(m_run[k], l_run[k]);
     }
   }
 }

@@ -16,6 +16,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kF16Max = 65504.f;
 
@@ -31,6 +32,20 @@ constexpr float kLog2e = 1.442695040888963407f;
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) {
   return x < lo ? lo : (x > hi ? hi : x);
+}
+
+// Device-coherent 8-byte store and load (relaxed atomics at agent scope:
+// the sc1 bit, so the data bypass this XCD's L2, whose lines other XCDs do
+// not see).  Used for data that another workgroup of the same launch reads
+// after an arrival counter says it is complete; no cache-wide writeback or
+// invalidate is needed for it.
+__device__ __forceinline__ void store_coherent8(void* p, uint64_t v) {
+  __hip_atomic_store(static_cast<uint64_t*>(p), v, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t load_coherent8(const void* p) {
+  return __hip_atomic_load(static_cast<uint64_t*>(const_cast<void*>(p)),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // 2^x on the hardware exponential unit (exact 0 for -inf).

@@ -22,7 +22,7 @@ using namespace tree_attn;
 
 namespace {
 
-constexpr int kAbiVersion = 9;
+constexpr int kAbiVersion = 10;
 constexpr int kMaxDevices = 64;
 constexpr int kMaxSplits = 256;
 constexpr int kMinKeysPerSplit = 256;
@@ -69,9 +69,20 @@ struct Plan {
   int splits = 1;    // key-range splits
   int chunk = 0;     // keys per split (multiple of the 64-key tile)
   int units = 0;     // sequences * kv heads * splits * row blocks
+  int blocks = 0;    // sequences * kv heads * row blocks (merge counters)
   size_t part_ml_off = 0;
   size_t ws_bytes = 0;
 };
+
+// Workspace of a split launch (both paths, so that one workspace can serve
+// both): kCounterBytes of arrival counters, then the fp16 partials
+// [splits][N*Hq][D], then the (max, row sum) pairs [splits][N*Hq][2].
+// The counter area sits at a fixed offset whatever the sizes, so counters
+// left at zero by one call are zero for the next call of any shape.
+size_t partials_bytes(size_t rows_all, int D, size_t* part_ml_off) {
+  *part_ml_off = kCounterBytes + align_up(rows_all * D * sizeof(_Float16), 256);
+  return *part_ml_off + align_up(rows_all * 2 * sizeof(float), 256);
+}
 
 // Launch planning from host-side bounds only (no device-to-host copy).
 // Row blocks: 256 rows (8 waves of 32 rows) when a (sequence, kv head)
@@ -143,10 +154,10 @@ int make_plan(int S, int N, int Hq, int Hkv, int max_prefix_len,
   const long long units = units0 * splits;
   if (units > (1LL << 30)) return TREE_ATTN_ERR_UNSUPPORTED;
   pl.units = (int)units;
+  pl.blocks = (int)units0;
   if (splits > 1) {
-    const size_t rows_all = (size_t)N * Hq * splits;
-    pl.part_ml_off = align_up(rows_all * kHeadDim * sizeof(_Float16), 256);
-    pl.ws_bytes = pl.part_ml_off + align_up(rows_all * 2 * sizeof(float), 256);
+    pl.ws_bytes = partials_bytes((size_t)N * Hq * splits, kHeadDim,
+                                 &pl.part_ml_off);
   }
   *out = pl;
   return TREE_ATTN_OK;
@@ -300,9 +311,7 @@ int make_var_plan(int S, int N, int Hq, int Hkv, int D, int max_prefix_len,
   pl.grid = units0 * splits;
   if (pl.grid > 0x7fffffffLL) return TREE_ATTN_ERR_UNSUPPORTED;
   if (splits > 1) {
-    const size_t rows_all = (size_t)N * Hq * splits;
-    pl.part_ml_off = align_up(rows_all * D * sizeof(_Float16), 256);
-    pl.ws_bytes = pl.part_ml_off + align_up(rows_all * 2 * sizeof(float), 256);
+    pl.ws_bytes = partials_bytes((size_t)N * Hq * splits, D, &pl.part_ml_off);
   }
   *out = pl;
   return TREE_ATTN_OK;
@@ -386,9 +395,15 @@ int run_verify(int phases, const void* q, const void* k_cache, const void* v_cac
   fp.masks = masks;
   fp.out = static_cast<__bf16*>(out);
   fp.lse = lse;
-  fp.part_o = static_cast<_Float16*>(workspace);
+  fp.part_o = reinterpret_cast<_Float16*>(static_cast<char*>(workspace) +
+                                          kCounterBytes);
   fp.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                         pl.part_ml_off);
+  // Both phases in one call with split partials: the attention kernel's
+  // last split workgroup of each row block merges it (no merge launch).
+  const bool fused = (phases & kPhaseAttend) && (phases & kPhaseMerge) &&
+                     pl.splits > 1 && pl.blocks <= kMergeCounters;
+  fp.counters = fused ? static_cast<unsigned*>(workspace) : nullptr;
   fp.max_pps = max_pages_per_seq;
   fp.num_pages = num_pages;
   fp.log2_page = ilog2(page_size);
@@ -418,7 +433,7 @@ int run_verify(int phases, const void* q, const void* k_cache, const void* v_cac
   }
   if (hipGetLastError() != hipSuccess) return TREE_ATTN_ERR_HIP;
 
-  if ((phases & kPhaseMerge) && pl.splits > 1) {
+  if ((phases & kPhaseMerge) && pl.splits > 1 && !fused) {
     MergeParams mp;
     mp.prefix_lens = prefix_lens;
     mp.tree_offsets = tree_offsets;
@@ -886,7 +901,8 @@ int tree_attn_verify_ex(const void* q, const void* k_cache,
   vp.masks = masks;
   vp.out = static_cast<__bf16*>(out);
   vp.lse = lse;
-  vp.part_o = static_cast<_Float16*>(workspace);
+  vp.part_o = reinterpret_cast<_Float16*>(static_cast<char*>(workspace) +
+                                          kCounterBytes);
   vp.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                         pl.part_ml_off);
   vp.max_pps = max_pages_per_seq;
