@@ -127,3 +127,51 @@ def test_variant_full_size_sampled(name, fmt, d):
     say(f"  {wl.name} seqs {seqs} kv head {heads}: max|dout| {eo:.2e}, "
         f"max rel dlse {el:.2e}")
     assert eo <= OUT_ATOL and el <= LSE_RTOL
+
+
+def test_workspace_reuse_across_formats():
+    # One zero-filled workspace for calls of different formats, head dims
+    # and split counts in a row: each call matches the oracle and leaves
+    # the counter area (the first 64 KB, which tree_attn_verify's launches
+    # use) at zero, so one workspace serves both entry points.
+    import tree_masked_attention_amd.api as api
+    dev = torch.device("cuda:0")
+    bf = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    runs = [(_case("reuse-e4m3", 60, "e4m3", 128, prefix_lens=[700, 90],
+                   tree_sizes=[40, 70]), 3),
+            (_case("reuse-d64", 61, "bf16", 64, prefix_lens=[2000, 0, 31],
+                   tree_sizes=[100, 16, 1]), 5),
+            (_case("reuse-e4m3-d64", 62, "e4m3", 64, prefix_lens=[1500],
+                   tree_sizes=[64]), 0)]
+    ws = torch.zeros((64 << 20,), dtype=torch.uint8, device=dev)
+    for wl, splits in runs:
+        kvd = api.KV_FP8_E4M3 if wl.kv_format == "e4m3" else api.KV_BF16
+        need = int(api._lib.tree_attn_workspace_size_ex(
+            kvd, wl.num_seqs, wl.total_nodes, wl.num_q_heads,
+            wl.num_kv_heads, wl.head_dim, wl.max_prefix_len, wl.max_nodes,
+            wl.page_size, splits))
+        assert 65536 < need <= ws.numel()
+        if wl.kv_format == "bf16":
+            k, v, ks, vs = bf(wl.k_cache), bf(wl.v_cache), None, None
+        else:
+            k, v = to_dev(wl.k_cache), to_dev(wl.v_cache)
+            ks, vs = to_dev(wl.k_scale), to_dev(wl.v_scale)
+        masks, _ = api.build_mask(to_dev(wl.parents), to_dev(wl.tree_offsets),
+                                  wl.max_nodes)
+        say(f"[gpu] variant workspace reuse {wl.name}, splits {splits}")
+        out, lse = api.verify_ex(bf(wl.q), k, v, to_dev(wl.page_table),
+                                 to_dev(wl.prefix_lens), to_dev(wl.tree_offsets),
+                                 masks, wl.max_prefix_len, wl.max_nodes,
+                                 wl.scale, ks, vs, num_splits=splits,
+                                 workspace=ws)
+        torch.cuda.synchronize()
+        assert int(ws[:65536].count_nonzero()) == 0, "counters left set"
+        ref_o, ref_l = oracle.workload_attention(wl)
+        sel = ~np.isnan(ref_l)
+        o = out.float().cpu().numpy()
+        l = lse.cpu().numpy().astype(np.float64)
+        eo = np.abs(o - ref_o)[sel].max()
+        el = (np.abs(l - ref_l) / np.maximum(np.abs(ref_l), 1))[sel].max()
+        say(f"  max|dout| {eo:.2e}, max rel dlse {el:.2e}")
+        assert eo <= OUT_ATOL and el <= LSE_RTOL

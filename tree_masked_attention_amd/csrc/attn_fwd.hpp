@@ -138,7 +138,7 @@ __device__ __forceinline__ void store_rows_staged(const u32x2 (&pk)[16],
       char* dst = base + (size_t)dr * 256 + ch * 16;
       if (coherent) {
         // device-coherent (sc1) 16-byte store; the compiler does not track
-        // it, so the caller waits for it with wait_vmcnt<0>
+        // it; merge_if_last_rows waits for it (vmcnt 0) before counting in
         asm volatile("global_store_dwordx4 %0, %1, off sc1"
                      :: "v"(dst), "v"(v) : "memory");
       } else {
@@ -202,41 +202,20 @@ __device__ __forceinline__ void apply_tile_mask(f32x16 (&S)[2], uint64_t allow,
   }
 }
 
-// Epilogue of a split workgroup when the launch merges its own partials.
-// Every workgroup of the row block (s, g, mb) that reaches its epilogue
-// (splits whose first key is below T) has stored its partials; each then
-// stored its partials with device-coherent stores (the reader may run on
-// another XCD, whose L2 does not see this one's lines), waits for them to
-// complete and counts itself in by a wrapping atomic increment at device
-// scope.  The one that sees the count reach nsplit - 1 is the last, resets
-// the counter to zero by the same increment (so that the next call finds
-// it at zero) and merges the block's rows, reading the partials with
-// device-coherent loads.  This is the release/acquire pattern with the
-// cache-wide writeback and invalidate left out, which only plain
-// (non-coherent) accesses need.  No workgroup waits for another.
+// Epilogue of a split workgroup of a launch that merges its own partials
+// (merge_if_last_rows): the row block (s, g, mb), rows [r0, r0 +
+// rows_per_wg) of the pair, whose splits with a first key below T reach
+// their epilogue.
 template <int NT>
 __device__ __forceinline__ void merge_if_last(const FwdParams& p, int s, int g,
                                               int mb, int a, int rows, int r0,
                                               int rows_per_wg, int T, int tid,
                                               int* flag_lds) {
   const int nsplit = min(p.splits, (T + p.chunk - 1) / p.chunk);
-  unsigned* ctr = p.counters + ((size_t)s * p.Hkv + g) * p.mblocks + mb;
-  // the partials went out as device-coherent stores: once they have
-  // completed (vmcnt 0) they are visible to every XCD
-  wait_vmcnt<0>();
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned old = __builtin_amdgcn_atomic_inc32(
-        ctr, (unsigned)(nsplit - 1), __ATOMIC_RELAXED, "agent");
-    *flag_lds = old == (unsigned)(nsplit - 1) ? 1 : 0;
-  }
-  __syncthreads();
-  if (*flag_lds == 0) return;
-  // issued after the barrier, i.e. after the count was seen complete;
-  // device-coherent loads read what the other workgroups stored
-  merge_rows_wg<NT, true>(p.part_o, p.part_ml, p.out, p.lse, (size_t)p.N * p.Hq,
-                    p.Hq, p.G, g, a, r0, min(r0 + rows_per_wg, rows), nsplit,
-                    tid);
+  merge_if_last_rows<NT, kHeadDim>(
+      p.counters + ((size_t)s * p.Hkv + g) * p.mblocks + mb, nsplit, p.part_o,
+      p.part_ml, p.out, p.lse, (size_t)p.N * p.Hq, p.Hq, p.G, g, a, r0,
+      min(r0 + rows_per_wg, rows), tid, flag_lds);
 }
 
 }  // namespace tree_attn

@@ -154,23 +154,26 @@ __global__ __launch_bounds__(kMergeWaves * 64) void attn_merge_kernel(
 
 // Merges rows [r_lo, r_hi) of the (sequence, kv head g) pair whose tree
 // starts at node a, over its nsplit splits, with the NT threads of a
-// workgroup: thread t takes the 16-byte column chunk t % 16 of rows
-// r_lo + t / 16 + k * NT / 16; the loads of kMergeRowsPerThread rows and
-// kMergeSplits splits are issued before any is used.  kCoherent: the
-// partials are read with device-coherent loads (written by other
-// workgroups of the running launch).
+// workgroup (head dim D, rows of D fp16 partials): thread t takes the
+// 16-byte column chunk t % (D/8) of rows r_lo + t / (D/8) + k * NT / (D/8);
+// the loads of kMergeRowsPerThread rows and kMergeSplits splits are issued
+// before any is used.  kCoherent: the partials are read with
+// device-coherent loads (written by other workgroups of the running
+// launch).
 constexpr int kMergeRowsPerThread = 4;
 
-template <int NT, bool kCoherent>
+template <int NT, int D, bool kCoherent>
 __device__ __forceinline__ void merge_rows_wg(
     const _Float16* part_o, const float* part_ml, __bf16* out, float* lse,
     size_t NH, int Hq, int G, int g, int a, int r_lo, int r_hi, int nsplit,
     int tid) {
-  constexpr int RS = NT / 16;                // rows per pass of the group
+  constexpr int CH = D / 8;                  // 16-byte chunks per row
+  constexpr int RS = NT / CH;                // rows per pass of the group
   constexpr int RT = kMergeRowsPerThread;
   constexpr int KS = kMergeSplits;
+  static_assert(NT % CH == 0, "merge layout");
   typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-  const int ch = tid & 15, rsub = tid / 16;
+  const int ch = tid % CH, rsub = tid / CH;
   for (int rb = r_lo; rb < r_hi; rb += RS * RT) {
     size_t qrow[RT];
     float m_run[RT], l_run[RT], acc[RT][8];
@@ -192,7 +195,7 @@ __device__ __forceinline__ void merge_rows_wg(
         for (int u = 0; u < KS; ++u) {
           const int c = min(c0 + u, nsplit - 1);  // in range; unused if past
           const size_t prow = (size_t)c * NH + qrow[k];
-          const _Float16* po = part_o + prow * kHeadDim + ch * 8;
+          const _Float16* po = part_o + prow * D + ch * 8;
           if (kCoherent) {
             const uint64_t m2 = load_coherent8(part_ml + prow * 2);
             const uint64_t o0 = load_coherent8(po);
@@ -227,10 +230,42 @@ __device__ __forceinline__ void merge_rows_wg(
       bf16x8 r8;
 #pragma unroll
       for (int e = 0; e < 8; ++e) r8[e] = (__bf16)(acc[k][e] * inv);
-      *reinterpret_cast<bf16x8*>(out + qrow[k] * kHeadDim + ch * 8) = r8;
+      *reinterpret_cast<bf16x8*>(out + qrow[k] * D + ch * 8) = r8;
       if (ch == 0) lse[qrow[k]] = merge_lse(m_run[k], l_run[k]);
     }
   }
+}
+
+// Epilogue of a split workgroup when the launch merges its own partials.
+// Every workgroup of a row block that reaches its epilogue (nsplit of
+// them) has stored its partials with device-coherent stores (the reader
+// may run on another XCD, whose L2 does not see this one's lines); each
+// waits for them to complete and counts itself in by a wrapping atomic
+// increment at device scope on the block's counter ctr.  The one that sees
+// the count reach nsplit - 1 is the last, resets the counter to zero by
+// the same increment (so that the next call finds it at zero) and merges
+// rows [r_lo, r_hi), reading the partials with device-coherent loads.
+// This is the release/acquire pattern with the cache-wide writeback and
+// invalidate left out, which only plain (non-coherent) accesses need.  No
+// workgroup waits for another.  flag_lds: one int of LDS that no wave uses
+// any more.
+template <int NT, int D>
+__device__ __forceinline__ void merge_if_last_rows(
+    unsigned* ctr, int nsplit, const _Float16* part_o, const float* part_ml,
+    __bf16* out, float* lse, size_t NH, int Hq, int G, int g, int a, int r_lo,
+    int r_hi, int tid, int* flag_lds) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // own partials complete
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned old = __builtin_amdgcn_atomic_inc32(
+        ctr, (unsigned)(nsplit - 1), __ATOMIC_RELAXED, "agent");
+    *flag_lds = old == (unsigned)(nsplit - 1) ? 1 : 0;
+  }
+  __syncthreads();
+  if (*flag_lds == 0) return;
+  // issued after the barrier, i.e. after the count was seen complete
+  merge_rows_wg<NT, D, true>(part_o, part_ml, out, lse, NH, Hq, G, g, a,
+                             r_lo, r_hi, nsplit, tid);
 }
 
 }  // namespace tree_attn

@@ -25,6 +25,7 @@
 // combination of V rows, so within V's range) and (max, sum) in fp32.
 #pragma once
 
+#include "attn_merge.hpp"
 #include "common.hpp"
 
 namespace tree_attn {
@@ -359,9 +360,9 @@ __global__ __launch_bounds__(kVarThreads, 2) void attn_var_kernel(VarParams p) {
   }
 }
 
-// LSE merge of the split partials: m* = max m_c, w_c = l_c 2^(m_c - m*),
-// out = sum w_c O'_c / sum w_c with O'_c = O_c / l_c, lse = ln 2 (m* +
-// log2 sum w_c).  One thread per (row, 4 dims).
+// LSE merge of the split partials (the identity and arithmetic of
+// attn_merge.hpp: running maximum, merge_weights / merge_acc, splits in
+// index order).  One thread per (row, 4 dims).
 template <int D>
 __global__ __launch_bounds__(256) void attn_var_merge_kernel(VarParams p) {
   const size_t rows_all = (size_t)p.N * p.Hq;
@@ -369,31 +370,23 @@ __global__ __launch_bounds__(256) void attn_var_merge_kernel(VarParams p) {
   const size_t row = gid / (D / 4);
   const int d4 = (int)(gid % (D / 4)) * 4;
   if (row >= rows_all) return;
-  float mx = -__builtin_inff();
+  float m_run = -INFINITY, l_run = 0.f;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
   for (int c = 0; c < p.splits; ++c) {
-    mx = __builtin_fmaxf(mx, p.part_ml[((size_t)c * rows_all + row) * 2]);
-  }
-  const float mref = mx == -__builtin_inff() ? 0.f : mx;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float den = 0.f;
-  for (int c = 0; c < p.splits; ++c) {
-    const float* ml = p.part_ml + ((size_t)c * rows_all + row) * 2;
-    const float wc = fast_exp2(ml[0] - mref) * ml[1];
-    den += wc;
-    const f16x4 o = *reinterpret_cast<const f16x4*>(
-        p.part_o + ((size_t)c * rows_all + row) * D + d4);
+    const size_t prow = (size_t)c * rows_all + row;
+    const f32x2 ml = *reinterpret_cast<const f32x2*>(p.part_ml + prow * 2);
+    const f16x4 o = *reinterpret_cast<const f16x4*>(p.part_o + prow * D + d4);
+    float s_old, w;
+    if (!merge_weights(m_run, l_run, ml, s_old, w)) continue;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] += wc * (float)o[e];
+    for (int e = 0; e < 4; ++e) acc[e] = merge_acc(acc[e], s_old, w, (float)o[e]);
   }
-  const float inv = den > 0.f ? 1.f / den : 0.f;
+  const float inv = merge_inv(l_run);
   bf16x4 o4;
 #pragma unroll
   for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(acc[e] * inv);
   *reinterpret_cast<bf16x4*>(p.out + row * D + d4) = o4;
-  if (d4 == 0) {
-    p.lse[row] = den > 0.f ? (mx + __builtin_log2f(den)) * kLn2
-                           : -__builtin_inff();
-  }
+  if (d4 == 0) p.lse[row] = merge_lse(m_run, l_run);
 }
 
 }  // namespace tree_attn

@@ -929,6 +929,9 @@ int tree_attn_verify_ex(const void* q, const void* k_cache,
   }
   if (hipGetLastError() != hipSuccess) return TREE_ATTN_ERR_HIP;
   if (pl.splits > 1) {
+    // a separate merge launch: the partials of this kernel are scattered
+    // 8-byte rows and its plans use more splits, so merging in the last
+    // workgroup of a row block was slower than this launch
     const long long work = (long long)total_nodes * num_q_heads * (head_dim / 4);
     const unsigned mgrid = (unsigned)((work + 255) / 256);
     if (head_dim == 64) {
