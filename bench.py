@@ -847,11 +847,32 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / args.steps
 
+    def per_call(fn, pick, reps=20):
+        """Median and minimum over single calls: an event between every two
+        consecutive calls of a back-to-back run (input copies rotated), so
+        each interval is one call plus its dispatch gap, without the host's
+        launch latency."""
+        for i in range(3):
+            fn(*pick(i))
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for i in range(reps):
+            if fn(*pick(i)) != 0:
+                raise RuntimeError("tree_attn call failed")
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        times = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3
+                       for i in range(reps))
+        return {"median": times[len(times) // 2], "min": times[0],
+                "calls": reps}
+
     mask_ms = per_launch(f_mask, lambda i: calls[i % copies][0])
     # tree_attn_verify: one attention launch (a split launch merges its
     # partials in its last workgroups); the variant path launches its merge
     # kernel after the attention kernel
     ver_ms = per_launch(f_ver, lambda i: calls[i % copies][1])
+    ver_call = per_call(f_ver, lambda i: calls[i % copies][1])
     phases = None
     if args.phases and not variant:
         # the two-launch form (attention kernel writing partials, then the
@@ -862,7 +883,9 @@ def main():
                   if plan["splits"] > 1 else 0.0)
         phases = {"attend_us": att_ms * 1e3, "merge_us": mer_ms * 1e3}
     log(f"[bench] step {ms_per_step * 1e3:.1f} us; mask build "
-        f"{mask_ms * 1e3:.1f} us; verify {ver_ms * 1e3:.1f} us"
+        f"{mask_ms * 1e3:.1f} us; verify {ver_ms * 1e3:.1f} us back to back, "
+        f"single calls median {ver_call['median']:.1f} / min "
+        f"{ver_call['min']:.1f} us"
         + (f" (two-launch form: attend {phases['attend_us']:.1f} us + merge "
            f"{phases['merge_us']:.1f} us)" if phases else ""))
 
@@ -923,6 +946,7 @@ def main():
             "avg_launch_us": ver_ms * 1e3,
         },
         "verify_us": ver_ms * 1e3,
+        "verify_call_us": ver_call,
         "mask_build_us": mask_ms * 1e3,
         "verify_tflops": alg_flops / v_s / 1e12,
         "verify_hbm_gbps": alg_bytes / v_s / 1e9,
