@@ -517,8 +517,12 @@ int tree_attn_gdn_commit(const void* k, const float* u, const float* g,
  * own row sum in fp16, as for tree_attn_verify, so |v| * scale must stay
  * below 65504); its workspace size comes from tree_attn_workspace_size_ex.
  *
+ * The key range is cut into at most 256 splits of at most 1039 pages each
+ * (the kernel copies a split's page ids to LDS), as for tree_attn_verify.
+ *
  * Host-side errors: as tree_attn_verify; ERR_UNSUPPORTED also for
- * head_dim not 64 or 128 and for an unknown kv_dtype.
+ * head_dim not 64 or 128, for an unknown kv_dtype, and for key ranges
+ * longer than 256 splits of 1039 pages.
  */
 int tree_attn_verify_ex(const void* q, const void* k_cache,
                         const void* v_cache, int32_t kv_dtype,

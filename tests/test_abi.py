@@ -382,6 +382,8 @@ def _vex(**over):
     (dict(masks=None), api.ERR_NULL),
     (dict(lse=None), api.ERR_NULL),
     (dict(max_p=100000, S=64, N=64), api.ERR_WORKSPACE),
+    # more than 256 splits of 1039 pages (page size 1): not supported
+    (dict(max_p=300000, page_size=1), api.ERR_UNSUPPORTED),
 ])
 def test_verify_ex_rejects(over, code):
     assert _vex(**over) == code
@@ -409,3 +411,8 @@ def test_workspace_size_ex_rules():
     assert f(0, 1, 8, 8, 2, 128, 4000, 8, 16, 4) == \
         api._lib.tree_attn_workspace_size(1, 8, 8, 2, 128, 4000, 8, 16, 4)
     assert f(1, 1, 8, 8, 2, 96, 4000, 8, 16, 4) == 0   # rejected sizes
+    # a split's page ids fit the kernel's LDS copy: page size 1 and 4000
+    # keys need at least 4 splits (1039 pages each), so one is not enough
+    one = f(1, 1, 8, 8, 2, 64, 4000, 8, 1, 1)
+    assert one >= 4 * 8 * 8 * 64 * 2
+    assert f(1, 1, 8, 8, 2, 64, 300000, 8, 1, 0) == 0  # > 256 x 1039 pages

@@ -69,6 +69,10 @@ CASES = {
                  num_kv_heads=4),
     "empty-tree-in-batch": dict(prefix_lens=[20, 40, 0], tree_sizes=[5, 0, 9]),
     "page1": dict(prefix_lens=[70, 3], tree_sizes=[12, 7], page_size=1),
+    # page size 1 over 3000 keys: a split holds at most 1039 page ids, so
+    # the plan makes at least three splits whatever is asked
+    "page1-long": dict(prefix_lens=[3000, 1500], tree_sizes=[40, 9],
+                       page_size=1),
     "page64": dict(prefix_lens=[70, 200], tree_sizes=[12, 70], page_size=64),
     "max-tree-1024": dict(prefix_lens=[50], tree_sizes=[1024], num_q_heads=2,
                           num_kv_heads=1, p_chain=0.7),

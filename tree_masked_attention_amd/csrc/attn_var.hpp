@@ -32,6 +32,9 @@ namespace tree_attn {
 
 constexpr int kVarRows = 128;   // query rows per workgroup (4 waves x 32)
 constexpr int kVarTile = 64;    // keys per tile
+constexpr int kVarDepth = 3;    // tiles in registers (in use + in flight)
+constexpr int kVarPageCache = 1040;       // page ids of a split, in LDS
+constexpr int kVarMaskCache = 129 * 16;   // mask words of a workgroup's nodes
 constexpr int kVarThreads = 256;
 constexpr int kVarVPitch = kVarTile * 2 + 8;  // bytes per V^T row in LDS
 
@@ -89,6 +92,11 @@ __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
          (__builtin_bit_cast(uint32_t, f1) & 0xffff0000u);
 }
 
+__device__ __forceinline__ const int32_t* table_row(const VarParams& p,
+                                                   int s) {
+  return p.page_table + (size_t)s * p.max_pps;
+}
+
 template <int D, bool FP8>
 __global__ __launch_bounds__(kVarThreads, 2) void attn_var_kernel(VarParams p) {
   constexpr int EB = FP8 ? 1 : 2;         // bytes per cached element
@@ -101,6 +109,8 @@ __global__ __launch_bounds__(kVarThreads, 2) void attn_var_kernel(VarParams p) {
   static_assert(NCH >= 1 && kVarTile * CR % kVarThreads == 0, "tile split");
   __shared__ __align__(16) unsigned char kl[kVarTile * KP];
   __shared__ __align__(16) unsigned char vl[D * kVarVPitch];
+  __shared__ int pg_var[kVarPageCache];
+  __shared__ uint64_t mk_var[kVarMaskCache];
   const unsigned kb =
       (unsigned)(size_t)(__attribute__((address_space(3))) unsigned char*)kl;
   const unsigned vb =
@@ -113,9 +123,9 @@ __global__ __launch_bounds__(kVarThreads, 2) void attn_var_kernel(VarParams p) {
   idx /= p.mblocks;
   const int g = idx % p.Hkv;
   const int s = idx / p.Hkv;
-  const int n0 = p.tree_offsets[s];
-  const int B = p.tree_offsets[s + 1] - n0;
-  const int P = p.prefix_lens[s];
+  const int n0 = clampi(p.tree_offsets[s], 0, p.N);
+  const int B = clampi(p.tree_offsets[s + 1], n0, p.N) - n0;
+  const int P = max(p.prefix_lens[s], 0);
   const int rows = B * p.G;
   if (mb * kVarRows >= rows) return;
   const int T = min(P + B, p.max_tokens);
@@ -143,40 +153,63 @@ __global__ __launch_bounds__(kVarThreads, 2) void attn_var_kernel(VarParams p) {
   const float ksc = FP8 && p.k_scale ? p.k_scale[g] : 1.f;
   const float vsc = FP8 && p.v_scale ? p.v_scale[g] : 1.f;
   const float sl2 = p.scale_log2 * ksc;
-  const uint64_t* mrow = p.masks + (size_t)(n0 + node) * p.W;
+
+  // The split's page ids and, when the split reaches the tree keys, the
+  // mask rows of the workgroup's nodes go to LDS first, so that the loop's
+  // lookups wait on LDS only (a global load there would have to wait for
+  // every K/V load in flight before it).  The plan keeps a split's pages
+  // within kVarPageCache; the rows are at most 129 nodes of at most 16
+  // words.
+  const int lp0 = k0 >> p.log2_page;
+  const int npg =
+      k0 < k1 ? min(((k1 - 1) >> p.log2_page) - lp0 + 1, kVarPageCache) : 0;
+  for (int i = tid; i < npg; i += kVarThreads) {
+    // a page id outside the pool is clamped into it (never read past)
+    pg_var[i] = min(max(table_row(p, s)[lp0 + i], 0), p.num_pages - 1);
+  }
+  const int n_lo = mb * kVarRows / p.G;
+  const int n_hi = (min(mb * kVarRows + kVarRows, rows) - 1) / p.G;
+  const int nmw = k1 > P ? min((n_hi - n_lo + 1) * p.W, kVarMaskCache) : 0;
+  for (int i = tid; i < nmw; i += kVarThreads) {
+    mk_var[i] = p.masks[(size_t)(n0 + n_lo) * p.W + i];
+  }
+  const int mrow = (valid ? node - n_lo : 0) * p.W;
+  __syncthreads();
 
   f32x16 oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
   float m = -__builtin_inff(), l = 0.f;
 
-  const int32_t* table = p.page_table + (size_t)s * p.max_pps;
   const int pmask = (1 << p.log2_page) - 1;
   // Staging: thread t moves 16-byte chunk ch = t % CR of NCH consecutive
   // keys kq .. kq + NCH - 1, so that its V^T writes cover NCH keys of one
-  // dimension at once.  The next tile is loaded into registers while the
-  // current one is in use.
+  // dimension at once.  Tiles go through a ring of kVarDepth register
+  // buffers: tiles t+1 .. t+kVarDepth-1 are in flight while tile t is
+  // used, and the buffer of tile t is refilled with tile t+kVarDepth as soon
+  // as it has been written to LDS (the loop is unrolled by the ring depth so
+  // that every buffer index is a constant).
   const int ch = tid % CR, kq = (tid / CR) * NCH;
-  u32x4 kc[NCH], vc[NCH];
-  auto load_tile = [&](int t) {
+  u32x4 kc[kVarDepth][NCH], vc[kVarDepth][NCH];
+  // Every load is issued unconditionally (the compiler can then count the
+  // loads in flight and wait for one tile's only): keys past the split end
+  // read the split's last key again (their scores are masked, so these
+  // rows get probability 0), and t is at most the last tile's start.
+  auto load_tile = [&](int t, u32x4 (&kd)[NCH], u32x4 (&vd)[NCH]) {
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
-      const int key = t + kq + j;
-      kc[j] = u32x4{0u, 0u, 0u, 0u};
-      vc[j] = u32x4{0u, 0u, 0u, 0u};
-      if (key < k1) {
-        // a page id outside the pool is clamped into it (never read past)
-        const int page =
-            min(max(table[key >> p.log2_page], 0), p.num_pages - 1);
-        const size_t off =
-            (((size_t)page << p.log2_page) + (key & pmask)) * p.Hkv + g;
-        kc[j] = *reinterpret_cast<const u32x4*>(p.k + off * RB + ch * 16);
-        vc[j] = *reinterpret_cast<const u32x4*>(p.v + off * RB + ch * 16);
-      }
+      const int key = min(t + kq + j, k1 - 1);
+      const int page =
+          pg_var[clampi((key >> p.log2_page) - lp0, 0, kVarPageCache - 1)];
+      const size_t off =
+          (((size_t)page << p.log2_page) + (key & pmask)) * p.Hkv + g;
+      kd[j] = *reinterpret_cast<const u32x4*>(p.k + off * RB + ch * 16);
+      vd[j] = *reinterpret_cast<const u32x4*>(p.v + off * RB + ch * 16);
     }
   };
-  if (k0 < k1) load_tile(k0);
-  for (int t = k0; t < k1; t += kVarTile) {
+  // start of the split's last tile
+  const int t_last = k0 + max((k1 - 1 - k0) / kVarTile, 0) * kVarTile;
+  auto tile = [&](int t, u32x4 (&kcur)[NCH], u32x4 (&vcur)[NCH]) {
     __syncthreads();  // the previous tile's products are done
     // ---- K rows (bf16) and V^T[d][key] to LDS
     constexpr int DPC = 16 / EB;  // dims per chunk
@@ -188,8 +221,8 @@ __global__ __launch_bounds__(kVarThreads, 2) void attn_var_kernel(VarParams p) {
         u32x4 lo4, hi4;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const uint32_t a0 = e4m3x2_to_bf16x2<false>(kc[j][q4]);
-          const uint32_t a1 = e4m3x2_to_bf16x2<true>(kc[j][q4]);
+          const uint32_t a0 = e4m3x2_to_bf16x2<false>(kcur[j][q4]);
+          const uint32_t a1 = e4m3x2_to_bf16x2<true>(kcur[j][q4]);
           if (q4 < 2) {
             lo4[2 * q4] = a0;
             lo4[2 * q4 + 1] = a1;
@@ -197,15 +230,15 @@ __global__ __launch_bounds__(kVarThreads, 2) void attn_var_kernel(VarParams p) {
             hi4[2 * q4 - 4] = a0;
             hi4[2 * q4 - 3] = a1;
           }
-          vv[2 * q4] = e4m3x2_to_bf16x2<false>(vc[j][q4]);
-          vv[2 * q4 + 1] = e4m3x2_to_bf16x2<true>(vc[j][q4]);
+          vv[2 * q4] = e4m3x2_to_bf16x2<false>(vcur[j][q4]);
+          vv[2 * q4 + 1] = e4m3x2_to_bf16x2<true>(vcur[j][q4]);
         }
         *(var_lds_u32x4*)(size_t)(kb + (kq + j) * KP + ch * 32) = lo4;
         *(var_lds_u32x4*)(size_t)(kb + (kq + j) * KP + ch * 32 + 16) = hi4;
       } else {
-        *(var_lds_u32x4*)(size_t)(kb + (kq + j) * KP + ch * 16) = kc[j];
+        *(var_lds_u32x4*)(size_t)(kb + (kq + j) * KP + ch * 16) = kcur[j];
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) vv[q4] = vc[j][q4];
+        for (int q4 = 0; q4 < 4; ++q4) vv[q4] = vcur[j][q4];
       }
       // dim e of this key -> 16-bit slot j of vt[e]
 #pragma unroll
@@ -231,7 +264,10 @@ __global__ __launch_bounds__(kVarThreads, 2) void attn_var_kernel(VarParams p) {
       }
     }
     __syncthreads();
-    if (t + kVarTile < k1) load_tile(t + kVarTile);
+    // refill: past the last tile this reloads the last tile (an L2 hit,
+    // never used), which keeps the count of loads in flight the same on
+    // every path through the loop
+    load_tile(min(t + kVarDepth * kVarTile, t_last), kcur, vcur);
 
     // ---- S^T = K Q^T, two halves of 32 keys
     f32x16 sc[2];
@@ -263,7 +299,9 @@ __global__ __launch_bounds__(kVarThreads, 2) void attn_var_kernel(VarParams p) {
             if (j < 0) {
               on = true;
             } else {
-              on = j < B && ((mrow[j >> 6] >> (j & 63)) & 1u);
+              on = j < B &&
+                   ((mk_var[min(mrow + (j >> 6), kVarMaskCache - 1)] >>
+                     (j & 63)) & 1u);
             }
             bits |= (on ? 1u : 0u) << (4 * q + e);
           }
@@ -312,6 +350,19 @@ __global__ __launch_bounds__(kVarThreads, 2) void attn_var_kernel(VarParams p) {
           oacc[dt] = mfma32x32x16(a, pb, oacc[dt]);
         }
       }
+    }
+  };
+  static_assert(kVarDepth == 3, "the loop below is unrolled by 3");
+  if (k0 < k1) {
+#pragma unroll
+    for (int d = 0; d < kVarDepth; ++d) {
+      load_tile(min(k0 + d * kVarTile, t_last), kc[d], vc[d]);
+    }
+    // the back edge is taken only after all three tiles of an iteration
+    for (int t = k0; t < k1; t += kVarDepth * kVarTile) {
+      tile(t, kc[0], vc[0]);
+      if (t + kVarTile < k1) tile(t + kVarTile, kc[1], vc[1]);
+      if (t + 2 * kVarTile < k1) tile(t + 2 * kVarTile, kc[2], vc[2]);
     }
   }
 

@@ -290,21 +290,30 @@ struct VarPlan {
 };
 
 int make_var_plan(int S, int N, int Hq, int Hkv, int D, int max_prefix_len,
-                  int max_nodes, int req_splits, int cus, VarPlan* out) {
+                  int max_nodes, int page_size, int req_splits, int cus,
+                  VarPlan* out) {
   VarPlan pl;
   const long long G = Hq / Hkv;
   const long long rows = G * max_nodes;
   const long long T = std::max(1LL, (long long)max_prefix_len + max_nodes);
   pl.mblocks = (int)std::max(1LL, (rows + kVarRows - 1) / kVarRows);
   const long long units0 = (long long)S * Hkv * pl.mblocks;
+  // a split's page ids must fit the kernel's LDS copy of them
+  const long long max_chunk = std::max<long long>(
+      kVarTile,
+      ((long long)(kVarPageCache - 1) * page_size) / kVarTile * kVarTile);
+  const long long min_splits = (T + max_chunk - 1) / max_chunk;
+  if (min_splits > kMaxSplits) return TREE_ATTN_ERR_UNSUPPORTED;
   long long splits = req_splits;
   if (splits <= 0) {
     splits = (2LL * cus + units0 - 1) / std::max(1LL, units0);
     splits = std::min(splits, std::max(1LL, T / kMinKeysPerSplit));
   }
-  splits = std::min<long long>(std::max(1LL, splits), kMaxSplits);
+  splits = std::min<long long>(std::max(std::max(1LL, splits), min_splits),
+                               kMaxSplits);
   long long chunk = (T + splits - 1) / splits;
   chunk = (chunk + kVarTile - 1) / kVarTile * kVarTile;
+  chunk = std::min(chunk, max_chunk);
   splits = (T + chunk - 1) / chunk;
   pl.splits = (int)splits;
   pl.chunk = (int)chunk;
@@ -834,7 +843,7 @@ size_t tree_attn_workspace_size_ex(int32_t kv_dtype, int32_t num_seqs,
   }
   VarPlan pl;
   if (make_var_plan(num_seqs, total_nodes, num_q_heads, num_kv_heads,
-                    head_dim, max_prefix_len, max_nodes, num_splits,
+                    head_dim, max_prefix_len, max_nodes, page_size, num_splits,
                     cu_count(), &pl) != TREE_ATTN_OK) {
     return 0;
   }
@@ -880,7 +889,7 @@ int tree_attn_verify_ex(const void* q, const void* k_cache,
   }
   VarPlan pl;
   st = make_var_plan(num_seqs, total_nodes, num_q_heads, num_kv_heads,
-                     head_dim, max_prefix_len, max_nodes, num_splits,
+                     head_dim, max_prefix_len, max_nodes, page_size, num_splits,
                      cu_count(), &pl);
   if (st != TREE_ATTN_OK) return st;
   if (pl.ws_bytes > 0) {
@@ -925,7 +934,8 @@ int tree_attn_verify_ex(const void* q, const void* k_cache,
   if (head_dim == 64) {
     if (fp8) launch_var<64, true>(pl, vp, hs); else launch_var<64, false>(pl, vp, hs);
   } else {
-    if (fp8) launch_var<128, true>(pl, vp, hs); else launch_var<128, false>(pl, vp, hs);
+    // bf16 with head dim 128 never gets here: it runs the tuned kernels
+    launch_var<128, true>(pl, vp, hs);
   }
   if (hipGetLastError() != hipSuccess) return TREE_ATTN_ERR_HIP;
   if (pl.splits > 1) {
