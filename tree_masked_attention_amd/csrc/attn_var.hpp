@@ -33,6 +33,7 @@ namespace tree_attn {
 constexpr int kVarRows = 128;   // query rows per workgroup (4 waves x 32)
 constexpr int kVarTile = 64;    // keys per tile
 constexpr int kVarDepth = 3;    // tiles in registers (in use + in flight)
+constexpr float kVarLazy = 8.f; // lazy-rescale margin, log2 units
 constexpr int kVarPageCache = 1040;       // page ids of a split, in LDS
 constexpr int kVarMaskCache = 129 * 16;   // mask words of a workgroup's nodes
 constexpr int kVarThreads = 256;
@@ -78,18 +79,17 @@ __device__ __forceinline__ bf16x8 var_read_perm(unsigned arr, int row, int cb,
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// Two E4M3 codes (bytes 2 sel, 2 sel + 1 of w) -> two bf16 in one word.
-// v_cvt_pk_f32_fp8 decodes OCP E4M3 on gfx950 (checked against the format
-// definition on all 256 codes); every E4M3 value is a bf16 value, so the
-// top halves of the fp32 results are exact.
+// Two E4M3 codes (bytes 2 kHi, 2 kHi + 1 of w) -> two bf16 in one word,
+// by the direct conversion v_cvt_scalef32_pk_bf16_fp8 with scale 1.  Every
+// E4M3 value is a bf16 value, so the conversion is exact; on gfx950 it
+// gives the bits of v_cvt_pk_f32_fp8 followed by a truncation to bf16 for
+// all 256 codes in every byte position (NaN codes included), and that
+// instruction decodes OCP E4M3 (both checked on the device against the
+// format's definition).
 template <bool kHi>
 __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
-  const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(w, kHi);
-  // elements through scalars: a bit cast of a vector element itself reads
-  // element 0 with this compiler
-  const float f0 = f[0], f1 = f[1];
-  return (__builtin_bit_cast(uint32_t, f0) >> 16) |
-         (__builtin_bit_cast(uint32_t, f1) & 0xffff0000u);
+  return __builtin_bit_cast(
+      uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHi));
 }
 
 __device__ __forceinline__ const int32_t* table_row(const VarParams& p,
@@ -317,9 +317,19 @@ __global__ __launch_bounds__(kVarThreads, 2) void attn_var_kernel(VarParams p) {
       }
     }
     mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = __builtin_fmaxf(m, mx);
-    const float mref = mnew == -__builtin_inff() ? 0.f : mnew;
-    const float alpha = fast_exp2(m - mref);
+    // lazy rescale: the reference max m is raised only when the tile's max
+    // exceeds it by more than kVarLazy (log2 units), which bounds the
+    // probabilities by 2^kVarLazy and leaves O alone on most tiles
+    const bool need = mx > m + kVarLazy;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      const float mnew = need ? mx : m;
+      const float alpha = need ? fast_exp2(m - mnew) : 1.f;
+      l *= alpha;
+      m = mnew;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+    }
+    const float mref = m == -__builtin_inff() ? 0.f : m;
     float ps = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -331,10 +341,7 @@ __global__ __launch_bounds__(kVarThreads, 2) void attn_var_kernel(VarParams p) {
       }
     }
     ps += __shfl_xor(ps, 32);
-    l = l * alpha + ps;
-    m = mnew;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+    l += ps;
     // ---- O^T += V^T P^T
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
