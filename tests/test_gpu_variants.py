@@ -179,3 +179,39 @@ def test_workspace_reuse_across_formats():
         el = (np.abs(l - ref_l) / np.maximum(np.abs(ref_l), 1))[sel].max()
         say(f"  max|dout| {eo:.2e}, max rel dlse {el:.2e}")
         assert eo <= OUT_ATOL and el <= LSE_RTOL
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_decode_exact_through_the_path(d):
+    # One node per sequence, no prefix: the node's only key is itself, its
+    # softmax weight is exactly 1, so out is its V row decoded (times
+    # v_scale = 1), bit for bit in bf16 -- every E4M3 value is a bf16
+    # value.  The V rows hold all 256 codes; out must equal the oracle's
+    # decoding from the format definition (NaN where the code is NaN).
+    import tree_masked_attention_amd.api as api
+    dev = torch.device("cuda:0")
+    S = 256 // d
+    codes = np.arange(256, dtype=np.uint8).reshape(S, d)
+    page = 16
+    k = np.full((S, page, 1, d), 0x38, dtype=np.uint8)  # 1.0 everywhere
+    v = np.full((S, page, 1, d), 0x38, dtype=np.uint8)
+    v[:, 0, 0, :] = codes
+    q = torch.ones((S, 1, d), dtype=torch.bfloat16, device=dev)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    table = t(np.arange(S, dtype=np.int32).reshape(S, 1))
+    prefix = t(np.zeros(S, dtype=np.int32))
+    offs = t(np.arange(S + 1, dtype=np.int32))
+    parents = t(np.full(S, -1, dtype=np.int32))
+    masks, _ = api.build_mask(parents, offs, 1)
+    ones = t(np.ones(1, dtype=np.float32))
+    say(f"[gpu] fp8 decode through the path, d = {d}")
+    out, lse = api.verify_ex(q, t(k), t(v), table, prefix, offs, masks, 0,
+                             1, 1.0 / np.sqrt(d), ones, ones)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().reshape(S, d)
+    from oracle.tree_oracle import widen_e4m3
+    want = widen_e4m3(codes)
+    nan = np.isnan(want)
+    assert (np.isnan(got) == nan).all()
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.isfinite(lse.cpu().numpy()).all()
