@@ -371,3 +371,88 @@ def test_one_launch_merge_reuses_workspace():
                         ref_lse)
         say(f"  max|dout| {eo:.2e}, lse rel {el:.2e}")
         assert eo <= 2e-2 and el <= 1e-3
+
+
+def _split_case_inputs(name, seed, splits):
+    import tree_masked_attention_amd.api as api
+    wl = _case(name, seed, prefix_lens=[2500, 700, 64], tree_sizes=[64, 17, 3])
+    dev = device_inputs(wl)
+    masks, _ = api.build_mask(dev["parents"], dev["tree_offsets"],
+                              wl.max_nodes, wl.mask_words())
+    args = (dev["q"], dev["k_cache"], dev["v_cache"], dev["page_table"],
+            dev["prefix_lens"], dev["tree_offsets"], masks, wl.max_prefix_len,
+            wl.max_nodes, wl.scale)
+    nbytes = api.workspace_size(wl.num_seqs, wl.total_nodes, wl.num_q_heads,
+                                wl.num_kv_heads, wl.head_dim,
+                                wl.max_prefix_len, wl.max_nodes,
+                                wl.page_size, splits)
+    assert nbytes > 65536
+    return wl, dev, args, nbytes
+
+
+def test_overlapping_calls_with_own_workspaces():
+    # two calls on two streams at the same time, each with its own
+    # workspace (the arrival counters live in the workspace): each gives
+    # the bits of the same call made alone
+    import tree_masked_attention_amd.api as api
+    splits = 4
+    wl, dev, args, nbytes = _split_case_inputs("overlap", 160, splits)
+    say("[gpu] overlapping verify calls on two streams")
+    ref_out, ref_lse = api.verify(*args, num_splits=splits)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for st in streams:
+        ws = torch.zeros((nbytes,), dtype=torch.uint8, device="cuda:0")
+        outs.append((torch.empty_like(ref_out), torch.empty_like(ref_lse), ws))
+    torch.cuda.synchronize()  # the zero fills are done before the streams
+    for rep in range(3):
+        for st, (o, l, ws) in zip(streams, outs):
+            with torch.cuda.stream(st):
+                for _ in range(4):
+                    api.verify(*args, num_splits=splits, out=o, lse=l,
+                               workspace=ws, stream=st)
+        torch.cuda.synchronize()
+        for o, l, ws in outs:
+            assert torch.equal(o.view(torch.int16), ref_out.view(torch.int16))
+            assert torch.equal(l, ref_lse)
+            assert int(ws[:65536].count_nonzero()) == 0
+
+
+def test_graph_capture_replays():
+    # tree_attn_verify (with split partials merged in its last workgroups)
+    # captured in a graph: every replay, with eager work and a sync between
+    # replays, gives the bits of the eager call; the arrival counters are
+    # back at zero after each replay
+    import tree_masked_attention_amd.api as api
+    splits = 3
+    wl, dev, args, nbytes = _split_case_inputs("graph", 161, splits)
+    say("[gpu] graph capture of verify, 4 replays")
+    ref_out, ref_lse = api.verify(*args, num_splits=splits)
+    torch.cuda.synchronize()
+    out = torch.empty_like(ref_out)
+    lse = torch.empty_like(ref_lse)
+    ws = torch.zeros((nbytes,), dtype=torch.uint8, device="cuda:0")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        # warm call outside the capture on the capture stream
+        api.verify(*args, num_splits=splits, out=out, lse=lse, workspace=ws,
+                   stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        api.verify(*args, num_splits=splits, out=out, lse=lse, workspace=ws,
+                   stream=torch.cuda.current_stream())
+    for rep in range(4):
+        out.zero_()
+        lse.zero_()
+        scratch = torch.randn(1 << 20, device="cuda:0") * 2.0  # eager work
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)), rep
+        assert torch.equal(lse, ref_lse), rep
+        assert int(ws[:65536].count_nonzero()) == 0
+        del scratch
