@@ -118,6 +118,27 @@ def kernel_source_hash(kernel):
     return h.hexdigest()[:16]
 
 
+def copy_bandwidth(torch, dev, stream, mib=512, reps=10):
+    """HBM bandwidth of a plain device-to-device copy (bytes read + bytes
+    written per second, GB/s), the practical ceiling the attention
+    kernel's HBM figure is also compared with."""
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) * 1e-3 / reps
+    del src, dst
+    return 2 * n / sec / 1e9
+
+
 def measured_traffic(workload, kernel):
     """HBM bytes per launch of one kernel from the committed counter
     summary, when it was taken on the kernel's current sources; else
@@ -953,6 +974,10 @@ def main():
     }
     if phases:
         result["two_launch_form"] = phases
+    if bound == "hbm":
+        cp = copy_bandwidth(torch, dev, stream)
+        result["roofline"]["measured_copy_gbps"] = cp
+        result["roofline"]["frac_of_measured_copy"] = achieved / cp
     if not args.no_cpu_baseline:
         log("[bench] CPU baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
