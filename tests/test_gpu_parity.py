@@ -456,3 +456,46 @@ def test_graph_capture_replays():
         assert torch.equal(lse, ref_lse), rep
         assert int(ws[:65536].count_nonzero()) == 0
         del scratch
+
+
+def test_many_row_blocks_take_the_merge_launch():
+    # 4200 one-node trees x 4 kv heads = 16800 row blocks, more than the
+    # workspace's 16384 arrival counters: tree_attn_verify then merges in a
+    # second launch. Its results equal the two-launch entry points' bit for
+    # bit, and the counter area is not touched. (Inputs drawn on the GPU:
+    # this branch is about the launch choice; parity of the two-launch form
+    # with the oracle is covered above.)
+    import tree_masked_attention_amd.api as api
+    S, P, H, d, page = 4200, 100, 4, 128, 64
+    npp = (P + 1 + page - 1) // page
+    g = torch.Generator(device="cuda:0").manual_seed(170)
+    kw = dict(device="cuda:0", generator=g)
+    q = torch.randn((S, H, d), **kw).to(torch.bfloat16)
+    k = torch.randn((S * npp, page, H, d), **kw).to(torch.bfloat16)
+    v = torch.randn((S * npp, page, H, d), **kw).to(torch.bfloat16)
+    i32 = dict(dtype=torch.int32, device="cuda:0")
+    table = torch.arange(S * npp, **i32).view(S, npp)
+    prefix = torch.full((S,), P, **i32)
+    offs = torch.arange(S + 1, **i32)
+    parents = torch.full((S,), -1, **i32)
+    masks, bad = api.build_mask(parents, offs, 1)
+    args = (q, k, v, table, prefix, offs, masks, P, 1, d ** -0.5)
+    plan = api.describe_plan(S, S, H, H, d, P, 1, page, 2)
+    say(f"[gpu] {S} one-node trees x {H} kv heads, plan {plan}")
+    assert plan["splits"] == 2
+    nbytes = api.workspace_size(S, S, H, H, d, P, 1, page, 2)
+    ws = torch.zeros((nbytes,), dtype=torch.uint8, device="cuda:0")
+    out1, lse1 = api.verify(*args, num_splits=2, workspace=ws)
+    ws2 = torch.zeros_like(ws)
+    out2 = torch.empty_like(out1)
+    lse2 = torch.empty_like(lse1)
+    api.verify(*args, num_splits=2, out=out2, lse=lse2, workspace=ws2,
+               phase="attend")
+    api.verify(*args, num_splits=2, out=out2, lse=lse2, workspace=ws2,
+               phase="merge")
+    torch.cuda.synchronize()
+    assert (bad.cpu() == -1).all()
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(lse1, lse2)
+    assert torch.isfinite(lse1).all()
+    assert int(ws[:65536].count_nonzero()) == 0
