@@ -37,7 +37,6 @@ constexpr float kVarLazy = 8.f; // lazy-rescale margin, log2 units
 constexpr int kVarPageCache = 1040;       // page ids of a split, in LDS
 constexpr int kVarMaskCache = 129 * 16;   // mask words of a workgroup's nodes
 constexpr int kVarThreads = 256;
-constexpr int kVarVPitch = kVarTile * 2 + 8;  // bytes per V^T row in LDS
 
 struct VarParams {
   const __bf16* q;             // [N][Hq][D]
@@ -63,21 +62,19 @@ struct VarParams {
 typedef __attribute__((address_space(3))) u32x4 var_lds_u32x4;
 typedef __attribute__((address_space(3))) u32x2 var_lds_u32x2;
 typedef __attribute__((address_space(3))) __bf16 var_lds_bf16;
+typedef short var_s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) var_s16x4 var_lds_s16x4;
+
+// Transposing LDS read (ds_read_b64_tr_b16): four 16-bit values of four
+// consecutive rows at one column for each lane.
+__device__ __forceinline__ var_s16x4 var_read_tr(unsigned addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((var_lds_s16x4*)(size_t)addr);
+}
 
 __device__ __forceinline__ bf16x8 var_read16(unsigned addr) {
   return __builtin_bit_cast(bf16x8, *(const var_lds_u32x4*)(size_t)addr);
 }
 
-// A operand whose B operand is an accumulator tile (runs of 4 keys per lane
-// half): keys cb + 4 half .. +3 and cb + 8 + 4 half .. +3 of V^T row `row`.
-__device__ __forceinline__ bf16x8 var_read_perm(unsigned arr, int row, int cb,
-                                                int half) {
-  const unsigned a = arr + row * kVarVPitch + (cb + 4 * half) * 2;
-  const u32x2 x = *(const var_lds_u32x2*)(size_t)a;
-  const u32x2 y = *(const var_lds_u32x2*)(size_t)(a + 16);
-  const u32x4 r = {x.x, x.y, y.x, y.y};
-  return __builtin_bit_cast(bf16x8, r);
-}
 
 // Two E4M3 codes (bytes 2 kHi, 2 kHi + 1 of w) -> two bf16 in one word,
 // by the direct conversion v_cvt_scalef32_pk_bf16_fp8 with scale 1.  Every
@@ -106,9 +103,14 @@ __global__ __launch_bounds__(kVarThreads, 2) void attn_var_kernel(VarParams p) {
   constexpr int NCH = kVarTile * CR / kVarThreads;  // chunks per thread
   constexpr int DT = D / 32;              // output tiles of 32 dims
   constexpr int KS = D / 16;              // k-steps of the score product
+  // V goes to LDS row-major in bf16, one 256-byte row per key (half of it
+  // unused for head dim 64), 16-byte chunk c of row r at slot c ^ 4 (r & 3),
+  // and the V^T operand comes from transposing reads: the tuned 128-row
+  // kernel's layout and read addresses, whose dim block dt reads chunks
+  // 4 dt .. 4 dt + 3 only.
   static_assert(NCH >= 1 && kVarTile * CR % kVarThreads == 0, "tile split");
   __shared__ __align__(16) unsigned char kl[kVarTile * KP];
-  __shared__ __align__(16) unsigned char vl[D * kVarVPitch];
+  __shared__ __align__(16) unsigned char vl[kVarTile * 256];
   __shared__ int pg_var[kVarPageCache];
   __shared__ uint64_t mk_var[kVarMaskCache];
   const unsigned kb =
@@ -133,6 +135,9 @@ __global__ __launch_bounds__(kVarThreads, 2) void attn_var_kernel(VarParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
+  // transposing-read lane offsets (the tuned kernels' V operand pattern)
+  const int ty = (lane & 15) >> 2;
+  const int tx = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
   const int r = mb * kVarRows + w * 32 + col;  // this lane's query row
   const bool valid = r < rows;
   const int node = valid ? r / p.G : 0;
@@ -211,56 +216,32 @@ __global__ __launch_bounds__(kVarThreads, 2) void attn_var_kernel(VarParams p) {
   const int t_last = k0 + max((k1 - 1 - k0) / kVarTile, 0) * kVarTile;
   auto tile = [&](int t, u32x4 (&kcur)[NCH], u32x4 (&vcur)[NCH]) {
     __syncthreads();  // the previous tile's products are done
-    // ---- K rows (bf16) and V^T[d][key] to LDS
-    constexpr int DPC = 16 / EB;  // dims per chunk
-    uint32_t vt[DPC][(NCH + 1) / 2];  // V^T: NCH keys of each dim, packed
+    // ---- K rows and V rows (bf16) to LDS
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
-      uint32_t vv[DPC / 2];  // this key's dims as bf16 pairs
+      const int r = kq + j, sw = 4 * (r & 3);
+      const unsigned vr = vb + r * 256;
       if (FP8) {
-        u32x4 lo4, hi4;
+        // 16 codes = dims 16 ch .. 16 ch + 15 = bf16 chunks 2 ch, 2 ch + 1
+        u32x4 k0, k1, v0, v1;
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const uint32_t a0 = e4m3x2_to_bf16x2<false>(kcur[j][q4]);
-          const uint32_t a1 = e4m3x2_to_bf16x2<true>(kcur[j][q4]);
-          if (q4 < 2) {
-            lo4[2 * q4] = a0;
-            lo4[2 * q4 + 1] = a1;
-          } else {
-            hi4[2 * q4 - 4] = a0;
-            hi4[2 * q4 - 3] = a1;
-          }
-          vv[2 * q4] = e4m3x2_to_bf16x2<false>(vcur[j][q4]);
-          vv[2 * q4 + 1] = e4m3x2_to_bf16x2<true>(vcur[j][q4]);
+        for (int q4 = 0; q4 < 2; ++q4) {
+          k0[2 * q4] = e4m3x2_to_bf16x2<false>(kcur[j][q4]);
+          k0[2 * q4 + 1] = e4m3x2_to_bf16x2<true>(kcur[j][q4]);
+          k1[2 * q4] = e4m3x2_to_bf16x2<false>(kcur[j][q4 + 2]);
+          k1[2 * q4 + 1] = e4m3x2_to_bf16x2<true>(kcur[j][q4 + 2]);
+          v0[2 * q4] = e4m3x2_to_bf16x2<false>(vcur[j][q4]);
+          v0[2 * q4 + 1] = e4m3x2_to_bf16x2<true>(vcur[j][q4]);
+          v1[2 * q4] = e4m3x2_to_bf16x2<false>(vcur[j][q4 + 2]);
+          v1[2 * q4 + 1] = e4m3x2_to_bf16x2<true>(vcur[j][q4 + 2]);
         }
-        *(var_lds_u32x4*)(size_t)(kb + (kq + j) * KP + ch * 32) = lo4;
-        *(var_lds_u32x4*)(size_t)(kb + (kq + j) * KP + ch * 32 + 16) = hi4;
+        *(var_lds_u32x4*)(size_t)(kb + r * KP + ch * 32) = k0;
+        *(var_lds_u32x4*)(size_t)(kb + r * KP + ch * 32 + 16) = k1;
+        *(var_lds_u32x4*)(size_t)(vr + (((2 * ch) ^ sw) << 4)) = v0;
+        *(var_lds_u32x4*)(size_t)(vr + (((2 * ch + 1) ^ sw) << 4)) = v1;
       } else {
-        *(var_lds_u32x4*)(size_t)(kb + (kq + j) * KP + ch * 16) = kcur[j];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) vv[q4] = vcur[j][q4];
-      }
-      // dim e of this key -> 16-bit slot j of vt[e]
-#pragma unroll
-      for (int e = 0; e < DPC; ++e) {
-        const uint32_t x = (vv[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-        if ((j & 1) == 0) {
-          vt[e][j >> 1] = x;
-        } else {
-          vt[e][j >> 1] |= x << 16;
-        }
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < DPC; ++e) {
-      const unsigned a = vb + (DPC * ch + e) * kVarVPitch + kq * 2;
-      if (NCH == 4) {
-        *(var_lds_u32x2*)(size_t)a = u32x2{vt[e][0], vt[e][(NCH + 1) / 2 - 1]};
-      } else if (NCH == 2) {
-        *(__attribute__((address_space(3))) uint32_t*)(size_t)a = vt[e][0];
-      } else {
-        *(var_lds_bf16*)(size_t)a =
-            __builtin_bit_cast(__bf16, (unsigned short)(vt[e][0] & 0xffffu));
+        *(var_lds_u32x4*)(size_t)(kb + r * KP + ch * 16) = kcur[j];
+        *(var_lds_u32x4*)(size_t)(vr + ((ch ^ sw) << 4)) = vcur[j];
       }
     }
     __syncthreads();
@@ -352,8 +333,12 @@ __global__ __launch_bounds__(kVarThreads, 2) void attn_var_kernel(VarParams p) {
         for (int e = 0; e < 8; ++e) pb[e] = (__bf16)sc[kt][8 * s2 + e];
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const bf16x8 a =
-              var_read_perm(vb, dt * 32 + col, kt * 32 + 16 * s2, half);
+          const unsigned va = vb + (kt * 32 + 16 * s2 + 4 * half + ty) * 256 +
+                              ((4 * (dt ^ ty) + tx) << 4) + 8 * (lane & 1);
+          const var_s16x4 lo = var_read_tr(va);
+          const var_s16x4 hi = var_read_tr(va + 8 * 256);
+          const bf16x8 a = __builtin_bit_cast(
+              bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           oacc[dt] = mfma32x32x16(a, pb, oacc[dt]);
         }
       }
