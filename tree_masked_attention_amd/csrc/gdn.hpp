@@ -741,27 +741,11 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_commit_kernel(
     cf[j] = n >= 0 ? p.g[(size_t)n * H + h] : 0.f;
   }
   __syncthreads();
-  if (tid == 0) {
-    // suffix sums of g from the end of the path, over LDS
-    float gsum = 0.f;
-    for (int j = tau - 1; j >= 0; --j) {
-      const float gj = cf[j];
-      cf[j] = fast_exp2(gsum * kLog2e);
-      gsum += gj;
-    }
-    gam_n = fast_exp2(gsum * kLog2e);
-  }
-  __syncthreads();
-  const float gn = gam_n;
-#pragma unroll
-  for (int m = 0; m < 16; ++m) acc[m] *= gn;
-
-  for (int j0 = 0; j0 < tau; j0 += kGdnCommitChunk) {
-    const int nc = min(kGdnCommitChunk, tau - j0);
-    // 32 nodes x (16 k chunks + 32 u chunks) of 16 bytes, six per thread,
-    // all loads issued before the LDS writes
-    constexpr int kChunks = kGdnCommitChunk * 48 / kGdnThreads;
-    u32x4 raw[kChunks];
+  // the first 32 nodes' k (bf16) and u (fp32): 32 x (16 + 32) chunks of 16
+  // bytes, six per thread, issued before the decays are summed
+  constexpr int kChunks = kGdnCommitChunk * 48 / kGdnThreads;
+  u32x4 raw[kChunks];
+  auto load_chunk = [&](int j0, int nc) {
 #pragma unroll
     for (int q = 0; q < kChunks; ++q) {
       const int x = tid + kGdnThreads * q;
@@ -774,6 +758,36 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_commit_kernel(
             : *reinterpret_cast<const u32x4*>(p.u + o + (ch - 16) * 4);
       }
     }
+  };
+  load_chunk(0, min(kGdnCommitChunk, tau));
+  if (tid < 64) {
+    // suffix sums of g from the end of the path (cf[j] becomes
+    // e^{sum of g over the nodes after j}), 64 nodes per round: an
+    // inclusive suffix scan within the wave plus the total of the rounds
+    // after it
+    float carry = 0.f;
+    for (int base = ((tau - 1) >> 6) << 6; base >= 0; base -= 64) {
+      const int j = base + tid;
+      const float gj = j < tau ? cf[j] : 0.f;
+      float x = gj;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const float y = __shfl_down(x, d);
+        if (tid + d < 64) x += y;
+      }
+      if (j < tau) cf[j] = fast_exp2((carry + (x - gj)) * kLog2e);
+      carry += __shfl(x, 0);
+    }
+    if (tid == 0) gam_n = fast_exp2(carry * kLog2e);
+  }
+  __syncthreads();
+  const float gn = gam_n;
+#pragma unroll
+  for (int m = 0; m < 16; ++m) acc[m] *= gn;
+
+  for (int j0 = 0; j0 < tau; j0 += kGdnCommitChunk) {
+    const int nc = min(kGdnCommitChunk, tau - j0);
+    if (j0 > 0) load_chunk(j0, nc);
 #pragma unroll
     for (int q = 0; q < kChunks; ++q) {
       const int x = tid + kGdnThreads * q;
