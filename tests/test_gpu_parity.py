@@ -499,3 +499,40 @@ def test_many_row_blocks_take_the_merge_launch():
     assert torch.equal(lse1, lse2)
     assert torch.isfinite(lse1).all()
     assert int(ws[:65536].count_nonzero()) == 0
+
+
+@pytest.mark.parametrize("seed", list(range(700, 716)))
+def test_random_split_merge_repeated(seed):
+    # random shapes (both kernels) with random forced splits, three calls in
+    # a row on one workspace: every call gives the two-launch form's bits
+    # and leaves the arrival counters at zero
+    import tree_masked_attention_amd.api as api
+    wl, _ = _random_case(seed, wide=bool(seed % 2))
+    splits = int(np.random.default_rng(seed + 1).integers(2, 9))
+    dev = device_inputs(wl)
+    masks, _ = api.build_mask(dev["parents"], dev["tree_offsets"],
+                              max(wl.max_nodes, 1), wl.mask_words())
+    args = (dev["q"], dev["k_cache"], dev["v_cache"], dev["page_table"],
+            dev["prefix_lens"], dev["tree_offsets"], masks, wl.max_prefix_len,
+            wl.max_nodes, wl.scale)
+    plan = api.describe_plan(wl.num_seqs, wl.total_nodes, wl.num_q_heads,
+                             wl.num_kv_heads, wl.head_dim, wl.max_prefix_len,
+                             wl.max_nodes, wl.page_size, splits)
+    say(f"[gpu] random split merge {seed}: P={list(wl.prefix_lens)} "
+        f"B={list(wl.tree_sizes)} plan={plan}")
+    nbytes = api.workspace_size(wl.num_seqs, wl.total_nodes, wl.num_q_heads,
+                                wl.num_kv_heads, wl.head_dim,
+                                wl.max_prefix_len, wl.max_nodes,
+                                wl.page_size, splits)
+    ws2 = torch.zeros((max(nbytes, 256),), dtype=torch.uint8, device="cuda:0")
+    ref_out, ref_lse = api.verify(*args, num_splits=splits, workspace=ws2,
+                                  phase="attend")
+    api.verify(*args, num_splits=splits, out=ref_out, lse=ref_lse,
+               workspace=ws2, phase="merge")
+    ws = torch.zeros_like(ws2)
+    for rep in range(3):
+        out, lse = api.verify(*args, num_splits=splits, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)), rep
+        assert torch.equal(lse, ref_lse), rep
+        assert int(ws[:65536].count_nonzero()) == 0
