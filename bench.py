@@ -29,12 +29,13 @@ import argparse
 import json
 import math
 import os
+import platform
 import sys
 import time
 
 import numpy as np
 
-DEFAULT_WORKLOAD = "qwen3-8b-b256-p4k"
+DEFAULT_WORKLOAD = "long-32k-4x-b256"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
 ROTATE_BYTES = 1 << 30
@@ -54,6 +55,10 @@ def parse():
     ap.add_argument("--splits", type=int, default=0,
                     help="0 = planned by the library")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", action="store_true",
+                    help="verify: time the chosen workload alone (by "
+                         "default the other standard workloads are timed "
+                         "after it and summarised in the same line)")
     ap.add_argument("--phases", action="store_true",
                     help="also time the two-launch form of the verification "
                          "(attention kernel writing split partials, then "
@@ -99,7 +104,7 @@ TRAFFIC_FILE = os.path.join(HERE, "profiles", "hbm_traffic.txt")
 KERNEL_SOURCES = {
     "attn_fwd128h_kernel": ("common.hpp", "attn_merge.hpp", "attn_fwd.hpp",
                             "attn_fwd128h.hpp"),
-    "attn_fwd256_kernel<8>": ("common.hpp", "attn_merge.hpp", "attn_fwd.hpp",
+    "attn_fwd256_kernel": ("common.hpp", "attn_merge.hpp", "attn_fwd.hpp",
                               "attn_fwd8.hpp"),
     "attn_merge_kernel": ("common.hpp", "attn_merge.hpp"),
     "gdn_verify_kernel": ("common.hpp", "gdn.hpp"),
@@ -218,27 +223,55 @@ def algorithmic_work(wl, with_output=True, kv_bytes=None):
 # CPU baseline: the oracle as it stands, on the host cores
 # --------------------------------------------------------------------------
 
-def cpu_baseline(wl, target_s):
-    import oracle
+def cpu_model():
+    """Model name of the host CPU (for the baseline's record)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()]
-                      or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()]
+                   or [1])
     except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
-    reps, t = 0, 0.0
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(wl, target_s):
+    """The oracle as it stands (mask build + fp64 attention) on whole
+    sequences of the workload, in order and cycling, until about target_s
+    seconds have passed (at least one sequence, at most about 30 s); the
+    rate is the tree tokens of the sequences done per second."""
+    import oracle
+    threads = blas_threads()
+    S = wl.num_seqs
+    W = wl.mask_words()
+    done, seqs, t = 0, 0, 0.0
     t0 = time.perf_counter()
     while True:
-        oracle.workload_masks(wl)
-        oracle.workload_attention(wl)
-        reps += 1
+        s = seqs % S
+        a, b = int(wl.tree_offsets[s]), int(wl.tree_offsets[s + 1])
+        oracle.ancestor_masks(wl.parents[a:b], np.array([0, b - a]), W)
+        oracle.workload_attention(wl, seq_ids=[s])
+        done += b - a
+        seqs += 1
         t = time.perf_counter() - t0
-        if t >= target_s or t / reps * (reps + 1) > 30.0:
+        if t >= target_s or t / seqs * (seqs + 1) > 30.0:
             break
-    return {"value": wl.total_nodes * reps / t, "unit": "tree tokens/s",
-            "cores": int(threads), "kind": "oracle",
-            "sample": f"{reps} full pass(es) of workload {wl.name} "
-                      f"(mask build + fp64 attention), {t:.1f} s"}
+    return {"value": done / t, "unit": "tree tokens/s",
+            "cores": int(threads), "cpu_model": cpu_model(),
+            "kind": "oracle",
+            "sample": f"{seqs} sequence(s) of workload {wl.name}, in "
+                      f"order and cycling ({done} tree tokens; one pass of "
+                      f"the workload has {wl.total_nodes}): mask build + "
+                      f"fp64 attention over all kv heads, {t:.1f} s"}
 
 
 def cpu_baseline_accept(wl, tokens, target_s):
@@ -256,7 +289,7 @@ def cpu_baseline_accept(wl, tokens, target_s):
         if el >= target_s or el / reps * (reps + 1) > 30.0:
             break
     return {"value": wl.total_nodes * reps / el, "unit": "tree tokens/s",
-            "cores": 1, "kind": "oracle",
+            "cores": 1, "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"{reps} full pass(es) of workload {wl.name} "
                       f"(acceptance + commit on copies of the caches), "
                       f"{el:.1f} s"}
@@ -487,7 +520,7 @@ def tree_build_stage(args, torch, api, wl, stream):
                 break
         result["cpu_baseline"] = {
             "value": S * B * reps / el, "unit": "tree nodes/s", "cores": 1,
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"{reps} full pass(es) of the same {S} trees, {el:.1f} s"}
     print(json.dumps(result), flush=True)
     return 0
@@ -687,7 +720,7 @@ def gdn_stage(args, torch, api):
         el = time.perf_counter() - t0
         result["cpu_baseline"] = {
             "value": B * pairs / H / el, "unit": "tree tokens/s",
-            "cores": 1, "kind": "oracle",
+            "cores": 1, "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"{pairs} (tree, head) pairs of {B} nodes, first "
                       f"trees first, all heads of a tree in turn, {el:.1f} s"}
     print(json.dumps(result), flush=True)
@@ -698,38 +731,14 @@ def gdn_stage(args, torch, api):
 # GPU timing
 # --------------------------------------------------------------------------
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only "
-              f"(--gpus {args.gpus} requested); nothing was run.",
-              file=sys.stderr)
-        return 2
-    import torch
-    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
-    import tree_masked_attention_amd.api as api
-    from tree_masked_attention_amd.workloads import standard_workload
+# --------------------------------------------------------------------------
+# verification timing
+# --------------------------------------------------------------------------
 
-    assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    if args.copy_calibration:
-        return copy_calibration(torch)
-
-    if args.stage == "gdn":
-        return gdn_stage(args, torch, api)
-    log(f"[bench] drawing workload {args.workload}")
-    wl = standard_workload(args.workload, kv_format=args.kv,
-                           head_dim=args.head_dim)
-    variant = args.kv != "bf16" or args.head_dim != 128
-    if args.stage == "tree-build":
-        return tree_build_stage(args, torch, api, wl,
-                                torch.cuda.current_stream())
-    alg_bytes, alg_flops = algorithmic_work(wl)
-    ai = alg_flops / alg_bytes
-    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
-    bound = "mfma" if ai > ridge else "hbm"
-
+def device_sets(torch, wl, dev):
+    """Copies of the workload's inputs on the device, enough of them
+    (>= 1 GiB in all) that no step finds its K/V in the 256 MB Infinity
+    Cache left there by the previous step."""
     bf = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
     if wl.kv_format == "bf16":
         kv_host = dict(k=bf(wl.k_cache), v=bf(wl.v_cache))
@@ -745,189 +754,268 @@ def main():
                 parents=torch.from_numpy(wl.parents))
     per_copy = sum(t.numel() * t.element_size() for t in host.values())
     copies = int(min(256, max(2, math.ceil(ROTATE_BYTES / per_copy))))
-    log(f"[bench] {per_copy / 2**20:.1f} MiB per input set, {copies} copies")
-    sets = []
-    for _ in range(copies):
-        sets.append({k: t.to(dev) for k, t in host.items()})
+    log(f"[bench] {wl.name}: {per_copy / 2**20:.1f} MiB per input set, "
+        f"{copies} copies")
+    sets = [{k: t.to(dev) for k, t in host.items()} for _ in range(copies)]
+    return sets, copies
 
+
+def per_launch(torch, stream, fn, pick, steps):
+    """Milliseconds per call of K calls back to back on the launch stream
+    between one pair of events (input copies rotated): the kernel's own
+    time plus the dispatch gap between consecutive launches."""
+    for i in range(3):
+        fn(*pick(i))
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(steps):
+        if fn(*pick(i)) != 0:
+            raise RuntimeError("tree_attn call failed")
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def per_call(torch, stream, fn, pick, reps=20):
+    """Median and minimum over single calls: an event between every two
+    consecutive calls of a back-to-back run (input copies rotated), so
+    each interval is one call plus its dispatch gap, without the host's
+    launch latency."""
+    for i in range(3):
+        fn(*pick(i))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(reps):
+        if fn(*pick(i)) != 0:
+            raise RuntimeError("tree_attn call failed")
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    times = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(reps))
+    return {"median": times[len(times) // 2], "min": times[0], "calls": reps}
+
+
+class VerifyBench:
+    """Pre-marshalled C-ABI calls of one workload (mask build + verify),
+    one argument list per input copy."""
+
+    def __init__(self, torch, api, wl, sets, splits, stream):
+        self.torch, self.api, self.wl, self.stream = torch, api, wl, stream
+        dev = sets[0]["q"].device
+        N, Hq, d = wl.q.shape
+        S, W = wl.num_seqs, wl.mask_words()
+        max_b = max(wl.max_nodes, 1)
+        self.variant = wl.kv_format != "bf16" or wl.head_dim != 128
+        self.masks = torch.empty((N, W), dtype=torch.int64, device=dev)
+        self.bad = torch.empty((max(S, 1),), dtype=torch.int32, device=dev)
+        self.out = torch.empty((N, Hq, d), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((N, Hq), dtype=torch.float32, device=dev)
+        kvd = api.KV_FP8_E4M3 if wl.kv_format == "e4m3" else api.KV_BF16
+        self.ws_bytes = int(api._lib.tree_attn_workspace_size_ex(
+            kvd, S, N, Hq, wl.num_kv_heads, d, wl.max_prefix_len,
+            wl.max_nodes, wl.page_size, splits))
+        # zero-filled once: the split launch's arrival counters start at 0
+        self.ws = torch.zeros((max(self.ws_bytes, 256),), dtype=torch.uint8,
+                              device=dev)
+        sptr = stream.cuda_stream
+        ws, masks = self.ws, self.masks
+        self.calls = []
+        for c in sets:
+            mask_args = (c["parents"].data_ptr(), c["offs"].data_ptr(), S, N,
+                         max_b, W, masks.data_ptr(), self.bad.data_ptr(),
+                         sptr)
+            if self.variant:
+                ver_args = (c["q"].data_ptr(), c["k"].data_ptr(),
+                            c["v"].data_ptr(), kvd,
+                            c["ks"].data_ptr() if "ks" in c else None,
+                            c["vs"].data_ptr() if "vs" in c else None,
+                            c["table"].data_ptr(), wl.max_pages_per_seq,
+                            wl.num_pages, wl.page_size,
+                            c["prefix"].data_ptr(), c["offs"].data_ptr(),
+                            masks.data_ptr(), W, S, N, wl.max_prefix_len,
+                            wl.max_nodes, Hq, wl.num_kv_heads, d, wl.scale,
+                            splits, self.out.data_ptr(), self.lse.data_ptr(),
+                            ws.data_ptr(), ws.numel(), sptr)
+            else:
+                ver_args = (c["q"].data_ptr(), c["k"].data_ptr(),
+                            c["v"].data_ptr(), c["table"].data_ptr(),
+                            wl.max_pages_per_seq, wl.num_pages, wl.page_size,
+                            c["prefix"].data_ptr(), c["offs"].data_ptr(),
+                            masks.data_ptr(), W, S, N, wl.max_prefix_len,
+                            wl.max_nodes, Hq, wl.num_kv_heads, d, wl.scale,
+                            splits, self.out.data_ptr(), self.lse.data_ptr(),
+                            ws.data_ptr(), ws.numel(), sptr)
+            self.calls.append((mask_args, ver_args))
+        self.f_mask = api._lib.tree_attn_build_mask
+        self.f_ver = (api._lib.tree_attn_verify_ex if self.variant
+                      else api._lib.tree_attn_verify)
+        if self.variant:
+            self.plan = {"kernel": "attn_var_kernel (+ attn_var_merge_kernel)",
+                         "rows": 128, "workspace_bytes": self.ws_bytes}
+        else:
+            self.plan = api.describe_plan(S, N, Hq, wl.num_kv_heads, d,
+                                          wl.max_prefix_len, wl.max_nodes,
+                                          wl.page_size, splits)
+
+    def mask_args(self, i):
+        return self.calls[i % len(self.calls)][0]
+
+    def ver_args(self, i):
+        return self.calls[i % len(self.calls)][1]
+
+    def step(self, i):
+        return self.f_mask(*self.mask_args(i)) | self.f_ver(*self.ver_args(i))
+
+    def warm(self, warmup):
+        """W warmup steps, then as many more as fill WARM_SECONDS, enqueued
+        back to back like the timed steps.  Under sustained back-to-back
+        load the GPU's power management lowers clocks, so the whole-step
+        figure is the sustained rate; the per-launch figures, taken with
+        small gaps between launches, run at higher clocks."""
+        torch = self.torch
+        t_w = time.perf_counter()
+        n = 0
+        for _ in range(max(warmup, 1)):
+            if self.step(n) != 0:
+                raise RuntimeError("tree_attn call failed during warmup")
+            n += 1
+        torch.cuda.synchronize()
+        per = (time.perf_counter() - t_w) / n
+        extra = int(max(0.0, WARM_SECONDS - (time.perf_counter() - t_w)) /
+                    per)
+        for _ in range(extra):
+            self.step(n)
+            n += 1
+        torch.cuda.synchronize()
+        log(f"[bench] warmup: {n} steps ({warmup} requested), "
+            f"{time.perf_counter() - t_w:.2f} s")
+        return n
+
+    def kernel_name(self):
+        if self.variant:
+            return "attn_var_kernel"
+        return ("attn_fwd256_kernel" if self.plan["rows"] == 256
+                else "attn_fwd128h_kernel")
+
+    def measure(self, steps):
+        """Per-launch verify and mask-build times and the verify launch's
+        algorithmic rates (the one attention launch does all the method's
+        flops and bytes, its merge included)."""
+        torch, st = self.torch, self.stream
+        mask_ms = per_launch(torch, st, self.f_mask, self.mask_args, steps)
+        ver_ms = per_launch(torch, st, self.f_ver, self.ver_args, steps)
+        call = per_call(torch, st, self.f_ver, self.ver_args)
+        nbytes, flops = algorithmic_work(self.wl)
+        ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+        sec = ver_ms * 1e-3
+        return {"verify_us": ver_ms * 1e3, "verify_call_us": call,
+                "mask_build_us": mask_ms * 1e3, "alg_bytes": nbytes,
+                "alg_flops": flops,
+                "bound": "mfma" if flops / nbytes > ridge else "hbm",
+                "tflops": flops / sec / 1e12, "hbm_gbps": nbytes / sec / 1e9,
+                "plan": self.plan}
+
+
+def summary_entry(wl, m):
+    """One workload's line of the all-workload summary."""
+    return {"verify_us": m["verify_us"],
+            "verify_call_median_us": m["verify_call_us"]["median"],
+            "tree_tokens_per_s": wl.total_nodes / (m["verify_us"] * 1e-6),
+            "bound": m["bound"],
+            "tflops": m["tflops"],
+            "frac_mfma_bf16": m["tflops"] / MFMA_BF16_PEAK_TFLOPS,
+            "hbm_gbps": m["hbm_gbps"],
+            "frac_hbm": m["hbm_gbps"] / HBM_PEAK_GBPS,
+            "alg_bytes": m["alg_bytes"], "alg_flops": m["alg_flops"],
+            "plan": m["plan"]}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only "
+              f"(--gpus {args.gpus} requested); nothing was run.",
+              file=sys.stderr)
+        return 2
+    import torch
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import tree_masked_attention_amd.api as api
+    from tree_masked_attention_amd.workloads import (STANDARD_ORDER,
+                                                     standard_workload)
+
+    assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        return copy_calibration(torch)
+
+    if args.stage == "gdn":
+        return gdn_stage(args, torch, api)
+    log(f"[bench] drawing workload {args.workload}")
+    wl = standard_workload(args.workload, kv_format=args.kv,
+                           head_dim=args.head_dim)
+    if args.stage == "tree-build":
+        return tree_build_stage(args, torch, api, wl,
+                                torch.cuda.current_stream())
     stream = torch.cuda.current_stream()
+    sets, copies = device_sets(torch, wl, dev)
     if args.stage == "accept-commit":
         return accept_commit_stage(args, torch, api, wl, sets, stream)
 
-    N, Hq, d = wl.q.shape
-    S = wl.num_seqs
-    W = wl.mask_words()
-    max_b = max(wl.max_nodes, 1)
-    masks = torch.empty((N, W), dtype=torch.int64, device=dev)
-    bad = torch.empty((max(S, 1),), dtype=torch.int32, device=dev)
-    out = torch.empty((N, Hq, d), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((N, Hq), dtype=torch.float32, device=dev)
-    kvd = api.KV_FP8_E4M3 if wl.kv_format == "e4m3" else api.KV_BF16
-    ws_bytes = int(api._lib.tree_attn_workspace_size_ex(
-        kvd, S, N, Hq, wl.num_kv_heads, d, wl.max_prefix_len, wl.max_nodes,
-        wl.page_size, args.splits))
-    # zero-filled once: the split launch's arrival counters start at zero
-    ws = torch.zeros((max(ws_bytes, 256),), dtype=torch.uint8, device=dev)
-    sptr = stream.cuda_stream
-
-    # pre-marshalled C-ABI argument lists, one per input copy
-    calls = []
-    for c in sets:
-        mask_args = (c["parents"].data_ptr(), c["offs"].data_ptr(), S, N,
-                     max_b, W, masks.data_ptr(), bad.data_ptr(), sptr)
-        if variant:
-            ver_args = (c["q"].data_ptr(), c["k"].data_ptr(),
-                        c["v"].data_ptr(), kvd,
-                        c["ks"].data_ptr() if "ks" in c else None,
-                        c["vs"].data_ptr() if "vs" in c else None,
-                        c["table"].data_ptr(), wl.max_pages_per_seq,
-                        wl.num_pages, wl.page_size, c["prefix"].data_ptr(),
-                        c["offs"].data_ptr(), masks.data_ptr(), W, S, N,
-                        wl.max_prefix_len, wl.max_nodes, Hq, wl.num_kv_heads,
-                        d, wl.scale, args.splits, out.data_ptr(),
-                        lse.data_ptr(), ws.data_ptr(), ws.numel(), sptr)
-        else:
-            ver_args = (c["q"].data_ptr(), c["k"].data_ptr(),
-                        c["v"].data_ptr(), c["table"].data_ptr(),
-                        wl.max_pages_per_seq, wl.num_pages, wl.page_size,
-                        c["prefix"].data_ptr(), c["offs"].data_ptr(),
-                        masks.data_ptr(), W, S, N, wl.max_prefix_len,
-                        wl.max_nodes, Hq, wl.num_kv_heads, d, wl.scale,
-                        args.splits, out.data_ptr(), lse.data_ptr(),
-                        ws.data_ptr(), ws.numel(), sptr)
-        calls.append((mask_args, ver_args))
-    f_mask = api._lib.tree_attn_build_mask
-    f_ver = (api._lib.tree_attn_verify_ex if variant
-             else api._lib.tree_attn_verify)
-
-    def step(i):
-        ma, va = calls[i % copies]
-        return f_mask(*ma) | f_ver(*va)
-
-    # W warmup steps, then as many more as fill WARM_SECONDS, enqueued back
-    # to back like the timed steps.  Under sustained back-to-back load the
-    # GPU's power management lowers clocks (long-context kernels go from
-    # ~570 us to 620-770 us within ~20 launches), so the whole-step figure
-    # below is the sustained rate; the per-launch figures, taken with small
-    # gaps between launches, run at higher clocks.
-    t_w = time.perf_counter()
-    n_warm = 0
-    for _ in range(max(args.warmup, 1)):
-        if step(n_warm) != 0:
-            raise RuntimeError("tree_attn call failed during warmup")
-        n_warm += 1
-    torch.cuda.synchronize()
-    per = (time.perf_counter() - t_w) / n_warm
-    extra = int(max(0.0, WARM_SECONDS - (time.perf_counter() - t_w)) / per)
-    for _ in range(extra):
-        step(n_warm)
-        n_warm += 1
-    torch.cuda.synchronize()
-    log(f"[bench] warmup: {n_warm} steps ({args.warmup} requested), "
-        f"{time.perf_counter() - t_w:.2f} s")
-    if (bad[:S] != -1).any():
+    vb = VerifyBench(torch, api, wl, sets, args.splits, stream)
+    n_warm = vb.warm(args.warmup)
+    if (vb.bad[:wl.num_seqs] != -1).any():
         raise RuntimeError("invalid tree in benchmark input")
 
-    # (1) whole-step throughput: K back-to-back steps
+    # (1) whole-step throughput: K back-to-back steps (mask build + verify)
     torch.cuda.synchronize()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     t_start.record(stream)
     for i in range(args.steps):
-        step(i)
+        vb.step(i)
     t_end.record(stream)
     torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_per_step = total_ms / args.steps
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
 
-    # (2) per-launch durations: each launch made K times back to back on
-    #     the launch stream between one pair of events (input copies
-    #     rotated as above), so the figure is the kernel's own time plus
-    #     the dispatch gap between consecutive launches
-    if variant:
-        plan = {"kernel": "attn_var_kernel (+ attn_var_merge_kernel)",
-                "rows": 128, "workspace_bytes": ws_bytes}
-    else:
-        plan = api.describe_plan(S, N, Hq, wl.num_kv_heads, d,
-                                 wl.max_prefix_len, wl.max_nodes,
-                                 wl.page_size, args.splits)
-    f_att = api._lib.tree_attn_verify_attend
-    f_mer = api._lib.tree_attn_verify_merge
-
-    def per_launch(fn, pick):
-        for i in range(3):
-            fn(*pick(i))
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for i in range(args.steps):
-            if fn(*pick(i)) != 0:
-                raise RuntimeError("tree_attn call failed")
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / args.steps
-
-    def per_call(fn, pick, reps=20):
-        """Median and minimum over single calls: an event between every two
-        consecutive calls of a back-to-back run (input copies rotated), so
-        each interval is one call plus its dispatch gap, without the host's
-        launch latency."""
-        for i in range(3):
-            fn(*pick(i))
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
-        torch.cuda.synchronize()
-        ev[0].record(stream)
-        for i in range(reps):
-            if fn(*pick(i)) != 0:
-                raise RuntimeError("tree_attn call failed")
-            ev[i + 1].record(stream)
-        torch.cuda.synchronize()
-        times = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3
-                       for i in range(reps))
-        return {"median": times[len(times) // 2], "min": times[0],
-                "calls": reps}
-
-    mask_ms = per_launch(f_mask, lambda i: calls[i % copies][0])
-    # tree_attn_verify: one attention launch (a split launch merges its
-    # partials in its last workgroups); the variant path launches its merge
-    # kernel after the attention kernel
-    ver_ms = per_launch(f_ver, lambda i: calls[i % copies][1])
-    ver_call = per_call(f_ver, lambda i: calls[i % copies][1])
+    # (2) per-launch durations of the mask build and of the verify launch
+    m = vb.measure(args.steps)
     phases = None
-    if args.phases and not variant:
+    if args.phases and not vb.variant:
         # the two-launch form (attention kernel writing partials, then the
         # merge kernel); its attention launches carry the same kernel name,
         # so a kernel trace of such a run mixes the two forms
-        att_ms = per_launch(f_att, lambda i: calls[i % copies][1])
-        mer_ms = (per_launch(f_mer, lambda i: calls[i % copies][1])
-                  if plan["splits"] > 1 else 0.0)
+        f_att = api._lib.tree_attn_verify_attend
+        f_mer = api._lib.tree_attn_verify_merge
+        att_ms = per_launch(torch, stream, f_att, vb.ver_args, args.steps)
+        mer_ms = (per_launch(torch, stream, f_mer, vb.ver_args, args.steps)
+                  if vb.plan["splits"] > 1 else 0.0)
         phases = {"attend_us": att_ms * 1e3, "merge_us": mer_ms * 1e3}
-    log(f"[bench] step {ms_per_step * 1e3:.1f} us; mask build "
-        f"{mask_ms * 1e3:.1f} us; verify {ver_ms * 1e3:.1f} us back to back, "
-        f"single calls median {ver_call['median']:.1f} / min "
-        f"{ver_call['min']:.1f} us"
+    log(f"[bench] {wl.name}: step {ms_per_step * 1e3:.1f} us; mask build "
+        f"{m['mask_build_us']:.1f} us; verify {m['verify_us']:.1f} us back "
+        f"to back, single calls median {m['verify_call_us']['median']:.1f} "
+        f"/ min {m['verify_call_us']['min']:.1f} us"
         + (f" (two-launch form: attend {phases['attend_us']:.1f} us + merge "
            f"{phases['merge_us']:.1f} us)" if phases else ""))
 
-    if variant:
-        kname = "attn_var_kernel"
-    else:
-        kname = ("attn_fwd256_kernel<8>" if plan["rows"] == 256
-                 else "attn_fwd128h_kernel")
-    att_bytes, _ = algorithmic_work(wl, with_output=True)
-    value = N / (ms_per_step * 1e-3)
-    a_s = ver_ms * 1e-3
+    N, Hq, d = wl.q.shape
+    S = wl.num_seqs
+    kname = vb.kernel_name()
+    bound = m["bound"]
+    frac_m = m["tflops"] / MFMA_BF16_PEAK_TFLOPS
+    frac_h = m["hbm_gbps"] / HBM_PEAK_GBPS
     if bound == "hbm":
-        achieved, peak, unit = att_bytes / a_s / 1e9, HBM_PEAK_GBPS, "GB/s"
+        achieved, peak, unit, frac = (m["hbm_gbps"], HBM_PEAK_GBPS, "GB/s",
+                                      frac_h)
     else:
-        achieved, peak, unit = (alg_flops / a_s / 1e12, MFMA_BF16_PEAK_TFLOPS,
-                                "TFLOP/s")
-    v_s = ver_ms * 1e-3
+        achieved, peak, unit, frac = (m["tflops"], MFMA_BF16_PEAK_TFLOPS,
+                                      "TFLOP/s", frac_m)
     result = {
         "metric": "tree-verify attention tree tokens/s + achieved HBM GB/s "
                   "/ MFMA% of peak",
-        "value": value,
+        "value": N / (ms_per_step * 1e-3),
         "unit": "tree tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -949,28 +1037,32 @@ def main():
             "q_heads": Hq, "kv_heads": wl.num_kv_heads, "head_dim": d,
             "page_size": wl.page_size,
             "splits_requested": args.splits or "planned",
-            "plan": plan,
+            "plan": vb.plan,
             "input_copies_rotated": copies,
         },
         "roofline": {
             "bound": bound,
             "kernel": (f"{kname} with its merge (tree_attn_verify_ex, one "
-                       f"call)" if variant
+                       f"call)" if vb.variant
                        else f"{kname} (tree_attn_verify, one launch)"),
             "achieved": achieved,
             "peak": peak,
             "unit": unit,
-            "frac": achieved / peak,
+            "frac": frac,
             "traffic": measured_traffic(wl.name, kname),
-            "alg_bytes_per_launch": att_bytes,
-            "alg_flops_per_launch": alg_flops,
-            "avg_launch_us": ver_ms * 1e3,
+            "tflops": m["tflops"],
+            "frac_mfma_bf16": frac_m,
+            "hbm_gbps": m["hbm_gbps"],
+            "frac_hbm": frac_h,
+            "alg_bytes_per_launch": m["alg_bytes"],
+            "alg_flops_per_launch": m["alg_flops"],
+            "avg_launch_us": m["verify_us"],
         },
-        "verify_us": ver_ms * 1e3,
-        "verify_call_us": ver_call,
-        "mask_build_us": mask_ms * 1e3,
-        "verify_tflops": alg_flops / v_s / 1e12,
-        "verify_hbm_gbps": alg_bytes / v_s / 1e9,
+        "verify_us": m["verify_us"],
+        "verify_call_us": m["verify_call_us"],
+        "mask_build_us": m["mask_build_us"],
+        "verify_tflops": m["tflops"],
+        "verify_hbm_gbps": m["hbm_gbps"],
     }
     if phases:
         result["two_launch_form"] = phases
@@ -978,6 +1070,29 @@ def main():
         cp = copy_bandwidth(torch, dev, stream)
         result["roofline"]["measured_copy_gbps"] = cp
         result["roofline"]["frac_of_measured_copy"] = achieved / cp
+    if not args.only and not vb.variant and args.splits == 0:
+        # the other standard workloads, timed the same way (per launch,
+        # inputs rotated), each with both roofline fractions
+        del vb, sets
+        torch.cuda.empty_cache()
+        summary = {wl.name: summary_entry(wl, m)}
+        for name in STANDARD_ORDER:
+            if name == wl.name:
+                continue
+            log(f"[bench] workload {name}")
+            w2 = standard_workload(name)
+            sets2, _ = device_sets(torch, w2, dev)
+            vb2 = VerifyBench(torch, api, w2, sets2, 0, stream)
+            vb2.warm(args.warmup)
+            summary[name] = summary_entry(w2, vb2.measure(args.steps))
+            log(f"[bench]   verify {summary[name]['verify_us']:.1f} us, "
+                f"{summary[name]['tflops']:.0f} TFLOP/s "
+                f"({summary[name]['frac_mfma_bf16']:.3f}), "
+                f"{summary[name]['hbm_gbps']:.0f} GB/s "
+                f"({summary[name]['frac_hbm']:.3f})")
+            del vb2, sets2
+            torch.cuda.empty_cache()
+        result["workloads"] = summary
     if not args.no_cpu_baseline:
         log("[bench] CPU baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

@@ -22,8 +22,16 @@
  *    device memory and keeps no pointer after a call returns.
  *  - `stream` is a hipStream_t passed as void* (NULL = default stream).
  *    Calls only enqueue work on it; none synchronises.
- *  - Every status is returned synchronously.  When a call returns anything
- *    but TREE_ATTN_OK, nothing was launched and nothing was written.
+ *  - Every status is returned synchronously.  Argument errors (every
+ *    status but TREE_ATTN_ERR_HIP) are found before any HIP call: nothing
+ *    was launched and nothing was written.  TREE_ATTN_ERR_HIP means that
+ *    the HIP runtime refused one of the call's own launches (checked by
+ *    each launch's return code; an error that an earlier, unrelated HIP
+ *    call left pending on the thread is neither reported nor cleared).
+ *    Calls that make two launches (tree_attn_verify with its separate
+ *    merge launch, tree_attn_verify_ex with split partials) may return it
+ *    after the first launch was enqueued: that launch then writes only
+ *    the workspace's partials, and out and lse are left unspecified.
  *  - All arrays are contiguous and row-major.
  *  - bf16 is the 16-bit bfloat16 format (1 sign, 8 exponent, 7 mantissa).
  *
@@ -175,9 +183,9 @@ int tree_attn_describe_plan(int32_t num_seqs, int32_t total_nodes,
  * Precision.  Scores, softmax and the P*V products accumulate in fp32
  * (P rounded to bf16 for the matrix cores).  When the key range is split
  * (workspace size > 0), each split's output, normalised by its own row
- * sum, passes through the workspace in fp16 (a convex combination of V
- * rows, so it needs V entries within fp16's range, |v| <= 65504; larger
- * values saturate there) before the log-sum-exp merge in fp32.
+ * sum, passes through the workspace in fp16 scaled by a power of two per
+ * row (so any bf16 V keeps fp16's 11-bit precision relative to the row's
+ * largest entry), before the log-sum-exp merge in fp32.
  *
  * Device values outside the stated bounds (a prefix longer than
  * max_prefix_len, a tree larger than max_nodes, page ids outside
@@ -514,8 +522,9 @@ int tree_attn_gdn_commit(const void* k, const float* u, const float* g,
  * kernels).  The other combinations run a separate kernel (128 query rows
  * per workgroup, fp8 converted to bf16 exactly on its way into LDS, bf16
  * matrix cores, fp32 accumulation, split partials normalised by their
- * own row sum in fp16, as for tree_attn_verify, so |v| * scale must stay
- * below 65504); its workspace size comes from tree_attn_workspace_size_ex.
+ * own row sum and stored in fp16 with a power-of-two scale per row, as
+ * for tree_attn_verify); its workspace size comes from
+ * tree_attn_workspace_size_ex.
  *
  * The key range is cut into at most 256 splits of at most 1039 pages each
  * (the kernel copies a split's page ids to LDS), as for tree_attn_verify.

@@ -9,6 +9,8 @@ this module raises.
 from __future__ import annotations
 
 import ctypes
+import functools
+import inspect
 import os
 from typing import Optional, Tuple
 
@@ -121,6 +123,24 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _on_stream(fn):
+    """Runs fn with its `stream` argument, when one is given, as torch's
+    current stream: the buffers fn allocates (and zero-fills) are then
+    ordered before its launches on that stream, and the caching allocator
+    ties them to it, so they are not handed to other work while the
+    launches still use them."""
+    sig = inspect.signature(fn)
+
+    @functools.wraps(fn)
+    def wrapper(*args, **kw):
+        stream = sig.bind(*args, **kw).arguments.get("stream")
+        if stream is None:
+            return fn(*args, **kw)
+        with torch.cuda.stream(stream):
+            return fn(*args, **kw)
+    return wrapper
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -148,6 +168,7 @@ def build_mask_raw(parents, tree_offsets, num_seqs, total_nodes, max_nodes,
         masks, bad_node, stream))
 
 
+@_on_stream
 def build_mask(parents: torch.Tensor, tree_offsets: torch.Tensor,
                max_nodes: int, mask_words: Optional[int] = None,
                masks: Optional[torch.Tensor] = None,
@@ -201,6 +222,7 @@ def describe_plan(num_seqs: int, total_nodes: int, num_q_heads: int,
             "chunk": info[3], "workgroups": info[4]}
 
 
+@_on_stream
 def verify(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
            page_table: torch.Tensor, prefix_lens: torch.Tensor,
            tree_offsets: torch.Tensor, masks: torch.Tensor,
@@ -249,6 +271,9 @@ def verify(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         lse = torch.empty((N, Hq), dtype=torch.float32, device=q.device)
     ws_bytes = workspace_size(S, N, Hq, Hkv, d, max_prefix_len, max_nodes,
                               page_size, num_splits)
+    if phase != "both" and workspace is None and ws_bytes > 0:
+        raise ValueError(f"phase {phase!r} needs the caller's workspace: "
+                         "the attend and merge launches must share one")
     if workspace is None and ws_bytes > 0:
         workspace = torch.zeros((ws_bytes,), dtype=torch.uint8,
                                 device=q.device)
@@ -266,6 +291,7 @@ def verify(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     return out, lse
 
 
+@_on_stream
 def accept(parents: torch.Tensor, tree_offsets: torch.Tensor,
            masks: torch.Tensor, draft_tokens: torch.Tensor,
            target_tokens: torch.Tensor, root_tokens: torch.Tensor,
@@ -344,6 +370,7 @@ def _token_bytes(k_cache: torch.Tensor) -> int:
             if k_cache.shape[0] else 16)
 
 
+@_on_stream
 def accept_commit(parents: torch.Tensor, tree_offsets: torch.Tensor,
                   masks: torch.Tensor, draft_tokens: torch.Tensor,
                   target_tokens: torch.Tensor, root_tokens: torch.Tensor,
@@ -397,6 +424,7 @@ def accept_commit(parents: torch.Tensor, tree_offsets: torch.Tensor,
     return accept_len[:S], accept_nodes[:S], bonus_tokens[:S]
 
 
+@_on_stream
 def build_tree(logp: torch.Tensor, tokens: torch.Tensor, budget: int,
                width: int = 1, stream=None) -> dict:
     """Draft trees by best-first expansion (width candidates per step).
@@ -424,6 +452,7 @@ def build_tree(logp: torch.Tensor, tokens: torch.Tensor, budget: int,
     return out
 
 
+@_on_stream
 def gdn_verify(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                g: torch.Tensor, beta: torch.Tensor, state: torch.Tensor,
                tree_offsets: torch.Tensor, masks: torch.Tensor,
@@ -488,6 +517,7 @@ def gdn_commit(k: torch.Tensor, u: torch.Tensor, g: torch.Tensor,
     _raise(code, "tree_attn_gdn_commit")
 
 
+@_on_stream
 def verify_ex(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
               page_table: torch.Tensor, prefix_lens: torch.Tensor,
               tree_offsets: torch.Tensor, masks: torch.Tensor,

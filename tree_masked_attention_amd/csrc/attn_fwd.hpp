@@ -179,14 +179,6 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
 
-// Value of the other lane half (lane ^ 32).
-__device__ __forceinline__ float other_half(float x) {
-  const unsigned u = __builtin_bit_cast(unsigned, x);
-  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  // r[0]: lanes 32..63 now hold lanes 0..31; r[1]: lanes 0..31 hold 32..63
-  return __builtin_bit_cast(float, __lane_id() < 32 ? r[1] : r[0]);
-}
-
 // Applies the mask of one tile (keys past the split end; tree keys off the
 // node's root-to-node path) to the scores of one 32-query block.
 __device__ __forceinline__ void apply_tile_mask(f32x16 (&S)[2], uint64_t allow,

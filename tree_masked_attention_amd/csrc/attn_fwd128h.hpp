@@ -473,9 +473,23 @@ __global__ __launch_bounds__(512, 1) void attn_fwd128h_kernel(FwdParams p) {
     m_ref = mx;
 
     // ---- epilogue (lower-half waves): the normalised output in bf16 (one
-    // split) or fp16 (a split's partial), staged through LDS past the
-    // exchange area so that the stores write whole rows
+    // split) or, for a split's partial, in fp16 scaled by 2^-ex (the row's
+    // scale exponent), staged through LDS past the exchange area so that
+    // the stores write whole rows
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    int ex = 0;
+    if (p.splits > 1) {
+      float amax = 0.f;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          amax = __builtin_elementwise_maximum(amax, __builtin_fabsf(o[db][e]));
+        }
+      }
+      ex = f16_row_exp(__builtin_elementwise_maximum(amax, other_half(amax)) *
+                       inv);
+    }
     u32x2 pk[16];
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
@@ -489,7 +503,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd128h_kernel(FwdParams p) {
         } else {
           f16x4 v4;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v4[e] = to_f16_sat(o[db][g4 * 4 + e] * inv);
+          for (int e = 0; e < 4; ++e) {
+            v4[e] = to_f16_sat(ldexp2(o[db][g4 * 4 + e] * inv, -ex));
+          }
           pk[db * 4 + g4] = __builtin_bit_cast(u32x2, v4);
         }
       }
@@ -508,11 +524,11 @@ __global__ __launch_bounds__(512, 1) void attn_fwd128h_kernel(FwdParams p) {
                         lane, p.counters != nullptr);
       if (half == 0 && rvalid) {
         float* dst = p.part_ml + (prow0 + qrow) * 2;
+        const uint64_t st = pack_split_stats(split_lse2(m_ref, l_tot), ex);
         if (p.counters != nullptr) {
-          store_coherent8(dst, (uint64_t)__float_as_uint(m_ref) |
-                                   ((uint64_t)__float_as_uint(l_tot) << 32));
+          store_coherent8(dst, st);
         } else {
-          *reinterpret_cast<f32x2*>(dst) = f32x2{m_ref, l_tot};
+          *reinterpret_cast<uint64_t*>(dst) = st;
         }
       }
     }

@@ -1,21 +1,16 @@
-// 256-row variants of the split-KV tree-verification attention kernel, for
+// 256-row variant of the split-KV tree-verification attention kernel, for
 // (sequence, kv head) pairs with at least 256 query rows.
 //
 // Same operation, data layout, MFMA mapping, LDS ring format and pipeline
 // as the 128-row kernel (definitions in attn_fwd.hpp); each K/V tile staged
-// in LDS serves 256 rows.  Two shapes (only NW = 8 is launched):
-//  * NW = 8 waves of 32 rows, two waves per SIMD: the vector ALU of a SIMD
-//    issues about twice as many instructions per cycle (and the exponential
-//    about three times as many) when two waves feed it; 256 registers per
-//    wave.
-//  * NW = 4 waves of 64 rows (QB = 2 query blocks), one wave per SIMD with
-//    up to 512 registers: each K or V operand read from LDS feeds two
-//    MFMAs, which halves the LDS reads per flop (every wave reads the whole
-//    K and V tile; with 32 rows per wave those reads come close to the
-//    LDS bandwidth).
-// Each wave overlaps its own S^T MFMAs of tile j+1 with the softmax of
-// tile j; scores are built one 32-key block at a time and the K/V operands
-// are read from LDS a quarter tile at a time.
+// in LDS serves 256 rows.  Eight waves of 32 rows, two waves per SIMD: the
+// vector ALU of a SIMD issues about twice as many instructions per cycle
+// (and the exponential about three times as many) when two waves feed it;
+// 256 registers per wave.  Each wave overlaps its own S^T MFMAs of tile
+// j+1 with the softmax of tile j; scores are built one 32-key block at a
+// time and the K/V operands are read from LDS a quarter tile at a time.
+// The per-wave state is written over QB query blocks of 32 rows (QB = 1
+// here), so that the row bookkeeping reads the same for any block count.
 #pragma once
 
 #include "attn_fwd.hpp"
@@ -24,15 +19,15 @@ namespace tree_attn {
 
 constexpr int kRowsPerWG8 = 256;
 
-template <int NW>
-__global__ __launch_bounds__(NW * 64, 1) void attn_fwd256_kernel(FwdParams p) {
-  constexpr int QB = 8 / NW;             // 32-query blocks per wave
+__global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
+  constexpr int NW = 8;
+  constexpr int QB = 1;                  // 32-query blocks per wave
   constexpr int kThreads = NW * 64;
   constexpr int kOpsPerMat = 16 / NW;    // 1-KB DMA ops per wave per matrix
   constexpr int kOps = 2 * kOpsPerMat;
   constexpr int kDmaRows = 4 * kOpsPerMat;  // tile rows a wave moves
-  constexpr int kLog2DmaRows = NW == 8 ? 3 : 4;
-  static_assert(QB * NW == 8 && (1 << kLog2DmaRows) == kDmaRows, "shape");
+  constexpr int kLog2DmaRows = 3;
+  static_assert((1 << kLog2DmaRows) == kDmaRows, "shape");
   __shared__ __align__(1024) unsigned char ring[2 * kVOff];
   __shared__ int pg_lds[kPageCache];
   __shared__ uint64_t mk_lds[kMaskCache];
@@ -553,6 +548,20 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd256_kernel(FwdParams p) {
   for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = l_run[qb] + other_half(l_run[qb]);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    int ex = 0;  // scale exponent of a split's partial row (f16_row_exp)
+    if (p.splits > 1) {
+      float amax = 0.f;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          amax = __builtin_elementwise_maximum(amax,
+                                               __builtin_fabsf(o[qb][db][e]));
+        }
+      }
+      ex = f16_row_exp(__builtin_elementwise_maximum(amax, other_half(amax)) *
+                       inv);
+    }
     u32x2 pk[16];
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
@@ -569,7 +578,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd256_kernel(FwdParams p) {
           f16x4 v4;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            v4[e] = to_f16_sat(o[qb][db][g4 * 4 + e] * inv);
+            v4[e] = to_f16_sat(ldexp2(o[qb][db][g4 * 4 + e] * inv, -ex));
           }
           pk[db * 4 + g4] = __builtin_bit_cast(u32x2, v4);
         }
@@ -590,11 +599,11 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd256_kernel(FwdParams p) {
                         lane, p.counters != nullptr);
       if (half == 0 && rvalid[qb]) {
         float* dst = p.part_ml + (prow0 + qrow[qb]) * 2;
+        const uint64_t st = pack_split_stats(split_lse2(m_ref[qb], l_tot), ex);
         if (p.counters != nullptr) {
-          store_coherent8(dst, (uint64_t)__float_as_uint(m_ref[qb]) |
-                                   ((uint64_t)__float_as_uint(l_tot) << 32));
+          store_coherent8(dst, st);
         } else {
-          *reinterpret_cast<f32x2*>(dst) = f32x2{m_ref[qb], l_tot};
+          *reinterpret_cast<uint64_t*>(dst) = st;
         }
       }
     }

@@ -1,11 +1,14 @@
 // Log-sum-exp merge of split-KV partials.
 //
-// Each split c of a row's key range left its output normalised by its own
-// row sum, O'_c = O_c / l_c (fp16), its running max m_c (log2 units) and
-// its row sum l_c.  With m* = max_c m_c and w_c = 2^(m_c - m*) l_c:
-//     out = sum_c w_c O'_c / sum_c w_c,
-//     lse = ln2 * (m* + log2 sum_c w_c).
-// A split in which the row saw no allowed key has m_c = -inf, l_c = 0 and
+// Each split c of a row's key range leaves its output normalised by its
+// own row sum, O'_c = O_c / l_c, stored in fp16 as 2^-e_c O'_c with the
+// row's scale exponent e_c (f16_row_exp in common.hpp: 0 unless the row
+// reaches 2^15), and two 32-bit words: its log-sum-exp in log2 units,
+// L_c = m_c + log2 l_c (m_c its running max, scores in log2 units), and
+// e_c.  With L* = max_c L_c and w_c = 2^(L_c - L*):
+//     out = sum_c w_c 2^e_c (2^-e_c O'_c) / sum_c w_c,
+//     lse = ln2 * (L* + log2 sum_c w_c).
+// A split in which the row saw no allowed key has L_c = -inf and
 // contributes nothing.  The sums are accumulated with a running maximum,
 // which gives the same values up to rounding order.
 //
@@ -25,17 +28,29 @@ namespace tree_attn {
 constexpr int kMergeCounters = 16384;
 constexpr size_t kCounterBytes = (size_t)kMergeCounters * 4;
 
-// Folds split c's (m_c, l_c) into a row's running (m, l); returns false
-// when no split so far saw an allowed key (the row's sums stay zero), else
-// the factors for acc <- acc * s_old + w * O'_c (merge_acc).
+// Split statistics word pair: (L_c, e_c) as (fp32, int32 bits).
+__device__ __forceinline__ uint64_t pack_split_stats(float lse2, int e) {
+  return (uint64_t)__float_as_uint(lse2) | ((uint64_t)(unsigned)e << 32);
+}
+
+// L_c of a split from its running max and row sum (-inf when empty).
+__device__ __forceinline__ float split_lse2(float m, float l) {
+  return l > 0.f ? m + log2f(l) : -INFINITY;
+}
+
+// Folds split c's (L_c, e_c) into a row's running (max, sum of weights);
+// returns false when no split so far saw an allowed key (the row's sums
+// stay zero), else the factors for acc <- acc * s_old + w * stored_c
+// (merge_acc), where w = w_c 2^e_c undoes the partial's scale.
 __device__ __forceinline__ bool merge_weights(float& m_run, float& l_run,
                                               f32x2 ml, float& s_old,
                                               float& w) {
   const float m_new = fmaxf(m_run, ml[0]);
   if (m_new == -INFINITY) return false;
   s_old = fast_exp2(m_run - m_new);
-  w = fast_exp2(ml[0] - m_new) * ml[1];
-  l_run = __builtin_fmaf(l_run, s_old, w);
+  const float wc = fast_exp2(ml[0] - m_new);
+  l_run = __builtin_fmaf(l_run, s_old, wc);
+  w = ldexp2(wc, __float_as_int(ml[1]));
   m_run = m_new;
   return true;
 }

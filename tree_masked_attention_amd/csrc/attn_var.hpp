@@ -385,20 +385,32 @@ __global__ __launch_bounds__(kVarThreads, 2) void attn_var_kernel(VarParams p) {
     const size_t rows_all = (size_t)p.N * p.Hq;
     _Float16* po = p.part_o + ((size_t)c * rows_all + qrow) * D;
     const float inv = l > 0.f ? vsc / l : 0.f;
+    // fp16 scaled by 2^-ex, the row's scale exponent (f16_row_exp)
+    float amax = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        amax = __builtin_elementwise_maximum(amax, __builtin_fabsf(oacc[dt][e]));
+      }
+    }
+    const int ex = f16_row_exp(
+        __builtin_elementwise_maximum(amax, other_half(amax)) * inv);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         f16x4 o4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o4[e] = to_f16_sat(oacc[dt][4 * q + e] * inv);
+        for (int e = 0; e < 4; ++e) {
+          o4[e] = to_f16_sat(ldexp2(oacc[dt][4 * q + e] * inv, -ex));
+        }
         *reinterpret_cast<f16x4*>(po + 32 * dt + 8 * q + 4 * half) = o4;
       }
     }
     if (half == 0) {
       float* ml = p.part_ml + ((size_t)c * rows_all + qrow) * 2;
-      ml[0] = m;
-      ml[1] = l;
+      *reinterpret_cast<uint64_t*>(ml) = pack_split_stats(split_lse2(m, l), ex);
     }
   }
 }

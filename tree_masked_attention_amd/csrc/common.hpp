@@ -26,6 +26,21 @@ __device__ __forceinline__ _Float16 to_f16_sat(float x) {
       __builtin_elementwise_max(x, -kF16Max), kF16Max);
 }
 
+// Split partials travel in fp16 with a power-of-two scale per row: the
+// exponent e >= 0 such that 2^-e * amax < 2^15 for the row's largest
+// magnitude amax (e = 0 whenever amax < 2^15).  Scaling by a power of two
+// is exact, so a partial keeps fp16's 11-bit precision relative to its row
+// maximum over the whole bf16 range; the merge multiplies the weight of
+// the partial by 2^e.
+__device__ __forceinline__ int f16_row_exp(float amax) {
+  const int e = __builtin_amdgcn_frexp_expf(amax) - 15;
+  return e > 0 ? e : 0;
+}
+
+__device__ __forceinline__ float ldexp2(float x, int e) {
+  return __builtin_amdgcn_ldexpf(x, e);
+}
+
 constexpr int kHeadDim = 128;
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.442695040888963407f;
@@ -51,6 +66,14 @@ __device__ __forceinline__ uint64_t load_coherent8(const void* p) {
 // 2^x on the hardware exponential unit (exact 0 for -inf).
 __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);
+}
+
+// Value of the other lane half (lane ^ 32).
+__device__ __forceinline__ float other_half(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  // r[0]: lanes 32..63 now hold lanes 0..31; r[1]: lanes 0..31 hold 32..63
+  return __builtin_bit_cast(float, __lane_id() < 32 ? r[1] : r[0]);
 }
 
 // D = A(32x16) * B(16x32) + C on the bf16 matrix cores, fp32 accumulate.

@@ -3,9 +3,13 @@
 // Every check that can fail runs before the first HIP call, so an error
 // status means nothing was launched.  The library owns no device memory.
 #include "tree_attn.h"
+#ifdef TREE_ATTN_DEBUG
+#include "tree_attn_debug.h"
+#endif
 
 #include <atomic>
 #include <cmath>
+#include <tuple>
 
 #include "accept_commit.hpp"
 #include "attn_fwd.hpp"
@@ -51,6 +55,27 @@ int cu_count() {
   }
   g_cu_count[dev].store(n, std::memory_order_relaxed);
   return n;
+}
+
+// Launches a kernel on stream st and returns that launch's own status
+// (hipLaunchKernel's return code).  An error that an earlier, unrelated HIP
+// call left pending on this thread is neither reported nor cleared.
+template <typename... KArgs, typename... Args>
+int launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t st,
+           const Args&... args) {
+  static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel arguments");
+  std::tuple<KArgs...> vals(args...);
+  void* ptrs[sizeof...(KArgs)];
+  std::apply(
+      [&ptrs](auto&... v) {
+        int i = 0;
+        ((ptrs[i++] = static_cast<void*>(&v)), ...);
+      },
+      vals);
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block,
+                         ptrs, 0, st) == hipSuccess
+             ? TREE_ATTN_OK
+             : TREE_ATTN_ERR_HIP;
 }
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
@@ -141,10 +166,6 @@ int make_plan(int S, int N, int Hq, int Hkv, int max_prefix_len,
     if (st != TREE_ATTN_OK) return st;
     if (chunk >= kMinKeysPerWG8) rpw = kRowsPerWG8;
   }
-#ifdef TREE_ATTN_FORCE_SHAPE  // build-time override for tuning runs
-  if (TREE_ATTN_FORCE_SHAPE == 2 && can8) rpw = kRowsPerWG8;
-  if (TREE_ATTN_FORCE_SHAPE == 3) rpw = kRowsPerWG128;
-#endif
   {
     const int st = choose(rpw);
     if (st != TREE_ATTN_OK) return st;
@@ -345,9 +366,28 @@ int check_var_sizes(int kv_dtype, int S, int N, int Hq, int Hkv, int D,
 }
 
 template <int D, bool FP8>
-void launch_var(const VarPlan& pl, const VarParams& vp, hipStream_t hs) {
-  hipLaunchKernelGGL((attn_var_kernel<D, FP8>), dim3((unsigned)pl.grid),
-                     dim3(kVarThreads), 0, hs, vp);
+int launch_var(const VarPlan& pl, const VarParams& vp, hipStream_t hs) {
+  return launch(&attn_var_kernel<D, FP8>, dim3((unsigned)pl.grid),
+                dim3(kVarThreads), hs, vp);
+}
+
+// Size checks of a verify call (everything but the pointers).
+int check_verify_sizes(int S, int N, int Hq, int Hkv, int head_dim,
+                       int max_prefix_len, int max_nodes, int num_splits,
+                       int mask_words, int max_pages_per_seq, int num_pages,
+                       int page_size, float scale) {
+  int st = check_sizes(S, N, Hq, Hkv, head_dim, max_prefix_len, max_nodes);
+  if (st != TREE_ATTN_OK) return st;
+  if (num_splits < 0 || mask_words < 1 || max_pages_per_seq < 0 ||
+      num_pages < 0) {
+    return TREE_ATTN_ERR_SHAPE;
+  }
+  if (!is_pow2(page_size) || page_size > 4096) return TREE_ATTN_ERR_SHAPE;
+  if ((long long)mask_words * 64 < max_nodes) return TREE_ATTN_ERR_SHAPE;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return TREE_ATTN_ERR_SHAPE;
+  if (S == 0 || N == 0) return TREE_ATTN_OK;
+  if (num_pages < 1 || max_pages_per_seq < 1) return TREE_ATTN_ERR_SHAPE;
+  return TREE_ATTN_OK;
 }
 
 // Phases of a verify call: the split-KV + tree pass, then the LSE merge.
@@ -364,18 +404,12 @@ int run_verify(int phases, const void* q, const void* k_cache, const void* v_cac
                      int32_t head_dim, float scale, int32_t num_splits,
                      void* out, float* lse, void* workspace,
                      size_t workspace_bytes, void* stream) {
-  int st = check_sizes(num_seqs, total_nodes, num_q_heads, num_kv_heads,
-                       head_dim, max_prefix_len, max_nodes);
+  int st = check_verify_sizes(num_seqs, total_nodes, num_q_heads,
+                              num_kv_heads, head_dim, max_prefix_len,
+                              max_nodes, num_splits, mask_words,
+                              max_pages_per_seq, num_pages, page_size, scale);
   if (st != TREE_ATTN_OK) return st;
-  if (num_splits < 0 || mask_words < 1 || max_pages_per_seq < 0 ||
-      num_pages < 0) {
-    return TREE_ATTN_ERR_SHAPE;
-  }
-  if (!is_pow2(page_size) || page_size > 4096) return TREE_ATTN_ERR_SHAPE;
-  if ((long long)mask_words * 64 < max_nodes) return TREE_ATTN_ERR_SHAPE;
-  if (!std::isfinite(scale) || !(scale > 0.f)) return TREE_ATTN_ERR_SHAPE;
   if (num_seqs == 0 || total_nodes == 0) return TREE_ATTN_OK;
-  if (num_pages < 1 || max_pages_per_seq < 1) return TREE_ATTN_ERR_SHAPE;
   if (!q || !k_cache || !v_cache || !page_table || !prefix_lens ||
       !tree_offsets || !masks || !out || !lse) {
     return TREE_ATTN_ERR_NULL;
@@ -433,14 +467,12 @@ int run_verify(int phases, const void* q, const void* k_cache, const void* v_cac
 
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const unsigned grid = 8u * (unsigned)fp.per_xcd;
-  if (!(phases & kPhaseAttend)) {
-    // merge only
-  } else if (pl.rows == kRowsPerWG8) {
-    hipLaunchKernelGGL(attn_fwd256_kernel<8>, dim3(grid), dim3(512), 0, hs, fp);
-  } else {
-    hipLaunchKernelGGL(attn_fwd128h_kernel, dim3(grid), dim3(512), 0, hs, fp);
+  if (phases & kPhaseAttend) {
+    st = launch(pl.rows == kRowsPerWG8 ? &attn_fwd256_kernel
+                                       : &attn_fwd128h_kernel,
+                dim3(grid), dim3(512), hs, fp);
+    if (st != TREE_ATTN_OK) return st;
   }
-  if (hipGetLastError() != hipSuccess) return TREE_ATTN_ERR_HIP;
 
   if ((phases & kPhaseMerge) && pl.splits > 1 && !fused) {
     MergeParams mp;
@@ -462,9 +494,9 @@ int run_verify(int phases, const void* q, const void* k_cache, const void* v_cac
     mp.rows_per_block = pl.rows;
     const long long mgrid = (long long)num_seqs * num_kv_heads * pl.mblocks *
                             (mp.rows_per_block / kMergeRowsPerWG);
-    hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)mgrid),
-                       dim3(kMergeWaves * 64), 0, hs, mp);
-    if (hipGetLastError() != hipSuccess) return TREE_ATTN_ERR_HIP;
+    st = launch(&attn_merge_kernel, dim3((unsigned)mgrid),
+                dim3(kMergeWaves * 64), hs, mp);
+    if (st != TREE_ATTN_OK) return st;
   }
   return TREE_ATTN_OK;
 }
@@ -506,10 +538,9 @@ int tree_attn_build_mask(const int32_t* parents, const int32_t* tree_offsets,
   // one thread per node of the largest tree, whole waves
   const int threads = std::min(kMaskThreads, (cap + 63) / 64 * 64);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(build_mask_kernel, dim3(num_seqs), dim3(threads), 0, st,
-                     parents, tree_offsets, num_seqs, total_nodes, cap,
-                     (int)mask_words, masks, bad_node);
-  return hipGetLastError() == hipSuccess ? TREE_ATTN_OK : TREE_ATTN_ERR_HIP;
+  return launch(&build_mask_kernel, dim3(num_seqs), dim3(threads), st, parents,
+                tree_offsets, num_seqs, total_nodes, cap, (int)mask_words,
+                masks, bad_node);
 }
 
 size_t tree_attn_workspace_size(int32_t num_seqs, int32_t total_nodes,
@@ -644,20 +675,12 @@ int tree_attn_build_tree(const float* logp, const int32_t* tokens,
   const int ms = budget / 64 + 1;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const dim3 grid(num_seqs), block(64);
-  if (ms <= 1) {
-    hipLaunchKernelGGL(build_tree_kernel<1>, grid, block, 0, hs, tp);
-  } else if (ms <= 2) {
-    hipLaunchKernelGGL(build_tree_kernel<2>, grid, block, 0, hs, tp);
-  } else if (ms <= 4) {
-    hipLaunchKernelGGL(build_tree_kernel<4>, grid, block, 0, hs, tp);
-  } else if (ms <= 8) {
-    hipLaunchKernelGGL(build_tree_kernel<8>, grid, block, 0, hs, tp);
-  } else if (ms <= 16) {
-    hipLaunchKernelGGL(build_tree_kernel<16>, grid, block, 0, hs, tp);
-  } else {
-    hipLaunchKernelGGL(build_tree_kernel<17>, grid, block, 0, hs, tp);
-  }
-  return hipGetLastError() == hipSuccess ? TREE_ATTN_OK : TREE_ATTN_ERR_HIP;
+  if (ms <= 1) return launch(&build_tree_kernel<1>, grid, block, hs, tp);
+  if (ms <= 2) return launch(&build_tree_kernel<2>, grid, block, hs, tp);
+  if (ms <= 4) return launch(&build_tree_kernel<4>, grid, block, hs, tp);
+  if (ms <= 8) return launch(&build_tree_kernel<8>, grid, block, hs, tp);
+  if (ms <= 16) return launch(&build_tree_kernel<16>, grid, block, hs, tp);
+  return launch(&build_tree_kernel<17>, grid, block, hs, tp);
 }
 
 int tree_attn_accept(const int32_t* parents, const int32_t* tree_offsets,
@@ -678,9 +701,8 @@ int tree_attn_accept(const int32_t* parents, const int32_t* tree_offsets,
                                     draft_tokens, target_tokens, root_tokens,
                                     total_nodes, max_nodes, accept_len,
                                     accept_nodes, bonus_tokens);
-  hipLaunchKernelGGL(accept_kernel, dim3(num_seqs), dim3(threads), 0,
-                     reinterpret_cast<hipStream_t>(stream), ap);
-  return hipGetLastError() == hipSuccess ? TREE_ATTN_OK : TREE_ATTN_ERR_HIP;
+  return launch(&accept_kernel, dim3(num_seqs), dim3(threads),
+                reinterpret_cast<hipStream_t>(stream), ap);
 }
 
 int tree_attn_commit_kv(void* k_cache, void* v_cache,
@@ -701,10 +723,8 @@ int tree_attn_commit_kv(void* k_cache, void* v_cache,
       kCommitThreads);
   const long long grid = (long long)num_seqs * cp.slices;
   if (grid > 0x7fffffffLL) return TREE_ATTN_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(commit_kv_kernel, dim3((unsigned)grid),
-                     dim3(kCommitThreads), 0,
-                     reinterpret_cast<hipStream_t>(stream), cp);
-  return hipGetLastError() == hipSuccess ? TREE_ATTN_OK : TREE_ATTN_ERR_HIP;
+  return launch(&commit_kv_kernel, dim3((unsigned)grid), dim3(kCommitThreads),
+                reinterpret_cast<hipStream_t>(stream), cp);
 }
 
 int tree_attn_accept_commit(
@@ -738,10 +758,8 @@ int tree_attn_accept_commit(
       prefix_lens, accept_len, accept_nodes, max_nodes, token_bytes, threads);
   const long long grid = (long long)num_seqs * cp.slices;
   if (grid > 0x7fffffffLL) return TREE_ATTN_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(accept_commit_kernel, dim3((unsigned)grid),
-                     dim3(threads), 0, reinterpret_cast<hipStream_t>(stream),
-                     ap, cp);
-  return hipGetLastError() == hipSuccess ? TREE_ATTN_OK : TREE_ATTN_ERR_HIP;
+  return launch(&accept_commit_kernel, dim3((unsigned)grid), dim3(threads),
+                reinterpret_cast<hipStream_t>(stream), ap, cp);
 }
 
 int tree_attn_gdn_verify(const void* q, const void* k, const void* v,
@@ -783,10 +801,8 @@ int tree_attn_gdn_verify(const void* q, const void* k, const void* v,
   gp.u = u;
   gp.H = num_heads;
   gp.W = mask_words;
-  hipLaunchKernelGGL(gdn_verify_kernel, dim3((unsigned)(num_seqs * num_heads)),
-                     dim3(kGdnThreads), 0,
-                     reinterpret_cast<hipStream_t>(stream), gp);
-  return hipGetLastError() == hipSuccess ? TREE_ATTN_OK : TREE_ATTN_ERR_HIP;
+  return launch(&gdn_verify_kernel, dim3((unsigned)(num_seqs * num_heads)),
+                dim3(kGdnThreads), reinterpret_cast<hipStream_t>(stream), gp);
 }
 
 int tree_attn_gdn_commit(const void* k, const float* u, const float* g,
@@ -819,10 +835,8 @@ int tree_attn_gdn_commit(const void* k, const float* u, const float* g,
   cp.state = state;
   cp.H = num_heads;
   cp.max_nodes = max_nodes;
-  hipLaunchKernelGGL(gdn_commit_kernel, dim3((unsigned)(num_seqs * num_heads)),
-                     dim3(kGdnThreads), 0,
-                     reinterpret_cast<hipStream_t>(stream), cp);
-  return hipGetLastError() == hipSuccess ? TREE_ATTN_OK : TREE_ATTN_ERR_HIP;
+  return launch(&gdn_commit_kernel, dim3((unsigned)(num_seqs * num_heads)),
+                dim3(kGdnThreads), reinterpret_cast<hipStream_t>(stream), cp);
 }
 
 size_t tree_attn_workspace_size_ex(int32_t kv_dtype, int32_t num_seqs,
@@ -932,28 +946,107 @@ int tree_attn_verify_ex(const void* q, const void* k_cache,
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const bool fp8 = kv_dtype == TREE_ATTN_KV_FP8_E4M3;
   if (head_dim == 64) {
-    if (fp8) launch_var<64, true>(pl, vp, hs); else launch_var<64, false>(pl, vp, hs);
+    st = fp8 ? launch_var<64, true>(pl, vp, hs)
+             : launch_var<64, false>(pl, vp, hs);
   } else {
     // bf16 with head dim 128 never gets here: it runs the tuned kernels
-    launch_var<128, true>(pl, vp, hs);
+    st = launch_var<128, true>(pl, vp, hs);
   }
-  if (hipGetLastError() != hipSuccess) return TREE_ATTN_ERR_HIP;
+  if (st != TREE_ATTN_OK) return st;
   if (pl.splits > 1) {
     // a separate merge launch: the partials of this kernel are scattered
     // 8-byte rows and its plans use more splits, so merging in the last
     // workgroup of a row block was slower than this launch
     const long long work = (long long)total_nodes * num_q_heads * (head_dim / 4);
     const unsigned mgrid = (unsigned)((work + 255) / 256);
-    if (head_dim == 64) {
-      hipLaunchKernelGGL(attn_var_merge_kernel<64>, dim3(mgrid), dim3(256), 0,
-                         hs, vp);
-    } else {
-      hipLaunchKernelGGL(attn_var_merge_kernel<128>, dim3(mgrid), dim3(256),
-                         0, hs, vp);
-    }
-    if (hipGetLastError() != hipSuccess) return TREE_ATTN_ERR_HIP;
+    st = head_dim == 64
+             ? launch(&attn_var_merge_kernel<64>, dim3(mgrid), dim3(256), hs, vp)
+             : launch(&attn_var_merge_kernel<128>, dim3(mgrid), dim3(256), hs,
+                      vp);
+    if (st != TREE_ATTN_OK) return st;
   }
   return TREE_ATTN_OK;
 }
+
+#ifdef TREE_ATTN_DEBUG
+// Debug builds: the device values tree_attn_verify trusts, checked on host
+// copies of them.  The kernels clamp what is out of range (a page id past
+// the pool, a tree offset past N) so that no access leaves the buffers;
+// this replays the planned launch's indexing on the host and names the
+// first value that would have been clamped.
+int tree_attn_debug_check_verify(
+    const int32_t* page_table, int32_t max_pages_per_seq, int32_t num_pages,
+    int32_t page_size, const int32_t* prefix_lens,
+    const int32_t* tree_offsets, const int32_t* parents, int32_t mask_words,
+    int32_t num_seqs, int32_t total_nodes, int32_t max_prefix_len,
+    int32_t max_nodes, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t num_splits, int32_t* report) {
+  if (!report) return TREE_ATTN_ERR_NULL;
+  for (int i = 0; i < 4; ++i) report[i] = -1;
+  report[0] = TREE_ATTN_DEBUG_OK;
+  int st = check_verify_sizes(num_seqs, total_nodes, num_q_heads,
+                              num_kv_heads, head_dim, max_prefix_len,
+                              max_nodes, num_splits, mask_words,
+                              max_pages_per_seq, num_pages, page_size, 1.f);
+  if (st != TREE_ATTN_OK || num_seqs == 0 || total_nodes == 0) return st;
+  if (!page_table || !prefix_lens || !tree_offsets || !parents) {
+    return TREE_ATTN_ERR_NULL;
+  }
+  auto fail = [&](int kind, int s, long long idx, long long val) {
+    report[0] = kind;
+    report[1] = s;
+    report[2] = (int32_t)idx;
+    report[3] = (int32_t)val;
+    return TREE_ATTN_ERR_SHAPE;
+  };
+  Plan pl;
+  st = make_plan(num_seqs, total_nodes, num_q_heads, num_kv_heads,
+                 max_prefix_len, max_nodes, page_size, num_splits, cu_count(),
+                 &pl);
+  if (st != TREE_ATTN_OK) return st;
+  const int log2_page = ilog2(page_size);
+  const long long max_tokens = (long long)max_pages_per_seq * page_size;
+  if (tree_offsets[0] != 0) return fail(TREE_ATTN_DEBUG_OFFSETS, 0, 0,
+                                        tree_offsets[0]);
+  for (int s = 0; s < num_seqs; ++s) {
+    const int a = tree_offsets[s], b = tree_offsets[s + 1];
+    if (b < a || b > total_nodes) {
+      return fail(TREE_ATTN_DEBUG_OFFSETS, s, s + 1, b);
+    }
+    if (b - a > max_nodes) return fail(TREE_ATTN_DEBUG_TREE_SIZE, s, 0, b - a);
+    const int P = prefix_lens[s];
+    if (P < 0 || P > max_prefix_len) {
+      return fail(TREE_ATTN_DEBUG_PREFIX, s, 0, P);
+    }
+    for (int i = 0; i < b - a; ++i) {
+      const int par = parents[a + i];
+      if (par < -1 || par >= i) return fail(TREE_ATTN_DEBUG_PARENT, s, i, par);
+    }
+    const long long T = (long long)P + (b - a);
+    if (T > max_tokens) return fail(TREE_ATTN_DEBUG_TABLE, s, 0, T);
+    // the pages each split of the plan reads, through its LDS copy of the
+    // split's slice of the page table
+    for (long long kbeg = 0; kbeg < T; kbeg += pl.chunk) {
+      const long long kend = std::min(T, kbeg + pl.chunk);
+      const long long lp0 = kbeg >> log2_page;
+      const long long lp1 = (kend - 1) >> log2_page;
+      if (lp1 - lp0 + 1 > kPageCache) {
+        return fail(TREE_ATTN_DEBUG_PAGE_CACHE, s, lp1, lp1 - lp0 + 1);
+      }
+      for (long long lp = lp0; lp <= lp1; ++lp) {
+        const int pg = page_table[(size_t)s * max_pages_per_seq + lp];
+        if (pg < 0 || pg >= num_pages) {
+          return fail(TREE_ATTN_DEBUG_PAGE_ID, s, lp, pg);
+        }
+      }
+    }
+  }
+  if (tree_offsets[num_seqs] != total_nodes) {
+    return fail(TREE_ATTN_DEBUG_OFFSETS, num_seqs, num_seqs,
+                tree_offsets[num_seqs]);
+  }
+  return TREE_ATTN_OK;
+}
+#endif  // TREE_ATTN_DEBUG
 
 }  // extern "C"

@@ -232,6 +232,7 @@ def make_workload(seed: int, prefix_lens: Sequence[int] | None = None,
                   num_seqs: Optional[int] = None,
                   extra_pages: int = 0,
                   kv_format: str = "bf16",
+                  value_scale: float = 1.0,
                   name: str = "custom") -> Workload:
     """Draw one synthetic workload.
 
@@ -243,6 +244,9 @@ def make_workload(seed: int, prefix_lens: Sequence[int] | None = None,
     bf16 rounding.  ``extra_pages`` appends unused physical pages to the
     pool (filled with noise), so a page table can address a pool larger
     than the live tokens.
+    ``value_scale`` multiplies every cached value row in float32 before the
+    rounding (a power of two keeps the bf16 values exact multiples of the
+    unscaled ones).
     """
     rng = np.random.default_rng(seed)
     if prefix_lens is None:
@@ -297,6 +301,8 @@ def make_workload(seed: int, prefix_lens: Sequence[int] | None = None,
         fac = _bulk_uniform(ss_f, (num_pages, page_size), lo, hi)
         k32 *= fac[:, :, None, None]
     v32 = _bulk_normal(ss_v, kv_shape)
+    if value_scale != 1.0:
+        v32 *= np.float32(value_scale)
     k_scale = v_scale = None
     if kv_format == "e4m3":
         k_cache, k_scale = quantize_e4m3(k32)
