@@ -548,3 +548,51 @@ def test_random_split_merge_repeated(seed):
         assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)), rep
         assert torch.equal(lse, ref_lse), rep
         assert int(ws[:65536].count_nonzero()) == 0
+
+
+# --------------------------------------------------------------------------
+# status contract: an error left pending by an unrelated HIP call
+# --------------------------------------------------------------------------
+
+def test_stale_hip_error_not_reported_by_verify():
+    """A failed, unchecked HIP call made just before a valid verify call
+    (hipSetDevice on an ordinal that does not exist) does not turn the
+    verify call's status into ERR_HIP; the call runs and matches the
+    oracle."""
+    import ctypes
+    import tree_masked_attention_amd.api as api
+    wl = SMALL_CASES["gqa8"]()
+    dev = device_inputs(wl)
+    W = wl.mask_words()
+    masks, bad = api.build_mask(dev["parents"], dev["tree_offsets"],
+                                max(wl.max_nodes, 1), W)
+    N, Hq, d = wl.q.shape
+    out = torch.empty((N, Hq, d), dtype=torch.bfloat16, device="cuda:0")
+    lse = torch.empty((N, Hq), dtype=torch.float32, device="cuda:0")
+    ws_bytes = api.workspace_size(wl.num_seqs, N, Hq, wl.num_kv_heads, d,
+                                  wl.max_prefix_len, wl.max_nodes,
+                                  wl.page_size, 0)
+    ws = torch.zeros((max(ws_bytes, 256),), dtype=torch.uint8,
+                     device="cuda:0")
+    torch.cuda.synchronize()
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    planted = hip.hipSetDevice(ctypes.c_int(1 << 20))
+    assert planted != 0
+    code = api._lib.tree_attn_verify(
+        dev["q"].data_ptr(), dev["k_cache"].data_ptr(),
+        dev["v_cache"].data_ptr(), dev["page_table"].data_ptr(),
+        wl.max_pages_per_seq, wl.num_pages, wl.page_size,
+        dev["prefix_lens"].data_ptr(), dev["tree_offsets"].data_ptr(),
+        masks.data_ptr(), W, wl.num_seqs, N, wl.max_prefix_len,
+        wl.max_nodes, Hq, wl.num_kv_heads, d, wl.scale, 0, out.data_ptr(),
+        lse.data_ptr(), ws.data_ptr(), ws.numel(),
+        torch.cuda.current_stream().cuda_stream)
+    pending = hip.hipGetLastError()  # consume what is left for torch
+    say(f"  planted error {planted}; verify status {code}; pending after "
+        f"the call {pending}")
+    assert code == api.OK
+    torch.cuda.synchronize()
+    got = dict(out=out.float().cpu().numpy().astype(np.float64),
+               lse=lse.cpu().numpy().astype(np.float64))
+    ref_out, ref_lse = oracle.workload_attention(wl)
+    assert_parity(got, ref_out, ref_lse, "after a stale HIP error")
