@@ -210,6 +210,36 @@ int tree_attn_verify(const void* q, const void* k_cache, const void* v_cache,
                      size_t workspace_bytes, void* stream);
 
 /*
+ * tree_attn_verify_noalloc - tree_attn_verify for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).
+ *
+ * Same operation, arguments (minus workspace and workspace_bytes), checks
+ * and kernels as tree_attn_verify.  The split partials and arrival
+ * counters live in a device array inside the library, one per GPU, of
+ * TREE_ATTN_NOALLOC_SCRATCH_BYTES bytes, held from the library's load to
+ * the end of the process; the call itself allocates nothing (no hipMalloc,
+ * no allocating library routine).  Sizes whose plan needs more than that
+ * (tree_attn_workspace_size(...) > TREE_ATTN_NOALLOC_SCRATCH_BYTES) return
+ * TREE_ATTN_ERR_WORKSPACE before any launch.  The first call on a device
+ * clears the array's counter area with a kernel on `stream`; every call
+ * that completes leaves it at zero again.  All calls on one GPU share the
+ * array: calls that overlap (other streams, other threads) race and give
+ * wrong output; calls made one after another on one stream do not.
+ */
+#define TREE_ATTN_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+int tree_attn_verify_noalloc(
+    const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* page_table, int32_t max_pages_per_seq, int32_t num_pages,
+    int32_t page_size, const int32_t* prefix_lens,
+    const int32_t* tree_offsets, const uint64_t* masks, int32_t mask_words,
+    int32_t num_seqs, int32_t total_nodes, int32_t max_prefix_len,
+    int32_t max_nodes, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, float scale, int32_t num_splits, void* out, float* lse,
+    void* stream);
+
+/*
  * tree_attn_verify_attend, tree_attn_verify_merge - the two launches of
  * tree_attn_verify, for callers that schedule or time them separately.
  *

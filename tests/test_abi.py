@@ -420,3 +420,45 @@ def test_workspace_size_ex_rules():
     one = f(1, 1, 8, 8, 2, 64, 4000, 8, 1, 1)
     assert one >= 4 * 8 * 8 * 64 * 2
     assert f(1, 1, 8, 8, 2, 64, 300000, 8, 1, 0) == 0  # > 256 x 1039 pages
+
+
+def _noalloc(**over):
+    args = dict(q=1, k=1, v=1, table=1, max_pps=20, num_pages=20,
+                page_size=16, prefix=1, offs=1, masks=1, W=1, S=1, N=16,
+                max_p=256, max_b=16, Hq=8, Hkv=2, d=128, scale=0.088,
+                splits=0, out=1, lse=1)
+    args.update(over)
+    a = args
+    return int(api._lib.tree_attn_verify_noalloc(
+        a["q"], a["k"], a["v"], a["table"], a["max_pps"], a["num_pages"],
+        a["page_size"], a["prefix"], a["offs"], a["masks"], a["W"], a["S"],
+        a["N"], a["max_p"], a["max_b"], a["Hq"], a["Hkv"], a["d"],
+        a["scale"], a["splits"], a["out"], a["lse"], None))
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(Hkv=3), api.ERR_SHAPE),
+    (dict(d=64), api.ERR_UNSUPPORTED),
+    (dict(max_b=65, W=1), api.ERR_SHAPE),
+    (dict(page_size=12), api.ERR_SHAPE),
+    (dict(scale=0.0), api.ERR_SHAPE),
+    (dict(q=None), api.ERR_NULL),
+    (dict(lse=None), api.ERR_NULL),
+    # a plan whose partials exceed the library's device scratch
+    (dict(S=1, N=256, max_p=30000, max_b=256, W=4, Hq=32, Hkv=8,
+          splits=256), api.ERR_WORKSPACE),
+])
+def test_verify_noalloc_rejects(over, code):
+    assert _noalloc(**over) == code
+
+
+def test_verify_noalloc_empty_is_noop():
+    assert _noalloc(S=0, N=0, q=None, k=None, v=None) == api.OK
+    assert _noalloc(N=0) == api.OK
+
+
+def test_noalloc_scratch_limit_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define TREE_ATTN_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)",
+                  text)
+    assert m and int(m.group(1)) << int(m.group(2)) == api.NOALLOC_SCRATCH_BYTES

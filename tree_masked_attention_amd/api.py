@@ -50,6 +50,10 @@ for _name in ("tree_attn_verify_attend", "tree_attn_verify_merge"):
     getattr(_lib, _name).restype = ctypes.c_int
     getattr(_lib, _name).argtypes = _VERIFY_ARGS
 
+_lib.tree_attn_verify_noalloc.restype = ctypes.c_int
+_lib.tree_attn_verify_noalloc.argtypes = _VERIFY_ARGS[:22] + [_p]
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
 _lib.tree_attn_describe_plan.restype = ctypes.c_int
 _lib.tree_attn_describe_plan.argtypes = [_i] * 9 + [_p]
 
@@ -89,6 +93,7 @@ EXPORTED = ("tree_attn_status_string", "tree_attn_abi_version",
             "tree_attn_build_mask", "tree_attn_workspace_size",
             "tree_attn_describe_plan", "tree_attn_verify",
             "tree_attn_verify_attend", "tree_attn_verify_merge",
+            "tree_attn_verify_noalloc",
             "tree_attn_accept", "tree_attn_commit_kv",
             "tree_attn_accept_commit", "tree_attn_build_tree",
             "tree_attn_gdn_verify", "tree_attn_gdn_commit",

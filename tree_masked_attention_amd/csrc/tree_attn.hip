@@ -9,6 +9,7 @@
 
 #include <atomic>
 #include <cmath>
+#include <mutex>
 #include <tuple>
 
 #include "accept_commit.hpp"
@@ -23,6 +24,10 @@
 #include "tree_build.hpp"
 
 using namespace tree_attn;
+
+// Device scratch of tree_attn_verify_noalloc (see device_scratch below).
+static __device__ __align__(256) unsigned char
+    scratch[TREE_ATTN_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -501,6 +506,56 @@ int run_verify(int phases, const void* q, const void* k_cache, const void* v_cac
   return TREE_ATTN_OK;
 }
 
+// ---- device scratch of tree_attn_verify_noalloc
+//
+// A file-scope device array, one copy per GPU, holding what a workspace
+// holds for tree_attn_verify: the arrival counters, then the split
+// partials.  In host code its name stands for a host-side shadow, not a
+// device address: the device address comes from hipGetSymbolAddress, once
+// per device with that device current, and only that address is handed to
+// kernels.
+constexpr size_t kScratchBytes = TREE_ATTN_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes > kCounterBytes, "scratch holds the counters");
+
+__global__ void zero_words_kernel(unsigned* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch; the first call on a
+// device looks it up and clears its counter area on `stream` (a kernel,
+// not a memset, so that a captured graph replays it correctly).  Every
+// call that completes leaves the counters at zero again.
+int device_scratch(hipStream_t stream, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return TREE_ATTN_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return TREE_ATTN_ERR_UNSUPPORTED;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+      void* q = nullptr;
+      if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess ||
+          q == nullptr) {
+        return TREE_ATTN_ERR_HIP;
+      }
+      const int st = launch(&zero_words_kernel,
+                            dim3((kMergeCounters + 255) / 256), dim3(256),
+                            stream, static_cast<unsigned*>(q),
+                            kMergeCounters);
+      if (st != TREE_ATTN_OK) return st;
+      g_scratch[dev].store(q, std::memory_order_release);
+      p = q;
+    }
+  }
+  *out = p;
+  return TREE_ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -605,6 +660,45 @@ int tree_attn_verify(const void* q, const void* k_cache, const void* v_cache,
                     total_nodes, max_prefix_len, max_nodes, num_q_heads,
                     num_kv_heads, head_dim, scale, num_splits, out, lse,
                     workspace, workspace_bytes, stream);
+}
+
+int tree_attn_verify_noalloc(
+    const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* page_table, int32_t max_pages_per_seq, int32_t num_pages,
+    int32_t page_size, const int32_t* prefix_lens,
+    const int32_t* tree_offsets, const uint64_t* masks, int32_t mask_words,
+    int32_t num_seqs, int32_t total_nodes, int32_t max_prefix_len,
+    int32_t max_nodes, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, float scale, int32_t num_splits, void* out, float* lse,
+    void* stream) {
+  // the same checks as tree_attn_verify, and the scratch-size check, before
+  // any HIP call
+  int st = check_verify_sizes(num_seqs, total_nodes, num_q_heads,
+                              num_kv_heads, head_dim, max_prefix_len,
+                              max_nodes, num_splits, mask_words,
+                              max_pages_per_seq, num_pages, page_size, scale);
+  if (st != TREE_ATTN_OK) return st;
+  if (num_seqs == 0 || total_nodes == 0) return TREE_ATTN_OK;
+  Plan pl;
+  st = make_plan(num_seqs, total_nodes, num_q_heads, num_kv_heads,
+                 max_prefix_len, max_nodes, page_size, num_splits, cu_count(),
+                 &pl);
+  if (st != TREE_ATTN_OK) return st;
+  if (pl.ws_bytes > kScratchBytes) return TREE_ATTN_ERR_WORKSPACE;
+  if (!q || !k_cache || !v_cache || !page_table || !prefix_lens ||
+      !tree_offsets || !masks || !out || !lse) {
+    return TREE_ATTN_ERR_NULL;
+  }
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  st = device_scratch(hs, &ws);
+  if (st != TREE_ATTN_OK) return st;
+  return run_verify(kPhaseAttend | kPhaseMerge, q, k_cache, v_cache,
+                    page_table, max_pages_per_seq, num_pages, page_size,
+                    prefix_lens, tree_offsets, masks, mask_words, num_seqs,
+                    total_nodes, max_prefix_len, max_nodes, num_q_heads,
+                    num_kv_heads, head_dim, scale, num_splits, out, lse, ws,
+                    kScratchBytes, stream);
 }
 
 int tree_attn_verify_attend(
