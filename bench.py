@@ -102,7 +102,9 @@ TRAFFIC_FILE = os.path.join(HERE, "profiles", "hbm_traffic.txt")
 # HIP sources of each measured kernel: HBM counters taken on other sources
 # of that kernel are not reported
 KERNEL_SOURCES = {
-    "attn_fwd128h_kernel": ("common.hpp", "attn_merge.hpp", "attn_fwd.hpp",
+    "attn_fwdh_kernel<8>": ("common.hpp", "attn_merge.hpp", "attn_fwd.hpp",
+                            "attn_fwd128h.hpp"),
+    "attn_fwdh_kernel<4>": ("common.hpp", "attn_merge.hpp", "attn_fwd.hpp",
                             "attn_fwd128h.hpp"),
     "attn_fwd256_kernel": ("common.hpp", "attn_merge.hpp", "attn_fwd.hpp",
                               "attn_fwd8.hpp"),
@@ -896,8 +898,8 @@ class VerifyBench:
     def kernel_name(self):
         if self.variant:
             return "attn_var_kernel"
-        return ("attn_fwd256_kernel" if self.plan["rows"] == 256
-                else "attn_fwd128h_kernel")
+        return {256: "attn_fwd256_kernel", 128: "attn_fwdh_kernel<8>",
+                64: "attn_fwdh_kernel<4>"}[self.plan["rows"]]
 
     def measure(self, steps):
         """Per-launch verify and mask-build times and the verify launch's

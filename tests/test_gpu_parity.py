@@ -205,6 +205,50 @@ def test_invalid_parents_reported():
     assert (got[64:] == 0).all()
 
 
+# Cases sized so that the planner takes the 64-row kernel (pairs of at most
+# 128 query rows, enough of them that 64-row blocks fill the CUs: no split).
+def _r64(name, seed, **kw):
+    kw.setdefault("num_q_heads", 32)
+    kw.setdefault("num_kv_heads", 4)
+    return make_workload(seed, name=name, **kw)
+
+
+SIXTY_FOUR_ROW_CASES = {
+    "r64-ragged": lambda: _r64("r64-ragged", 160, prefix_range=(0, 900),
+                               num_seqs=32,
+                               tree_sizes=[1 + (7 * s) % 16 for s in range(32)]),
+    "r64-page4-slow-dma": lambda: _r64("r64-page4", 161,
+                                       prefix_range=(100, 700), num_seqs=32,
+                                       tree_sizes=[16], page_size=4),
+    "r64-page64": lambda: _r64("r64-page64", 162, prefix_range=(600, 1200),
+                               num_seqs=32, tree_sizes=[16], page_size=64),
+    "r64-forest": lambda: _forest(_r64("r64-forest", 163,
+                                       prefix_range=(600, 900), num_seqs=32,
+                                       tree_sizes=[16])),
+    "r64-g4-b32": lambda: _r64("r64-g4-b32", 164, prefix_range=(520, 900),
+                               num_seqs=32, tree_sizes=[32], num_q_heads=16,
+                               num_kv_heads=4, tree_rules="chain"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SIXTY_FOUR_ROW_CASES))
+def test_sixty_four_row_parity(name):
+    import tree_masked_attention_amd.api as api
+    wl = SIXTY_FOUR_ROW_CASES[name]()
+    plan = api.describe_plan(wl.num_seqs, wl.total_nodes, wl.num_q_heads,
+                             wl.num_kv_heads, 128, wl.max_prefix_len,
+                             wl.max_nodes, wl.page_size, 0)
+    say(f"[gpu] 64-row case {name}: plan {plan}")
+    assert plan["rows"] == 64 and plan["waves"] == 4 and plan["splits"] == 1
+    got = run_gpu(wl)
+    assert np.array_equal(got["masks"], oracle.workload_masks(wl))
+    ref_out, ref_lse = oracle.workload_attention(wl)
+    assert_parity(got, ref_out, ref_lse, name)
+    # the same inputs with forced splits take the 128-row kernel
+    two = run_gpu(wl, num_splits=2)
+    assert_parity(two, ref_out, ref_lse, f"{name}, 2 splits")
+
+
 # --------------------------------------------------------------------------
 # the five standard workloads at full size, planned launch (as benchmarked)
 # --------------------------------------------------------------------------

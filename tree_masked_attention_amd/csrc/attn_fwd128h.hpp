@@ -1,14 +1,17 @@
-// 128-row variant of the split-KV tree-verification attention kernel with
-// eight waves: two waves per SIMD on the same 32 query rows, each taking
-// one 32-key half of every 64-key tile.
+// Split-KV tree-verification attention kernel whose waves split every
+// 64-key tile in two key halves: NW = 8 waves on 128 query rows, or NW = 4
+// waves on 64 rows.
 //
 // Same operation, data layout, MFMA mapping, LDS ring format, DMA and mask
 // handling as the 256-row kernel (definitions in attn_fwd.hpp).  Wave w
-// owns query rows 32 (w & 3) .. +31 of the workgroup's 128 and keys
-// 32 (w >> 2) .. +31 of each tile; waves w and w + 4 share a SIMD, so every
-// SIMD holds two waves and its vector ALU issues at the two-wave rate
-// (about twice the one-wave rate, three times for the exponential), where
-// four waves of 32 rows would leave one wave per SIMD.  Each wave keeps
+// owns query rows 32 (w % (NW/2)) .. +31 of the workgroup's rows and keys
+// 32 (w / (NW/2)) .. +31 of each tile.  With NW = 8, waves w and w + 4
+// share a SIMD, so every SIMD holds two waves and its vector ALU issues at
+// the two-wave rate (about twice the one-wave rate, three times for the
+// exponential), where four waves of 32 rows would leave one wave per SIMD.
+// The 64-row shape (one wave per SIMD) serves bandwidth-bound launches in
+// which 64-row blocks alone give every CU a workgroup: the key range then
+// needs no split, so no partials are written or merged.  Each wave keeps
 // its own online-softmax state (reference max, row sum, O) over its half
 // of the keys; at the end the wave of the upper half hands its state to the
 // lower-half wave of the same rows through LDS, which combines the two
@@ -21,16 +24,19 @@
 namespace tree_attn {
 
 constexpr int kRowsPerWG128 = 128;
+constexpr int kRowsPerWG64 = 64;
 // ring offset of the epilogue's row staging (past the halves' exchange)
 constexpr int kEpilogueStage = 68 * 1024;
 
-__global__ __launch_bounds__(512, 1) void attn_fwd128h_kernel(FwdParams p) {
-  constexpr int NW = 8;
+template <int NW>
+__global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
+  static_assert(NW == 8 || NW == 4, "shape");
+  constexpr int kRows = 16 * NW;         // query rows per workgroup
   constexpr int kThreads = NW * 64;
   constexpr int kOpsPerMat = 16 / NW;    // 1-KB DMA ops per wave per matrix
   constexpr int kOps = 2 * kOpsPerMat;
   constexpr int kDmaRows = 4 * kOpsPerMat;  // tile rows a wave moves
-  constexpr int kLog2DmaRows = 3;
+  constexpr int kLog2DmaRows = NW == 8 ? 3 : 4;
   static_assert((1 << kLog2DmaRows) == kDmaRows, "shape");
   __shared__ __align__(1024) unsigned char ring[2 * kVOff];
   __shared__ int pg_lds[kPageCache];
@@ -49,8 +55,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd128h_kernel(FwdParams p) {
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int rg = wave & 3;   // 32-row group
-  const int kh = wave >> 2;  // key half of every tile (32-key block)
+  const int rg = wave % (NW / 2);  // 32-row group
+  const int kh = wave / (NW / 2);  // key half of every tile (32-key block)
   const int lane = tid & 63;
   const int col = lane & 31, half = lane >> 5;
 
@@ -83,7 +89,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd128h_kernel(FwdParams p) {
   const int B = b - a;
   const int P = max(p.prefix_lens[s], 0);
   const int rows = p.G * B;
-  const int r0 = mb * kRowsPerWG128;
+  const int r0 = mb * kRows;
   const int T = min(P + B, p.max_tokens);
   if (r0 >= rows || kbeg >= T) {
     wait_vmcnt<0>();  // no DMA into LDS outlives the workgroup
@@ -95,7 +101,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd128h_kernel(FwdParams p) {
   // ancestor-mask rows of the workgroup's nodes, all W words (the window
   // of words the split needs starts at word 0)
   const int n_lo = r0 / p.G;
-  const int n_hi = (min(r0 + kRowsPerWG128, rows) - 1) / p.G;
+  const int n_hi = (min(r0 + kRows, rows) - 1) / p.G;
   const int nnodes = n_hi - n_lo + 1;
   const bool has_tree = kend > P;
   const int wlo = 0;
@@ -113,9 +119,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd128h_kernel(FwdParams p) {
 
   wait_vmcnt<0>();
   __syncthreads();  // page slice visible
-  // Q rows r0 .. r0+127 (rows past the last one repeat it): instruction i
-  // moves rows 4i .. 4i+3, chunk-swizzled like K; rows 0-63 go to the K
-  // half of stage 3, rows 64-127 to its V half
+  // Q rows r0 .. r0+kRows-1 (rows past the last one repeat it):
+  // instruction i moves rows 4i .. 4i+3, chunk-swizzled like K; rows 0-63
+  // go to the K half of stage 3, rows 64-127 to its V half
   const unsigned q_lds = ring_base + 3 * kTileBytes;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -338,14 +344,20 @@ __global__ __launch_bounds__(512, 1) void attn_fwd128h_kernel(FwdParams p) {
     // S^T(j+1) on the matrix core | probabilities of tile j
     qk_half(j + 1, Snext);
     exps_half(Scur, pf);
-    if (dma_inbody) dma_part(dp, 0);  // first half of tile j+3's DMA
+    if (dma_inbody) {  // first half of tile j+3's DMA
+#pragma unroll
+      for (int k = 0; k < kOpsPerMat / 2; ++k) dma_part(dp, k);
+    }
     // PV(j) | mask and max of tile j+1
     pv_half(j, pf);
     if (mask_next) {
       apply_half_mask(Snext, half_allow(kbeg + (j + 1) * kKeyTile));
     }
     const bool need = next_ref(Snext, m_new, alpha);
-    if (dma_inbody) dma_part(dp, 1);  // second half
+    if (dma_inbody) {  // second half
+#pragma unroll
+      for (int k = kOpsPerMat / 2; k < kOpsPerMat; ++k) dma_part(dp, k);
+    }
     return need;
   };
   auto finish = [&](bool r, float m_new, float alpha) {
@@ -534,7 +546,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd128h_kernel(FwdParams p) {
     }
   }
   if (p.counters != nullptr) {
-    merge_if_last<kThreads>(p, s, g, mb, a, rows, r0, kRowsPerWG128, T, tid,
+    merge_if_last<kThreads>(p, s, g, mb, a, rows, r0, kRows, T, tid,
                             pg_lds);
   }
 }

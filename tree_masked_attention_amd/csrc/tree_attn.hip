@@ -94,7 +94,7 @@ int ilog2(int x) {
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct Plan {
-  int rows = 128;    // query rows per workgroup (128 or 256; 8 waves)
+  int rows = 128;    // query rows per workgroup (64: 4 waves; 128, 256: 8)
   int mblocks = 0;   // row blocks per (sequence, kv head)
   int splits = 1;    // key-range splits
   int chunk = 0;     // keys per split (multiple of the 64-key tile)
@@ -174,6 +174,20 @@ int make_plan(int S, int N, int Hq, int Hkv, int max_prefix_len,
   {
     const int st = choose(rpw);
     if (st != TREE_ATTN_OK) return st;
+  }
+  // Bandwidth-bound launches whose (sequence, kv head) pairs have at most
+  // 128 rows: when 64-row blocks alone give every CU a workgroup, they
+  // replace a split of the key range (the two blocks of a pair read the
+  // same K/V, which the XCD-aware order keeps in one L2), so no partials
+  // are written or merged.
+  if (rpw == kRowsPerWG128 && req_splits <= 0 && rows <= kRowsPerWG128 &&
+      splits > 1 && min_splits == 1) {
+    const long long units64 =
+        (long long)S * Hkv * ((rows + kRowsPerWG64 - 1) / kRowsPerWG64);
+    if (units64 >= cus) {
+      const int st = choose(kRowsPerWG64);
+      if (st != TREE_ATTN_OK) return st;
+    }
   }
   pl.splits = (int)splits;
   pl.chunk = (int)chunk;
@@ -473,9 +487,13 @@ int run_verify(int phases, const void* q, const void* k_cache, const void* v_cac
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const unsigned grid = 8u * (unsigned)fp.per_xcd;
   if (phases & kPhaseAttend) {
-    st = launch(pl.rows == kRowsPerWG8 ? &attn_fwd256_kernel
-                                       : &attn_fwd128h_kernel,
-                dim3(grid), dim3(512), hs, fp);
+    if (pl.rows == kRowsPerWG8) {
+      st = launch(&attn_fwd256_kernel, dim3(grid), dim3(512), hs, fp);
+    } else if (pl.rows == kRowsPerWG128) {
+      st = launch(&attn_fwdh_kernel<8>, dim3(grid), dim3(512), hs, fp);
+    } else {
+      st = launch(&attn_fwdh_kernel<4>, dim3(grid), dim3(256), hs, fp);
+    }
     if (st != TREE_ATTN_OK) return st;
   }
 
@@ -635,7 +653,7 @@ int tree_attn_describe_plan(int32_t num_seqs, int32_t total_nodes,
                  max_prefix_len, max_nodes, page_size, num_splits, cu_count(),
                  &pl);
   if (st != TREE_ATTN_OK) return st;
-  info[0] = kWaves;
+  info[0] = pl.rows == kRowsPerWG64 ? 4 : kWaves;
   info[1] = pl.rows;
   info[2] = pl.splits;
   info[3] = pl.chunk;
