@@ -51,7 +51,7 @@ def _call(api, fn_name, wl, dev, masks, splits, with_ws):
 def test_noalloc_matches_verify_twice():
     import tree_masked_attention_amd.api as api
     cases = [
-        (standard_workload("qwen3-30b-a3b-32x-b16-p2k"), 0),
+        (standard_workload("qwen3-8b-b256-p4k"), 0),
         (make_workload(401, name="smaller", prefix_lens=[700, 300, 33],
                        tree_sizes=[40, 20, 64], num_q_heads=8,
                        num_kv_heads=2), 3),

@@ -301,17 +301,19 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
   // probabilities against m_ref; adds their fp32 sum
   auto exps_half = [&](const f32x16& S, bf16x8 (&pf)[2]) {
     const float mu = (m_ref == -INFINITY) ? 0.f : m_ref;
-    float ps0 = 0.f, ps1 = 0.f;
+    float e[16];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) e[rr] = fast_exp2(fmaf(S[rr], c2, -mu));
 #pragma unroll
     for (int rr = 0; rr < 16; rr += 2) {
-      const float e0 = fast_exp2(fmaf(S[rr], c2, -mu));
-      const float e1 = fast_exp2(fmaf(S[rr + 1], c2, -mu));
-      ps0 += e0;
-      ps1 += e1;
-      pf[rr >> 3][rr & 7] = (__bf16)e0;
-      pf[rr >> 3][(rr & 7) + 1] = (__bf16)e1;
+      pf[rr >> 3][rr & 7] = (__bf16)e[rr];
+      pf[rr >> 3][(rr & 7) + 1] = (__bf16)e[rr + 1];
     }
-    l_run += ps0 + ps1;
+    float t8[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) t8[k] = e[2 * k] + e[2 * k + 1];
+    l_run += ((t8[0] + t8[1]) + (t8[2] + t8[3])) +
+             ((t8[4] + t8[5]) + (t8[6] + t8[7]));
   };
   // reference max for the next half tile (lazy raise, as in the others)
   auto next_ref = [&](const f32x16& Sx, float& m_new, float& alpha) -> bool {
@@ -319,7 +321,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
 #pragma unroll
     for (int rr = 0; rr < 16; rr += 2) {
       tmax = __builtin_elementwise_maximum(
-          tmax, __builtin_elementwise_maximum(Sx[rr], Sx[rr + 1]));
+          __builtin_elementwise_maximum(tmax, Sx[rr]), Sx[rr + 1]);
     }
     tmax = __builtin_elementwise_maximum(tmax, other_half(tmax)) * c2;
     const bool need = tmax > m_ref + kLazyRescale;

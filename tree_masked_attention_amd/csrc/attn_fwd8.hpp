@@ -339,17 +339,22 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const float mu = (m_ref[qb] == -INFINITY) ? 0.f : m_ref[qb];
-      float ps0 = 0.f, ps1 = 0.f;
+      float e[16];
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        e[rr] = fast_exp2(fmaf(S[qb][kb][rr], c2, -mu));
+      }
 #pragma unroll
       for (int rr = 0; rr < 16; rr += 2) {
-        const float e0 = fast_exp2(fmaf(S[qb][kb][rr], c2, -mu));
-        const float e1 = fast_exp2(fmaf(S[qb][kb][rr + 1], c2, -mu));
-        ps0 += e0;
-        ps1 += e1;
-        pf[qb][kb][rr >> 3][rr & 7] = (__bf16)e0;
-        pf[qb][kb][rr >> 3][(rr & 7) + 1] = (__bf16)e1;
+        pf[qb][kb][rr >> 3][rr & 7] = (__bf16)e[rr];
+        pf[qb][kb][rr >> 3][(rr & 7) + 1] = (__bf16)e[rr + 1];
       }
-      l_run[qb] += ps0 + ps1;
+      float t8[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) t8[k] = e[2 * k] + e[2 * k + 1];
+      const float t4a = (t8[0] + t8[1]) + (t8[2] + t8[3]);
+      const float t4b = (t8[4] + t8[5]) + (t8[6] + t8[7]);
+      l_run[qb] += t4a + t4b;
     }
   };
   // reference max for a tile, raised only past the lazy-rescale margin
@@ -364,8 +369,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
 #pragma unroll
         for (int rr = 0; rr < 16; rr += 2) {
           tmax = __builtin_elementwise_maximum(
-              tmax, __builtin_elementwise_maximum(Sx[qb][kb][rr],
-                                                  Sx[qb][kb][rr + 1]));
+              __builtin_elementwise_maximum(tmax, Sx[qb][kb][rr]),
+              Sx[qb][kb][rr + 1]);
         }
       }
       tmax = __builtin_elementwise_maximum(tmax, other_half(tmax)) * c2;
@@ -393,14 +398,10 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
     // segment 1: S^T(j+1) keys 0..31 | probabilities of keys 0..31
     qk_block(j + 1, 0, Snext);
     exps_block(Scur, 0, pf);
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-    for (int i = 0; i < 8 * QB; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-    }
-    // the segments are scheduled separately: without this fence the
-    // scheduler mixes their groups and the matrix core waits more
+    // the segments are scheduled separately: without these fences the
+    // scheduler mixes them and the matrix core waits more (inside a
+    // segment the compiler's own interleave beat explicit interleave
+    // groups by 1-2% on the long-context workload)
     __builtin_amdgcn_sched_barrier(0);
     if (dma_inbody) {  // first half of tile j+3's DMA
 #pragma unroll
@@ -412,18 +413,6 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
     qk_block(j + 1, 1, Snext);
     pv_block(j, 0, pf);
     exps_block(Scur, 1, pf);
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-    for (int i = 0; i < 8 * QB; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 / QB, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 8 * QB; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-    }
     __builtin_amdgcn_sched_barrier(0);
     if (dma_inbody) {  // second half
 #pragma unroll
