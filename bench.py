@@ -102,13 +102,13 @@ TRAFFIC_FILE = os.path.join(HERE, "profiles", "hbm_traffic.txt")
 # HIP sources of each measured kernel: HBM counters taken on other sources
 # of that kernel are not reported
 KERNEL_SOURCES = {
-    "attn_fwdh_kernel<8>": ("common.hpp", "attn_merge.hpp", "attn_fwd.hpp",
-                            "attn_fwd128h.hpp"),
-    "attn_fwdh_kernel<4>": ("common.hpp", "attn_merge.hpp", "attn_fwd.hpp",
-                            "attn_fwd128h.hpp"),
-    "attn_fwd256_kernel": ("common.hpp", "attn_merge.hpp", "attn_fwd.hpp",
-                              "attn_fwd8.hpp"),
-    "attn_merge_kernel": ("common.hpp", "attn_merge.hpp"),
+    "attn_fwdh_kernel<8>": ("common.hpp", "split_plan.hpp", "attn_merge.hpp",
+                            "attn_fwd.hpp", "attn_fwd128h.hpp"),
+    "attn_fwdh_kernel<4>": ("common.hpp", "split_plan.hpp", "attn_merge.hpp",
+                            "attn_fwd.hpp", "attn_fwd128h.hpp"),
+    "attn_fwd256_kernel": ("common.hpp", "split_plan.hpp", "attn_merge.hpp",
+                           "attn_fwd.hpp", "attn_fwd8.hpp"),
+    "attn_merge_kernel": ("common.hpp", "split_plan.hpp", "attn_merge.hpp"),
     "gdn_verify_kernel": ("common.hpp", "gdn.hpp"),
     "attn_var_kernel": ("common.hpp", "attn_var.hpp"),
 }

@@ -100,9 +100,13 @@ def test_workspace_size_rules():
     ws1 = api.workspace_size(1, 16, 8, 2, 128, 256, 16, 16, 1)
     ws4 = api.workspace_size(1, 16, 8, 2, 128, 1024, 16, 16, 4)
     assert ws1 == 0
-    # 64 KB of arrival counters, then per split and row the fp16 output
-    # (256 B) and fp32 (max, sum), each part rounded up to 256 B
-    rows = 4 * 16 * 8
+    # 64 KB of arrival counters, then one slot of partial rows per work
+    # unit (4 splits x 2 kv heads x 1 row block of 128 rows): per row the
+    # fp16 output (256 B) and two 32-bit statistics, each part rounded up
+    # to 256 B
+    plan = api.describe_plan(1, 16, 8, 2, 128, 1024, 16, 16, 4)
+    assert plan["rows"] == 128 and plan["splits"] == 4
+    rows = 4 * 2 * 128
     part_o = -(-rows * 256 // 256) * 256
     part_ml = -(-rows * 8 // 256) * 256
     assert ws4 == 65536 + part_o + part_ml
@@ -110,7 +114,7 @@ def test_workspace_size_rules():
     assert api.workspace_size(1, 16, 8, 2, 128, 256, 16, 12, 0) == 0  # page
     # tiny pages force more splits (each split's page slice is bounded)
     assert api.workspace_size(1, 16, 8, 2, 128, 5000, 16, 1, 1) >= \
-        5 * 16 * 8 * (128 * 2 + 2 * 4)
+        5 * 2 * 128 * (128 * 2 + 2 * 4)
 
 
 def test_describe_plan():

@@ -595,6 +595,100 @@ def test_random_split_merge_repeated(seed):
 
 
 # --------------------------------------------------------------------------
+# device-balanced split plans: a split launch over 2 .. 64 sequences sizes
+# its splits on the device from each sequence's own key range (one shared
+# split length, as many splits per sequence as its keys need), so short
+# sequences take few workgroups and long ones many
+# --------------------------------------------------------------------------
+
+def _balanced_many(seed, S):
+    r = np.random.default_rng(seed)
+    return _case(f"bal-{S}", seed,
+                 prefix_lens=[int(x) for x in r.integers(0, 3000, size=S)],
+                 tree_sizes=[int(x) for x in r.integers(0, 40, size=S)],
+                 num_q_heads=8, num_kv_heads=1)
+
+
+BALANCED_CASES = {
+    # lengths 12x apart; 128-row kernel
+    "bal-ragged": (lambda: _case("bal-ragged", 180,
+                                 prefix_lens=[300, 4000, 12000],
+                                 tree_sizes=[40, 9, 70]), True),
+    # sequences without tree nodes (no units) and one without prefix
+    "bal-empty-trees": (lambda: _case("bal-empty", 181,
+                                      prefix_lens=[0, 2500, 6000, 10],
+                                      tree_sizes=[0, 30, 0, 5]), True),
+    # 256-row kernel, two and three sequences of different lengths, one
+    # with fewer rows than a block
+    "bal-256": (lambda: _case("bal-256", 182, prefix_lens=[16000, 9000],
+                              tree_sizes=[64, 70], num_q_heads=32,
+                              num_kv_heads=8), True),
+    "bal-256-ragged": (lambda: _case("bal-256r", 183,
+                                     prefix_lens=[17000, 300, 6000],
+                                     tree_sizes=[64, 3, 70], num_q_heads=32,
+                                     num_kv_heads=8, page_size=32), True),
+    # the largest batch the device plan takes, and one sequence more (the
+    # host's uniform plan)
+    "bal-64-seqs": (lambda: _balanced_many(184, 64), True),
+    "uniform-65-seqs": (lambda: _balanced_many(185, 65), False),
+}
+
+
+def _balanced_inputs(name):
+    import tree_masked_attention_amd.api as api
+    make, balanced = BALANCED_CASES[name]
+    wl = make()
+    plan = api.describe_plan(wl.num_seqs, wl.total_nodes, wl.num_q_heads,
+                             wl.num_kv_heads, wl.head_dim, wl.max_prefix_len,
+                             wl.max_nodes, wl.page_size, 0)
+    say(f"[gpu] {name}: S={wl.num_seqs} P={[int(x) for x in wl.prefix_lens]} "
+        f"B={[int(x) for x in wl.tree_sizes]} Hq={wl.num_q_heads} "
+        f"Hkv={wl.num_kv_heads} page={wl.page_size} plan={plan}")
+    assert plan["splits"] > 1
+    assert (2 <= wl.num_seqs <= 64) == balanced
+    return wl, plan
+
+
+@pytest.mark.parametrize("name", sorted(BALANCED_CASES))
+def test_balanced_plan_parity(name):
+    wl, _ = _balanced_inputs(name)
+    got = run_gpu(wl)
+    assert (got["bad"] == -1).all()
+    ref_out, ref_lse = oracle.workload_attention(wl)
+    assert_parity(got, ref_out, ref_lse, name)
+
+
+@pytest.mark.parametrize("name", sorted(BALANCED_CASES))
+def test_balanced_plan_two_launches_and_repeats(name):
+    # the one-call form (last split workgroup merges) equals the two-launch
+    # form (attention kernel, then merge kernel) bit for bit, on three
+    # calls in a row over one workspace, each leaving the arrival counters
+    # at zero
+    import tree_masked_attention_amd.api as api
+    wl, _ = _balanced_inputs(name)
+    dev = device_inputs(wl)
+    masks, _ = api.build_mask(dev["parents"], dev["tree_offsets"],
+                              max(wl.max_nodes, 1), wl.mask_words())
+    args = (dev["q"], dev["k_cache"], dev["v_cache"], dev["page_table"],
+            dev["prefix_lens"], dev["tree_offsets"], masks, wl.max_prefix_len,
+            wl.max_nodes, wl.scale)
+    nbytes = api.workspace_size(wl.num_seqs, wl.total_nodes, wl.num_q_heads,
+                                wl.num_kv_heads, wl.head_dim,
+                                wl.max_prefix_len, wl.max_nodes,
+                                wl.page_size, 0)
+    ws2 = torch.zeros((max(nbytes, 256),), dtype=torch.uint8, device="cuda:0")
+    ref_out, ref_lse = api.verify(*args, workspace=ws2, phase="attend")
+    api.verify(*args, out=ref_out, lse=ref_lse, workspace=ws2, phase="merge")
+    ws = torch.zeros_like(ws2)
+    for rep in range(3):
+        out, lse = api.verify(*args, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)), rep
+        assert torch.equal(lse, ref_lse), rep
+        assert int(ws[:65536].count_nonzero()) == 0
+
+
+# --------------------------------------------------------------------------
 # status contract: an error left pending by an unrelated HIP call
 # --------------------------------------------------------------------------
 

@@ -58,6 +58,7 @@
 
 #include "attn_merge.hpp"
 #include "common.hpp"
+#include "split_plan.hpp"
 
 namespace tree_attn {
 
@@ -71,15 +72,15 @@ struct FwdParams {
   const uint64_t* masks;
   __bf16* out;
   float* lse;
-  _Float16* part_o;  // [splits][N*Hq][128]  O of the split / its row sum
-  float* part_ml;    // [splits][N*Hq][2]  (max in log2 units, row sum)
-  unsigned* counters;  // [S][Hkv][mblocks] arrival counts, or null: the
-                       // merge kernel merges the partials
+  _Float16* part_o;  // [units][rows per workgroup][128] partial outputs
+  float* part_ml;    // [units][rows per workgroup][2] split statistics
+  unsigned* counters;  // one arrival count per (sequence, kv head, row
+                       // block), or null: the merge kernel merges
   int max_pps, num_pages, log2_page, W;
   int max_tokens;  // min(max_pps * page_size, 2^30)
   int S, N, Hq, Hkv, G;
-  int mblocks, splits, chunk;
-  int units, per_xcd;  // work units; units handled per XCD slot column
+  int per_xcd;     // units handled per XCD slot column of the grid
+  SplitParams plan;  // the work units (split_plan.hpp)
   float scale_log2;
 };
 
@@ -195,19 +196,16 @@ __device__ __forceinline__ void apply_tile_mask(f32x16 (&S)[2], uint64_t allow,
 }
 
 // Epilogue of a split workgroup of a launch that merges its own partials
-// (merge_if_last_rows): the row block (s, g, mb), rows [r0, r0 +
-// rows_per_wg) of the pair, whose splits with a first key below T reach
-// their epilogue.
+// (merge_if_last_rows): unit un, rows [r0, r0 + rows_per_wg) of its pair.
 template <int NT>
-__device__ __forceinline__ void merge_if_last(const FwdParams& p, int s, int g,
-                                              int mb, int a, int rows, int r0,
-                                              int rows_per_wg, int T, int tid,
-                                              int* flag_lds) {
-  const int nsplit = min(p.splits, (T + p.chunk - 1) / p.chunk);
+__device__ __forceinline__ void merge_if_last(const FwdParams& p,
+                                              const Unit& un, int rows,
+                                              int r0, int rows_per_wg,
+                                              int tid, int* flag_lds) {
   merge_if_last_rows<NT, kHeadDim>(
-      p.counters + ((size_t)s * p.Hkv + g) * p.mblocks + mb, nsplit, p.part_o,
-      p.part_ml, p.out, p.lse, (size_t)p.N * p.Hq, p.Hq, p.G, g, a, r0,
-      min(r0 + rows_per_wg, rows), tid, flag_lds);
+      p.counters + un.seg, un.nsplit, p.part_o, p.part_ml, p.out, p.lse,
+      p.Hq, p.G, un.g, un.a, r0, min(r0 + rows_per_wg, rows),
+      PartSlots{un.slot0, un.mblocks, rows_per_wg, r0}, tid, flag_lds);
 }
 
 }  // namespace tree_attn

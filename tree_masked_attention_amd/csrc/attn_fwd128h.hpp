@@ -28,7 +28,7 @@ constexpr int kRowsPerWG64 = 64;
 // ring offset of the epilogue's row staging (past the halves' exchange)
 constexpr int kEpilogueStage = 68 * 1024;
 
-template <int NW>
+template <int NW, bool kBalanced>
 __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
   static_assert(NW == 8 || NW == 4, "shape");
   constexpr int kRows = 16 * NW;         // query rows per workgroup
@@ -42,16 +42,13 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
   __shared__ int pg_lds[kPageCache];
   __shared__ uint64_t mk_lds[kMaskCache];
 
-  // XCD-aware decode, as in the other kernels
+  // XCD-aware numbering (consecutive units on one XCD), then the unit
   const int bid = blockIdx.x;
-  int L = (bid & 7) * p.per_xcd + (bid >> 3);
-  if (L >= p.units) return;
-  const int mb = L % p.mblocks;
-  L /= p.mblocks;
-  const int split = L % p.splits;
-  L /= p.splits;
-  const int g = L % p.Hkv;
-  const int s = L / p.Hkv;
+  const int L = (bid & 7) * p.per_xcd + (bid >> 3);
+  if (L >= p.plan.parts) return;
+  Unit un = decode_unit<kBalanced>(p.plan, L);
+  if (!un.valid) return;
+  const int s = un.s, g = un.g, mb = un.mb, split = un.split;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -73,10 +70,10 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
   // bounds load; (2) once the entries are in, Q (staged in ring stage 3,
   // which tile 3 only overwrites after every wave has read it), the
   // ancestor-mask rows and tiles 0-2 are all in flight together.
-  const int kbeg = split * p.chunk;
+  const int kbeg = split * un.chunk;
   const int lp0 = kbeg >> p.log2_page;
   {
-    const int npg_max = min(min(((p.chunk - 1) >> p.log2_page) + 2, kPageCache),
+    const int npg_max = min(min(((un.chunk - 1) >> p.log2_page) + 2, kPageCache),
                             p.max_pps - lp0);
     const int* ptab = p.page_table + (size_t)s * p.max_pps + lp0;
     for (int i0 = wave * 64; i0 < npg_max; i0 += kThreads) {
@@ -84,18 +81,15 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
     }
   }
 
-  const int a = clampi(p.tree_offsets[s], 0, p.N);
-  const int b = clampi(p.tree_offsets[s + 1], a, p.N);
-  const int B = b - a;
-  const int P = max(p.prefix_lens[s], 0);
+  load_bounds(p.plan, un);
+  const int a = un.a, B = un.B, P = un.P, T = un.T;
   const int rows = p.G * B;
   const int r0 = mb * kRows;
-  const int T = min(P + B, p.max_tokens);
   if (r0 >= rows || kbeg >= T) {
     wait_vmcnt<0>();  // no DMA into LDS outlives the workgroup
     return;
   }
-  const int kend = min(T, kbeg + p.chunk);
+  const int kend = min(T, kbeg + un.chunk);
   const int n = (kend - kbeg + kKeyTile - 1) / kKeyTile;  // tiles, >= 1
 
   // ancestor-mask rows of the workgroup's nodes, all W words (the window
@@ -492,7 +486,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
     // the stores write whole rows
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     int ex = 0;
-    if (p.splits > 1) {
+    if (un.nsplit > 1) {
       float amax = 0.f;
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
@@ -509,7 +503,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
     for (int db = 0; db < 4; ++db) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        if (p.splits == 1) {
+        if (un.nsplit == 1) {
           bf16x4 v4;
 #pragma unroll
           for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(o[db][g4 * 4 + e] * inv);
@@ -525,19 +519,20 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
       }
     }
     const unsigned stg = ring_base + kEpilogueStage + rg * 8192;
-    const int row = rvalid ? (int)qrow : -1;
-    if (p.splits == 1) {
-      store_rows_staged(pk, stg, row, reinterpret_cast<char*>(p.out), lane);
+    if (un.nsplit == 1) {
+      store_rows_staged(pk, stg, rvalid ? (int)qrow : -1,
+                        reinterpret_cast<char*>(p.out), lane);
       if (half == 0 && rvalid) {
         p.lse[qrow] = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
       }
     } else {
-      const size_t prow0 = (size_t)split * p.N * p.Hq;
-      store_rows_staged(pk, stg, row,
+      // the unit's partial slot: its rows in row-block order
+      const size_t prow0 = (size_t)L * kRows;
+      store_rows_staged(pk, stg, rvalid ? r - r0 : -1,
                         reinterpret_cast<char*>(p.part_o + prow0 * kHeadDim),
                         lane, p.counters != nullptr);
       if (half == 0 && rvalid) {
-        float* dst = p.part_ml + (prow0 + qrow) * 2;
+        float* dst = p.part_ml + (prow0 + (r - r0)) * 2;
         const uint64_t st = pack_split_stats(split_lse2(m_ref, l_tot), ex);
         if (p.counters != nullptr) {
           store_coherent8(dst, st);
@@ -547,9 +542,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
       }
     }
   }
-  if (p.counters != nullptr) {
-    merge_if_last<kThreads>(p, s, g, mb, a, rows, r0, kRows, T, tid,
-                            pg_lds);
+  if (p.counters != nullptr && un.nsplit > 1) {
+    merge_if_last<kThreads>(p, un, rows, r0, kRows, tid, pg_lds);
   }
 }
 

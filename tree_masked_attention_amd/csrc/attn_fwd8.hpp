@@ -19,6 +19,7 @@ namespace tree_attn {
 
 constexpr int kRowsPerWG8 = 256;
 
+template <bool kBalanced>
 __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
   constexpr int NW = 8;
   constexpr int QB = 1;                  // 32-query blocks per wave
@@ -35,14 +36,11 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
   // XCD-aware decode: consecutive work units (the row blocks of one
   // (sequence, kv head, split), which read the same K/V) go to one XCD.
   const int bid = blockIdx.x;
-  int L = (bid & 7) * p.per_xcd + (bid >> 3);
-  if (L >= p.units) return;
-  const int mb = L % p.mblocks;
-  L /= p.mblocks;
-  const int split = L % p.splits;
-  L /= p.splits;
-  const int g = L % p.Hkv;
-  const int s = L / p.Hkv;
+  const int L = (bid & 7) * p.per_xcd + (bid >> 3);
+  if (L >= p.plan.parts) return;
+  Unit un = decode_unit<kBalanced>(p.plan, L);
+  if (!un.valid) return;
+  const int s = un.s, g = un.g, mb = un.mb, split = un.split;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -52,12 +50,12 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
   // All prologue loads are issued before any is waited for: the split's
   // page-table entries first (they need only the sequence and the split),
   // then, once the tree bounds are in, the mask words and Q.
-  const int kbeg = split * p.chunk;
+  const int kbeg = split * un.chunk;
   const int lp0 = kbeg >> p.log2_page;
   constexpr int kPgPer = (kPageCache + kThreads - 1) / kThreads;
   int pgv[kPgPer];
   {
-    const int npg_max = min(min(((p.chunk - 1) >> p.log2_page) + 2, kPageCache),
+    const int npg_max = min(min(((un.chunk - 1) >> p.log2_page) + 2, kPageCache),
                             p.max_pps - lp0);
     const int* ptab = p.page_table + (size_t)s * p.max_pps + lp0;
 #pragma unroll
@@ -67,16 +65,13 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
     }
   }
 
-  const int a = clampi(p.tree_offsets[s], 0, p.N);
-  const int b = clampi(p.tree_offsets[s + 1], a, p.N);
-  const int B = b - a;
-  const int P = max(p.prefix_lens[s], 0);
+  load_bounds(p.plan, un);
+  const int a = un.a, B = un.B, P = un.P, T = un.T;
   const int rows = p.G * B;
   const int r0 = mb * kRowsPerWG8;
   if (r0 >= rows) return;
-  const int T = min(P + B, p.max_tokens);
   if (kbeg >= T) return;
-  const int kend = min(T, kbeg + p.chunk);
+  const int kend = min(T, kbeg + un.chunk);
   const int n = (kend - kbeg + kKeyTile - 1) / kKeyTile;  // tiles, >= 1
   const int npg = min(((kend - 1) >> p.log2_page) - lp0 + 1, kPageCache);
 
@@ -538,7 +533,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
     const float l_tot = l_run[qb] + other_half(l_run[qb]);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     int ex = 0;  // scale exponent of a split's partial row (f16_row_exp)
-    if (p.splits > 1) {
+    if (un.nsplit > 1) {
       float amax = 0.f;
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
@@ -556,7 +551,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
     for (int db = 0; db < 4; ++db) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        if (p.splits == 1) {
+        if (un.nsplit == 1) {
           bf16x4 v4;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -574,20 +569,22 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
       }
     }
     const unsigned stg = ring_base + (unsigned)(wave * QB + qb) * 8192;
-    const int row = rvalid[qb] ? (int)qrow[qb] : -1;
-    if (p.splits == 1) {
-      store_rows_staged(pk, stg, row, reinterpret_cast<char*>(p.out), lane);
+    if (un.nsplit == 1) {
+      store_rows_staged(pk, stg, rvalid[qb] ? (int)qrow[qb] : -1,
+                        reinterpret_cast<char*>(p.out), lane);
       if (half == 0 && rvalid[qb]) {
         p.lse[qrow[qb]] =
             l_tot > 0.f ? (m_ref[qb] + log2f(l_tot)) * kLn2 : -INFINITY;
       }
     } else {
-      const size_t prow0 = (size_t)split * p.N * p.Hq;
-      store_rows_staged(pk, stg, row,
+      // the unit's partial slot: its rows in row-block order
+      const int rl = (wave * QB + qb) * 32 + col;
+      const size_t prow0 = (size_t)L * kRowsPerWG8;
+      store_rows_staged(pk, stg, rvalid[qb] ? rl : -1,
                         reinterpret_cast<char*>(p.part_o + prow0 * kHeadDim),
                         lane, p.counters != nullptr);
       if (half == 0 && rvalid[qb]) {
-        float* dst = p.part_ml + (prow0 + qrow[qb]) * 2;
+        float* dst = p.part_ml + (prow0 + rl) * 2;
         const uint64_t st = pack_split_stats(split_lse2(m_ref[qb], l_tot), ex);
         if (p.counters != nullptr) {
           store_coherent8(dst, st);
@@ -597,9 +594,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
       }
     }
   }
-  if (p.counters != nullptr) {
-    merge_if_last<kThreads>(p, s, g, mb, a, rows, r0, kRowsPerWG8, T, tid,
-                            pg_lds);
+  if (p.counters != nullptr && un.nsplit > 1) {
+    merge_if_last<kThreads>(p, un, rows, r0, kRowsPerWG8, tid, pg_lds);
   }
 }
 

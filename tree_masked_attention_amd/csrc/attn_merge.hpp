@@ -20,6 +20,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "split_plan.hpp"
 
 namespace tree_attn {
 
@@ -55,6 +56,16 @@ __device__ __forceinline__ bool merge_weights(float& m_run, float& l_run,
   return true;
 }
 
+// Where the partials of one row block's splits live: split k's row r of
+// the pair is row (slot0 + k * stride) * rows_per_wg + r - r0 of the
+// partial arrays (the unit slots of split_plan.hpp).
+struct PartSlots {
+  int slot0, stride, rows_per_wg, r0;
+  __device__ __forceinline__ size_t row(int k, int r) const {
+    return (size_t)(slot0 + k * stride) * rows_per_wg + (r - r0);
+  }
+};
+
 // One output element's running sum (an explicit fma, so that no compiler
 // contraction choice can make the two merge paths differ).
 __device__ __forceinline__ float merge_acc(float acc, float s_old, float w,
@@ -71,14 +82,12 @@ __device__ __forceinline__ float merge_lse(float m_run, float l_run) {
 }
 
 struct MergeParams {
-  const int32_t* prefix_lens;
-  const int32_t* tree_offsets;
   const _Float16* part_o;
   const float* part_ml;
   __bf16* out;
   float* lse;
-  int S, N, Hq, Hkv, G, splits, chunk, max_tokens;
-  int mblocks, rows_per_block;  // row blocks of the attention launch
+  int Hq, G;
+  SplitParams plan;  // the attention launch's units
 };
 
 constexpr int kMergeWaves = 4;
@@ -86,9 +95,9 @@ constexpr int kMergeRows = 8;    // rows per wave: 4 per lane half
 constexpr int kMergeSplits = 4;  // splits whose loads are issued together
 constexpr int kMergeRowsPerWG = kMergeWaves * kMergeRows;
 
-// Workgroups are laid out like the attention launch: (sequence, kv head,
-// row block), each row block cut into pieces of kMergeRowsPerWG rows, so
-// the sequence of every row is known from the workgroup id.  A wave merges
+// Workgroups follow the attention launch's units, each unit's rows cut
+// into pieces of kMergeRowsPerWG rows; the workgroups of a row block's
+// split-0 unit merge it (the others have nothing to do).  A wave merges
 // kMergeRows rows, each lane half one row at a time with four columns per
 // lane (8-byte loads, a whole 256-byte row per half-wave instruction); the
 // loads of kMergeSplits splits of all its rows are issued before any is
@@ -98,31 +107,29 @@ __global__ __launch_bounds__(kMergeWaves * 64) void attn_merge_kernel(
   constexpr int RL = kMergeRows / 2;  // rows per lane
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int half = lane >> 5, c4 = (lane & 31) * 4;
-  const int pieces = p.rows_per_block / kMergeRowsPerWG;
-  int L = blockIdx.x / pieces;
+  const int pieces = p.plan.rows_per_wg / kMergeRowsPerWG;
+  const int L = blockIdx.x / pieces;
   const int piece = blockIdx.x - L * pieces;
-  const int mb = L % p.mblocks;
-  L /= p.mblocks;
-  const int g = L % p.Hkv;
-  const int s = L / p.Hkv;
-  const int a = clampi(p.tree_offsets[s], 0, p.N);
-  const int b = clampi(p.tree_offsets[s + 1], a, p.N);
-  const int rows = p.G * (b - a);
-  const int r0 = mb * p.rows_per_block + piece * kMergeRowsPerWG +
-                 wave * kMergeRows;
+  if (L >= p.plan.parts) return;
+  Unit un = decode_unit(p.plan, L);
+  if (!un.valid || un.split != 0) return;
+  load_bounds(p.plan, un);
+  if (un.nsplit == 1) return;
+  const int rows = p.G * un.B;
+  const int rb = un.mb * p.plan.rows_per_wg;
+  const int r0 = rb + piece * kMergeRowsPerWG + wave * kMergeRows;
   if (r0 >= rows) return;
-  const int P = max(p.prefix_lens[s], 0);
-  const int T = min(P + (b - a), p.max_tokens);
-  const int nsplit = min(p.splits, (T + p.chunk - 1) / p.chunk);
-  const size_t NH = (size_t)p.N * p.Hq;
+  const int nsplit = un.nsplit;
+  const PartSlots slots{un.slot0, un.mblocks, p.plan.rows_per_wg, rb};
 
   size_t qrow[RL];
+  int rr[RL];
   float m_run[RL], l_run[RL];
   f32x4 acc[RL];
 #pragma unroll
   for (int k = 0; k < RL; ++k) {
-    const int r = min(r0 + 2 * k + half, rows - 1);
-    qrow[k] = (size_t)(a + r / p.G) * p.Hq + g * p.G + r % p.G;
+    rr[k] = min(r0 + 2 * k + half, rows - 1);
+    qrow[k] = (size_t)(un.a + rr[k] / p.G) * p.Hq + un.g * p.G + rr[k] % p.G;
     m_run[k] = -INFINITY;
     l_run[k] = 0.f;
     acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -135,7 +142,7 @@ __global__ __launch_bounds__(kMergeWaves * 64) void attn_merge_kernel(
 #pragma unroll
       for (int u = 0; u < kMergeSplits; ++u) {
         const int c = min(c0 + u, nsplit - 1);  // in range; unused if past
-        const size_t prow = (size_t)c * NH + qrow[k];
+        const size_t prow = slots.row(c, rr[k]);
         ml[k][u] = *reinterpret_cast<const f32x2*>(p.part_ml + prow * 2);
         oc[k][u] = *reinterpret_cast<const f16x4*>(p.part_o + prow * kHeadDim +
                                                    c4);
@@ -168,8 +175,9 @@ __global__ __launch_bounds__(kMergeWaves * 64) void attn_merge_kernel(
 }
 
 // Merges rows [r_lo, r_hi) of the (sequence, kv head g) pair whose tree
-// starts at node a, over its nsplit splits, with the NT threads of a
-// workgroup (head dim D, rows of D fp16 partials): thread t takes the
+// starts at node a, over its nsplit splits (partials at slots), with the
+// NT threads of a workgroup (head dim D, rows of D fp16 partials): thread
+// t takes the
 // 16-byte column chunk t % (D/8) of rows r_lo + t / (D/8) + k * NT / (D/8);
 // the loads of kMergeRowsPerThread rows and kMergeSplits splits are issued
 // before any is used.  kCoherent: the partials are read with
@@ -180,8 +188,8 @@ constexpr int kMergeRowsPerThread = 4;
 template <int NT, int D, bool kCoherent>
 __device__ __forceinline__ void merge_rows_wg(
     const _Float16* part_o, const float* part_ml, __bf16* out, float* lse,
-    size_t NH, int Hq, int G, int g, int a, int r_lo, int r_hi, int nsplit,
-    int tid) {
+    int Hq, int G, int g, int a, int r_lo, int r_hi, int nsplit,
+    const PartSlots& slots, int tid) {
   constexpr int CH = D / 8;                  // 16-byte chunks per row
   constexpr int RS = NT / CH;                // rows per pass of the group
   constexpr int RT = kMergeRowsPerThread;
@@ -191,10 +199,12 @@ __device__ __forceinline__ void merge_rows_wg(
   const int ch = tid % CH, rsub = tid / CH;
   for (int rb = r_lo; rb < r_hi; rb += RS * RT) {
     size_t qrow[RT];
+    int rr[RT];
     float m_run[RT], l_run[RT], acc[RT][8];
 #pragma unroll
     for (int k = 0; k < RT; ++k) {
       const int r = min(rb + rsub + k * RS, r_hi - 1);
+      rr[k] = r;
       qrow[k] = (size_t)(a + r / G) * Hq + g * G + r % G;
       m_run[k] = -INFINITY;
       l_run[k] = 0.f;
@@ -209,7 +219,7 @@ __device__ __forceinline__ void merge_rows_wg(
 #pragma unroll
         for (int u = 0; u < KS; ++u) {
           const int c = min(c0 + u, nsplit - 1);  // in range; unused if past
-          const size_t prow = (size_t)c * NH + qrow[k];
+          const size_t prow = slots.row(c, rr[k]);
           const _Float16* po = part_o + prow * D + ch * 8;
           if (kCoherent) {
             const uint64_t m2 = load_coherent8(part_ml + prow * 2);
@@ -267,8 +277,8 @@ __device__ __forceinline__ void merge_rows_wg(
 template <int NT, int D>
 __device__ __forceinline__ void merge_if_last_rows(
     unsigned* ctr, int nsplit, const _Float16* part_o, const float* part_ml,
-    __bf16* out, float* lse, size_t NH, int Hq, int G, int g, int a, int r_lo,
-    int r_hi, int tid, int* flag_lds) {
+    __bf16* out, float* lse, int Hq, int G, int g, int a, int r_lo,
+    int r_hi, const PartSlots& slots, int tid, int* flag_lds) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // own partials complete
   __syncthreads();
   if (tid == 0) {
@@ -279,8 +289,8 @@ __device__ __forceinline__ void merge_if_last_rows(
   __syncthreads();
   if (*flag_lds == 0) return;
   // issued after the barrier, i.e. after the count was seen complete
-  merge_rows_wg<NT, D, true>(part_o, part_ml, out, lse, NH, Hq, G, g, a,
-                             r_lo, r_hi, nsplit, tid);
+  merge_rows_wg<NT, D, true>(part_o, part_ml, out, lse, Hq, G, g, a, r_lo,
+                             r_hi, nsplit, slots, tid);
 }
 
 }  // namespace tree_attn

@@ -35,6 +35,9 @@ constexpr int kAbiVersion = 10;
 constexpr int kMaxDevices = 64;
 constexpr int kMaxSplits = 256;
 constexpr int kMinKeysPerSplit = 256;
+// launches of up to this many sequences balance their splits on the device
+// (one lane per sequence in split_plan.hpp)
+constexpr int kBalancedMaxSeqs = 64;
 // keys per workgroup from which the 256-row kernel (8 waves of 32 rows) is
 // used; shorter key ranges take the 128-row kernel (8 waves: 4 row groups
 // x 2 key halves).  Both kernels run 8 waves per workgroup.
@@ -100,6 +103,7 @@ struct Plan {
   int chunk = 0;     // keys per split (multiple of the 64-key tile)
   int units = 0;     // sequences * kv heads * splits * row blocks
   int blocks = 0;    // sequences * kv heads * row blocks (merge counters)
+  int max_chunk = 0; // longest split whose page ids fit the kernels' LDS
   size_t part_ml_off = 0;
   size_t ws_bytes = 0;
 };
@@ -191,12 +195,14 @@ int make_plan(int S, int N, int Hq, int Hkv, int max_prefix_len,
   }
   pl.splits = (int)splits;
   pl.chunk = (int)chunk;
+  pl.max_chunk = (int)max_chunk;
   const long long units = units0 * splits;
   if (units > (1LL << 30)) return TREE_ATTN_ERR_UNSUPPORTED;
   pl.units = (int)units;
   pl.blocks = (int)units0;
   if (splits > 1) {
-    pl.ws_bytes = partials_bytes((size_t)N * Hq * splits, kHeadDim,
+    // one slot of partial rows per unit (split_plan.hpp)
+    pl.ws_bytes = partials_bytes((size_t)pl.units * pl.rows, kHeadDim,
                                  &pl.part_ml_off);
   }
   *out = pl;
@@ -409,6 +415,36 @@ int check_verify_sizes(int S, int N, int Hq, int Hkv, int head_dim,
   return TREE_ATTN_OK;
 }
 
+// The device-side unit plan of a launch (split_plan.hpp).  Launches that
+// split the key range and hold 2 .. 64 sequences are balanced on the
+// device from the actual sequence lengths; one sequence, forced splits,
+// unsplit launches and larger batches use the host's uniform plan.
+SplitParams split_params(const Plan& pl, const int32_t* prefix_lens,
+                         const int32_t* tree_offsets, int S, int N, int Hkv,
+                         int G, int max_tokens, int max_prefix_len,
+                         int max_nodes, int req_splits) {
+  SplitParams q;
+  q.prefix_lens = prefix_lens;
+  q.tree_offsets = tree_offsets;
+  q.S = S;
+  q.N = N;
+  q.Hkv = Hkv;
+  q.G = G;
+  q.rows_per_wg = pl.rows;
+  q.max_tokens = (int)std::min<long long>(
+      max_tokens, (long long)max_prefix_len + max_nodes);
+  q.max_nodes = max_nodes;
+  q.parts = pl.units;
+  q.chunk_max = pl.max_chunk;
+  q.chunk_min = std::min(kMinKeysPerSplit, pl.max_chunk);
+  const bool balanced = req_splits <= 0 && pl.splits > 1 && S > 1 &&
+                        S <= kBalancedMaxSeqs;
+  q.uniform_chunk = balanced ? 0 : pl.chunk;
+  q.uniform_splits = pl.splits;
+  q.uniform_mblocks = pl.mblocks;
+  return q;
+}
+
 // Phases of a verify call: the split-KV + tree pass, then the LSE merge.
 enum { kPhaseAttend = 1, kPhaseMerge = 2 };
 
@@ -477,46 +513,47 @@ int run_verify(int phases, const void* q, const void* k_cache, const void* v_cac
   fp.Hq = num_q_heads;
   fp.Hkv = num_kv_heads;
   fp.G = num_q_heads / num_kv_heads;
-  fp.mblocks = pl.mblocks;
-  fp.splits = pl.splits;
-  fp.chunk = pl.chunk;
-  fp.units = pl.units;
   fp.per_xcd = (pl.units + 7) / 8;
+  fp.plan = split_params(pl, prefix_lens, tree_offsets, num_seqs, total_nodes,
+                         num_kv_heads, fp.G, fp.max_tokens, max_prefix_len,
+                         max_nodes, num_splits);
   fp.scale_log2 = scale * kLog2e;
 
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const unsigned grid = 8u * (unsigned)fp.per_xcd;
   if (phases & kPhaseAttend) {
+    // balanced plans run the instantiations that carry the device plan
+    const bool bal = fp.plan.uniform_chunk == 0;
     if (pl.rows == kRowsPerWG8) {
-      st = launch(&attn_fwd256_kernel, dim3(grid), dim3(512), hs, fp);
+      st = bal ? launch(&attn_fwd256_kernel<true>, dim3(grid), dim3(512), hs,
+                        fp)
+               : launch(&attn_fwd256_kernel<false>, dim3(grid), dim3(512), hs,
+                        fp);
     } else if (pl.rows == kRowsPerWG128) {
-      st = launch(&attn_fwdh_kernel<8>, dim3(grid), dim3(512), hs, fp);
+      st = bal ? launch(&attn_fwdh_kernel<8, true>, dim3(grid), dim3(512), hs,
+                        fp)
+               : launch(&attn_fwdh_kernel<8, false>, dim3(grid), dim3(512),
+                        hs, fp);
     } else {
-      st = launch(&attn_fwdh_kernel<4>, dim3(grid), dim3(256), hs, fp);
+      st = bal ? launch(&attn_fwdh_kernel<4, true>, dim3(grid), dim3(256), hs,
+                        fp)
+               : launch(&attn_fwdh_kernel<4, false>, dim3(grid), dim3(256),
+                        hs, fp);
     }
     if (st != TREE_ATTN_OK) return st;
   }
 
   if ((phases & kPhaseMerge) && pl.splits > 1 && !fused) {
     MergeParams mp;
-    mp.prefix_lens = prefix_lens;
-    mp.tree_offsets = tree_offsets;
     mp.part_o = fp.part_o;
     mp.part_ml = fp.part_ml;
     mp.out = fp.out;
     mp.lse = lse;
-    mp.S = num_seqs;
-    mp.N = total_nodes;
     mp.Hq = num_q_heads;
-    mp.Hkv = num_kv_heads;
     mp.G = fp.G;
-    mp.splits = pl.splits;
-    mp.chunk = pl.chunk;
-    mp.max_tokens = fp.max_tokens;
-    mp.mblocks = pl.mblocks;
-    mp.rows_per_block = pl.rows;
-    const long long mgrid = (long long)num_seqs * num_kv_heads * pl.mblocks *
-                            (mp.rows_per_block / kMergeRowsPerWG);
+    mp.plan = fp.plan;
+    const long long mgrid =
+        (long long)pl.units * (pl.rows / kMergeRowsPerWG);
     st = launch(&attn_merge_kernel, dim3((unsigned)mgrid),
                 dim3(kMergeWaves * 64), hs, mp);
     if (st != TREE_ATTN_OK) return st;
