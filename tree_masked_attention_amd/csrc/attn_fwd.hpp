@@ -149,6 +149,39 @@ __device__ __forceinline__ void store_rows_staged(const u32x2 (&pk)[16],
   }
 }
 
+// Same for one half of each row: the wave's 32 rows of 64 two-byte values
+// (pk[c] = columns 8c + 4 half .. +3 of the half), staged at stg (4 KB)
+// and stored as 128-byte half rows at byte offset 128 * hh of each 256-byte
+// row, 8 half rows per instruction.
+__device__ __forceinline__ void store_half_rows_staged(const u32x2 (&pk)[8],
+                                                       unsigned stg, int row,
+                                                       int hh, char* base,
+                                                       int lane,
+                                                       bool coherent = false) {
+  const int col = lane & 31, half = lane >> 5;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    lds_write8(stg + col * 128 + ((c ^ (col & 7)) << 4) + half * 8, pk[c]);
+  }
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int rr = 8 * k + (lane >> 3), ch = lane & 7;
+    const u32x4 v = *(const lds_u32x4*)(size_t)(stg + rr * 128 +
+                                                ((ch ^ (rr & 7)) << 4));
+    const int dr = __shfl(row, rr);
+    if (dr >= 0) {
+      char* dst = base + (size_t)dr * 256 + hh * 128 + ch * 16;
+      if (coherent) {
+        asm volatile("global_store_dwordx4 %0, %1, off sc1"
+                     :: "v"(dst), "v"(v) : "memory");
+      } else {
+        *reinterpret_cast<u32x4*>(dst) = v;
+      }
+    }
+  }
+}
+
 // Transposing LDS read (see the file comment).
 __device__ __forceinline__ s16x4 lds_read_tr(unsigned addr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(size_t)addr);

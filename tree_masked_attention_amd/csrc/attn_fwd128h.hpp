@@ -25,8 +25,9 @@ namespace tree_attn {
 
 constexpr int kRowsPerWG128 = 128;
 constexpr int kRowsPerWG64 = 64;
-// ring offset of the epilogue's row staging (past the halves' exchange)
-constexpr int kEpilogueStage = 68 * 1024;
+// ring offset of the epilogue's row staging (past the halves' exchange:
+// 8 KB of O, 512 B of statistics and 128 B of row maxima per wave)
+constexpr int kEpilogueStage = 72 * 1024;
 
 template <int NW, bool kBalanced>
 __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
@@ -67,9 +68,10 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
 
   // Prologue, two rounds of memory latency before the first tile's scores:
   // (1) the split's page-table entries go to LDS by DMA while the tree
-  // bounds load; (2) once the entries are in, Q (staged in ring stage 3,
-  // which tile 3 only overwrites after every wave has read it), the
-  // ancestor-mask rows and tiles 0-2 are all in flight together.
+  // bounds load, then Q (staged in ring stage 3, which tile 3 only
+  // overwrites after every wave has read it) and the ancestor-mask rows
+  // join them in flight; (2) once all of these are in, tiles 0-2 are
+  // issued and the first scores wait for tile 0 alone.
   const int kbeg = split * un.chunk;
   const int lp0 = kbeg >> p.log2_page;
   {
@@ -111,8 +113,6 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
   bf16x8 qf[8];  // Q^T fragments (B operand): d = kc*16 + half*8 + 0..7,
                  // read from LDS once the prologue DMA has landed
 
-  wait_vmcnt<0>();
-  __syncthreads();  // page slice visible
   // Q rows r0 .. r0+kRows-1 (rows past the last one repeat it):
   // instruction i moves rows 4i .. 4i+3, chunk-swizzled like K; rows 0-63
   // go to the K half of stage 3, rows 64-127 to its V half
@@ -135,6 +135,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
       if (i0 + lane < nd) dma4(msrc + 4 * (i0 + lane), mk_base + 4 * i0);
     }
   }
+  wait_vmcnt<0>();
+  __syncthreads();  // page slice, Q and mask rows visible
 
   // ---- LDS operand addresses of this wave's key half (stage 0)
   unsigned k_off[8];
@@ -440,105 +442,131 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
     if (j + 3 < n) step(j + 3, SB, SA);
   }
 
-  // ---- combine the two key halves: the upper-half wave of each row group
-  // leaves (max, row sum, O) in the ring, the lower-half wave merges them
+  // ---- combine the two key halves.  Wave (rg, kh) finishes head-dim half
+  // kh (O^T blocks 2 kh, 2 kh + 1) of its 32 rows: it hands the other two
+  // blocks and its (max, row sum) to the partner wave (rg, 1 - kh) through
+  // LDS and takes the partner's share of its own two, so both waves of a
+  // row group do half of the epilogue.
   float l_tot = l_run + other_half(l_run);
+  // (selected by a wave-uniform branch: indexing o[] by kh would put the
+  // array in scratch memory)
+  f32x16 o_own[2], o_give[2];
+  if (kh == 0) {
+    o_own[0] = o[0];
+    o_own[1] = o[1];
+    o_give[0] = o[2];
+    o_give[1] = o[3];
+  } else {
+    o_own[0] = o[2];
+    o_own[1] = o[3];
+    o_give[0] = o[0];
+    o_give[1] = o[1];
+  }
   __syncthreads();  // every wave is done with the ring
-  float* xo = reinterpret_cast<float*>(ring) + rg * (64 * 64);
-  float* xml = reinterpret_cast<float*>(ring) + 4 * 64 * 64 + rg * 128;
-  if (kh == 1) {
+  {
+    float* xo_out = reinterpret_cast<float*>(ring) + wave * (8 * 64 * 4);
+    float* xml_out = reinterpret_cast<float*>(ring) + NW * (8 * 64 * 4) +
+                     wave * 128;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
+    for (int b = 0; b < 2; ++b) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        *reinterpret_cast<f32x4*>(xo + ((db * 4 + g4) * 64 + lane) * 4) =
-            f32x4{o[db][g4 * 4 + 0], o[db][g4 * 4 + 1], o[db][g4 * 4 + 2],
-                  o[db][g4 * 4 + 3]};
+        *reinterpret_cast<f32x4*>(xo_out + ((b * 4 + g4) * 64 + lane) * 4) =
+            f32x4{o_give[b][g4 * 4 + 0], o_give[b][g4 * 4 + 1],
+                  o_give[b][g4 * 4 + 2], o_give[b][g4 * 4 + 3]};
       }
     }
-    xml[lane] = m_ref;
-    xml[64 + lane] = l_tot;
+    xml_out[lane] = m_ref;
+    xml_out[64 + lane] = l_tot;
   }
   __syncthreads();
-  if (kh == 0) {
-    const float m1 = xml[lane], l1 = xml[64 + lane];
-    const float mx = __builtin_elementwise_maximum(m_ref, m1);
-    const float a0 = mx == -INFINITY ? 0.f : fast_exp2(m_ref - mx);
-    const float a1 = mx == -INFINITY ? 0.f : fast_exp2(m1 - mx);
+  const int partner = wave ^ (NW / 2);
+  const float* xo_in = reinterpret_cast<const float*>(ring) +
+                       partner * (8 * 64 * 4);
+  const float* xml_in = reinterpret_cast<const float*>(ring) +
+                        NW * (8 * 64 * 4) + partner * 128;
+  // both waves form the combined statistics from the same operands in the
+  // same order (key half 0 first), so they agree bit for bit
+  const float m_p = xml_in[lane], l_p = xml_in[64 + lane];
+  const float m0 = kh == 0 ? m_ref : m_p, m1 = kh == 0 ? m_p : m_ref;
+  const float l0 = kh == 0 ? l_tot : l_p, l1 = kh == 0 ? l_p : l_tot;
+  const float mx = __builtin_elementwise_maximum(m0, m1);
+  const float a0 = mx == -INFINITY ? 0.f : fast_exp2(m0 - mx);
+  const float a1 = mx == -INFINITY ? 0.f : fast_exp2(m1 - mx);
+  const float a_own = kh == 0 ? a0 : a1, a_p = kh == 0 ? a1 : a0;
+  f32x16 oc[2];
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
+  for (int b = 0; b < 2; ++b) {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x4 u =
-            *reinterpret_cast<const f32x4*>(xo + ((db * 4 + g4) * 64 + lane) * 4);
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x4 u =
+          *reinterpret_cast<const f32x4*>(xo_in + ((b * 4 + g4) * 64 + lane) * 4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          o[db][g4 * 4 + e] = o[db][g4 * 4 + e] * a0 + u[e] * a1;
-        }
+      for (int e = 0; e < 4; ++e) {
+        oc[b][g4 * 4 + e] = o_own[b][g4 * 4 + e] * a_own + u[e] * a_p;
       }
     }
-    l_tot = l_tot * a0 + l1 * a1;
-    m_ref = mx;
+  }
+  l_tot = l0 * a0 + l1 * a1;
+  m_ref = mx;
 
-    // ---- epilogue (lower-half waves): the normalised output in bf16 (one
-    // split) or, for a split's partial, in fp16 scaled by 2^-ex (the row's
-    // scale exponent), staged through LDS past the exchange area so that
-    // the stores write whole rows
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    int ex = 0;
-    if (un.nsplit > 1) {
-      float amax = 0.f;
+  // ---- epilogue: this wave's half of each of its rows, the normalised
+  // output in bf16 (one split) or, for a split's partial, in fp16 scaled by
+  // 2^-ex (the row's scale exponent, from the whole row's largest value:
+  // the two waves exchange their halves' maxima), staged through LDS past
+  // the exchange area so that the stores write whole half rows
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const unsigned stg = ring_base + kEpilogueStage + wave * 4096;
+  u32x2 pk[8];
+  if (un.nsplit == 1) {
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
+    for (int c = 0; c < 8; ++c) {
+      bf16x4 v4;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          amax = __builtin_elementwise_maximum(amax, __builtin_fabsf(o[db][e]));
-        }
-      }
-      ex = f16_row_exp(__builtin_elementwise_maximum(amax, other_half(amax)) *
-                       inv);
+      for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(oc[c >> 2][(c & 3) * 4 + e] * inv);
+      pk[c] = __builtin_bit_cast(u32x2, v4);
     }
-    u32x2 pk[16];
+    store_half_rows_staged(pk, stg, rvalid ? (int)qrow : -1, kh,
+                           reinterpret_cast<char*>(p.out), lane);
+    if (kh == 0 && half == 0 && rvalid) {
+      p.lse[qrow] = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+  } else {
+    float amax = 0.f;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
+    for (int b = 0; b < 2; ++b) {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        if (un.nsplit == 1) {
-          bf16x4 v4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(o[db][g4 * 4 + e] * inv);
-          pk[db * 4 + g4] = __builtin_bit_cast(u32x2, v4);
-        } else {
-          f16x4 v4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            v4[e] = to_f16_sat(ldexp2(o[db][g4 * 4 + e] * inv, -ex));
-          }
-          pk[db * 4 + g4] = __builtin_bit_cast(u32x2, v4);
-        }
+      for (int e = 0; e < 16; ++e) {
+        amax = __builtin_elementwise_maximum(amax, __builtin_fabsf(oc[b][e]));
       }
     }
-    const unsigned stg = ring_base + kEpilogueStage + rg * 8192;
-    if (un.nsplit == 1) {
-      store_rows_staged(pk, stg, rvalid ? (int)qrow : -1,
-                        reinterpret_cast<char*>(p.out), lane);
-      if (half == 0 && rvalid) {
-        p.lse[qrow] = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
+    amax = __builtin_elementwise_maximum(amax, other_half(amax));
+    float* xam = reinterpret_cast<float*>(ring) + NW * (8 * 64 * 4 + 128);
+    if (half == 0) xam[wave * 32 + col] = amax;
+    __syncthreads();
+    amax = __builtin_elementwise_maximum(amax, xam[partner * 32 + col]);
+    const int ex = f16_row_exp(amax * inv);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      f16x4 v4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v4[e] = to_f16_sat(ldexp2(oc[c >> 2][(c & 3) * 4 + e] * inv, -ex));
       }
-    } else {
-      // the unit's partial slot: its rows in row-block order
-      const size_t prow0 = (size_t)L * kRows;
-      store_rows_staged(pk, stg, rvalid ? r - r0 : -1,
-                        reinterpret_cast<char*>(p.part_o + prow0 * kHeadDim),
-                        lane, p.counters != nullptr);
-      if (half == 0 && rvalid) {
-        float* dst = p.part_ml + (prow0 + (r - r0)) * 2;
-        const uint64_t st = pack_split_stats(split_lse2(m_ref, l_tot), ex);
-        if (p.counters != nullptr) {
-          store_coherent8(dst, st);
-        } else {
-          *reinterpret_cast<uint64_t*>(dst) = st;
-        }
+      pk[c] = __builtin_bit_cast(u32x2, v4);
+    }
+    // the unit's partial slot: its rows in row-block order
+    const size_t prow0 = (size_t)L * kRows;
+    store_half_rows_staged(pk, stg, rvalid ? r - r0 : -1, kh,
+                           reinterpret_cast<char*>(p.part_o + prow0 * kHeadDim),
+                           lane, p.counters != nullptr);
+    if (kh == 0 && half == 0 && rvalid) {
+      float* dst = p.part_ml + (prow0 + (r - r0)) * 2;
+      const uint64_t st = pack_split_stats(split_lse2(m_ref, l_tot), ex);
+      if (p.counters != nullptr) {
+        store_coherent8(dst, st);
+      } else {
+        *reinterpret_cast<uint64_t*>(dst) = st;
       }
     }
   }
