@@ -853,9 +853,15 @@ class VerifyBench:
         self.f_mask = api._lib.tree_attn_build_mask
         self.f_ver = (api._lib.tree_attn_verify_ex if self.variant
                       else api._lib.tree_attn_verify)
-        if self.variant:
+        if self.variant and d != 128:
             self.plan = {"kernel": "attn_var_kernel (+ attn_var_merge_kernel)",
                          "rows": 128, "workspace_bytes": self.ws_bytes}
+        elif self.variant:
+            # fp8 K/V, head dim 128: the tuned kernels' 128- and 64-row shapes
+            self.plan = api.describe_plan_ex(kvd, S, N, Hq, wl.num_kv_heads,
+                                             d, wl.max_prefix_len,
+                                             wl.max_nodes, wl.page_size,
+                                             splits)
         else:
             self.plan = api.describe_plan(S, N, Hq, wl.num_kv_heads, d,
                                           wl.max_prefix_len, wl.max_nodes,
@@ -896,7 +902,7 @@ class VerifyBench:
         return n
 
     def kernel_name(self):
-        if self.variant:
+        if "kernel" in self.plan:
             return "attn_var_kernel"
         return {256: "attn_fwd256_kernel", 128: "attn_fwdh_kernel<8>",
                 64: "attn_fwdh_kernel<4>"}[self.plan["rows"]]

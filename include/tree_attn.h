@@ -122,9 +122,10 @@ size_t tree_attn_workspace_size(int32_t num_seqs, int32_t total_nodes,
  * tree_attn_describe_plan - the launch tree_attn_verify would make for
  * these sizes, for tests and benchmarks.  Arguments as for
  * tree_attn_workspace_size; info is a host array of 5 int32 that receives
- * { waves per workgroup (8), query rows per workgroup (128 or 256),
- *   splits of the key range, keys per split, workgroups launched }.  Returns TREE_ATTN_OK, or the status
- * tree_attn_verify would return for these sizes (info untouched).
+ * { waves per workgroup (4 or 8), query rows per workgroup (64, 128 or
+ *   256), splits of the key range, keys per split, workgroups launched }.
+ * Returns TREE_ATTN_OK, or the status tree_attn_verify would return for
+ * these sizes (info untouched).
  */
 int tree_attn_describe_plan(int32_t num_seqs, int32_t total_nodes,
                             int32_t num_q_heads, int32_t num_kv_heads,
@@ -549,11 +550,15 @@ int tree_attn_gdn_commit(const void* k, const float* u, const float* g,
  *                 Ignored for bf16.
  *   head_dim      64 or 128 (q, out: [total_nodes][num_q_heads][head_dim])
  * With bf16 and head_dim 128 this is exactly tree_attn_verify (the same
- * kernels).  The other combinations run a separate kernel (128 query rows
- * per workgroup, fp8 converted to bf16 exactly on its way into LDS, bf16
- * matrix cores, fp32 accumulation, split partials normalised by their
- * own row sum and stored in fp16 with a power-of-two scale per row, as
- * for tree_attn_verify); its workspace size comes from
+ * kernels).  FP8 with head_dim 128 runs the same kernels' 128- and 64-row
+ * shapes on FP8 tiles: the DMA ring moves the codes, and each wave
+ * converts its operands to bf16 (exactly: every E4M3 value is a bf16
+ * value) as it reads them from LDS; the K scale folds into the softmax
+ * scale and the V scale into the output.  Head dim 64 runs a separate
+ * kernel (128 query rows per workgroup, fp8 converted to bf16 on its way
+ * into LDS, bf16 matrix cores, fp32 accumulation, split partials
+ * normalised by their own row sum and stored in fp16 with a power-of-two
+ * scale per row, as for tree_attn_verify).  Workspace sizes come from
  * tree_attn_workspace_size_ex.
  *
  * The key range is cut into at most 256 splits of at most 1039 pages each
@@ -586,6 +591,20 @@ size_t tree_attn_workspace_size_ex(int32_t kv_dtype, int32_t num_seqs,
                                    int32_t num_kv_heads, int32_t head_dim,
                                    int32_t max_prefix_len, int32_t max_nodes,
                                    int32_t page_size, int32_t num_splits);
+
+/*
+ * tree_attn_describe_plan_ex - tree_attn_describe_plan for the launches of
+ * tree_attn_verify_ex (kv_dtype and head_dim as there).  Head dim 128
+ * (bf16 or FP8) runs the tuned kernels (FP8: 64 or 128 query rows per
+ * workgroup); head dim 64 the 4-wave, 128-row kernel (workgroups: its
+ * attention launch's).
+ */
+int tree_attn_describe_plan_ex(int32_t kv_dtype, int32_t num_seqs,
+                               int32_t total_nodes, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim,
+                               int32_t max_prefix_len, int32_t max_nodes,
+                               int32_t page_size, int32_t num_splits,
+                               int32_t* info);
 
 #ifdef __cplusplus
 }

@@ -181,6 +181,76 @@ def test_workspace_reuse_across_formats():
         assert eo <= OUT_ATOL and el <= LSE_RTOL
 
 
+# FP8 K/V with head dim 128 runs the tuned kernels (128 or 64 query rows
+# per workgroup, fp8 tiles converted to bf16 as the matrix cores read
+# them).  Shapes that take the 64-row kernel (pairs of at most 128 rows,
+# enough of them to fill the CUs), the device-balanced split plan (2 to 64
+# sequences with splits), and the slow DMA path (pages of 4 keys).
+def _fp8(name, seed, **kw):
+    kw.setdefault("num_q_heads", 32)
+    kw.setdefault("num_kv_heads", 4)
+    return make_workload(seed, name=name, kv_format="e4m3", **kw)
+
+
+FP8_TUNED_CASES = {
+    "fp8-r64-ragged": (lambda: _fp8("fp8-r64", 190, prefix_range=(0, 900),
+                                    num_seqs=32,
+                                    tree_sizes=[1 + (7 * s) % 16
+                                                for s in range(32)]), 64),
+    "fp8-r64-page4": (lambda: _fp8("fp8-r64-p4", 191,
+                                   prefix_range=(100, 700), num_seqs=32,
+                                   tree_sizes=[16], page_size=4), 64),
+    "fp8-balanced": (lambda: _fp8("fp8-bal", 192,
+                                  prefix_lens=[300, 4000, 9000],
+                                  tree_sizes=[40, 9, 70], num_q_heads=8,
+                                  num_kv_heads=2), 128),
+    "fp8-page8-chain": (lambda: _fp8("fp8-p8", 193, prefix_lens=[2500],
+                                     tree_sizes=[100], page_size=8,
+                                     num_q_heads=8, num_kv_heads=2,
+                                     tree_rules="chain"), 128),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FP8_TUNED_CASES))
+def test_fp8_tuned_parity(name):
+    import tree_masked_attention_amd.api as api
+    make, rows = FP8_TUNED_CASES[name]
+    wl = make()
+    plan = api.describe_plan_ex(api.KV_FP8_E4M3, wl.num_seqs,
+                                wl.total_nodes, wl.num_q_heads,
+                                wl.num_kv_heads, 128, wl.max_prefix_len,
+                                wl.max_nodes, wl.page_size, 0)
+    say(f"[gpu] fp8 tuned {name}: plan {plan}")
+    assert plan["rows"] == rows
+    if name == "fp8-balanced":
+        assert plan["splits"] > 1  # 3 sequences: the device-balanced plan
+    check(wl, name)
+    check(wl, f"{name}, 3 splits", num_splits=3)
+
+
+@pytest.mark.parametrize("splits", [2, 5, 64])
+def test_fp8_large_v_scale_splits(splits):
+    # v_scale times 2^20: decoded values reach about 448 * 2^13, far past
+    # fp16's range; split partials keep them through their per-row
+    # power-of-two scale
+    wl = _case("fp8-bigv", 194, "e4m3", 128, prefix_lens=[3000, 700],
+               tree_sizes=[30, 64])
+    wl.v_scale = (wl.v_scale * np.float32(2.0 ** 20)).astype(np.float32)
+    from oracle.tree_oracle import widen_e4m3
+    assert float(np.nanmax(np.abs(widen_e4m3(wl.v_cache))) *
+                 wl.v_scale.max()) > 1e6
+    say(f"[gpu] fp8 large v_scale, splits {splits}")
+    out, lse = run_ex(wl, splits)
+    ref_o, ref_l = oracle.workload_attention(wl)
+    sel = ~np.isnan(ref_l)
+    assert np.isfinite(out).all()
+    rel = np.abs(out - ref_o)[sel].max() / np.abs(ref_o[sel]).max()
+    el = (np.abs(lse - ref_l) / np.maximum(np.abs(ref_l), 1))[sel].max()
+    say(f"  max|dout| / max|out| {rel:.2e}, max rel dlse {el:.2e}")
+    # the bar relative to the output's scale (2e-2 of unit-scale outputs)
+    assert rel <= OUT_ATOL / 4 and el <= LSE_RTOL
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_fp8_decode_exact_through_the_path(d):
     # One node per sequence, no prefix: the node's only key is itself, its

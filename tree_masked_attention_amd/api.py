@@ -86,6 +86,8 @@ _lib.tree_attn_verify_ex.argtypes = (
      _i, _i, _i, ctypes.c_float, _i, _p, _p, _p, ctypes.c_size_t, _p])
 _lib.tree_attn_workspace_size_ex.restype = ctypes.c_size_t
 _lib.tree_attn_workspace_size_ex.argtypes = [_i] * 10
+_lib.tree_attn_describe_plan_ex.restype = ctypes.c_int
+_lib.tree_attn_describe_plan_ex.argtypes = [_i] * 10 + [_p]
 
 KV_BF16, KV_FP8_E4M3 = 0, 1
 
@@ -97,7 +99,8 @@ EXPORTED = ("tree_attn_status_string", "tree_attn_abi_version",
             "tree_attn_accept", "tree_attn_commit_kv",
             "tree_attn_accept_commit", "tree_attn_build_tree",
             "tree_attn_gdn_verify", "tree_attn_gdn_commit",
-            "tree_attn_verify_ex", "tree_attn_workspace_size_ex")
+            "tree_attn_verify_ex", "tree_attn_workspace_size_ex",
+            "tree_attn_describe_plan_ex")
 GDN_MAX_NODES = 128
 
 
@@ -223,6 +226,22 @@ def describe_plan(num_seqs: int, total_nodes: int, num_q_heads: int,
         max_prefix_len, max_nodes, page_size, num_splits,
         ctypes.cast(info, ctypes.c_void_p))
     _raise(code, "tree_attn_describe_plan")
+    return {"waves": info[0], "rows": info[1], "splits": info[2],
+            "chunk": info[3], "workgroups": info[4]}
+
+
+def describe_plan_ex(kv_dtype: int, num_seqs: int, total_nodes: int,
+                     num_q_heads: int, num_kv_heads: int, head_dim: int,
+                     max_prefix_len: int, max_nodes: int, page_size: int = 16,
+                     num_splits: int = 0) -> dict:
+    """The launch verify_ex() makes for these sizes (same keys as
+    describe_plan)."""
+    info = (ctypes.c_int32 * 5)()
+    code = _lib.tree_attn_describe_plan_ex(
+        kv_dtype, num_seqs, total_nodes, num_q_heads, num_kv_heads, head_dim,
+        max_prefix_len, max_nodes, page_size, num_splits,
+        ctypes.cast(info, ctypes.c_void_p))
+    _raise(code, "tree_attn_describe_plan_ex")
     return {"waves": info[0], "rows": info[1], "splits": info[2],
             "chunk": info[3], "workgroups": info[4]}
 

@@ -74,6 +74,8 @@ struct FwdParams {
   float* lse;
   _Float16* part_o;  // [units][rows per workgroup][128] partial outputs
   float* part_ml;    // [units][rows per workgroup][2] split statistics
+  const float* k_scale;  // fp8 K/V: [Hkv] scale of the cached codes, or
+  const float* v_scale;  // null (1); unused for bf16
   unsigned* counters;  // one arrival count per (sequence, kv head, row
                        // block), or null: the merge kernel merges
   int max_pps, num_pages, log2_page, W;
@@ -185,6 +187,30 @@ __device__ __forceinline__ void store_half_rows_staged(const u32x2 (&pk)[8],
 // Transposing LDS read (see the file comment).
 __device__ __forceinline__ s16x4 lds_read_tr(unsigned addr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(size_t)addr);
+}
+
+__device__ __forceinline__ u32x2 lds_read8(unsigned addr) {
+  return *(const lds_u32x2*)(size_t)addr;
+}
+
+// Transposing LDS read of bytes (ds_read_b64_tr_b8): in each group of 16
+// lanes, lanes 2r and 2r+1 address bytes 0-7 and 8-15 of row r (r = 0..7)
+// and lane i of the group receives byte i of rows 0..7, in row order.
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+__device__ __forceinline__ u32x2 lds_read_tr8(unsigned addr) {
+  return __builtin_bit_cast(
+      u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(size_t)addr));
+}
+
+// Eight E4M3 codes (byte i of w = element i) -> eight bf16, exactly.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(u32x2 w) {
+  u32x4 r;
+  r[0] = e4m3x2_to_bf16x2<false>(w[0]);
+  r[1] = e4m3x2_to_bf16x2<true>(w[0]);
+  r[2] = e4m3x2_to_bf16x2<false>(w[1]);
+  r[3] = e4m3x2_to_bf16x2<true>(w[1]);
+  return __builtin_bit_cast(bf16x8, r);
 }
 
 // 16 bytes per lane from global memory to LDS at lds_base + 16 * lane.

@@ -29,14 +29,18 @@ constexpr int kRowsPerWG64 = 64;
 // 8 KB of O, 512 B of statistics and 128 B of row maxima per wave)
 constexpr int kEpilogueStage = 72 * 1024;
 
-template <int NW, bool kBalanced>
+template <int NW, bool kBalanced, bool kFp8>
 __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
   static_assert(NW == 8 || NW == 4, "shape");
   constexpr int kRows = 16 * NW;         // query rows per workgroup
   constexpr int kThreads = NW * 64;
-  constexpr int kOpsPerMat = 16 / NW;    // 1-KB DMA ops per wave per matrix
+  constexpr int kEB = kFp8 ? 1 : 2;      // bytes per cached element
+  constexpr int kRowB = kHeadDim * kEB;  // bytes per cached (token, head)
+  // 1-KB DMA ops per wave per matrix: each moves 4 bf16 or 8 fp8 rows
+  constexpr int kOpsPerMat = (kFp8 ? 8 : 16) / NW;
   constexpr int kOps = 2 * kOpsPerMat;
-  constexpr int kDmaRows = 4 * kOpsPerMat;  // tile rows a wave moves
+  constexpr int kRowsPerOp = 1024 / kRowB;
+  constexpr int kDmaRows = kRowsPerOp * kOpsPerMat;  // tile rows a wave moves
   constexpr int kLog2DmaRows = NW == 8 ? 3 : 4;
   static_assert((1 << kLog2DmaRows) == kDmaRows, "shape");
   __shared__ __align__(1024) unsigned char ring[2 * kVOff];
@@ -64,7 +68,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
       (unsigned)(size_t)(__attribute__((address_space(3))) int*)pg_lds;
   const unsigned mk_base =
       (unsigned)(size_t)(__attribute__((address_space(3))) uint64_t*)mk_lds;
-  const int lrow = lane >> 4, lchunk = lane & 15;
+  const int lrow = lane >> 4, lchunk = lane & 15;  // Q rows, 16-B chunks
+  // a lane's row and 16-byte chunk within one K/V DMA op
+  const int drow = kFp8 ? lane >> 3 : lrow, dchunk = kFp8 ? lane & 7 : lchunk;
 
   // Prologue, two rounds of memory latency before the first tile's scores:
   // (1) the split's page-table entries go to LDS by DMA while the tree
@@ -142,34 +148,64 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
   unsigned k_off[8];
 #pragma unroll
   for (int kc = 0; kc < 8; ++kc) {
-    k_off[kc] = ring_base + (kh * 32 + col) * 256 +
-                (((2 * kc + half) ^ (col & 15)) << 4);
+    if constexpr (kFp8) {
+      // fp8 rows of 128 B, 16-byte chunk c stored at c ^ ((row >> 1) & 7);
+      // the lane's 8 values d = kc*16 + half*8 .. +7 are half of chunk kc
+      const int row = kh * 32 + col;
+      k_off[kc] = ring_base + row * 128 + ((kc ^ ((row >> 1) & 7)) << 4) +
+                  half * 8;
+    } else {
+      k_off[kc] = ring_base + (kh * 32 + col) * 256 +
+                  (((2 * kc + half) ^ (col & 15)) << 4);
+    }
   }
   const int y = (lane & 15) >> 2;
   const int x = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
   unsigned v_off[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
-    v_off[db] = ring_base + kVOff + (kh * 32 + 4 * half + y) * 256 +
-                ((4 * (db ^ y) + x) << 4) + 8 * (lane & 1);
+    if constexpr (kFp8) {
+      // ds_read_b64_tr_b8: in each group of 16 lanes, lanes 2r and 2r+1
+      // name bytes 0-7 and 8-15 of "row" r (r = 0..7), and lane i of the
+      // group receives byte i of rows 0..7.  Row r is key 8*(r/4) + 4*half
+      // + r%4 of the 16-key block (the order of the probabilities' k
+      // index), the 16 bytes are columns db*32 + 16*((lane >> 4) & 1) ..
+      const int j = lane & 15, r8 = j >> 1;
+      const int row = kh * 32 + 8 * (r8 >> 2) + 4 * half + (r8 & 3);
+      const int chunk = 2 * db + ((lane >> 4) & 1);
+      v_off[db] = ring_base + kVOff + row * 128 +
+                  ((chunk ^ ((row >> 1) & 7)) << 4) + 8 * (j & 1);
+    } else {
+      v_off[db] = ring_base + kVOff + (kh * 32 + 4 * half + y) * 256 +
+                  ((4 * (db ^ y) + x) << 4) + 8 * (lane & 1);
+    }
   }
 
   // ---- DMA of one tile: wave w moves rows kDmaRows*w .. of K and of V
   const int pmask = (1 << p.log2_page) - 1;
-  const unsigned tok_bytes = (unsigned)p.Hkv * kHeadDim * 2;
+  const unsigned tok_bytes = (unsigned)p.Hkv * kRowB;
   const unsigned page_bytes = tok_bytes << p.log2_page;
   const char* kbase = reinterpret_cast<const char*>(p.k);
   const char* vbase = reinterpret_cast<const char*>(p.v);
   const bool fast_pages = p.log2_page >= kLog2DmaRows;
   // page ids are clamped to the cache when used (the table is not checked)
   const unsigned pg_last = (unsigned)max(p.num_pages - 1, 0);
+  // source chunk of the lane's 16 bytes (the LDS chunk is fixed by the
+  // lane): bf16 K chunk ^ (row & 15), bf16 V chunk ^ 4 (row & 3) (for the
+  // 16-bit transposing reads), fp8 K and V chunk ^ ((row >> 1) & 7)
+  auto k_chunk = [](int c, int row) -> unsigned {
+    return (unsigned)(kFp8 ? c ^ ((row >> 1) & 7) : c ^ (row & 15));
+  };
+  auto v_chunk = [](int c, int row) -> unsigned {
+    return (unsigned)(kFp8 ? c ^ ((row >> 1) & 7) : c ^ (4 * (row & 3)));
+  };
   unsigned k_row_off[kOpsPerMat], v_row_off[kOpsPerMat];
 #pragma unroll
   for (int k = 0; k < kOpsPerMat; ++k) {
-    const int rw = 4 * k + lrow;
+    const int rw = kRowsPerOp * k + drow;
     const int row = kDmaRows * wave + rw;  // row within the tile
-    k_row_off[k] = rw * tok_bytes + ((lchunk ^ (row & 15)) << 4);
-    v_row_off[k] = rw * tok_bytes + ((lchunk ^ (4 * (row & 3))) << 4);
+    k_row_off[k] = rw * tok_bytes + (k_chunk(dchunk, row) << 4);
+    v_row_off[k] = rw * tok_bytes + (v_chunk(dchunk, row) << 4);
   }
   struct DmaPlan {
     const char* kb0;
@@ -182,7 +218,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
     const unsigned pgu =
         min((unsigned)__builtin_amdgcn_readfirstlane(pg_lds[pi]), pg_last);
     const size_t off = (size_t)pgu * page_bytes +
-                       (unsigned)(w0 & pmask) * tok_bytes + g * kHeadDim * 2;
+                       (unsigned)(w0 & pmask) * tok_bytes + g * kRowB;
     return DmaPlan{kbase + off, vbase + off,
                    ring_base + (unsigned)(t & (kStages - 1)) * kTileBytes};
   };
@@ -204,7 +240,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
     int pg[kOpsPerMat], slot[kOpsPerMat];
 #pragma unroll
     for (int k = 0; k < kOpsPerMat; ++k) {
-      const int pos = min(w0 + 4 * k + lrow, kend - 1);
+      const int pos = min(w0 + kRowsPerOp * k + drow, kend - 1);
       slot[k] = pos & pmask;
       pg[k] = clampi(pg_lds[clampi((pos >> p.log2_page) - lp0, 0,
                                    kPageCache - 1)],
@@ -212,12 +248,12 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
     }
 #pragma unroll
     for (int k = 0; k < kOpsPerMat; ++k) {
-      const int row = kDmaRows * wave + 4 * k + lrow;
+      const int row = kDmaRows * wave + kRowsPerOp * k + drow;
       const size_t off = (size_t)(unsigned)pg[k] * page_bytes +
-                         (unsigned)slot[k] * tok_bytes + g * kHeadDim * 2;
+                         (unsigned)slot[k] * tok_bytes + g * kRowB;
       const unsigned dst = st + (wave * kOpsPerMat + k) * 1024;
-      dma16(kbase + off + ((lchunk ^ (row & 15)) << 4), dst);
-      dma16(vbase + off + ((lchunk ^ (4 * (row & 3))) << 4), dst + kVOff);
+      dma16(kbase + off + (k_chunk(dchunk, row) << 4), dst);
+      dma16(vbase + off + (v_chunk(dchunk, row) << 4), dst + kVOff);
     }
   };
 
@@ -261,7 +297,14 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
   float m_ref = -INFINITY;  // reference max, log2 units
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = f32x16{};
-  const float c2 = p.scale_log2;
+  // fp8: the cached values stand for code * scale[g]; the K scale folds
+  // into the score scale, the V scale into the output normalisation
+  float c2 = p.scale_log2;
+  float v_sc = 1.f;
+  if constexpr (kFp8) {
+    if (p.k_scale != nullptr) c2 *= p.k_scale[g];
+    if (p.v_scale != nullptr) v_sc = p.v_scale[g];
+  }
 
   // ---- S^T of this wave's key half of tile t (one accumulation chain over
   // the head dimension; the other wave of the SIMD fills its latency)
@@ -269,7 +312,13 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
     const unsigned so = (unsigned)(t & (kStages - 1)) * kTileBytes;
     bf16x8 kf[8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) kf[c] = lds_read16(k_off[c] + so);
+    for (int c = 0; c < 8; ++c) {
+      if constexpr (kFp8) {
+        kf[c] = e4m3x8_to_bf16(lds_read8(k_off[c] + so));
+      } else {
+        kf[c] = lds_read16(k_off[c] + so);
+      }
+    }
     S = f32x16{};
 #pragma unroll
     for (int c = 0; c < 8; ++c) S = mfma32x32x16(kf[c], qf[c], S);
@@ -282,11 +331,15 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
       bf16x8 vf[4];
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const unsigned va = v_off[db] + so + hf * 16 * 256;
-        const s16x4 lo = lds_read_tr(va);
-        const s16x4 hi = lds_read_tr(va + 8 * 256);
-        vf[db] = __builtin_bit_cast(
-            bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        if constexpr (kFp8) {
+          vf[db] = e4m3x8_to_bf16(lds_read_tr8(v_off[db] + so + hf * 16 * 128));
+        } else {
+          const unsigned va = v_off[db] + so + hf * 16 * 256;
+          const s16x4 lo = lds_read_tr(va);
+          const s16x4 hi = lds_read_tr(va + 8 * 256);
+          vf[db] = __builtin_bit_cast(
+              bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
       }
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
@@ -376,11 +429,11 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
     if (j + kStages - 1 < n) issue(j + kStages - 1);
     float m_new, alpha;
     bool r;
-    if (j + 1 < n && kbeg + (j + 2) * kKeyTile > min(P, kend)) {
-      r = body(j, Scur, Snext, true, false, m_new, alpha);
-    } else {
-      r = body(j, Scur, Snext, false, false, m_new, alpha);
-    }
+    // (one copy of the body for masked and unmasked tiles: the tail runs
+    // once per workgroup, so its code size, fetched cold into the
+    // instruction cache, costs more than the branch)
+    const bool mk = j + 1 < n && kbeg + (j + 2) * kKeyTile > min(P, kend);
+    r = body(j, Scur, Snext, mk, false, m_new, alpha);
     if (j + 1 >= n) {  // the scores past the last tile are not data
       r = false;
       m_new = m_ref;
@@ -434,12 +487,11 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
     hot_step(j + 2, SA, SB);
     hot_step(j + 3, SB, SA);
   }
-  for (int i = n_hot / 4; 4 * i < n; ++i) {
-    const int j = 4 * i;
+  // the remaining steps, two per iteration (the score registers swap
+  // roles every step; stage offsets are computed, not unrolled)
+  for (int j = n_hot; j < n; j += 2) {
     step(j, SA, SB);
     if (j + 1 < n) step(j + 1, SB, SA);
-    if (j + 2 < n) step(j + 2, SA, SB);
-    if (j + 3 < n) step(j + 3, SB, SA);
   }
 
   // ---- combine the two key halves.  Wave (rg, kh) finishes head-dim half
@@ -515,7 +567,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
   // 2^-ex (the row's scale exponent, from the whole row's largest value:
   // the two waves exchange their halves' maxima), staged through LDS past
   // the exchange area so that the stores write whole half rows
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float inv = l_tot > 0.f ? v_sc / l_tot : 0.f;
   const unsigned stg = ring_base + kEpilogueStage + wave * 4096;
   u32x2 pk[8];
   if (un.nsplit == 1) {

@@ -448,11 +448,11 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
     if (j + kStages - 1 < n) issue(j + kStages - 1);
     float m_new[QB], alpha[QB];
     bool r;
-    if (j + 1 < n && kbeg + (j + 2) * kKeyTile > min(P, kend)) {
-      r = body(j, Scur, Snext, true, false, m_new, alpha);
-    } else {
-      r = body(j, Scur, Snext, false, false, m_new, alpha);
-    }
+    // (one copy of the body for masked and unmasked tiles: the tail runs
+    // once per workgroup, so its code size, fetched cold into the
+    // instruction cache, costs more than the branch)
+    const bool mk = j + 1 < n && kbeg + (j + 2) * kKeyTile > min(P, kend);
+    r = body(j, Scur, Snext, mk, false, m_new, alpha);
     if (j + 1 >= n) {  // the scores past the last tile are not data
       r = false;
 #pragma unroll
@@ -516,12 +516,11 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
     hot_step(j + 2, SA, SB);
     hot_step(j + 3, SB, SA);
   }
-  for (int i = n_hot / 4; 4 * i < n; ++i) {
-    const int j = 4 * i;
+  // the remaining steps, two per iteration (the score registers swap
+  // roles every step; stage offsets are computed, not unrolled)
+  for (int j = n_hot; j < n; j += 2) {
     step(j, SA, SB);
     if (j + 1 < n) step(j + 1, SB, SA);
-    if (j + 2 < n) step(j + 2, SA, SB);
-    if (j + 3 < n) step(j + 3, SB, SA);
   }
 
   // ---- epilogue: the normalised output in bf16 (one split) or fp16 (a
@@ -532,8 +531,26 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
   for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = l_run[qb] + other_half(l_run[qb]);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    int ex = 0;  // scale exponent of a split's partial row (f16_row_exp)
-    if (un.nsplit > 1) {
+    const unsigned stg = ring_base + (unsigned)(wave * QB + qb) * 8192;
+    u32x2 pk[16];
+    if (un.nsplit == 1) {
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        bf16x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v4[e] = (__bf16)(o[qb][c >> 2][(c & 3) * 4 + e] * inv);
+        }
+        pk[c] = __builtin_bit_cast(u32x2, v4);
+      }
+      store_rows_staged(pk, stg, rvalid[qb] ? (int)qrow[qb] : -1,
+                        reinterpret_cast<char*>(p.out), lane);
+      if (half == 0 && rvalid[qb]) {
+        p.lse[qrow[qb]] =
+            l_tot > 0.f ? (m_ref[qb] + log2f(l_tot)) * kLn2 : -INFINITY;
+      }
+    } else {
+      // scale exponent of the partial row (f16_row_exp)
       float amax = 0.f;
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
@@ -543,40 +560,17 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
                                                __builtin_fabsf(o[qb][db][e]));
         }
       }
-      ex = f16_row_exp(__builtin_elementwise_maximum(amax, other_half(amax)) *
-                       inv);
-    }
-    u32x2 pk[16];
+      const int ex = f16_row_exp(
+          __builtin_elementwise_maximum(amax, other_half(amax)) * inv);
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
+      for (int c = 0; c < 16; ++c) {
+        f16x4 v4;
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        if (un.nsplit == 1) {
-          bf16x4 v4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            v4[e] = (__bf16)(o[qb][db][g4 * 4 + e] * inv);
-          }
-          pk[db * 4 + g4] = __builtin_bit_cast(u32x2, v4);
-        } else {
-          f16x4 v4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            v4[e] = to_f16_sat(ldexp2(o[qb][db][g4 * 4 + e] * inv, -ex));
-          }
-          pk[db * 4 + g4] = __builtin_bit_cast(u32x2, v4);
+        for (int e = 0; e < 4; ++e) {
+          v4[e] = to_f16_sat(ldexp2(o[qb][c >> 2][(c & 3) * 4 + e] * inv, -ex));
         }
+        pk[c] = __builtin_bit_cast(u32x2, v4);
       }
-    }
-    const unsigned stg = ring_base + (unsigned)(wave * QB + qb) * 8192;
-    if (un.nsplit == 1) {
-      store_rows_staged(pk, stg, rvalid[qb] ? (int)qrow[qb] : -1,
-                        reinterpret_cast<char*>(p.out), lane);
-      if (half == 0 && rvalid[qb]) {
-        p.lse[qrow[qb]] =
-            l_tot > 0.f ? (m_ref[qb] + log2f(l_tot)) * kLn2 : -INFINITY;
-      }
-    } else {
       // the unit's partial slot: its rows in row-block order
       const int rl = (wave * QB + qb) * 32 + col;
       const size_t prow0 = (size_t)L * kRowsPerWG8;

@@ -76,19 +76,6 @@ __device__ __forceinline__ bf16x8 var_read16(unsigned addr) {
 }
 
 
-// Two E4M3 codes (bytes 2 kHi, 2 kHi + 1 of w) -> two bf16 in one word,
-// by the direct conversion v_cvt_scalef32_pk_bf16_fp8 with scale 1.  Every
-// E4M3 value is a bf16 value, so the conversion is exact; on gfx950 it
-// gives the bits of v_cvt_pk_f32_fp8 followed by a truncation to bf16 for
-// all 256 codes in every byte position (NaN codes included), and that
-// instruction decodes OCP E4M3 (both checked on the device against the
-// format's definition).
-template <bool kHi>
-__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
-  return __builtin_bit_cast(
-      uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHi));
-}
-
 __device__ __forceinline__ const int32_t* table_row(const VarParams& p,
                                                    int s) {
   return p.page_table + (size_t)s * p.max_pps;

@@ -76,6 +76,19 @@ __device__ __forceinline__ float other_half(float x) {
   return __builtin_bit_cast(float, __lane_id() < 32 ? r[1] : r[0]);
 }
 
+// Two E4M3 codes (bytes 2 kHi, 2 kHi + 1 of w) -> two bf16 in one word,
+// by the direct conversion v_cvt_scalef32_pk_bf16_fp8 with scale 1.  Every
+// E4M3 value is a bf16 value, so the conversion is exact; on gfx950 it
+// gives the bits of v_cvt_pk_f32_fp8 followed by a truncation to bf16 for
+// all 256 codes in every byte position (NaN codes included), and that
+// instruction decodes OCP E4M3 (both checked on the device against the
+// format's definition).
+template <bool kHi>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(
+      uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHi));
+}
+
 // D = A(32x16) * B(16x32) + C on the bf16 matrix cores, fp32 accumulate.
 __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);

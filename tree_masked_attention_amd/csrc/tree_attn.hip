@@ -128,7 +128,7 @@ size_t partials_bytes(size_t rows_all, int D, size_t* part_ml_off) {
 // LDS page cache.
 int make_plan(int S, int N, int Hq, int Hkv, int max_prefix_len,
               int max_nodes, int page_size, int req_splits, int cus,
-              Plan* out) {
+              Plan* out, bool fp8 = false) {
   Plan pl;
   const int G = Hq / Hkv;
   const long long rows = (long long)G * max_nodes;
@@ -168,7 +168,9 @@ int make_plan(int S, int N, int Hq, int Hkv, int max_prefix_len,
   // which always fits).
   const long long mask_words = (max_nodes + 63) / 64;
   const long long nodes8 = (kRowsPerWG8 + G - 1) / G + 1;
-  const bool can8 = rows >= kRowsPerWG8 && nodes8 * mask_words <= kMaskCache;
+  // (fp8 K/V: 128 or 64 rows only)
+  const bool can8 = !fp8 && rows >= kRowsPerWG8 &&
+                    nodes8 * mask_words <= kMaskCache;
   int rpw = kRowsPerWG128;
   if (can8) {
     const int st = choose(kRowsPerWG8);
@@ -445,6 +447,20 @@ SplitParams split_params(const Plan& pl, const int32_t* prefix_lens,
   return q;
 }
 
+// The instantiation of the 128/64-row kernel for a launch: balanced or
+// uniform unit plan, fp8 or bf16 K/V.
+template <int NW>
+int launch_fwdh(bool bal, bool fp8, unsigned grid, hipStream_t hs,
+                const FwdParams& fp) {
+  const dim3 g(grid), b(NW * 64);
+  if (fp8) {
+    return bal ? launch(&attn_fwdh_kernel<NW, true, true>, g, b, hs, fp)
+               : launch(&attn_fwdh_kernel<NW, false, true>, g, b, hs, fp);
+  }
+  return bal ? launch(&attn_fwdh_kernel<NW, true, false>, g, b, hs, fp)
+             : launch(&attn_fwdh_kernel<NW, false, false>, g, b, hs, fp);
+}
+
 // Phases of a verify call: the split-KV + tree pass, then the LSE merge.
 enum { kPhaseAttend = 1, kPhaseMerge = 2 };
 
@@ -458,7 +474,9 @@ int run_verify(int phases, const void* q, const void* k_cache, const void* v_cac
                      int32_t num_q_heads, int32_t num_kv_heads,
                      int32_t head_dim, float scale, int32_t num_splits,
                      void* out, float* lse, void* workspace,
-                     size_t workspace_bytes, void* stream) {
+                     size_t workspace_bytes, void* stream,
+                     bool fp8 = false, const float* k_scale = nullptr,
+                     const float* v_scale = nullptr) {
   int st = check_verify_sizes(num_seqs, total_nodes, num_q_heads,
                               num_kv_heads, head_dim, max_prefix_len,
                               max_nodes, num_splits, mask_words,
@@ -473,7 +491,7 @@ int run_verify(int phases, const void* q, const void* k_cache, const void* v_cac
   Plan pl;
   st = make_plan(num_seqs, total_nodes, num_q_heads, num_kv_heads,
                  max_prefix_len, max_nodes, page_size, num_splits, cu_count(),
-                 &pl);
+                 &pl, fp8);
   if (st != TREE_ATTN_OK) return st;
   if (pl.ws_bytes > 0) {
     if (!workspace) return TREE_ATTN_ERR_WORKSPACE;
@@ -497,6 +515,8 @@ int run_verify(int phases, const void* q, const void* k_cache, const void* v_cac
                                           kCounterBytes);
   fp.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                         pl.part_ml_off);
+  fp.k_scale = fp8 ? k_scale : nullptr;
+  fp.v_scale = fp8 ? v_scale : nullptr;
   // Both phases in one call with split partials: the attention kernel's
   // last split workgroup of each row block merges it (no merge launch).
   const bool fused = (phases & kPhaseAttend) && (phases & kPhaseMerge) &&
@@ -530,15 +550,9 @@ int run_verify(int phases, const void* q, const void* k_cache, const void* v_cac
                : launch(&attn_fwd256_kernel<false>, dim3(grid), dim3(512), hs,
                         fp);
     } else if (pl.rows == kRowsPerWG128) {
-      st = bal ? launch(&attn_fwdh_kernel<8, true>, dim3(grid), dim3(512), hs,
-                        fp)
-               : launch(&attn_fwdh_kernel<8, false>, dim3(grid), dim3(512),
-                        hs, fp);
+      st = launch_fwdh<8>(bal, fp8, grid, hs, fp);
     } else {
-      st = bal ? launch(&attn_fwdh_kernel<4, true>, dim3(grid), dim3(256), hs,
-                        fp)
-               : launch(&attn_fwdh_kernel<4, false>, dim3(grid), dim3(256),
-                        hs, fp);
+      st = launch_fwdh<4>(bal, fp8, grid, hs, fp);
     }
     if (st != TREE_ATTN_OK) return st;
   }
@@ -653,11 +667,12 @@ int tree_attn_build_mask(const int32_t* parents, const int32_t* tree_offsets,
                 masks, bad_node);
 }
 
-size_t tree_attn_workspace_size(int32_t num_seqs, int32_t total_nodes,
-                                int32_t num_q_heads, int32_t num_kv_heads,
-                                int32_t head_dim, int32_t max_prefix_len,
-                                int32_t max_nodes, int32_t page_size,
-                                int32_t num_splits) {
+// Workspace of the tuned kernels' plan (bf16 or fp8 K/V, head dim 128).
+size_t tuned_workspace_size(int32_t num_seqs, int32_t total_nodes,
+                            int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t max_prefix_len,
+                            int32_t max_nodes, int32_t page_size,
+                            int32_t num_splits, bool fp8) {
   if (check_sizes(num_seqs, total_nodes, num_q_heads, num_kv_heads, head_dim,
                   max_prefix_len, max_nodes) != TREE_ATTN_OK ||
       num_splits < 0 || !is_pow2(page_size) || page_size > 4096) {
@@ -667,17 +682,28 @@ size_t tree_attn_workspace_size(int32_t num_seqs, int32_t total_nodes,
   Plan pl;
   if (make_plan(num_seqs, total_nodes, num_q_heads, num_kv_heads,
                 max_prefix_len, max_nodes, page_size, num_splits, cu_count(),
-                &pl) != TREE_ATTN_OK) {
+                &pl, fp8) != TREE_ATTN_OK) {
     return 0;
   }
   return pl.ws_bytes;
 }
 
-int tree_attn_describe_plan(int32_t num_seqs, int32_t total_nodes,
-                            int32_t num_q_heads, int32_t num_kv_heads,
-                            int32_t head_dim, int32_t max_prefix_len,
-                            int32_t max_nodes, int32_t page_size,
-                            int32_t num_splits, int32_t* info) {
+size_t tree_attn_workspace_size(int32_t num_seqs, int32_t total_nodes,
+                                int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t max_prefix_len,
+                                int32_t max_nodes, int32_t page_size,
+                                int32_t num_splits) {
+  return tuned_workspace_size(num_seqs, total_nodes, num_q_heads,
+                              num_kv_heads, head_dim, max_prefix_len,
+                              max_nodes, page_size, num_splits, false);
+}
+
+// The tuned kernels' launch for these sizes (bf16 or fp8 K/V).
+int describe_tuned(int32_t num_seqs, int32_t total_nodes, int32_t num_q_heads,
+                   int32_t num_kv_heads, int32_t head_dim,
+                   int32_t max_prefix_len, int32_t max_nodes,
+                   int32_t page_size, int32_t num_splits, bool fp8,
+                   int32_t* info) {
   if (info == nullptr) return TREE_ATTN_ERR_NULL;
   int st = check_sizes(num_seqs, total_nodes, num_q_heads, num_kv_heads,
                        head_dim, max_prefix_len, max_nodes);
@@ -688,13 +714,53 @@ int tree_attn_describe_plan(int32_t num_seqs, int32_t total_nodes,
   Plan pl;
   st = make_plan(num_seqs, total_nodes, num_q_heads, num_kv_heads,
                  max_prefix_len, max_nodes, page_size, num_splits, cu_count(),
-                 &pl);
+                 &pl, fp8);
   if (st != TREE_ATTN_OK) return st;
   info[0] = pl.rows == kRowsPerWG64 ? 4 : kWaves;
   info[1] = pl.rows;
   info[2] = pl.splits;
   info[3] = pl.chunk;
   info[4] = 8 * ((pl.units + 7) / 8);
+  return TREE_ATTN_OK;
+}
+
+int tree_attn_describe_plan(int32_t num_seqs, int32_t total_nodes,
+                            int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t max_prefix_len,
+                            int32_t max_nodes, int32_t page_size,
+                            int32_t num_splits, int32_t* info) {
+  return describe_tuned(num_seqs, total_nodes, num_q_heads, num_kv_heads,
+                        head_dim, max_prefix_len, max_nodes, page_size,
+                        num_splits, false, info);
+}
+
+int tree_attn_describe_plan_ex(int32_t kv_dtype, int32_t num_seqs,
+                               int32_t total_nodes, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim,
+                               int32_t max_prefix_len, int32_t max_nodes,
+                               int32_t page_size, int32_t num_splits,
+                               int32_t* info) {
+  if (info == nullptr) return TREE_ATTN_ERR_NULL;
+  if (head_dim == kHeadDim && (kv_dtype == TREE_ATTN_KV_BF16 ||
+                               kv_dtype == TREE_ATTN_KV_FP8_E4M3)) {
+    return describe_tuned(num_seqs, total_nodes, num_q_heads, num_kv_heads,
+                          head_dim, max_prefix_len, max_nodes, page_size,
+                          num_splits, kv_dtype == TREE_ATTN_KV_FP8_E4M3, info);
+  }
+  int st = check_var_sizes(kv_dtype, num_seqs, total_nodes, num_q_heads,
+                           num_kv_heads, head_dim, max_prefix_len, max_nodes,
+                           page_size, num_splits);
+  if (st != TREE_ATTN_OK) return st;
+  VarPlan pl;
+  st = make_var_plan(num_seqs, total_nodes, num_q_heads, num_kv_heads,
+                     head_dim, max_prefix_len, max_nodes, page_size,
+                     num_splits, cu_count(), &pl);
+  if (st != TREE_ATTN_OK) return st;
+  info[0] = kVarThreads / 64;
+  info[1] = kVarRows;
+  info[2] = pl.splits;
+  info[3] = pl.chunk;
+  info[4] = (int)pl.grid;
   return TREE_ATTN_OK;
 }
 
@@ -993,10 +1059,12 @@ size_t tree_attn_workspace_size_ex(int32_t kv_dtype, int32_t num_seqs,
                                    int32_t num_kv_heads, int32_t head_dim,
                                    int32_t max_prefix_len, int32_t max_nodes,
                                    int32_t page_size, int32_t num_splits) {
-  if (kv_dtype == TREE_ATTN_KV_BF16 && head_dim == kHeadDim) {
-    return tree_attn_workspace_size(num_seqs, total_nodes, num_q_heads,
-                                    num_kv_heads, head_dim, max_prefix_len,
-                                    max_nodes, page_size, num_splits);
+  if (head_dim == kHeadDim && (kv_dtype == TREE_ATTN_KV_BF16 ||
+                               kv_dtype == TREE_ATTN_KV_FP8_E4M3)) {
+    return tuned_workspace_size(num_seqs, total_nodes, num_q_heads,
+                                num_kv_heads, head_dim, max_prefix_len,
+                                max_nodes, page_size, num_splits,
+                                kv_dtype == TREE_ATTN_KV_FP8_E4M3);
   }
   if (check_var_sizes(kv_dtype, num_seqs, total_nodes, num_q_heads,
                       num_kv_heads, head_dim, max_prefix_len, max_nodes,
@@ -1027,13 +1095,15 @@ int tree_attn_verify_ex(const void* q, const void* k_cache,
                         int32_t num_splits, void* out, float* lse,
                         void* workspace, size_t workspace_bytes,
                         void* stream) {
-  if (kv_dtype == TREE_ATTN_KV_BF16 && head_dim == kHeadDim) {
+  if (head_dim == kHeadDim && (kv_dtype == TREE_ATTN_KV_BF16 ||
+                               kv_dtype == TREE_ATTN_KV_FP8_E4M3)) {
     return run_verify(kPhaseAttend | kPhaseMerge, q, k_cache, v_cache,
                       page_table, max_pages_per_seq, num_pages, page_size,
                       prefix_lens, tree_offsets, masks, mask_words, num_seqs,
                       total_nodes, max_prefix_len, max_nodes, num_q_heads,
                       num_kv_heads, head_dim, scale, num_splits, out, lse,
-                      workspace, workspace_bytes, stream);
+                      workspace, workspace_bytes, stream,
+                      kv_dtype == TREE_ATTN_KV_FP8_E4M3, k_scale, v_scale);
   }
   int st = check_var_sizes(kv_dtype, num_seqs, total_nodes, num_q_heads,
                            num_kv_heads, head_dim, max_prefix_len, max_nodes,
@@ -1093,14 +1163,9 @@ int tree_attn_verify_ex(const void* q, const void* k_cache,
   vp.chunk = pl.chunk;
   vp.scale_log2 = scale * kLog2e;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  const bool fp8 = kv_dtype == TREE_ATTN_KV_FP8_E4M3;
-  if (head_dim == 64) {
-    st = fp8 ? launch_var<64, true>(pl, vp, hs)
-             : launch_var<64, false>(pl, vp, hs);
-  } else {
-    // bf16 with head dim 128 never gets here: it runs the tuned kernels
-    st = launch_var<128, true>(pl, vp, hs);
-  }
+  // head dim 64 (128 ran the tuned kernels above)
+  st = kv_dtype == TREE_ATTN_KV_FP8_E4M3 ? launch_var<64, true>(pl, vp, hs)
+                                         : launch_var<64, false>(pl, vp, hs);
   if (st != TREE_ATTN_OK) return st;
   if (pl.splits > 1) {
     // a separate merge launch: the partials of this kernel are scattered
@@ -1108,10 +1173,7 @@ int tree_attn_verify_ex(const void* q, const void* k_cache,
     // workgroup of a row block was slower than this launch
     const long long work = (long long)total_nodes * num_q_heads * (head_dim / 4);
     const unsigned mgrid = (unsigned)((work + 255) / 256);
-    st = head_dim == 64
-             ? launch(&attn_var_merge_kernel<64>, dim3(mgrid), dim3(256), hs, vp)
-             : launch(&attn_var_merge_kernel<128>, dim3(mgrid), dim3(256), hs,
-                      vp);
+    st = launch(&attn_var_merge_kernel<64>, dim3(mgrid), dim3(256), hs, vp);
     if (st != TREE_ATTN_OK) return st;
   }
   return TREE_ATTN_OK;
