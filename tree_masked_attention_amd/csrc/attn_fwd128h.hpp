@@ -74,10 +74,11 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
 
   // Prologue, two rounds of memory latency before the first tile's scores:
   // (1) the split's page-table entries go to LDS by DMA while the tree
-  // bounds load, then Q (staged in ring stage 3, which tile 3 only
-  // overwrites after every wave has read it) and the ancestor-mask rows
-  // join them in flight; (2) once all of these are in, tiles 0-2 are
-  // issued and the first scores wait for tile 0 alone.
+  // bounds load, and Q (staged in ring stage 3, which tile 3 only
+  // overwrites after every wave has read it) follows as soon as the bounds
+  // are in; (2) once the page-table entries are in, the ancestor-mask rows
+  // and tiles 0-2 are issued behind Q, and the first scores wait for Q,
+  // the mask rows and tile 0.
   const int kbeg = split * un.chunk;
   const int lp0 = kbeg >> p.log2_page;
   {
@@ -133,6 +134,10 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
               ((lchunk ^ (rl & 15)) << 4),
           q_lds + (i < 16 ? 0u : (unsigned)kVOff) + ((4 * i) & 63) * 256);
   }
+  // the page-table slice has landed (issued before Q's four ops); Q may
+  // still be in flight
+  wait_vmcnt<4>();
+  __syncthreads();  // page slice visible
   if (nm > 0) {
     const int nd = 2 * nm;  // dwords
     const char* msrc =
@@ -141,8 +146,6 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
       if (i0 + lane < nd) dma4(msrc + 4 * (i0 + lane), mk_base + 4 * i0);
     }
   }
-  wait_vmcnt<0>();
-  __syncthreads();  // page slice, Q and mask rows visible
 
   // ---- LDS operand addresses of this wave's key half (stage 0)
   unsigned k_off[8];
