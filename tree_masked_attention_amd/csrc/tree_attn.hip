@@ -31,7 +31,7 @@ static __device__ __align__(256) unsigned char
 
 namespace {
 
-constexpr int kAbiVersion = 10;
+constexpr int kAbiVersion = 11;
 constexpr int kMaxDevices = 64;
 constexpr int kMaxSplits = 256;
 constexpr int kMinKeysPerSplit = 256;
