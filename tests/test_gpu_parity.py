@@ -475,6 +475,42 @@ def test_overlapping_calls_with_own_workspaces():
             assert int(ws[:65536].count_nonzero()) == 0
 
 
+def test_side_stream_without_workspace():
+    # verify on a stream that is not torch's current one, with the binding
+    # allocating the (zero-filled) workspace and the outputs: the fills are
+    # ordered before the launches on that stream, and the result equals the
+    # call on the current stream bit for bit, in a loop that keeps the
+    # allocator busy on the current stream meanwhile
+    import tree_masked_attention_amd.api as api
+    splits = 4
+    wl, dev, args, nbytes = _split_case_inputs("side", 161, splits)
+    say("[gpu] verify on a side stream, workspace allocated by the binding")
+    ref_out, ref_lse = api.verify(*args, num_splits=splits)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    for rep in range(4):
+        out, lse = api.verify(*args, num_splits=splits, stream=side)
+        # unrelated allocations and work on the current stream
+        junk = torch.full((1 << 20,), 7, dtype=torch.int32, device="cuda:0")
+        junk.add_(1)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)), rep
+        assert torch.equal(lse, ref_lse), rep
+        del junk
+
+
+def test_two_phases_without_workspace_rejected():
+    # the attend and merge launches must share a workspace: asking for a
+    # phase of a split call without one is an error, not a silent zero merge
+    import tree_masked_attention_amd.api as api
+    splits = 4
+    wl, dev, args, nbytes = _split_case_inputs("phase-ws", 162, splits)
+    with pytest.raises(ValueError):
+        api.verify(*args, num_splits=splits, phase="attend")
+
+
 def test_graph_capture_replays():
     # tree_attn_verify (with split partials merged in its last workgroups)
     # captured in a graph: every replay, with eager work and a sync between
