@@ -208,6 +208,11 @@ FP8_TUNED_CASES = {
                                      tree_sizes=[100], page_size=8,
                                      num_q_heads=8, num_kv_heads=2,
                                      tree_rules="chain"), 128),
+    # 256-row kernel on FP8 tiles (balanced plan over two sequences)
+    "fp8-r256-balanced": (lambda: _fp8("fp8-r256", 195,
+                                       prefix_lens=[16000, 9000],
+                                       tree_sizes=[64, 70], num_q_heads=32,
+                                       num_kv_heads=8), 256),
 }
 
 
@@ -226,6 +231,23 @@ def test_fp8_tuned_parity(name):
         assert plan["splits"] > 1  # 3 sequences: the device-balanced plan
     check(wl, name)
     check(wl, f"{name}, 3 splits", num_splits=3)
+
+
+@pytest.mark.parametrize("page", [4, 16])
+def test_fp8_256_rows_one_split(page):
+    # one split of 3964 keys on the 256-row kernel (within the 1039 page
+    # ids a split can hold at 4 keys per page): the tree tile's mask, the
+    # slow DMA path (pages of 4 keys) and the fast one
+    import tree_masked_attention_amd.api as api
+    wl = _fp8(f"fp8-r256-p{page}", 196, prefix_lens=[3900], tree_sizes=[64],
+              page_size=page, num_q_heads=16, num_kv_heads=4)
+    plan = api.describe_plan_ex(api.KV_FP8_E4M3, wl.num_seqs, wl.total_nodes,
+                                wl.num_q_heads, wl.num_kv_heads, 128,
+                                wl.max_prefix_len, wl.max_nodes, wl.page_size,
+                                1)
+    say(f"[gpu] fp8 256 rows, one split, page {page}: plan {plan}")
+    assert plan["rows"] == 256 and plan["splits"] == 1
+    check(wl, f"fp8-r256-p{page}", num_splits=1)
 
 
 @pytest.mark.parametrize("splits", [2, 5, 64])

@@ -19,14 +19,18 @@ namespace tree_attn {
 
 constexpr int kRowsPerWG8 = 256;
 
-template <bool kBalanced>
+template <bool kBalanced, bool kFp8>
 __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
   constexpr int NW = 8;
   constexpr int QB = 1;                  // 32-query blocks per wave
   constexpr int kThreads = NW * 64;
-  constexpr int kOpsPerMat = 16 / NW;    // 1-KB DMA ops per wave per matrix
+  constexpr int kEB = kFp8 ? 1 : 2;      // bytes per cached element
+  constexpr int kRowB = kHeadDim * kEB;  // bytes per cached (token, head)
+  // 1-KB DMA ops per wave per matrix: each moves 4 bf16 or 8 fp8 rows
+  constexpr int kOpsPerMat = (kFp8 ? 8 : 16) / NW;
   constexpr int kOps = 2 * kOpsPerMat;
-  constexpr int kDmaRows = 4 * kOpsPerMat;  // tile rows a wave moves
+  constexpr int kRowsPerOp = 1024 / kRowB;
+  constexpr int kDmaRows = kRowsPerOp * kOpsPerMat;  // tile rows a wave moves
   constexpr int kLog2DmaRows = 3;
   static_assert((1 << kLog2DmaRows) == kDmaRows, "shape");
   __shared__ __align__(1024) unsigned char ring[2 * kVOff];
@@ -140,23 +144,52 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
   unsigned k_off[8];
 #pragma unroll
   for (int kc = 0; kc < 8; ++kc) {
-    k_off[kc] = ring_base + col * 256 + (((2 * kc + half) ^ (col & 15)) << 4);
+    if constexpr (kFp8) {
+      // fp8 rows of 128 B, 16-byte chunk c stored at c ^ ((row >> 1) & 7);
+      // the lane's 8 values d = kc*16 + half*8 .. +7 are half of chunk kc
+      // (32-key block offsets keep the swizzle: 32 rows = 16 row pairs)
+      k_off[kc] = ring_base + col * 128 + ((kc ^ ((col >> 1) & 7)) << 4) +
+                  half * 8;
+    } else {
+      k_off[kc] = ring_base + col * 256 + (((2 * kc + half) ^ (col & 15)) << 4);
+    }
   }
   const int y = (lane & 15) >> 2;
   const int x = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
   unsigned v_off[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
-    v_off[db] = ring_base + kVOff + (4 * half + y) * 256 +
-                ((4 * (db ^ y) + x) << 4) + 8 * (lane & 1);
+    if constexpr (kFp8) {
+      // ds_read_b64_tr_b8 (attn_fwd.hpp): lanes 2r, 2r+1 of a 16-lane group
+      // name row r = key 8*(r/4) + 4*half + r%4 of the 16-key block
+      const int j = lane & 15, r8 = j >> 1;
+      const int row = 8 * (r8 >> 2) + 4 * half + (r8 & 3);
+      const int chunk = 2 * db + ((lane >> 4) & 1);
+      v_off[db] = ring_base + kVOff + row * 128 +
+                  ((chunk ^ ((row >> 1) & 7)) << 4) + 8 * (j & 1);
+    } else {
+      v_off[db] = ring_base + kVOff + (4 * half + y) * 256 +
+                  ((4 * (db ^ y) + x) << 4) + 8 * (lane & 1);
+    }
   }
 
   // ---- DMA of one tile: wave w moves rows kDmaRows*w .. of K and of V, as
   // kOpsPerMat instructions of 4 rows (lane l: row 4k + l/16, chunk l%16).
   const int pmask = (1 << p.log2_page) - 1;
-  const unsigned tok_bytes = (unsigned)p.Hkv * kHeadDim * 2;
+  const unsigned tok_bytes = (unsigned)p.Hkv * kRowB;
   const unsigned page_bytes = tok_bytes << p.log2_page;
-  const int lrow = lane >> 4, lchunk = lane & 15;
+  // a lane's row and 16-byte chunk within one DMA op
+  const int lrow = kFp8 ? lane >> 3 : lane >> 4;
+  const int lchunk = kFp8 ? lane & 7 : lane & 15;
+  // source chunk of the lane's 16 bytes (the LDS chunk is fixed by the
+  // lane): bf16 K chunk ^ (row & 15), bf16 V chunk ^ 4 (row & 3), fp8 K
+  // and V chunk ^ ((row >> 1) & 7)
+  auto k_chunk = [](int c, int row) -> unsigned {
+    return (unsigned)(kFp8 ? c ^ ((row >> 1) & 7) : c ^ (row & 15));
+  };
+  auto v_chunk = [](int c, int row) -> unsigned {
+    return (unsigned)(kFp8 ? c ^ ((row >> 1) & 7) : c ^ (4 * (row & 3)));
+  };
   const char* kbase = reinterpret_cast<const char*>(p.k);
   const char* vbase = reinterpret_cast<const char*>(p.v);
   // fast path: the wave's rows lie in one page (pages of >= kDmaRows tokens)
@@ -164,10 +197,10 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
   unsigned k_row_off[kOpsPerMat], v_row_off[kOpsPerMat];
 #pragma unroll
   for (int k = 0; k < kOpsPerMat; ++k) {
-    const int rw = 4 * k + lrow;
+    const int rw = kRowsPerOp * k + lrow;
     const int row = kDmaRows * wave + rw;  // row within the tile
-    k_row_off[k] = rw * tok_bytes + ((lchunk ^ (row & 15)) << 4);
-    v_row_off[k] = rw * tok_bytes + ((lchunk ^ (4 * (row & 3))) << 4);
+    k_row_off[k] = rw * tok_bytes + (k_chunk(lchunk, row) << 4);
+    v_row_off[k] = rw * tok_bytes + (v_chunk(lchunk, row) << 4);
   }
   // DMA of a full tile on the fast path (pages of >= kDmaRows tokens), in
   // pieces: the page lookup first, then part k (one K and one V
@@ -182,7 +215,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
     const int pi = clampi((w0 >> p.log2_page) - lp0, 0, kPageCache - 1);
     const unsigned pgu = (unsigned)__builtin_amdgcn_readfirstlane(pg_lds[pi]);
     const size_t off = (size_t)pgu * page_bytes +
-                       (unsigned)(w0 & pmask) * tok_bytes + g * kHeadDim * 2;
+                       (unsigned)(w0 & pmask) * tok_bytes + g * kRowB;
     return DmaPlan{kbase + off, vbase + off,
                    ring_base + (unsigned)(t & (kStages - 1)) * kTileBytes};
   };
@@ -200,7 +233,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
       const unsigned pgu =
           (unsigned)__builtin_amdgcn_readfirstlane(pg_lds[pi]);
       const size_t off = (size_t)pgu * page_bytes +
-                         (unsigned)(w0 & pmask) * tok_bytes + g * kHeadDim * 2;
+                         (unsigned)(w0 & pmask) * tok_bytes + g * kRowB;
 #pragma unroll
       for (int k = 0; k < kOpsPerMat; ++k) {
         const unsigned dst = st + (wave * kOpsPerMat + k) * 1024;
@@ -212,18 +245,18 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
     int pg[kOpsPerMat], slot[kOpsPerMat];
 #pragma unroll
     for (int k = 0; k < kOpsPerMat; ++k) {
-      const int pos = min(w0 + 4 * k + lrow, kend - 1);
+      const int pos = min(w0 + kRowsPerOp * k + lrow, kend - 1);
       slot[k] = pos & pmask;
       pg[k] = pg_lds[clampi((pos >> p.log2_page) - lp0, 0, kPageCache - 1)];
     }
 #pragma unroll
     for (int k = 0; k < kOpsPerMat; ++k) {
-      const int row = kDmaRows * wave + 4 * k + lrow;
+      const int row = kDmaRows * wave + kRowsPerOp * k + lrow;
       const size_t off = (size_t)(unsigned)pg[k] * page_bytes +
-                         (unsigned)slot[k] * tok_bytes + g * kHeadDim * 2;
+                         (unsigned)slot[k] * tok_bytes + g * kRowB;
       const unsigned dst = st + (wave * kOpsPerMat + k) * 1024;
-      dma16(kbase + off + ((lchunk ^ (row & 15)) << 4), dst);
-      dma16(vbase + off + ((lchunk ^ (4 * (row & 3))) << 4), dst + kVOff);
+      dma16(kbase + off + (k_chunk(lchunk, row) << 4), dst);
+      dma16(vbase + off + (v_chunk(lchunk, row) << 4), dst + kVOff);
     }
   };
 
@@ -263,7 +296,14 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
     l_run[qb] = 0.f;
     m_ref[qb] = -INFINITY;
   }
-  const float c2 = p.scale_log2;
+  // fp8: the cached values stand for code * scale[g]; the K scale folds
+  // into the score scale, the V scale into the output normalisation
+  float c2 = p.scale_log2;
+  float v_sc = 1.f;
+  if constexpr (kFp8) {
+    if (p.k_scale != nullptr) c2 *= p.k_scale[g];
+    if (p.v_scale != nullptr) v_sc = p.v_scale[g];
+  }
 
   // ---- LDS operand reads.  K fragments of key block kb, head-dim chunks
   // kc = 4h .. 4h+3; V^T fragments of key block kb, 16-key half hf.
@@ -271,18 +311,27 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
     const unsigned so = (unsigned)(t & (kStages - 1)) * kTileBytes;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      kf[c] = lds_read16(k_off[4 * h + c] + so + kb * 32 * 256);
+      if constexpr (kFp8) {
+        kf[c] = e4m3x8_to_bf16(lds_read8(k_off[4 * h + c] + so + kb * 32 * 128));
+      } else {
+        kf[c] = lds_read16(k_off[4 * h + c] + so + kb * 32 * 256);
+      }
     }
   };
   auto read_vq = [&](int t, int kb, int hf, bf16x8 (&vf)[4]) {
     const unsigned so = (unsigned)(t & (kStages - 1)) * kTileBytes;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-      const unsigned va = v_off[db] + so + (kb * 32 + hf * 16) * 256;
-      const s16x4 lo = lds_read_tr(va);
-      const s16x4 hi = lds_read_tr(va + 8 * 256);
-      vf[db] = __builtin_bit_cast(
-          bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      if constexpr (kFp8) {
+        vf[db] = e4m3x8_to_bf16(
+            lds_read_tr8(v_off[db] + so + (kb * 32 + hf * 16) * 128));
+      } else {
+        const unsigned va = v_off[db] + so + (kb * 32 + hf * 16) * 256;
+        const s16x4 lo = lds_read_tr(va);
+        const s16x4 hi = lds_read_tr(va + 8 * 256);
+        vf[db] = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
     }
   };
   // S^T of key block kb of tile t for every query block: QB accumulation
@@ -530,7 +579,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = l_run[qb] + other_half(l_run[qb]);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float inv = l_tot > 0.f ? v_sc / l_tot : 0.f;
     const unsigned stg = ring_base + (unsigned)(wave * QB + qb) * 8192;
     u32x2 pk[16];
     if (un.nsplit == 1) {

@@ -128,7 +128,7 @@ size_t partials_bytes(size_t rows_all, int D, size_t* part_ml_off) {
 // LDS page cache.
 int make_plan(int S, int N, int Hq, int Hkv, int max_prefix_len,
               int max_nodes, int page_size, int req_splits, int cus,
-              Plan* out, bool fp8 = false) {
+              Plan* out) {
   Plan pl;
   const int G = Hq / Hkv;
   const long long rows = (long long)G * max_nodes;
@@ -168,9 +168,7 @@ int make_plan(int S, int N, int Hq, int Hkv, int max_prefix_len,
   // which always fits).
   const long long mask_words = (max_nodes + 63) / 64;
   const long long nodes8 = (kRowsPerWG8 + G - 1) / G + 1;
-  // (fp8 K/V: 128 or 64 rows only)
-  const bool can8 = !fp8 && rows >= kRowsPerWG8 &&
-                    nodes8 * mask_words <= kMaskCache;
+  const bool can8 = rows >= kRowsPerWG8 && nodes8 * mask_words <= kMaskCache;
   int rpw = kRowsPerWG128;
   if (can8) {
     const int st = choose(kRowsPerWG8);
@@ -461,6 +459,18 @@ int launch_fwdh(bool bal, bool fp8, unsigned grid, hipStream_t hs,
              : launch(&attn_fwdh_kernel<NW, false, false>, g, b, hs, fp);
 }
 
+// The instantiation of the 256-row kernel for a launch.
+int launch_fwd256(bool bal, bool fp8, unsigned grid, hipStream_t hs,
+                  const FwdParams& fp) {
+  const dim3 g(grid), b(512);
+  if (fp8) {
+    return bal ? launch(&attn_fwd256_kernel<true, true>, g, b, hs, fp)
+               : launch(&attn_fwd256_kernel<false, true>, g, b, hs, fp);
+  }
+  return bal ? launch(&attn_fwd256_kernel<true, false>, g, b, hs, fp)
+             : launch(&attn_fwd256_kernel<false, false>, g, b, hs, fp);
+}
+
 // Phases of a verify call: the split-KV + tree pass, then the LSE merge.
 enum { kPhaseAttend = 1, kPhaseMerge = 2 };
 
@@ -491,7 +501,7 @@ int run_verify(int phases, const void* q, const void* k_cache, const void* v_cac
   Plan pl;
   st = make_plan(num_seqs, total_nodes, num_q_heads, num_kv_heads,
                  max_prefix_len, max_nodes, page_size, num_splits, cu_count(),
-                 &pl, fp8);
+                 &pl);
   if (st != TREE_ATTN_OK) return st;
   if (pl.ws_bytes > 0) {
     if (!workspace) return TREE_ATTN_ERR_WORKSPACE;
@@ -545,10 +555,7 @@ int run_verify(int phases, const void* q, const void* k_cache, const void* v_cac
     // balanced plans run the instantiations that carry the device plan
     const bool bal = fp.plan.uniform_chunk == 0;
     if (pl.rows == kRowsPerWG8) {
-      st = bal ? launch(&attn_fwd256_kernel<true>, dim3(grid), dim3(512), hs,
-                        fp)
-               : launch(&attn_fwd256_kernel<false>, dim3(grid), dim3(512), hs,
-                        fp);
+      st = launch_fwd256(bal, fp8, grid, hs, fp);
     } else if (pl.rows == kRowsPerWG128) {
       st = launch_fwdh<8>(bal, fp8, grid, hs, fp);
     } else {
@@ -667,12 +674,12 @@ int tree_attn_build_mask(const int32_t* parents, const int32_t* tree_offsets,
                 masks, bad_node);
 }
 
-// Workspace of the tuned kernels' plan (bf16 or fp8 K/V, head dim 128).
+// Workspace of the tuned kernels' plan (the same for bf16 and fp8 K/V).
 size_t tuned_workspace_size(int32_t num_seqs, int32_t total_nodes,
                             int32_t num_q_heads, int32_t num_kv_heads,
                             int32_t head_dim, int32_t max_prefix_len,
                             int32_t max_nodes, int32_t page_size,
-                            int32_t num_splits, bool fp8) {
+                            int32_t num_splits) {
   if (check_sizes(num_seqs, total_nodes, num_q_heads, num_kv_heads, head_dim,
                   max_prefix_len, max_nodes) != TREE_ATTN_OK ||
       num_splits < 0 || !is_pow2(page_size) || page_size > 4096) {
@@ -682,7 +689,7 @@ size_t tuned_workspace_size(int32_t num_seqs, int32_t total_nodes,
   Plan pl;
   if (make_plan(num_seqs, total_nodes, num_q_heads, num_kv_heads,
                 max_prefix_len, max_nodes, page_size, num_splits, cu_count(),
-                &pl, fp8) != TREE_ATTN_OK) {
+                &pl) != TREE_ATTN_OK) {
     return 0;
   }
   return pl.ws_bytes;
@@ -695,15 +702,14 @@ size_t tree_attn_workspace_size(int32_t num_seqs, int32_t total_nodes,
                                 int32_t num_splits) {
   return tuned_workspace_size(num_seqs, total_nodes, num_q_heads,
                               num_kv_heads, head_dim, max_prefix_len,
-                              max_nodes, page_size, num_splits, false);
+                              max_nodes, page_size, num_splits);
 }
 
 // The tuned kernels' launch for these sizes (bf16 or fp8 K/V).
 int describe_tuned(int32_t num_seqs, int32_t total_nodes, int32_t num_q_heads,
                    int32_t num_kv_heads, int32_t head_dim,
                    int32_t max_prefix_len, int32_t max_nodes,
-                   int32_t page_size, int32_t num_splits, bool fp8,
-                   int32_t* info) {
+                   int32_t page_size, int32_t num_splits, int32_t* info) {
   if (info == nullptr) return TREE_ATTN_ERR_NULL;
   int st = check_sizes(num_seqs, total_nodes, num_q_heads, num_kv_heads,
                        head_dim, max_prefix_len, max_nodes);
@@ -714,7 +720,7 @@ int describe_tuned(int32_t num_seqs, int32_t total_nodes, int32_t num_q_heads,
   Plan pl;
   st = make_plan(num_seqs, total_nodes, num_q_heads, num_kv_heads,
                  max_prefix_len, max_nodes, page_size, num_splits, cu_count(),
-                 &pl, fp8);
+                 &pl);
   if (st != TREE_ATTN_OK) return st;
   info[0] = pl.rows == kRowsPerWG64 ? 4 : kWaves;
   info[1] = pl.rows;
@@ -731,7 +737,7 @@ int tree_attn_describe_plan(int32_t num_seqs, int32_t total_nodes,
                             int32_t num_splits, int32_t* info) {
   return describe_tuned(num_seqs, total_nodes, num_q_heads, num_kv_heads,
                         head_dim, max_prefix_len, max_nodes, page_size,
-                        num_splits, false, info);
+                        num_splits, info);
 }
 
 int tree_attn_describe_plan_ex(int32_t kv_dtype, int32_t num_seqs,
@@ -745,7 +751,7 @@ int tree_attn_describe_plan_ex(int32_t kv_dtype, int32_t num_seqs,
                                kv_dtype == TREE_ATTN_KV_FP8_E4M3)) {
     return describe_tuned(num_seqs, total_nodes, num_q_heads, num_kv_heads,
                           head_dim, max_prefix_len, max_nodes, page_size,
-                          num_splits, kv_dtype == TREE_ATTN_KV_FP8_E4M3, info);
+                          num_splits, info);
   }
   int st = check_var_sizes(kv_dtype, num_seqs, total_nodes, num_q_heads,
                            num_kv_heads, head_dim, max_prefix_len, max_nodes,
@@ -1063,8 +1069,7 @@ size_t tree_attn_workspace_size_ex(int32_t kv_dtype, int32_t num_seqs,
                                kv_dtype == TREE_ATTN_KV_FP8_E4M3)) {
     return tuned_workspace_size(num_seqs, total_nodes, num_q_heads,
                                 num_kv_heads, head_dim, max_prefix_len,
-                                max_nodes, page_size, num_splits,
-                                kv_dtype == TREE_ATTN_KV_FP8_E4M3);
+                                max_nodes, page_size, num_splits);
   }
   if (check_var_sizes(kv_dtype, num_seqs, total_nodes, num_q_heads,
                       num_kv_heads, head_dim, max_prefix_len, max_nodes,
