@@ -550,8 +550,8 @@ int tree_attn_gdn_commit(const void* k, const float* u, const float* g,
  *                 Ignored for bf16.
  *   head_dim      64 or 128 (q, out: [total_nodes][num_q_heads][head_dim])
  * With bf16 and head_dim 128 this is exactly tree_attn_verify (the same
- * kernels).  FP8 with head_dim 128 runs the same kernels' 128- and 64-row
- * shapes on FP8 tiles: the DMA ring moves the codes, and each wave
+ * kernels).  FP8 with head_dim 128 runs the same kernels, with the same
+ * plan, on FP8 tiles: the DMA ring moves the codes, and each wave
  * converts its operands to bf16 (exactly: every E4M3 value is a bf16
  * value) as it reads them from LDS; the K scale folds into the softmax
  * scale and the V scale into the output.  Head dim 64 runs a separate
@@ -595,9 +595,9 @@ size_t tree_attn_workspace_size_ex(int32_t kv_dtype, int32_t num_seqs,
 /*
  * tree_attn_describe_plan_ex - tree_attn_describe_plan for the launches of
  * tree_attn_verify_ex (kv_dtype and head_dim as there).  Head dim 128
- * (bf16 or FP8) runs the tuned kernels (FP8: 64 or 128 query rows per
- * workgroup); head dim 64 the 4-wave, 128-row kernel (workgroups: its
- * attention launch's).
+ * (bf16 or FP8) runs the tuned kernels with tree_attn_verify's plan; head
+ * dim 64 the 4-wave, 128-row kernel (workgroups: its attention
+ * launch's).
  */
 int tree_attn_describe_plan_ex(int32_t kv_dtype, int32_t num_seqs,
                                int32_t total_nodes, int32_t num_q_heads,

@@ -1,6 +1,6 @@
 // Shared definitions of the split-KV tree-verification attention kernels on
-// the gfx950 bf16 matrix cores (attn_fwd128h.hpp: 128 query rows per
-// workgroup; attn_fwd8.hpp: 256 rows).
+// the gfx950 bf16 matrix cores (attn_fwd128h.hpp: 128 or 64 query rows per
+// workgroup; attn_fwd8.hpp: 256 rows), for bf16 or fp8 (E4M3) K/V tiles.
 //
 // The kernels compute, for every query row (node i, q head h) of a
 // sequence, softmax attention over the prefix keys plus the tree keys
@@ -47,6 +47,14 @@
 // the MFMA operand reads hit distinct LDS banks.  The split's page-table
 // slice and the ancestor-mask words its tree keys need are copied to LDS
 // before the ring starts, so the loop issues no other global loads.
+//
+// FP8 tiles (E4M3 codes, 128-byte rows): the same ring and DMA ops, each
+// moving 8 rows instead of 4, with 16-byte chunk c of row r stored at
+// c ^ ((r >> 1) & 7).  Each wave converts its operands to bf16 as it reads
+// them (exact: every E4M3 value is a bf16 value): K by ds_read_b64 of the
+// lane's 8 codes, V^T by the byte-transposing ds_read_b64_tr_b8 of the 8
+// keys of its register run pair.  The K scale folds into the softmax
+// scale, the V scale into the output normalisation.
 //
 // Softmax runs in base 2 with scale*log2(e) folded into the FMA that
 // subtracts the running max; the running max is only raised when a tile's

@@ -1,7 +1,9 @@
-// Tree-verification attention for the variants the tuned kernels
-// (attn_fwd128h.hpp, attn_fwd8.hpp) do not cover: head dimension 64, and
-// K/V pages stored in fp8 (OCP E4M3, one fp32 scale per kv head) for head
-// dimension 64 or 128.  The operation is the same as theirs -- every tree
+// Tree-verification attention for the variant the tuned kernels
+// (attn_fwd128h.hpp, attn_fwd8.hpp) do not cover: head dimension 64, with
+// K/V pages in bf16 or in fp8 (OCP E4M3, one fp32 scale per kv head; fp8
+// with head dimension 128 runs the tuned kernels).  The template also
+// compiles for D = 128, which is not launched.  The operation is the same
+// as theirs -- every tree
 // node attends to its sequence's prefix and to its ancestors (JETFLOW,
 // gist.science 2606.18394, section 2 "Arquitectura Central", bullet on the
 // tree-causal mask) -- and so is the split-KV decomposition with an LSE
