@@ -6,6 +6,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -137,6 +138,65 @@ def test_describe_plan():
         api.describe_plan(1, 16, 8, 3, 128, 256, 16, 16, 0)
     with pytest.raises(NotImplementedError):
         api.describe_plan(1, 16, 8, 2, 64, 256, 16, 16, 0)
+
+
+def test_describe_plan_ex():
+    # FP8 with head dim 128 runs the tuned kernels with tree_attn_verify's
+    # plan and workspace; head dim 64 the 4-wave, 128-row variant kernel
+    for sizes in [(1, 16, 8, 2, 128, 256, 16, 16, 0),
+                  (4, 1024, 32, 8, 128, 32768, 256, 16, 0),
+                  (32, 512, 32, 4, 128, 2048, 16, 16, 0),
+                  (3, 119, 8, 2, 128, 9000, 70, 16, 0),
+                  (1, 64, 16, 4, 128, 6000, 64, 16, 3)]:
+        bf = api.describe_plan(*sizes)
+        f8 = api.describe_plan_ex(api.KV_FP8_E4M3, *sizes)
+        assert bf == f8, sizes
+        assert api._lib.tree_attn_workspace_size_ex(api.KV_FP8_E4M3, *sizes) \
+            == api._lib.tree_attn_workspace_size(*sizes)
+    p = api.describe_plan_ex(api.KV_BF16, 1, 16, 8, 2, 64, 256, 16, 16, 0)
+    assert p["waves"] == 4 and p["rows"] == 128
+    with pytest.raises(NotImplementedError):
+        api.describe_plan_ex(api.KV_BF16, 1, 16, 8, 2, 96, 256, 16, 16, 0)
+    with pytest.raises(NotImplementedError):
+        api.describe_plan_ex(7, 1, 16, 8, 2, 128, 256, 16, 16, 0)
+
+
+def test_plan_invariants_random_shapes():
+    # host planning over random shapes: tile-multiple chunks covering the
+    # key range, at most 256 splits, a kernel shape for every row count,
+    # the 64-row shape only without a split, a workspace exactly when the
+    # key range is split, and the workgroup count of the unit grid
+    rng = np.random.default_rng(3)
+    for _ in range(400):
+        S = int(rng.integers(1, 80))
+        hkv = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.choice([1, 2, 4, 8]))
+        max_b = int(rng.integers(1, 1025))
+        max_p = int(rng.integers(0, 40000))
+        page = int(rng.choice([1, 4, 16, 64, 256]))
+        splits = int(rng.choice([0, 0, 0, 1, 2, 7]))
+        N = S * max_b
+        args = (S, N, G * hkv, hkv, 128, max_p, max_b, page, splits)
+        try:
+            p = api.describe_plan(*args)
+        except NotImplementedError:
+            continue  # key ranges beyond 256 splits of 1039 pages
+        T = max_p + max_b
+        assert p["chunk"] % 64 == 0 and 1 <= p["splits"] <= 256, args
+        assert p["chunk"] * p["splits"] >= T, args
+        assert (p["chunk"] - 64) * p["splits"] < T or p["splits"] == 1, args
+        assert (p["waves"], p["rows"]) in ((4, 64), (8, 128), (8, 256)), args
+        if p["rows"] == 64:
+            assert p["splits"] == 1 and G * max_b <= 128, args
+        if p["rows"] == 256:
+            assert G * max_b >= 256 and p["chunk"] >= 2048, args
+        if splits > 0:
+            assert p["splits"] >= min(splits, -(-T // p["chunk"])), args
+        mblocks = -(-G * max_b // p["rows"])
+        units = S * hkv * mblocks * p["splits"]
+        assert p["workgroups"] == 8 * -(-units // 8), args
+        ws = api.workspace_size(*args)
+        assert (ws > 0) == (p["splits"] > 1), args
 
 
 def _accept(**over):
