@@ -263,13 +263,14 @@ __device__ __forceinline__ void apply_tile_mask(f32x16 (&S)[2], uint64_t allow,
 }
 
 // Epilogue of a split workgroup of a launch that merges its own partials
-// (merge_if_last_rows): unit un, rows [r0, r0 + rows_per_wg) of its pair.
-template <int NT>
+// (merge_if_last_rows): unit un, rows [r0, r0 + rows_per_wg) of its pair;
+// RT rows per thread in the merge's rounds of loads.
+template <int NT, int RT = 4>
 __device__ __forceinline__ void merge_if_last(const FwdParams& p,
                                               const Unit& un, int rows,
                                               int r0, int rows_per_wg,
                                               int tid, int* flag_lds) {
-  merge_if_last_rows<NT, kHeadDim>(
+  merge_if_last_rows<NT, kHeadDim, RT>(
       p.counters + un.seg, un.nsplit, p.part_o, p.part_ml, p.out, p.lse,
       p.Hq, p.G, un.g, un.a, r0, min(r0 + rows_per_wg, rows),
       PartSlots{un.slot0, un.mblocks, rows_per_wg, r0}, tid, flag_lds);

@@ -638,7 +638,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
     }
   }
   if (p.counters != nullptr && un.nsplit > 1) {
-    merge_if_last<kThreads>(p, un, rows, r0, kRowsPerWG8, tid, pg_lds);
+    // (256 rows: one round of loads, two splits at a time)
+    merge_if_last<kThreads, 8>(p, un, rows, r0, kRowsPerWG8, tid, pg_lds);
   }
 }
 

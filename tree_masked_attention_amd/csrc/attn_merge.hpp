@@ -179,21 +179,20 @@ __global__ __launch_bounds__(kMergeWaves * 64) void attn_merge_kernel(
 // NT threads of a workgroup (head dim D, rows of D fp16 partials): thread
 // t takes the
 // 16-byte column chunk t % (D/8) of rows r_lo + t / (D/8) + k * NT / (D/8);
-// the loads of kMergeRowsPerThread rows and kMergeSplits splits are issued
-// before any is used.  kCoherent: the partials are read with
-// device-coherent loads (written by other workgroups of the running
-// launch).
-constexpr int kMergeRowsPerThread = 4;
-
-template <int NT, int D, bool kCoherent>
+// the loads of RT rows and 16 / RT splits are issued before any is used
+// (RT = 8 lets a 512-thread workgroup take 256 rows in one pass, whose
+// loads then cover two splits at a time), and only those of splits that
+// exist.  kCoherent: the partials are read with device-coherent loads
+// (written by other workgroups of the running launch).
+template <int NT, int D, bool kCoherent, int RT = 4>
 __device__ __forceinline__ void merge_rows_wg(
     const _Float16* part_o, const float* part_ml, __bf16* out, float* lse,
     int Hq, int G, int g, int a, int r_lo, int r_hi, int nsplit,
     const PartSlots& slots, int tid) {
   constexpr int CH = D / 8;                  // 16-byte chunks per row
   constexpr int RS = NT / CH;                // rows per pass of the group
-  constexpr int RT = kMergeRowsPerThread;
-  constexpr int KS = kMergeSplits;
+  constexpr int KS = 16 / RT;                // splits per round of loads
+  static_assert(RT * KS == 16, "merge batch");
   static_assert(NT % CH == 0, "merge layout");
   typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
   const int ch = tid % CH, rsub = tid / CH;
@@ -218,7 +217,8 @@ __device__ __forceinline__ void merge_rows_wg(
       for (int k = 0; k < RT; ++k) {
 #pragma unroll
         for (int u = 0; u < KS; ++u) {
-          const int c = min(c0 + u, nsplit - 1);  // in range; unused if past
+          if (c0 + u >= nsplit) break;  // (uniform over the workgroup)
+          const int c = c0 + u;
           const size_t prow = slots.row(c, rr[k]);
           const _Float16* po = part_o + prow * D + ch * 8;
           if (kCoherent) {
@@ -274,7 +274,7 @@ __device__ __forceinline__ void merge_rows_wg(
 // invalidate left out, which only plain (non-coherent) accesses need.  No
 // workgroup waits for another.  flag_lds: one int of LDS that no wave uses
 // any more.
-template <int NT, int D>
+template <int NT, int D, int RT = 4>
 __device__ __forceinline__ void merge_if_last_rows(
     unsigned* ctr, int nsplit, const _Float16* part_o, const float* part_ml,
     __bf16* out, float* lse, int Hq, int G, int g, int a, int r_lo,
@@ -289,7 +289,7 @@ __device__ __forceinline__ void merge_if_last_rows(
   __syncthreads();
   if (*flag_lds == 0) return;
   // issued after the barrier, i.e. after the count was seen complete
-  merge_rows_wg<NT, D, true>(part_o, part_ml, out, lse, Hq, G, g, a, r_lo,
+  merge_rows_wg<NT, D, true, RT>(part_o, part_ml, out, lse, Hq, G, g, a, r_lo,
                              r_hi, nsplit, slots, tid);
 }
 
