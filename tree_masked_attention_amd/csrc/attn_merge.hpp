@@ -141,7 +141,8 @@ __global__ __launch_bounds__(kMergeWaves * 64) void attn_merge_kernel(
     for (int k = 0; k < RL; ++k) {
 #pragma unroll
       for (int u = 0; u < kMergeSplits; ++u) {
-        const int c = min(c0 + u, nsplit - 1);  // in range; unused if past
+        if (c0 + u >= nsplit) break;  // (uniform over the workgroup)
+        const int c = c0 + u;
         const size_t prow = slots.row(c, rr[k]);
         ml[k][u] = *reinterpret_cast<const f32x2*>(p.part_ml + prow * 2);
         oc[k][u] = *reinterpret_cast<const f16x4*>(p.part_o + prow * kHeadDim +
