@@ -113,8 +113,11 @@ int main() {
               continue;
             }
             const long long T = (long long)P + B;
-            EXPECT_EQ(info[0], 8);
-            EXPECT_EQ(info[1] == 128 || info[1] == 256, 1);
+            // 64-row blocks run four waves, 128- and 256-row blocks eight
+            EXPECT_EQ(info[0], info[1] == 64 ? 4 : 8);
+            EXPECT_EQ(info[1] == 64 || info[1] == 128 || info[1] == 256, 1);
+            const int G = h[0] / h[1];
+            EXPECT_EQ(info[1] != 64 || G * B <= 128, 1);
             EXPECT_EQ(info[3] % 64, 0);
             EXPECT_EQ((long long)info[2] * info[3] >= T, 1);
             EXPECT_EQ((long long)(info[2] - 1) * info[3] < T, 1);

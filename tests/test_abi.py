@@ -102,12 +102,12 @@ def test_workspace_size_rules():
     ws4 = api.workspace_size(1, 16, 8, 2, 128, 1024, 16, 16, 4)
     assert ws1 == 0
     # 64 KB of arrival counters, then one slot of partial rows per work
-    # unit (4 splits x 2 kv heads x 1 row block of 128 rows): per row the
-    # fp16 output (256 B) and two 32-bit statistics, each part rounded up
-    # to 256 B
+    # unit (4 splits x 2 kv heads x 1 row block of 64 rows: pairs of 64
+    # rows take 64-row blocks): per row the fp16 output (256 B) and two
+    # 32-bit statistics, each part rounded up to 256 B
     plan = api.describe_plan(1, 16, 8, 2, 128, 1024, 16, 16, 4)
-    assert plan["rows"] == 128 and plan["splits"] == 4
-    rows = 4 * 2 * 128
+    assert plan["rows"] == 64 and plan["splits"] == 4
+    rows = 4 * 2 * 64
     part_o = -(-rows * 256 // 256) * 256
     part_ml = -(-rows * 8 // 256) * 256
     assert ws4 == 65536 + part_o + part_ml
@@ -115,15 +115,18 @@ def test_workspace_size_rules():
     assert api.workspace_size(1, 16, 8, 2, 128, 256, 16, 12, 0) == 0  # page
     # tiny pages force more splits (each split's page slice is bounded)
     assert api.workspace_size(1, 16, 8, 2, 128, 5000, 16, 1, 1) >= \
-        5 * 2 * 128 * (128 * 2 + 2 * 4)
+        5 * 2 * 64 * (128 * 2 + 2 * 4)
 
 
 def test_describe_plan():
-    # small work: 128-row blocks (eight waves: four row groups x two key
-    # halves); the key range is split to fill the CUs
+    # pairs of at most 64 rows: 64-row blocks (four waves)
     p = api.describe_plan(1, 16, 8, 2, 128, 256, 16, 16, 0)
-    assert p["waves"] == 8 and p["rows"] == 128 and p["splits"] >= 1
+    assert p["waves"] == 4 and p["rows"] == 64 and p["splits"] >= 1
     assert p["chunk"] % 64 == 0 and p["chunk"] * p["splits"] >= 256 + 16
+    # 96 rows per pair: 128-row blocks (eight waves: four row groups x two
+    # key halves); the key range is split to fill the CUs
+    p = api.describe_plan(1, 24, 8, 2, 128, 2048, 24, 16, 0)
+    assert p["waves"] == 8 and p["rows"] == 128 and p["splits"] > 1
     # 1024 rows per kv head and one long split: eight waves
     p = api.describe_plan(4, 1024, 32, 8, 128, 32768, 256, 16, 0)
     assert p["waves"] == 8 and p["rows"] == 256 and p["splits"] == 2
@@ -187,7 +190,8 @@ def test_plan_invariants_random_shapes():
         assert (p["chunk"] - 64) * p["splits"] < T or p["splits"] == 1, args
         assert (p["waves"], p["rows"]) in ((4, 64), (8, 128), (8, 256)), args
         if p["rows"] == 64:
-            assert p["splits"] == 1 and G * max_b <= 128, args
+            assert G * max_b <= 64 or (p["splits"] == 1 and
+                                       G * max_b <= 128), args
         if p["rows"] == 256:
             assert G * max_b >= 256 and p["chunk"] >= 2048, args
         if splits > 0:

@@ -193,6 +193,13 @@ int make_plan(int S, int N, int Hq, int Hkv, int max_prefix_len,
       if (st != TREE_ATTN_OK) return st;
     }
   }
+  // Pairs of at most 64 rows: a 128-row block would run half its waves on
+  // rows that do not exist, so 64-row blocks take them (with or without a
+  // split of the key range).
+  if (rpw == kRowsPerWG128 && rows <= kRowsPerWG64) {
+    const int st = choose(kRowsPerWG64);
+    if (st != TREE_ATTN_OK) return st;
+  }
   pl.splits = (int)splits;
   pl.chunk = (int)chunk;
   pl.max_chunk = (int)max_chunk;
