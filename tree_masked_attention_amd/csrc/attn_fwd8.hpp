@@ -242,21 +242,30 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
       }
       return;
     }
+    // The lane's row and chunk are derived again here from an opaque copy
+    // of the lane id: otherwise the compiler keeps the per-lane 64-bit
+    // source pointers of this path live across the whole loop, runs out of
+    // registers and reloads them from scratch, and its wait for those
+    // reloads also waits for every DMA in flight.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int slrow = kFp8 ? ln >> 3 : ln >> 4;
+    const int slchunk = kFp8 ? ln & 7 : ln & 15;
     int pg[kOpsPerMat], slot[kOpsPerMat];
 #pragma unroll
     for (int k = 0; k < kOpsPerMat; ++k) {
-      const int pos = min(w0 + kRowsPerOp * k + lrow, kend - 1);
+      const int pos = min(w0 + kRowsPerOp * k + slrow, kend - 1);
       slot[k] = pos & pmask;
       pg[k] = pg_lds[clampi((pos >> p.log2_page) - lp0, 0, kPageCache - 1)];
     }
 #pragma unroll
     for (int k = 0; k < kOpsPerMat; ++k) {
-      const int row = kDmaRows * wave + kRowsPerOp * k + lrow;
+      const int row = kDmaRows * wave + kRowsPerOp * k + slrow;
       const size_t off = (size_t)(unsigned)pg[k] * page_bytes +
                          (unsigned)slot[k] * tok_bytes + g * kRowB;
       const unsigned dst = st + (wave * kOpsPerMat + k) * 1024;
-      dma16(kbase + off + (k_chunk(lchunk, row) << 4), dst);
-      dma16(vbase + off + (v_chunk(lchunk, row) << 4), dst + kVOff);
+      dma16(kbase + off + (k_chunk(slchunk, row) << 4), dst);
+      dma16(vbase + off + (v_chunk(slchunk, row) << 4), dst + kVOff);
     }
   };
 
