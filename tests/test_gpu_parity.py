@@ -249,6 +249,41 @@ def test_sixty_four_row_parity(name):
     assert_parity(two, ref_out, ref_lse, f"{name}, 2 splits")
 
 
+# Pairs of at most 64 query rows take 64-row blocks whatever the split
+# count: the planned launch (balanced over the sequences) and forced
+# uniform splits, with the merge of the last split workgroup.
+SIXTY_FOUR_ROW_SPLIT_CASES = {
+    "r64s-g4-b16": lambda: _r64("r64s-g4-b16", 165, prefix_lens=[5000] * 4,
+                                tree_sizes=[16], num_q_heads=16,
+                                num_kv_heads=4),
+    "r64s-ragged": lambda: _r64("r64s-ragged", 166, prefix_range=(300, 7000),
+                                num_seqs=6, tree_sizes=[1 + (5 * s) % 16
+                                                        for s in range(6)],
+                                num_q_heads=16, num_kv_heads=4),
+    "r64s-g8-b8-page4": lambda: _r64("r64s-g8-b8-page4", 167,
+                                     prefix_range=(2000, 3000), num_seqs=3,
+                                     tree_sizes=[8], page_size=4),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SIXTY_FOUR_ROW_SPLIT_CASES))
+def test_sixty_four_row_split_parity(name):
+    import tree_masked_attention_amd.api as api
+    wl = SIXTY_FOUR_ROW_SPLIT_CASES[name]()
+    ref_out, ref_lse = oracle.workload_attention(wl)
+    for req in (0, 3):
+        plan = api.describe_plan(wl.num_seqs, wl.total_nodes,
+                                 wl.num_q_heads, wl.num_kv_heads, 128,
+                                 wl.max_prefix_len, wl.max_nodes,
+                                 wl.page_size, req)
+        say(f"[gpu] 64-row split case {name}, requested {req}: plan {plan}")
+        assert plan["rows"] == 64 and plan["waves"] == 4
+        assert plan["splits"] > 1
+        got = run_gpu(wl, num_splits=req)
+        assert np.array_equal(got["masks"], oracle.workload_masks(wl))
+        assert_parity(got, ref_out, ref_lse, f"{name}, requested {req}")
+
+
 # --------------------------------------------------------------------------
 # the five standard workloads at full size, planned launch (as benchmarked)
 # --------------------------------------------------------------------------
