@@ -121,8 +121,9 @@ size_t partials_bytes(size_t rows_all, int D, size_t* part_ml_off) {
 // Launch planning from host-side bounds only (no device-to-host copy).
 // Row blocks: 256 rows (8 waves of 32 rows) when a (sequence, kv head)
 // pair has at least 256 rows and a workgroup gets a long key range, else
-// 128 rows (8 waves: 4 row groups x 2 key halves); either way one workgroup
-// fills a CU's LDS.  The key range [0, max_prefix_len + max_nodes) is cut into
+// 128 rows (8 waves: 4 row groups x 2 key halves), or 64 rows (4 waves)
+// for pairs of at most 64 rows and for bandwidth-bound launches in which
+// 64-row blocks fill the CUs without a split; any shape takes a CU's LDS.  The key range [0, max_prefix_len + max_nodes) is cut into
 // splits so that the grid offers about one workgroup per CU, with at least
 // 256 keys per split, and each split's page-table slice fits the kernel's
 // LDS page cache.
