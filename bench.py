@@ -853,11 +853,12 @@ class VerifyBench:
         self.f_mask = api._lib.tree_attn_build_mask
         self.f_ver = (api._lib.tree_attn_verify_ex if self.variant
                       else api._lib.tree_attn_verify)
-        if self.variant and d != 128:
+        if self.variant and d != 128 and wl.kv_format != "bf16":
             self.plan = {"kernel": "attn_var_kernel (+ attn_var_merge_kernel)",
                          "rows": 128, "workspace_bytes": self.ws_bytes}
         elif self.variant:
-            # fp8 K/V, head dim 128: the tuned kernels' 128- and 64-row shapes
+            # fp8 K/V with head dim 128, bf16 K/V with head dim 64: the tuned
+            # kernels (the standard workloads' plans merge in the kernel)
             self.plan = api.describe_plan_ex(kvd, S, N, Hq, wl.num_kv_heads,
                                              d, wl.max_prefix_len,
                                              wl.max_nodes, wl.page_size,

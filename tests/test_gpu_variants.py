@@ -233,6 +233,56 @@ def test_fp8_tuned_parity(name):
     check(wl, f"{name}, 3 splits", num_splits=3)
 
 
+# bf16 K/V with head dim 64 runs the same three tuned kernel shapes (rows
+# of 128 bytes, like the FP8 tiles of head dim 128)
+def _d64(name, seed, **kw):
+    kw.setdefault("num_q_heads", 32)
+    kw.setdefault("num_kv_heads", 4)
+    return make_workload(seed, name=name, kv_format="bf16", head_dim=64,
+                         **kw)
+
+
+D64_TUNED_CASES = {
+    "d64-r64-ragged": (lambda: _d64("d64-r64", 180, prefix_range=(0, 900),
+                                    num_seqs=32,
+                                    tree_sizes=[1 + (7 * s) % 16
+                                                for s in range(32)]), 64),
+    "d64-r64-split": (lambda: _d64("d64-r64s", 181, prefix_lens=[5000] * 4,
+                                   tree_sizes=[16], num_q_heads=16), 64),
+    "d64-balanced": (lambda: _d64("d64-bal", 182,
+                                  prefix_lens=[300, 4000, 9000],
+                                  tree_sizes=[40, 9, 70], num_q_heads=8,
+                                  num_kv_heads=2), 128),
+    "d64-page4-chain": (lambda: _d64("d64-p4", 183, prefix_lens=[2500],
+                                     tree_sizes=[100], page_size=4,
+                                     num_q_heads=8, num_kv_heads=2,
+                                     tree_rules="chain"), 128),
+    "d64-r256-balanced": (lambda: _d64("d64-r256", 185,
+                                       prefix_lens=[16000, 9000],
+                                       tree_sizes=[64, 70],
+                                       num_kv_heads=8), 256),
+    "d64-r256-page4": (lambda: _d64("d64-r256-p4", 186, prefix_lens=[3900],
+                                    tree_sizes=[64], page_size=4,
+                                    num_q_heads=16), 256),
+}
+
+
+@pytest.mark.parametrize("name", sorted(D64_TUNED_CASES))
+def test_d64_tuned_parity(name):
+    import tree_masked_attention_amd.api as api
+    make, rows = D64_TUNED_CASES[name]
+    wl = make()
+    req = 1 if name == "d64-r256-page4" else 0
+    plan = api.describe_plan_ex(api.KV_BF16, wl.num_seqs, wl.total_nodes,
+                                wl.num_q_heads, wl.num_kv_heads, 64,
+                                wl.max_prefix_len, wl.max_nodes,
+                                wl.page_size, req)
+    say(f"[gpu] bf16 d=64 tuned {name}: plan {plan}")
+    assert plan["rows"] == rows
+    check(wl, name, num_splits=req)
+    check(wl, f"{name}, 3 splits", num_splits=3)
+
+
 @pytest.mark.parametrize("page", [4, 16])
 def test_fp8_256_rows_one_split(page):
     # one split of 3964 keys on the 256-row kernel (within the 1039 page

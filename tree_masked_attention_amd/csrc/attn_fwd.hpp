@@ -80,7 +80,7 @@ struct FwdParams {
   const uint64_t* masks;
   __bf16* out;
   float* lse;
-  _Float16* part_o;  // [units][rows per workgroup][128] partial outputs
+  _Float16* part_o;  // [units][rows per workgroup][head dim] partials
   float* part_ml;    // [units][rows per workgroup][2] split statistics
   const float* k_scale;  // fp8 K/V: [Hkv] scale of the cached codes, or
   const float* v_scale;  // null (1); unused for bf16
@@ -159,15 +159,17 @@ __device__ __forceinline__ void store_rows_staged(const u32x2 (&pk)[16],
   }
 }
 
-// Same for one half of each row: the wave's 32 rows of 64 two-byte values
-// (pk[c] = columns 8c + 4 half .. +3 of the half), staged at stg (4 KB)
-// and stored as 128-byte half rows at byte offset 128 * hh of each 256-byte
-// row, 8 half rows per instruction.
+// Same for 64 two-byte values per row: the wave's 32 rows (pk[c] =
+// columns 8c + 4 half .. +3 of the 64), staged at stg (4 KB) and stored as
+// 128-byte segments at byte offset 128 * hh of rows row_bytes apart (half
+// rows of 256-byte rows, or whole rows of 64 values), 8 rows per
+// instruction.
 __device__ __forceinline__ void store_half_rows_staged(const u32x2 (&pk)[8],
                                                        unsigned stg, int row,
                                                        int hh, char* base,
                                                        int lane,
-                                                       bool coherent = false) {
+                                                       bool coherent = false,
+                                                       int row_bytes = 256) {
   const int col = lane & 31, half = lane >> 5;
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
@@ -181,7 +183,45 @@ __device__ __forceinline__ void store_half_rows_staged(const u32x2 (&pk)[8],
                                                 ((ch ^ (rr & 7)) << 4));
     const int dr = __shfl(row, rr);
     if (dr >= 0) {
-      char* dst = base + (size_t)dr * 256 + hh * 128 + ch * 16;
+      char* dst = base + (size_t)dr * row_bytes + hh * 128 + ch * 16;
+      if (coherent) {
+        asm volatile("global_store_dwordx4 %0, %1, off sc1"
+                     :: "v"(dst), "v"(v) : "memory");
+      } else {
+        *reinterpret_cast<u32x4*>(dst) = v;
+      }
+    }
+  }
+}
+
+// Same for a wave's 32 rows of NC * 8 two-byte values (pk[c] = columns
+// 8c + 4 half .. +3), staged at stg (NC * 512 bytes) and stored as
+// NC * 16-byte segments at base + row * row_bytes, 64 / NC rows per
+// instruction.
+template <int NC>
+__device__ __forceinline__ void store_seg_rows_staged(const u32x2 (&pk)[NC],
+                                                      unsigned stg, int row,
+                                                      char* base,
+                                                      int row_bytes, int lane,
+                                                      bool coherent) {
+  static_assert(NC == 2 || NC == 4 || NC == 8 || NC == 16, "segment");
+  constexpr int RPI = 64 / NC;  // rows per instruction
+  const int col = lane & 31, half = lane >> 5;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    lds_write8(stg + col * (NC * 16) + ((c ^ (col & (NC - 1))) << 4) +
+                   half * 8,
+               pk[c]);
+  }
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int k = 0; k < 32 / RPI; ++k) {
+    const int rr = RPI * k + lane / NC, ch = lane % NC;
+    const u32x4 v = *(const lds_u32x4*)(size_t)(stg + rr * (NC * 16) +
+                                                ((ch ^ (rr & (NC - 1))) << 4));
+    const int dr = __shfl(row, rr);
+    if (dr >= 0) {
+      char* dst = base + (size_t)dr * row_bytes + ch * 16;
       if (coherent) {
         asm volatile("global_store_dwordx4 %0, %1, off sc1"
                      :: "v"(dst), "v"(v) : "memory");
@@ -265,12 +305,12 @@ __device__ __forceinline__ void apply_tile_mask(f32x16 (&S)[2], uint64_t allow,
 // Epilogue of a split workgroup of a launch that merges its own partials
 // (merge_if_last_rows): unit un, rows [r0, r0 + rows_per_wg) of its pair;
 // RT rows per thread in the merge's rounds of loads.
-template <int NT, int RT = 4>
+template <int NT, int RT = 4, int D = kHeadDim>
 __device__ __forceinline__ void merge_if_last(const FwdParams& p,
                                               const Unit& un, int rows,
                                               int r0, int rows_per_wg,
                                               int tid, int* flag_lds) {
-  merge_if_last_rows<NT, kHeadDim, RT>(
+  merge_if_last_rows<NT, D, RT>(
       p.counters + un.seg, un.nsplit, p.part_o, p.part_ml, p.out, p.lse,
       p.Hq, p.G, un.g, un.a, r0, min(r0 + rows_per_wg, rows),
       PartSlots{un.slot0, un.mblocks, rows_per_wg, r0}, tid, flag_lds);

@@ -29,15 +29,24 @@ constexpr int kRowsPerWG64 = 64;
 // 8 KB of O, 512 B of statistics and 128 B of row maxima per wave)
 constexpr int kEpilogueStage = 72 * 1024;
 
-template <int NW, bool kBalanced, bool kFp8>
+template <int NW, bool kBalanced, bool kFp8, int D = kHeadDim>
 __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
   static_assert(NW == 8 || NW == 4, "shape");
+  static_assert(D == kHeadDim || (D == 64 && !kFp8), "head dim");
   constexpr int kRows = 16 * NW;         // query rows per workgroup
   constexpr int kThreads = NW * 64;
   constexpr int kEB = kFp8 ? 1 : 2;      // bytes per cached element
-  constexpr int kRowB = kHeadDim * kEB;  // bytes per cached (token, head)
+  constexpr int kRowB = D * kEB;         // bytes per cached (token, head)
+  // 128-byte rows (fp8 with d = 128, bf16 with d = 64): 8 chunks of 16
+  // bytes per row, 8 rows per DMA op
+  constexpr bool kNarrow = kRowB == 128;
+  constexpr int kKSteps = D / 16;        // MFMA k-steps over the head dim
+  constexpr int kDB = D / 32;            // 32-wide head-dim blocks of O
+  constexpr int kHalfDB = kDB / 2;       // the blocks a wave finishes
+  // Q staging DMA ops per wave (bf16 rows of D values, 1 KB per op)
+  constexpr int kQOps = kRows * D * 2 / 1024 / NW;
   // 1-KB DMA ops per wave per matrix: each moves 4 bf16 or 8 fp8 rows
-  constexpr int kOpsPerMat = (kFp8 ? 8 : 16) / NW;
+  constexpr int kOpsPerMat = (kRowB / 16) / NW;
   constexpr int kOps = 2 * kOpsPerMat;
   constexpr int kRowsPerOp = 1024 / kRowB;
   constexpr int kDmaRows = kRowsPerOp * kOpsPerMat;  // tile rows a wave moves
@@ -70,7 +79,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
       (unsigned)(size_t)(__attribute__((address_space(3))) uint64_t*)mk_lds;
   const int lrow = lane >> 4, lchunk = lane & 15;  // Q rows, 16-B chunks
   // a lane's row and 16-byte chunk within one K/V DMA op
-  const int drow = kFp8 ? lane >> 3 : lrow, dchunk = kFp8 ? lane & 7 : lchunk;
+  const int drow = kNarrow ? lane >> 3 : lrow, dchunk = kNarrow ? lane & 7 : lchunk;
 
   // Prologue, two rounds of memory latency before the first tile's scores:
   // (1) the split's page-table entries go to LDS by DMA while the tree
@@ -117,26 +126,36 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
   const int node = rvalid ? r / p.G : n_hi;
   const size_t qrow =
       (size_t)(a + node) * p.Hq + g * p.G + (rvalid ? r % p.G : 0);
-  bf16x8 qf[8];  // Q^T fragments (B operand): d = kc*16 + half*8 + 0..7,
+  bf16x8 qf[kKSteps];  // Q^T fragments (B operand): d = kc*16 + half*8 + 0..7,
                  // read from LDS once the prologue DMA has landed
 
-  // Q rows r0 .. r0+kRows-1 (rows past the last one repeat it):
-  // instruction i moves rows 4i .. 4i+3, chunk-swizzled like K; rows 0-63
-  // go to the K half of stage 3, rows 64-127 to its V half
+  // Q rows r0 .. r0+kRows-1 (rows past the last one repeat it), swizzled
+  // like K.  d = 128: instruction i moves rows 4i .. 4i+3; rows 0-63 go to
+  // the K half of stage 3, rows 64-127 to its V half.  d = 64 (128-byte
+  // rows): instruction i moves rows 8i .. 8i+7, all in the K half.
   const unsigned q_lds = ring_base + 3 * kTileBytes;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int i = 4 * wave + k;
-    const int rl = 4 * i + lrow;
-    const int rq = min(r0 + rl, rows - 1);
-    const size_t qr = (size_t)(a + rq / p.G) * p.Hq + g * p.G + rq % p.G;
-    dma16(reinterpret_cast<const char*>(p.q + qr * kHeadDim) +
-              ((lchunk ^ (rl & 15)) << 4),
-          q_lds + (i < 16 ? 0u : (unsigned)kVOff) + ((4 * i) & 63) * 256);
+  for (int k = 0; k < kQOps; ++k) {
+    const int i = kQOps * wave + k;
+    if constexpr (D == 128) {
+      const int rl = 4 * i + lrow;
+      const int rq = min(r0 + rl, rows - 1);
+      const size_t qr = (size_t)(a + rq / p.G) * p.Hq + g * p.G + rq % p.G;
+      dma16(reinterpret_cast<const char*>(p.q + qr * D) +
+                ((lchunk ^ (rl & 15)) << 4),
+            q_lds + (i < 16 ? 0u : (unsigned)kVOff) + ((4 * i) & 63) * 256);
+    } else {
+      const int rl = 8 * i + (lane >> 3);
+      const int rq = min(r0 + rl, rows - 1);
+      const size_t qr = (size_t)(a + rq / p.G) * p.Hq + g * p.G + rq % p.G;
+      dma16(reinterpret_cast<const char*>(p.q + qr * D) +
+                (((lane & 7) ^ ((rl >> 1) & 7)) << 4),
+            q_lds + 8 * i * 128);
+    }
   }
-  // the page-table slice has landed (issued before Q's four ops); Q may
-  // still be in flight
-  wait_vmcnt<4>();
+  // the page-table slice has landed (issued before Q's ops); Q may still
+  // be in flight
+  wait_vmcnt<kQOps>();
   __syncthreads();  // page slice visible
   if (nm > 0) {
     const int nd = 2 * nm;  // dwords
@@ -148,15 +167,21 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
   }
 
   // ---- LDS operand addresses of this wave's key half (stage 0)
-  unsigned k_off[8];
+  unsigned k_off[kKSteps];
 #pragma unroll
-  for (int kc = 0; kc < 8; ++kc) {
+  for (int kc = 0; kc < kKSteps; ++kc) {
     if constexpr (kFp8) {
       // fp8 rows of 128 B, 16-byte chunk c stored at c ^ ((row >> 1) & 7);
       // the lane's 8 values d = kc*16 + half*8 .. +7 are half of chunk kc
       const int row = kh * 32 + col;
       k_off[kc] = ring_base + row * 128 + ((kc ^ ((row >> 1) & 7)) << 4) +
                   half * 8;
+    } else if constexpr (kNarrow) {
+      // bf16 rows of 128 B (d = 64), the same swizzle; the lane's 8
+      // values are chunk 2 kc + half
+      const int row = kh * 32 + col;
+      k_off[kc] = ring_base + row * 128 +
+                  (((2 * kc + half) ^ ((row >> 1) & 7)) << 4);
     } else {
       k_off[kc] = ring_base + (kh * 32 + col) * 256 +
                   (((2 * kc + half) ^ (col & 15)) << 4);
@@ -164,9 +189,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
   }
   const int y = (lane & 15) >> 2;
   const int x = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-  unsigned v_off[4];
+  unsigned v_off[kDB];
 #pragma unroll
-  for (int db = 0; db < 4; ++db) {
+  for (int db = 0; db < kDB; ++db) {
     if constexpr (kFp8) {
       // ds_read_b64_tr_b8: in each group of 16 lanes, lanes 2r and 2r+1
       // name bytes 0-7 and 8-15 of "row" r (r = 0..7), and lane i of the
@@ -178,6 +203,12 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
       const int chunk = 2 * db + ((lane >> 4) & 1);
       v_off[db] = ring_base + kVOff + row * 128 +
                   ((chunk ^ ((row >> 1) & 7)) << 4) + 8 * (j & 1);
+    } else if constexpr (kNarrow) {
+      // bf16 rows of 128 B (d = 64): chunk c stored at c ^ 4 ((row >> 1) & 1)
+      const int row = kh * 32 + 4 * half + y;
+      v_off[db] = ring_base + kVOff + row * 128 +
+                  (((4 * db + x) ^ (4 * ((row >> 1) & 1))) << 4) +
+                  8 * (lane & 1);
     } else {
       v_off[db] = ring_base + kVOff + (kh * 32 + 4 * half + y) * 256 +
                   ((4 * (db ^ y) + x) << 4) + 8 * (lane & 1);
@@ -194,13 +225,16 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
   // page ids are clamped to the cache when used (the table is not checked)
   const unsigned pg_last = (unsigned)max(p.num_pages - 1, 0);
   // source chunk of the lane's 16 bytes (the LDS chunk is fixed by the
-  // lane): bf16 K chunk ^ (row & 15), bf16 V chunk ^ 4 (row & 3) (for the
-  // 16-bit transposing reads), fp8 K and V chunk ^ ((row >> 1) & 7)
+  // lane): 256-byte rows K chunk ^ (row & 15), V chunk ^ 4 (row & 3) (for
+  // the 16-bit transposing reads); 128-byte rows K chunk ^ ((row >> 1) & 7),
+  // V the same for fp8 and chunk ^ 4 ((row >> 1) & 1) for bf16
   auto k_chunk = [](int c, int row) -> unsigned {
-    return (unsigned)(kFp8 ? c ^ ((row >> 1) & 7) : c ^ (row & 15));
+    return (unsigned)(kNarrow ? c ^ ((row >> 1) & 7) : c ^ (row & 15));
   };
   auto v_chunk = [](int c, int row) -> unsigned {
-    return (unsigned)(kFp8 ? c ^ ((row >> 1) & 7) : c ^ (4 * (row & 3)));
+    return (unsigned)(kFp8 ? c ^ ((row >> 1) & 7)
+                           : (kNarrow ? c ^ (4 * ((row >> 1) & 1))
+                                      : c ^ (4 * (row & 3))));
   };
   unsigned k_row_off[kOpsPerMat], v_row_off[kOpsPerMat];
 #pragma unroll
@@ -295,11 +329,11 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
     }
   };
 
-  f32x16 o[4];
+  f32x16 o[kDB];
   float l_run = 0.f;        // this lane half's share of the row sum
   float m_ref = -INFINITY;  // reference max, log2 units
 #pragma unroll
-  for (int db = 0; db < 4; ++db) o[db] = f32x16{};
+  for (int db = 0; db < kDB; ++db) o[db] = f32x16{};
   // fp8: the cached values stand for code * scale[g]; the K scale folds
   // into the score scale, the V scale into the output normalisation
   float c2 = p.scale_log2;
@@ -313,9 +347,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
   // the head dimension; the other wave of the SIMD fills its latency)
   auto qk_half = [&](int t, f32x16& S) {
     const unsigned so = (unsigned)(t & (kStages - 1)) * kTileBytes;
-    bf16x8 kf[8];
+    bf16x8 kf[kKSteps];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
+    for (int c = 0; c < kKSteps; ++c) {
       if constexpr (kFp8) {
         kf[c] = e4m3x8_to_bf16(lds_read8(k_off[c] + so));
       } else {
@@ -324,28 +358,28 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
     }
     S = f32x16{};
 #pragma unroll
-    for (int c = 0; c < 8; ++c) S = mfma32x32x16(kf[c], qf[c], S);
+    for (int c = 0; c < kKSteps; ++c) S = mfma32x32x16(kf[c], qf[c], S);
   };
   // O^T += V^T P^T over this wave's key half of tile t
   auto pv_half = [&](int t, const bf16x8 (&pf)[2]) {
     const unsigned so = (unsigned)(t & (kStages - 1)) * kTileBytes;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      bf16x8 vf[4];
+      bf16x8 vf[kDB];
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
+      for (int db = 0; db < kDB; ++db) {
         if constexpr (kFp8) {
           vf[db] = e4m3x8_to_bf16(lds_read_tr8(v_off[db] + so + hf * 16 * 128));
         } else {
-          const unsigned va = v_off[db] + so + hf * 16 * 256;
+          const unsigned va = v_off[db] + so + hf * 16 * kRowB;
           const s16x4 lo = lds_read_tr(va);
-          const s16x4 hi = lds_read_tr(va + 8 * 256);
+          const s16x4 hi = lds_read_tr(va + 8 * kRowB);
           vf[db] = __builtin_bit_cast(
               bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         }
       }
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
+      for (int db = 0; db < kDB; ++db) {
         o[db] = mfma32x32x16(vf[db], pf[hf], o[db]);
       }
     }
@@ -418,7 +452,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
     if (__any(r)) {
       l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] *= alpha;
+      for (int db = 0; db < kDB; ++db) o[db] *= alpha;
     }
     m_ref = m_new;
   };
@@ -463,10 +497,19 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
   __syncthreads();
   {
     const int rl = rg * 32 + col;
-    const unsigned qa = q_lds + (rg < 2 ? 0u : (unsigned)kVOff) + (rl & 63) * 256;
+    if constexpr (D == 128) {
+      const unsigned qa =
+          q_lds + (rg < 2 ? 0u : (unsigned)kVOff) + (rl & 63) * 256;
 #pragma unroll
-    for (int kc = 0; kc < 8; ++kc) {
-      qf[kc] = lds_read16(qa + (((2 * kc + half) ^ (col & 15)) << 4));
+      for (int kc = 0; kc < kKSteps; ++kc) {
+        qf[kc] = lds_read16(qa + (((2 * kc + half) ^ (col & 15)) << 4));
+      }
+    } else {
+      const unsigned qa = q_lds + rl * 128;
+#pragma unroll
+      for (int kc = 0; kc < kKSteps; ++kc) {
+        qf[kc] = lds_read16(qa + (((2 * kc + half) ^ ((rl >> 1) & 7)) << 4));
+      }
     }
   }
   f32x16 SA, SB;
@@ -498,24 +541,26 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
   }
 
   // ---- combine the two key halves.  Wave (rg, kh) finishes head-dim half
-  // kh (O^T blocks 2 kh, 2 kh + 1) of its 32 rows: it hands the other two
-  // blocks and its (max, row sum) to the partner wave (rg, 1 - kh) through
-  // LDS and takes the partner's share of its own two, so both waves of a
-  // row group do half of the epilogue.
+  // kh (O^T blocks kh kHalfDB .. +kHalfDB-1) of its 32 rows: it hands the
+  // other blocks and its (max, row sum) to the partner wave (rg, 1 - kh)
+  // through LDS and takes the partner's share of its own, so both waves of
+  // a row group do half of the epilogue.
   float l_tot = l_run + other_half(l_run);
   // (selected by a wave-uniform branch: indexing o[] by kh would put the
   // array in scratch memory)
-  f32x16 o_own[2], o_give[2];
+  f32x16 o_own[kHalfDB], o_give[kHalfDB];
   if (kh == 0) {
-    o_own[0] = o[0];
-    o_own[1] = o[1];
-    o_give[0] = o[2];
-    o_give[1] = o[3];
+#pragma unroll
+    for (int b = 0; b < kHalfDB; ++b) {
+      o_own[b] = o[b];
+      o_give[b] = o[kHalfDB + b];
+    }
   } else {
-    o_own[0] = o[2];
-    o_own[1] = o[3];
-    o_give[0] = o[0];
-    o_give[1] = o[1];
+#pragma unroll
+    for (int b = 0; b < kHalfDB; ++b) {
+      o_own[b] = o[kHalfDB + b];
+      o_give[b] = o[b];
+    }
   }
   __syncthreads();  // every wave is done with the ring
   {
@@ -523,7 +568,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
     float* xml_out = reinterpret_cast<float*>(ring) + NW * (8 * 64 * 4) +
                      wave * 128;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
+    for (int b = 0; b < kHalfDB; ++b) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         *reinterpret_cast<f32x4*>(xo_out + ((b * 4 + g4) * 64 + lane) * 4) =
@@ -549,9 +594,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
   const float a0 = mx == -INFINITY ? 0.f : fast_exp2(m0 - mx);
   const float a1 = mx == -INFINITY ? 0.f : fast_exp2(m1 - mx);
   const float a_own = kh == 0 ? a0 : a1, a_p = kh == 0 ? a1 : a0;
-  f32x16 oc[2];
+  f32x16 oc[kHalfDB];
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
+  for (int b = 0; b < kHalfDB; ++b) {
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const f32x4 u =
@@ -572,24 +617,32 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
   // the exchange area so that the stores write whole half rows
   const float inv = l_tot > 0.f ? v_sc / l_tot : 0.f;
   const unsigned stg = ring_base + kEpilogueStage + wave * 4096;
-  u32x2 pk[8];
+  u32x2 pk[4 * kHalfDB];
+  // this wave's half of each row (d = D/2 kh + 8c + 4 half .. +3 from pk)
+  auto store_half = [&](int row, char* base, bool coherent) {
+    if constexpr (D == 128) {
+      store_half_rows_staged(pk, stg, row, kh, base, lane, coherent);
+    } else {
+      store_seg_rows_staged<4>(pk, stg, row, base + kh * 64, D * 2, lane,
+                               coherent);
+    }
+  };
   if (un.nsplit == 1) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
+    for (int c = 0; c < 4 * kHalfDB; ++c) {
       bf16x4 v4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(oc[c >> 2][(c & 3) * 4 + e] * inv);
       pk[c] = __builtin_bit_cast(u32x2, v4);
     }
-    store_half_rows_staged(pk, stg, rvalid ? (int)qrow : -1, kh,
-                           reinterpret_cast<char*>(p.out), lane);
+    store_half(rvalid ? (int)qrow : -1, reinterpret_cast<char*>(p.out), false);
     if (kh == 0 && half == 0 && rvalid) {
       p.lse[qrow] = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
     }
   } else {
     float amax = 0.f;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
+    for (int b = 0; b < kHalfDB; ++b) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         amax = __builtin_elementwise_maximum(amax, __builtin_fabsf(oc[b][e]));
@@ -602,7 +655,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
     amax = __builtin_elementwise_maximum(amax, xam[partner * 32 + col]);
     const int ex = f16_row_exp(amax * inv);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
+    for (int c = 0; c < 4 * kHalfDB; ++c) {
       f16x4 v4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -612,9 +665,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
     }
     // the unit's partial slot: its rows in row-block order
     const size_t prow0 = (size_t)L * kRows;
-    store_half_rows_staged(pk, stg, rvalid ? r - r0 : -1, kh,
-                           reinterpret_cast<char*>(p.part_o + prow0 * kHeadDim),
-                           lane, p.counters != nullptr);
+    store_half(rvalid ? r - r0 : -1,
+               reinterpret_cast<char*>(p.part_o + prow0 * D),
+               p.counters != nullptr);
     if (kh == 0 && half == 0 && rvalid) {
       float* dst = p.part_ml + (prow0 + (r - r0)) * 2;
       const uint64_t st = pack_split_stats(split_lse2(m_ref, l_tot), ex);
@@ -626,7 +679,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
     }
   }
   if (p.counters != nullptr && un.nsplit > 1) {
-    merge_if_last<kThreads>(p, un, rows, r0, kRows, tid, pg_lds);
+    merge_if_last<kThreads, 4, D>(p, un, rows, r0, kRows, tid, pg_lds);
   }
 }
 

@@ -19,15 +19,21 @@ namespace tree_attn {
 
 constexpr int kRowsPerWG8 = 256;
 
-template <bool kBalanced, bool kFp8>
+template <bool kBalanced, bool kFp8, int D = kHeadDim>
 __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
+  static_assert(D == kHeadDim || (D == 64 && !kFp8), "head dim");
   constexpr int NW = 8;
   constexpr int QB = 1;                  // 32-query blocks per wave
   constexpr int kThreads = NW * 64;
   constexpr int kEB = kFp8 ? 1 : 2;      // bytes per cached element
-  constexpr int kRowB = kHeadDim * kEB;  // bytes per cached (token, head)
-  // 1-KB DMA ops per wave per matrix: each moves 4 bf16 or 8 fp8 rows
-  constexpr int kOpsPerMat = (kFp8 ? 8 : 16) / NW;
+  constexpr int kRowB = D * kEB;         // bytes per cached (token, head)
+  // 128-byte rows (fp8 with d = 128, bf16 with d = 64): 8 chunks of 16
+  // bytes per row, 8 rows per DMA op
+  constexpr bool kNarrow = kRowB == 128;
+  constexpr int kKSteps = D / 16;        // MFMA k-steps over the head dim
+  constexpr int kDB = D / 32;            // 32-wide head-dim blocks of O
+  // 1-KB DMA ops per wave per matrix: each moves 4 or 8 rows
+  constexpr int kOpsPerMat = (kRowB / 16) / NW;
   constexpr int kOps = 2 * kOpsPerMat;
   constexpr int kRowsPerOp = 1024 / kRowB;
   constexpr int kDmaRows = kRowsPerOp * kOpsPerMat;  // tile rows a wave moves
@@ -109,7 +115,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
   bool rvalid[QB];
   int node[QB];
   size_t qrow[QB];
-  bf16x8 qf[QB][8];  // Q^T fragments (B operand): d = kc*16 + half*8 + 0..7
+  bf16x8 qf[QB][kKSteps];  // Q^T fragments (B operand): d = kc*16 + half*8 + 0..7
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int r = r0 + (wave * QB + qb) * 32 + col;
@@ -117,9 +123,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
     node[qb] = rvalid[qb] ? r / p.G : n_hi;
     qrow[qb] = (size_t)(a + node[qb]) * p.Hq + g * p.G +
                (rvalid[qb] ? r % p.G : 0);
-    const __bf16* qp = p.q + qrow[qb] * kHeadDim + half * 8;
+    const __bf16* qp = p.q + qrow[qb] * D + half * 8;
 #pragma unroll
-    for (int kc = 0; kc < 8; ++kc) {
+    for (int kc = 0; kc < kKSteps; ++kc) {
       u32x4 raw = rvalid[qb] ? *reinterpret_cast<const u32x4*>(qp + kc * 16)
                              : u32x4{0, 0, 0, 0};
       qf[qb][kc] = __builtin_bit_cast(bf16x8, raw);
@@ -141,24 +147,29 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
   // ---- LDS operand addresses (stage 0; the stage offset is added per tile)
   const unsigned ring_base =
       (unsigned)(size_t)(__attribute__((address_space(3))) unsigned char*)ring;
-  unsigned k_off[8];
+  unsigned k_off[kKSteps];
 #pragma unroll
-  for (int kc = 0; kc < 8; ++kc) {
+  for (int kc = 0; kc < kKSteps; ++kc) {
     if constexpr (kFp8) {
       // fp8 rows of 128 B, 16-byte chunk c stored at c ^ ((row >> 1) & 7);
       // the lane's 8 values d = kc*16 + half*8 .. +7 are half of chunk kc
       // (32-key block offsets keep the swizzle: 32 rows = 16 row pairs)
       k_off[kc] = ring_base + col * 128 + ((kc ^ ((col >> 1) & 7)) << 4) +
                   half * 8;
+    } else if constexpr (kNarrow) {
+      // bf16 rows of 128 B (d = 64), the same swizzle; the lane's 8
+      // values are chunk 2 kc + half
+      k_off[kc] = ring_base + col * 128 +
+                  (((2 * kc + half) ^ ((col >> 1) & 7)) << 4);
     } else {
       k_off[kc] = ring_base + col * 256 + (((2 * kc + half) ^ (col & 15)) << 4);
     }
   }
   const int y = (lane & 15) >> 2;
   const int x = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-  unsigned v_off[4];
+  unsigned v_off[kDB];
 #pragma unroll
-  for (int db = 0; db < 4; ++db) {
+  for (int db = 0; db < kDB; ++db) {
     if constexpr (kFp8) {
       // ds_read_b64_tr_b8 (attn_fwd.hpp): lanes 2r, 2r+1 of a 16-lane group
       // name row r = key 8*(r/4) + 4*half + r%4 of the 16-key block
@@ -167,6 +178,13 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
       const int chunk = 2 * db + ((lane >> 4) & 1);
       v_off[db] = ring_base + kVOff + row * 128 +
                   ((chunk ^ ((row >> 1) & 7)) << 4) + 8 * (j & 1);
+    } else if constexpr (kNarrow) {
+      // bf16 rows of 128 B (d = 64): chunk c stored at c ^ 4 ((row >> 1) & 1)
+      // (the four rows a half-wave reads then cover all banks)
+      const int row = 4 * half + y;
+      v_off[db] = ring_base + kVOff + row * 128 +
+                  (((4 * db + x) ^ (4 * ((row >> 1) & 1))) << 4) +
+                  8 * (lane & 1);
     } else {
       v_off[db] = ring_base + kVOff + (4 * half + y) * 256 +
                   ((4 * (db ^ y) + x) << 4) + 8 * (lane & 1);
@@ -179,16 +197,19 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
   const unsigned tok_bytes = (unsigned)p.Hkv * kRowB;
   const unsigned page_bytes = tok_bytes << p.log2_page;
   // a lane's row and 16-byte chunk within one DMA op
-  const int lrow = kFp8 ? lane >> 3 : lane >> 4;
-  const int lchunk = kFp8 ? lane & 7 : lane & 15;
+  const int lrow = kNarrow ? lane >> 3 : lane >> 4;
+  const int lchunk = kNarrow ? lane & 7 : lane & 15;
   // source chunk of the lane's 16 bytes (the LDS chunk is fixed by the
-  // lane): bf16 K chunk ^ (row & 15), bf16 V chunk ^ 4 (row & 3), fp8 K
-  // and V chunk ^ ((row >> 1) & 7)
+  // lane): 256-byte rows K chunk ^ (row & 15), V chunk ^ 4 (row & 3);
+  // 128-byte rows K chunk ^ ((row >> 1) & 7), V the same for fp8 and
+  // chunk ^ 4 ((row >> 1) & 1) for bf16
   auto k_chunk = [](int c, int row) -> unsigned {
-    return (unsigned)(kFp8 ? c ^ ((row >> 1) & 7) : c ^ (row & 15));
+    return (unsigned)(kNarrow ? c ^ ((row >> 1) & 7) : c ^ (row & 15));
   };
   auto v_chunk = [](int c, int row) -> unsigned {
-    return (unsigned)(kFp8 ? c ^ ((row >> 1) & 7) : c ^ (4 * (row & 3)));
+    return (unsigned)(kFp8 ? c ^ ((row >> 1) & 7)
+                           : (kNarrow ? c ^ (4 * ((row >> 1) & 1))
+                                      : c ^ (4 * (row & 3))));
   };
   const char* kbase = reinterpret_cast<const char*>(p.k);
   const char* vbase = reinterpret_cast<const char*>(p.v);
@@ -249,8 +270,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
     // reloads also waits for every DMA in flight.
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    const int slrow = kFp8 ? ln >> 3 : ln >> 4;
-    const int slchunk = kFp8 ? ln & 7 : ln & 15;
+    const int slrow = kNarrow ? ln >> 3 : ln >> 4;
+    const int slchunk = kNarrow ? ln & 7 : ln & 15;
     int pg[kOpsPerMat], slot[kOpsPerMat];
 #pragma unroll
     for (int k = 0; k < kOpsPerMat; ++k) {
@@ -295,13 +316,13 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
     return allow & (pre | tree);
   };
 
-  f32x16 o[QB][4];
+  f32x16 o[QB][kDB];
   float l_run[QB];  // this lane half's share of the row sum
   float m_ref[QB];  // reference max, log2 units
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-    for (int db = 0; db < 4; ++db) o[qb][db] = f32x16{};
+    for (int db = 0; db < kDB; ++db) o[qb][db] = f32x16{};
     l_run[qb] = 0.f;
     m_ref[qb] = -INFINITY;
   }
@@ -323,21 +344,21 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
       if constexpr (kFp8) {
         kf[c] = e4m3x8_to_bf16(lds_read8(k_off[4 * h + c] + so + kb * 32 * 128));
       } else {
-        kf[c] = lds_read16(k_off[4 * h + c] + so + kb * 32 * 256);
+        kf[c] = lds_read16(k_off[4 * h + c] + so + kb * 32 * kRowB);
       }
     }
   };
-  auto read_vq = [&](int t, int kb, int hf, bf16x8 (&vf)[4]) {
+  auto read_vq = [&](int t, int kb, int hf, bf16x8 (&vf)[kDB]) {
     const unsigned so = (unsigned)(t & (kStages - 1)) * kTileBytes;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
+    for (int db = 0; db < kDB; ++db) {
       if constexpr (kFp8) {
         vf[db] = e4m3x8_to_bf16(
             lds_read_tr8(v_off[db] + so + (kb * 32 + hf * 16) * 128));
       } else {
-        const unsigned va = v_off[db] + so + (kb * 32 + hf * 16) * 256;
+        const unsigned va = v_off[db] + so + (kb * 32 + hf * 16) * kRowB;
         const s16x4 lo = lds_read_tr(va);
-        const s16x4 hi = lds_read_tr(va + 8 * 256);
+        const s16x4 hi = lds_read_tr(va + 8 * kRowB);
         vf[db] = __builtin_bit_cast(
             bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
@@ -348,7 +369,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
   auto qk_block = [&](int t, int kb, f32x16 (&S)[QB][2]) {
     bf16x8 kf0[4], kf1[4];
     read_kq(t, kb, 0, kf0);
-    read_kq(t, kb, 1, kf1);
+    if constexpr (kKSteps == 8) read_kq(t, kb, 1, kf1);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) S[qb][kb] = f32x16{};
 #pragma unroll
@@ -358,28 +379,30 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
         S[qb][kb] = mfma32x32x16(kf0[c], qf[qb][c], S[qb][kb]);
       }
     }
+    if constexpr (kKSteps == 8) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < 4; ++c) {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        S[qb][kb] = mfma32x32x16(kf1[c], qf[qb][4 + c], S[qb][kb]);
+        for (int qb = 0; qb < QB; ++qb) {
+          S[qb][kb] = mfma32x32x16(kf1[c], qf[qb][4 + c], S[qb][kb]);
+        }
       }
     }
   };
-  // O^T += V^T P^T over key block kb of tile t (4*QB accumulation chains)
+  // O^T += V^T P^T over key block kb of tile t (kDB*QB accumulation chains)
   auto pv_block = [&](int t, int kb, const bf16x8 (&pf)[QB][2][2]) {
-    bf16x8 vf0[4], vf1[4];
+    bf16x8 vf0[kDB], vf1[kDB];
     read_vq(t, kb, 0, vf0);
     read_vq(t, kb, 1, vf1);
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
+    for (int db = 0; db < kDB; ++db) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         o[qb][db] = mfma32x32x16(vf0[db], pf[qb][kb][0], o[qb][db]);
       }
     }
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
+    for (int db = 0; db < kDB; ++db) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         o[qb][db] = mfma32x32x16(vf1[db], pf[qb][kb][1], o[qb][db]);
@@ -490,7 +513,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
       for (int qb = 0; qb < QB; ++qb) {
         l_run[qb] *= alpha[qb];
 #pragma unroll
-        for (int db = 0; db < 4; ++db) o[qb][db] *= alpha[qb];
+        for (int db = 0; db < kDB; ++db) o[qb][db] *= alpha[qb];
       }
     }
 #pragma unroll
@@ -531,9 +554,14 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
   // wait at the first use of qf would also drain the ring).
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    asm volatile("" :: "v"(qf[qb][0]), "v"(qf[qb][1]), "v"(qf[qb][2]),
-                 "v"(qf[qb][3]), "v"(qf[qb][4]), "v"(qf[qb][5]),
-                 "v"(qf[qb][6]), "v"(qf[qb][7]));
+    if constexpr (kKSteps == 8) {
+      asm volatile("" :: "v"(qf[qb][0]), "v"(qf[qb][1]), "v"(qf[qb][2]),
+                   "v"(qf[qb][3]), "v"(qf[qb][4]), "v"(qf[qb][5]),
+                   "v"(qf[qb][6]), "v"(qf[qb][7]));
+    } else {
+      asm volatile("" :: "v"(qf[qb][0]), "v"(qf[qb][1]), "v"(qf[qb][2]),
+                   "v"(qf[qb][3]));
+    }
   }
   __syncthreads();  // page slice and mask window visible
 #pragma unroll
@@ -590,10 +618,18 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
     const float l_tot = l_run[qb] + other_half(l_run[qb]);
     const float inv = l_tot > 0.f ? v_sc / l_tot : 0.f;
     const unsigned stg = ring_base + (unsigned)(wave * QB + qb) * 8192;
-    u32x2 pk[16];
+    u32x2 pk[4 * kDB];
+    // whole rows of D two-byte values from pk (d = 8c + 4 half .. +3)
+    auto store_rows = [&](int row, char* base, bool coherent) {
+      if constexpr (D == 128) {
+        store_rows_staged(pk, stg, row, base, lane, coherent);
+      } else {
+        store_half_rows_staged(pk, stg, row, 0, base, lane, coherent, 128);
+      }
+    };
     if (un.nsplit == 1) {
 #pragma unroll
-      for (int c = 0; c < 16; ++c) {
+      for (int c = 0; c < 4 * kDB; ++c) {
         bf16x4 v4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -601,8 +637,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
         }
         pk[c] = __builtin_bit_cast(u32x2, v4);
       }
-      store_rows_staged(pk, stg, rvalid[qb] ? (int)qrow[qb] : -1,
-                        reinterpret_cast<char*>(p.out), lane);
+      store_rows(rvalid[qb] ? (int)qrow[qb] : -1,
+                 reinterpret_cast<char*>(p.out), false);
       if (half == 0 && rvalid[qb]) {
         p.lse[qrow[qb]] =
             l_tot > 0.f ? (m_ref[qb] + log2f(l_tot)) * kLn2 : -INFINITY;
@@ -611,7 +647,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
       // scale exponent of the partial row (f16_row_exp)
       float amax = 0.f;
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
+      for (int db = 0; db < kDB; ++db) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           amax = __builtin_elementwise_maximum(amax,
@@ -621,7 +657,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
       const int ex = f16_row_exp(
           __builtin_elementwise_maximum(amax, other_half(amax)) * inv);
 #pragma unroll
-      for (int c = 0; c < 16; ++c) {
+      for (int c = 0; c < 4 * kDB; ++c) {
         f16x4 v4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -632,9 +668,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
       // the unit's partial slot: its rows in row-block order
       const int rl = (wave * QB + qb) * 32 + col;
       const size_t prow0 = (size_t)L * kRowsPerWG8;
-      store_rows_staged(pk, stg, rvalid[qb] ? rl : -1,
-                        reinterpret_cast<char*>(p.part_o + prow0 * kHeadDim),
-                        lane, p.counters != nullptr);
+      store_rows(rvalid[qb] ? rl : -1,
+                 reinterpret_cast<char*>(p.part_o + prow0 * D),
+                 p.counters != nullptr);
       if (half == 0 && rvalid[qb]) {
         float* dst = p.part_ml + (prow0 + rl) * 2;
         const uint64_t st = pack_split_stats(split_lse2(m_ref[qb], l_tot), ex);
@@ -648,7 +684,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
   }
   if (p.counters != nullptr && un.nsplit > 1) {
     // (256 rows: one round of loads, two splits at a time)
-    merge_if_last<kThreads, 8>(p, un, rows, r0, kRowsPerWG8, tid, pg_lds);
+    merge_if_last<kThreads, 8, D>(p, un, rows, r0, kRowsPerWG8, tid, pg_lds);
   }
 }
 

@@ -129,7 +129,7 @@ size_t partials_bytes(size_t rows_all, int D, size_t* part_ml_off) {
 // LDS page cache.
 int make_plan(int S, int N, int Hq, int Hkv, int max_prefix_len,
               int max_nodes, int page_size, int req_splits, int cus,
-              Plan* out) {
+              Plan* out, int head_dim = kHeadDim) {
   Plan pl;
   const int G = Hq / Hkv;
   const long long rows = (long long)G * max_nodes;
@@ -210,7 +210,7 @@ int make_plan(int S, int N, int Hq, int Hkv, int max_prefix_len,
   pl.blocks = (int)units0;
   if (splits > 1) {
     // one slot of partial rows per unit (split_plan.hpp)
-    pl.ws_bytes = partials_bytes((size_t)pl.units * pl.rows, kHeadDim,
+    pl.ws_bytes = partials_bytes((size_t)pl.units * pl.rows, head_dim,
                                  &pl.part_ml_off);
   }
   *out = pl;
@@ -454,29 +454,41 @@ SplitParams split_params(const Plan& pl, const int32_t* prefix_lens,
 }
 
 // The instantiation of the 128/64-row kernel for a launch: balanced or
-// uniform unit plan, fp8 or bf16 K/V.
-template <int NW>
+// uniform unit plan, fp8 or bf16 K/V, head dim D (64: bf16 only).
+template <int NW, int D = kHeadDim>
 int launch_fwdh(bool bal, bool fp8, unsigned grid, hipStream_t hs,
                 const FwdParams& fp) {
   const dim3 g(grid), b(NW * 64);
-  if (fp8) {
-    return bal ? launch(&attn_fwdh_kernel<NW, true, true>, g, b, hs, fp)
-               : launch(&attn_fwdh_kernel<NW, false, true>, g, b, hs, fp);
+  if constexpr (D == kHeadDim) {
+    if (fp8) {
+      return bal ? launch(&attn_fwdh_kernel<NW, true, true>, g, b, hs, fp)
+                 : launch(&attn_fwdh_kernel<NW, false, true>, g, b, hs, fp);
+    }
   }
-  return bal ? launch(&attn_fwdh_kernel<NW, true, false>, g, b, hs, fp)
-             : launch(&attn_fwdh_kernel<NW, false, false>, g, b, hs, fp);
+  return bal ? launch(&attn_fwdh_kernel<NW, true, false, D>, g, b, hs, fp)
+             : launch(&attn_fwdh_kernel<NW, false, false, D>, g, b, hs, fp);
 }
 
 // The instantiation of the 256-row kernel for a launch.
+template <int D = kHeadDim>
 int launch_fwd256(bool bal, bool fp8, unsigned grid, hipStream_t hs,
                   const FwdParams& fp) {
   const dim3 g(grid), b(512);
-  if (fp8) {
-    return bal ? launch(&attn_fwd256_kernel<true, true>, g, b, hs, fp)
-               : launch(&attn_fwd256_kernel<false, true>, g, b, hs, fp);
+  if constexpr (D == kHeadDim) {
+    if (fp8) {
+      return bal ? launch(&attn_fwd256_kernel<true, true>, g, b, hs, fp)
+                 : launch(&attn_fwd256_kernel<false, true>, g, b, hs, fp);
+    }
   }
-  return bal ? launch(&attn_fwd256_kernel<true, false>, g, b, hs, fp)
-             : launch(&attn_fwd256_kernel<false, false>, g, b, hs, fp);
+  return bal ? launch(&attn_fwd256_kernel<true, false, D>, g, b, hs, fp)
+             : launch(&attn_fwd256_kernel<false, false, D>, g, b, hs, fp);
+}
+
+// Head dim 64 with bf16 K/V runs the tuned kernels when the launch merges
+// its own partials (one split, or few enough row blocks for the in-kernel
+// merge); the separate merge launch is built for head dim 128 only.
+bool tuned_d64(const Plan& pl) {
+  return pl.splits == 1 || pl.blocks <= kMergeCounters;
 }
 
 // Phases of a verify call: the split-KV + tree pass, then the LSE merge.
@@ -494,11 +506,16 @@ int run_verify(int phases, const void* q, const void* k_cache, const void* v_cac
                      void* out, float* lse, void* workspace,
                      size_t workspace_bytes, void* stream,
                      bool fp8 = false, const float* k_scale = nullptr,
-                     const float* v_scale = nullptr) {
+                     const float* v_scale = nullptr, bool allow_d64 = false) {
+  // head dim 64 (tree_attn_verify_ex only): bf16 K/V, both phases in one
+  // call; the caller has checked tuned_d64 for the plan
+  const bool d64 = allow_d64 && head_dim == 64 && !fp8 &&
+                   phases == (kPhaseAttend | kPhaseMerge);
   int st = check_verify_sizes(num_seqs, total_nodes, num_q_heads,
-                              num_kv_heads, head_dim, max_prefix_len,
-                              max_nodes, num_splits, mask_words,
-                              max_pages_per_seq, num_pages, page_size, scale);
+                              num_kv_heads, d64 ? kHeadDim : head_dim,
+                              max_prefix_len, max_nodes, num_splits,
+                              mask_words, max_pages_per_seq, num_pages,
+                              page_size, scale);
   if (st != TREE_ATTN_OK) return st;
   if (num_seqs == 0 || total_nodes == 0) return TREE_ATTN_OK;
   if (!q || !k_cache || !v_cache || !page_table || !prefix_lens ||
@@ -509,8 +526,9 @@ int run_verify(int phases, const void* q, const void* k_cache, const void* v_cac
   Plan pl;
   st = make_plan(num_seqs, total_nodes, num_q_heads, num_kv_heads,
                  max_prefix_len, max_nodes, page_size, num_splits, cu_count(),
-                 &pl);
+                 &pl, d64 ? 64 : kHeadDim);
   if (st != TREE_ATTN_OK) return st;
+  if (d64 && !tuned_d64(pl)) return TREE_ATTN_ERR_UNSUPPORTED;
   if (pl.ws_bytes > 0) {
     if (!workspace) return TREE_ATTN_ERR_WORKSPACE;
     if (workspace_bytes < pl.ws_bytes) return TREE_ATTN_ERR_WORKSPACE;
@@ -562,7 +580,15 @@ int run_verify(int phases, const void* q, const void* k_cache, const void* v_cac
   if (phases & kPhaseAttend) {
     // balanced plans run the instantiations that carry the device plan
     const bool bal = fp.plan.uniform_chunk == 0;
-    if (pl.rows == kRowsPerWG8) {
+    if (d64) {
+      if (pl.rows == kRowsPerWG8) {
+        st = launch_fwd256<64>(bal, false, grid, hs, fp);
+      } else if (pl.rows == kRowsPerWG128) {
+        st = launch_fwdh<8, 64>(bal, false, grid, hs, fp);
+      } else {
+        st = launch_fwdh<4, 64>(bal, false, grid, hs, fp);
+      }
+    } else if (pl.rows == kRowsPerWG8) {
       st = launch_fwd256(bal, fp8, grid, hs, fp);
     } else if (pl.rows == kRowsPerWG128) {
       st = launch_fwdh<8>(bal, fp8, grid, hs, fp);
@@ -682,6 +708,34 @@ int tree_attn_build_mask(const int32_t* parents, const int32_t* tree_offsets,
                 masks, bad_node);
 }
 
+// The tuned kernels' plan of a head-dim-64 call with bf16 K/V, when they
+// take it (tuned_d64); otherwise the variant kernel runs the call.
+bool plan_tuned_d64(int32_t num_seqs, int32_t total_nodes,
+                    int32_t num_q_heads, int32_t num_kv_heads,
+                    int32_t max_prefix_len, int32_t max_nodes,
+                    int32_t page_size, int32_t num_splits, Plan* pl) {
+  if (check_sizes(num_seqs, total_nodes, num_q_heads, num_kv_heads, kHeadDim,
+                  max_prefix_len, max_nodes) != TREE_ATTN_OK ||
+      num_splits < 0 || !is_pow2(page_size) || page_size > 4096 ||
+      num_seqs == 0 || total_nodes == 0) {
+    return false;
+  }
+  if (make_plan(num_seqs, total_nodes, num_q_heads, num_kv_heads,
+                max_prefix_len, max_nodes, page_size, num_splits, cu_count(),
+                pl, 64) != TREE_ATTN_OK) {
+    return false;
+  }
+  return tuned_d64(*pl);
+}
+
+void plan_info(const Plan& pl, int32_t* info) {
+  info[0] = pl.rows == kRowsPerWG64 ? 4 : kWaves;
+  info[1] = pl.rows;
+  info[2] = pl.splits;
+  info[3] = pl.chunk;
+  info[4] = 8 * ((pl.units + 7) / 8);
+}
+
 // Workspace of the tuned kernels' plan (the same for bf16 and fp8 K/V).
 size_t tuned_workspace_size(int32_t num_seqs, int32_t total_nodes,
                             int32_t num_q_heads, int32_t num_kv_heads,
@@ -730,11 +784,7 @@ int describe_tuned(int32_t num_seqs, int32_t total_nodes, int32_t num_q_heads,
                  max_prefix_len, max_nodes, page_size, num_splits, cu_count(),
                  &pl);
   if (st != TREE_ATTN_OK) return st;
-  info[0] = pl.rows == kRowsPerWG64 ? 4 : kWaves;
-  info[1] = pl.rows;
-  info[2] = pl.splits;
-  info[3] = pl.chunk;
-  info[4] = 8 * ((pl.units + 7) / 8);
+  plan_info(pl, info);
   return TREE_ATTN_OK;
 }
 
@@ -760,6 +810,13 @@ int tree_attn_describe_plan_ex(int32_t kv_dtype, int32_t num_seqs,
     return describe_tuned(num_seqs, total_nodes, num_q_heads, num_kv_heads,
                           head_dim, max_prefix_len, max_nodes, page_size,
                           num_splits, info);
+  }
+  Plan tp;
+  if (head_dim == 64 && kv_dtype == TREE_ATTN_KV_BF16 &&
+      plan_tuned_d64(num_seqs, total_nodes, num_q_heads, num_kv_heads,
+                     max_prefix_len, max_nodes, page_size, num_splits, &tp)) {
+    plan_info(tp, info);
+    return TREE_ATTN_OK;
   }
   int st = check_var_sizes(kv_dtype, num_seqs, total_nodes, num_q_heads,
                            num_kv_heads, head_dim, max_prefix_len, max_nodes,
@@ -1079,6 +1136,12 @@ size_t tree_attn_workspace_size_ex(int32_t kv_dtype, int32_t num_seqs,
                                 num_kv_heads, head_dim, max_prefix_len,
                                 max_nodes, page_size, num_splits);
   }
+  Plan tp;
+  if (head_dim == 64 && kv_dtype == TREE_ATTN_KV_BF16 &&
+      plan_tuned_d64(num_seqs, total_nodes, num_q_heads, num_kv_heads,
+                     max_prefix_len, max_nodes, page_size, num_splits, &tp)) {
+    return tp.ws_bytes;
+  }
   if (check_var_sizes(kv_dtype, num_seqs, total_nodes, num_q_heads,
                       num_kv_heads, head_dim, max_prefix_len, max_nodes,
                       page_size, num_splits) != TREE_ATTN_OK ||
@@ -1117,6 +1180,18 @@ int tree_attn_verify_ex(const void* q, const void* k_cache,
                       num_kv_heads, head_dim, scale, num_splits, out, lse,
                       workspace, workspace_bytes, stream,
                       kv_dtype == TREE_ATTN_KV_FP8_E4M3, k_scale, v_scale);
+  }
+  Plan tp;
+  if (head_dim == 64 && kv_dtype == TREE_ATTN_KV_BF16 &&
+      plan_tuned_d64(num_seqs, total_nodes, num_q_heads, num_kv_heads,
+                     max_prefix_len, max_nodes, page_size, num_splits, &tp)) {
+    return run_verify(kPhaseAttend | kPhaseMerge, q, k_cache, v_cache,
+                      page_table, max_pages_per_seq, num_pages, page_size,
+                      prefix_lens, tree_offsets, masks, mask_words, num_seqs,
+                      total_nodes, max_prefix_len, max_nodes, num_q_heads,
+                      num_kv_heads, head_dim, scale, num_splits, out, lse,
+                      workspace, workspace_bytes, stream, false, nullptr,
+                      nullptr, true);
   }
   int st = check_var_sizes(kv_dtype, num_seqs, total_nodes, num_q_heads,
                            num_kv_heads, head_dim, max_prefix_len, max_nodes,
