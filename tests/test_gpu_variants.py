@@ -283,6 +283,47 @@ def test_d64_tuned_parity(name):
     check(wl, f"{name}, 3 splits", num_splits=3)
 
 
+def _random_d64(seed):
+    """Seeded random shapes for bf16 head dim 64 (all three kernel shapes
+    get drawn: narrow and wide GQA groups, short and long key ranges)."""
+    r = np.random.default_rng(seed)
+    wide = seed % 2 == 1
+    hkv = int(r.choice([1, 2, 4]))
+    g = int(r.choice([4, 8]) if wide else r.choice([1, 2, 4, 8]))
+    s = int(r.integers(1, 5))
+    prefix = [int(x) for x in r.integers(2500 if wide else 0,
+                                          5000 if wide else 1500, size=s)]
+    sizes = [int(x) for x in r.integers(0, 300, size=s)]
+    if wide:
+        sizes[0] = max(sizes[0], 256 // g)
+    if max(sizes) == 0:
+        sizes[0] = 1
+    rules = [str(x) for x in r.choice(["pchain", "wide", "chain", "star"],
+                                      size=s)]
+    page = int(r.choice([2, 4, 8, 16, 32, 64]))
+    splits = int(r.choice([0, 1] if wide else [0, 0, 1, 2, 3, 7]))
+    wl = make_workload(seed, prefix_lens=prefix, tree_sizes=sizes,
+                       num_q_heads=g * hkv, num_kv_heads=hkv, page_size=page,
+                       tree_rules=rules, p_chain=float(r.uniform(0.2, 0.95)),
+                       kv_format="bf16", head_dim=64, name=f"d64-random-{seed}")
+    return wl, splits
+
+
+@pytest.mark.parametrize("seed", list(range(600, 612)))
+def test_d64_random_shapes_parity(seed):
+    import tree_masked_attention_amd.api as api
+    wl, splits = _random_d64(seed)
+    plan = api.describe_plan_ex(api.KV_BF16, wl.num_seqs, wl.total_nodes,
+                                wl.num_q_heads, wl.num_kv_heads, 64,
+                                wl.max_prefix_len, wl.max_nodes,
+                                wl.page_size, splits)
+    say(f"[gpu] d64 random {seed}: P={[int(x) for x in wl.prefix_lens]} "
+        f"B={[int(x) for x in wl.tree_sizes]} Hq={wl.num_q_heads} "
+        f"Hkv={wl.num_kv_heads} page={wl.page_size} splits={splits} "
+        f"plan={plan}")
+    check(wl, f"d64-random-{seed}", num_splits=splits)
+
+
 @pytest.mark.parametrize("page", [4, 16])
 def test_fp8_256_rows_one_split(page):
     # one split of 3964 keys on the 256-row kernel (within the 1039 page
