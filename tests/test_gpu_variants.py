@@ -324,6 +324,33 @@ def test_d64_random_shapes_parity(seed):
     check(wl, f"d64-random-{seed}", num_splits=splits)
 
 
+def test_d64_many_row_blocks_take_the_merge_launch():
+    # 4200 one-node trees x 4 kv heads = 16800 row blocks with 2 splits,
+    # more than the workspace's 16384 arrival counters: the head-dim-64
+    # partials are merged by the merge kernel's d = 64 instantiation in a
+    # second launch; sampled sequences against the oracle
+    import tree_masked_attention_amd.api as api
+    wl = make_workload(171, prefix_lens=[100] * 4200, tree_sizes=[1],
+                       num_q_heads=4, num_kv_heads=4, page_size=64,
+                       head_dim=64, kv_format="bf16", name="d64-many-blocks")
+    plan = api.describe_plan_ex(api.KV_BF16, wl.num_seqs, wl.total_nodes, 4,
+                                4, 64, wl.max_prefix_len, wl.max_nodes,
+                                wl.page_size, 2)
+    say(f"[gpu] d64 with 16800 row blocks: plan {plan}")
+    assert plan["splits"] == 2 and plan["rows"] == 64
+    out, lse = run_ex(wl, 2)
+    assert np.isfinite(lse).all()
+    seqs = [0, 1, 777, 2048, 4198, 4199]
+    ref_o, ref_l = oracle.workload_attention(wl, seq_ids=seqs)
+    rows = np.array(seqs)  # one node per sequence
+    eo = np.abs(out[rows] - ref_o[rows]).max()
+    el = (np.abs(lse[rows] - ref_l[rows]) /
+          np.maximum(np.abs(ref_l[rows]), 1)).max()
+    say(f"  sampled sequences {seqs}: max|dout| {eo:.2e}, "
+        f"max rel dlse {el:.2e}")
+    assert eo <= OUT_ATOL and el <= LSE_RTOL
+
+
 @pytest.mark.parametrize("page", [4, 16])
 def test_fp8_256_rows_one_split(page):
     # one split of 3964 keys on the 256-row kernel (within the 1039 page

@@ -98,15 +98,19 @@ constexpr int kMergeRowsPerWG = kMergeWaves * kMergeRows;
 // Workgroups follow the attention launch's units, each unit's rows cut
 // into pieces of kMergeRowsPerWG rows; the workgroups of a row block's
 // split-0 unit merge it (the others have nothing to do).  A wave merges
-// kMergeRows rows, each lane half one row at a time with four columns per
-// lane (8-byte loads, a whole 256-byte row per half-wave instruction); the
-// loads of kMergeSplits splits of all its rows are issued before any is
-// used, and the sums run with a running maximum.
+// kMergeRows rows, D/4 lanes per row (one row per half-wave for D = 128,
+// per quarter-wave for D = 64) with four columns per lane (8-byte loads,
+// a whole row per instruction); the loads of kMergeSplits splits of all
+// its rows are issued before any is used, and the sums run with a running
+// maximum.
+template <int D = kHeadDim>
 __global__ __launch_bounds__(kMergeWaves * 64) void attn_merge_kernel(
     MergeParams p) {
-  constexpr int RL = kMergeRows / 2;  // rows per lane
+  constexpr int LPR = D / 4;          // lanes per row
+  constexpr int RPP = 64 / LPR;       // rows per pass of the wave
+  constexpr int RL = kMergeRows / RPP;  // rows per lane
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int half = lane >> 5, c4 = (lane & 31) * 4;
+  const int half = lane / LPR, c4 = (lane % LPR) * 4;
   const int pieces = p.plan.rows_per_wg / kMergeRowsPerWG;
   const int L = blockIdx.x / pieces;
   const int piece = blockIdx.x - L * pieces;
@@ -128,7 +132,7 @@ __global__ __launch_bounds__(kMergeWaves * 64) void attn_merge_kernel(
   f32x4 acc[RL];
 #pragma unroll
   for (int k = 0; k < RL; ++k) {
-    rr[k] = min(r0 + 2 * k + half, rows - 1);
+    rr[k] = min(r0 + RPP * k + half, rows - 1);
     qrow[k] = (size_t)(un.a + rr[k] / p.G) * p.Hq + un.g * p.G + rr[k] % p.G;
     m_run[k] = -INFINITY;
     l_run[k] = 0.f;
@@ -145,8 +149,7 @@ __global__ __launch_bounds__(kMergeWaves * 64) void attn_merge_kernel(
         const int c = c0 + u;
         const size_t prow = slots.row(c, rr[k]);
         ml[k][u] = *reinterpret_cast<const f32x2*>(p.part_ml + prow * 2);
-        oc[k][u] = *reinterpret_cast<const f16x4*>(p.part_o + prow * kHeadDim +
-                                                   c4);
+        oc[k][u] = *reinterpret_cast<const f16x4*>(p.part_o + prow * D + c4);
       }
     }
 #pragma unroll
@@ -165,13 +168,13 @@ __global__ __launch_bounds__(kMergeWaves * 64) void attn_merge_kernel(
   }
 #pragma unroll
   for (int k = 0; k < RL; ++k) {
-    if (r0 + 2 * k + half >= rows) continue;
+    if (r0 + RPP * k + half >= rows) continue;
     const float inv = merge_inv(l_run[k]);
     bf16x4 r4;
 #pragma unroll
     for (int e = 0; e < 4; ++e) r4[e] = (__bf16)(acc[k][e] * inv);
-    *reinterpret_cast<bf16x4*>(p.out + qrow[k] * kHeadDim + c4) = r4;
-    if ((lane & 31) == 0) p.lse[qrow[k]] = merge_lse(m_run[k], l_run[k]);
+    *reinterpret_cast<bf16x4*>(p.out + qrow[k] * D + c4) = r4;
+    if (c4 == 0) p.lse[qrow[k]] = merge_lse(m_run[k], l_run[k]);
   }
 }
 

@@ -484,12 +484,6 @@ int launch_fwd256(bool bal, bool fp8, unsigned grid, hipStream_t hs,
              : launch(&attn_fwd256_kernel<false, false, D>, g, b, hs, fp);
 }
 
-// Head dim 64 with bf16 K/V runs the tuned kernels when the launch merges
-// its own partials (one split, or few enough row blocks for the in-kernel
-// merge); the separate merge launch is built for head dim 128 only.
-bool tuned_d64(const Plan& pl) {
-  return pl.splits == 1 || pl.blocks <= kMergeCounters;
-}
 
 // Phases of a verify call: the split-KV + tree pass, then the LSE merge.
 enum { kPhaseAttend = 1, kPhaseMerge = 2 };
@@ -508,7 +502,7 @@ int run_verify(int phases, const void* q, const void* k_cache, const void* v_cac
                      bool fp8 = false, const float* k_scale = nullptr,
                      const float* v_scale = nullptr, bool allow_d64 = false) {
   // head dim 64 (tree_attn_verify_ex only): bf16 K/V, both phases in one
-  // call; the caller has checked tuned_d64 for the plan
+  // call
   const bool d64 = allow_d64 && head_dim == 64 && !fp8 &&
                    phases == (kPhaseAttend | kPhaseMerge);
   int st = check_verify_sizes(num_seqs, total_nodes, num_q_heads,
@@ -528,7 +522,6 @@ int run_verify(int phases, const void* q, const void* k_cache, const void* v_cac
                  max_prefix_len, max_nodes, page_size, num_splits, cu_count(),
                  &pl, d64 ? 64 : kHeadDim);
   if (st != TREE_ATTN_OK) return st;
-  if (d64 && !tuned_d64(pl)) return TREE_ATTN_ERR_UNSUPPORTED;
   if (pl.ws_bytes > 0) {
     if (!workspace) return TREE_ATTN_ERR_WORKSPACE;
     if (workspace_bytes < pl.ws_bytes) return TREE_ATTN_ERR_WORKSPACE;
@@ -609,8 +602,10 @@ int run_verify(int phases, const void* q, const void* k_cache, const void* v_cac
     mp.plan = fp.plan;
     const long long mgrid =
         (long long)pl.units * (pl.rows / kMergeRowsPerWG);
-    st = launch(&attn_merge_kernel, dim3((unsigned)mgrid),
-                dim3(kMergeWaves * 64), hs, mp);
+    st = d64 ? launch(&attn_merge_kernel<64>, dim3((unsigned)mgrid),
+                      dim3(kMergeWaves * 64), hs, mp)
+             : launch(&attn_merge_kernel<>, dim3((unsigned)mgrid),
+                      dim3(kMergeWaves * 64), hs, mp);
     if (st != TREE_ATTN_OK) return st;
   }
   return TREE_ATTN_OK;
@@ -708,8 +703,9 @@ int tree_attn_build_mask(const int32_t* parents, const int32_t* tree_offsets,
                 masks, bad_node);
 }
 
-// The tuned kernels' plan of a head-dim-64 call with bf16 K/V, when they
-// take it (tuned_d64); otherwise the variant kernel runs the call.
+// The tuned kernels' plan of a head-dim-64 call with bf16 K/V (false for
+// sizes the plan rejects and for empty calls, which the variant path
+// answers with its own checks).
 bool plan_tuned_d64(int32_t num_seqs, int32_t total_nodes,
                     int32_t num_q_heads, int32_t num_kv_heads,
                     int32_t max_prefix_len, int32_t max_nodes,
@@ -725,7 +721,7 @@ bool plan_tuned_d64(int32_t num_seqs, int32_t total_nodes,
                 pl, 64) != TREE_ATTN_OK) {
     return false;
   }
-  return tuned_d64(*pl);
+  return true;
 }
 
 void plan_info(const Plan& pl, int32_t* info) {
