@@ -110,7 +110,6 @@ KERNEL_SOURCES = {
                            "attn_fwd.hpp", "attn_fwd8.hpp"),
     "attn_merge_kernel": ("common.hpp", "split_plan.hpp", "attn_merge.hpp"),
     "gdn_verify_kernel": ("common.hpp", "gdn.hpp"),
-    "attn_var_kernel": ("common.hpp", "attn_var.hpp"),
 }
 
 
@@ -853,12 +852,8 @@ class VerifyBench:
         self.f_mask = api._lib.tree_attn_build_mask
         self.f_ver = (api._lib.tree_attn_verify_ex if self.variant
                       else api._lib.tree_attn_verify)
-        if self.variant and d != 128 and wl.kv_format != "bf16":
-            self.plan = {"kernel": "attn_var_kernel (+ attn_var_merge_kernel)",
-                         "rows": 128, "workspace_bytes": self.ws_bytes}
-        elif self.variant:
-            # fp8 K/V with head dim 128, bf16 K/V with head dim 64: the tuned
-            # kernels (the standard workloads' plans merge in the kernel)
+        if self.variant:
+            # fp8 K/V or head dim 64: the same tuned kernels and plan
             self.plan = api.describe_plan_ex(kvd, S, N, Hq, wl.num_kv_heads,
                                              d, wl.max_prefix_len,
                                              wl.max_nodes, wl.page_size,
@@ -903,8 +898,6 @@ class VerifyBench:
         return n
 
     def kernel_name(self):
-        if "kernel" in self.plan:
-            return "attn_var_kernel"
         return {256: "attn_fwd256_kernel", 128: "attn_fwdh_kernel<8>",
                 64: "attn_fwdh_kernel<4>"}[self.plan["rows"]]
 

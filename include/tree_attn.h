@@ -554,13 +554,10 @@ int tree_attn_gdn_commit(const void* k, const float* u, const float* g,
  * plan, on FP8 tiles: the DMA ring moves the codes, and each wave
  * converts its operands to bf16 (exactly: every E4M3 value is a bf16
  * value) as it reads them from LDS; the K scale folds into the softmax
- * scale and the V scale into the output.  bf16 with head_dim 64 runs the
- * same kernels on rows of 128 bytes, with the same plan.  FP8 with
- * head_dim 64 runs a separate kernel (128 query rows per workgroup, fp8
- * converted to bf16 on its way into LDS, bf16 matrix cores, fp32
- * accumulation, split partials normalised by their own row sum and stored
- * in fp16 with a power-of-two scale per row, as for tree_attn_verify).
- * Workspace sizes come from tree_attn_workspace_size_ex.
+ * scale and the V scale into the output.  Head dim 64 runs the same
+ * kernels with the same plan, on rows of 128 bytes (bf16) or 64 bytes
+ * (FP8), with split partials of 64 values per row.  Workspace sizes come
+ * from tree_attn_workspace_size_ex.
  *
  * The key range is cut into at most 256 splits of at most 1039 pages each
  * (the kernel copies a split's page ids to LDS), as for tree_attn_verify.
@@ -596,9 +593,8 @@ size_t tree_attn_workspace_size_ex(int32_t kv_dtype, int32_t num_seqs,
 /*
  * tree_attn_describe_plan_ex - tree_attn_describe_plan for the launches of
  * tree_attn_verify_ex (kv_dtype and head_dim as there).  Head dim 128
- * (bf16 or FP8) runs the tuned kernels with tree_attn_verify's plan, and
- * so does bf16 with head dim 64; FP8 with head dim 64 runs the 4-wave,
- * 128-row kernel (workgroups: its attention launch's).
+ * and 64, bf16 or FP8, run the tuned kernels with tree_attn_verify's
+ * plan.
  */
 int tree_attn_describe_plan_ex(int32_t kv_dtype, int32_t num_seqs,
                                int32_t total_nodes, int32_t num_q_heads,

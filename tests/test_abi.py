@@ -144,10 +144,9 @@ def test_describe_plan():
 
 
 def test_describe_plan_ex():
-    # FP8 with head dim 128 runs the tuned kernels with tree_attn_verify's
-    # plan and workspace; bf16 with head dim 64 the tuned kernels with the
-    # same plan (partials of 64 values per row); FP8 with head dim 64 the
-    # 4-wave, 128-row variant kernel
+    # every format and head dim runs the tuned kernels with
+    # tree_attn_verify's plan: FP8 with head dim 128 with its workspace,
+    # head dim 64 (bf16 or FP8) with partials of 64 values per row
     for sizes in [(1, 16, 8, 2, 128, 256, 16, 16, 0),
                   (4, 1024, 32, 8, 128, 32768, 256, 16, 0),
                   (32, 512, 32, 4, 128, 2048, 16, 16, 0),
@@ -159,16 +158,15 @@ def test_describe_plan_ex():
         assert api._lib.tree_attn_workspace_size_ex(api.KV_FP8_E4M3, *sizes) \
             == api._lib.tree_attn_workspace_size(*sizes)
         d64 = sizes[:4] + (64,) + sizes[5:]
-        assert api.describe_plan_ex(api.KV_BF16, *d64) == bf, sizes
-        ws = api._lib.tree_attn_workspace_size_ex(api.KV_BF16, *d64)
-        if bf["splits"] == 1:
-            assert ws == 0
-        else:
-            units = bf["workgroups"]
-            assert 65536 < ws <= 65536 + units * bf["rows"] * (128 + 8) + 512
-    p = api.describe_plan_ex(api.KV_FP8_E4M3, 1, 16, 8, 2, 64, 256, 16, 16,
-                             0)
-    assert p["waves"] == 4 and p["rows"] == 128
+        for kvd in (api.KV_BF16, api.KV_FP8_E4M3):
+            assert api.describe_plan_ex(kvd, *d64) == bf, sizes
+            ws = api._lib.tree_attn_workspace_size_ex(kvd, *d64)
+            if bf["splits"] == 1:
+                assert ws == 0
+            else:
+                units = bf["workgroups"]
+                assert 65536 < ws <= \
+                    65536 + units * bf["rows"] * (128 + 8) + 512
     with pytest.raises(NotImplementedError):
         api.describe_plan_ex(api.KV_BF16, 1, 16, 8, 2, 96, 256, 16, 16, 0)
     with pytest.raises(NotImplementedError):

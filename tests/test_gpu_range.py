@@ -2,7 +2,8 @@
 
 Values far beyond fp16's finite range (|v| up to about 5e5) go through
 forced key-range splits, whose partials travel in fp16 with a power-of-two
-scale per row, on both tuned kernels and on the variant kernel.  The
+scale per row, on the tuned kernels (bf16 and FP8 K/V, head dims 128
+and 64).  The
 attention output is linear in V, so the bar scales with V: max |out -
 oracle| <= 2e-2 * value_scale; the lse does not depend on V (1e-3
 relative, as everywhere).  The scale is a power of two, so the scaled bf16

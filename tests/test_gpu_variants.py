@@ -233,54 +233,50 @@ def test_fp8_tuned_parity(name):
     check(wl, f"{name}, 3 splits", num_splits=3)
 
 
-# bf16 K/V with head dim 64 runs the same three tuned kernel shapes (rows
-# of 128 bytes, like the FP8 tiles of head dim 128)
-def _d64(name, seed, **kw):
+# Head dim 64 runs the same three tuned kernel shapes: bf16 K/V in rows of
+# 128 bytes (like the FP8 tiles of head dim 128), FP8 K/V in rows of 64
+# bytes (one DMA op per wave per tile on the 8-wave shapes)
+def _d64(name, seed, fmt="bf16", **kw):
     kw.setdefault("num_q_heads", 32)
     kw.setdefault("num_kv_heads", 4)
-    return make_workload(seed, name=name, kv_format="bf16", head_dim=64,
-                         **kw)
+    return make_workload(seed, name=name, kv_format=fmt, head_dim=64, **kw)
 
 
 D64_TUNED_CASES = {
-    "d64-r64-ragged": (lambda: _d64("d64-r64", 180, prefix_range=(0, 900),
-                                    num_seqs=32,
-                                    tree_sizes=[1 + (7 * s) % 16
-                                                for s in range(32)]), 64),
-    "d64-r64-split": (lambda: _d64("d64-r64s", 181, prefix_lens=[5000] * 4,
-                                   tree_sizes=[16], num_q_heads=16), 64),
-    "d64-balanced": (lambda: _d64("d64-bal", 182,
-                                  prefix_lens=[300, 4000, 9000],
-                                  tree_sizes=[40, 9, 70], num_q_heads=8,
-                                  num_kv_heads=2), 128),
-    "d64-page4-chain": (lambda: _d64("d64-p4", 183, prefix_lens=[2500],
-                                     tree_sizes=[100], page_size=4,
-                                     num_q_heads=8, num_kv_heads=2,
-                                     tree_rules="chain"), 128),
-    "d64-r256-balanced": (lambda: _d64("d64-r256", 185,
-                                       prefix_lens=[16000, 9000],
-                                       tree_sizes=[64, 70],
-                                       num_kv_heads=8), 256),
-    "d64-r256-page4": (lambda: _d64("d64-r256-p4", 186, prefix_lens=[3900],
-                                    tree_sizes=[64], page_size=4,
-                                    num_q_heads=16), 256),
+    "d64-r64-ragged": (180, dict(prefix_range=(0, 900), num_seqs=32,
+                                 tree_sizes=[1 + (7 * s) % 16
+                                             for s in range(32)]), 64),
+    "d64-r64-split": (181, dict(prefix_lens=[5000] * 4, tree_sizes=[16],
+                                num_q_heads=16), 64),
+    "d64-balanced": (182, dict(prefix_lens=[300, 4000, 9000],
+                               tree_sizes=[40, 9, 70], num_q_heads=8,
+                               num_kv_heads=2), 128),
+    "d64-page4-chain": (183, dict(prefix_lens=[2500], tree_sizes=[100],
+                                  page_size=4, num_q_heads=8, num_kv_heads=2,
+                                  tree_rules="chain"), 128),
+    "d64-r256-balanced": (185, dict(prefix_lens=[16000, 9000],
+                                    tree_sizes=[64, 70], num_kv_heads=8), 256),
+    "d64-r256-page4": (186, dict(prefix_lens=[3900], tree_sizes=[64],
+                                 page_size=4, num_q_heads=16), 256),
 }
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "e4m3"])
 @pytest.mark.parametrize("name", sorted(D64_TUNED_CASES))
-def test_d64_tuned_parity(name):
+def test_d64_tuned_parity(name, fmt):
     import tree_masked_attention_amd.api as api
-    make, rows = D64_TUNED_CASES[name]
-    wl = make()
+    seed, kw, rows = D64_TUNED_CASES[name]
+    wl = _d64(f"{name}-{fmt}", seed, fmt, **kw)
+    kvd = api.KV_BF16 if fmt == "bf16" else api.KV_FP8_E4M3
     req = 1 if name == "d64-r256-page4" else 0
-    plan = api.describe_plan_ex(api.KV_BF16, wl.num_seqs, wl.total_nodes,
+    plan = api.describe_plan_ex(kvd, wl.num_seqs, wl.total_nodes,
                                 wl.num_q_heads, wl.num_kv_heads, 64,
                                 wl.max_prefix_len, wl.max_nodes,
                                 wl.page_size, req)
-    say(f"[gpu] bf16 d=64 tuned {name}: plan {plan}")
+    say(f"[gpu] {fmt} d=64 tuned {name}: plan {plan}")
     assert plan["rows"] == rows
-    check(wl, name, num_splits=req)
-    check(wl, f"{name}, 3 splits", num_splits=3)
+    check(wl, f"{name}/{fmt}", num_splits=req)
+    check(wl, f"{name}/{fmt}, 3 splits", num_splits=3)
 
 
 def _random_d64(seed):

@@ -32,7 +32,7 @@ constexpr int kEpilogueStage = 72 * 1024;
 template <int NW, bool kBalanced, bool kFp8, int D = kHeadDim>
 __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
   static_assert(NW == 8 || NW == 4, "shape");
-  static_assert(D == kHeadDim || (D == 64 && !kFp8), "head dim");
+  static_assert(D == kHeadDim || D == 64, "head dim");
   constexpr int kRows = 16 * NW;         // query rows per workgroup
   constexpr int kThreads = NW * 64;
   constexpr int kEB = kFp8 ? 1 : 2;      // bytes per cached element
@@ -40,17 +40,23 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
   // 128-byte rows (fp8 with d = 128, bf16 with d = 64): 8 chunks of 16
   // bytes per row, 8 rows per DMA op
   constexpr bool kNarrow = kRowB == 128;
+  constexpr int kRowChunks = kRowB / 16;  // 16-byte chunks per row
+  // 1-KB DMA ops of a 64-row matrix tile; with fewer than one per wave
+  // (64-byte rows of fp8 with d = 64 on 8 waves), each wave moves one op,
+  // of K (waves 0-3) or of V
+  constexpr int kMatOps = kRowChunks;
+  constexpr bool kSplitOps = kMatOps < NW;
   constexpr int kKSteps = D / 16;        // MFMA k-steps over the head dim
   constexpr int kDB = D / 32;            // 32-wide head-dim blocks of O
   constexpr int kHalfDB = kDB / 2;       // the blocks a wave finishes
   // Q staging DMA ops per wave (bf16 rows of D values, 1 KB per op)
   constexpr int kQOps = kRows * D * 2 / 1024 / NW;
   // 1-KB DMA ops per wave per matrix: each moves 4 bf16 or 8 fp8 rows
-  constexpr int kOpsPerMat = (kRowB / 16) / NW;
-  constexpr int kOps = 2 * kOpsPerMat;
+  constexpr int kOpsPerMat = kSplitOps ? 1 : kMatOps / NW;
+  constexpr int kOps = kSplitOps ? 1 : 2 * kOpsPerMat;
   constexpr int kRowsPerOp = 1024 / kRowB;
   constexpr int kDmaRows = kRowsPerOp * kOpsPerMat;  // tile rows a wave moves
-  constexpr int kLog2DmaRows = NW == 8 ? 3 : 4;
+  constexpr int kLog2DmaRows = kDmaRows == 8 ? 3 : 4;
   static_assert((1 << kLog2DmaRows) == kDmaRows, "shape");
   __shared__ __align__(1024) unsigned char ring[2 * kVOff];
   __shared__ int pg_lds[kPageCache];
@@ -79,7 +85,11 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
       (unsigned)(size_t)(__attribute__((address_space(3))) uint64_t*)mk_lds;
   const int lrow = lane >> 4, lchunk = lane & 15;  // Q rows, 16-B chunks
   // a lane's row and 16-byte chunk within one K/V DMA op
-  const int drow = kNarrow ? lane >> 3 : lrow, dchunk = kNarrow ? lane & 7 : lchunk;
+  const int drow = lane / kRowChunks, dchunk = lane % kRowChunks;
+  // the wave's row group within the matrix tile it moves, and (64-byte
+  // rows) whether that is V
+  const int dma_w = kSplitOps ? wave % kMatOps : wave;
+  const bool dma_v = kSplitOps && wave >= kMatOps;
 
   // Prologue, two rounds of memory latency before the first tile's scores:
   // (1) the split's page-table entries go to LDS by DMA while the tree
@@ -170,7 +180,13 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
   unsigned k_off[kKSteps];
 #pragma unroll
   for (int kc = 0; kc < kKSteps; ++kc) {
-    if constexpr (kFp8) {
+    if constexpr (kFp8 && kRowB == 64) {
+      // fp8 rows of 64 B (d = 64), chunk c stored at c ^ ((row >> 2) & 3);
+      // the lane's 8 values are half of chunk kc
+      const int row = kh * 32 + col;
+      k_off[kc] = ring_base + row * 64 + ((kc ^ ((row >> 2) & 3)) << 4) +
+                  half * 8;
+    } else if constexpr (kFp8) {
       // fp8 rows of 128 B, 16-byte chunk c stored at c ^ ((row >> 1) & 7);
       // the lane's 8 values d = kc*16 + half*8 .. +7 are half of chunk kc
       const int row = kh * 32 + col;
@@ -201,8 +217,14 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
       const int j = lane & 15, r8 = j >> 1;
       const int row = kh * 32 + 8 * (r8 >> 2) + 4 * half + (r8 & 3);
       const int chunk = 2 * db + ((lane >> 4) & 1);
-      v_off[db] = ring_base + kVOff + row * 128 +
-                  ((chunk ^ ((row >> 1) & 7)) << 4) + 8 * (j & 1);
+      if constexpr (kRowB == 64) {
+        // rows of 64 B: chunk c stored at c ^ 2 ((row >> 2) & 1)
+        v_off[db] = ring_base + kVOff + row * 64 +
+                    ((chunk ^ (2 * ((row >> 2) & 1))) << 4) + 8 * (j & 1);
+      } else {
+        v_off[db] = ring_base + kVOff + row * 128 +
+                    ((chunk ^ ((row >> 1) & 7)) << 4) + 8 * (j & 1);
+      }
     } else if constexpr (kNarrow) {
       // bf16 rows of 128 B (d = 64): chunk c stored at c ^ 4 ((row >> 1) & 1)
       const int row = kh * 32 + 4 * half + y;
@@ -227,20 +249,24 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
   // source chunk of the lane's 16 bytes (the LDS chunk is fixed by the
   // lane): 256-byte rows K chunk ^ (row & 15), V chunk ^ 4 (row & 3) (for
   // the 16-bit transposing reads); 128-byte rows K chunk ^ ((row >> 1) & 7),
-  // V the same for fp8 and chunk ^ 4 ((row >> 1) & 1) for bf16
+  // V the same for fp8 and chunk ^ 4 ((row >> 1) & 1) for bf16; 64-byte
+  // rows K chunk ^ ((row >> 2) & 3), V chunk ^ 2 ((row >> 2) & 1)
   auto k_chunk = [](int c, int row) -> unsigned {
-    return (unsigned)(kNarrow ? c ^ ((row >> 1) & 7) : c ^ (row & 15));
+    return (unsigned)(kRowB == 64 ? c ^ ((row >> 2) & 3)
+                                  : (kNarrow ? c ^ ((row >> 1) & 7)
+                                             : c ^ (row & 15)));
   };
   auto v_chunk = [](int c, int row) -> unsigned {
-    return (unsigned)(kFp8 ? c ^ ((row >> 1) & 7)
-                           : (kNarrow ? c ^ (4 * ((row >> 1) & 1))
-                                      : c ^ (4 * (row & 3))));
+    return (unsigned)(kRowB == 64 ? c ^ (2 * ((row >> 2) & 1))
+                      : (kFp8 ? c ^ ((row >> 1) & 7)
+                              : (kNarrow ? c ^ (4 * ((row >> 1) & 1))
+                                         : c ^ (4 * (row & 3)))));
   };
   unsigned k_row_off[kOpsPerMat], v_row_off[kOpsPerMat];
 #pragma unroll
   for (int k = 0; k < kOpsPerMat; ++k) {
     const int rw = kRowsPerOp * k + drow;
-    const int row = kDmaRows * wave + rw;  // row within the tile
+    const int row = kDmaRows * dma_w + rw;  // row within the tile
     k_row_off[k] = rw * tok_bytes + (k_chunk(dchunk, row) << 4);
     v_row_off[k] = rw * tok_bytes + (v_chunk(dchunk, row) << 4);
   }
@@ -250,7 +276,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
     unsigned st;
   };
   auto dma_plan = [&](int t) -> DmaPlan {
-    const int w0 = kbeg + t * kKeyTile + kDmaRows * wave;
+    const int w0 = kbeg + t * kKeyTile + kDmaRows * dma_w;
     const int pi = clampi((w0 >> p.log2_page) - lp0, 0, kPageCache - 1);
     const unsigned pgu =
         min((unsigned)__builtin_amdgcn_readfirstlane(pg_lds[pi]), pg_last);
@@ -260,14 +286,22 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
                    ring_base + (unsigned)(t & (kStages - 1)) * kTileBytes};
   };
   auto dma_part = [&](const DmaPlan& dp, int k) {
-    const unsigned dst = dp.st + (wave * kOpsPerMat + k) * 1024;
-    dma16_sbase(dp.kb0, k_row_off[k], dst);
-    dma16_sbase(dp.vb0, v_row_off[k], dst + kVOff);
+    const unsigned dst = dp.st + (dma_w * kOpsPerMat + k) * 1024;
+    if constexpr (kSplitOps) {
+      if (dma_v) {
+        dma16_sbase(dp.vb0, v_row_off[k], dst + kVOff);
+      } else {
+        dma16_sbase(dp.kb0, k_row_off[k], dst);
+      }
+    } else {
+      dma16_sbase(dp.kb0, k_row_off[k], dst);
+      dma16_sbase(dp.vb0, v_row_off[k], dst + kVOff);
+    }
   };
   auto issue = [&](int t) {
     const int t0 = kbeg + t * kKeyTile;
     const unsigned st = ring_base + (unsigned)(t & (kStages - 1)) * kTileBytes;
-    const int w0 = t0 + kDmaRows * wave;
+    const int w0 = t0 + kDmaRows * dma_w;
     if (fast_pages && w0 + kDmaRows - 1 < kend) {
       const DmaPlan dp = dma_plan(t);
 #pragma unroll
@@ -285,12 +319,20 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
     }
 #pragma unroll
     for (int k = 0; k < kOpsPerMat; ++k) {
-      const int row = kDmaRows * wave + kRowsPerOp * k + drow;
+      const int row = kDmaRows * dma_w + kRowsPerOp * k + drow;
       const size_t off = (size_t)(unsigned)pg[k] * page_bytes +
                          (unsigned)slot[k] * tok_bytes + g * kRowB;
-      const unsigned dst = st + (wave * kOpsPerMat + k) * 1024;
-      dma16(kbase + off + (k_chunk(dchunk, row) << 4), dst);
-      dma16(vbase + off + (v_chunk(dchunk, row) << 4), dst + kVOff);
+      const unsigned dst = st + (dma_w * kOpsPerMat + k) * 1024;
+      if constexpr (kSplitOps) {
+        if (dma_v) {
+          dma16(vbase + off + (v_chunk(dchunk, row) << 4), dst + kVOff);
+        } else {
+          dma16(kbase + off + (k_chunk(dchunk, row) << 4), dst);
+        }
+      } else {
+        dma16(kbase + off + (k_chunk(dchunk, row) << 4), dst);
+        dma16(vbase + off + (v_chunk(dchunk, row) << 4), dst + kVOff);
+      }
     }
   };
 
@@ -369,7 +411,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
 #pragma unroll
       for (int db = 0; db < kDB; ++db) {
         if constexpr (kFp8) {
-          vf[db] = e4m3x8_to_bf16(lds_read_tr8(v_off[db] + so + hf * 16 * 128));
+          vf[db] = e4m3x8_to_bf16(lds_read_tr8(v_off[db] + so + hf * 16 * kRowB));
         } else {
           const unsigned va = v_off[db] + so + hf * 16 * kRowB;
           const s16x4 lo = lds_read_tr(va);

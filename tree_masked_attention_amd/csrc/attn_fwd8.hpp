@@ -21,23 +21,29 @@ constexpr int kRowsPerWG8 = 256;
 
 template <bool kBalanced, bool kFp8, int D = kHeadDim>
 __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
-  static_assert(D == kHeadDim || (D == 64 && !kFp8), "head dim");
+  static_assert(D == kHeadDim || D == 64, "head dim");
   constexpr int NW = 8;
   constexpr int QB = 1;                  // 32-query blocks per wave
   constexpr int kThreads = NW * 64;
   constexpr int kEB = kFp8 ? 1 : 2;      // bytes per cached element
   constexpr int kRowB = D * kEB;         // bytes per cached (token, head)
   // 128-byte rows (fp8 with d = 128, bf16 with d = 64): 8 chunks of 16
-  // bytes per row, 8 rows per DMA op
+  // bytes per row, 8 rows per DMA op; 64-byte rows (fp8 with d = 64): 4
+  // chunks, 16 rows per op
   constexpr bool kNarrow = kRowB == 128;
+  constexpr int kRowChunks = kRowB / 16;  // 16-byte chunks per row
   constexpr int kKSteps = D / 16;        // MFMA k-steps over the head dim
   constexpr int kDB = D / 32;            // 32-wide head-dim blocks of O
-  // 1-KB DMA ops per wave per matrix: each moves 4 or 8 rows
-  constexpr int kOpsPerMat = (kRowB / 16) / NW;
-  constexpr int kOps = 2 * kOpsPerMat;
+  // 1-KB DMA ops of a 64-row matrix tile; with fewer than one per wave
+  // (64-byte rows), each wave moves one op, of K (waves 0-3) or of V
+  constexpr int kMatOps = kRowChunks;
+  constexpr bool kSplitOps = kMatOps < NW;
+  // 1-KB DMA ops per wave per matrix it moves: each moves 4, 8 or 16 rows
+  constexpr int kOpsPerMat = kSplitOps ? 1 : kMatOps / NW;
+  constexpr int kOps = kSplitOps ? 1 : 2 * kOpsPerMat;
   constexpr int kRowsPerOp = 1024 / kRowB;
   constexpr int kDmaRows = kRowsPerOp * kOpsPerMat;  // tile rows a wave moves
-  constexpr int kLog2DmaRows = 3;
+  constexpr int kLog2DmaRows = kDmaRows == 8 ? 3 : 4;
   static_assert((1 << kLog2DmaRows) == kDmaRows, "shape");
   __shared__ __align__(1024) unsigned char ring[2 * kVOff];
   __shared__ int pg_lds[kPageCache];
@@ -150,7 +156,12 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
   unsigned k_off[kKSteps];
 #pragma unroll
   for (int kc = 0; kc < kKSteps; ++kc) {
-    if constexpr (kFp8) {
+    if constexpr (kFp8 && kRowB == 64) {
+      // fp8 rows of 64 B (d = 64), chunk c stored at c ^ ((row >> 2) & 3);
+      // the lane's 8 values are half of chunk kc
+      k_off[kc] = ring_base + col * 64 + ((kc ^ ((col >> 2) & 3)) << 4) +
+                  half * 8;
+    } else if constexpr (kFp8) {
       // fp8 rows of 128 B, 16-byte chunk c stored at c ^ ((row >> 1) & 7);
       // the lane's 8 values d = kc*16 + half*8 .. +7 are half of chunk kc
       // (32-key block offsets keep the swizzle: 32 rows = 16 row pairs)
@@ -176,8 +187,14 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
       const int j = lane & 15, r8 = j >> 1;
       const int row = 8 * (r8 >> 2) + 4 * half + (r8 & 3);
       const int chunk = 2 * db + ((lane >> 4) & 1);
-      v_off[db] = ring_base + kVOff + row * 128 +
-                  ((chunk ^ ((row >> 1) & 7)) << 4) + 8 * (j & 1);
+      if constexpr (kRowB == 64) {
+        // rows of 64 B: chunk c stored at c ^ 2 ((row >> 2) & 1)
+        v_off[db] = ring_base + kVOff + row * 64 +
+                    ((chunk ^ (2 * ((row >> 2) & 1))) << 4) + 8 * (j & 1);
+      } else {
+        v_off[db] = ring_base + kVOff + row * 128 +
+                    ((chunk ^ ((row >> 1) & 7)) << 4) + 8 * (j & 1);
+      }
     } else if constexpr (kNarrow) {
       // bf16 rows of 128 B (d = 64): chunk c stored at c ^ 4 ((row >> 1) & 1)
       // (the four rows a half-wave reads then cover all banks)
@@ -192,24 +209,33 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
   }
 
   // ---- DMA of one tile: wave w moves rows kDmaRows*w .. of K and of V, as
-  // kOpsPerMat instructions of 4 rows (lane l: row 4k + l/16, chunk l%16).
+  // kOpsPerMat instructions of 4 rows (lane l: row 4k + l/16, chunk l%16)
+  // or 8 rows; with 64-byte rows, rows 16 (w % 4) .. of K or V.
   const int pmask = (1 << p.log2_page) - 1;
   const unsigned tok_bytes = (unsigned)p.Hkv * kRowB;
   const unsigned page_bytes = tok_bytes << p.log2_page;
   // a lane's row and 16-byte chunk within one DMA op
-  const int lrow = kNarrow ? lane >> 3 : lane >> 4;
-  const int lchunk = kNarrow ? lane & 7 : lane & 15;
+  const int lrow = lane / kRowChunks;
+  const int lchunk = lane % kRowChunks;
+  // the wave's row group within the matrix tile it moves, and (64-byte
+  // rows) whether that is V
+  const int dma_w = kSplitOps ? wave % kMatOps : wave;
+  const bool dma_v = kSplitOps && wave >= kMatOps;
   // source chunk of the lane's 16 bytes (the LDS chunk is fixed by the
   // lane): 256-byte rows K chunk ^ (row & 15), V chunk ^ 4 (row & 3);
   // 128-byte rows K chunk ^ ((row >> 1) & 7), V the same for fp8 and
-  // chunk ^ 4 ((row >> 1) & 1) for bf16
+  // chunk ^ 4 ((row >> 1) & 1) for bf16; 64-byte rows K chunk ^
+  // ((row >> 2) & 3), V chunk ^ 2 ((row >> 2) & 1)
   auto k_chunk = [](int c, int row) -> unsigned {
-    return (unsigned)(kNarrow ? c ^ ((row >> 1) & 7) : c ^ (row & 15));
+    return (unsigned)(kRowB == 64 ? c ^ ((row >> 2) & 3)
+                                  : (kNarrow ? c ^ ((row >> 1) & 7)
+                                             : c ^ (row & 15)));
   };
   auto v_chunk = [](int c, int row) -> unsigned {
-    return (unsigned)(kFp8 ? c ^ ((row >> 1) & 7)
-                           : (kNarrow ? c ^ (4 * ((row >> 1) & 1))
-                                      : c ^ (4 * (row & 3))));
+    return (unsigned)(kRowB == 64 ? c ^ (2 * ((row >> 2) & 1))
+                      : (kFp8 ? c ^ ((row >> 1) & 7)
+                              : (kNarrow ? c ^ (4 * ((row >> 1) & 1))
+                                         : c ^ (4 * (row & 3)))));
   };
   const char* kbase = reinterpret_cast<const char*>(p.k);
   const char* vbase = reinterpret_cast<const char*>(p.v);
@@ -219,7 +245,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
 #pragma unroll
   for (int k = 0; k < kOpsPerMat; ++k) {
     const int rw = kRowsPerOp * k + lrow;
-    const int row = kDmaRows * wave + rw;  // row within the tile
+    const int row = kDmaRows * dma_w + rw;  // row within the tile
     k_row_off[k] = rw * tok_bytes + (k_chunk(lchunk, row) << 4);
     v_row_off[k] = rw * tok_bytes + (v_chunk(lchunk, row) << 4);
   }
@@ -232,7 +258,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
     unsigned st;
   };
   auto dma_plan = [&](int t) -> DmaPlan {
-    const int w0 = kbeg + t * kKeyTile + kDmaRows * wave;
+    const int w0 = kbeg + t * kKeyTile + kDmaRows * dma_w;
     const int pi = clampi((w0 >> p.log2_page) - lp0, 0, kPageCache - 1);
     const unsigned pgu = (unsigned)__builtin_amdgcn_readfirstlane(pg_lds[pi]);
     const size_t off = (size_t)pgu * page_bytes +
@@ -241,14 +267,22 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
                    ring_base + (unsigned)(t & (kStages - 1)) * kTileBytes};
   };
   auto dma_part = [&](const DmaPlan& dp, int k) {
-    const unsigned dst = dp.st + (wave * kOpsPerMat + k) * 1024;
-    dma16_sbase(dp.kb0, k_row_off[k], dst);
-    dma16_sbase(dp.vb0, v_row_off[k], dst + kVOff);
+    const unsigned dst = dp.st + (dma_w * kOpsPerMat + k) * 1024;
+    if constexpr (kSplitOps) {
+      if (dma_v) {
+        dma16_sbase(dp.vb0, v_row_off[k], dst + kVOff);
+      } else {
+        dma16_sbase(dp.kb0, k_row_off[k], dst);
+      }
+    } else {
+      dma16_sbase(dp.kb0, k_row_off[k], dst);
+      dma16_sbase(dp.vb0, v_row_off[k], dst + kVOff);
+    }
   };
   auto issue = [&](int t) {
     const int t0 = kbeg + t * kKeyTile;
     const unsigned st = ring_base + (unsigned)(t & (kStages - 1)) * kTileBytes;
-    const int w0 = t0 + kDmaRows * wave;
+    const int w0 = t0 + kDmaRows * dma_w;
     if (fast_pages && w0 + kDmaRows - 1 < kend) {
       const int pi = clampi((w0 >> p.log2_page) - lp0, 0, kPageCache - 1);
       const unsigned pgu =
@@ -257,9 +291,17 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
                          (unsigned)(w0 & pmask) * tok_bytes + g * kRowB;
 #pragma unroll
       for (int k = 0; k < kOpsPerMat; ++k) {
-        const unsigned dst = st + (wave * kOpsPerMat + k) * 1024;
-        dma16_sbase(kbase + off, k_row_off[k], dst);
-        dma16_sbase(vbase + off, v_row_off[k], dst + kVOff);
+        const unsigned dst = st + (dma_w * kOpsPerMat + k) * 1024;
+        if constexpr (kSplitOps) {
+          if (dma_v) {
+            dma16_sbase(vbase + off, v_row_off[k], dst + kVOff);
+          } else {
+            dma16_sbase(kbase + off, k_row_off[k], dst);
+          }
+        } else {
+          dma16_sbase(kbase + off, k_row_off[k], dst);
+          dma16_sbase(vbase + off, v_row_off[k], dst + kVOff);
+        }
       }
       return;
     }
@@ -270,8 +312,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
     // reloads also waits for every DMA in flight.
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    const int slrow = kNarrow ? ln >> 3 : ln >> 4;
-    const int slchunk = kNarrow ? ln & 7 : ln & 15;
+    const int slrow = (int)((unsigned)ln / kRowChunks);
+    const int slchunk = (int)((unsigned)ln % kRowChunks);
     int pg[kOpsPerMat], slot[kOpsPerMat];
 #pragma unroll
     for (int k = 0; k < kOpsPerMat; ++k) {
@@ -281,12 +323,20 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
     }
 #pragma unroll
     for (int k = 0; k < kOpsPerMat; ++k) {
-      const int row = kDmaRows * wave + kRowsPerOp * k + slrow;
+      const int row = kDmaRows * dma_w + kRowsPerOp * k + slrow;
       const size_t off = (size_t)(unsigned)pg[k] * page_bytes +
                          (unsigned)slot[k] * tok_bytes + g * kRowB;
-      const unsigned dst = st + (wave * kOpsPerMat + k) * 1024;
-      dma16(kbase + off + (k_chunk(slchunk, row) << 4), dst);
-      dma16(vbase + off + (v_chunk(slchunk, row) << 4), dst + kVOff);
+      const unsigned dst = st + (dma_w * kOpsPerMat + k) * 1024;
+      if constexpr (kSplitOps) {
+        if (dma_v) {
+          dma16(vbase + off + (v_chunk(slchunk, row) << 4), dst + kVOff);
+        } else {
+          dma16(kbase + off + (k_chunk(slchunk, row) << 4), dst);
+        }
+      } else {
+        dma16(kbase + off + (k_chunk(slchunk, row) << 4), dst);
+        dma16(vbase + off + (v_chunk(slchunk, row) << 4), dst + kVOff);
+      }
     }
   };
 
@@ -342,7 +392,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       if constexpr (kFp8) {
-        kf[c] = e4m3x8_to_bf16(lds_read8(k_off[4 * h + c] + so + kb * 32 * 128));
+        kf[c] = e4m3x8_to_bf16(lds_read8(k_off[4 * h + c] + so + kb * 32 * kRowB));
       } else {
         kf[c] = lds_read16(k_off[4 * h + c] + so + kb * 32 * kRowB);
       }
@@ -354,7 +404,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
     for (int db = 0; db < kDB; ++db) {
       if constexpr (kFp8) {
         vf[db] = e4m3x8_to_bf16(
-            lds_read_tr8(v_off[db] + so + (kb * 32 + hf * 16) * 128));
+            lds_read_tr8(v_off[db] + so + (kb * 32 + hf * 16) * kRowB));
       } else {
         const unsigned va = v_off[db] + so + (kb * 32 + hf * 16) * kRowB;
         const s16x4 lo = lds_read_tr(va);

@@ -17,7 +17,6 @@
 #include "attn_fwd128h.hpp"
 #include "attn_fwd8.hpp"
 #include "attn_merge.hpp"
-#include "attn_var.hpp"
 #include "common.hpp"
 #include "gdn.hpp"
 #include "mask_build.hpp"
@@ -329,81 +328,6 @@ CommitParams commit_params(void* k_cache, void* v_cache,
   return cp;
 }
 
-// Plan of the variant kernel (head dim 64, or fp8 K/V): 128 query rows per
-// workgroup, up to four workgroups per CU; the key range is cut until the
-// grid offers about two workgroups per CU (at least 256 keys per split, at
-// most kMaxSplits splits) -- more splits would cost more in partials than
-// they gain in occupancy.
-struct VarPlan {
-  int mblocks = 0;
-  int splits = 1;
-  int chunk = 0;
-  long long grid = 0;
-  size_t part_ml_off = 0;
-  size_t ws_bytes = 0;
-};
-
-int make_var_plan(int S, int N, int Hq, int Hkv, int D, int max_prefix_len,
-                  int max_nodes, int page_size, int req_splits, int cus,
-                  VarPlan* out) {
-  VarPlan pl;
-  const long long G = Hq / Hkv;
-  const long long rows = G * max_nodes;
-  const long long T = std::max(1LL, (long long)max_prefix_len + max_nodes);
-  pl.mblocks = (int)std::max(1LL, (rows + kVarRows - 1) / kVarRows);
-  const long long units0 = (long long)S * Hkv * pl.mblocks;
-  // a split's page ids must fit the kernel's LDS copy of them
-  const long long max_chunk = std::max<long long>(
-      kVarTile,
-      ((long long)(kVarPageCache - 1) * page_size) / kVarTile * kVarTile);
-  const long long min_splits = (T + max_chunk - 1) / max_chunk;
-  if (min_splits > kMaxSplits) return TREE_ATTN_ERR_UNSUPPORTED;
-  long long splits = req_splits;
-  if (splits <= 0) {
-    splits = (2LL * cus + units0 - 1) / std::max(1LL, units0);
-    splits = std::min(splits, std::max(1LL, T / kMinKeysPerSplit));
-  }
-  splits = std::min<long long>(std::max(std::max(1LL, splits), min_splits),
-                               kMaxSplits);
-  long long chunk = (T + splits - 1) / splits;
-  chunk = (chunk + kVarTile - 1) / kVarTile * kVarTile;
-  chunk = std::min(chunk, max_chunk);
-  splits = (T + chunk - 1) / chunk;
-  pl.splits = (int)splits;
-  pl.chunk = (int)chunk;
-  pl.grid = units0 * splits;
-  if (pl.grid > 0x7fffffffLL) return TREE_ATTN_ERR_UNSUPPORTED;
-  if (splits > 1) {
-    pl.ws_bytes = partials_bytes((size_t)N * Hq * splits, D, &pl.part_ml_off);
-  }
-  *out = pl;
-  return TREE_ATTN_OK;
-}
-
-int check_var_sizes(int kv_dtype, int S, int N, int Hq, int Hkv, int D,
-                    int max_prefix_len, int max_nodes, int page_size,
-                    int num_splits) {
-  if (S < 0 || N < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 ||
-      max_prefix_len < 0 || max_nodes < 0 || num_splits < 0 ||
-      Hq % Hkv != 0) {
-    return TREE_ATTN_ERR_SHAPE;
-  }
-  if (!is_pow2(page_size) || page_size > 4096) return TREE_ATTN_ERR_SHAPE;
-  if ((D != 64 && D != 128) ||
-      (kv_dtype != TREE_ATTN_KV_BF16 && kv_dtype != TREE_ATTN_KV_FP8_E4M3) ||
-      max_nodes > TREE_ATTN_MAX_NODES ||
-      (long long)max_prefix_len + max_nodes > (1LL << 30)) {
-    return TREE_ATTN_ERR_UNSUPPORTED;
-  }
-  return TREE_ATTN_OK;
-}
-
-template <int D, bool FP8>
-int launch_var(const VarPlan& pl, const VarParams& vp, hipStream_t hs) {
-  return launch(&attn_var_kernel<D, FP8>, dim3((unsigned)pl.grid),
-                dim3(kVarThreads), hs, vp);
-}
-
 // Size checks of a verify call (everything but the pointers).
 int check_verify_sizes(int S, int N, int Hq, int Hkv, int head_dim,
                        int max_prefix_len, int max_nodes, int num_splits,
@@ -454,16 +378,14 @@ SplitParams split_params(const Plan& pl, const int32_t* prefix_lens,
 }
 
 // The instantiation of the 128/64-row kernel for a launch: balanced or
-// uniform unit plan, fp8 or bf16 K/V, head dim D (64: bf16 only).
+// uniform unit plan, fp8 or bf16 K/V, head dim D.
 template <int NW, int D = kHeadDim>
 int launch_fwdh(bool bal, bool fp8, unsigned grid, hipStream_t hs,
                 const FwdParams& fp) {
   const dim3 g(grid), b(NW * 64);
-  if constexpr (D == kHeadDim) {
-    if (fp8) {
-      return bal ? launch(&attn_fwdh_kernel<NW, true, true>, g, b, hs, fp)
-                 : launch(&attn_fwdh_kernel<NW, false, true>, g, b, hs, fp);
-    }
+  if (fp8) {
+    return bal ? launch(&attn_fwdh_kernel<NW, true, true, D>, g, b, hs, fp)
+               : launch(&attn_fwdh_kernel<NW, false, true, D>, g, b, hs, fp);
   }
   return bal ? launch(&attn_fwdh_kernel<NW, true, false, D>, g, b, hs, fp)
              : launch(&attn_fwdh_kernel<NW, false, false, D>, g, b, hs, fp);
@@ -474,11 +396,9 @@ template <int D = kHeadDim>
 int launch_fwd256(bool bal, bool fp8, unsigned grid, hipStream_t hs,
                   const FwdParams& fp) {
   const dim3 g(grid), b(512);
-  if constexpr (D == kHeadDim) {
-    if (fp8) {
-      return bal ? launch(&attn_fwd256_kernel<true, true>, g, b, hs, fp)
-                 : launch(&attn_fwd256_kernel<false, true>, g, b, hs, fp);
-    }
+  if (fp8) {
+    return bal ? launch(&attn_fwd256_kernel<true, true, D>, g, b, hs, fp)
+               : launch(&attn_fwd256_kernel<false, true, D>, g, b, hs, fp);
   }
   return bal ? launch(&attn_fwd256_kernel<true, false, D>, g, b, hs, fp)
              : launch(&attn_fwd256_kernel<false, false, D>, g, b, hs, fp);
@@ -501,9 +421,8 @@ int run_verify(int phases, const void* q, const void* k_cache, const void* v_cac
                      size_t workspace_bytes, void* stream,
                      bool fp8 = false, const float* k_scale = nullptr,
                      const float* v_scale = nullptr, bool allow_d64 = false) {
-  // head dim 64 (tree_attn_verify_ex only): bf16 K/V, both phases in one
-  // call
-  const bool d64 = allow_d64 && head_dim == 64 && !fp8 &&
+  // head dim 64 (tree_attn_verify_ex only): both phases in one call
+  const bool d64 = allow_d64 && head_dim == 64 &&
                    phases == (kPhaseAttend | kPhaseMerge);
   int st = check_verify_sizes(num_seqs, total_nodes, num_q_heads,
                               num_kv_heads, d64 ? kHeadDim : head_dim,
@@ -575,11 +494,11 @@ int run_verify(int phases, const void* q, const void* k_cache, const void* v_cac
     const bool bal = fp.plan.uniform_chunk == 0;
     if (d64) {
       if (pl.rows == kRowsPerWG8) {
-        st = launch_fwd256<64>(bal, false, grid, hs, fp);
+        st = launch_fwd256<64>(bal, fp8, grid, hs, fp);
       } else if (pl.rows == kRowsPerWG128) {
-        st = launch_fwdh<8, 64>(bal, false, grid, hs, fp);
+        st = launch_fwdh<8, 64>(bal, fp8, grid, hs, fp);
       } else {
-        st = launch_fwdh<4, 64>(bal, false, grid, hs, fp);
+        st = launch_fwdh<4, 64>(bal, fp8, grid, hs, fp);
       }
     } else if (pl.rows == kRowsPerWG8) {
       st = launch_fwd256(bal, fp8, grid, hs, fp);
@@ -703,27 +622,6 @@ int tree_attn_build_mask(const int32_t* parents, const int32_t* tree_offsets,
                 masks, bad_node);
 }
 
-// The tuned kernels' plan of a head-dim-64 call with bf16 K/V (false for
-// sizes the plan rejects and for empty calls, which the variant path
-// answers with its own checks).
-bool plan_tuned_d64(int32_t num_seqs, int32_t total_nodes,
-                    int32_t num_q_heads, int32_t num_kv_heads,
-                    int32_t max_prefix_len, int32_t max_nodes,
-                    int32_t page_size, int32_t num_splits, Plan* pl) {
-  if (check_sizes(num_seqs, total_nodes, num_q_heads, num_kv_heads, kHeadDim,
-                  max_prefix_len, max_nodes) != TREE_ATTN_OK ||
-      num_splits < 0 || !is_pow2(page_size) || page_size > 4096 ||
-      num_seqs == 0 || total_nodes == 0) {
-    return false;
-  }
-  if (make_plan(num_seqs, total_nodes, num_q_heads, num_kv_heads,
-                max_prefix_len, max_nodes, page_size, num_splits, cu_count(),
-                pl, 64) != TREE_ATTN_OK) {
-    return false;
-  }
-  return true;
-}
-
 void plan_info(const Plan& pl, int32_t* info) {
   info[0] = pl.rows == kRowsPerWG64 ? 4 : kWaves;
   info[1] = pl.rows;
@@ -732,14 +630,25 @@ void plan_info(const Plan& pl, int32_t* info) {
   info[4] = 8 * ((pl.units + 7) / 8);
 }
 
-// Workspace of the tuned kernels' plan (the same for bf16 and fp8 K/V).
+// Cache formats of tree_attn_verify_ex: bf16 or FP8 E4M3 K/V with head
+// dim 64 or 128, all on the tuned kernels.
+bool ex_format_ok(int32_t kv_dtype, int32_t head_dim) {
+  return (kv_dtype == TREE_ATTN_KV_BF16 ||
+          kv_dtype == TREE_ATTN_KV_FP8_E4M3) &&
+         (head_dim == 64 || head_dim == kHeadDim);
+}
+
+// Workspace of the tuned kernels' plan (the same for bf16 and fp8 K/V;
+// head dim 64 only for tree_attn_verify_ex's calls).
 size_t tuned_workspace_size(int32_t num_seqs, int32_t total_nodes,
                             int32_t num_q_heads, int32_t num_kv_heads,
                             int32_t head_dim, int32_t max_prefix_len,
                             int32_t max_nodes, int32_t page_size,
-                            int32_t num_splits) {
-  if (check_sizes(num_seqs, total_nodes, num_q_heads, num_kv_heads, head_dim,
-                  max_prefix_len, max_nodes) != TREE_ATTN_OK ||
+                            int32_t num_splits, bool allow_d64 = false) {
+  const bool d64 = allow_d64 && head_dim == 64;
+  if (check_sizes(num_seqs, total_nodes, num_q_heads, num_kv_heads,
+                  d64 ? kHeadDim : head_dim, max_prefix_len,
+                  max_nodes) != TREE_ATTN_OK ||
       num_splits < 0 || !is_pow2(page_size) || page_size > 4096) {
     return 0;
   }
@@ -747,7 +656,7 @@ size_t tuned_workspace_size(int32_t num_seqs, int32_t total_nodes,
   Plan pl;
   if (make_plan(num_seqs, total_nodes, num_q_heads, num_kv_heads,
                 max_prefix_len, max_nodes, page_size, num_splits, cu_count(),
-                &pl) != TREE_ATTN_OK) {
+                &pl, d64 ? 64 : kHeadDim) != TREE_ATTN_OK) {
     return 0;
   }
   return pl.ws_bytes;
@@ -763,14 +672,17 @@ size_t tree_attn_workspace_size(int32_t num_seqs, int32_t total_nodes,
                               max_nodes, page_size, num_splits);
 }
 
-// The tuned kernels' launch for these sizes (bf16 or fp8 K/V).
+// The tuned kernels' launch for these sizes (bf16 or fp8 K/V; head dim 64
+// only for tree_attn_verify_ex's calls: the plan does not depend on it).
 int describe_tuned(int32_t num_seqs, int32_t total_nodes, int32_t num_q_heads,
                    int32_t num_kv_heads, int32_t head_dim,
                    int32_t max_prefix_len, int32_t max_nodes,
-                   int32_t page_size, int32_t num_splits, int32_t* info) {
+                   int32_t page_size, int32_t num_splits, int32_t* info,
+                   bool allow_d64 = false) {
   if (info == nullptr) return TREE_ATTN_ERR_NULL;
+  const bool d64 = allow_d64 && head_dim == 64;
   int st = check_sizes(num_seqs, total_nodes, num_q_heads, num_kv_heads,
-                       head_dim, max_prefix_len, max_nodes);
+                       d64 ? kHeadDim : head_dim, max_prefix_len, max_nodes);
   if (st != TREE_ATTN_OK) return st;
   if (num_splits < 0 || !is_pow2(page_size) || page_size > 4096) {
     return TREE_ATTN_ERR_SHAPE;
@@ -778,7 +690,7 @@ int describe_tuned(int32_t num_seqs, int32_t total_nodes, int32_t num_q_heads,
   Plan pl;
   st = make_plan(num_seqs, total_nodes, num_q_heads, num_kv_heads,
                  max_prefix_len, max_nodes, page_size, num_splits, cu_count(),
-                 &pl);
+                 &pl, d64 ? 64 : kHeadDim);
   if (st != TREE_ATTN_OK) return st;
   plan_info(pl, info);
   return TREE_ATTN_OK;
@@ -801,34 +713,10 @@ int tree_attn_describe_plan_ex(int32_t kv_dtype, int32_t num_seqs,
                                int32_t page_size, int32_t num_splits,
                                int32_t* info) {
   if (info == nullptr) return TREE_ATTN_ERR_NULL;
-  if (head_dim == kHeadDim && (kv_dtype == TREE_ATTN_KV_BF16 ||
-                               kv_dtype == TREE_ATTN_KV_FP8_E4M3)) {
-    return describe_tuned(num_seqs, total_nodes, num_q_heads, num_kv_heads,
-                          head_dim, max_prefix_len, max_nodes, page_size,
-                          num_splits, info);
-  }
-  Plan tp;
-  if (head_dim == 64 && kv_dtype == TREE_ATTN_KV_BF16 &&
-      plan_tuned_d64(num_seqs, total_nodes, num_q_heads, num_kv_heads,
-                     max_prefix_len, max_nodes, page_size, num_splits, &tp)) {
-    plan_info(tp, info);
-    return TREE_ATTN_OK;
-  }
-  int st = check_var_sizes(kv_dtype, num_seqs, total_nodes, num_q_heads,
-                           num_kv_heads, head_dim, max_prefix_len, max_nodes,
-                           page_size, num_splits);
-  if (st != TREE_ATTN_OK) return st;
-  VarPlan pl;
-  st = make_var_plan(num_seqs, total_nodes, num_q_heads, num_kv_heads,
-                     head_dim, max_prefix_len, max_nodes, page_size,
-                     num_splits, cu_count(), &pl);
-  if (st != TREE_ATTN_OK) return st;
-  info[0] = kVarThreads / 64;
-  info[1] = kVarRows;
-  info[2] = pl.splits;
-  info[3] = pl.chunk;
-  info[4] = (int)pl.grid;
-  return TREE_ATTN_OK;
+  if (!ex_format_ok(kv_dtype, head_dim)) return TREE_ATTN_ERR_UNSUPPORTED;
+  return describe_tuned(num_seqs, total_nodes, num_q_heads, num_kv_heads,
+                        head_dim, max_prefix_len, max_nodes, page_size,
+                        num_splits, info, true);
 }
 
 int tree_attn_verify(const void* q, const void* k_cache, const void* v_cache,
@@ -1126,31 +1014,10 @@ size_t tree_attn_workspace_size_ex(int32_t kv_dtype, int32_t num_seqs,
                                    int32_t num_kv_heads, int32_t head_dim,
                                    int32_t max_prefix_len, int32_t max_nodes,
                                    int32_t page_size, int32_t num_splits) {
-  if (head_dim == kHeadDim && (kv_dtype == TREE_ATTN_KV_BF16 ||
-                               kv_dtype == TREE_ATTN_KV_FP8_E4M3)) {
-    return tuned_workspace_size(num_seqs, total_nodes, num_q_heads,
-                                num_kv_heads, head_dim, max_prefix_len,
-                                max_nodes, page_size, num_splits);
-  }
-  Plan tp;
-  if (head_dim == 64 && kv_dtype == TREE_ATTN_KV_BF16 &&
-      plan_tuned_d64(num_seqs, total_nodes, num_q_heads, num_kv_heads,
-                     max_prefix_len, max_nodes, page_size, num_splits, &tp)) {
-    return tp.ws_bytes;
-  }
-  if (check_var_sizes(kv_dtype, num_seqs, total_nodes, num_q_heads,
-                      num_kv_heads, head_dim, max_prefix_len, max_nodes,
-                      page_size, num_splits) != TREE_ATTN_OK ||
-      num_seqs == 0 || total_nodes == 0) {
-    return 0;
-  }
-  VarPlan pl;
-  if (make_var_plan(num_seqs, total_nodes, num_q_heads, num_kv_heads,
-                    head_dim, max_prefix_len, max_nodes, page_size, num_splits,
-                    cu_count(), &pl) != TREE_ATTN_OK) {
-    return 0;
-  }
-  return pl.ws_bytes;
+  if (!ex_format_ok(kv_dtype, head_dim)) return 0;
+  return tuned_workspace_size(num_seqs, total_nodes, num_q_heads,
+                              num_kv_heads, head_dim, max_prefix_len,
+                              max_nodes, page_size, num_splits, true);
 }
 
 int tree_attn_verify_ex(const void* q, const void* k_cache,
@@ -1167,100 +1034,14 @@ int tree_attn_verify_ex(const void* q, const void* k_cache,
                         int32_t num_splits, void* out, float* lse,
                         void* workspace, size_t workspace_bytes,
                         void* stream) {
-  if (head_dim == kHeadDim && (kv_dtype == TREE_ATTN_KV_BF16 ||
-                               kv_dtype == TREE_ATTN_KV_FP8_E4M3)) {
-    return run_verify(kPhaseAttend | kPhaseMerge, q, k_cache, v_cache,
-                      page_table, max_pages_per_seq, num_pages, page_size,
-                      prefix_lens, tree_offsets, masks, mask_words, num_seqs,
-                      total_nodes, max_prefix_len, max_nodes, num_q_heads,
-                      num_kv_heads, head_dim, scale, num_splits, out, lse,
-                      workspace, workspace_bytes, stream,
-                      kv_dtype == TREE_ATTN_KV_FP8_E4M3, k_scale, v_scale);
-  }
-  Plan tp;
-  if (head_dim == 64 && kv_dtype == TREE_ATTN_KV_BF16 &&
-      plan_tuned_d64(num_seqs, total_nodes, num_q_heads, num_kv_heads,
-                     max_prefix_len, max_nodes, page_size, num_splits, &tp)) {
-    return run_verify(kPhaseAttend | kPhaseMerge, q, k_cache, v_cache,
-                      page_table, max_pages_per_seq, num_pages, page_size,
-                      prefix_lens, tree_offsets, masks, mask_words, num_seqs,
-                      total_nodes, max_prefix_len, max_nodes, num_q_heads,
-                      num_kv_heads, head_dim, scale, num_splits, out, lse,
-                      workspace, workspace_bytes, stream, false, nullptr,
-                      nullptr, true);
-  }
-  int st = check_var_sizes(kv_dtype, num_seqs, total_nodes, num_q_heads,
-                           num_kv_heads, head_dim, max_prefix_len, max_nodes,
-                           page_size, num_splits);
-  if (st != TREE_ATTN_OK) return st;
-  if (mask_words < 1 || max_pages_per_seq < 0 || num_pages < 0) {
-    return TREE_ATTN_ERR_SHAPE;
-  }
-  if ((long long)mask_words * 64 < max_nodes) return TREE_ATTN_ERR_SHAPE;
-  if (!std::isfinite(scale) || !(scale > 0.f)) return TREE_ATTN_ERR_SHAPE;
-  if (num_seqs == 0 || total_nodes == 0) return TREE_ATTN_OK;
-  if (num_pages < 1 || max_pages_per_seq < 1) return TREE_ATTN_ERR_SHAPE;
-  if (!q || !k_cache || !v_cache || !page_table || !prefix_lens ||
-      !tree_offsets || !masks || !out || !lse) {
-    return TREE_ATTN_ERR_NULL;
-  }
-  VarPlan pl;
-  st = make_var_plan(num_seqs, total_nodes, num_q_heads, num_kv_heads,
-                     head_dim, max_prefix_len, max_nodes, page_size, num_splits,
-                     cu_count(), &pl);
-  if (st != TREE_ATTN_OK) return st;
-  if (pl.ws_bytes > 0) {
-    if (!workspace || workspace_bytes < pl.ws_bytes ||
-        reinterpret_cast<uintptr_t>(workspace) % 256 != 0) {
-      return TREE_ATTN_ERR_WORKSPACE;
-    }
-  }
-  VarParams vp;
-  vp.q = static_cast<const __bf16*>(q);
-  vp.k = static_cast<const unsigned char*>(k_cache);
-  vp.v = static_cast<const unsigned char*>(v_cache);
-  vp.k_scale = k_scale;
-  vp.v_scale = v_scale;
-  vp.page_table = page_table;
-  vp.prefix_lens = prefix_lens;
-  vp.tree_offsets = tree_offsets;
-  vp.masks = masks;
-  vp.out = static_cast<__bf16*>(out);
-  vp.lse = lse;
-  vp.part_o = reinterpret_cast<_Float16*>(static_cast<char*>(workspace) +
-                                          kCounterBytes);
-  vp.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                        pl.part_ml_off);
-  vp.max_pps = max_pages_per_seq;
-  vp.num_pages = num_pages;
-  vp.max_tokens = (int)std::min<long long>(
-      (long long)max_pages_per_seq * page_size, 1LL << 30);
-  vp.log2_page = ilog2(page_size);
-  vp.W = mask_words;
-  vp.S = num_seqs;
-  vp.N = total_nodes;
-  vp.Hq = num_q_heads;
-  vp.Hkv = num_kv_heads;
-  vp.G = num_q_heads / num_kv_heads;
-  vp.mblocks = pl.mblocks;
-  vp.splits = pl.splits;
-  vp.chunk = pl.chunk;
-  vp.scale_log2 = scale * kLog2e;
-  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  // head dim 64 (128 ran the tuned kernels above)
-  st = kv_dtype == TREE_ATTN_KV_FP8_E4M3 ? launch_var<64, true>(pl, vp, hs)
-                                         : launch_var<64, false>(pl, vp, hs);
-  if (st != TREE_ATTN_OK) return st;
-  if (pl.splits > 1) {
-    // a separate merge launch: the partials of this kernel are scattered
-    // 8-byte rows and its plans use more splits, so merging in the last
-    // workgroup of a row block was slower than this launch
-    const long long work = (long long)total_nodes * num_q_heads * (head_dim / 4);
-    const unsigned mgrid = (unsigned)((work + 255) / 256);
-    st = launch(&attn_var_merge_kernel<64>, dim3(mgrid), dim3(256), hs, vp);
-    if (st != TREE_ATTN_OK) return st;
-  }
-  return TREE_ATTN_OK;
+  if (!ex_format_ok(kv_dtype, head_dim)) return TREE_ATTN_ERR_UNSUPPORTED;
+  return run_verify(kPhaseAttend | kPhaseMerge, q, k_cache, v_cache,
+                    page_table, max_pages_per_seq, num_pages, page_size,
+                    prefix_lens, tree_offsets, masks, mask_words, num_seqs,
+                    total_nodes, max_prefix_len, max_nodes, num_q_heads,
+                    num_kv_heads, head_dim, scale, num_splits, out, lse,
+                    workspace, workspace_bytes, stream,
+                    kv_dtype == TREE_ATTN_KV_FP8_E4M3, k_scale, v_scale, true);
 }
 
 #ifdef TREE_ATTN_DEBUG
