@@ -65,14 +65,15 @@ def test_large_values_tuned_kernels(name):
                ref_o, ref_l)
 
 
-@pytest.mark.parametrize("fmt,d", [("bf16", 64), ("e4m3", 128)])
-def test_large_values_variant_kernel(fmt, d):
+@pytest.mark.parametrize("fmt,d", [("bf16", 64), ("e4m3", 128),
+                                   ("e4m3", 64)])
+def test_large_values_other_formats(fmt, d):
     from test_gpu_variants import run_ex
     wl = make_workload(302, name=f"big-v-{fmt}-{d}", prefix_lens=[700, 90],
                        tree_sizes=[33, 64], num_q_heads=8, num_kv_heads=2,
                        kv_format=fmt, head_dim=d, value_scale=VSCALE)
     ref_o, ref_l = oracle.workload_attention(wl)
-    say(f"[gpu] large V variant {fmt} d={d}: "
+    say(f"[gpu] large V {fmt} d={d}: "
         f"max|v| = {np.nanmax(np.abs(ref_o)):.3e} (output)")
     for splits in (2, 5):
         out, lse = run_ex(wl, num_splits=splits)
