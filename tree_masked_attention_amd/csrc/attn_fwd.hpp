@@ -287,6 +287,19 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
 
+// Max of a lane's 16 scores of one 32-key block, as a tree of three-way
+// maxima (three dependent steps instead of eight).
+__device__ __forceinline__ float max16(const f32x16& v) {
+  auto mx3 = [](float a, float b, float c) {
+    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b),
+                                         c);
+  };
+  const float a = mx3(v[0], v[1], v[2]), b = mx3(v[3], v[4], v[5]);
+  const float c = mx3(v[6], v[7], v[8]), d = mx3(v[9], v[10], v[11]);
+  const float e = mx3(v[12], v[13], v[14]);
+  return __builtin_elementwise_maximum(mx3(a, b, c), mx3(d, e, v[15]));
+}
+
 // Applies the mask of one tile (keys past the split end; tree keys off the
 // node's root-to-node path) to the scores of one 32-query block.
 __device__ __forceinline__ void apply_tile_mask(f32x16 (&S)[2], uint64_t allow,

@@ -483,22 +483,17 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
       l_run[qb] += t4a + t4b;
     }
   };
-  // reference max for a tile, raised only past the lazy-rescale margin
+  // reference max for a tile, raised only past the lazy-rescale margin;
+  // pm0: this lane's max over key block 0, when found earlier (else
+  // -inf and both blocks are scanned here)
   auto next_ref = [&](const f32x16 (&Sx)[QB][2], float (&m_new)[QB],
-                      float (&alpha)[QB]) -> bool {
+                      float (&alpha)[QB], const float (&pm0)[QB],
+                      bool have_pm0) -> bool {
     bool any_need = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int rr = 0; rr < 16; rr += 2) {
-          tmax = __builtin_elementwise_maximum(
-              __builtin_elementwise_maximum(tmax, Sx[qb][kb][rr]),
-              Sx[qb][kb][rr + 1]);
-        }
-      }
+      float tmax = __builtin_elementwise_maximum(
+          have_pm0 ? pm0[qb] : max16(Sx[qb][0]), max16(Sx[qb][1]));
       tmax = __builtin_elementwise_maximum(tmax, other_half(tmax)) * c2;
       const bool need = tmax > m_ref[qb] + kLazyRescale;
       m_new[qb] = need ? tmax : m_ref[qb];
@@ -535,10 +530,16 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
       __builtin_amdgcn_sched_barrier(0);
     }
     // segment 2: S^T(j+1) keys 32..63, PV(j) keys 0..31 | probabilities
-    // of keys 32..63
+    // of keys 32..63 and (unmasked tiles) the max over keys 0..31 of
+    // tile j+1, so that the step's tail scans only keys 32..63
     qk_block(j + 1, 1, Snext);
     pv_block(j, 0, pf);
     exps_block(Scur, 1, pf);
+    float pm0[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      pm0[qb] = mask_next ? -INFINITY : max16(Snext[qb][0]);
+    }
     __builtin_amdgcn_sched_barrier(0);
     if (dma_inbody) {  // second half
 #pragma unroll
@@ -554,7 +555,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
         apply_tile_mask(Snext[qb], tile_allow(t1, node[qb]), half);
       }
     }
-    return next_ref(Snext, m_new, alpha);
+    return next_ref(Snext, m_new, alpha, pm0, !mask_next);
   };
   auto finish = [&](bool r, const float (&m_new)[QB],
                     const float (&alpha)[QB]) {
@@ -632,8 +633,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd256_kernel(FwdParams p) {
     }
   }
   {
-    float m_new[QB], alpha[QB];
-    next_ref(SA, m_new, alpha);
+    float m_new[QB], alpha[QB], pm0[QB];
+    next_ref(SA, m_new, alpha, pm0, false);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) m_ref[qb] = m_new[qb];
   }
