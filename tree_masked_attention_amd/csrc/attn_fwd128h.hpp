@@ -445,12 +445,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwdh_kernel(FwdParams p) {
   };
   // reference max for the next half tile (lazy raise, as in the others)
   auto next_ref = [&](const f32x16& Sx, float& m_new, float& alpha) -> bool {
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int rr = 0; rr < 16; rr += 2) {
-      tmax = __builtin_elementwise_maximum(
-          __builtin_elementwise_maximum(tmax, Sx[rr]), Sx[rr + 1]);
-    }
+    float tmax = max16(Sx);
     tmax = __builtin_elementwise_maximum(tmax, other_half(tmax)) * c2;
     const bool need = tmax > m_ref + kLazyRescale;
     m_new = need ? tmax : m_ref;
