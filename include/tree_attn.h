@@ -550,14 +550,17 @@ int tree_attn_gdn_commit(const void* k, const float* u, const float* g,
  *                 Ignored for bf16.
  *   head_dim      64 or 128 (q, out: [total_nodes][num_q_heads][head_dim])
  * With bf16 and head_dim 128 this is exactly tree_attn_verify (the same
- * kernels).  FP8 with head_dim 128 runs the same kernels, with the same
- * plan, on FP8 tiles: the DMA ring moves the codes, and each wave
- * converts its operands to bf16 (exactly: every E4M3 value is a bf16
- * value) as it reads them from LDS; the K scale folds into the softmax
- * scale and the V scale into the output.  Head dim 64 runs the same
- * kernels with the same plan, on rows of 128 bytes (bf16) or 64 bytes
- * (FP8), with split partials of 64 values per row.  Workspace sizes come
- * from tree_attn_workspace_size_ex.
+ * kernels).  FP8 with head_dim 128 runs the same kernels on FP8 tiles:
+ * the DMA ring moves the codes, and each wave converts its operands to
+ * bf16 (exactly: every E4M3 value is a bf16 value) as it reads them from
+ * LDS; the K scale folds into the softmax scale and the V scale into the
+ * output.  Head dim 64 runs the same kernels on rows of 128 bytes (bf16)
+ * or 64 bytes (FP8), with split partials of 64 values per row.  The plan
+ * is tree_attn_verify's, with one difference: where bf16 with head_dim
+ * 128 replaces a split of the key range by 64-row blocks (pairs of at
+ * most 128 rows, bandwidth-bound launches), these narrower rows keep
+ * 128-row blocks and the split.  Workspace sizes come from
+ * tree_attn_workspace_size_ex.
  *
  * The key range is cut into at most 256 splits of at most 1039 pages each
  * (the kernel copies a split's page ids to LDS), as for tree_attn_verify.
@@ -582,8 +585,9 @@ int tree_attn_verify_ex(const void* q, const void* k_cache,
                         void* stream);
 
 /* Workspace bytes tree_attn_verify_ex needs for these sizes (0: none, or
- * sizes it would reject).  Same layout and rules as tree_attn_verify's
- * (the first 64 KB are the counter area), so one workspace serves both. */
+ * sizes it would reject).  Same layout as tree_attn_verify's (the first
+ * 64 KB are the counter area), so one workspace of the larger size serves
+ * both. */
 size_t tree_attn_workspace_size_ex(int32_t kv_dtype, int32_t num_seqs,
                                    int32_t total_nodes, int32_t num_q_heads,
                                    int32_t num_kv_heads, int32_t head_dim,
@@ -594,7 +598,8 @@ size_t tree_attn_workspace_size_ex(int32_t kv_dtype, int32_t num_seqs,
  * tree_attn_describe_plan_ex - tree_attn_describe_plan for the launches of
  * tree_attn_verify_ex (kv_dtype and head_dim as there).  Head dim 128
  * and 64, bf16 or FP8, run the tuned kernels with tree_attn_verify's
- * plan.
+ * plan, except that rows narrower than 256 bytes keep a split where that
+ * plan takes 64-row blocks without one.
  */
 int tree_attn_describe_plan_ex(int32_t kv_dtype, int32_t num_seqs,
                                int32_t total_nodes, int32_t num_q_heads,

@@ -143,30 +143,57 @@ def test_describe_plan():
         api.describe_plan(1, 16, 8, 2, 64, 256, 16, 16, 0)
 
 
+def _narrow_row_plan(sizes):
+    """The plan tree_attn_verify_ex takes for rows narrower than 256 bytes
+    (fp8, or head dim 64): tree_attn_verify's plan, except where that plan
+    replaces a key split by 64-row blocks (pairs of 65 .. 128 rows, no
+    requested split): the split is kept, on 128-row blocks."""
+    bf = api.describe_plan(*sizes)
+    S, N, Hq, Hkv, d, P, B, page, req = sizes
+    rows = Hq // Hkv * B
+    if bf["rows"] == 64 and 64 < rows <= 128 and req == 0:
+        two = api.describe_plan(*sizes[:8], 2)
+        # the 128-row plan that the substitution replaced has >= 2 splits
+        assert two["rows"] == 128
+        return None
+    return bf
+
+
 def test_describe_plan_ex():
     # every format and head dim runs the tuned kernels with
-    # tree_attn_verify's plan: FP8 with head dim 128 with its workspace,
-    # head dim 64 (bf16 or FP8) with partials of 64 values per row
+    # tree_attn_verify's plan (FP8 with head dim 128 with its workspace,
+    # head dim 64 with partials of 64 values per row), except that rows
+    # narrower than 256 bytes keep the key split where bf16 with head dim
+    # 128 takes 64-row blocks without one
     for sizes in [(1, 16, 8, 2, 128, 256, 16, 16, 0),
                   (4, 1024, 32, 8, 128, 32768, 256, 16, 0),
                   (32, 512, 32, 4, 128, 2048, 16, 16, 0),
                   (3, 119, 8, 2, 128, 9000, 70, 16, 0),
                   (1, 64, 16, 4, 128, 6000, 64, 16, 3)]:
         bf = api.describe_plan(*sizes)
+        want = _narrow_row_plan(sizes)
         f8 = api.describe_plan_ex(api.KV_FP8_E4M3, *sizes)
-        assert bf == f8, sizes
-        assert api._lib.tree_attn_workspace_size_ex(api.KV_FP8_E4M3, *sizes) \
-            == api._lib.tree_attn_workspace_size(*sizes)
         d64 = sizes[:4] + (64,) + sizes[5:]
-        for kvd in (api.KV_BF16, api.KV_FP8_E4M3):
-            assert api.describe_plan_ex(kvd, *d64) == bf, sizes
-            ws = api._lib.tree_attn_workspace_size_ex(kvd, *d64)
-            if bf["splits"] == 1:
+        plans = [(api.KV_FP8_E4M3, sizes, f8)] + [
+            (kvd, d64, api.describe_plan_ex(kvd, *d64))
+            for kvd in (api.KV_BF16, api.KV_FP8_E4M3)]
+        for kvd, sz, pl in plans:
+            if want is not None:
+                assert pl == want, (sizes, kvd)
+            else:
+                assert pl["rows"] == 128 and pl["waves"] == 8, (sizes, kvd)
+                assert pl["splits"] >= 2, (sizes, kvd)
+            ws = api._lib.tree_attn_workspace_size_ex(kvd, *sz)
+            per_row = 2 * sz[4] + 8
+            if pl["splits"] == 1:
                 assert ws == 0
             else:
-                units = bf["workgroups"]
                 assert 65536 < ws <= \
-                    65536 + units * bf["rows"] * (128 + 8) + 512
+                    65536 + pl["workgroups"] * pl["rows"] * per_row + 512
+        if want is not None:
+            assert api._lib.tree_attn_workspace_size_ex(
+                api.KV_FP8_E4M3, *sizes) == \
+                api._lib.tree_attn_workspace_size(*sizes)
     with pytest.raises(NotImplementedError):
         api.describe_plan_ex(api.KV_BF16, 1, 16, 8, 2, 96, 256, 16, 16, 0)
     with pytest.raises(NotImplementedError):

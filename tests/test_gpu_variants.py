@@ -183,9 +183,10 @@ def test_workspace_reuse_across_formats():
 
 # FP8 K/V with head dim 128 runs the tuned kernels (128 or 64 query rows
 # per workgroup, fp8 tiles converted to bf16 as the matrix cores read
-# them).  Shapes that take the 64-row kernel (pairs of at most 128 rows,
-# enough of them to fill the CUs), the device-balanced split plan (2 to 64
-# sequences with splits), and the slow DMA path (pages of 4 keys).
+# them).  Shapes that take the 64-row kernel (pairs of at most 64 rows),
+# pairs of 65-128 rows on 128-row blocks with a key split (where bf16
+# takes 64-row blocks without one), the device-balanced split plan (2 to
+# 64 sequences with splits), and the slow DMA path (pages of 4 keys).
 def _fp8(name, seed, **kw):
     kw.setdefault("num_q_heads", 32)
     kw.setdefault("num_kv_heads", 4)
@@ -193,13 +194,24 @@ def _fp8(name, seed, **kw):
 
 
 FP8_TUNED_CASES = {
-    "fp8-r64-ragged": (lambda: _fp8("fp8-r64", 190, prefix_range=(0, 900),
-                                    num_seqs=32,
+    "fp8-r128-split-ragged": (lambda: _fp8("fp8-r128s", 190,
+                                           prefix_range=(0, 900),
+                                           num_seqs=32,
+                                           tree_sizes=[1 + (7 * s) % 16
+                                                       for s in range(32)]),
+                              128),
+    "fp8-r128-split-page4": (lambda: _fp8("fp8-r128s-p4", 191,
+                                          prefix_range=(100, 700),
+                                          num_seqs=32, tree_sizes=[16],
+                                          page_size=4), 128),
+    "fp8-r64-ragged": (lambda: _fp8("fp8-r64", 197, prefix_range=(0, 900),
+                                    num_seqs=32, num_q_heads=16,
                                     tree_sizes=[1 + (7 * s) % 16
                                                 for s in range(32)]), 64),
-    "fp8-r64-page4": (lambda: _fp8("fp8-r64-p4", 191,
+    "fp8-r64-page4": (lambda: _fp8("fp8-r64-p4", 198,
                                    prefix_range=(100, 700), num_seqs=32,
-                                   tree_sizes=[16], page_size=4), 64),
+                                   num_q_heads=16, tree_sizes=[16],
+                                   page_size=4), 64),
     "fp8-balanced": (lambda: _fp8("fp8-bal", 192,
                                   prefix_lens=[300, 4000, 9000],
                                   tree_sizes=[40, 9, 70], num_q_heads=8,
@@ -227,8 +239,8 @@ def test_fp8_tuned_parity(name):
                                 wl.max_nodes, wl.page_size, 0)
     say(f"[gpu] fp8 tuned {name}: plan {plan}")
     assert plan["rows"] == rows
-    if name == "fp8-balanced":
-        assert plan["splits"] > 1  # 3 sequences: the device-balanced plan
+    if name == "fp8-balanced" or "split" in name:
+        assert plan["splits"] > 1  # the device-balanced plan
     check(wl, name)
     check(wl, f"{name}, 3 splits", num_splits=3)
 
@@ -243,7 +255,12 @@ def _d64(name, seed, fmt="bf16", **kw):
 
 
 D64_TUNED_CASES = {
-    "d64-r64-ragged": (180, dict(prefix_range=(0, 900), num_seqs=32,
+    "d64-r128-split-ragged": (180, dict(prefix_range=(0, 900), num_seqs=32,
+                                        tree_sizes=[1 + (7 * s) % 16
+                                                    for s in range(32)]),
+                              128),
+    "d64-r64-ragged": (187, dict(prefix_range=(0, 900), num_seqs=32,
+                                 num_q_heads=16,
                                  tree_sizes=[1 + (7 * s) % 16
                                              for s in range(32)]), 64),
     "d64-r64-split": (181, dict(prefix_lens=[5000] * 4, tree_sizes=[16],

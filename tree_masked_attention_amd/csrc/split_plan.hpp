@@ -67,25 +67,44 @@ __device__ __forceinline__ void load_bounds(const SplitParams& q, Unit& u) {
   u.bounds = true;
 }
 
-// Sum over the 64 lanes of a wave (every lane gets the sum).
-__device__ __forceinline__ int wave_sum(int v) {
-  v += __builtin_amdgcn_ds_swizzle(v, 0x1F | (16 << 10));
-  v += __builtin_amdgcn_ds_swizzle(v, 0x1F | (8 << 10));
-  v += __builtin_amdgcn_ds_swizzle(v, 0x1F | (4 << 10));
-  v += __builtin_amdgcn_ds_swizzle(v, 0x1F | (2 << 10));
-  v += __builtin_amdgcn_ds_swizzle(v, 0x1F | (1 << 10));
-  return v + __builtin_bit_cast(int, other_half(__builtin_bit_cast(float, v)));
+// Sum over the 64 lanes of a wave, as a wave-uniform value, from VALU
+// cross-lane moves (DPP) and four lane reads (no LDS-pipe round trips; the
+// balanced decode takes one sum per step of its search).  quad_perm
+// [1,0,3,2] and [2,3,0,1] sum each quad, row_half_mirror and row_mirror
+// each row of 16 lanes; the four row sums are then added.
+__device__ __forceinline__ int wave_sum_uniform(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);
+  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+         __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
 }
 
-// Inclusive prefix sum over the lanes of a wave.
-__device__ __forceinline__ int wave_scan(int v, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int u = __shfl_up(v, d);
-    if (lane >= d) v += u;
-  }
+// ceil(a / b) for 0 <= a < 2^24 and 1 <= b < 2^16: a float quotient (off
+// by at most 2, the quotient being below 2^24), corrected exactly in
+// integers.
+__device__ __forceinline__ int ceil_div_small(int a, int b) {
+  int q = (int)__builtin_ceilf((float)a / (float)b);
+  while (q * b < a) ++q;
+  while (q > 0 && (q - 1) * b >= a) --q;
+  return q;
+}
+
+// Inclusive prefix sum over the lanes of a wave, from DPP moves: row_shr
+// 1, 2, 4, 8 scan each row of 16 lanes, then row_bcast:15 adds the last
+// lane of rows 0 and 2 to rows 1 and 3, and row_bcast:31 the last lane of
+// row 1 to rows 2 and 3 (lanes a move does not reach add 0).
+__device__ __forceinline__ int wave_scan_dpp(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);
   return v;
 }
+
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
@@ -155,8 +174,10 @@ __device__ __forceinline__ Unit decode_unit_lanes(const SplitParams& q,
     T = min(P + B, q.max_tokens);
     w = (B > 0 && T > 0) ? q.Hkv * ceil_div(q.G * B, q.rows_per_wg) : 0;
   }
+  // key range in tiles (T < 2^30, so T64 < 2^24); chunks are whole tiles
+  const int T64 = (T + 63) >> 6;
   auto parts_for = [&](int chunk) -> int {
-    return wave_sum(w > 0 ? w * ceil_div(T, chunk) : 0);
+    return wave_sum_uniform(w > 0 ? w * ceil_div_small(T64, chunk >> 6) : 0);
   };
   // shortest chunk (in tiles) whose units fit the launch
   int lo = q.chunk_min >> 6, hi = q.chunk_max >> 6;
@@ -170,20 +191,20 @@ __device__ __forceinline__ Unit decode_unit_lanes(const SplitParams& q,
   const int chunk = hi << 6;
   const int ns = w > 0 ? ceil_div(T, chunk) : 0;
   const int parts = w * ns;
-  const int incl = wave_scan(parts, lane);
-  const int segs = wave_scan(w, lane);
+  const int incl = wave_scan_dpp(parts);
+  const int segs = wave_scan_dpp(w);
   // the sequence whose units contain L
   const uint64_t hit = __ballot(lane < q.S && L < incl && L >= incl - parts);
   if (hit == 0) return u;
-  const int s = (int)__builtin_ctzll(hit);
-  const int base = __shfl(incl - parts, s);
-  const int seg_base = __shfl(segs - w, s);
+  const int s = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
+  const int base = __builtin_amdgcn_readlane(incl - parts, s);
+  const int seg_base = __builtin_amdgcn_readlane(segs - w, s);
   u.s = s;
-  u.a = __shfl(a, s);
-  u.B = __shfl(B, s);
-  u.P = __shfl(P, s);
-  u.T = __shfl(T, s);
-  u.nsplit = __shfl(ns, s);
+  u.a = __builtin_amdgcn_readlane(a, s);
+  u.B = __builtin_amdgcn_readlane(B, s);
+  u.P = __builtin_amdgcn_readlane(P, s);
+  u.T = __builtin_amdgcn_readlane(T, s);
+  u.nsplit = __builtin_amdgcn_readlane(ns, s);
   u.chunk = chunk;
   u.mblocks = ceil_div(q.G * u.B, q.rows_per_wg);
   int r = L - base;

@@ -97,6 +97,7 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct Plan {
   int rows = 128;    // query rows per workgroup (64: 4 waves; 128, 256: 8)
+  bool uniform = false;  // keep the host's uniform unit plan (no balancing)
   int mblocks = 0;   // row blocks per (sequence, kv head)
   int splits = 1;    // key-range splits
   int chunk = 0;     // keys per split (multiple of the 64-key tile)
@@ -128,7 +129,8 @@ size_t partials_bytes(size_t rows_all, int D, size_t* part_ml_off) {
 // LDS page cache.
 int make_plan(int S, int N, int Hq, int Hkv, int max_prefix_len,
               int max_nodes, int page_size, int req_splits, int cus,
-              Plan* out, int head_dim = kHeadDim) {
+              Plan* out, int head_dim = kHeadDim,
+              int row_bytes = kHeadDim * 2) {
   Plan pl;
   const int G = Hq / Hkv;
   const long long rows = (long long)G * max_nodes;
@@ -183,14 +185,26 @@ int make_plan(int S, int N, int Hq, int Hkv, int max_prefix_len,
   // 128 rows: when 64-row blocks alone give every CU a workgroup, they
   // replace a split of the key range (the two blocks of a pair read the
   // same K/V, which the XCD-aware order keeps in one L2), so no partials
-  // are written or merged.
+  // are written or merged.  Only for cached rows of 256 bytes (bf16, head
+  // dim 128): with narrower rows (fp8, or head dim 64) a tile moves half
+  // the bytes or less for the same vector work (fp8: the conversions too),
+  // and the 64-row kernel's single wave per SIMD costs more than the split.
+  // Those launches keep the split on 128-row blocks with the host's
+  // uniform plan: the device-balanced plan reads every sequence's bounds
+  // before a workgroup knows its unit, a memory round trip ahead of its
+  // page-table slice (measured ~2.5 us per launch on the 30B shape, more
+  // than balancing gains there).
   if (rpw == kRowsPerWG128 && req_splits <= 0 && rows <= kRowsPerWG128 &&
       splits > 1 && min_splits == 1) {
     const long long units64 =
         (long long)S * Hkv * ((rows + kRowsPerWG64 - 1) / kRowsPerWG64);
     if (units64 >= cus) {
-      const int st = choose(kRowsPerWG64);
-      if (st != TREE_ATTN_OK) return st;
+      if (row_bytes == kHeadDim * 2) {
+        const int st = choose(kRowsPerWG64);
+        if (st != TREE_ATTN_OK) return st;
+      } else {
+        pl.uniform = true;
+      }
     }
   }
   // Pairs of at most 64 rows: a 128-row block would run half its waves on
@@ -370,7 +384,7 @@ SplitParams split_params(const Plan& pl, const int32_t* prefix_lens,
   q.chunk_max = pl.max_chunk;
   q.chunk_min = std::min(kMinKeysPerSplit, pl.max_chunk);
   const bool balanced = req_splits <= 0 && pl.splits > 1 && S > 1 &&
-                        S <= kBalancedMaxSeqs;
+                        S <= kBalancedMaxSeqs && !pl.uniform;
   q.uniform_chunk = balanced ? 0 : pl.chunk;
   q.uniform_splits = pl.splits;
   q.uniform_mblocks = pl.mblocks;
@@ -439,7 +453,7 @@ int run_verify(int phases, const void* q, const void* k_cache, const void* v_cac
   Plan pl;
   st = make_plan(num_seqs, total_nodes, num_q_heads, num_kv_heads,
                  max_prefix_len, max_nodes, page_size, num_splits, cu_count(),
-                 &pl, d64 ? 64 : kHeadDim);
+                 &pl, d64 ? 64 : kHeadDim, (d64 ? 64 : kHeadDim) * (fp8 ? 1 : 2));
   if (st != TREE_ATTN_OK) return st;
   if (pl.ws_bytes > 0) {
     if (!workspace) return TREE_ATTN_ERR_WORKSPACE;
@@ -644,7 +658,8 @@ size_t tuned_workspace_size(int32_t num_seqs, int32_t total_nodes,
                             int32_t num_q_heads, int32_t num_kv_heads,
                             int32_t head_dim, int32_t max_prefix_len,
                             int32_t max_nodes, int32_t page_size,
-                            int32_t num_splits, bool allow_d64 = false) {
+                            int32_t num_splits, bool allow_d64 = false,
+                            bool fp8 = false) {
   const bool d64 = allow_d64 && head_dim == 64;
   if (check_sizes(num_seqs, total_nodes, num_q_heads, num_kv_heads,
                   d64 ? kHeadDim : head_dim, max_prefix_len,
@@ -656,7 +671,8 @@ size_t tuned_workspace_size(int32_t num_seqs, int32_t total_nodes,
   Plan pl;
   if (make_plan(num_seqs, total_nodes, num_q_heads, num_kv_heads,
                 max_prefix_len, max_nodes, page_size, num_splits, cu_count(),
-                &pl, d64 ? 64 : kHeadDim) != TREE_ATTN_OK) {
+                &pl, d64 ? 64 : kHeadDim,
+                (d64 ? 64 : kHeadDim) * (fp8 ? 1 : 2)) != TREE_ATTN_OK) {
     return 0;
   }
   return pl.ws_bytes;
@@ -678,7 +694,7 @@ int describe_tuned(int32_t num_seqs, int32_t total_nodes, int32_t num_q_heads,
                    int32_t num_kv_heads, int32_t head_dim,
                    int32_t max_prefix_len, int32_t max_nodes,
                    int32_t page_size, int32_t num_splits, int32_t* info,
-                   bool allow_d64 = false) {
+                   bool allow_d64 = false, bool fp8 = false) {
   if (info == nullptr) return TREE_ATTN_ERR_NULL;
   const bool d64 = allow_d64 && head_dim == 64;
   int st = check_sizes(num_seqs, total_nodes, num_q_heads, num_kv_heads,
@@ -690,7 +706,7 @@ int describe_tuned(int32_t num_seqs, int32_t total_nodes, int32_t num_q_heads,
   Plan pl;
   st = make_plan(num_seqs, total_nodes, num_q_heads, num_kv_heads,
                  max_prefix_len, max_nodes, page_size, num_splits, cu_count(),
-                 &pl, d64 ? 64 : kHeadDim);
+                 &pl, d64 ? 64 : kHeadDim, (d64 ? 64 : kHeadDim) * (fp8 ? 1 : 2));
   if (st != TREE_ATTN_OK) return st;
   plan_info(pl, info);
   return TREE_ATTN_OK;
@@ -716,7 +732,8 @@ int tree_attn_describe_plan_ex(int32_t kv_dtype, int32_t num_seqs,
   if (!ex_format_ok(kv_dtype, head_dim)) return TREE_ATTN_ERR_UNSUPPORTED;
   return describe_tuned(num_seqs, total_nodes, num_q_heads, num_kv_heads,
                         head_dim, max_prefix_len, max_nodes, page_size,
-                        num_splits, info, true);
+                        num_splits, info, true,
+                        kv_dtype == TREE_ATTN_KV_FP8_E4M3);
 }
 
 int tree_attn_verify(const void* q, const void* k_cache, const void* v_cache,
@@ -1017,7 +1034,8 @@ size_t tree_attn_workspace_size_ex(int32_t kv_dtype, int32_t num_seqs,
   if (!ex_format_ok(kv_dtype, head_dim)) return 0;
   return tuned_workspace_size(num_seqs, total_nodes, num_q_heads,
                               num_kv_heads, head_dim, max_prefix_len,
-                              max_nodes, page_size, num_splits, true);
+                              max_nodes, page_size, num_splits, true,
+                              kv_dtype == TREE_ATTN_KV_FP8_E4M3);
 }
 
 int tree_attn_verify_ex(const void* q, const void* k_cache,
