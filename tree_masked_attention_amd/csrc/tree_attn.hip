@@ -594,6 +594,22 @@ int device_scratch(hipStream_t stream, void** out) {
   return TREE_ATTN_OK;
 }
 
+// Tree construction with MS register slots per lane (MS >= ceil((B+1)/64));
+// kStrict is the one-candidate-per-step build.
+template <bool kStrict>
+int launch_tree(int ms, dim3 grid, dim3 block, hipStream_t hs,
+                const TreeParams& tp) {
+  if (ms <= 1) return launch(&build_tree_kernel<1, kStrict>, grid, block, hs, tp);
+  if (ms <= 2) return launch(&build_tree_kernel<2, kStrict>, grid, block, hs, tp);
+  if (ms <= 3) return launch(&build_tree_kernel<3, kStrict>, grid, block, hs, tp);
+  if (ms <= 4) return launch(&build_tree_kernel<4, kStrict>, grid, block, hs, tp);
+  if (ms <= 5) return launch(&build_tree_kernel<5, kStrict>, grid, block, hs, tp);
+  if (ms <= 6) return launch(&build_tree_kernel<6, kStrict>, grid, block, hs, tp);
+  if (ms <= 8) return launch(&build_tree_kernel<8, kStrict>, grid, block, hs, tp);
+  if (ms <= 16) return launch(&build_tree_kernel<16, kStrict>, grid, block, hs, tp);
+  return launch(&build_tree_kernel<17, kStrict>, grid, block, hs, tp);
+}
+
 }  // namespace
 
 extern "C" {
@@ -862,12 +878,10 @@ int tree_attn_build_tree(const float* logp, const int32_t* tokens,
   const int ms = budget / 64 + 1;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const dim3 grid(num_seqs), block(64);
-  if (ms <= 1) return launch(&build_tree_kernel<1>, grid, block, hs, tp);
-  if (ms <= 2) return launch(&build_tree_kernel<2>, grid, block, hs, tp);
-  if (ms <= 4) return launch(&build_tree_kernel<4>, grid, block, hs, tp);
-  if (ms <= 8) return launch(&build_tree_kernel<8>, grid, block, hs, tp);
-  if (ms <= 16) return launch(&build_tree_kernel<16>, grid, block, hs, tp);
-  return launch(&build_tree_kernel<17>, grid, block, hs, tp);
+  // (an instantiation per slot count up to 8: each extraction selects and
+  // updates a lane's MS slots, so unused slots cost time)
+  return width == 1 ? launch_tree<true>(ms, grid, block, hs, tp)
+                    : launch_tree<false>(ms, grid, block, hs, tp);
 }
 
 int tree_attn_accept(const int32_t* parents, const int32_t* tree_offsets,

@@ -57,9 +57,6 @@ __device__ __forceinline__ float key_score(uint32_t k) {
   return __builtin_bit_cast(float, b);
 }
 
-// Wave-wide max / min through DPP lane moves (no LDS round trip): within
-// quads, half rows and rows by mirrors, then across rows by the row-15 and
-// row-31 broadcasts; lane 63 ends with the result.
 // Wave-wide max / min through DPP operands (no LDS round trip): within
 // quads, half rows and rows by mirrors, then across rows by the row-15 and
 // row-31 broadcasts; lane 63 ends with the result.  Each step is one
@@ -91,25 +88,24 @@ __device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
 
-template <int MS>
+template <int MS, bool kStrict>
 __global__ __launch_bounds__(64) void build_tree_kernel(TreeParams p) {
   __shared__ float L[kTreeMaxLogp];
-  __shared__ int npar[kTreeMaxNodes];
-  __shared__ int nrank[kTreeMaxNodes];
-  __shared__ int ndep[kTreeMaxNodes];
-  __shared__ float nsc[kTreeMaxNodes];
   const int s = blockIdx.x, lane = threadIdx.x;
   const int D = p.D, K = p.K, B = p.B;
   const float* lp = p.logp + (size_t)s * D * K;
   for (int i = lane; i < D * K; i += 64) L[i] = lp[i];
   __syncthreads();
 
-  // this lane's slots: sigma = lane + 64 m
+  // this lane's slots: sigma = lane + 64 m; slot sigma > 0 also keeps the
+  // record of node sigma - 1 (parent slot, rank, depth, score)
   uint32_t key[MS];   // live candidate of the slot (ordered score), 0 = none
   uint32_t pend[MS];  // candidate that becomes live at the end of the step
   int nx[MS];         // rank of the slot's live candidate
   int sdep[MS];       // depth of the slot's node (0: the prefix)
   float ssc[MS];      // score of the slot's node (0: the prefix)
+  int spar[MS];       // parent node index of the slot's node
+  int srank[MS];      // rank of the slot's node among its parent's children
 #pragma unroll
   for (int m = 0; m < MS; ++m) {
     key[m] = 0u;
@@ -117,6 +113,8 @@ __global__ __launch_bounds__(64) void build_tree_kernel(TreeParams p) {
     nx[m] = 0;
     sdep[m] = 0;
     ssc[m] = 0.f;
+    spar[m] = -1;
+    srank[m] = 0;
   }
   if (lane == 0 && D > 0 && K > 0) key[0] = ordered_key(L[0]);  // prefix slot
 
@@ -128,20 +126,22 @@ __global__ __launch_bounds__(64) void build_tree_kernel(TreeParams p) {
     bslot = 0;
 #pragma unroll
     for (int m = 0; m < MS; ++m) {
-      if (key[m] > bkey) {
-        bkey = key[m];
-        bslot = lane + 64 * m;
-      }
+      const bool better = key[m] > bkey;
+      bkey = better ? key[m] : bkey;
+      bslot = better ? lane + 64 * m : bslot;
     }
   };
   rescan();
 
+  // Every update below is a per-lane select on (lane, slot) rather than a
+  // branch on the owning lane: the extraction is one dependent chain, and
+  // on one wave a branch costs more than the selects it skips.
   const int last = max(D * K - 1, 0);
   int size = 0;
   while (size < B) {
     // a step takes min(w, B - size) candidates, fewer when the live ones
     // run out (the step's new nodes only add candidates at its end)
-    const int take = min(p.W, B - size);
+    const int take = kStrict ? 1 : min(p.W, B - size);
     int done = 0;
     for (; done < take; ++done) {
       const uint32_t top = wave_reduce_u32<true>(bkey);
@@ -157,7 +157,8 @@ __global__ __launch_bounds__(64) void build_tree_kernel(TreeParams p) {
       }
       sig = __builtin_amdgcn_readfirstlane(sig);
       const int owner = sig & 63, ms = sig >> 6;
-      // the owner's view of the slot: next rank, its node's depth and score
+      // every lane's view of its register ms: next rank, node depth and
+      // score; the owner's is the extracted slot's
       int c = 0, pd = 0;
       float ps = 0.f;
 #pragma unroll
@@ -168,88 +169,74 @@ __global__ __launch_bounds__(64) void build_tree_kernel(TreeParams p) {
           ps = ssc[m];
         }
       }
-      // the slot's next child (row pd: its children are at depth pd + 1);
-      // read by every lane at its own in-range address, used by the owner
+      // the slot's next child (row pd: its children are at depth pd + 1),
+      // read by every lane at its own in-range address
       const int c1 = c + 1;
-      const float l1 = L[min(pd * K + min(c1, K - 1), last)];
+      const float l1 = L[min(__mul24(pd, K) + min(c1, K - 1), last)];
       const int cu = __builtin_amdgcn_readlane(c, owner);
       const int d = __builtin_amdgcn_readlane(pd, owner) + 1;
       const float sc = key_score(top);
       // the new node's first child (row d)
       const float l0 = L[min(d, D - 1) * K];
       const int v = size++;
-      if (lane == 0) {
-        npar[v] = sig - 1;
-        nrank[v] = cu;
-        ndep[v] = d;
-        nsc[v] = sc;
-      }
-      if (lane == owner) {
-        // depth-1 scores are the row values themselves
-        const uint32_t nk =
-            c1 < K ? ordered_key(pd == 0 ? l1 : ps + l1) : 0u;
-#pragma unroll
-        for (int m = 0; m < MS; ++m) {
-          if (m == ms) {
-            key[m] = nk;
-            nx[m] = c1;
-          }
-        }
-        rescan();
-      }
-      const int sig2 = v + 1;
+      // the owner's slot advances to its next child (depth-1 scores are
+      // the row values themselves)
+      const uint32_t nk = c1 < K ? ordered_key(pd == 0 ? l1 : ps + l1) : 0u;
+      // the new node takes slot v + 1
+      const int sig2 = v + 1, m2 = sig2 >> 6;
+      const bool own = lane == owner, mine = lane == (sig2 & 63);
       const uint32_t pk = d < D ? ordered_key(sc + l0) : 0u;
-      if (lane == (sig2 & 63)) {
 #pragma unroll
-        for (int m = 0; m < MS; ++m) {
-          if (m == (sig2 >> 6)) {
-            sdep[m] = d;
-            ssc[m] = sc;
-            nx[m] = 0;
-            if (p.W == 1) {
-              key[m] = pk;  // the step ends with this extraction
-            } else {
-              pend[m] = pk;
-            }
-          }
-        }
-        // sig2 is this lane's highest slot: it wins only on a higher key
-        if (p.W == 1 && pk > bkey) {
-          bkey = pk;
-          bslot = sig2;
+      for (int m = 0; m < MS; ++m) {
+        const bool adv = own && m == ms;
+        key[m] = adv ? nk : key[m];
+        nx[m] = adv ? c1 : nx[m];
+        const bool put = mine && m == m2;
+        sdep[m] = put ? d : sdep[m];
+        ssc[m] = put ? sc : ssc[m];
+        spar[m] = put ? sig - 1 : spar[m];
+        srank[m] = put ? cu : srank[m];
+        nx[m] = put ? 0 : nx[m];
+        if (kStrict) {
+          key[m] = put ? pk : key[m];  // the step ends with this extraction
+        } else {
+          pend[m] = put ? pk : pend[m];
         }
       }
+      rescan();
     }
-    if (p.W > 1) {
+    if (!kStrict) {
       // end of the step: the new nodes' first children become candidates
 #pragma unroll
       for (int m = 0; m < MS; ++m) {
-        if (pend[m] != 0u) {
-          key[m] = pend[m];
-          pend[m] = 0u;
-        }
+        key[m] = pend[m] != 0u ? pend[m] : key[m];
+        pend[m] = 0u;
       }
       rescan();
     }
     if (done == 0) break;  // nothing was live: the tree is complete
   }
-  __syncthreads();
 
-  // outputs, padded past the tree's size
+  // outputs from the slot records (node v is slot v + 1), padded past the
+  // tree's size
   const size_t o = (size_t)s * B;
-  for (int v = lane; v < B; v += 64) {
-    if (v < size) {
-      const int d = ndep[v];
-      p.parents[o + v] = npar[v];
-      p.out_tokens[o + v] =
-          p.tokens[((size_t)s * D + (d - 1)) * K + nrank[v]];
-      p.depths[o + v] = d;
-      p.scores[o + v] = nsc[v];
-    } else {
-      p.parents[o + v] = -1;
-      p.out_tokens[o + v] = -1;
-      p.depths[o + v] = 0;
-      p.scores[o + v] = 0.f;
+#pragma unroll
+  for (int m = 0; m < MS; ++m) {
+    const int v = lane + 64 * m - 1;
+    if (v >= 0 && v < B) {
+      if (v < size) {
+        const int d = sdep[m];
+        p.parents[o + v] = spar[m];
+        p.out_tokens[o + v] =
+            p.tokens[((size_t)s * D + (d - 1)) * K + srank[m]];
+        p.depths[o + v] = d;
+        p.scores[o + v] = ssc[m];
+      } else {
+        p.parents[o + v] = -1;
+        p.out_tokens[o + v] = -1;
+        p.depths[o + v] = 0;
+        p.scores[o + v] = 0.f;
+      }
     }
   }
   if (lane == 0) p.sizes[s] = size;
