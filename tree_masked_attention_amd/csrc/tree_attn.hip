@@ -596,6 +596,8 @@ int device_scratch(hipStream_t stream, void** out) {
 
 // Tree construction with MS register slots per lane (MS >= ceil((B+1)/64));
 // kStrict is the one-candidate-per-step build.
+static_assert(TREE_ATTN_MAX_NODES / 64 + 1 <= 17,
+              "the largest tree needs at most 17 slots per lane");
 template <bool kStrict>
 int launch_tree(int ms, dim3 grid, dim3 block, hipStream_t hs,
                 const TreeParams& tp) {

@@ -22,8 +22,10 @@
 // ties to the lowest slot), appends the node, advances the slot to its
 // next child and records the new node's own first child as a candidate
 // that becomes live when the step's w extractions are done.  The
-// log-probability rows and the node records live in LDS; the extractions
-// of a tree are sequential, so the kernel is bound by their latency.
+// log-probability rows live in LDS, and slot v + 1 keeps node v's record
+// (parent, rank, depth, score) in its lane's registers until the outputs
+// are written; the extractions of a tree are sequential, so the kernel is
+// bound by their latency.
 #pragma once
 
 #include "common.hpp"
@@ -32,7 +34,6 @@ namespace tree_attn {
 
 constexpr int kTreeMaxLogp = 8192;    // D * K values staged in LDS
 constexpr int kTreeMaxTopK = 64;
-constexpr int kTreeMaxNodes = 1024;
 
 struct TreeParams {
   const float* logp;      // [S][D][K]
