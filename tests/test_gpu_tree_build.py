@@ -67,6 +67,9 @@ CASES = {
     "b64-k8": (4, 16, 8, 64, (1, 8)),
     "b256-k8": (2, 16, 8, 256, (1, 16, 64)),
     "b256-deep": (1, 256, 2, 256, (1, 3)),
+    "b150-k8": (3, 16, 8, 150, (1, 5)),      # 3 slots per lane
+    "b300-k8": (2, 16, 8, 300, (1, 9)),      # 5 slots per lane
+    "b350-k6": (2, 20, 6, 350, (1, 2)),      # 6 slots per lane
     "b1024-k16": (2, 64, 16, 1024, (1, 32)),
     "b1024-k64-d128": (1, 128, 64, 1024, (7,)),
     "b63-edge": (3, 5, 3, 63, (1, 2)),
@@ -97,6 +100,20 @@ def test_tree_build_ties():
     for w in (1, 2, 7):
         say(f"[gpu] tree build ties width {w}")
         check(lp, tok, 100, w, f"ties/w{w}")
+
+
+@pytest.mark.parametrize("budget", (150, 300, 350, 1000))
+def test_tree_build_ties_many_slots(budget):
+    # equal scores between slots held in different registers of a lane
+    # (slot sigma and sigma + 64 m share lane sigma mod 64)
+    rng = np.random.default_rng(budget)
+    S, D, K = 2, 14, 6
+    lp = -np.sort(rng.integers(0, 3, size=(S, D, K)) * 0.25, axis=2)
+    lp = np.ascontiguousarray(-np.sort(-lp, axis=2)).astype(np.float32)
+    tok = rng.integers(0, 1000, size=(S, D, K)).astype(np.int32)
+    for w in (1, 4):
+        say(f"[gpu] tree build ties budget {budget} width {w}")
+        check(lp, tok, budget, w, f"ties-{budget}/w{w}")
 
 
 def test_tree_build_zero_budget_and_depth():
